@@ -1,0 +1,151 @@
+"""Seeded synthetic inputs for the Hyena operator forward hot path.
+
+This module only draws random numbers and lays them out; it holds none of the
+operator's arithmetic (no short convolution, no gating, no transform).  Both the
+fp64 oracle and the HIP library consume exactly the arrays produced here.
+
+Shapes follow the operator as written in the HyenaDNA walkthrough (page "HyenaDNA
+model architecture", section 2.1, HyenaOperator code): ``u_proj`` is the
+in-projected activation after the ``b l d -> b d l`` rearrange, of shape
+[B, (N+1)*D, L]; the long filters are ``k`` rearranged to [N-1, D, L]; the
+long-filter bias is [N-1, D] (HyenaFilter code, section 2.2: ``torch.randn``
+initialisation); the short depthwise Conv1d weight is [(N+1)*D, 3].
+
+Distributions (the pages give no data; these stand in for the language-model and
+genome workloads they describe):
+  * ``normal`` activations: u_proj ~ N(0, 1).
+  * ``onehot`` activations: 4-symbol tokens (nucleotides) drawn uniformly, then a
+    random bias-free Linear(4 -> (N+1)*D) with N(0, 1) weights, i.e. a column
+    lookup ``u_proj[b, :, t] = W[:, tok[b, t]]``.
+  * short conv weights ~ N(0, 1/3) (variance 1/3).
+  * h[o, d, t] = N(0, 1) * exp(-alpha_d * t / L), alpha_d log-spaced over
+    [alpha_lo, alpha_hi] across channels and shared across o.
+  * bias[o, d] ~ N(0, 1).
+Draw order: activations (tokens then W for ``onehot``), short weights, filter
+noise, bias.  bf16 activations are drawn in fp32 and rounded to bf16 with
+round-to-nearest-even; the rounded values are the input to both sides.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    D: int
+    L: int
+    order: int
+    dtype: str  # "f32" or "bf16": dtype of u_proj and y only
+    kind: str  # "normal" or "onehot"
+    alpha_lo: float
+    alpha_hi: float
+    seed: int
+
+    @property
+    def channels(self) -> int:
+        return (self.order + 1) * self.D
+
+    def describe(self) -> str:
+        return (f"B={self.B} D={self.D} L={self.L} order={self.order} "
+                f"{self.dtype} {self.kind}")
+
+
+# The operator shapes of the workloads: a tiny case, HyenaDNA-small, Hyena-LM-125M,
+# a 64K long-context operator (order 3, and the same shape at order 2) and HyenaDNA-1M.
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", 1, 64, 1024, 2, "f32", "normal", 0.3, 30.0, 0),
+    "dna_small": Workload("dna_small", 4, 256, 16384, 2, "f32", "onehot", 0.3, 30.0, 1),
+    "lm125m": Workload("lm125m", 8, 768, 8192, 2, "bf16", "normal", 0.3, 30.0, 2),
+    "long64k_o3": Workload("long64k_o3", 1, 768, 65536, 3, "f32", "normal", 0.3, 30.0, 3),
+    "long64k": Workload("long64k", 1, 768, 65536, 2, "f32", "normal", 0.3, 30.0, 3),
+    "dna_1m": Workload("dna_1m", 1, 256, 1048576, 2, "f32", "onehot", 0.03, 30.0, 4),
+}
+
+
+def custom(B: int, D: int, L: int, order: int, dtype: str = "f32",
+           kind: str = "normal", seed: int = 0, alpha_lo: float = 0.3,
+           alpha_hi: float = 30.0, name: str = "custom") -> Workload:
+    return Workload(name, B, D, L, order, dtype, kind, alpha_lo, alpha_hi, seed)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to the nearest bf16 (ties to even); returns fp32 holding bf16 values."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    rounded = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    out = (rounded << 16).astype(np.uint32)
+    return out.view(np.float32).reshape(x.shape)
+
+
+def bf16_bits(x_bf16_values: np.ndarray) -> np.ndarray:
+    """Upper 16 bits of fp32 values that are already exactly representable in bf16."""
+    x = np.ascontiguousarray(x_bf16_values, dtype=np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Host copies of one workload's inputs (all fp32; bf16 u_proj holds bf16 values)."""
+    wl: Workload
+    u_proj: np.ndarray  # [B, (N+1)D, L] float32
+    short_w: np.ndarray  # [(N+1)D, 3] float32
+    h: np.ndarray  # [N-1, D, L] float32
+    bias: np.ndarray  # [N-1, D] float32
+
+
+def _alphas(D: int, lo: float, hi: float) -> np.ndarray:
+    if D == 1:
+        return np.array([lo], dtype=np.float64)
+    return lo * (hi / lo) ** (np.arange(D, dtype=np.float64) / (D - 1))
+
+
+def generate(wl: Workload, seed: Optional[int] = None) -> Inputs:
+    """Draw one workload's inputs from numpy's PCG64 with the given (or the workload's) seed."""
+    rng = np.random.Generator(np.random.PCG64(wl.seed if seed is None else seed))
+    B, D, L, N = wl.B, wl.D, wl.L, wl.order
+    C = (N + 1) * D
+    if wl.kind == "normal":
+        u = rng.standard_normal((B, C, L), dtype=np.float32)
+    elif wl.kind == "onehot":
+        tok = rng.integers(0, 4, size=(B, L))
+        W = rng.standard_normal((C, 4), dtype=np.float32)
+        u = np.empty((B, C, L), dtype=np.float32)
+        for b in range(B):
+            u[b] = W[:, tok[b]]
+    else:
+        raise ValueError(f"unknown input kind {wl.kind!r}")
+    if wl.dtype == "bf16":
+        u = round_to_bf16(u)
+    elif wl.dtype != "f32":
+        raise ValueError(f"unknown dtype {wl.dtype!r}")
+    short_w = (rng.standard_normal((C, 3), dtype=np.float32)
+               * np.float32(1.0 / np.sqrt(3.0))).astype(np.float32)
+    noise = rng.standard_normal((N - 1, D, L), dtype=np.float32)
+    alpha = _alphas(D, wl.alpha_lo, wl.alpha_hi)
+    t = np.arange(L, dtype=np.float64) / L
+    decay = np.exp(-alpha[:, None] * t[None, :]).astype(np.float32)  # [D, L]
+    h = (noise * decay[None, :, :]).astype(np.float32)
+    bias = rng.standard_normal((N - 1, D), dtype=np.float32)
+    return Inputs(wl, np.ascontiguousarray(u), np.ascontiguousarray(short_w),
+                  np.ascontiguousarray(h), np.ascontiguousarray(bias))
+
+
+def sample_rows(wl: Workload, count: int, seed: int = 12345) -> np.ndarray:
+    """A seeded, sorted sample of flat row indices b*D + d (always includes the first and last)."""
+    total = wl.B * wl.D
+    if count >= total:
+        return np.arange(total, dtype=np.int64)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    picks = set(rng.choice(total, size=max(count - 2, 0), replace=False).tolist())
+    picks.update({0, total - 1})
+    return np.array(sorted(picks), dtype=np.int64)

@@ -1,0 +1,145 @@
+"""fp64 CPU oracle for the Hyena operator forward hot path (test infrastructure).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product (the HIP library and its binding) never does.
+
+The arithmetic lives in ``hyena_oracle.c`` (plain C, fp64, OpenMP over rows);
+this wrapper only marshals numpy arrays.  See that file's header for the
+passages of the pages each step follows and the readings taken where the pages
+are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "hyena_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (fp64, -O2, OpenMP). Returns the library path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.POINTER
+        f32p, f64p, i64p = P(ctypes.c_float), P(ctypes.c_double), P(ctypes.c_int64)
+        i64 = ctypes.c_int64
+        lib.oracle_short_conv_row.argtypes = [f32p, f32p, i64, f64p]
+        lib.oracle_short_conv_row.restype = None
+        lib.oracle_causal_conv_direct.argtypes = [f64p, f64p, i64, f64p]
+        lib.oracle_causal_conv_direct.restype = None
+        lib.oracle_causal_conv_fft.argtypes = [f64p, f64p, i64, f64p]
+        lib.oracle_causal_conv_fft.restype = None
+        lib.oracle_fft.argtypes = [f64p, f64p, i64, ctypes.c_int]
+        lib.oracle_fft.restype = ctypes.c_int
+        lib.oracle_hyena_forward.argtypes = [i64, i64, i64, ctypes.c_int, f32p, f32p, f32p, f32p,
+                                             i64p, i64, f64p, ctypes.c_int, ctypes.c_int]
+        lib.oracle_hyena_forward.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def fft(x: np.ndarray, inverse: bool = False) -> np.ndarray:
+    """Unscaled radix-2 DFT of a complex vector (sign -1 forward, +1 inverse)."""
+    x = np.asarray(x, dtype=np.complex128)
+    re = np.ascontiguousarray(x.real, dtype=np.float64).copy()
+    im = np.ascontiguousarray(x.imag, dtype=np.float64).copy()
+    rc = _load().oracle_fft(_ptr(re, ctypes.c_double), _ptr(im, ctypes.c_double), re.size,
+                            1 if inverse else -1)
+    if rc != 0:
+        raise ValueError("length must be a power of two")
+    return re + 1j * im
+
+
+def short_conv_row(u: np.ndarray, w3: np.ndarray) -> np.ndarray:
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    w3 = np.ascontiguousarray(w3, dtype=np.float32)
+    out = np.empty(u.size, dtype=np.float64)
+    _load().oracle_short_conv_row(_ptr(u, ctypes.c_float), _ptr(w3, ctypes.c_float), u.size,
+                                  _ptr(out, ctypes.c_double))
+    return out
+
+
+def causal_conv(v: np.ndarray, h: np.ndarray, mode: str = "fft") -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    if v.size != h.size:
+        raise ValueError("v and h must have the same length")
+    out = np.empty(v.size, dtype=np.float64)
+    fn = _load().oracle_causal_conv_fft if mode == "fft" else _load().oracle_causal_conv_direct
+    fn(_ptr(v, ctypes.c_double), _ptr(h, ctypes.c_double), v.size, _ptr(out, ctypes.c_double))
+    return out
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def forward(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray,
+            order: int, mode: str = "fft", rows: Optional[Sequence[int]] = None,
+            threads: int = 0) -> np.ndarray:
+    """Hyena operator forward hot path in fp64.
+
+    u_proj [B,(N+1)D,L], short_w [(N+1)D,3], h [N-1,D,L], bias [N-1,D] (all taken as
+    fp32 values).  Returns y as float64, [B,D,L] when ``rows`` is None, otherwise
+    [len(rows), L] for the flat rows b*D + d.
+    """
+    u = np.ascontiguousarray(u_proj, dtype=np.float32)
+    w = np.ascontiguousarray(short_w, dtype=np.float32)
+    hh = np.ascontiguousarray(h, dtype=np.float32)
+    bb = np.ascontiguousarray(bias, dtype=np.float32)
+    B, C, L = u.shape
+    N = int(order)
+    if C % (N + 1):
+        raise ValueError("u_proj channel count must be (order+1)*D")
+    D = C // (N + 1)
+    if w.shape != (C, 3) or hh.shape != (N - 1, D, L) or bb.shape != (N - 1, D):
+        raise ValueError("parameter shapes do not match u_proj")
+    if rows is None:
+        out = np.empty((B, D, L), dtype=np.float64)
+        rp, nr = None, 0
+    else:
+        ra = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        out = np.empty((ra.size, L), dtype=np.float64)
+        rp, nr = _ptr(ra, ctypes.c_int64), ra.size
+    rc = _load().oracle_hyena_forward(B, D, L, N, _ptr(u, ctypes.c_float), _ptr(w, ctypes.c_float),
+                                      _ptr(hh, ctypes.c_float), _ptr(bb, ctypes.c_float), rp, nr,
+                                      _ptr(out, ctypes.c_double), 0 if mode == "direct" else 1,
+                                      int(threads))
+    if rc != 0:
+        raise ValueError("oracle_hyena_forward rejected its arguments")
+    return out
+
+
+def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+    """||got - ref||_2 / ||ref||_2 with got widened to fp64."""
+    g = np.asarray(got, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    den = float(np.linalg.norm(r.ravel()))
+    num = float(np.linalg.norm((g - r).ravel()))
+    return num / den if den > 0 else num
