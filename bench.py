@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the Hyena operator forward hot path (libhyena) on one MI355X.
+
+One step = one hyena_forward over one batch of a workload: short conv + split,
+the order-N gated chain of FFT long convolutions with bias skip, and the final
+gate, all in libhyena's HIP kernels; inputs and the filter spectrum are
+resident in HBM before timing starts (the spectrum is made once per plan and
+timed separately).
+
+Prints ONE JSON line:
+  value            channel-tokens/s = B*D*L / t_step
+  roofline         the dominant kernel against the 8 TB/s HBM peak (algorithmic bytes)
+  cpu_baseline     the fp64 oracle on the host cores, over a bounded sample of rows
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "channel-tokens/s (B·D·L/s) and % HBM peak, Hyena op fwd at L=64K order 2"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def io_bytes(wl) -> int:
+    return 2 if wl.dtype == "bf16" else 4
+
+
+def alg_bytes_forward(wl) -> int:
+    """One read of u_proj, one write of y, one read of the fp32 filter spectrum
+    (bins 0..L of each (o, d)) and of the small parameters."""
+    s = io_bytes(wl)
+    B, D, L, N = wl.B, wl.D, wl.L, wl.order
+    return (s * B * (N + 1) * D * L + s * B * D * L + 8 * (N - 1) * D * (L + 1)
+            + 4 * (N + 1) * D * 3 + 4 * (N - 1) * D)
+
+
+def alg_bytes_pass(wl, family: str) -> int:
+    """Bytes each four-step pass must move by design, per forward (all rows):
+    pass A reads two u_proj rows and writes the L-point complex tile; pass B
+    reads the tile and the spectrum and writes the tile; pass C reads the tile
+    and, for the last step, one gate row and writes y (earlier steps also read
+    the next gate row and write the tile again)."""
+    s = io_bytes(wl)
+    B, D, L, N = wl.B, wl.D, wl.L, wl.order
+    rows = B * D
+    tile = 8 * L
+    if family == "pass_a":
+        return rows * (2 * s * L + tile)
+    if family == "pass_b":
+        return (N - 1) * (rows * (2 * tile) + 8 * D * L)
+    if family == "pass_c":
+        return (N - 1) * rows * (tile + s * L) + rows * s * L + (N - 2) * rows * tile
+    raise ValueError(family)
+
+
+def cpu_baseline(x, wl, budget_s: float):
+    """The oracle (fp64 FFT mode) on a bounded, seeded sample of (b, d) rows."""
+    import oracle
+    from fft_long_convolution_libhyena_amd import synth
+
+    threads = oracle.max_threads()
+    n = max(1, min(wl.B * wl.D, 2 * threads))
+    rows = synth.sample_rows(wl, n, seed=99)
+    t0 = time.perf_counter()
+    oracle.forward(x.u_proj, x.short_w, x.h, x.bias, wl.order, mode="fft", rows=rows)
+    dt = time.perf_counter() - t0
+    if dt < budget_s / 4 and n < wl.B * wl.D:
+        n = int(min(wl.B * wl.D, max(n + 1, n * budget_s / max(dt, 1e-3) * 0.8)))
+        rows = synth.sample_rows(wl, n, seed=99)
+        t0 = time.perf_counter()
+        oracle.forward(x.u_proj, x.short_w, x.h, x.bias, wl.order, mode="fft", rows=rows)
+        dt = time.perf_counter() - t0
+    return {"value": len(rows) * wl.L / dt, "unit": "channel-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {wl.B * wl.D} (b,d) rows of the same inputs, fp64 radix-2 FFT "
+                      f"convolution, OpenMP over rows, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long64k")
+    ap.add_argument("--reps", type=int, default=5, help="timed repetitions of --steps; the median is reported")
+    ap.add_argument("--workspace-mb", type=float, default=0.0,
+                    help="four-step workspace (0 = the library's recommendation)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--check", action="store_true", help="also compare sampled rows with the oracle")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} (WORLD_SIZE={world}) is not supported; "
+              "the path shards over channels with no exchange (see the design notes), run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = synth.WORKLOADS[args.workload]
+    log(f"[bench] workload {wl.name}: {wl.describe()}")
+    t0 = time.perf_counter()
+    x = synth.generate(wl)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    dev = torch.device("cuda", 0)
+    u = torch.from_numpy(x.u_proj).to(dev)
+    if wl.dtype == "bf16":
+        u = u.to(torch.bfloat16)
+    u = u.contiguous()
+    w = torch.from_numpy(x.short_w).to(dev)
+    h = torch.from_numpy(x.h).to(dev)
+    bias = torch.from_numpy(x.bias).to(dev)
+
+    plan = Plan(wl.L, wl.D, wl.order, wl.dtype)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    spec = plan.spectrum(h)
+    ev1.record()
+    torch.cuda.synchronize()
+    spectrum_ms = ev0.elapsed_time(ev1)
+    ws_bytes = int(args.workspace_mb * 2 ** 20) if args.workspace_mb > 0 else plan.workspace_bytes(wl.B)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    y = torch.empty((wl.B, wl.D, wl.L), dtype=plan.io_dtype, device=dev)
+    log(f"[bench] path={plan.path} spectrum {spectrum_ms:.3f} ms workspace {ws_bytes / 2**20:.1f} MiB")
+
+    for _ in range(args.warmup):
+        plan.forward(u, w, spec, bias, y, ws)
+    torch.cuda.synchronize()
+
+    times = []
+    for rep in range(args.reps):
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            plan.forward(u, w, spec, bias, y, ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / args.steps)
+        log(f"[bench] rep {rep}: {times[-1] * 1e3:.1f} us/step")
+    ms = float(np.median(times))
+    value = wl.B * wl.D * wl.L / (ms * 1e-3)
+    fwd_bytes = alg_bytes_forward(wl)
+    hbm_frac = fwd_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)
+
+    # per-kernel durations, HIP events on the library's stream around every launch
+    fam_ms = {}
+    nt = max(3, min(args.steps, 10))
+    for _ in range(nt):
+        r = plan.forward_timed(u, w, spec, bias, y, ws)
+        for k, v in r.items():
+            fam_ms[k] = fam_ms.get(k, 0.0) + v / nt
+    log(f"[bench] per-forward kernel-family ms: {json.dumps({k: round(v, 4) for k, v in fam_ms.items()})}")
+    if plan.path == "lds":
+        dom, dom_ms, dom_bytes = "k_lds_forward", fam_ms["lds"], fwd_bytes
+        launches = 1
+    else:
+        fam = max(("pass_a", "pass_b", "pass_c"), key=lambda k: fam_ms[k])
+        dom = {"pass_a": "k_fs_colfwd", "pass_b": "k_fs_row", "pass_c": "k_fs_colinv"}[fam]
+        dom_ms, dom_bytes = fam_ms[fam], alg_bytes_pass(wl, fam)
+        rows = wl.B * wl.D
+        chunk = max(1, min(rows, (ws_bytes // (8 * wl.L)) if ws_bytes else rows))
+        launches = math.ceil(rows / chunk) * (1 if fam == "pass_a" else wl.order - 1)
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "launches_per_step": launches, "kernel_ms_per_step": round(dom_ms, 5)}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "channel-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "bf16-io/f32",
+        "data": f"synthetic seeded ({wl.kind} activations, exponentially decaying random filters)",
+        "config": {"workload": wl.name, "B": wl.B, "D": wl.D, "L": wl.L, "order": wl.order,
+                   "io_dtype": wl.dtype, "path": plan.path},
+        "hbm_frac_forward": round(hbm_frac, 4),
+        "alg_bytes_per_step": fwd_bytes,
+        "spectrum_ms": round(spectrum_ms, 4),
+        "roofline": roofline,
+    }
+
+    if args.check:
+        import oracle
+
+        rows = synth.sample_rows(wl, 8)
+        ref = oracle.forward(x.u_proj, x.short_w, x.h, x.bias, wl.order, rows=rows)
+        got = y.float().cpu().numpy().reshape(-1, wl.L)[rows]
+        out["check_rel_l2"] = oracle.rel_l2(got, ref)
+        log(f"[bench] oracle check on {len(rows)} rows: rel_l2 {out['check_rel_l2']:.3e}")
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    plan.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+"""Thin ctypes binding over libhyena's C ABI (include/hyena.h).
+
+Only argument marshalling happens here: shapes and dtypes are checked, torch
+tensors supply device pointers and the current HIP stream, and every step of
+the hot path runs in the library's HIP kernels. There is no fallback: if
+libhyena.so is missing or no GPU is present, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhyena.so")
+
+HYENA_F32, HYENA_BF16 = 0, 1
+PATH_AUTO, PATH_LDS, PATH_FOURSTEP = 0, 1, 2
+STATUS = {0: "HYENA_OK", 1: "HYENA_ERR_INVALID_ARG", 2: "HYENA_ERR_UNSUPPORTED",
+          3: "HYENA_ERR_WORKSPACE", 4: "HYENA_ERR_DEVICE"}
+_PATHS = {"auto": PATH_AUTO, "lds": PATH_LDS, "fourstep": PATH_FOURSTEP}
+_DTYPES = {"f32": HYENA_F32, "bf16": HYENA_BF16}
+
+# every symbol include/hyena.h declares
+EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_destroy", "hyena_plan_path",
+           "hyena_spectrum_bytes", "hyena_workspace_bytes", "hyena_filter_spectrum", "hyena_forward",
+           "hyena_forward_timed", "hyena_status_string")
+
+
+class HyenaError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        self.status = status
+        super().__init__(f"{call} failed: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libhyena.so and declare its signatures (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libhyena is not built ({p} is missing); run __graft_entry__.build()")
+    lib = ctypes.CDLL(p)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    ci = ctypes.c_int
+    lib.hyena_plan_create.argtypes = [ctypes.POINTER(vp), i64, i64, ci, ci]
+    lib.hyena_plan_create.restype = ci
+    lib.hyena_plan_create_path.argtypes = [ctypes.POINTER(vp), i64, i64, ci, ci, ci]
+    lib.hyena_plan_create_path.restype = ci
+    lib.hyena_plan_destroy.argtypes = [vp]
+    lib.hyena_plan_destroy.restype = ci
+    lib.hyena_plan_path.argtypes = [vp]
+    lib.hyena_plan_path.restype = ci
+    lib.hyena_spectrum_bytes.argtypes = [vp]
+    lib.hyena_spectrum_bytes.restype = sz
+    lib.hyena_workspace_bytes.argtypes = [vp, i64]
+    lib.hyena_workspace_bytes.restype = sz
+    lib.hyena_filter_spectrum.argtypes = [vp, vp, vp, vp]
+    lib.hyena_filter_spectrum.restype = ci
+    lib.hyena_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hyena_forward.restype = ci
+    lib.hyena_forward_timed.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
+    lib.hyena_forward_timed.restype = ci
+    lib.hyena_status_string.argtypes = [ci]
+    lib.hyena_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(call: str, st: int) -> None:
+    if st != 0:
+        raise HyenaError(call, st)
+
+
+def _stream_handle(torch, device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+class Plan:
+    """A libhyena plan: fixed L, D, order and I/O dtype ("f32" or "bf16")."""
+
+    def __init__(self, L: int, D: int, order: int, dtype: str = "f32", path: str = "auto"):
+        import torch  # device memory and streams only
+
+        self._torch = torch
+        self.lib = load_library()
+        self.L, self.D, self.order, self.dtype = int(L), int(D), int(order), dtype
+        if dtype not in _DTYPES or path not in _PATHS:
+            raise ValueError(f"dtype must be one of {list(_DTYPES)}, path one of {list(_PATHS)}")
+        self.device = torch.device("cuda", torch.cuda.current_device())
+        h = ctypes.c_void_p()
+        _check("hyena_plan_create_path",
+               self.lib.hyena_plan_create_path(ctypes.byref(h), self.L, self.D, self.order, _DTYPES[dtype],
+                                               _PATHS[path]))
+        self.handle = h
+        self.path = {PATH_LDS: "lds", PATH_FOURSTEP: "fourstep"}[self.lib.hyena_plan_path(h)]
+
+    @property
+    def io_dtype(self):
+        return self._torch.bfloat16 if self.dtype == "bf16" else self._torch.float32
+
+    def spectrum_bytes(self) -> int:
+        return int(self.lib.hyena_spectrum_bytes(self.handle))
+
+    def workspace_bytes(self, B: int) -> int:
+        return int(self.lib.hyena_workspace_bytes(self.handle, int(B)))
+
+    def _need(self, t, name, shape, dtype):
+        torch = self._torch
+        if not isinstance(t, torch.Tensor) or t.device != self.device:
+            raise ValueError(f"{name} must be a tensor on {self.device}")
+        if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}, "
+                             f"got {t.dtype} {tuple(t.shape)}")
+
+    def spectrum(self, h, out=None):
+        """hyena_filter_spectrum: h [N-1, D, L] fp32 -> opaque uint8 device buffer."""
+        torch = self._torch
+        N, D, L = self.order, self.D, self.L
+        self._need(h, "h", (N - 1, D, L), torch.float32)
+        if out is None:
+            out = torch.empty(self.spectrum_bytes(), dtype=torch.uint8, device=self.device)
+        elif out.numel() * out.element_size() < self.spectrum_bytes():
+            raise ValueError("spectrum buffer too small")
+        _check("hyena_filter_spectrum",
+               self.lib.hyena_filter_spectrum(self.handle, h.data_ptr(), out.data_ptr(),
+                                              _stream_handle(torch, self.device)))
+        return out
+
+    def forward(self, u_proj, short_w, spec, bias, y=None, workspace=None):
+        """hyena_forward: u_proj [B,(N+1)D,L], short_w [(N+1)D,3], bias [N-1,D] -> y [B,D,L]."""
+        torch = self._torch
+        N, D, L = self.order, self.D, self.L
+        if u_proj.dim() != 3:
+            raise ValueError("u_proj must be [B, (N+1)*D, L]")
+        B = int(u_proj.shape[0])
+        self._need(u_proj, "u_proj", (B, (N + 1) * D, L), self.io_dtype)
+        self._need(short_w, "short_w", ((N + 1) * D, 3), torch.float32)
+        self._need(bias, "bias", (N - 1, D), torch.float32)
+        if spec.device != self.device or spec.numel() * spec.element_size() < self.spectrum_bytes():
+            raise ValueError("spec must come from Plan.spectrum of an equal plan")
+        if y is None:
+            y = torch.empty((B, D, L), dtype=self.io_dtype, device=self.device)
+        self._need(y, "y", (B, D, L), self.io_dtype)
+        ws_ptr, ws_bytes = 0, 0
+        need = self.workspace_bytes(B)
+        if need:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        _check("hyena_forward",
+               self.lib.hyena_forward(self.handle, B, u_proj.data_ptr(), short_w.data_ptr(), spec.data_ptr(),
+                                      bias.data_ptr(), y.data_ptr(), ws_ptr or None, ws_bytes,
+                                      _stream_handle(torch, self.device)))
+        return y
+
+    def forward_timed(self, u_proj, short_w, spec, bias, y, workspace=None):
+        """hyena_forward_timed: runs one forward (synchronously) and returns the
+        per-kernel-family milliseconds {"lds", "pass_a", "pass_b", "pass_c", "total"}."""
+        torch = self._torch
+        B = int(u_proj.shape[0])
+        ws_ptr, ws_bytes = 0, 0
+        if self.workspace_bytes(B):
+            if workspace is None:
+                workspace = torch.empty(self.workspace_bytes(B), dtype=torch.uint8, device=self.device)
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        ms = (ctypes.c_float * 5)()
+        _check("hyena_forward_timed",
+               self.lib.hyena_forward_timed(self.handle, B, u_proj.data_ptr(), short_w.data_ptr(),
+                                            spec.data_ptr(), bias.data_ptr(), y.data_ptr(), ws_ptr or None,
+                                            ws_bytes, _stream_handle(torch, self.device), ms))
+        return dict(zip(("lds", "pass_a", "pass_b", "pass_c", "total"), [float(v) for v in ms]))
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            self.lib.hyena_plan_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

@@ -1,0 +1,331 @@
+// C-ABI layer of libhyena: plans, argument checks, twiddle tables, dispatch.
+// See include/hyena.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/hyena.h"
+#include "fft_core.hpp"
+#include "kernels.hpp"
+
+struct hyena_plan_s {
+    int64_t L = 0, D = 0;
+    int order = 0;
+    int logL = 0;
+    hyena_dtype_t dtype = HYENA_F32;
+    hyena_path_t path = HYENA_PATH_AUTO;
+    int device = -1;
+    float2* dtab = nullptr;  // all twiddle tables, one device allocation
+    // LDS path
+    const float2* tw = nullptr;
+    const float2* wpair = nullptr;
+    // four-step path
+    int log1 = 0, log2 = 0;
+    hy::FsTables fs{};
+};
+
+namespace {
+
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr int64_t kMaxLog = 20;
+constexpr size_t kChunkTargetBytes = 128u << 20;  // in-flight four-step intermediates per launch
+constexpr int64_t kMaxChunkRows = 65536;
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2_64(int64_t x) {
+    int l = 0;
+    while ((int64_t(1) << l) < x) ++l;
+    return l;
+}
+
+// exp(-2 pi i num / den) computed in fp64 after an exact integer reduction.
+float2 wfwd(int64_t num, int64_t den) {
+    int64_t r = num % den;
+    if (r < 0) r += den;
+    const double a = -kTwoPi * (double)r / (double)den;
+    return make_float2((float)cos(a), (float)sin(a));
+}
+
+// Stockham per-pass tables for a length-n transform, in the order the device
+// schedule reads them: pass p (radix R, NS = 16^p) holds W_{NS*R}^{r*k} at
+// [(r-1)*NS + k], r = 1..R-1, k = 0..NS-1.
+void append_stockham(std::vector<float2>& out, int logn) {
+    const int full = logn / 4, rem = logn % 4;
+    const int npass = full + (rem ? 1 : 0);
+    int64_t ns = 1;
+    for (int p = 0; p < npass; ++p) {
+        const int R = p < full ? 16 : (1 << rem);
+        for (int r = 1; r < R; ++r)
+            for (int64_t k = 0; k < ns; ++k) out.push_back(wfwd((int64_t)r * k, ns * R));
+        ns *= R;
+    }
+}
+
+size_t stockham_size(int logn) {
+    std::vector<float2> tmp;
+    append_stockham(tmp, logn);
+    return tmp.size();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+hyena_status_t check_device(const hyena_plan_t plan) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return HYENA_ERR_DEVICE;
+    return dev == plan->device ? HYENA_OK : HYENA_ERR_DEVICE;
+}
+
+int64_t chunk_rows(const hyena_plan_t plan, int64_t rows, size_t ws_bytes) {
+    const size_t per_row = (size_t)plan->L * sizeof(float2);
+    int64_t n = (int64_t)(ws_bytes / per_row);
+    if (n > rows) n = rows;
+    if (n > kMaxChunkRows) n = kMaxChunkRows;  // keeps every grid dimension far below 2^31
+    return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hyena_status_string(hyena_status_t s) {
+    switch (s) {
+        case HYENA_OK: return "ok";
+        case HYENA_ERR_INVALID_ARG: return "invalid argument";
+        case HYENA_ERR_UNSUPPORTED: return "unsupported size or option";
+        case HYENA_ERR_WORKSPACE: return "workspace missing or too small";
+        case HYENA_ERR_DEVICE: return "HIP device error";
+        default: return "unknown status";
+    }
+}
+
+hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype,
+                                      hyena_path_t path) {
+    if (!out) return HYENA_ERR_INVALID_ARG;
+    if (D < 1 || L < 1 || order < 2) return HYENA_ERR_INVALID_ARG;
+    if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
+    if (path != HYENA_PATH_AUTO && path != HYENA_PATH_LDS && path != HYENA_PATH_FOURSTEP)
+        return HYENA_ERR_INVALID_ARG;
+    if (!is_pow2(L) || L < 16 || L > (int64_t(1) << kMaxLog) || order > 8) return HYENA_ERR_UNSUPPORTED;
+    if (D > (int64_t(1) << 24)) return HYENA_ERR_UNSUPPORTED;
+    const int logL = ilog2_64(L);
+    hyena_path_t p = path;
+    if (p == HYENA_PATH_AUTO) p = logL <= hy::kLdsMaxLog ? HYENA_PATH_LDS : HYENA_PATH_FOURSTEP;
+    if (p == HYENA_PATH_LDS && logL > hy::kLdsMaxLog) return HYENA_ERR_UNSUPPORTED;
+    if (p == HYENA_PATH_FOURSTEP && logL < hy::kFsMinLog) return HYENA_ERR_UNSUPPORTED;
+
+    // host tables (fp64 -> fp32)
+    std::vector<float2> tab;
+    size_t o_tw = 0, o_wpair = 0, o_tw1 = 0, o_tw2 = 0, o_lo = 0, o_hi = 0, o_pa = 0, o_pb = 0;
+    int log1 = 0, log2 = 0, slo = 0;
+    if (p == HYENA_PATH_LDS) {
+        o_tw = tab.size();
+        append_stockham(tab, logL);
+        o_wpair = tab.size();
+        for (int64_t k = 0; k <= L / 2; ++k) tab.push_back(wfwd(k, 2 * L));
+    } else {
+        hy::fs_split(logL, &log1, &log2);
+        const int64_t L1 = int64_t(1) << log1, L2 = int64_t(1) << log2;
+        o_tw1 = tab.size();
+        append_stockham(tab, log1);
+        o_tw2 = tab.size();
+        append_stockham(tab, log2);
+        slo = (logL + 1) / 2;
+        o_lo = tab.size();
+        for (int64_t j = 0; j < (int64_t(1) << slo); ++j) tab.push_back(wfwd(j, L));
+        o_hi = tab.size();
+        for (int64_t j = 0; j < (L >> slo); ++j) tab.push_back(wfwd(j << slo, L));
+        o_pa = tab.size();
+        for (int64_t k1 = 0; k1 < L1; ++k1) tab.push_back(wfwd(k1, 2 * L));
+        o_pb = tab.size();
+        for (int64_t k2 = 0; k2 < L2; ++k2) tab.push_back(wfwd(L1 * k2, 2 * L));
+    }
+
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return HYENA_ERR_DEVICE;
+    float2* dtab = nullptr;
+    if (hipMalloc((void**)&dtab, tab.size() * sizeof(float2)) != hipSuccess) return HYENA_ERR_DEVICE;
+    if (hipMemcpy(dtab, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(dtab);
+        return HYENA_ERR_DEVICE;
+    }
+    hyena_plan_s* plan = new (std::nothrow) hyena_plan_s();
+    if (!plan) {
+        (void)hipFree(dtab);
+        return HYENA_ERR_DEVICE;
+    }
+    plan->L = L;
+    plan->D = D;
+    plan->order = order;
+    plan->logL = logL;
+    plan->dtype = dtype;
+    plan->path = p;
+    plan->device = dev;
+    plan->dtab = dtab;
+    if (p == HYENA_PATH_LDS) {
+        plan->tw = dtab + o_tw;
+        plan->wpair = dtab + o_wpair;
+    } else {
+        plan->log1 = log1;
+        plan->log2 = log2;
+        plan->fs.tw1 = dtab + o_tw1;
+        plan->fs.tw2 = dtab + o_tw2;
+        plan->fs.otlo = dtab + o_lo;
+        plan->fs.othi = dtab + o_hi;
+        plan->fs.pa = dtab + o_pa;
+        plan->fs.pb = dtab + o_pb;
+        plan->fs.slo = slo;
+    }
+    *out = plan;
+    return HYENA_OK;
+}
+
+hyena_status_t hyena_plan_create(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype) {
+    return hyena_plan_create_path(out, L, D, order, dtype, HYENA_PATH_AUTO);
+}
+
+hyena_status_t hyena_plan_destroy(hyena_plan_t plan) {
+    if (!plan) return HYENA_OK;
+    hyena_status_t st = HYENA_OK;
+    if (plan->dtab && hipFree(plan->dtab) != hipSuccess) st = HYENA_ERR_DEVICE;
+    delete plan;
+    return st;
+}
+
+hyena_path_t hyena_plan_path(hyena_plan_t plan) { return plan ? plan->path : HYENA_PATH_AUTO; }
+
+size_t hyena_spectrum_bytes(hyena_plan_t plan) {
+    if (!plan) return 0;
+    return (size_t)(plan->order - 1) * (size_t)plan->D * (size_t)plan->L * sizeof(float2);
+}
+
+size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B) {
+    if (!plan || B < 1) return 0;
+    if (plan->path == HYENA_PATH_LDS) return 0;
+    const size_t per_row = (size_t)plan->L * sizeof(float2);
+    int64_t rows = B * plan->D;
+    int64_t want = (int64_t)(kChunkTargetBytes / per_row);
+    if (want < 1) want = 1;
+    if (want > rows) want = rows;
+    return (size_t)want * per_row;
+}
+
+hyena_status_t hyena_filter_spectrum(hyena_plan_t plan, const float* h, void* spec, hipStream_t stream) {
+    if (!plan || !h || !spec) return HYENA_ERR_INVALID_ARG;
+    if (!aligned16(h) || !aligned16(spec)) return HYENA_ERR_INVALID_ARG;
+    if (check_device(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
+    const int64_t rows = (int64_t)(plan->order - 1) * plan->D;
+    hipError_t e;
+    if (plan->path == HYENA_PATH_LDS)
+        e = hy::launch_lds_spectrum(plan->logL, h, (float2*)spec, rows, plan->tw, plan->wpair, stream);
+    else
+        e = hy::launch_fs_spectrum(plan->logL, h, (float2*)spec, rows, plan->fs, stream);
+    return e == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared body of hyena_forward and hyena_forward_timed. With `ms`, HIP events are
+// recorded around every launch on `stream`, the call waits for them, and the
+// elapsed milliseconds are summed per kernel family (see hyena_forward_timed).
+hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                            const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream, float* ms) {
+    if (!plan || B < 1 || !u_proj || !short_w || !spec || !bias || !y) return HYENA_ERR_INVALID_ARG;
+    if (!aligned16(u_proj) || !aligned16(spec) || !aligned16(y) || !aligned16(short_w) || !aligned16(bias))
+        return HYENA_ERR_INVALID_ARG;
+    // grid sizes are 32-bit: B*D rows times at most L/16 column blocks
+    if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 26)) return HYENA_ERR_INVALID_ARG;
+    const bool bf16 = plan->dtype == HYENA_BF16;
+    const int64_t rows = B * plan->D;
+    int64_t chunk = 0;
+    if (plan->path == HYENA_PATH_FOURSTEP) {
+        if (!workspace || !aligned16(workspace)) return HYENA_ERR_WORKSPACE;
+        chunk = chunk_rows(plan, rows, workspace_bytes);
+        if (chunk < 1) return HYENA_ERR_WORKSPACE;
+    }
+    if (check_device(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
+
+    const int per_chunk = 2 * plan->order - 1;  // launches per chunk on the four-step path
+    const int64_t nchunks = plan->path == HYENA_PATH_FOURSTEP ? (rows + chunk - 1) / chunk : 1;
+    std::vector<hipEvent_t> ev;
+    if (ms) {
+        for (int i = 0; i < 5; ++i) ms[i] = 0.f;
+        const int64_t n = plan->path == HYENA_PATH_FOURSTEP ? nchunks * (per_chunk + 1) : 2;
+        if (n > 4096) return HYENA_ERR_INVALID_ARG;  // timing is for bounded chunk counts
+        ev.resize((size_t)n, nullptr);
+        for (auto& e : ev)
+            if (hipEventCreate(&e) != hipSuccess) {
+                for (auto& f : ev)
+                    if (f) (void)hipEventDestroy(f);
+                return HYENA_ERR_DEVICE;
+            }
+    }
+    hyena_status_t st = HYENA_OK;
+    if (plan->path == HYENA_PATH_LDS) {
+        if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
+        hy::LdsArgs a{u_proj, short_w, (const float2*)spec, bias, y, plan->tw, plan->wpair,
+                      (int)B, (int)plan->D, plan->order, bf16};
+        if (ms) (void)hipEventRecord(ev[0], stream);
+        if (hy::launch_lds_forward(plan->logL, a, stream) != hipSuccess) st = HYENA_ERR_DEVICE;
+        if (ms) (void)hipEventRecord(ev[1], stream);
+    } else {
+        hy::FsArgs a{u_proj, short_w, (const float2*)spec, bias, y, (float2*)workspace, plan->fs,
+                     (int)plan->D, plan->order, bf16};
+        int64_t ci = 0;
+        for (int64_t r0 = 0; r0 < rows && st == HYENA_OK; r0 += chunk, ++ci) {
+            const int64_t n = (rows - r0) < chunk ? (rows - r0) : chunk;
+            hipEvent_t* marks = ms ? ev.data() + ci * (per_chunk + 1) : nullptr;
+            if (hy::launch_fs_forward_chunk(plan->logL, a, r0, n, stream, marks) != hipSuccess)
+                st = HYENA_ERR_DEVICE;
+        }
+    }
+    if (ms) {
+        if (st == HYENA_OK && hipEventSynchronize(ev.back()) != hipSuccess) st = HYENA_ERR_DEVICE;
+        if (st == HYENA_OK) {
+            float t = 0.f;
+            if (plan->path == HYENA_PATH_LDS) {
+                (void)hipEventElapsedTime(&t, ev[0], ev[1]);
+                ms[0] = t;
+            } else {
+                for (int64_t c = 0; c < nchunks; ++c) {
+                    hipEvent_t* m = ev.data() + c * (per_chunk + 1);
+                    for (int i = 0; i < per_chunk; ++i) {
+                        (void)hipEventElapsedTime(&t, m[i], m[i + 1]);
+                        // launch 0 is pass A; then pass B / pass C alternate
+                        const int fam = i == 0 ? 1 : (i % 2 == 1 ? 2 : 3);
+                        ms[fam] += t;
+                    }
+                }
+            }
+            (void)hipEventElapsedTime(&t, ev.front(), ev.back());
+            ms[4] = t;
+        }
+        for (auto& e : ev) (void)hipEventDestroy(e);
+    }
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                             const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    return forward_impl(plan, B, u_proj, short_w, spec, bias, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                                   const void* spec, const float* bias, void* y, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream, float* ms) {
+    if (!ms) return HYENA_ERR_INVALID_ARG;
+    return forward_impl(plan, B, u_proj, short_w, spec, bias, y, workspace, workspace_bytes, stream, ms);
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hy {
+
+// LDS path: one workgroup per (b, d) row, L/16 threads, the whole packed
+// transform (L complex values plus one pad slot per 16) in LDS.
+template <int LOGL>
+struct LdsCfg {
+    static constexpr int L = 1 << LOGL;
+    static constexpr int THREADS = L / 16;
+};
+constexpr int kLdsMaxLog = 14;  // L = 16384: 139,264 bytes of LDS
+
+// Four-step path geometry for L = L1 * L2.
+template <int LOG1, int LOG2>
+struct FsCfg {
+    static constexpr int L1 = 1 << LOG1;
+    static constexpr int L2 = 1 << LOG2;
+    static constexpr int T1 = L1 / 16;                 // threads per column transform
+    static constexpr int T2 = L2 / 16;                 // threads per row transform
+    static constexpr int CB = 16;                      // columns per pass A/C workgroup
+    static constexpr int CP = CB + 1;                  // LDS pitch of the column tile
+    static constexpr int COL_THREADS = CB * T1;
+    static constexpr int U0 = 256 / (2 * T2);
+    static constexpr int UNITS = U0 < 1 ? 1 : (U0 > L1 / 2 ? L1 / 2 : U0);  // row pairs per pass B workgroup
+    static constexpr int ROW_THREADS = UNITS * 2 * T2;
+    static constexpr int RP = L2 + L2 / 16;            // padded LDS row length
+};
+constexpr int kFsMinLog = 8;
+constexpr int kFsMaxLog = 20;
+
+struct LdsArgs {
+    const void* u;
+    const float* w3;
+    const float2* spec;
+    const float* bias;
+    void* y;
+    const float2* tw;     // Stockham twiddles for length L
+    const float2* wpair;  // W_{2L}^k, k = 0..L/2
+    int B, D, N;
+    bool bf16;
+};
+
+struct FsTables {
+    const float2* tw1;   // Stockham twiddles for length L1
+    const float2* tw2;   // Stockham twiddles for length L2
+    const float2* otlo;  // W_L^j, j < 2^slo
+    const float2* othi;  // W_L^(j * 2^slo), j < L / 2^slo
+    const float2* pa;    // W_{2L}^k1, k1 < L1
+    const float2* pb;    // W_{2L}^(L1*k2), k2 < L2
+    int slo;
+};
+
+struct FsArgs {
+    const void* u;
+    const float* w3;
+    const float2* spec;
+    const float* bias;
+    void* y;
+    float2* ws;  // nrows * L complex values
+    FsTables tb;
+    int D, N;
+    bool bf16;
+};
+
+hipError_t launch_lds_forward(int logL, const LdsArgs& a, hipStream_t st);
+hipError_t launch_lds_spectrum(int logL, const float* h, float2* spec, int64_t rows, const float2* tw,
+                               const float2* wpair, hipStream_t st);
+hipError_t launch_fs_forward_chunk(int logL, const FsArgs& a, int64_t row0, int64_t nrows, hipStream_t st,
+                                   hipEvent_t* marks = nullptr);
+hipError_t launch_fs_spectrum(int logL, const float* h, float2* spec, int64_t rows, const FsTables& tb,
+                              hipStream_t st);
+void fs_split(int logL, int* log1, int* log2);
+int fs_row_units(int logL);
+
+}  // namespace hy

@@ -1,0 +1,149 @@
+/*
+ * libhyena — the Hyena operator forward hot path on AMD MI355X (gfx950).
+ *
+ * The operator (HyenaDNA walkthrough, section 2.1, HyenaOperator.forward):
+ *   uc  = ShortConv(u_proj)[..., :L]    depthwise Conv1d, 3 taps, padding 2
+ *   x_0 .. x_{N-1}, v = split(uc, D)    gates first, the value v is the last chunk
+ *   for o in 0 .. N-2:                  gates taken from reversed(x[1:])
+ *       v = v * x_{N-1-o}
+ *       v = conv(v, h[o]) + bias[o] * v (HyenaFilter.forward -> fftconv, section 2.2)
+ *   y = v * x_0
+ * where conv is the causal per-channel long convolution
+ *   conv(v, h)[t] = sum_{s <= t} h[s] v[t - s],
+ * evaluated by FFT on the sequence zero-padded to 2L (the HyenaND summary's
+ * boundary handling; the Hyena Hierarchy concept page, section 3.2, FFT
+ * acceleration). The in/out projections and the b l d <-> b d l rearranges of
+ * the module are outside this library; dropout is the identity; the short
+ * Conv1d bias is taken as zero.
+ *
+ * Conventions for every call:
+ *  - Device pointers are plain device memory on the device that was current when
+ *    the plan was created; that device must be current for every later call.
+ *    The caller owns every buffer; libhyena never frees caller memory.
+ *  - Tensors are dense and row-major (C order) with the shapes given below and
+ *    16-byte aligned base pointers. Outputs must not alias inputs.
+ *  - Calls that take a stream enqueue work on it and return without
+ *    synchronising; results are ready when the stream reaches that point.
+ *  - Errors are reported by return value; nothing throws across this ABI.
+ *    Argument errors are detected on the host before any HIP call is made.
+ *  - A plan is immutable after creation and may be shared read-only between
+ *    host threads; concurrent forwards need distinct workspaces and outputs.
+ */
+#ifndef LIBHYENA_HYENA_H
+#define LIBHYENA_HYENA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct hyena_plan_s* hyena_plan_t; /* opaque */
+
+/* Element type of u_proj and y. All parameters (short_w, h, bias) and every
+ * intermediate are fp32; bf16 outputs are rounded to nearest even. */
+typedef enum { HYENA_F32 = 0, HYENA_BF16 = 1 } hyena_dtype_t;
+
+typedef enum {
+    HYENA_OK = 0,
+    HYENA_ERR_INVALID_ARG = 1, /* NULL pointer, bad size or shape, misaligned pointer */
+    HYENA_ERR_UNSUPPORTED = 2, /* valid request outside what this build implements */
+    HYENA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    HYENA_ERR_DEVICE = 4       /* no usable HIP device, allocation or launch failure */
+} hyena_status_t;
+
+/* Which kernel family runs a plan. AUTO keeps the whole transform in LDS when
+ * L <= 16384 and uses the four-step multi-pass transform above that. */
+typedef enum { HYENA_PATH_AUTO = 0, HYENA_PATH_LDS = 1, HYENA_PATH_FOURSTEP = 2 } hyena_path_t;
+
+/* Create a plan for sequence length L, operator width D and recurrence order
+ * N = `order` (N-1 long filters, N gates). Requirements: L a power of two in
+ * [16, 2^20], D >= 1, 2 <= order <= 8, dtype one of hyena_dtype_t.
+ * Builds the twiddle tables on the host in fp64 and uploads them to the current
+ * device (the plan owns that memory; hyena_plan_destroy releases it).
+ * Returns HYENA_ERR_INVALID_ARG / HYENA_ERR_UNSUPPORTED for bad arguments,
+ * HYENA_ERR_DEVICE when no HIP device is usable. *out is set only on success. */
+hyena_status_t hyena_plan_create(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype);
+
+/* As hyena_plan_create, with an explicit kernel family. HYENA_PATH_LDS needs
+ * L <= 16384; HYENA_PATH_FOURSTEP needs L >= 256 (HYENA_ERR_UNSUPPORTED
+ * otherwise). The spectrum layout depends on the path, so a spectrum must be
+ * made by a plan of the same path as the plan that consumes it. */
+hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype,
+                                      hyena_path_t path);
+
+/* Release a plan and its device tables. NULL is a no-op returning HYENA_OK.
+ * The caller must ensure no enqueued work still uses the plan. */
+hyena_status_t hyena_plan_destroy(hyena_plan_t plan);
+
+/* The path a plan resolved to (HYENA_PATH_LDS or HYENA_PATH_FOURSTEP), or
+ * HYENA_PATH_AUTO for a NULL plan. */
+hyena_path_t hyena_plan_path(hyena_plan_t plan);
+
+/* Bytes of the opaque spectrum buffer: (N-1) * D * L complex fp32 values, i.e.
+ * 8 * (N-1) * D * L. Returns 0 for a NULL plan. */
+size_t hyena_spectrum_bytes(hyena_plan_t plan);
+
+/* Recommended workspace for a forward over batch B: 0 on the LDS path; on the
+ * four-step path 8*L bytes per (b, d) row held in flight, for a chunk of rows
+ * chosen to stay cache-resident. Any workspace of at least 8*L bytes (one row)
+ * is accepted by hyena_forward; a larger one lets more rows run per launch.
+ * Returns 0 for a NULL plan or B < 1. */
+size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B);
+
+/* The real FFT of the long filters, once per plan (the filter spectrum of the
+ * causal convolution; HyenaDNA walkthrough section 2.2, fftconv).
+ *   h    [N-1][D][L] fp32, device: filter o of channel d at h[(o*D + d)*L + t]
+ *   spec device buffer of hyena_spectrum_bytes(plan) bytes, written in the
+ *        plan's private layout (the 2L-point spectrum bins 0..L of each
+ *        zero-padded filter, scaled by 2^-(log2 L + 2)).
+ * Enqueued on `stream`. HYENA_ERR_INVALID_ARG for NULL pointers or misaligned
+ * buffers; HYENA_ERR_DEVICE if the launch fails or the plan's device is not
+ * current. */
+hyena_status_t hyena_filter_spectrum(hyena_plan_t plan, const float* h, void* spec, hipStream_t stream);
+
+/* The forward hot path for a batch of B sequences.
+ *   u_proj  [B][(N+1)*D][L] of the plan dtype, device: channel i*D + d is gate
+ *           x_i for i < N and channel N*D + d is the value v (the in-projected,
+ *           rearranged activation)
+ *   short_w [(N+1)*D][3] fp32, device: PyTorch Conv1d taps; uc[t] =
+ *           w[0]*u[t-2] + w[1]*u[t-1] + w[2]*u[t] with u[t<0] = 0
+ *   spec    from hyena_filter_spectrum of a plan with the same L, D, order, path
+ *   bias    [N-1][D] fp32, device: the bias skip term of step o is bias[o][d]*v
+ *   y       [B][D][L] of the plan dtype, device (output, before the b d l ->
+ *           b l d rearrange)
+ *   workspace / workspace_bytes: device scratch, at least 8*L bytes on the
+ *           four-step path (see hyena_workspace_bytes); ignored (may be NULL)
+ *           on the LDS path. Contents on entry are irrelevant.
+ * Enqueued on `stream`; no host synchronisation. Errors: HYENA_ERR_INVALID_ARG
+ * (NULL/misaligned pointers, B < 1 or B*D*L too large), HYENA_ERR_WORKSPACE,
+ * HYENA_ERR_DEVICE (launch failure, wrong current device). */
+hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                             const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* hyena_forward with per-kernel timing, for measurement. HIP events are
+ * recorded on `stream` around every kernel launch of this forward; the call
+ * then waits for the last event (so it is synchronous), and writes elapsed
+ * milliseconds summed per kernel family into ms[5]:
+ *   ms[0] fused LDS-path kernel, ms[1] four-step pass A (column FFTs of the
+ *   gated input), ms[2] pass B (row FFTs, spectrum multiply, inverse rows),
+ *   ms[3] pass C (inverse columns and gate; for order > 2 it also carries the
+ *   next step's pass A), ms[4] first event to last event.
+ * Same arguments, results and errors as hyena_forward; HYENA_ERR_INVALID_ARG
+ * also for ms == NULL or more than 4096 events. */
+hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                                   const void* spec, const float* bias, void* y, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream, float* ms);
+
+/* Static, NUL-terminated description of a status code. */
+const char* hyena_status_string(hyena_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBHYENA_HYENA_H */

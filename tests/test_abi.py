@@ -1,0 +1,105 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before touching a device. No compute
+call is made here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from fft_long_convolution_libhyena_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hyena.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from fft_long_convolution_libhyena_amd import build
+
+        build.build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hyena_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (hyena_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, f"{name} is declared in hyena.h but not exported"
+        getattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        s = lib.hyena_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.hyena_status_string(99) == b"unknown status"
+
+
+def test_null_plan_queries(lib):
+    assert lib.hyena_plan_destroy(None) == 0
+    assert lib.hyena_spectrum_bytes(None) == 0
+    assert lib.hyena_workspace_bytes(None, 4) == 0
+    assert lib.hyena_plan_path(None) == binding.PATH_AUTO
+
+
+def _create(lib, L, D, order, dtype=0, path=0):
+    h = ctypes.c_void_p()
+    st = lib.hyena_plan_create_path(ctypes.byref(h), L, D, order, dtype, path)
+    if st == 0:
+        lib.hyena_plan_destroy(h)
+    return st, h
+
+
+@pytest.mark.parametrize("L,D,order,dtype,path,want", [
+    (1024, 0, 2, 0, 0, 1),        # D < 1
+    (1024, 4, 1, 0, 0, 1),        # order < 2
+    (0, 4, 2, 0, 0, 1),           # L < 1
+    (1024, 4, 2, 7, 0, 1),        # bad dtype
+    (1024, 4, 2, 0, 9, 1),        # bad path
+    (1000, 4, 2, 0, 0, 2),        # L not a power of two
+    (8, 4, 2, 0, 0, 2),           # L below 16
+    (1 << 21, 4, 2, 0, 0, 2),     # L above 2^20
+    (1024, 4, 9, 0, 0, 2),        # order above 8
+    (1 << 15, 4, 2, 0, 1, 2),     # LDS path beyond 16384
+    (128, 4, 2, 0, 2, 2),         # four-step below 256
+])
+def test_plan_argument_errors_before_any_device_call(lib, L, D, order, dtype, path, want):
+    st, h = _create(lib, L, D, order, dtype, path)
+    assert st == want
+    assert h.value is None  # *out untouched on failure
+
+
+def test_plan_create_null_out(lib):
+    assert lib.hyena_plan_create(None, 1024, 4, 2, 0) == 1
+
+
+def test_forward_and_spectrum_reject_null_plan(lib):
+    assert lib.hyena_forward(None, 1, 16, 16, 16, 16, 16, None, 0, None) == 1
+    assert lib.hyena_filter_spectrum(None, 16, 16, None) == 1
+
+
+def test_valid_plan_without_gpu_reports_device_error(lib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, _ = _create(lib, 1024, 4, 2)
+    assert st == 4  # HYENA_ERR_DEVICE
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        binding.load_library(str(tmp_path / "missing.so"))
