@@ -14,8 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhyena.so")
-SOURCES = ["hyena_api.hip", "kernels.hip"]
-HEADERS = ["fft_core.hpp", "kernels.hpp"]
+SOURCES = ["hyena_api.hip", "fourstep.hip", "lds_path_a.hip", "lds_path_b.hip", "lds_path_c.hip", "lds_path_d.hip"]
+HEADERS = ["fft_core.hpp", "kernels.hpp", "pair.hpp", "lds_path.hpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -32,23 +32,25 @@ def hipcc() -> str:
     return path
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source to an object in parallel, then link libhyena.so."""
-    objdir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, jobs: int = 4, out: str = LIB, defines=()) -> str:
+    """Compile every source to an object in parallel, then link libhyena.so
+    (or `out`, with extra -D tuning defines)."""
+    objdir = os.path.join(os.path.dirname(os.path.abspath(out)), "_build" + ("_" + "_".join(
+        d.replace("=", "") for d in defines) if defines else ""))
     os.makedirs(objdir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *HIPCC_FLAGS, *["-D" + d for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     failed = []
     for src, p in procs:
-        out, _ = p.communicate()
-        text = out.decode(errors="replace")
+        log, _ = p.communicate()
+        text = log.decode(errors="replace")
         if p.returncode != 0:
             failed.append((src, text))
         elif verbose and text.strip():
@@ -56,11 +58,11 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     if failed:
         msg = "\n".join(f"--- {s} ---\n{t}" for s, t in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -1,13 +1,15 @@
 // Device-side FFT building blocks for gfx950 (CDNA4, wave64).
 //
-// A length-N complex transform (N = 2^s, 16 <= N <= 16384) is carried by T = N/16
-// threads. Between passes every thread holds 16 values in registers in the
-// "strided" layout: thread t holds element t + T*e for e = 0..15. Each pass is a
+// A length-N complex transform (N = 2^s, 16 <= N <= 16384) is carried by T = N/E
+// threads (E = 16 or 32 values per thread). Between passes every thread holds E
+// values in registers in the "strided" layout: thread t holds element t + T*e
+// for e = 0..E-1. Each pass is a
 // Stockham (self-sorting) radix-R step: butterfly j reads x[j + r*N/R], scales
 // input r by W_{NS*R}^{r*(j mod NS)} and writes output r to
 // (j/NS)*NS*R + (j mod NS) + r*NS, where NS is the product of the radices of the
-// earlier passes. With N/16 threads and 16 values per thread, the inputs of every
-// pass are exactly the strided layout, and so are the outputs of the last pass,
+// earlier passes. With N/E threads and E values per thread (E/R butterflies per
+// thread), the inputs of every pass are exactly the strided layout, and so are
+// the outputs of the last pass,
 // so a transform takes natural order in and gives natural order out with only
 // (passes - 1) round trips through LDS. Radices are 16 (as 4x4) for every pass
 // except a final 2/4/8 pass when s is not a multiple of 4.
@@ -156,14 +158,15 @@ __device__ __forceinline__ void dft(float2* a) {
 
 constexpr int ilog2c(int n) { return n <= 1 ? 0 : 1 + ilog2c(n >> 1); }
 
-// Compile-time radix schedule for N = 2^LOG.
-template <int N>
+// Compile-time radix schedule for N = 2^LOG carried by N/E threads.
+template <int N, int E = 16>
 struct Sched {
+    static_assert(E == 16 || E == 32, "16 or 32 values per thread");
     static constexpr int LOG = ilog2c(N);
     static constexpr int FULL = LOG / 4;            // radix-16 passes
     static constexpr int REM = LOG % 4;             // trailing radix 2^REM pass if nonzero
     static constexpr int NPASS = FULL + (REM ? 1 : 0);
-    static constexpr int T = N / 16;                // threads per transform
+    static constexpr int T = N / E;                 // threads per transform
     static constexpr int radix(int p) { return p < FULL ? 16 : (1 << REM); }
     static constexpr int ns(int p) { return 1 << (4 * p); }  // product of earlier radices
     // offset of pass p's twiddles inside this size's table
@@ -175,47 +178,82 @@ struct Sched {
     static constexpr int twsize() { return twoff(NPASS); }
 };
 
-// LDS accessor for one transform stored contiguously (with one pad slot per 16
-// elements to spread power-of-two strides over the banks).
+// LDS accessors. phys(i) is the slot of element i; off(c) is the slot distance
+// of c elements when c is a multiple of 16 (so the per-thread part of an address
+// is computed once and the rest becomes an instruction's immediate offset);
+// small(r) is the distance of r < 16 elements from a multiple of 16.
+//
+// One transform stored contiguously with one pad slot per 16 elements, which
+// spreads power-of-two strides over the banks.
 struct RowAcc {
     float2* base;
-    __device__ __forceinline__ float2& operator[](int i) const { return base[i + (i >> 4)]; }
+    __device__ __forceinline__ uint32_t phys(uint32_t i) const { return i + (i >> 4); }
+    static constexpr uint32_t off(uint32_t c) { return c + c / 16; }
+    static constexpr uint32_t small(uint32_t r) { return r; }
+    __device__ __forceinline__ float2& operator[](uint32_t i) const { return base[phys(i)]; }
+    __device__ __forceinline__ float2& at(uint32_t slot) const { return base[slot]; }
 };
-// LDS accessor for one column of a [len][CP] tile: element i of column c.
+// One column of a [len][PITCH] tile: element i of the column at base + i*PITCH.
+template <int PITCH>
 struct ColAcc {
     float2* base;  // already offset by the column
-    int pitch;
-    __device__ __forceinline__ float2& operator[](int i) const { return base[i * pitch]; }
+    __device__ __forceinline__ uint32_t phys(uint32_t i) const { return i * PITCH; }
+    static constexpr uint32_t off(uint32_t c) { return c * PITCH; }
+    static constexpr uint32_t small(uint32_t r) { return r * PITCH; }
+    __device__ __forceinline__ float2& operator[](uint32_t i) const { return base[phys(i)]; }
+    __device__ __forceinline__ float2& at(uint32_t slot) const { return base[slot]; }
 };
 
 template <int N>
 __host__ __device__ constexpr int padded_len() { return N + N / 16; }
 
+// v[e] <-> element t + T*e of an LDS-resident transform.
+template <int T, int E, class Acc>
+__device__ __forceinline__ void lds_store_strided(const Acc& acc, int t, const float2 (&v)[E]) {
+    if constexpr (T % 16 == 0) {
+        const uint32_t b = acc.phys(t);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc.at(b + Acc::off(T * e)) = v[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[t + T * e] = v[e];
+    }
+}
+template <int T, int E, class Acc>
+__device__ __forceinline__ void lds_load_strided(const Acc& acc, int t, float2 (&v)[E]) {
+    if constexpr (T % 16 == 0) {
+        const uint32_t b = acc.phys(t);
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = acc.at(b + Acc::off(T * e));
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = acc[t + T * e];
+    }
+}
+
 // One Stockham pass P of a length-N transform (see the file header).
-template <int N, int P, bool INV, bool HALF_IN, bool LAST, class Acc>
-__device__ __forceinline__ void fft_pass(float2 (&v)[16], int t, const float2* __restrict__ tw,
-                                         const Acc& acc) {
-    using S = Sched<N>;
+template <int N, int E, int P, bool INV, bool HALF_IN, bool LAST, class Acc>
+__device__ __forceinline__ void fft_pass(float2 (&v)[E], int t, const float2* __restrict__ tw, const Acc& acc) {
+    using S = Sched<N, E>;
     constexpr int T = S::T;
     constexpr int R = S::radix(P);
     constexpr int NS = S::ns(P);
-    constexpr int Q = 16 / R;
+    constexpr int Q = E / R;
     if constexpr (P > 0) {
         __syncthreads();
-#pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] = acc[t + T * e];
+        lds_load_strided<T>(acc, t, v);
     }
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
-        const int j = t + T * q;
-        const int k = j & (NS - 1);
+        const uint32_t j = t + T * q;
+        const uint32_t k = j & (NS - 1);
         float2 a[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) a[r] = v[q + r * Q];
         if constexpr (NS > 1) {
-            const float2* twp = tw + S::twoff(P) + k;
+            const uint32_t tk = S::twoff(P) + k;
 #pragma unroll
-            for (int r = 1; r < R; ++r) a[r] = twmul<INV>(a[r], twp[(r - 1) * NS]);
+            for (int r = 1; r < R; ++r) a[r] = twmul<INV>(a[r], tw[tk + (r - 1) * NS]);
         }
         if constexpr (HALF_IN && P == 0 && R == 16)
             dft16<INV, true>(a);  // a[8..15] are the zero padding
@@ -228,40 +266,45 @@ __device__ __forceinline__ void fft_pass(float2 (&v)[16], int t, const float2* _
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            const int j = t + T * q;
-            const int k = j & (NS - 1);
-            const int base = (j / NS) * NS * R + k;
+            const uint32_t j = t + T * q;
+            const uint32_t k = j & (NS - 1);
+            const uint32_t pb = acc.phys((j / NS) * NS * R + k);
 #pragma unroll
-            for (int r = 0; r < R; ++r) acc[base + r * NS] = v[q + r * Q];
+            for (int r = 0; r < R; ++r) {
+                // NS >= 16: r*NS is a multiple of 16; NS == 1: the base is 16*j and r < 16
+                const uint32_t o = NS >= 16 ? Acc::off(r * NS) : Acc::small(r);
+                acc.at(pb + o) = v[q + r * Q];
+            }
         }
     }
 }
 
-template <int N, bool INV, bool HALF_IN, class Acc, int... Ps>
-__device__ __forceinline__ void fft_all_passes(float2 (&v)[16], int t, const float2* __restrict__ tw,
+template <int N, int E, bool INV, bool HALF_IN, class Acc, int... Ps>
+__device__ __forceinline__ void fft_all_passes(float2 (&v)[E], int t, const float2* __restrict__ tw,
                                                const Acc& acc, std::integer_sequence<int, Ps...>) {
-    (fft_pass<N, Ps, INV, HALF_IN, Ps == Sched<N>::NPASS - 1>(v, t, tw, acc), ...);
+    (fft_pass<N, E, Ps, INV, HALF_IN, Ps == Sched<N, E>::NPASS - 1>(v, t, tw, acc), ...);
 }
 
-// One length-N transform held in the strided layout v[e] = x[t + T*e]; on return
-// v[e] = X[t + T*e] in natural order. All threads of the block must call this
-// together (it synchronises the block). It begins with a barrier before its first
-// LDS write, so the caller may still have been reading LDS. HALF_IN: inputs
-// e >= 8 are zero (the zero-padded second half) and are not read.
-template <int N, bool INV, bool HALF_IN, class Acc>
-__device__ __forceinline__ void fft_strided(float2 (&v)[16], int t, const float2* __restrict__ tw,
-                                            const Acc& acc) {
+// One length-N transform held in the strided layout v[e] = x[t + T*e] (T = N/E);
+// on return v[e] = X[t + T*e] in natural order. All threads of the block must call
+// this together (it synchronises the block). It begins with a barrier before its
+// first LDS write, so the caller may still have been reading LDS. HALF_IN: inputs
+// e >= E/2 are zero (the zero-padded second half) and are not read.
+template <int N, bool INV, bool HALF_IN, int E, class Acc>
+__device__ __forceinline__ void fft_strided(float2 (&v)[E], int t, const float2* __restrict__ tw, const Acc& acc) {
     static_assert(N >= 16 && (N & (N - 1)) == 0, "transform length must be a power of two >= 16");
-    fft_all_passes<N, INV, HALF_IN>(v, t, tw, acc, std::make_integer_sequence<int, Sched<N>::NPASS>{});
+    static_assert(N >= E, "at least one thread per transform");
+    fft_all_passes<N, E, INV, HALF_IN>(v, t, tw, acc, std::make_integer_sequence<int, Sched<N, E>::NPASS>{});
 }
 
 // ---------------------------------------------------------------- element I/O
 
-// Two consecutive samples (2m, 2m+1) of a row, widened to fp32.
-__device__ __forceinline__ float2 load_pair(const float* __restrict__ row, int64_t m) {
+// Two consecutive samples (2m, 2m+1) of a row, widened to fp32. Rows are
+// addressed by a workgroup-uniform base pointer and a 32-bit element offset.
+__device__ __forceinline__ float2 load_pair(const float* __restrict__ row, uint32_t m) {
     return reinterpret_cast<const float2*>(row)[m];
 }
-__device__ __forceinline__ float2 load_pair(const uint16_t* __restrict__ row, int64_t m) {
+__device__ __forceinline__ float2 load_pair(const uint16_t* __restrict__ row, uint32_t m) {
     uint32_t bits = reinterpret_cast<const uint32_t*>(row)[m];
     return make_float2(__uint_as_float(bits << 16), __uint_as_float(bits & 0xffff0000u));
 }
@@ -270,17 +313,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // quiet NaN
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
-__device__ __forceinline__ void store_pair(float* __restrict__ row, int64_t m, float2 v) {
+__device__ __forceinline__ void store_pair(float* __restrict__ row, uint32_t m, float2 v) {
     reinterpret_cast<float2*>(row)[m] = v;
 }
-__device__ __forceinline__ void store_pair(uint16_t* __restrict__ row, int64_t m, float2 v) {
+__device__ __forceinline__ void store_pair(uint16_t* __restrict__ row, uint32_t m, float2 v) {
     reinterpret_cast<uint32_t*>(row)[m] = f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16);
 }
 
 // Causal width-3 depthwise conv (PyTorch Conv1d cross-correlation, padding 2)
 // evaluated at samples 2m and 2m+1 of one channel row.
 template <class TIO>
-__device__ __forceinline__ float2 conv3_pair(const TIO* __restrict__ row, int64_t m, float w0, float w1,
+__device__ __forceinline__ float2 conv3_pair(const TIO* __restrict__ row, uint32_t m, float w0, float w1,
                                              float w2) {
     const float2 cur = load_pair(row, m);
     const float2 prev = m > 0 ? load_pair(row, m - 1) : make_float2(0.f, 0.f);

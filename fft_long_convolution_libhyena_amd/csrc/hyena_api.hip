@@ -175,9 +175,9 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
         plan->fs.tw2 = dtab + o_tw2;
         plan->fs.otlo = dtab + o_lo;
         plan->fs.othi = dtab + o_hi;
+        plan->fs.slo = slo;
         plan->fs.pa = dtab + o_pa;
         plan->fs.pb = dtab + o_pb;
-        plan->fs.slo = slo;
     }
     *out = plan;
     return HYENA_OK;

@@ -5,12 +5,23 @@
 
 namespace hy {
 
-// LDS path: one workgroup per (b, d) row, L/16 threads, the whole packed
-// transform (L complex values plus one pad slot per 16) in LDS.
+// LDS path: one workgroup per (b, d) row, L/E threads holding E values each,
+// the whole packed transform (L complex values plus one pad slot per 16) in LDS.
+// Build-time tuning knobs of the LDS path (defaults chosen by measurement):
+//   HY_LDS_E32_FROM   smallest log2 L that uses 32 values per thread (else 16)
+//   HY_LDS_PREFETCH   fetch the spectrum before the forward transform (1) or in
+//                     the pair step (0)
+#ifndef HY_LDS_E32_FROM
+#define HY_LDS_E32_FROM 14
+#endif
+#ifndef HY_LDS_PREFETCH
+#define HY_LDS_PREFETCH 1
+#endif
 template <int LOGL>
 struct LdsCfg {
     static constexpr int L = 1 << LOGL;
-    static constexpr int THREADS = L / 16;
+    static constexpr int E = LOGL >= HY_LDS_E32_FROM ? 32 : 16;
+    static constexpr int THREADS = L / E;
 };
 constexpr int kLdsMaxLog = 14;  // L = 16384: 139,264 bytes of LDS
 
@@ -45,12 +56,12 @@ struct LdsArgs {
 };
 
 struct FsTables {
-    const float2* tw1;   // Stockham twiddles for length L1
-    const float2* tw2;   // Stockham twiddles for length L2
-    const float2* otlo;  // W_L^j, j < 2^slo
-    const float2* othi;  // W_L^(j * 2^slo), j < L / 2^slo
-    const float2* pa;    // W_{2L}^k1, k1 < L1
-    const float2* pb;    // W_{2L}^(L1*k2), k2 < L2
+    const float2* tw1;    // Stockham twiddles for length L1
+    const float2* tw2;    // Stockham twiddles for length L2
+    const float2* otlo;   // W_L^j, j < 2^slo
+    const float2* othi;   // W_L^(j * 2^slo), j < L / 2^slo
+    const float2* pa;     // W_{2L}^k1, k1 < L1
+    const float2* pb;     // W_{2L}^(L1*k2), k2 < L2
     int slo;
 };
 
