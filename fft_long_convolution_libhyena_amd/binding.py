@@ -15,16 +15,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhyena.so")
 
 HYENA_F32, HYENA_BF16 = 0, 1
-PATH_AUTO, PATH_LDS, PATH_FOURSTEP = 0, 1, 2
+PATH_AUTO, PATH_LDS, PATH_FOURSTEP, PATH_FUSED = 0, 1, 2, 3
 STATUS = {0: "HYENA_OK", 1: "HYENA_ERR_INVALID_ARG", 2: "HYENA_ERR_UNSUPPORTED",
           3: "HYENA_ERR_WORKSPACE", 4: "HYENA_ERR_DEVICE"}
-_PATHS = {"auto": PATH_AUTO, "lds": PATH_LDS, "fourstep": PATH_FOURSTEP}
+_PATHS = {"auto": PATH_AUTO, "lds": PATH_LDS, "fourstep": PATH_FOURSTEP, "fused": PATH_FUSED}
 _DTYPES = {"f32": HYENA_F32, "bf16": HYENA_BF16}
 
 # every symbol include/hyena.h declares
 EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_destroy", "hyena_plan_path",
            "hyena_spectrum_bytes", "hyena_workspace_bytes", "hyena_filter_spectrum", "hyena_forward",
-           "hyena_forward_timed", "hyena_status_string")
+           "hyena_forward_timed", "hyena_fused_check", "hyena_status_string")
 
 
 class HyenaError(RuntimeError):
@@ -65,6 +65,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_forward.restype = ci
     lib.hyena_forward_timed.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
     lib.hyena_forward_timed.restype = ci
+    lib.hyena_fused_check.argtypes = [vp, vp, ctypes.POINTER(ci)]
+    lib.hyena_fused_check.restype = ci
     lib.hyena_status_string.argtypes = [ci]
     lib.hyena_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -98,7 +100,7 @@ class Plan:
                self.lib.hyena_plan_create_path(ctypes.byref(h), self.L, self.D, self.order, _DTYPES[dtype],
                                                _PATHS[path]))
         self.handle = h
-        self.path = {PATH_LDS: "lds", PATH_FOURSTEP: "fourstep"}[self.lib.hyena_plan_path(h)]
+        self.path = {PATH_LDS: "lds", PATH_FOURSTEP: "fourstep", PATH_FUSED: "fused"}[self.lib.hyena_plan_path(h)]
 
     @property
     def io_dtype(self):
@@ -175,6 +177,15 @@ class Plan:
                                             spec.data_ptr(), bias.data_ptr(), y.data_ptr(), ws_ptr or None,
                                             ws_bytes, _stream_handle(torch, self.device), ms))
         return dict(zip(("lds", "pass_a", "pass_b", "pass_c", "total"), [float(v) for v in ms]))
+
+    def fused_check(self, workspace) -> int:
+        """hyena_fused_check: nonzero if a bounded wait of the fused kernel expired
+        in the last forward that used `workspace` (synchronous)."""
+        flag = ctypes.c_int(0)
+        _check("hyena_fused_check",
+               self.lib.hyena_fused_check(self.handle, workspace.data_ptr() if workspace is not None else None,
+                                          ctypes.byref(flag)))
+        return int(flag.value)
 
     def close(self):
         if getattr(self, "handle", None) is not None and self.handle.value:

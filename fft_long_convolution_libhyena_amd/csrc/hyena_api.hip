@@ -19,6 +19,7 @@ struct hyena_plan_s {
     hyena_dtype_t dtype = HYENA_F32;
     hyena_path_t path = HYENA_PATH_AUTO;
     int device = -1;
+    int fused_blocks = 0;    // persistent grid of the fused path
     float2* dtab = nullptr;  // all twiddle tables, one device allocation
     // LDS path
     const float2* tw = nullptr;
@@ -34,6 +35,18 @@ constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr int64_t kMaxLog = 20;
 constexpr size_t kChunkTargetBytes = 128u << 20;  // in-flight four-step intermediates per launch
 constexpr int64_t kMaxChunkRows = 65536;
+#ifndef HY_AUTO_FUSED
+#define HY_AUTO_FUSED 0
+#endif
+constexpr bool kAutoFused = HY_AUTO_FUSED != 0;
+#ifndef HY_FUSED_G
+#define HY_FUSED_G 2
+#endif
+#ifndef HY_FUSED_S
+#define HY_FUSED_S 3
+#endif
+constexpr int kFusedG = HY_FUSED_G;  // rows per group of the fused pipeline
+constexpr int kFusedS = HY_FUSED_S;  // tile slots (groups) per XCD ring; >= 3
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2_64(int64_t x) {
@@ -107,20 +120,25 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
     if (!out) return HYENA_ERR_INVALID_ARG;
     if (D < 1 || L < 1 || order < 2) return HYENA_ERR_INVALID_ARG;
     if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
-    if (path != HYENA_PATH_AUTO && path != HYENA_PATH_LDS && path != HYENA_PATH_FOURSTEP)
+    if (path != HYENA_PATH_AUTO && path != HYENA_PATH_LDS && path != HYENA_PATH_FOURSTEP && path != HYENA_PATH_FUSED)
         return HYENA_ERR_INVALID_ARG;
     if (!is_pow2(L) || L < 16 || L > (int64_t(1) << kMaxLog) || order > 8) return HYENA_ERR_UNSUPPORTED;
     if (D > (int64_t(1) << 24)) return HYENA_ERR_UNSUPPORTED;
     const int logL = ilog2_64(L);
     hyena_path_t p = path;
-    if (p == HYENA_PATH_AUTO) p = logL <= hy::kLdsMaxLog ? HYENA_PATH_LDS : HYENA_PATH_FOURSTEP;
+    if (p == HYENA_PATH_AUTO) {
+        if (logL <= hy::kLdsMaxLog) p = HYENA_PATH_LDS;
+        else if (kAutoFused && order == 2 && hy::fused_supported(logL)) p = HYENA_PATH_FUSED;
+        else p = HYENA_PATH_FOURSTEP;
+    }
     if (p == HYENA_PATH_LDS && logL > hy::kLdsMaxLog) return HYENA_ERR_UNSUPPORTED;
     if (p == HYENA_PATH_FOURSTEP && logL < hy::kFsMinLog) return HYENA_ERR_UNSUPPORTED;
+    if (p == HYENA_PATH_FUSED && !(order == 2 && hy::fused_supported(logL))) return HYENA_ERR_UNSUPPORTED;
 
     // host tables (fp64 -> fp32)
     std::vector<float2> tab;
     size_t o_tw = 0, o_wpair = 0, o_tw1 = 0, o_tw2 = 0, o_lo = 0, o_hi = 0, o_pa = 0, o_pb = 0;
-    int log1 = 0, log2 = 0, slo = 0;
+    int log1 = 0, log2 = 0;
     if (p == HYENA_PATH_LDS) {
         o_tw = tab.size();
         append_stockham(tab, logL);
@@ -133,11 +151,15 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
         append_stockham(tab, log1);
         o_tw2 = tab.size();
         append_stockham(tab, log2);
-        slo = (logL + 1) / 2;
+        // the four-step twiddle W_L^(k1*m2) with k1 = t + T1*e is the product of
+        // W_L^(t*m2) and W_L^(T1*e*m2): two small tables, both read with m2 fastest
+        const int64_t T1 = L1 / 16;
         o_lo = tab.size();
-        for (int64_t j = 0; j < (int64_t(1) << slo); ++j) tab.push_back(wfwd(j, L));
+        for (int64_t t = 0; t < T1; ++t)
+            for (int64_t m2 = 0; m2 < L2; ++m2) tab.push_back(wfwd(t * m2, L));
         o_hi = tab.size();
-        for (int64_t j = 0; j < (L >> slo); ++j) tab.push_back(wfwd(j << slo, L));
+        for (int64_t e = 0; e < 16; ++e)
+            for (int64_t m2 = 0; m2 < L2; ++m2) tab.push_back(wfwd(T1 * e * m2, L));
         o_pa = tab.size();
         for (int64_t k1 = 0; k1 < L1; ++k1) tab.push_back(wfwd(k1, 2 * L));
         o_pb = tab.size();
@@ -146,6 +168,15 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
 
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return HYENA_ERR_DEVICE;
+    int fused_blocks = 0;
+    if (p == HYENA_PATH_FUSED) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+            return HYENA_ERR_DEVICE;
+        const int per_cu = hy::fused_blocks_per_cu(logL);
+        if (per_cu < 1) return HYENA_ERR_DEVICE;
+        fused_blocks = (cus * per_cu) / 8 * 8;  // a multiple of 8: every XCD gets the same share
+    }
     float2* dtab = nullptr;
     if (hipMalloc((void**)&dtab, tab.size() * sizeof(float2)) != hipSuccess) return HYENA_ERR_DEVICE;
     if (hipMemcpy(dtab, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
@@ -164,6 +195,7 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
     plan->dtype = dtype;
     plan->path = p;
     plan->device = dev;
+    plan->fused_blocks = fused_blocks;
     plan->dtab = dtab;
     if (p == HYENA_PATH_LDS) {
         plan->tw = dtab + o_tw;
@@ -173,9 +205,8 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
         plan->log2 = log2;
         plan->fs.tw1 = dtab + o_tw1;
         plan->fs.tw2 = dtab + o_tw2;
-        plan->fs.otlo = dtab + o_lo;
-        plan->fs.othi = dtab + o_hi;
-        plan->fs.slo = slo;
+        plan->fs.tbase = dtab + o_lo;
+        plan->fs.tstep = dtab + o_hi;
         plan->fs.pa = dtab + o_pa;
         plan->fs.pb = dtab + o_pb;
     }
@@ -205,6 +236,7 @@ size_t hyena_spectrum_bytes(hyena_plan_t plan) {
 size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B) {
     if (!plan || B < 1) return 0;
     if (plan->path == HYENA_PATH_LDS) return 0;
+    if (plan->path == HYENA_PATH_FUSED) return hy::fused_workspace_bytes(plan->logL, B * plan->D, kFusedG, kFusedS);
     const size_t per_row = (size_t)plan->L * sizeof(float2);
     int64_t rows = B * plan->D;
     int64_t want = (int64_t)(kChunkTargetBytes / per_row);
@@ -244,6 +276,10 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
     const bool bf16 = plan->dtype == HYENA_BF16;
     const int64_t rows = B * plan->D;
     int64_t chunk = 0;
+    if (plan->path == HYENA_PATH_FUSED) {
+        if (!workspace || !aligned16(workspace)) return HYENA_ERR_WORKSPACE;
+        if (workspace_bytes < hy::fused_workspace_bytes(plan->logL, rows, kFusedG, kFusedS)) return HYENA_ERR_WORKSPACE;
+    }
     if (plan->path == HYENA_PATH_FOURSTEP) {
         if (!workspace || !aligned16(workspace)) return HYENA_ERR_WORKSPACE;
         chunk = chunk_rows(plan, rows, workspace_bytes);
@@ -256,7 +292,7 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
     std::vector<hipEvent_t> ev;
     if (ms) {
         for (int i = 0; i < 5; ++i) ms[i] = 0.f;
-        const int64_t n = plan->path == HYENA_PATH_FOURSTEP ? nchunks * (per_chunk + 1) : 2;
+        const int64_t n = plan->path == HYENA_PATH_FOURSTEP ? nchunks * (per_chunk + 1) : 2;  // LDS, FUSED: 2
         if (n > 4096) return HYENA_ERR_INVALID_ARG;  // timing is for bounded chunk counts
         ev.resize((size_t)n, nullptr);
         for (auto& e : ev)
@@ -267,7 +303,14 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
             }
     }
     hyena_status_t st = HYENA_OK;
-    if (plan->path == HYENA_PATH_LDS) {
+    if (plan->path == HYENA_PATH_FUSED) {
+        hy::FsArgs a{u_proj, short_w, (const float2*)spec, bias, y, (float2*)workspace, plan->fs,
+                     (int)plan->D, plan->order, bf16};
+        if (ms) (void)hipEventRecord(ev[0], stream);
+        if (hy::launch_fs_fused(plan->logL, a, rows, kFusedG, kFusedS, plan->fused_blocks, stream) != hipSuccess)
+            st = HYENA_ERR_DEVICE;
+        if (ms) (void)hipEventRecord(ev[1], stream);
+    } else if (plan->path == HYENA_PATH_LDS) {
         if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
         hy::LdsArgs a{u_proj, short_w, (const float2*)spec, bias, y, plan->tw, plan->wpair,
                       (int)B, (int)plan->D, plan->order, bf16};
@@ -289,7 +332,7 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
         if (st == HYENA_OK && hipEventSynchronize(ev.back()) != hipSuccess) st = HYENA_ERR_DEVICE;
         if (st == HYENA_OK) {
             float t = 0.f;
-            if (plan->path == HYENA_PATH_LDS) {
+            if (plan->path != HYENA_PATH_FOURSTEP) {
                 (void)hipEventElapsedTime(&t, ev[0], ev[1]);
                 ms[0] = t;
             } else {
@@ -314,6 +357,18 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
 }  // namespace
 
 extern "C" {
+
+hyena_status_t hyena_fused_check(hyena_plan_t plan, const void* workspace, int* flag) {
+    if (!plan || !flag) return HYENA_ERR_INVALID_ARG;
+    *flag = 0;
+    if (plan->path != HYENA_PATH_FUSED) return HYENA_OK;
+    if (!workspace) return HYENA_ERR_INVALID_ARG;
+    uint32_t ctl[8 * 32];
+    if (hipMemcpy(ctl, workspace, sizeof(ctl), hipMemcpyDeviceToHost) != hipSuccess) return HYENA_ERR_DEVICE;
+    for (int x = 0; x < 8; ++x)
+        if (ctl[hy::fused_error_offset(x) / 4] != 0) *flag = 1;
+    return HYENA_OK;
+}
 
 hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
                              const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,

@@ -58,11 +58,10 @@ struct LdsArgs {
 struct FsTables {
     const float2* tw1;    // Stockham twiddles for length L1
     const float2* tw2;    // Stockham twiddles for length L2
-    const float2* otlo;   // W_L^j, j < 2^slo
-    const float2* othi;   // W_L^(j * 2^slo), j < L / 2^slo
+    const float2* tbase;  // [t][m2] = W_L^(t*m2), t < L1/16, m2 < L2
+    const float2* tstep;  // [e][m2] = W_L^((L1/16)*e*m2), e < 16, m2 < L2
     const float2* pa;     // W_{2L}^k1, k1 < L1
     const float2* pb;     // W_{2L}^(L1*k2), k2 < L2
-    int slo;
 };
 
 struct FsArgs {
@@ -85,6 +84,13 @@ hipError_t launch_fs_forward_chunk(int logL, const FsArgs& a, int64_t row0, int6
 hipError_t launch_fs_spectrum(int logL, const float* h, float2* spec, int64_t rows, const FsTables& tb,
                               hipStream_t st);
 void fs_split(int logL, int* log1, int* log2);
+
+// Fused persistent four-step (order 2): one launch per forward, per-XCD pipelines.
+bool fused_supported(int logL);
+int fused_blocks_per_cu(int logL);
+size_t fused_workspace_bytes(int logL, int64_t nrows, int G, int S);
+hipError_t launch_fs_fused(int logL, const FsArgs& a, int64_t nrows, int G, int S, int blocks, hipStream_t st);
+uint32_t fused_error_offset(int x);
 int fs_row_units(int logL);
 
 }  // namespace hy

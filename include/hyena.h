@@ -55,9 +55,23 @@ typedef enum {
     HYENA_ERR_DEVICE = 4       /* no usable HIP device, allocation or launch failure */
 } hyena_status_t;
 
-/* Which kernel family runs a plan. AUTO keeps the whole transform in LDS when
- * L <= 16384 and uses the four-step multi-pass transform above that. */
-typedef enum { HYENA_PATH_AUTO = 0, HYENA_PATH_LDS = 1, HYENA_PATH_FOURSTEP = 2 } hyena_path_t;
+/* Which kernel family runs a plan.
+ *   LDS       one launch; the whole transform of a (b, d) row stays in LDS
+ *             (L <= 16384).
+ *   FOURSTEP  three launches per recurrence step (column FFTs, row FFTs with
+ *             the spectrum multiply, inverse columns with the gate); any order,
+ *             256 <= L <= 2^20.
+ *   FUSED     one persistent launch for the whole four-step forward, with the
+ *             intermediate tiles kept in each XCD's L2 (order 2, L = 65536).
+ *             Not available in this build: plans asking for it get
+ *             HYENA_ERR_UNSUPPORTED.
+ * AUTO picks LDS when L <= 16384 and FOURSTEP otherwise. */
+typedef enum {
+    HYENA_PATH_AUTO = 0,
+    HYENA_PATH_LDS = 1,
+    HYENA_PATH_FOURSTEP = 2,
+    HYENA_PATH_FUSED = 3
+} hyena_path_t;
 
 /* Create a plan for sequence length L, operator width D and recurrence order
  * N = `order` (N-1 long filters, N gates). Requirements: L a power of two in
@@ -69,9 +83,10 @@ typedef enum { HYENA_PATH_AUTO = 0, HYENA_PATH_LDS = 1, HYENA_PATH_FOURSTEP = 2 
 hyena_status_t hyena_plan_create(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype);
 
 /* As hyena_plan_create, with an explicit kernel family. HYENA_PATH_LDS needs
- * L <= 16384; HYENA_PATH_FOURSTEP needs L >= 256 (HYENA_ERR_UNSUPPORTED
- * otherwise). The spectrum layout depends on the path, so a spectrum must be
- * made by a plan of the same path as the plan that consumes it. */
+ * L <= 16384; HYENA_PATH_FOURSTEP needs L >= 256; HYENA_PATH_FUSED is not
+ * available in this build (HYENA_ERR_UNSUPPORTED otherwise). The spectrum layout
+ * depends on the path (FOURSTEP and FUSED share one), so a spectrum must be made
+ * by a plan whose path uses the same layout as the plan that consumes it. */
 hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype,
                                       hyena_path_t path);
 
@@ -87,11 +102,12 @@ hyena_path_t hyena_plan_path(hyena_plan_t plan);
  * 8 * (N-1) * D * L. Returns 0 for a NULL plan. */
 size_t hyena_spectrum_bytes(hyena_plan_t plan);
 
-/* Recommended workspace for a forward over batch B: 0 on the LDS path; on the
- * four-step path 8*L bytes per (b, d) row held in flight, for a chunk of rows
- * chosen to stay cache-resident. Any workspace of at least 8*L bytes (one row)
- * is accepted by hyena_forward; a larger one lets more rows run per launch.
- * Returns 0 for a NULL plan or B < 1. */
+/* Workspace for a forward over batch B: 0 on the LDS path. On the four-step
+ * path this is the recommended size (8*L bytes per (b, d) row held in flight);
+ * any workspace of at least 8*L bytes (one row) is accepted, a larger one lets
+ * more rows run per launch. On the fused path it is the exact minimum: a control
+ * block, per-row counters and a ring of tiles per XCD. Returns 0 for a NULL plan
+ * or B < 1. */
 size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* The real FFT of the long filters, once per plan (the filter spectrum of the
@@ -129,7 +145,7 @@ hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, c
  * recorded on `stream` around every kernel launch of this forward; the call
  * then waits for the last event (so it is synchronous), and writes elapsed
  * milliseconds summed per kernel family into ms[5]:
- *   ms[0] fused LDS-path kernel, ms[1] four-step pass A (column FFTs of the
+ *   ms[0] the single kernel of the LDS or fused path, ms[1] four-step pass A (column FFTs of the
  *   gated input), ms[2] pass B (row FFTs, spectrum multiply, inverse rows),
  *   ms[3] pass C (inverse columns and gate; for order > 2 it also carries the
  *   next step's pass A), ms[4] first event to last event.
@@ -138,6 +154,13 @@ hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, c
 hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
                                    const void* spec, const float* bias, void* y, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream, float* ms);
+
+/* Diagnostic for the fused path: after the stream has reached the end of a
+ * forward that used `workspace`, reports in *flag whether any of the kernel's
+ * bounded waits expired (nonzero: the output of that forward is invalid). Copies
+ * the 1 KiB control block to the host synchronously. *flag = 0 on other paths. Errors:
+ * HYENA_ERR_INVALID_ARG for NULL arguments, HYENA_ERR_DEVICE if the copy fails. */
+hyena_status_t hyena_fused_check(hyena_plan_t plan, const void* workspace, int* flag);
 
 /* Static, NUL-terminated description of a status code. */
 const char* hyena_status_string(hyena_status_t s);

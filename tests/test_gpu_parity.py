@@ -262,5 +262,44 @@ def test_error_paths_on_device():
     lib = load_library()
     assert lib.hyena_plan_create_path(ctypes.byref(h), 1 << 15, 4, 2, 0, 1) == 2  # LDS path too long
     assert lib.hyena_plan_create_path(ctypes.byref(h), 128, 4, 2, 0, 2) == 2  # four-step too short
+    assert lib.hyena_plan_create_path(ctypes.byref(h), 65536, 4, 2, 0, 3) == 2  # fused path switched off
     with pytest.raises(HyenaError):
         Plan(1000, 4, 2)
+
+
+# ---------------------------------------------------------- fused path
+
+
+@pytest.mark.skip(reason="fused persistent path switched off: its first two runs on MI355X did not finish "
+                         "(the second with time-bounded waits); a CPU emulation of its ticket/counter logic "
+                         "completes, so the cause is not yet shown")
+@pytest.mark.parametrize("B,D", [(1, 1), (1, 13), (2, 24), (1, 96)])
+def test_fused_path_parity(B, D):
+    """The persistent single-launch four-step (order 2, L = 65536) against the oracle,
+    including fewer rows than XCDs; its bounded waits must never expire."""
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan
+
+    wl = synth.custom(B, D, 65536, 2, seed=100 + D)
+    x = synth.generate(wl)
+    t = to_device(x)
+    say(f"[fused] B={B} D={D}")
+    with Plan(wl.L, wl.D, 2, "f32", "fused") as p:
+        spec = p.spectrum(t["h"])
+        ws = torch.empty(p.workspace_bytes(B), dtype=torch.uint8, device="cuda")
+        say("   first forward")
+        y = p.forward(t["u"], t["w"], spec, t["bias"], workspace=ws)
+        torch.cuda.synchronize()
+        say(f"   done; bounded-wait error flag {p.fused_check(ws)}")
+        assert p.fused_check(ws) == 0
+        y2 = p.forward(t["u"], t["w"], spec, t["bias"], workspace=ws)
+        torch.cuda.synchronize()
+        assert p.fused_check(ws) == 0
+    rows = synth.sample_rows(wl, 8)
+    ref = oracle.forward(x.u_proj, x.short_w, x.h, x.bias, 2, rows=rows)
+    got = y.cpu().numpy().astype(np.float64).reshape(-1, wl.L)[rows]
+    err = oracle.rel_l2(got, ref)
+    say(f"   rel_l2={err:.3e}")
+    assert err <= 1e-4
+    assert bool((y == y2).all())
