@@ -15,6 +15,8 @@ Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
@@ -65,6 +67,39 @@ def alg_bytes_pass(wl, family: str) -> int:
     if family == "pass_c":
         return (N - 1) * rows * (tile + s * L) + rows * s * L + (N - 2) * rows * tile
     raise ValueError(family)
+
+
+def kernel_sources_hash() -> str:
+    """Hash of the HIP sources and the C header; counter summaries record it."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "fft_long_convolution_libhyena_amd", "csrc", "*.hip")) +
+                   glob.glob(os.path.join(ROOT, "fft_long_convolution_libhyena_amd", "csrc", "*.hpp")))
+    files.append(os.path.join(ROOT, "include", "hyena.h"))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, already scaled by the copy calibration), or None when
+    there is no summary or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("sources_sha256") != kernel_sources_hash():
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_dispatch"]) + float(kv["write_bytes_per_dispatch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(x, wl, budget_s: float):
@@ -180,10 +215,13 @@ def main():
         rows = wl.B * wl.D
         chunk = max(1, min(rows, (ws_bytes // (8 * wl.L)) if ws_bytes else rows))
         launches = math.ceil(rows / chunk) * (1 if fam == "pass_a" else wl.order - 1)
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    per_launch_ms = dom_ms / launches
+    per_launch_bytes = dom_bytes / launches
+    achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
-                "launches_per_step": launches, "kernel_ms_per_step": round(dom_ms, 5)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, wl.name),
+                "kernel": dom, "alg_bytes_per_launch": int(per_launch_bytes),
+                "launch_ms": round(per_launch_ms, 5), "launches_per_step": launches}
 
     out = {
         "metric": METRIC,

@@ -320,17 +320,47 @@ __device__ __forceinline__ void store_pair(uint16_t* __restrict__ row, uint32_t 
     reinterpret_cast<uint32_t*>(row)[m] = f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16);
 }
 
+// A pair of samples as stored (fp32 pair or two packed bf16), for fetching ahead
+// of use.
+template <class TIO>
+struct RawPair;
+template <>
+struct RawPair<float> {
+    using type = float2;
+    static __device__ __forceinline__ float2 zero() { return make_float2(0.f, 0.f); }
+};
+template <>
+struct RawPair<uint16_t> {
+    using type = uint32_t;
+    static __device__ __forceinline__ uint32_t zero() { return 0u; }
+};
+__device__ __forceinline__ float2 load_raw(const float* __restrict__ row, uint32_t m) {
+    return reinterpret_cast<const float2*>(row)[m];
+}
+__device__ __forceinline__ uint32_t load_raw(const uint16_t* __restrict__ row, uint32_t m) {
+    return reinterpret_cast<const uint32_t*>(row)[m];
+}
+__device__ __forceinline__ float2 unpack_raw(float2 v) { return v; }
+__device__ __forceinline__ float2 unpack_raw(uint32_t bits) {
+    return make_float2(__uint_as_float(bits << 16), __uint_as_float(bits & 0xffff0000u));
+}
+
 // Causal width-3 depthwise conv (PyTorch Conv1d cross-correlation, padding 2)
-// evaluated at samples 2m and 2m+1 of one channel row.
+// at samples 2m and 2m+1, from the pairs (2m-2, 2m-1) and (2m, 2m+1).
+__device__ __forceinline__ float2 conv3_from(float2 prev, float2 cur, float w0, float w1, float w2) {
+    float2 r;
+    r.x = fmaf(w0, prev.x, fmaf(w1, prev.y, w2 * cur.x));
+    r.y = fmaf(w0, prev.y, fmaf(w1, cur.x, w2 * cur.y));
+    return r;
+}
+
+// The same, reading both pairs of one channel row.
 template <class TIO>
 __device__ __forceinline__ float2 conv3_pair(const TIO* __restrict__ row, uint32_t m, float w0, float w1,
                                              float w2) {
     const float2 cur = load_pair(row, m);
     const float2 prev = m > 0 ? load_pair(row, m - 1) : make_float2(0.f, 0.f);
-    float2 r;
-    r.x = fmaf(w0, prev.x, fmaf(w1, prev.y, w2 * cur.x));
-    r.y = fmaf(w0, prev.y, fmaf(w1, cur.x, w2 * cur.y));
-    return r;
+    return conv3_from(prev, cur, w0, w1, w2);
 }
 
 }  // namespace hy

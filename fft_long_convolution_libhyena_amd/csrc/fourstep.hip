@@ -36,6 +36,10 @@
 #include "kernels.hpp"
 #include "pair.hpp"
 
+#ifndef HY_EXPERIMENTAL_FUSED
+#define HY_EXPERIMENTAL_FUSED 0
+#endif
+
 namespace hy {
 
 // defined in lds_path_*.hip
@@ -695,15 +699,21 @@ static int fused_occupancy_t() {
 // same ticket and counter logic completes for every tested shape. Until the cause
 // is found it is only built for experiments (HY_EXPERIMENTAL_FUSED=1) and plans
 // asking for it get HYENA_ERR_UNSUPPORTED.
-#ifndef HY_EXPERIMENTAL_FUSED
-#define HY_EXPERIMENTAL_FUSED 0
-#endif
 bool fused_supported(int logL) { return HY_EXPERIMENTAL_FUSED && logL == 16; }
 
-int fused_blocks_per_cu(int logL) { return logL == 16 ? fused_occupancy_t<8, 8>() : 0; }
+int fused_blocks_per_cu(int logL) {
+#if HY_EXPERIMENTAL_FUSED
+    if (logL == 16) return fused_occupancy_t<8, 8>();
+#endif
+    (void)logL;
+    return 0;
+}
 
 hipError_t launch_fs_fused(int logL, const FsArgs& a, int64_t nrows, int G, int S, int blocks, hipStream_t st) {
+#if HY_EXPERIMENTAL_FUSED
     if (logL == 16) return fused_launch_t<8, 8>(a, nrows, G, S, blocks, st);
+#endif
+    (void)logL; (void)a; (void)nrows; (void)G; (void)S; (void)blocks; (void)st;
     return hipErrorInvalidValue;
 }
 

@@ -11,11 +11,21 @@ namespace hy {
 //   HY_LDS_E32_FROM   smallest log2 L that uses 32 values per thread (else 16)
 //   HY_LDS_PREFETCH   fetch the spectrum before the forward transform (1) or in
 //                     the pair step (0)
+//   HY_LDS_PREFETCH_GATE  fetch the final gate's input rows before the inverse
+//                     transform (1) or after it (0)
+// and of the four-step path:
+//   HY_FS_CB          columns per pass A / pass C workgroup
 #ifndef HY_LDS_E32_FROM
 #define HY_LDS_E32_FROM 14
 #endif
 #ifndef HY_LDS_PREFETCH
 #define HY_LDS_PREFETCH 1
+#endif
+#ifndef HY_LDS_PREFETCH_GATE
+#define HY_LDS_PREFETCH_GATE 1
+#endif
+#ifndef HY_FS_CB
+#define HY_FS_CB 16
 #endif
 template <int LOGL>
 struct LdsCfg {
@@ -32,7 +42,7 @@ struct FsCfg {
     static constexpr int L2 = 1 << LOG2;
     static constexpr int T1 = L1 / 16;                 // threads per column transform
     static constexpr int T2 = L2 / 16;                 // threads per row transform
-    static constexpr int CB = 16;                      // columns per pass A/C workgroup
+    static constexpr int CB = HY_FS_CB;                // columns per pass A/C workgroup
     static constexpr int CP = CB + 1;                  // LDS pitch of the column tile
     static constexpr int COL_THREADS = CB * T1;
     static constexpr int U0 = 256 / (2 * T2);

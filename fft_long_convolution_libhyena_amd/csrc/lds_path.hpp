@@ -129,18 +129,36 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
         }
         __syncthreads();
         lds_load_strided<T>(acc, t, v);
-        fft_strided<L, true, false>(v, t, tw, acc);
-        // v[e], e < E/2, holds (c[2m], c[2m+1]) = conv + bias*v at m = t + T*e
         const bool last = (o == N - 2);
         const int cg = (last ? 0 : N - 2 - o) * D + d;
         const TIO* rg = ub + (int64_t)cg * L;
         const float* wg = w3 + 3 * cg;
+        // the gate's input samples, fetched before the inverse transform so that
+        // their latency hides behind it
+        typename RawPair<TIO>::type gcur[H], gprev[H];
+        if constexpr (HY_LDS_PREFETCH_GATE) {
+            if (last) {
+#pragma unroll
+                for (int e = 0; e < H; ++e) {
+                    const uint32_t m = t + T * e;
+                    gcur[e] = load_raw(rg, m);
+                    gprev[e] = m > 0 ? load_raw(rg, m - 1) : RawPair<TIO>::zero();
+                }
+            }
+        }
+        fft_strided<L, true, false>(v, t, tw, acc);
+        // v[e], e < E/2, holds (c[2m], c[2m+1]) = conv + bias*v at m = t + T*e
         if (last) {
             TIO* yr = y + ((int64_t)b * D + d) * L;
 #pragma unroll
             for (int e = 0; e < H; ++e) {
                 const uint32_t m = t + T * e;
-                store_pair(yr, m, emul(v[e], conv3_pair(rg, m, wg[0], wg[1], wg[2])));
+                float2 g;
+                if constexpr (HY_LDS_PREFETCH_GATE)
+                    g = conv3_from(unpack_raw(gprev[e]), unpack_raw(gcur[e]), wg[0], wg[1], wg[2]);
+                else
+                    g = conv3_pair(rg, m, wg[0], wg[1], wg[2]);
+                store_pair(yr, m, emul(v[e], g));
             }
         } else {
 #pragma unroll
