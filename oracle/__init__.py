@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the Hyena operator forward hot path (test infrastructure).
+"""fp64 CPU oracle for the Hyena operator forward hot path and its backward (test
+infrastructure).
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The product (the HIP library and its binding) never does.
@@ -54,6 +55,13 @@ def _load():
         lib.oracle_hyena_forward.argtypes = [i64, i64, i64, ctypes.c_int, f32p, f32p, f32p, f32p,
                                              i64p, i64, f64p, ctypes.c_int, ctypes.c_int]
         lib.oracle_hyena_forward.restype = ctypes.c_int
+        lib.oracle_causal_corr_direct.argtypes = [f64p, f64p, i64, f64p]
+        lib.oracle_causal_corr_direct.restype = None
+        lib.oracle_causal_corr_fft.argtypes = [f64p, f64p, i64, f64p]
+        lib.oracle_causal_corr_fft.restype = None
+        lib.oracle_hyena_backward.argtypes = [i64, i64, i64, ctypes.c_int, f32p, f32p, f32p, f32p, f32p,
+                                              f64p, f64p, f64p, f64p, ctypes.c_int, ctypes.c_int]
+        lib.oracle_hyena_backward.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib = lib
@@ -96,6 +104,18 @@ def causal_conv(v: np.ndarray, h: np.ndarray, mode: str = "fft") -> np.ndarray:
     return out
 
 
+def causal_corr(a: np.ndarray, k: np.ndarray, mode: str = "fft") -> np.ndarray:
+    """corr(a, k)[t] = sum_{s >= t} k[s - t] a[s]: the adjoint of v -> conv(v, k)."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    if a.size != k.size:
+        raise ValueError("a and k must have the same length")
+    out = np.empty(a.size, dtype=np.float64)
+    fn = _load().oracle_causal_corr_fft if mode == "fft" else _load().oracle_causal_corr_direct
+    fn(_ptr(a, ctypes.c_double), _ptr(k, ctypes.c_double), a.size, _ptr(out, ctypes.c_double))
+    return out
+
+
 def max_threads() -> int:
     return int(_load().oracle_max_threads())
 
@@ -134,6 +154,39 @@ def forward(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.nda
     if rc != 0:
         raise ValueError("oracle_hyena_forward rejected its arguments")
     return out
+
+
+def backward(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray, dy: np.ndarray,
+             order: int, mode: str = "fft", threads: int = 0):
+    """Gradients of the hot path in fp64 for upstream gradient dy [B,D,L].
+
+    Returns (du_proj [B,(N+1)D,L], dshort_w [(N+1)D,3], dh [N-1,D,L], dbias [N-1,D]),
+    all float64; every input is taken as fp32 values.
+    """
+    u = np.ascontiguousarray(u_proj, dtype=np.float32)
+    w = np.ascontiguousarray(short_w, dtype=np.float32)
+    hh = np.ascontiguousarray(h, dtype=np.float32)
+    bb = np.ascontiguousarray(bias, dtype=np.float32)
+    g = np.ascontiguousarray(dy, dtype=np.float32)
+    B, C, L = u.shape
+    N = int(order)
+    if C % (N + 1):
+        raise ValueError("u_proj channel count must be (order+1)*D")
+    D = C // (N + 1)
+    if w.shape != (C, 3) or hh.shape != (N - 1, D, L) or bb.shape != (N - 1, D) or g.shape != (B, D, L):
+        raise ValueError("parameter shapes do not match u_proj")
+    du = np.empty((B, C, L), dtype=np.float64)
+    dw = np.empty((C, 3), dtype=np.float64)
+    dh = np.empty((N - 1, D, L), dtype=np.float64)
+    db = np.empty((N - 1, D), dtype=np.float64)
+    d64 = ctypes.c_double
+    rc = _load().oracle_hyena_backward(B, D, L, N, _ptr(u, ctypes.c_float), _ptr(w, ctypes.c_float),
+                                       _ptr(hh, ctypes.c_float), _ptr(bb, ctypes.c_float),
+                                       _ptr(g, ctypes.c_float), _ptr(du, d64), _ptr(dw, d64), _ptr(dh, d64),
+                                       _ptr(db, d64), 0 if mode == "direct" else 1, int(threads))
+    if rc != 0:
+        raise ValueError("oracle_hyena_backward rejected its arguments")
+    return du, dw, dh, db
 
 
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:

@@ -1,5 +1,5 @@
 /*
- * Plain fp64 CPU oracle for the Hyena operator forward hot path.
+ * Plain fp64 CPU oracle for the Hyena operator forward hot path and its backward.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call
  * this file; only the tests, the smoke check and the benchmark's CPU-baseline
@@ -227,6 +227,211 @@ int oracle_hyena_forward(int64_t B, int64_t D, int64_t L, int N,
                 /* final gate */
                 double* out = y + r * L;
                 for (int64_t t = 0; t < L; ++t) out[t] = v[t] * xs[t];
+            }
+            free(buf);
+        }
+    }
+    free(tab);
+    return failed ? -1 : 0;
+}
+
+/*
+ * Backward of the hot path (gradients of a scalar loss with upstream gradient dy
+ * with respect to every input), by the chain rule on the same definitions.
+ *
+ * The adjoint of the causal convolution v -> conv(v, k) is the correlation
+ *   corr(a, k)[t] = sum_{s=t}^{L-1} k[s-t] a[s],
+ * and the gradient of conv(v, k) with respect to the kernel k, given the
+ * upstream a, is corr(a, v) (same formula with the roles of k and v swapped).
+ * With g_o = v_o * x_{N-1-o} and v_{o+1} = conv(g_o, h_o) + bias_o * g_o:
+ *   dv_{N-1} = dy * x_0,                 dx_0 = dy * v_{N-1}
+ *   for o = N-2 .. 0, with a = dv_{o+1}:
+ *     dh_o    += corr(a, g_o)            dbias_o += sum_t a[t] g_o[t]
+ *     dg_o     = corr(a, h_o) + bias_o * a
+ *     dx_{N-1-o} = dg_o * v_o,           dv_o = dg_o * x_{N-1-o}
+ * and through the short convolution uc = w0 u[t-2] + w1 u[t-1] + w2 u[t]:
+ *   du[t] = w2 duc[t] + w1 duc[t+1] + w0 duc[t+2]   (samples past L-1 are 0)
+ *   dw[j] += sum_t duc[t] u[t-2+j]                  (samples before 0 are 0)
+ * Sums over the batch are taken for dh, dbias and dw.
+ */
+
+/* corr(a, k) by its definition, O(L^2). */
+void oracle_causal_corr_direct(const double* a, const double* k, int64_t L, double* out) {
+    for (int64_t t = 0; t < L; ++t) {
+        double s = 0.0;
+        for (int64_t q = t; q < L; ++q) s += k[q - t] * a[q];
+        out[t] = s;
+    }
+}
+
+/* corr(a, k) through the FFT on n >= 2L zero-padded points:
+ * IFFT(FFT(a) * conj(FFT(k))) / n, first L samples (no wrap-around because the
+ * negative lags land in the zero padding). Scratch: 4*n doubles. */
+static void corr_fft_with(const double* a, const double* k, int64_t L, int64_t n,
+                          const double* fr, const double* fi, const double* ir, const double* ii,
+                          double* scratch, double* out) {
+    double *ar = scratch, *ai = scratch + n, *br = scratch + 2 * n, *bi = scratch + 3 * n;
+    for (int64_t t = 0; t < n; ++t) {
+        ar[t] = t < L ? a[t] : 0.0; ai[t] = 0.0;
+        br[t] = t < L ? k[t] : 0.0; bi[t] = 0.0;
+    }
+    fft_radix2(ar, ai, n, fr, fi);
+    fft_radix2(br, bi, n, fr, fi);
+    for (int64_t q = 0; q < n; ++q) {
+        /* a * conj(b) */
+        double cr = ar[q] * br[q] + ai[q] * bi[q];
+        double ci = ai[q] * br[q] - ar[q] * bi[q];
+        ar[q] = cr; ai[q] = ci;
+    }
+    fft_radix2(ar, ai, n, ir, ii);
+    for (int64_t t = 0; t < L; ++t) out[t] = ar[t] / (double)n;
+}
+
+void oracle_causal_corr_fft(const double* a, const double* k, int64_t L, double* out) {
+    int64_t n = pow2_at_least(2 * L);
+    double* tab = (double*)malloc(sizeof(double) * (size_t)(2 * n));
+    double* scratch = (double*)malloc(sizeof(double) * (size_t)(4 * n));
+    make_twiddles(n, -1, tab, tab + n / 2);
+    make_twiddles(n, +1, tab + n, tab + n + n / 2);
+    corr_fft_with(a, k, L, n, tab, tab + n / 2, tab + n, tab + n + n / 2, scratch, out);
+    free(tab); free(scratch);
+}
+
+/*
+ * Gradients of the hot path.
+ *   inputs  u [B][(N+1)D][L], w [(N+1)D][3], h [N-1][D][L], bias [N-1][D] as in the
+ *           forward, dy [B][D][L] (all fp32 values, widened exactly)
+ *   outputs du [B][(N+1)D][L], dw [(N+1)D][3], dh [N-1][D][L], dbias [N-1][D] (fp64)
+ *   mode    0 = direct O(L^2) convolutions and correlations, 1 = fp64 FFT
+ * Channels d are independent (every output row belongs to one d), so the work is
+ * split over d. Returns 0 on success, -1 on invalid arguments or allocation failure.
+ */
+int oracle_hyena_backward(int64_t B, int64_t D, int64_t L, int N,
+                          const float* u, const float* w, const float* h, const float* bias,
+                          const float* dy, double* du, double* dw, double* dh, double* dbias,
+                          int mode, int nthreads) {
+    if (B < 1 || D < 1 || L < 1 || N < 2 || !u || !w || !h || !bias || !dy) return -1;
+    if (!du || !dw || !dh || !dbias) return -1;
+    if (mode != 0 && mode != 1) return -1;
+    const int64_t C = (int64_t)(N + 1) * D;
+    const int64_t n = pow2_at_least(2 * L);
+    double* tab = NULL;
+    if (mode == 1) {
+        tab = (double*)malloc(sizeof(double) * (size_t)(2 * n));
+        make_twiddles(n, -1, tab, tab + n / 2);
+        make_twiddles(n, +1, tab + n, tab + n + n / 2);
+    }
+    const double *fr = tab, *fi = tab ? tab + n / 2 : NULL, *ir = tab ? tab + n : NULL,
+                 *ii = tab ? tab + n + n / 2 : NULL;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int failed = 0;
+#pragma omp parallel
+    {
+        /* x_0..x_{N-1}, v_0..v_{N-1}, g_0..g_{N-2}, duc_0..duc_N, filter, a, c, FFT scratch */
+        const int64_t nbuf = (int64_t)(N + N + (N - 1) + (N + 1) + 3) * L + (mode == 1 ? 4 * n : 0);
+        double* buf = (double*)malloc(sizeof(double) * (size_t)nbuf);
+        if (!buf) {
+#pragma omp atomic write
+            failed = 1;
+        } else {
+            double* xs = buf;
+            double* vs = xs + (int64_t)N * L;
+            double* gs = vs + (int64_t)N * L;
+            double* duc = gs + (int64_t)(N - 1) * L;
+            double* hk = duc + (int64_t)(N + 1) * L;
+            double* a = hk + L;
+            double* c = a + L;
+            double* scratch = c + L;
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t d = 0; d < D; ++d) {
+                for (int i = 0; i <= N; ++i)
+                    for (int j = 0; j < 3; ++j) dw[((int64_t)i * D + d) * 3 + j] = 0.0;
+                for (int o = 0; o <= N - 2; ++o) {
+                    dbias[(int64_t)o * D + d] = 0.0;
+                    for (int64_t t = 0; t < L; ++t) dh[((int64_t)o * D + d) * L + t] = 0.0;
+                }
+                for (int64_t b = 0; b < B; ++b) {
+                    /* forward, keeping every intermediate */
+                    for (int i = 0; i <= N; ++i) {
+                        const int64_t ch = (int64_t)i * D + d;
+                        double* dst = (i < N) ? xs + (int64_t)i * L : vs;
+                        oracle_short_conv_row(u + (b * C + ch) * L, w + ch * 3, L, dst);
+                    }
+                    for (int o = 0; o <= N - 2; ++o) {
+                        const double* x = xs + (int64_t)(N - 1 - o) * L;
+                        const double* vo = vs + (int64_t)o * L;
+                        double* g = gs + (int64_t)o * L;
+                        for (int64_t t = 0; t < L; ++t) g[t] = vo[t] * x[t];
+                        const float* hrow = h + ((int64_t)o * D + d) * L;
+                        for (int64_t t = 0; t < L; ++t) hk[t] = (double)hrow[t];
+                        if (mode == 0) oracle_causal_conv_direct(g, hk, L, c);
+                        else conv_fft_with(g, hk, L, n, fr, fi, ir, ii, scratch, c);
+                        const double bo = (double)bias[(int64_t)o * D + d];
+                        double* vn = vs + (int64_t)(o + 1) * L;
+                        for (int64_t t = 0; t < L; ++t) vn[t] = c[t] + bo * g[t];
+                    }
+                    /* final gate y = v_{N-1} * x_0 */
+                    const float* dyr = dy + (b * D + d) * L;
+                    const double* vl = vs + (int64_t)(N - 1) * L;
+                    for (int64_t t = 0; t < L; ++t) {
+                        a[t] = (double)dyr[t] * xs[t];
+                        duc[t] = (double)dyr[t] * vl[t];
+                    }
+                    /* the recurrence, last step first; a holds dv_{o+1} */
+                    for (int o = N - 2; o >= 0; --o) {
+                        const double* g = gs + (int64_t)o * L;
+                        const double* x = xs + (int64_t)(N - 1 - o) * L;
+                        const double* vo = vs + (int64_t)o * L;
+                        double sb = 0.0;
+                        for (int64_t t = 0; t < L; ++t) sb += a[t] * g[t];
+                        dbias[(int64_t)o * D + d] += sb;
+                        if (mode == 0) oracle_causal_corr_direct(a, g, L, c);
+                        else corr_fft_with(a, g, L, n, fr, fi, ir, ii, scratch, c);
+                        double* dho = dh + ((int64_t)o * D + d) * L;
+                        for (int64_t t = 0; t < L; ++t) dho[t] += c[t];
+                        const float* hrow = h + ((int64_t)o * D + d) * L;
+                        for (int64_t t = 0; t < L; ++t) hk[t] = (double)hrow[t];
+                        if (mode == 0) oracle_causal_corr_direct(a, hk, L, c);
+                        else corr_fft_with(a, hk, L, n, fr, fi, ir, ii, scratch, c);
+                        const double bo = (double)bias[(int64_t)o * D + d];
+                        double* dx = duc + (int64_t)(N - 1 - o) * L;
+                        for (int64_t t = 0; t < L; ++t) {
+                            const double dg = c[t] + bo * a[t];
+                            dx[t] = dg * vo[t];
+                            a[t] = dg * x[t];
+                        }
+                    }
+                    double* dv0 = duc + (int64_t)N * L;
+                    for (int64_t t = 0; t < L; ++t) dv0[t] = a[t];
+                    /* through the short convolution of every channel */
+                    for (int i = 0; i <= N; ++i) {
+                        const int64_t ch = (int64_t)i * D + d;
+                        const double* dc = duc + (int64_t)i * L;
+                        const float* ur = u + (b * C + ch) * L;
+                        const float* w3 = w + ch * 3;
+                        double* dur = du + (b * C + ch) * L;
+                        for (int64_t t = 0; t < L; ++t) {
+                            double s = 0.0;
+                            for (int j = 0; j < 3; ++j) {
+                                const int64_t q = t + 2 - j;
+                                if (q < L) s += (double)w3[j] * dc[q];
+                            }
+                            dur[t] = s;
+                        }
+                        for (int j = 0; j < 3; ++j) {
+                            double s = 0.0;
+                            for (int64_t t = 0; t < L; ++t) {
+                                const int64_t q = t - 2 + j;
+                                if (q >= 0) s += dc[t] * (double)ur[q];
+                            }
+                            dw[ch * 3 + j] += s;
+                        }
+                    }
+                }
             }
             free(buf);
         }
