@@ -24,7 +24,8 @@ _DTYPES = {"f32": HYENA_F32, "bf16": HYENA_BF16}
 # every symbol include/hyena.h declares
 EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_destroy", "hyena_plan_path",
            "hyena_spectrum_bytes", "hyena_workspace_bytes", "hyena_filter_spectrum", "hyena_forward",
-           "hyena_forward_timed", "hyena_fused_check", "hyena_status_string")
+           "hyena_forward_timed", "hyena_fused_check", "hyena_backward_workspace_bytes", "hyena_backward",
+           "hyena_status_string")
 
 
 class HyenaError(RuntimeError):
@@ -67,6 +68,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_forward_timed.restype = ci
     lib.hyena_fused_check.argtypes = [vp, vp, ctypes.POINTER(ci)]
     lib.hyena_fused_check.restype = ci
+    lib.hyena_backward_workspace_bytes.argtypes = [vp]
+    lib.hyena_backward_workspace_bytes.restype = sz
+    lib.hyena_backward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hyena_backward.restype = ci
     lib.hyena_status_string.argtypes = [ci]
     lib.hyena_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -177,6 +182,43 @@ class Plan:
                                             spec.data_ptr(), bias.data_ptr(), y.data_ptr(), ws_ptr or None,
                                             ws_bytes, _stream_handle(torch, self.device), ms))
         return dict(zip(("lds", "pass_a", "pass_b", "pass_c", "total"), [float(v) for v in ms]))
+
+    def backward_workspace_bytes(self) -> int:
+        return int(self.lib.hyena_backward_workspace_bytes(self.handle))
+
+    def backward(self, u_proj, short_w, spec, bias, dy, du=None, dw=None, dh=None, dbias=None, workspace=None):
+        """hyena_backward: gradients (du_proj [B,(N+1)D,L] io dtype, dshort_w [(N+1)D,3],
+        dh [N-1,D,L], dbias [N-1,D] fp32) of the forward for upstream gradient dy [B,D,L]."""
+        torch = self._torch
+        N, D, L = self.order, self.D, self.L
+        if u_proj.dim() != 3:
+            raise ValueError("u_proj must be [B, (N+1)*D, L]")
+        B = int(u_proj.shape[0])
+        self._need(u_proj, "u_proj", (B, (N + 1) * D, L), self.io_dtype)
+        self._need(short_w, "short_w", ((N + 1) * D, 3), torch.float32)
+        self._need(bias, "bias", (N - 1, D), torch.float32)
+        self._need(dy, "dy", (B, D, L), self.io_dtype)
+        if spec.device != self.device or spec.numel() * spec.element_size() < self.spectrum_bytes():
+            raise ValueError("spec must come from Plan.spectrum of an equal plan")
+        f32 = torch.float32
+        du = torch.empty((B, (N + 1) * D, L), dtype=self.io_dtype, device=self.device) if du is None else du
+        dw = torch.empty(((N + 1) * D, 3), dtype=f32, device=self.device) if dw is None else dw
+        dh = torch.empty((N - 1, D, L), dtype=f32, device=self.device) if dh is None else dh
+        dbias = torch.empty((N - 1, D), dtype=f32, device=self.device) if dbias is None else dbias
+        self._need(du, "du", (B, (N + 1) * D, L), self.io_dtype)
+        self._need(dw, "dw", ((N + 1) * D, 3), f32)
+        self._need(dh, "dh", (N - 1, D, L), f32)
+        self._need(dbias, "dbias", (N - 1, D), f32)
+        need = self.backward_workspace_bytes()
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        _check("hyena_backward",
+               self.lib.hyena_backward(self.handle, B, u_proj.data_ptr(), short_w.data_ptr(), spec.data_ptr(),
+                                       bias.data_ptr(), dy.data_ptr(), du.data_ptr(), dw.data_ptr(), dh.data_ptr(),
+                                       dbias.data_ptr(), ws_ptr, ws_bytes, _stream_handle(torch, self.device)))
+        return du, dw, dh, dbias
 
     def fused_check(self, workspace) -> int:
         """hyena_fused_check: nonzero if a bounded wait of the fused kernel expired

@@ -600,15 +600,27 @@ static hipError_t fs_spectrum_t(const float* h, float2* spec, int64_t rows, cons
     return hipGetLastError();
 }
 
-#define HY_FS_CASES(X)                                                                                    \
-    X(8, 4, 4) X(9, 4, 5) X(10, 5, 5) X(11, 5, 6) X(12, 6, 6) X(13, 6, 7) X(14, 7, 7) X(15, 7, 8) X(16, 8, 8) \
-        X(17, 8, 9) X(18, 9, 9) X(19, 9, 10) X(20, 9, 11)
+// log2 L -> (log2 L1, log2 L2). Square splits up to L1 = 512, whose pass A/C
+// tile (512 x 17 complex) still leaves room for two workgroups per CU.
+#ifndef HY_FS_LOG1_16
+#define HY_FS_LOG1_16 8
+#endif
+#ifndef HY_FS_LOG1_20
+#define HY_FS_LOG1_20 9
+#endif
+#define HY_FS_CASES(X)                                                                                   \
+    X(8, 4, 4) X(9, 4, 5) X(10, 5, 5) X(11, 5, 6) X(12, 6, 6) X(13, 6, 7) X(14, 7, 7) X(15, 7, 8)          \
+        X(16, HY_FS_LOG1_16, 16 - HY_FS_LOG1_16) X(17, 8, 9) X(18, 9, 9) X(19, 9, 10)                     \
+        X(20, HY_FS_LOG1_20, 20 - HY_FS_LOG1_20)
 
 void fs_split(int logL, int* log1, int* log2) {
-    int l1 = logL / 2;
-    if (l1 > 9) l1 = 9;
-    *log1 = l1;
-    *log2 = logL - l1;
+    switch (logL) {
+#define X(LG, A, B) \
+    case LG: *log1 = A; *log2 = B; return;
+        HY_FS_CASES(X)
+#undef X
+        default: *log1 = logL / 2; *log2 = logL - logL / 2;
+    }
 }
 
 hipError_t launch_fs_forward_chunk(int logL, const FsArgs& a, int64_t row0, int64_t nrows, hipStream_t st,

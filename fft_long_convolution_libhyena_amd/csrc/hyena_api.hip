@@ -11,23 +11,10 @@
 #include "../../include/hyena.h"
 #include "fft_core.hpp"
 #include "kernels.hpp"
+#include "plan.hpp"
 
-struct hyena_plan_s {
-    int64_t L = 0, D = 0;
-    int order = 0;
-    int logL = 0;
-    hyena_dtype_t dtype = HYENA_F32;
-    hyena_path_t path = HYENA_PATH_AUTO;
-    int device = -1;
-    int fused_blocks = 0;    // persistent grid of the fused path
-    float2* dtab = nullptr;  // all twiddle tables, one device allocation
-    // LDS path
-    const float2* tw = nullptr;
-    const float2* wpair = nullptr;
-    // four-step path
-    int log1 = 0, log2 = 0;
-    hy::FsTables fs{};
-};
+using hy::aligned16;
+using hy::check_device;
 
 namespace {
 
@@ -82,14 +69,6 @@ size_t stockham_size(int logn) {
     std::vector<float2> tmp;
     append_stockham(tmp, logn);
     return tmp.size();
-}
-
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-hyena_status_t check_device(const hyena_plan_t plan) {
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess) return HYENA_ERR_DEVICE;
-    return dev == plan->device ? HYENA_OK : HYENA_ERR_DEVICE;
 }
 
 int64_t chunk_rows(const hyena_plan_t plan, int64_t rows, size_t ws_bytes) {

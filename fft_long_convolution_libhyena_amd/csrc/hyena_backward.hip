@@ -1,0 +1,37 @@
+// C-ABI layer of the backward: argument checks and dispatch. See include/hyena.h
+// for the contract.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/hyena.h"
+#include "backward.hpp"
+#include "plan.hpp"
+
+extern "C" {
+
+size_t hyena_backward_workspace_bytes(hyena_plan_t plan) {
+    if (!plan || plan->path != HYENA_PATH_LDS) return 0;
+    return (size_t)hy::bwd_ws_per_channel(plan->L, plan->order) * (size_t)plan->D * sizeof(float2);
+}
+
+hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                              const void* spec, const float* bias, const void* dy, void* du_proj, float* dshort_w,
+                              float* dh, float* dbias, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    using hy::aligned16;
+    if (!plan || B < 1 || !u_proj || !short_w || !spec || !bias || !dy || !du_proj || !dshort_w || !dh || !dbias)
+        return HYENA_ERR_INVALID_ARG;
+    if (!aligned16(u_proj) || !aligned16(short_w) || !aligned16(spec) || !aligned16(bias) || !aligned16(dy) ||
+        !aligned16(du_proj) || !aligned16(dshort_w) || !aligned16(dh) || !aligned16(dbias))
+        return HYENA_ERR_INVALID_ARG;
+    if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 26)) return HYENA_ERR_INVALID_ARG;
+    if (plan->path != HYENA_PATH_LDS) return HYENA_ERR_UNSUPPORTED;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < hyena_backward_workspace_bytes(plan))
+        return HYENA_ERR_WORKSPACE;
+    if (hy::check_device(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
+    hy::LdsBwdArgs a{u_proj,   short_w,   (const float2*)spec, bias,      dy,         du_proj,
+                     dshort_w, dh,        dbias,               (float2*)workspace, plan->tw, plan->wpair,
+                     (int)B,   (int)plan->D, plan->order,       plan->dtype == HYENA_BF16};
+    return hy::launch_lds_backward(plan->logL, a, stream) == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
+}
+
+}  // extern "C"

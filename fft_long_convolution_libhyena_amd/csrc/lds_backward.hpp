@@ -1,0 +1,441 @@
+// Backward of the Hyena forward hot path on the LDS-resident path (L <= 16384),
+// for gfx950. Explicit instantiations live in lds_backward_*.hip.
+//
+// The forward (HyenaDNA walkthrough, section 2.1, HyenaOperator.forward; section
+// 2.2, HyenaFilter.forward and fftconv) is, per (b, d) row, with uc_i the short
+// conv of channel i*D + d, x_i = uc_i (i < N) and v_0 = uc_N:
+//   g_o = v_o * x_{N-1-o},  v_{o+1} = conv(g_o, h_o) + bias_o * g_o  (o = 0..N-2)
+//   y   = v_{N-1} * x_0.
+// Given dy, the chain rule gives (a = dv_{o+1} while step o is undone)
+//   dv_{N-1} = dy * x_0,  dx_0 = dy * v_{N-1}
+//   dh_o += corr(a, g_o),  dbias_o += <a, g_o>,  dg_o = corr(a, h_o) + bias_o * a
+//   dx_{N-1-o} = dg_o * v_o,  dv_o = dg_o * x_{N-1-o}
+//   du = conv3^T(duc),  dw_j += sum_t duc[t] u[t-2+j]
+// with corr(a, k)[t] = sum_{s>=t} k[s-t] a[s], the adjoint of the causal
+// convolution. In the frequency domain of the zero-padded 2L-point transform a
+// correlation is a product with a conjugate spectrum: dg_o comes from
+// A_dv * conj(H_o + bias_o) and dh_o from sum_b A_dv * conj(A_g).
+//
+// One workgroup owns one channel d and walks the batch, so every gradient of the
+// channel (dh, dbias, dw and the N+1 rows of du per b) is produced by that
+// workgroup alone: no atomics, and the batch sums are taken in a fixed order.
+// Per b it recomputes the forward chain on chip (2(N-1) transforms), then undoes
+// it (2(N-1) transforms); after the last b it inverts the N-1 accumulated
+// dh spectra.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "backward.hpp"
+#include "fft_core.hpp"
+#include "kernels.hpp"
+#include "pair.hpp"
+
+namespace hy {
+
+// The same pointer, made opaque to the optimiser by an empty asm statement (no
+// instruction is emitted): loads through the result are neither hoisted out of the
+// batch loop nor shared with an earlier phase, and values stored through one
+// phase's copy are not forwarded to another phase's loads. Otherwise every
+// twiddle, spectrum value, workspace value and re-read input row of the
+// workgroup would be kept live in registers from one phase to the next.
+template <class P>
+__device__ __forceinline__ P* fresh(P* p) {
+    uint32_t zero = 0;  // offsetting by an opaque zero keeps the global address space
+    asm volatile("" : "+s"(zero));
+    return p + zero;
+}
+
+// Scheduling fence between phases: keeps the loads of a later phase from being
+// issued (and held in registers) across an earlier transform.
+__device__ __forceinline__ void phase() { __builtin_amdgcn_sched_barrier(0); }
+
+// The thread index, made opaque in the same way at the start of every phase: the
+// LDS and global addresses derived from it are then computed where they are used
+// instead of once for the whole kernel (dozens of them would stay live).
+template <int T>
+__device__ __forceinline__ int fresh_tid(int t) {
+    asm volatile("" : "+v"(t));
+    __builtin_assume(t >= 0 && t < T);
+    return t;
+}
+
+// Filter spectrum (scaled) plus scaled bias at bins k and L-k; slot 0 of the
+// stored spectrum holds the two real bins 0 and L.
+__device__ __forceinline__ void spec_pair(const float2* __restrict__ Hs, uint32_t k, uint32_t km, float bs,
+                                          float2& Hk, float2& Hm) {
+    if (k == 0) {
+        const float2 h0 = Hs[0];
+        Hk = make_float2(h0.x + bs, 0.f);
+        Hm = make_float2(h0.y + bs, 0.f);
+    } else {
+        Hk = hadd(Hs[k], bs);
+        Hm = hadd(Hs[km], bs);
+    }
+}
+
+// Gradient through the short conv of one channel row. duc[e] holds the pair
+// (duc[2m], duc[2m+1]) at m = t + T*e. Writes du[2m], du[2m+1] and adds the
+// three tap sums into dws. The next pair comes through LDS.
+template <int L, int E, class TIO>
+__device__ __forceinline__ void short_conv_back(const RowAcc& acc, int t, const float2 (&duc)[E / 2],
+                                                const TIO* __restrict__ urow, const float* __restrict__ w,
+                                                TIO* __restrict__ durow, float (&dws)[3]) {
+    constexpr int H = E / 2, T = L / E;
+    phase();
+    t = fresh_tid<T>(t);
+    __syncthreads();  // the previous readers of LDS are done
+#pragma unroll
+    for (int e = 0; e < H; ++e) acc[t + T * e] = duc[e];
+    __syncthreads();
+    const float w0 = w[0], w1 = w[1], w2 = w[2];
+    const TIO* ur = fresh(urow);
+#pragma unroll
+    for (int e = 0; e < H; ++e) {
+        const uint32_t m = t + T * e;
+        const float2 nx = (m + 1 < (uint32_t)(L / 2)) ? acc[m + 1] : make_float2(0.f, 0.f);
+        const float2 dc = duc[e];
+        // du[t] = w2 duc[t] + w1 duc[t+1] + w0 duc[t+2]
+        store_pair(durow, m, make_float2(fmaf(w2, dc.x, fmaf(w1, dc.y, w0 * nx.x)),
+                                         fmaf(w2, dc.y, fmaf(w1, nx.x, w0 * nx.y))));
+        const float2 cur = load_pair(ur, m);
+        const float2 prev = m > 0 ? load_pair(ur, m - 1) : make_float2(0.f, 0.f);
+        // dw[j] += duc[2m] u[2m-2+j] + duc[2m+1] u[2m-1+j]
+        dws[0] = fmaf(dc.x, prev.x, fmaf(dc.y, prev.y, dws[0]));
+        dws[1] = fmaf(dc.x, prev.y, fmaf(dc.y, cur.x, dws[1]));
+        dws[2] = fmaf(dc.x, cur.x, fmaf(dc.y, cur.y, dws[2]));
+    }
+}
+
+// Workspace of one channel, in float2 units (see bwd_ws_per_channel):
+//   DH [N-1][L]    running batch sum of A_dv * conj(A_g), laid out like the spectrum
+//   G  [N-1][L]    unpacked spectra A_g of every step
+//   V  [N-2][L/2]  v_o of steps 1..N-2 as sample pairs
+// Every value is written and read back by the same thread.
+template <int LOGL, int N>
+struct BwdWs {
+    static constexpr int64_t L = int64_t(1) << LOGL;
+    static constexpr int64_t DH = 0;
+    static constexpr int64_t G = (N - 1) * L;
+    static constexpr int64_t V = G + (N - 1) * L;
+    static constexpr int64_t PER_D = V + (N - 2) * (L / 2);
+    static_assert(PER_D == (2 * N - 2) * L + (N - 2) * (L / 2), "matches bwd_ws_per_channel");
+};
+
+template <int LOGL, int N, class TIO>
+__global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS)
+k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const float2* __restrict__ spec,
+               const float* __restrict__ bias, const TIO* __restrict__ dy, TIO* __restrict__ du,
+               float* __restrict__ dw, float* __restrict__ dh, float* __restrict__ dbias, float2* __restrict__ ws,
+               const float2* __restrict__ tw, const float2* __restrict__ wpair, int B, int D) {
+    constexpr int L = 1 << LOGL;
+    constexpr int E = LdsCfg<LOGL>::E;
+    constexpr int H = E / 2;
+    constexpr int T = L / E;
+    constexpr int NV = 3 * (N + 1) + (N - 1);  // tap sums and bias sums per thread
+    static_assert(T * NV * 4 <= padded_len<L>() * 8, "reduction buffer fits in the transform's LDS");
+    using W = BwdWs<LOGL, N>;
+    __shared__ float2 lds[padded_len<L>()];
+    const RowAcc acc{lds};
+    const int d = blockIdx.x;
+    int t = threadIdx.x;
+    const int64_t C = (int64_t)(N + 1) * D;
+    float2* const wsd = ws + (int64_t)d * W::PER_D;
+    const float bscale = 1.0f / (4.0f * (float)L);
+
+    float dws[N + 1][3];
+    float dbs[N - 1];
+#pragma unroll
+    for (int i = 0; i <= N; ++i) dws[i][0] = dws[i][1] = dws[i][2] = 0.f;
+#pragma unroll
+    for (int o = 0; o < N - 1; ++o) dbs[o] = 0.f;
+
+    for (int b = 0; b < B; ++b) {
+        t = fresh_tid<T>(t);
+        const TIO* ub = u + (int64_t)b * C * L;
+        const TIO* urow[N + 1];
+#pragma unroll
+        for (int i = 0; i <= N; ++i) urow[i] = ub + ((int64_t)i * D + d) * L;
+        const float* wN = w3 + 3 * ((int64_t)N * D + d);
+
+        // ---------------------------------------------- forward chain, recomputed
+        float2 v[H];
+#pragma unroll
+        for (int e = 0; e < H; ++e) v[e] = conv3_pair(urow[N], (uint32_t)(t + T * e), wN[0], wN[1], wN[2]);
+#pragma unroll
+        for (int o = 0; o < N - 1; ++o) {
+            __builtin_amdgcn_sched_barrier(0);
+            t = fresh_tid<T>(t);
+            const int gi = N - 1 - o;
+            const float* wg = w3 + 3 * ((int64_t)gi * D + d);
+            if (o >= 1) {
+                float2* Vw = fresh(wsd) + W::V + (int64_t)(o - 1) * (L / 2);
+#pragma unroll
+                for (int e = 0; e < H; ++e) Vw[t + T * e] = v[e];
+            }
+            float2 f[E];
+            const TIO* xr = fresh(urow[gi]);
+#pragma unroll
+            for (int e = 0; e < H; ++e) f[e] = emul(v[e], conv3_pair(xr, (uint32_t)(t + T * e), wg[0], wg[1], wg[2]));
+#pragma unroll
+            for (int e = H; e < E; ++e) f[e] = make_float2(0.f, 0.f);
+            phase();
+            fft_strided<L, false, true>(f, t, fresh(tw), acc);
+            phase();
+            t = fresh_tid<T>(t);
+            __syncthreads();
+            lds_store_strided<T>(acc, t, f);
+            __syncthreads();
+            const float2* Hs = fresh(spec) + ((int64_t)o * D + d) * L;
+            const float2* wp = fresh(wpair);
+            const float bs = bias[(int64_t)o * D + d] * bscale;
+            float2* Gw = fresh(wsd) + W::G + (int64_t)o * L;
+#pragma unroll
+            for (int e = 0; e < H; ++e) {
+                const uint32_t k = t + T * e;
+                const uint32_t km = k == 0 ? 0 : L - k;
+                float2 Ak, Am, Hk, Hm, Yk, Ym;
+                const float2 wk = wp[k];
+                pair_unpack(acc[k], acc[km], wk, Ak, Am);
+                spec_pair(Hs, k, km, bs, Hk, Hm);
+                pair_repack(cmul(Ak, Hk), cmul(Am, Hm), wk, Yk, Ym);
+                acc[k] = Yk;
+                if (k != 0) acc[km] = Ym;
+                if (k != 0) {
+                    Gw[k] = Ak;
+                    Gw[km] = Am;
+                } else {
+                    Gw[0] = make_float2(Ak.x, Am.x);  // bins 0 and L are real
+                }
+            }
+            if (t == 0) {  // k = L/2 pairs with itself
+                const uint32_t k = L / 2;
+                float2 A, Am, Y, Yd;
+                pair_unpack(acc[k], acc[k], wp[k], A, Am);
+                const float2 Hh = hadd(Hs[k], bs);
+                pair_repack(cmul(A, Hh), cmul(A, Hh), wp[k], Y, Yd);
+                acc[k] = Y;
+                Gw[k] = A;
+            }
+            __syncthreads();
+            lds_load_strided<T>(acc, t, f);
+            phase();
+            fft_strided<L, true, false>(f, t, fresh(tw), acc);
+            phase();
+            t = fresh_tid<T>(t);
+#pragma unroll
+            for (int e = 0; e < H; ++e) v[e] = f[e];  // v_{o+1}
+        }
+
+        // --------------------------------------------------------------- backward
+        float2 a[H], dx[H];
+        {
+            const TIO* dyr = dy + ((int64_t)b * D + d) * L;
+            const float* w0p = w3 + 3 * (int64_t)d;
+            const TIO* x0r = fresh(urow[0]);
+#pragma unroll
+            for (int e = 0; e < H; ++e) {
+                const uint32_t m = t + T * e;
+                const float2 g = load_pair(dyr, m);
+                a[e] = emul(g, conv3_pair(x0r, m, w0p[0], w0p[1], w0p[2]));
+                dx[e] = emul(g, v[e]);
+            }
+            short_conv_back<L, E>(acc, t, dx, urow[0], w0p, du + ((int64_t)b * C + d) * L, dws[0]);
+        }
+#pragma unroll
+        for (int o = N - 2; o >= 0; --o) {
+            __builtin_amdgcn_sched_barrier(0);
+            t = fresh_tid<T>(t);
+            const int gi = N - 1 - o;
+            const float* wg = w3 + 3 * ((int64_t)gi * D + d);
+            // v_o and the gate x_{N-1-o} are fetched again after the transforms
+            // rather than held across them
+            auto value_at = [&](const TIO* vr, const float2* Vw, uint32_t m) {
+                return (o == 0) ? conv3_pair(vr, m, wN[0], wN[1], wN[2]) : Vw[m];
+            };
+            float sb = 0.f;
+            {
+                const TIO* vr = fresh(urow[N]);
+                const TIO* xr = fresh(urow[gi]);
+                const float2* Vw = fresh(wsd) + W::V + (int64_t)(o - 1) * (L / 2);
+#pragma unroll
+                for (int e = 0; e < H; ++e) {
+                    const uint32_t m = t + T * e;
+                    const float2 g = emul(value_at(vr, Vw, m), conv3_pair(xr, m, wg[0], wg[1], wg[2]));
+                    sb = fmaf(a[e].x, g.x, fmaf(a[e].y, g.y, sb));
+                }
+            }
+            dbs[o] += sb;
+            float2 f[E];
+#pragma unroll
+            for (int e = 0; e < H; ++e) f[e] = a[e];
+#pragma unroll
+            for (int e = H; e < E; ++e) f[e] = make_float2(0.f, 0.f);
+            phase();
+            fft_strided<L, false, true>(f, t, fresh(tw), acc);
+            phase();
+            t = fresh_tid<T>(t);
+            __syncthreads();
+            lds_store_strided<T>(acc, t, f);
+            __syncthreads();
+            const float2* Hs = fresh(spec) + ((int64_t)o * D + d) * L;
+            const float2* wp = fresh(wpair);
+            const float bs = bias[(int64_t)o * D + d] * bscale;
+            const float2* Gw = fresh(wsd) + W::G + (int64_t)o * L;
+            float2* DHw = fresh(wsd) + W::DH + (int64_t)o * L;
+#pragma unroll
+            for (int e = 0; e < H; ++e) {
+                const uint32_t k = t + T * e;
+                const uint32_t km = k == 0 ? 0 : L - k;
+                float2 Ak, Am, Hk, Hm, Yk, Ym, Gk, Gm;
+                const float2 wk = wp[k];
+                pair_unpack(acc[k], acc[km], wk, Ak, Am);
+                if (k != 0) {
+                    Gk = Gw[k];
+                    Gm = Gw[km];
+                } else {
+                    const float2 g0 = Gw[0];
+                    Gk = make_float2(g0.x, 0.f);
+                    Gm = make_float2(g0.y, 0.f);
+                }
+                float2 Pk = cmulc(Ak, Gk), Pm = cmulc(Am, Gm);
+                if (k != 0) {
+                    if (b > 0) {
+                        Pk = cadd(Pk, DHw[k]);
+                        Pm = cadd(Pm, DHw[km]);
+                    }
+                    DHw[k] = Pk;
+                    DHw[km] = Pm;
+                } else {
+                    float2 p0 = make_float2(Pk.x, Pm.x);
+                    if (b > 0) p0 = cadd(p0, DHw[0]);
+                    DHw[0] = p0;
+                }
+                spec_pair(Hs, k, km, bs, Hk, Hm);
+                pair_repack(cmulc(Ak, Hk), cmulc(Am, Hm), wk, Yk, Ym);
+                acc[k] = Yk;
+                if (k != 0) acc[km] = Ym;
+            }
+            if (t == 0) {
+                const uint32_t k = L / 2;
+                float2 A, Am, Y, Yd;
+                pair_unpack(acc[k], acc[k], wp[k], A, Am);
+                float2 P = cmulc(A, Gw[k]);
+                if (b > 0) P = cadd(P, DHw[k]);
+                DHw[k] = P;
+                const float2 Hh = hadd(Hs[k], bs);
+                pair_repack(cmulc(A, Hh), cmulc(A, Hh), wp[k], Y, Yd);
+                acc[k] = Y;
+            }
+            __syncthreads();
+            lds_load_strided<T>(acc, t, f);
+            phase();
+            fft_strided<L, true, false>(f, t, fresh(tw), acc);
+            phase();
+            t = fresh_tid<T>(t);
+            {
+                const TIO* vr = fresh(urow[N]);
+                const TIO* xr = fresh(urow[gi]);
+                const float2* Vw = fresh(wsd) + W::V + (int64_t)(o - 1) * (L / 2);
+#pragma unroll
+                for (int e = 0; e < H; ++e) {
+                    const uint32_t m = t + T * e;
+                    dx[e] = emul(f[e], value_at(vr, Vw, m));                      // dg * v_o
+                    a[e] = emul(f[e], conv3_pair(xr, m, wg[0], wg[1], wg[2]));  // dg * x_{N-1-o} = dv_o
+                }
+            }
+            short_conv_back<L, E>(acc, t, dx, urow[gi], wg, du + ((int64_t)b * C + (int64_t)gi * D + d) * L,
+                                  dws[gi]);
+        }
+        short_conv_back<L, E>(acc, t, a, urow[N], wN, du + ((int64_t)b * C + (int64_t)N * D + d) * L, dws[N]);
+    }
+
+    // ------------------------------------------- dh: invert the summed spectra
+    // repack + the unnormalised L-point inverse of X gives the 2L-point inverse of
+    // 2L*X; the products carry the factor 4 of the unpacked values: X = P / (8L)
+    const float sc = 1.0f / (8.0f * (float)L);
+#pragma unroll 1
+    for (int o = 0; o < N - 1; ++o) {
+        const float2* DHw = fresh(wsd) + W::DH + (int64_t)o * L;
+        t = fresh_tid<T>(t);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < H; ++e) {
+            const uint32_t k = t + T * e;
+            const uint32_t km = k == 0 ? 0 : L - k;
+            float2 Ck, Cm, Yk, Ym;
+            if (k != 0) {
+                Ck = fmul2(DHw[k], sc);
+                Cm = fmul2(DHw[km], sc);
+            } else {
+                const float2 p0 = DHw[0];
+                Ck = make_float2(p0.x * sc, 0.f);
+                Cm = make_float2(p0.y * sc, 0.f);
+            }
+            pair_repack(Ck, Cm, wpair[k], Yk, Ym);
+            acc[k] = Yk;
+            if (k != 0) acc[km] = Ym;
+        }
+        if (t == 0) {
+            const uint32_t k = L / 2;
+            const float2 P = fmul2(DHw[k], sc);
+            float2 Y, Yd;
+            pair_repack(P, P, wpair[k], Y, Yd);
+            acc[k] = Y;
+        }
+        __syncthreads();
+        float2 f[E];
+        lds_load_strided<T>(acc, t, f);
+        fft_strided<L, true, false>(f, t, tw, acc);
+        float* dhr = dh + ((int64_t)o * D + d) * L;
+#pragma unroll
+        for (int e = 0; e < H; ++e) store_pair(dhr, (uint32_t)(t + T * e), f[e]);
+    }
+
+    // --------------------------------------- tap and bias sums over the workgroup
+    float* red = reinterpret_cast<float*>(lds);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i <= N; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) red[(3 * i + j) * T + t] = dws[i][j];
+#pragma unroll
+    for (int o = 0; o < N - 1; ++o) red[(3 * (N + 1) + o) * T + t] = dbs[o];
+    __syncthreads();
+    for (int q = t; q < NV; q += T) {
+        float s = 0.f;
+        for (int r = 0; r < T; ++r) s += red[q * T + r];
+        if (q < 3 * (N + 1)) dw[((int64_t)(q / 3) * D + d) * 3 + (q % 3)] = s;
+        else dbias[(int64_t)(q - 3 * (N + 1)) * D + d] = s;
+    }
+}
+
+template <int LOGL, int N>
+inline void launch_lds_backward_n(const LdsBwdArgs& a, hipStream_t st) {
+    constexpr int T = LdsCfg<LOGL>::THREADS;
+    if (a.bf16)
+        hipLaunchKernelGGL((k_lds_backward<LOGL, N, uint16_t>), dim3((unsigned)a.D), dim3(T), 0, st,
+                           (const uint16_t*)a.u, a.w3, a.spec, a.bias, (const uint16_t*)a.dy, (uint16_t*)a.du,
+                           a.dw, a.dh, a.dbias, a.ws, a.tw, a.wpair, a.B, a.D);
+    else
+        hipLaunchKernelGGL((k_lds_backward<LOGL, N, float>), dim3((unsigned)a.D), dim3(T), 0, st,
+                           (const float*)a.u, a.w3, a.spec, a.bias, (const float*)a.dy, (float*)a.du, a.dw, a.dh,
+                           a.dbias, a.ws, a.tw, a.wpair, a.B, a.D);
+}
+
+template <int LOGL>
+hipError_t launch_lds_backward_t(const LdsBwdArgs& a, hipStream_t st) {
+    switch (a.N) {
+        case 2: launch_lds_backward_n<LOGL, 2>(a, st); break;
+        case 3: launch_lds_backward_n<LOGL, 3>(a, st); break;
+        case 4: launch_lds_backward_n<LOGL, 4>(a, st); break;
+        case 5: launch_lds_backward_n<LOGL, 5>(a, st); break;
+        case 6: launch_lds_backward_n<LOGL, 6>(a, st); break;
+        case 7: launch_lds_backward_n<LOGL, 7>(a, st); break;
+        case 8: launch_lds_backward_n<LOGL, 8>(a, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hy

@@ -1,0 +1,6 @@
+// Instantiations of the LDS-path backward for log2 L in {13}.
+#include "lds_backward.hpp"
+
+namespace hy {
+template hipError_t launch_lds_backward_t<13>(const LdsBwdArgs&, hipStream_t);
+}  // namespace hy

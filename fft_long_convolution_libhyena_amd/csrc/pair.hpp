@@ -23,21 +23,26 @@ __device__ __forceinline__ void pair_unpack(float2 Zk, float2 Zm, float2 w, floa
     Am = make_float2(Ep.x - P.x, P.y - Ep.y);  // conj(Ep - P)
 }
 
-// Spectrum multiply and repack for the inverse. Hk, Hm are the scaled filter
-// spectrum plus scaled bias at k and L-k. With C = A*H:
+// Repack of a real signal's 2L-point spectrum values C[k], C[L-k] into the
+// packed L-point spectrum that the inverse transform takes:
 //   Y[k] = Ec + i Oc, Ec = (C[k] + conj C[L-k])/2, Oc = (C[k] - conj C[L-k]) W^-k / 2,
 //   Y[L-k] = conj(Ec) + i conj(Oc).
-__device__ __forceinline__ void pair_conv(float2 Zk, float2 Zm, float2 Hk, float2 Hm, float2 w, float2& Yk,
-                                          float2& Ym) {
-    float2 Ak, Am;
-    pair_unpack(Zk, Zm, w, Ak, Am);
-    const float2 Ck = cmul(Ak, Hk);
-    const float2 Cm = cmul(Am, Hm);
+// (Computed without the halves: the scale is folded into the stored spectra.)
+__device__ __forceinline__ void pair_repack(float2 Ck, float2 Cm, float2 w, float2& Yk, float2& Ym) {
     const float2 Ec = make_float2(Ck.x + Cm.x, Ck.y - Cm.y);
     const float2 Dc = make_float2(Ck.x - Cm.x, Ck.y + Cm.y);
     const float2 Oc = cmulc(Dc, w);
     Yk = make_float2(Ec.x - Oc.y, Ec.y + Oc.x);
     Ym = make_float2(Ec.x + Oc.y, Oc.x - Ec.y);
+}
+
+// Spectrum multiply and repack for the inverse. Hk, Hm are the scaled filter
+// spectrum plus scaled bias at k and L-k; C = A*H.
+__device__ __forceinline__ void pair_conv(float2 Zk, float2 Zm, float2 Hk, float2 Hm, float2 w, float2& Yk,
+                                          float2& Ym) {
+    float2 Ak, Am;
+    pair_unpack(Zk, Zm, w, Ak, Am);
+    pair_repack(cmul(Ak, Hk), cmul(Am, Hm), w, Yk, Ym);
 }
 
 __device__ __forceinline__ float2 fmul2(float2 a, float s) { return make_float2(a.x * s, a.y * s); }

@@ -1,0 +1,38 @@
+// The plan object behind hyena_plan_t and small host helpers shared by the
+// C-ABI translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/hyena.h"
+#include "kernels.hpp"
+
+struct hyena_plan_s {
+    int64_t L = 0, D = 0;
+    int order = 0;
+    int logL = 0;
+    hyena_dtype_t dtype = HYENA_F32;
+    hyena_path_t path = HYENA_PATH_AUTO;
+    int device = -1;
+    int fused_blocks = 0;    // persistent grid of the fused path
+    float2* dtab = nullptr;  // all twiddle tables, one device allocation
+    // LDS path
+    const float2* tw = nullptr;
+    const float2* wpair = nullptr;
+    // four-step path
+    int log1 = 0, log2 = 0;
+    hy::FsTables fs{};
+};
+
+namespace hy {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The plan's device must be the current one.
+inline hyena_status_t check_device(const hyena_plan_t plan) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return HYENA_ERR_DEVICE;
+    return dev == plan->device ? HYENA_OK : HYENA_ERR_DEVICE;
+}
+
+}  // namespace hy

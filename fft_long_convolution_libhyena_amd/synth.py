@@ -140,6 +140,27 @@ def generate(wl: Workload, seed: Optional[int] = None) -> Inputs:
                   np.ascontiguousarray(h), np.ascontiguousarray(bias))
 
 
+def upstream_grad(wl: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """A seeded upstream gradient dy [B, D, L] ~ N(0, 1) for the backward, drawn from its
+    own PCG64 stream (seed + 1000 by default) and rounded to bf16 for bf16 workloads."""
+    rng = np.random.Generator(np.random.PCG64((wl.seed if seed is None else seed) + 1000))
+    dy = rng.standard_normal((wl.B, wl.D, wl.L), dtype=np.float32)
+    return np.ascontiguousarray(round_to_bf16(dy) if wl.dtype == "bf16" else dy)
+
+
+def channel_subset(x: Inputs, ds) -> Inputs:
+    """The inputs restricted to channels ds of every channel group (gates, value,
+    filters, biases): the hot path treats channels independently, so a subset is a
+    smaller instance of the same problem."""
+    wl = x.wl
+    ds = np.asarray(ds, dtype=np.int64)
+    N, D = wl.order, wl.D
+    cols = np.concatenate([i * D + ds for i in range(N + 1)])
+    sub = dataclasses.replace(wl, name=wl.name + f"[{len(ds)}ch]", D=int(len(ds)))
+    return Inputs(sub, np.ascontiguousarray(x.u_proj[:, cols]), np.ascontiguousarray(x.short_w[cols]),
+                  np.ascontiguousarray(x.h[:, ds]), np.ascontiguousarray(x.bias[:, ds]))
+
+
 def sample_rows(wl: Workload, count: int, seed: int = 12345) -> np.ndarray:
     """A seeded, sorted sample of flat row indices b*D + d (always includes the first and last)."""
     total = wl.B * wl.D

@@ -1,5 +1,6 @@
 /*
- * libhyena — the Hyena operator forward hot path on AMD MI355X (gfx950).
+ * libhyena — the Hyena operator forward hot path, and its backward, on AMD
+ * MI355X (gfx950).
  *
  * The operator (HyenaDNA walkthrough, section 2.1, HyenaOperator.forward):
  *   uc  = ShortConv(u_proj)[..., :L]    depthwise Conv1d, 3 taps, padding 2
@@ -161,6 +162,41 @@ hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_p
  * the 1 KiB control block to the host synchronously. *flag = 0 on other paths. Errors:
  * HYENA_ERR_INVALID_ARG for NULL arguments, HYENA_ERR_DEVICE if the copy fails. */
 hyena_status_t hyena_fused_check(hyena_plan_t plan, const void* workspace, int* flag);
+
+/* Bytes of workspace hyena_backward needs for this plan (independent of B):
+ * per channel, the N-1 running dh spectra, the gated-input spectra of the N-1
+ * steps and the values v_1..v_{N-2}, i.e. 8 * D * ((2N-2)*L + (N-2)*L/2).
+ * Returns 0 for a NULL plan or a plan whose path has no backward (FOURSTEP). */
+size_t hyena_backward_workspace_bytes(hyena_plan_t plan);
+
+/* Backward of the forward hot path: given the upstream gradient dy of y, the
+ * gradients of the same scalar loss with respect to u_proj, short_w, the long
+ * filters h (time domain, i.e. through hyena_filter_spectrum) and bias. They
+ * follow from the forward's definitions (HyenaDNA walkthrough, section 2.1,
+ * HyenaOperator.forward; section 2.2, HyenaFilter.forward and fftconv) by the
+ * chain rule; the adjoint of the causal convolution with h is the correlation
+ * corr(a, h)[t] = sum_{s >= t} h[s-t] a[s], taken through the same zero-padded
+ * 2L-point spectra with the filter spectrum conjugated.
+ *   u_proj, short_w, spec, bias: the forward's inputs (spec from
+ *           hyena_filter_spectrum of this plan)
+ *   dy      [B][D][L] of the plan dtype, device
+ *   du_proj [B][(N+1)*D][L] of the plan dtype, device (output; bf16 rounded to
+ *           nearest even)
+ *   dshort_w [(N+1)*D][3] fp32, dh [N-1][D][L] fp32, dbias [N-1][D] fp32, device
+ *           (outputs; the batch sums are complete, not accumulated into the
+ *           buffers' previous contents)
+ *   workspace / workspace_bytes: device scratch of at least
+ *           hyena_backward_workspace_bytes(plan); contents on entry irrelevant.
+ * Only the LDS path (L <= 16384) has a backward in this build; other plans get
+ * HYENA_ERR_UNSUPPORTED. One workgroup per channel walks the batch, so every
+ * sum is taken in a fixed order and results are bitwise reproducible.
+ * Enqueued on `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL or misaligned
+ * pointers, B < 1), HYENA_ERR_UNSUPPORTED, HYENA_ERR_WORKSPACE,
+ * HYENA_ERR_DEVICE (launch failure, wrong current device). Outputs must not
+ * alias inputs or each other. */
+hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                              const void* spec, const float* bias, const void* dy, void* du_proj, float* dshort_w,
+                              float* dh, float* dbias, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* hyena_status_string(hyena_status_t s);

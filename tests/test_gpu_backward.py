@@ -1,0 +1,145 @@
+"""GPU parity of the backward (hyena_backward, LDS path) against the fp64 oracle.
+
+Every gradient (du_proj, dshort_w, dh, dbias) is compared with the oracle's by
+relative L2: 1e-4 when u_proj/dy/du are fp32, and for bf16 I/O 1e-2 on du_proj
+(rounded to bf16 on output) and 1e-4 on the fp32 parameter gradients, which the
+kernel sums in fp32 from the same bf16 input values the oracle receives.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fft_long_convolution_libhyena_amd import synth
+from tests._hy import say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fft_long_convolution_libhyena_amd import load_library
+
+    load_library()
+    yield
+
+
+def _run_backward(x, dy, repeat=1):
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan
+
+    wl = x.wl
+    t = to_device(x)
+    dev = t["u"].device
+    g = torch.from_numpy(dy).to(dev)
+    if wl.dtype == "bf16":
+        g = g.to(torch.bfloat16)
+    outs = []
+    with Plan(wl.L, wl.D, wl.order, wl.dtype, "lds") as p:
+        spec = p.spectrum(t["h"])
+        for _ in range(repeat):
+            outs.append(p.backward(t["u"], t["w"], spec, t["bias"], g.contiguous()))
+        torch.cuda.synchronize()
+    return outs
+
+
+def _compare(x, dy, label, mode="fft"):
+    wl = x.wl
+    say(f"[backward] {label}: {wl.describe()}")
+    (du, dw, dh, db), = _run_backward(x, dy)
+    ref = oracle.backward(x.u_proj, x.short_w, x.h, x.bias, dy, wl.order, mode=mode)
+    got = [a.float().cpu().numpy().astype(np.float64) for a in (du, dw, dh, db)]
+    bounds = [1e-2 if wl.dtype == "bf16" else 1e-4, 1e-4, 1e-4, 1e-4]
+    for name, g, r, bound in zip(("du_proj", "dshort_w", "dh", "dbias"), got, ref, bounds):
+        assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+        err = oracle.rel_l2(g, r)
+        say(f"   {name:9s} rel_l2={err:.3e} (bound {bound:.0e})")
+        assert err <= bound, f"{name}: rel L2 {err:.3e} exceeds {bound:.0e}"
+    # per-channel check of du: a wrong channel hides easily in a global norm
+    g2 = got[0].reshape(-1, wl.L)
+    r2 = ref[0].reshape(-1, wl.L)
+    row = np.linalg.norm(g2 - r2, axis=1) / np.maximum(np.linalg.norm(r2, axis=1), 1e-30)
+    assert row.max() <= 10 * bounds[0], f"worst du row rel L2 {row.max():.3e}"
+
+
+SMALL = [
+    # B, D, L, order, dtype: every LDS size class, E = 16 and 32, orders 2..8, ragged D
+    (1, 1, 16, 2, "f32"),
+    (2, 3, 32, 3, "f32"),
+    (3, 5, 64, 2, "f32"),
+    (2, 4, 256, 4, "f32"),
+    (2, 7, 1024, 2, "f32"),
+    (1, 3, 2048, 5, "f32"),
+    (2, 4, 4096, 2, "f32"),
+    (2, 3, 8192, 2, "f32"),
+    (2, 2, 16384, 2, "f32"),
+    (1, 2, 16384, 3, "f32"),
+    (2, 2, 512, 8, "f32"),
+    (2, 5, 1024, 2, "bf16"),
+    (2, 3, 8192, 3, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,D,L,order,dtype", SMALL)
+def test_backward_small_shapes(B, D, L, order, dtype):
+    wl = synth.custom(B, D, L, order, dtype, seed=B * 1000 + D * 10 + order)
+    x = synth.generate(wl)
+    _compare(x, synth.upstream_grad(wl), f"small {B}x{D}x{L} N={order} {dtype}",
+             mode="direct" if L <= 256 else "fft")
+
+
+@pytest.mark.parametrize("name,nch", [("lm125m", 3), ("dna_small", 3), ("tiny", 64)])
+def test_backward_workload_channels(name, nch):
+    """Full-size rows of a workload (every b, all of L) on sampled channels: channels
+    are independent, so the oracle runs on the channel subset while the GPU runs the
+    subset too at the workload's B, L and dtype."""
+    wl = synth.WORKLOADS[name]
+    x = synth.generate(wl)
+    ds = np.unique(np.r_[0, wl.D - 1, np.random.default_rng(5).choice(wl.D, size=max(nch - 2, 0), replace=False)])
+    xs = synth.channel_subset(x, ds[:nch])
+    dy = synth.upstream_grad(xs.wl)
+    _compare(xs, dy, f"{name} channels {list(ds[:nch])}")
+
+
+def test_backward_is_deterministic():
+    wl = synth.custom(3, 6, 4096, 3, seed=21)
+    x = synth.generate(wl)
+    dy = synth.upstream_grad(wl)
+    a, b = _run_backward(x, dy, repeat=2)
+    for ta, tb in zip(a, b):
+        assert bool((ta == tb).all()), "two backward calls differ"
+
+
+def test_backward_zero_upstream_gives_zero():
+    wl = synth.custom(2, 4, 2048, 2, seed=3)
+    x = synth.generate(wl)
+    (du, dw, dh, db), = _run_backward(x, np.zeros((wl.B, wl.D, wl.L), np.float32))
+    for t in (du, dw, dh, db):
+        assert float(t.abs().max()) == 0.0
+
+
+def test_backward_rejects_fourstep_plan_and_small_workspace():
+    import torch
+
+    from fft_long_convolution_libhyena_amd import HyenaError, Plan
+
+    wl = synth.custom(1, 2, 1024, 2, seed=4)
+    x = synth.generate(wl)
+    t = to_device(x)
+    g = torch.zeros((1, 2, 1024), dtype=torch.float32, device=t["u"].device)
+    with Plan(1024, 2, 2, "f32", "fourstep") as p:
+        spec = p.spectrum(t["h"])
+        assert p.backward_workspace_bytes() == 0
+        with pytest.raises(HyenaError) as e:
+            p.backward(t["u"], t["w"], spec, t["bias"], g, workspace=torch.empty(16, dtype=torch.uint8,
+                                                                             device=g.device))
+        assert e.value.status == 2  # HYENA_ERR_UNSUPPORTED
+    with Plan(1024, 2, 2, "f32", "lds") as p:
+        spec = p.spectrum(t["h"])
+        small = torch.empty(p.backward_workspace_bytes() - 256, dtype=torch.uint8, device=g.device)
+        with pytest.raises(HyenaError) as e:
+            p.backward(t["u"], t["w"], spec, t["bias"], g, workspace=small)
+        assert e.value.status == 3  # HYENA_ERR_WORKSPACE
