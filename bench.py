@@ -15,7 +15,6 @@ Prints ONE JSON line:
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -50,6 +49,15 @@ def alg_bytes_forward(wl) -> int:
             + 4 * (N + 1) * D * 3 + 4 * (N - 1) * D)
 
 
+def alg_bytes_backward(wl) -> int:
+    """One read of u_proj, dy, the filter spectrum and the small parameters; one
+    write of du_proj, dh, dbias and dshort_w."""
+    s = io_bytes(wl)
+    B, D, L, N = wl.B, wl.D, wl.L, wl.order
+    return (2 * s * B * (N + 1) * D * L + s * B * D * L + 8 * (N - 1) * D * (L + 1) + 4 * (N - 1) * D * L
+            + 2 * (4 * (N + 1) * D * 3 + 4 * (N - 1) * D))
+
+
 def alg_bytes_pass(wl, family: str) -> int:
     """Bytes each four-step pass must move by design, per forward (all rows):
     pass A reads two u_proj rows and writes the L-point complex tile; pass B
@@ -76,10 +84,14 @@ KERNEL_SOURCES = {
     "lds": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "lds_path.hpp", "lds_path_a.hip", "lds_path_b.hip",
             "lds_path_c.hip", "lds_path_d.hip", "hyena_api.hip"],
     "fourstep": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "fourstep.hip", "hyena_api.hip"],
+    "backward": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "backward.hpp", "lds_backward.hpp", "lds_backward_a.hip",
+                 "lds_backward_b.hip", "lds_backward_c.hip", "lds_backward_d.hip", "hyena_backward.hip"],
 }
 
 
 def kernel_family(kernel: str) -> str:
+    if kernel == "k_lds_backward":
+        return "backward"
     return "lds" if kernel.startswith("k_lds") else "fourstep"
 
 
@@ -135,6 +147,102 @@ def cpu_baseline(x, wl, budget_s: float):
                       f"convolution, OpenMP over rows, {dt:.1f} s wall"}
 
 
+def cpu_baseline_backward(x, wl, budget_s: float):
+    """The fp64 backward oracle (FFT mode) on a bounded, seeded sample of channels
+    (all b and t of each); channels are independent, so this is a smaller instance."""
+    import oracle
+    from fft_long_convolution_libhyena_amd import synth
+
+    threads = oracle.max_threads()
+    rng = np.random.default_rng(99)
+    n = max(1, min(wl.D, threads))
+    while True:
+        ds = np.sort(rng.choice(wl.D, size=n, replace=False))
+        xs = synth.channel_subset(x, ds)
+        dy = synth.upstream_grad(xs.wl)
+        t0 = time.perf_counter()
+        oracle.backward(xs.u_proj, xs.short_w, xs.h, xs.bias, dy, wl.order, mode="fft")
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n >= wl.D:
+            break
+        n = int(min(wl.D, max(n + 1, n * budget_s / max(dt, 1e-3) * 0.8)))
+    return {"value": wl.B * n * wl.L / dt, "unit": "channel-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {wl.D} channels (all {wl.B} batch rows, all L) of the same inputs, fp64 radix-2 "
+                      f"FFT backward, OpenMP over channels, {dt:.1f} s wall"}
+
+
+def bench_backward(args, wl, x, torch, Plan):
+    from fft_long_convolution_libhyena_amd import synth
+
+    dev = torch.device("cuda", 0)
+    iot = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    u = torch.from_numpy(x.u_proj).to(dev).to(iot).contiguous()
+    w = torch.from_numpy(x.short_w).to(dev)
+    h = torch.from_numpy(x.h).to(dev)
+    bias = torch.from_numpy(x.bias).to(dev)
+    dy = torch.from_numpy(synth.upstream_grad(wl)).to(dev).to(iot).contiguous()
+    plan = Plan(wl.L, wl.D, wl.order, wl.dtype, "lds")
+    spec = plan.spectrum(h)
+    ws = torch.empty(plan.backward_workspace_bytes(), dtype=torch.uint8, device=dev)
+    N, D, L, B = wl.order, wl.D, wl.L, wl.B
+    outs = (torch.empty((B, (N + 1) * D, L), dtype=iot, device=dev),
+            torch.empty(((N + 1) * D, 3), dtype=torch.float32, device=dev),
+            torch.empty((N - 1, D, L), dtype=torch.float32, device=dev),
+            torch.empty((N - 1, D), dtype=torch.float32, device=dev))
+    log(f"[bench] backward workspace {ws.numel() / 2**20:.1f} MiB")
+
+    def step():
+        plan.backward(u, w, spec, bias, dy, *outs, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for rep in range(args.reps):
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / args.steps)
+        log(f"[bench] rep {rep}: {times[-1] * 1e3:.1f} us/step")
+    ms = float(np.median(times))
+    nbytes = alg_bytes_backward(wl)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "channel-tokens/s (B·D·L/s) and % HBM peak, Hyena op backward (gradients of u_proj, short_w, "
+                  "h, bias)",
+        "value": B * D * L / (ms * 1e-3), "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if wl.dtype == "f32" else "bf16-io/f32",
+        "data": f"synthetic seeded ({wl.kind} activations, N(0,1) upstream gradient)",
+        "config": {"workload": wl.name, "B": B, "D": D, "L": L, "order": N, "io_dtype": wl.dtype,
+                   "path": "lds", "pass": "backward"},
+        # the step is one launch of k_lds_backward: the timed region gives its duration
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("k_lds_backward",
+                                                                                             wl.name),
+                     "kernel": "k_lds_backward", "alg_bytes_per_launch": nbytes, "launch_ms": round(ms, 5),
+                     "launches_per_step": 1},
+    }
+    if args.check:
+        import oracle
+
+        ds = [0, D // 2, D - 1]
+        xs = synth.channel_subset(x, ds)
+        ref = oracle.backward(xs.u_proj, xs.short_w, xs.h, xs.bias, synth.upstream_grad(wl)[:, ds], N)
+        got = outs[0].float().cpu().numpy().reshape(B, N + 1, D, L)[:, :, ds].reshape(B, -1, L)
+        out["check_rel_l2_du"] = oracle.rel_l2(got, ref[0])
+        log(f"[bench] oracle check of du on channels {ds}: rel_l2 {out['check_rel_l2_du']:.3e}")
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (backward oracle) ...")
+        out["cpu_baseline"] = cpu_baseline_backward(x, wl, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    plan.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +255,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--check", action="store_true", help="also compare sampled rows with the oracle")
+    ap.add_argument("--backward", action="store_true",
+                    help="time hyena_backward instead of the forward (LDS-path workloads, L <= 16384)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -168,6 +278,12 @@ def main():
     t0 = time.perf_counter()
     x = synth.generate(wl)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    if args.backward:
+        if wl.L > 16384:
+            print("the backward runs on the LDS path only (L <= 16384)", file=sys.stderr)
+            sys.exit(2)
+        bench_backward(args, wl, x, torch, Plan)
+        return
     dev = torch.device("cuda", 0)
     u = torch.from_numpy(x.u_proj).to(dev)
     if wl.dtype == "bf16":

@@ -23,9 +23,9 @@ struct LdsBwdArgs {
 };
 
 // float2 values of backward workspace per channel: the N-1 running dh spectra,
-// the unpacked gated-input spectra of the N-1 steps and the values v_1..v_{N-2}.
+// the unpacked gated-input spectra of steps 0..N-3 and the values v_1..v_{N-2}.
 inline int64_t bwd_ws_per_channel(int64_t L, int N) {
-    return (int64_t)(2 * N - 2) * L + (int64_t)(N - 2) * (L / 2);
+    return (int64_t)(2 * N - 3) * L + (int64_t)(N - 2) * (L / 2);
 }
 
 hipError_t launch_lds_backward(int logL, const LdsBwdArgs& a, hipStream_t st);

@@ -8,7 +8,7 @@
 //   y   = v_{N-1} * x_0.
 // Given dy, the chain rule gives (a = dv_{o+1} while step o is undone)
 //   dv_{N-1} = dy * x_0,  dx_0 = dy * v_{N-1}
-//   dh_o += corr(a, g_o),  dbias_o += <a, g_o>,  dg_o = corr(a, h_o) + bias_o * a
+//   dh_o += corr(a, g_o),  dbias_o += <a, g_o> = corr(a, g_o)[0],  dg_o = corr(a, h_o) + bias_o * a
 //   dx_{N-1-o} = dg_o * v_o,  dv_o = dg_o * x_{N-1-o}
 //   du = conv3^T(duc),  dw_j += sum_t duc[t] u[t-2+j]
 // with corr(a, k)[t] = sum_{s>=t} k[s-t] a[s], the adjoint of the causal
@@ -60,6 +60,10 @@ __device__ __forceinline__ int fresh_tid(int t) {
     return t;
 }
 
+// Materialises a running sum where it is written: without it the compiler sinks
+// the arithmetic past the next transform and keeps all its inputs live there.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 // Filter spectrum (scaled) plus scaled bias at bins k and L-k; slot 0 of the
 // stored spectrum holds the two real bins 0 and L.
 __device__ __forceinline__ void spec_pair(const float2* __restrict__ Hs, uint32_t k, uint32_t km, float bs,
@@ -74,13 +78,13 @@ __device__ __forceinline__ void spec_pair(const float2* __restrict__ Hs, uint32_
     }
 }
 
-// Gradient through the short conv of one channel row. duc[e] holds the pair
-// (duc[2m], duc[2m+1]) at m = t + T*e. Writes du[2m], du[2m+1] and adds the
-// three tap sums into dws. The next pair comes through LDS.
+// Input gradient through the short conv of one channel row:
+// du[t] = w2 duc[t] + w1 duc[t+1] + w0 duc[t+2]. duc[e] holds the pair
+// (duc[2m], duc[2m+1]) at m = t + T*e; the pairs go through LDS (each thread
+// then reads its own pair and the next one back, so duc need not stay live).
 template <int L, int E, class TIO>
 __device__ __forceinline__ void short_conv_back(const RowAcc& acc, int t, const float2 (&duc)[E / 2],
-                                                const TIO* __restrict__ urow, const float* __restrict__ w,
-                                                TIO* __restrict__ durow, float (&dws)[3]) {
+                                                const float* __restrict__ w, TIO* __restrict__ durow) {
     constexpr int H = E / 2, T = L / E;
     phase();
     t = fresh_tid<T>(t);
@@ -88,28 +92,37 @@ __device__ __forceinline__ void short_conv_back(const RowAcc& acc, int t, const 
 #pragma unroll
     for (int e = 0; e < H; ++e) acc[t + T * e] = duc[e];
     __syncthreads();
+    phase();
+    t = fresh_tid<T>(t);
     const float w0 = w[0], w1 = w[1], w2 = w[2];
-    const TIO* ur = fresh(urow);
 #pragma unroll
     for (int e = 0; e < H; ++e) {
         const uint32_t m = t + T * e;
+        const float2 dc = acc[m];
         const float2 nx = (m + 1 < (uint32_t)(L / 2)) ? acc[m + 1] : make_float2(0.f, 0.f);
-        const float2 dc = duc[e];
-        // du[t] = w2 duc[t] + w1 duc[t+1] + w0 duc[t+2]
         store_pair(durow, m, make_float2(fmaf(w2, dc.x, fmaf(w1, dc.y, w0 * nx.x)),
                                          fmaf(w2, dc.y, fmaf(w1, nx.x, w0 * nx.y))));
-        const float2 cur = load_pair(ur, m);
-        const float2 prev = m > 0 ? load_pair(ur, m - 1) : make_float2(0.f, 0.f);
-        // dw[j] += duc[2m] u[2m-2+j] + duc[2m+1] u[2m-1+j]
-        dws[0] = fmaf(dc.x, prev.x, fmaf(dc.y, prev.y, dws[0]));
-        dws[1] = fmaf(dc.x, prev.y, fmaf(dc.y, cur.x, dws[1]));
-        dws[2] = fmaf(dc.x, cur.x, fmaf(dc.y, cur.y, dws[2]));
     }
+}
+
+// Raw samples (2m-2, 2m-1) and (2m, 2m+1) of a channel row.
+template <class TIO>
+__device__ __forceinline__ void raw_pairs(const TIO* __restrict__ row, uint32_t m, float2& prev, float2& cur) {
+    cur = load_pair(row, m);
+    prev = m > 0 ? load_pair(row, m - 1) : make_float2(0.f, 0.f);
+}
+
+// Tap gradients of the short conv: dw[j] += duc[2m] u[2m-2+j] + duc[2m+1] u[2m-1+j].
+__device__ __forceinline__ void tap_sums(float2 dc, float2 prev, float2 cur, float (&dws)[3]) {
+    dws[0] = fmaf(dc.x, prev.x, fmaf(dc.y, prev.y, dws[0]));
+    dws[1] = fmaf(dc.x, prev.y, fmaf(dc.y, cur.x, dws[1]));
+    dws[2] = fmaf(dc.x, cur.x, fmaf(dc.y, cur.y, dws[2]));
 }
 
 // Workspace of one channel, in float2 units (see bwd_ws_per_channel):
 //   DH [N-1][L]    running batch sum of A_dv * conj(A_g), laid out like the spectrum
-//   G  [N-1][L]    unpacked spectra A_g of every step
+//   G  [N-2][L]    unpacked spectra A_g of steps o < N-2 (the last step's stays in
+//                  registers, from the recomputed forward to the undoing of that step)
 //   V  [N-2][L/2]  v_o of steps 1..N-2 as sample pairs
 // Every value is written and read back by the same thread.
 template <int LOGL, int N>
@@ -117,9 +130,9 @@ struct BwdWs {
     static constexpr int64_t L = int64_t(1) << LOGL;
     static constexpr int64_t DH = 0;
     static constexpr int64_t G = (N - 1) * L;
-    static constexpr int64_t V = G + (N - 1) * L;
+    static constexpr int64_t V = G + (N - 2) * L;
     static constexpr int64_t PER_D = V + (N - 2) * (L / 2);
-    static_assert(PER_D == (2 * N - 2) * L + (N - 2) * (L / 2), "matches bwd_ws_per_channel");
+    static_assert(PER_D == (2 * N - 3) * L + (N - 2) * (L / 2), "matches bwd_ws_per_channel");
 };
 
 template <int LOGL, int N, class TIO>
@@ -132,7 +145,7 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
     constexpr int E = LdsCfg<LOGL>::E;
     constexpr int H = E / 2;
     constexpr int T = L / E;
-    constexpr int NV = 3 * (N + 1) + (N - 1);  // tap sums and bias sums per thread
+    constexpr int NV = 3 * (N + 1);  // tap sums per thread
     static_assert(T * NV * 4 <= padded_len<L>() * 8, "reduction buffer fits in the transform's LDS");
     using W = BwdWs<LOGL, N>;
     __shared__ float2 lds[padded_len<L>()];
@@ -144,11 +157,8 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
     const float bscale = 1.0f / (4.0f * (float)L);
 
     float dws[N + 1][3];
-    float dbs[N - 1];
 #pragma unroll
     for (int i = 0; i <= N; ++i) dws[i][0] = dws[i][1] = dws[i][2] = 0.f;
-#pragma unroll
-    for (int o = 0; o < N - 1; ++o) dbs[o] = 0.f;
 
     for (int b = 0; b < B; ++b) {
         t = fresh_tid<T>(t);
@@ -162,6 +172,8 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
         float2 v[H];
 #pragma unroll
         for (int e = 0; e < H; ++e) v[e] = conv3_pair(urow[N], (uint32_t)(t + T * e), wN[0], wN[1], wN[2]);
+        float2 ga[H], gb[H];  // A_g at k and L-k of the last step
+        float2 gh = make_float2(0.f, 0.f);
 #pragma unroll
         for (int o = 0; o < N - 1; ++o) {
             __builtin_amdgcn_sched_barrier(0);
@@ -201,7 +213,10 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
                 pair_repack(cmul(Ak, Hk), cmul(Am, Hm), wk, Yk, Ym);
                 acc[k] = Yk;
                 if (k != 0) acc[km] = Ym;
-                if (k != 0) {
+                if (o == N - 2) {
+                    ga[e] = Ak;
+                    gb[e] = Am;
+                } else if (k != 0) {
                     Gw[k] = Ak;
                     Gw[km] = Am;
                 } else {
@@ -215,7 +230,8 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
                 const float2 Hh = hadd(Hs[k], bs);
                 pair_repack(cmul(A, Hh), cmul(A, Hh), wp[k], Y, Yd);
                 acc[k] = Y;
-                Gw[k] = A;
+                if (o == N - 2) gh = A;
+                else Gw[k] = A;
             }
             __syncthreads();
             lds_load_strided<T>(acc, t, f);
@@ -237,10 +253,16 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
             for (int e = 0; e < H; ++e) {
                 const uint32_t m = t + T * e;
                 const float2 g = load_pair(dyr, m);
-                a[e] = emul(g, conv3_pair(x0r, m, w0p[0], w0p[1], w0p[2]));
+                float2 prev, cur;
+                raw_pairs(x0r, m, prev, cur);
+                a[e] = emul(g, conv3_from(prev, cur, w0p[0], w0p[1], w0p[2]));
                 dx[e] = emul(g, v[e]);
+                tap_sums(dx[e], prev, cur, dws[0]);
             }
-            short_conv_back<L, E>(acc, t, dx, urow[0], w0p, du + ((int64_t)b * C + d) * L, dws[0]);
+            pin(dws[0][0]);
+            pin(dws[0][1]);
+            pin(dws[0][2]);
+            short_conv_back<L, E>(acc, t, dx, w0p, du + ((int64_t)b * C + d) * L);
         }
 #pragma unroll
         for (int o = N - 2; o >= 0; --o) {
@@ -248,24 +270,6 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
             t = fresh_tid<T>(t);
             const int gi = N - 1 - o;
             const float* wg = w3 + 3 * ((int64_t)gi * D + d);
-            // v_o and the gate x_{N-1-o} are fetched again after the transforms
-            // rather than held across them
-            auto value_at = [&](const TIO* vr, const float2* Vw, uint32_t m) {
-                return (o == 0) ? conv3_pair(vr, m, wN[0], wN[1], wN[2]) : Vw[m];
-            };
-            float sb = 0.f;
-            {
-                const TIO* vr = fresh(urow[N]);
-                const TIO* xr = fresh(urow[gi]);
-                const float2* Vw = fresh(wsd) + W::V + (int64_t)(o - 1) * (L / 2);
-#pragma unroll
-                for (int e = 0; e < H; ++e) {
-                    const uint32_t m = t + T * e;
-                    const float2 g = emul(value_at(vr, Vw, m), conv3_pair(xr, m, wg[0], wg[1], wg[2]));
-                    sb = fmaf(a[e].x, g.x, fmaf(a[e].y, g.y, sb));
-                }
-            }
-            dbs[o] += sb;
             float2 f[E];
 #pragma unroll
             for (int e = 0; e < H; ++e) f[e] = a[e];
@@ -290,7 +294,10 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
                 float2 Ak, Am, Hk, Hm, Yk, Ym, Gk, Gm;
                 const float2 wk = wp[k];
                 pair_unpack(acc[k], acc[km], wk, Ak, Am);
-                if (k != 0) {
+                if (o == N - 2) {
+                    Gk = ga[e];
+                    Gm = gb[e];
+                } else if (k != 0) {
                     Gk = Gw[k];
                     Gm = Gw[km];
                 } else {
@@ -320,7 +327,7 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
                 const uint32_t k = L / 2;
                 float2 A, Am, Y, Yd;
                 pair_unpack(acc[k], acc[k], wp[k], A, Am);
-                float2 P = cmulc(A, Gw[k]);
+                float2 P = cmulc(A, o == N - 2 ? gh : Gw[k]);
                 if (b > 0) P = cadd(P, DHw[k]);
                 DHw[k] = P;
                 const float2 Hh = hadd(Hs[k], bs);
@@ -333,6 +340,8 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
             fft_strided<L, true, false>(f, t, fresh(tw), acc);
             phase();
             t = fresh_tid<T>(t);
+            // v_o and the gate x_{N-1-o} are fetched again here rather than held
+            // across the transforms; their raw samples also give the tap sums
             {
                 const TIO* vr = fresh(urow[N]);
                 const TIO* xr = fresh(urow[gi]);
@@ -340,14 +349,32 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
 #pragma unroll
                 for (int e = 0; e < H; ++e) {
                     const uint32_t m = t + T * e;
-                    dx[e] = emul(f[e], value_at(vr, Vw, m));                      // dg * v_o
-                    a[e] = emul(f[e], conv3_pair(xr, m, wg[0], wg[1], wg[2]));  // dg * x_{N-1-o} = dv_o
+                    float2 xp, xc;
+                    raw_pairs(xr, m, xp, xc);
+                    if (o == 0) {
+                        float2 vp, vc;
+                        raw_pairs(vr, m, vp, vc);
+                        dx[e] = emul(f[e], conv3_from(vp, vc, wN[0], wN[1], wN[2]));  // dg * v_0
+                        a[e] = emul(f[e], conv3_from(xp, xc, wg[0], wg[1], wg[2]));   // dv_0
+                        tap_sums(a[e], vp, vc, dws[N]);
+                    } else {
+                        dx[e] = emul(f[e], Vw[m]);                                  // dg * v_o
+                        a[e] = emul(f[e], conv3_from(xp, xc, wg[0], wg[1], wg[2]));  // dv_o
+                    }
+                    tap_sums(dx[e], xp, xc, dws[gi]);
+                }
+                pin(dws[gi][0]);
+                pin(dws[gi][1]);
+                pin(dws[gi][2]);
+                if (o == 0) {
+                    pin(dws[N][0]);
+                    pin(dws[N][1]);
+                    pin(dws[N][2]);
                 }
             }
-            short_conv_back<L, E>(acc, t, dx, urow[gi], wg, du + ((int64_t)b * C + (int64_t)gi * D + d) * L,
-                                  dws[gi]);
+            short_conv_back<L, E>(acc, t, dx, wg, du + ((int64_t)b * C + (int64_t)gi * D + d) * L);
         }
-        short_conv_back<L, E>(acc, t, a, urow[N], wN, du + ((int64_t)b * C + (int64_t)N * D + d) * L, dws[N]);
+        short_conv_back<L, E>(acc, t, a, wN, du + ((int64_t)b * C + (int64_t)N * D + d) * L);
     }
 
     // ------------------------------------------- dh: invert the summed spectra
@@ -390,23 +417,23 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
         float* dhr = dh + ((int64_t)o * D + d) * L;
 #pragma unroll
         for (int e = 0; e < H; ++e) store_pair(dhr, (uint32_t)(t + T * e), f[e]);
+        // the bias gradient sum_b sum_t dv[t] g[t] is the lag-0 value of the same
+        // correlation that gives dh
+        if (t == 0) dbias[(int64_t)o * D + d] = f[0].x;
     }
 
-    // --------------------------------------- tap and bias sums over the workgroup
+    // ------------------------------------------------ tap sums over the workgroup
     float* red = reinterpret_cast<float*>(lds);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i <= N; ++i)
 #pragma unroll
         for (int j = 0; j < 3; ++j) red[(3 * i + j) * T + t] = dws[i][j];
-#pragma unroll
-    for (int o = 0; o < N - 1; ++o) red[(3 * (N + 1) + o) * T + t] = dbs[o];
     __syncthreads();
     for (int q = t; q < NV; q += T) {
         float s = 0.f;
         for (int r = 0; r < T; ++r) s += red[q * T + r];
-        if (q < 3 * (N + 1)) dw[((int64_t)(q / 3) * D + d) * 3 + (q % 3)] = s;
-        else dbias[(int64_t)(q - 3 * (N + 1)) * D + d] = s;
+        dw[((int64_t)(q / 3) * D + d) * 3 + (q % 3)] = s;
     }
 }
 

@@ -164,8 +164,8 @@ hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_p
 hyena_status_t hyena_fused_check(hyena_plan_t plan, const void* workspace, int* flag);
 
 /* Bytes of workspace hyena_backward needs for this plan (independent of B):
- * per channel, the N-1 running dh spectra, the gated-input spectra of the N-1
- * steps and the values v_1..v_{N-2}, i.e. 8 * D * ((2N-2)*L + (N-2)*L/2).
+ * per channel, the N-1 running dh spectra, the gated-input spectra of steps
+ * 0..N-3 and the values v_1..v_{N-2}, i.e. 8 * D * ((2N-3)*L + (N-2)*L/2).
  * Returns 0 for a NULL plan or a plan whose path has no backward (FOURSTEP). */
 size_t hyena_backward_workspace_bytes(hyena_plan_t plan);
 
