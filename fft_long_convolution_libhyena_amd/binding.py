@@ -68,7 +68,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_forward_timed.restype = ci
     lib.hyena_fused_check.argtypes = [vp, vp, ctypes.POINTER(ci)]
     lib.hyena_fused_check.restype = ci
-    lib.hyena_backward_workspace_bytes.argtypes = [vp]
+    lib.hyena_backward_workspace_bytes.argtypes = [vp, i64]
     lib.hyena_backward_workspace_bytes.restype = sz
     lib.hyena_backward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hyena_backward.restype = ci
@@ -183,8 +183,8 @@ class Plan:
                                             ws_bytes, _stream_handle(torch, self.device), ms))
         return dict(zip(("lds", "pass_a", "pass_b", "pass_c", "total"), [float(v) for v in ms]))
 
-    def backward_workspace_bytes(self) -> int:
-        return int(self.lib.hyena_backward_workspace_bytes(self.handle))
+    def backward_workspace_bytes(self, B: int) -> int:
+        return int(self.lib.hyena_backward_workspace_bytes(self.handle, int(B)))
 
     def backward(self, u_proj, short_w, spec, bias, dy, du=None, dw=None, dh=None, dbias=None, workspace=None):
         """hyena_backward: gradients (du_proj [B,(N+1)D,L] io dtype, dshort_w [(N+1)D,3],
@@ -209,7 +209,7 @@ class Plan:
         self._need(dw, "dw", ((N + 1) * D, 3), f32)
         self._need(dh, "dh", (N - 1, D, L), f32)
         self._need(dbias, "dbias", (N - 1, D), f32)
-        need = self.backward_workspace_bytes()
+        need = self.backward_workspace_bytes(B)
         if workspace is None and need:
             workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None

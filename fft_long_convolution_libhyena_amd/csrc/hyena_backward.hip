@@ -9,9 +9,9 @@
 
 extern "C" {
 
-size_t hyena_backward_workspace_bytes(hyena_plan_t plan) {
-    if (!plan || plan->path != HYENA_PATH_LDS) return 0;
-    return (size_t)hy::bwd_ws_per_channel(plan->L, plan->order) * (size_t)plan->D * sizeof(float2);
+size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B) {
+    if (!plan || B < 1 || plan->path != HYENA_PATH_LDS) return 0;
+    return hy::bwd_ws_bytes(B, plan->D, plan->L, plan->order);
 }
 
 hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
@@ -25,7 +25,8 @@ hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, 
         return HYENA_ERR_INVALID_ARG;
     if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 26)) return HYENA_ERR_INVALID_ARG;
     if (plan->path != HYENA_PATH_LDS) return HYENA_ERR_UNSUPPORTED;
-    if (!workspace || !aligned16(workspace) || workspace_bytes < hyena_backward_workspace_bytes(plan))
+    if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
+    if (!workspace || !aligned16(workspace) || workspace_bytes < hyena_backward_workspace_bytes(plan, B))
         return HYENA_ERR_WORKSPACE;
     if (hy::check_device(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
     hy::LdsBwdArgs a{u_proj,   short_w,   (const float2*)spec, bias,      dy,         du_proj,

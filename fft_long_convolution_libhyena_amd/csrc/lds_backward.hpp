@@ -16,12 +16,13 @@
 // correlation is a product with a conjugate spectrum: dg_o comes from
 // A_dv * conj(H_o + bias_o) and dh_o from sum_b A_dv * conj(A_g).
 //
-// One workgroup owns one channel d and walks the batch, so every gradient of the
-// channel (dh, dbias, dw and the N+1 rows of du per b) is produced by that
-// workgroup alone: no atomics, and the batch sums are taken in a fixed order.
-// Per b it recomputes the forward chain on chip (2(N-1) transforms), then undoes
-// it (2(N-1) transforms); after the last b it inverts the N-1 accumulated
-// dh spectra.
+// Two kernels. k_lds_bwd_rows: one workgroup per (b, d) row (the B rows of a
+// channel on one XCD, sharing its filter spectrum in L2) recomputes the forward
+// chain on chip (2(N-1) transforms), undoes it (2(N-1) transforms), writes the
+// N+1 rows of du and, per step, the product spectrum A_dv * conj(A_g) and the
+// row's tap sums. k_lds_bwd_finish: one workgroup per (o, d) sums those over the
+// batch in a fixed order and inverts the dh spectrum (dbias is its lag-0 value);
+// no atomics, so results are reproducible bit for bit.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -119,28 +120,28 @@ __device__ __forceinline__ void tap_sums(float2 dc, float2 prev, float2 cur, flo
     dws[2] = fmaf(dc.x, cur.x, fmaf(dc.y, cur.y, dws[2]));
 }
 
-// Workspace of one channel, in float2 units (see bwd_ws_per_channel):
-//   DH [N-1][L]    running batch sum of A_dv * conj(A_g), laid out like the spectrum
-//   G  [N-2][L]    unpacked spectra A_g of steps o < N-2 (the last step's stays in
-//                  registers, from the recomputed forward to the undoing of that step)
-//   V  [N-2][L/2]  v_o of steps 1..N-2 as sample pairs
-// Every value is written and read back by the same thread.
+// Workspace layout in float2 units (see bwd_ws_bytes), rows r = b*D + d:
+//   P  [B*D][N-1][L]   per-row product spectra A_dv * conj(A_g), laid out like the
+//                      filter spectrum (slot 0 holds the real bins 0 and L)
+//   G  [B*D][N-2][L]   unpacked spectra A_g of steps o < N-2 (the last step's stays
+//                      in registers from the recomputed forward to its undoing)
+//   V  [B*D][N-2][L/2] v_o of steps 1..N-2 as sample pairs
+//   TW [B][(N+1)*D][3] (floats) per-row tap sums of the short conv
+// G and V are written and read back by the same thread.
 template <int LOGL, int N>
 struct BwdWs {
     static constexpr int64_t L = int64_t(1) << LOGL;
-    static constexpr int64_t DH = 0;
-    static constexpr int64_t G = (N - 1) * L;
-    static constexpr int64_t V = G + (N - 2) * L;
-    static constexpr int64_t PER_D = V + (N - 2) * (L / 2);
-    static_assert(PER_D == (2 * N - 3) * L + (N - 2) * (L / 2), "matches bwd_ws_per_channel");
+    static constexpr int64_t P_ROW = (N - 1) * L;
+    static constexpr int64_t G_ROW = (N - 2) * L;
+    static constexpr int64_t V_ROW = (N - 2) * (L / 2);
 };
 
 template <int LOGL, int N, class TIO>
 __global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS)
-k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const float2* __restrict__ spec,
+k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const float2* __restrict__ spec,
                const float* __restrict__ bias, const TIO* __restrict__ dy, TIO* __restrict__ du,
-               float* __restrict__ dw, float* __restrict__ dh, float* __restrict__ dbias, float2* __restrict__ ws,
-               const float2* __restrict__ tw, const float2* __restrict__ wpair, int B, int D) {
+               float2* __restrict__ ws, const float2* __restrict__ tw, const float2* __restrict__ wpair, int B,
+               int D) {
     constexpr int L = 1 << LOGL;
     constexpr int E = LdsCfg<LOGL>::E;
     constexpr int H = E / 2;
@@ -150,279 +151,236 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
     using W = BwdWs<LOGL, N>;
     __shared__ float2 lds[padded_len<L>()];
     const RowAcc acc{lds};
-    const int d = blockIdx.x;
+    // as in the forward: consecutive workgroups go to different XCDs, and the B
+    // rows of channel d to workgroups of one XCD, whose L2 then serves the filter
+    // spectrum of d to all of them
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, sidx = bid >> 3;
+    const int b = sidx % B;
+    const int d = (sidx / B) * 8 + xcd;
+    if (d >= D) return;
     int t = threadIdx.x;
     const int64_t C = (int64_t)(N + 1) * D;
-    float2* const wsd = ws + (int64_t)d * W::PER_D;
+    const int64_t r = (int64_t)b * D + d;
+    const int64_t rows = (int64_t)B * D;
+    float2* const Pr = ws + r * W::P_ROW;
+    float2* const Gr = ws + rows * W::P_ROW + r * W::G_ROW;
+    float2* const Vr = ws + rows * (W::P_ROW + W::G_ROW) + r * W::V_ROW;
+    float* const TWb = reinterpret_cast<float*>(ws + rows * (W::P_ROW + W::G_ROW + W::V_ROW)) +
+                       (int64_t)b * C * 3;
     const float bscale = 1.0f / (4.0f * (float)L);
 
     float dws[N + 1][3];
 #pragma unroll
     for (int i = 0; i <= N; ++i) dws[i][0] = dws[i][1] = dws[i][2] = 0.f;
 
-    for (int b = 0; b < B; ++b) {
-        t = fresh_tid<T>(t);
-        const TIO* ub = u + (int64_t)b * C * L;
-        const TIO* urow[N + 1];
+    const TIO* ub = u + (int64_t)b * C * L;
+    const TIO* urow[N + 1];
 #pragma unroll
-        for (int i = 0; i <= N; ++i) urow[i] = ub + ((int64_t)i * D + d) * L;
-        const float* wN = w3 + 3 * ((int64_t)N * D + d);
+    for (int i = 0; i <= N; ++i) urow[i] = ub + ((int64_t)i * D + d) * L;
+    const float* wN = w3 + 3 * ((int64_t)N * D + d);
 
-        // ---------------------------------------------- forward chain, recomputed
-        float2 v[H];
+    // -------------------------------------------------- forward chain, recomputed
+    float2 v[H];
 #pragma unroll
-        for (int e = 0; e < H; ++e) v[e] = conv3_pair(urow[N], (uint32_t)(t + T * e), wN[0], wN[1], wN[2]);
-        float2 ga[H], gb[H];  // A_g at k and L-k of the last step
-        float2 gh = make_float2(0.f, 0.f);
+    for (int e = 0; e < H; ++e) v[e] = conv3_pair(urow[N], (uint32_t)(t + T * e), wN[0], wN[1], wN[2]);
+    float2 ga[H], gb[H];  // A_g at k and L-k of the last step
+    float2 gh = make_float2(0.f, 0.f);
 #pragma unroll
-        for (int o = 0; o < N - 1; ++o) {
-            __builtin_amdgcn_sched_barrier(0);
-            t = fresh_tid<T>(t);
-            const int gi = N - 1 - o;
-            const float* wg = w3 + 3 * ((int64_t)gi * D + d);
-            if (o >= 1) {
-                float2* Vw = fresh(wsd) + W::V + (int64_t)(o - 1) * (L / 2);
-#pragma unroll
-                for (int e = 0; e < H; ++e) Vw[t + T * e] = v[e];
-            }
-            float2 f[E];
-            const TIO* xr = fresh(urow[gi]);
-#pragma unroll
-            for (int e = 0; e < H; ++e) f[e] = emul(v[e], conv3_pair(xr, (uint32_t)(t + T * e), wg[0], wg[1], wg[2]));
-#pragma unroll
-            for (int e = H; e < E; ++e) f[e] = make_float2(0.f, 0.f);
-            phase();
-            fft_strided<L, false, true>(f, t, fresh(tw), acc);
-            phase();
-            t = fresh_tid<T>(t);
-            __syncthreads();
-            lds_store_strided<T>(acc, t, f);
-            __syncthreads();
-            const float2* Hs = fresh(spec) + ((int64_t)o * D + d) * L;
-            const float2* wp = fresh(wpair);
-            const float bs = bias[(int64_t)o * D + d] * bscale;
-            float2* Gw = fresh(wsd) + W::G + (int64_t)o * L;
-#pragma unroll
-            for (int e = 0; e < H; ++e) {
-                const uint32_t k = t + T * e;
-                const uint32_t km = k == 0 ? 0 : L - k;
-                float2 Ak, Am, Hk, Hm, Yk, Ym;
-                const float2 wk = wp[k];
-                pair_unpack(acc[k], acc[km], wk, Ak, Am);
-                spec_pair(Hs, k, km, bs, Hk, Hm);
-                pair_repack(cmul(Ak, Hk), cmul(Am, Hm), wk, Yk, Ym);
-                acc[k] = Yk;
-                if (k != 0) acc[km] = Ym;
-                if (o == N - 2) {
-                    ga[e] = Ak;
-                    gb[e] = Am;
-                } else if (k != 0) {
-                    Gw[k] = Ak;
-                    Gw[km] = Am;
-                } else {
-                    Gw[0] = make_float2(Ak.x, Am.x);  // bins 0 and L are real
-                }
-            }
-            if (t == 0) {  // k = L/2 pairs with itself
-                const uint32_t k = L / 2;
-                float2 A, Am, Y, Yd;
-                pair_unpack(acc[k], acc[k], wp[k], A, Am);
-                const float2 Hh = hadd(Hs[k], bs);
-                pair_repack(cmul(A, Hh), cmul(A, Hh), wp[k], Y, Yd);
-                acc[k] = Y;
-                if (o == N - 2) gh = A;
-                else Gw[k] = A;
-            }
-            __syncthreads();
-            lds_load_strided<T>(acc, t, f);
-            phase();
-            fft_strided<L, true, false>(f, t, fresh(tw), acc);
-            phase();
-            t = fresh_tid<T>(t);
-#pragma unroll
-            for (int e = 0; e < H; ++e) v[e] = f[e];  // v_{o+1}
-        }
-
-        // --------------------------------------------------------------- backward
-        float2 a[H], dx[H];
-        {
-            const TIO* dyr = dy + ((int64_t)b * D + d) * L;
-            const float* w0p = w3 + 3 * (int64_t)d;
-            const TIO* x0r = fresh(urow[0]);
-#pragma unroll
-            for (int e = 0; e < H; ++e) {
-                const uint32_t m = t + T * e;
-                const float2 g = load_pair(dyr, m);
-                float2 prev, cur;
-                raw_pairs(x0r, m, prev, cur);
-                a[e] = emul(g, conv3_from(prev, cur, w0p[0], w0p[1], w0p[2]));
-                dx[e] = emul(g, v[e]);
-                tap_sums(dx[e], prev, cur, dws[0]);
-            }
-            pin(dws[0][0]);
-            pin(dws[0][1]);
-            pin(dws[0][2]);
-            short_conv_back<L, E>(acc, t, dx, w0p, du + ((int64_t)b * C + d) * L);
-        }
-#pragma unroll
-        for (int o = N - 2; o >= 0; --o) {
-            __builtin_amdgcn_sched_barrier(0);
-            t = fresh_tid<T>(t);
-            const int gi = N - 1 - o;
-            const float* wg = w3 + 3 * ((int64_t)gi * D + d);
-            float2 f[E];
-#pragma unroll
-            for (int e = 0; e < H; ++e) f[e] = a[e];
-#pragma unroll
-            for (int e = H; e < E; ++e) f[e] = make_float2(0.f, 0.f);
-            phase();
-            fft_strided<L, false, true>(f, t, fresh(tw), acc);
-            phase();
-            t = fresh_tid<T>(t);
-            __syncthreads();
-            lds_store_strided<T>(acc, t, f);
-            __syncthreads();
-            const float2* Hs = fresh(spec) + ((int64_t)o * D + d) * L;
-            const float2* wp = fresh(wpair);
-            const float bs = bias[(int64_t)o * D + d] * bscale;
-            const float2* Gw = fresh(wsd) + W::G + (int64_t)o * L;
-            float2* DHw = fresh(wsd) + W::DH + (int64_t)o * L;
-#pragma unroll
-            for (int e = 0; e < H; ++e) {
-                const uint32_t k = t + T * e;
-                const uint32_t km = k == 0 ? 0 : L - k;
-                float2 Ak, Am, Hk, Hm, Yk, Ym, Gk, Gm;
-                const float2 wk = wp[k];
-                pair_unpack(acc[k], acc[km], wk, Ak, Am);
-                if (o == N - 2) {
-                    Gk = ga[e];
-                    Gm = gb[e];
-                } else if (k != 0) {
-                    Gk = Gw[k];
-                    Gm = Gw[km];
-                } else {
-                    const float2 g0 = Gw[0];
-                    Gk = make_float2(g0.x, 0.f);
-                    Gm = make_float2(g0.y, 0.f);
-                }
-                float2 Pk = cmulc(Ak, Gk), Pm = cmulc(Am, Gm);
-                if (k != 0) {
-                    if (b > 0) {
-                        Pk = cadd(Pk, DHw[k]);
-                        Pm = cadd(Pm, DHw[km]);
-                    }
-                    DHw[k] = Pk;
-                    DHw[km] = Pm;
-                } else {
-                    float2 p0 = make_float2(Pk.x, Pm.x);
-                    if (b > 0) p0 = cadd(p0, DHw[0]);
-                    DHw[0] = p0;
-                }
-                spec_pair(Hs, k, km, bs, Hk, Hm);
-                pair_repack(cmulc(Ak, Hk), cmulc(Am, Hm), wk, Yk, Ym);
-                acc[k] = Yk;
-                if (k != 0) acc[km] = Ym;
-            }
-            if (t == 0) {
-                const uint32_t k = L / 2;
-                float2 A, Am, Y, Yd;
-                pair_unpack(acc[k], acc[k], wp[k], A, Am);
-                float2 P = cmulc(A, o == N - 2 ? gh : Gw[k]);
-                if (b > 0) P = cadd(P, DHw[k]);
-                DHw[k] = P;
-                const float2 Hh = hadd(Hs[k], bs);
-                pair_repack(cmulc(A, Hh), cmulc(A, Hh), wp[k], Y, Yd);
-                acc[k] = Y;
-            }
-            __syncthreads();
-            lds_load_strided<T>(acc, t, f);
-            phase();
-            fft_strided<L, true, false>(f, t, fresh(tw), acc);
-            phase();
-            t = fresh_tid<T>(t);
-            // v_o and the gate x_{N-1-o} are fetched again here rather than held
-            // across the transforms; their raw samples also give the tap sums
-            {
-                const TIO* vr = fresh(urow[N]);
-                const TIO* xr = fresh(urow[gi]);
-                const float2* Vw = fresh(wsd) + W::V + (int64_t)(o - 1) * (L / 2);
-#pragma unroll
-                for (int e = 0; e < H; ++e) {
-                    const uint32_t m = t + T * e;
-                    float2 xp, xc;
-                    raw_pairs(xr, m, xp, xc);
-                    if (o == 0) {
-                        float2 vp, vc;
-                        raw_pairs(vr, m, vp, vc);
-                        dx[e] = emul(f[e], conv3_from(vp, vc, wN[0], wN[1], wN[2]));  // dg * v_0
-                        a[e] = emul(f[e], conv3_from(xp, xc, wg[0], wg[1], wg[2]));   // dv_0
-                        tap_sums(a[e], vp, vc, dws[N]);
-                    } else {
-                        dx[e] = emul(f[e], Vw[m]);                                  // dg * v_o
-                        a[e] = emul(f[e], conv3_from(xp, xc, wg[0], wg[1], wg[2]));  // dv_o
-                    }
-                    tap_sums(dx[e], xp, xc, dws[gi]);
-                }
-                pin(dws[gi][0]);
-                pin(dws[gi][1]);
-                pin(dws[gi][2]);
-                if (o == 0) {
-                    pin(dws[N][0]);
-                    pin(dws[N][1]);
-                    pin(dws[N][2]);
-                }
-            }
-            short_conv_back<L, E>(acc, t, dx, wg, du + ((int64_t)b * C + (int64_t)gi * D + d) * L);
-        }
-        short_conv_back<L, E>(acc, t, a, wN, du + ((int64_t)b * C + (int64_t)N * D + d) * L);
-    }
-
-    // ------------------------------------------- dh: invert the summed spectra
-    // repack + the unnormalised L-point inverse of X gives the 2L-point inverse of
-    // 2L*X; the products carry the factor 4 of the unpacked values: X = P / (8L)
-    const float sc = 1.0f / (8.0f * (float)L);
-#pragma unroll 1
     for (int o = 0; o < N - 1; ++o) {
-        const float2* DHw = fresh(wsd) + W::DH + (int64_t)o * L;
+        phase();
+        t = fresh_tid<T>(t);
+        const int gi = N - 1 - o;
+        const float* wg = w3 + 3 * ((int64_t)gi * D + d);
+        if (o >= 1) {
+            float2* Vw = fresh(Vr) + (int64_t)(o - 1) * (L / 2);
+#pragma unroll
+            for (int e = 0; e < H; ++e) Vw[t + T * e] = v[e];
+        }
+        float2 f[E];
+        const TIO* xr = fresh(urow[gi]);
+#pragma unroll
+        for (int e = 0; e < H; ++e) f[e] = emul(v[e], conv3_pair(xr, (uint32_t)(t + T * e), wg[0], wg[1], wg[2]));
+#pragma unroll
+        for (int e = H; e < E; ++e) f[e] = make_float2(0.f, 0.f);
+        phase();
+        fft_strided<L, false, true>(f, t, fresh(tw), acc);
+        phase();
         t = fresh_tid<T>(t);
         __syncthreads();
+        lds_store_strided<T>(acc, t, f);
+        __syncthreads();
+        const float2* Hs = fresh(spec) + ((int64_t)o * D + d) * L;
+        const float2* wp = fresh(wpair);
+        const float bs = bias[(int64_t)o * D + d] * bscale;
+        float2* Gw = fresh(Gr) + (int64_t)o * L;
 #pragma unroll
         for (int e = 0; e < H; ++e) {
             const uint32_t k = t + T * e;
             const uint32_t km = k == 0 ? 0 : L - k;
-            float2 Ck, Cm, Yk, Ym;
-            if (k != 0) {
-                Ck = fmul2(DHw[k], sc);
-                Cm = fmul2(DHw[km], sc);
+            float2 Ak, Am, Hk, Hm, Yk, Ym;
+            const float2 wk = wp[k];
+            pair_unpack(acc[k], acc[km], wk, Ak, Am);
+            spec_pair(Hs, k, km, bs, Hk, Hm);
+            pair_repack(cmul(Ak, Hk), cmul(Am, Hm), wk, Yk, Ym);
+            acc[k] = Yk;
+            if (k != 0) acc[km] = Ym;
+            if (o == N - 2) {
+                ga[e] = Ak;
+                gb[e] = Am;
+            } else if (k != 0) {
+                Gw[k] = Ak;
+                Gw[km] = Am;
             } else {
-                const float2 p0 = DHw[0];
-                Ck = make_float2(p0.x * sc, 0.f);
-                Cm = make_float2(p0.y * sc, 0.f);
+                Gw[0] = make_float2(Ak.x, Am.x);  // bins 0 and L are real
             }
-            pair_repack(Ck, Cm, wpair[k], Yk, Ym);
+        }
+        if (t == 0) {  // k = L/2 pairs with itself
+            const uint32_t k = L / 2;
+            float2 A, Am, Y, Yd;
+            pair_unpack(acc[k], acc[k], wp[k], A, Am);
+            const float2 Hh = hadd(Hs[k], bs);
+            pair_repack(cmul(A, Hh), cmul(A, Hh), wp[k], Y, Yd);
+            acc[k] = Y;
+            if (o == N - 2) gh = A;
+            else Gw[k] = A;
+        }
+        __syncthreads();
+        lds_load_strided<T>(acc, t, f);
+        phase();
+        fft_strided<L, true, false>(f, t, fresh(tw), acc);
+        phase();
+        t = fresh_tid<T>(t);
+#pragma unroll
+        for (int e = 0; e < H; ++e) v[e] = f[e];  // v_{o+1}
+    }
+
+    // ------------------------------------------------------------------ backward
+    float2 a[H], dx[H];
+    {
+        const TIO* dyr = dy + r * L;
+        const float* w0p = w3 + 3 * (int64_t)d;
+        const TIO* x0r = fresh(urow[0]);
+#pragma unroll
+        for (int e = 0; e < H; ++e) {
+            const uint32_t m = t + T * e;
+            const float2 g = load_pair(dyr, m);
+            float2 prev, cur;
+            raw_pairs(x0r, m, prev, cur);
+            a[e] = emul(g, conv3_from(prev, cur, w0p[0], w0p[1], w0p[2]));
+            dx[e] = emul(g, v[e]);
+            tap_sums(dx[e], prev, cur, dws[0]);
+        }
+        pin(dws[0][0]);
+        pin(dws[0][1]);
+        pin(dws[0][2]);
+        short_conv_back<L, E>(acc, t, dx, w0p, du + ((int64_t)b * C + d) * L);
+    }
+#pragma unroll
+    for (int o = N - 2; o >= 0; --o) {
+        phase();
+        t = fresh_tid<T>(t);
+        const int gi = N - 1 - o;
+        const float* wg = w3 + 3 * ((int64_t)gi * D + d);
+        float2 f[E];
+#pragma unroll
+        for (int e = 0; e < H; ++e) f[e] = a[e];
+#pragma unroll
+        for (int e = H; e < E; ++e) f[e] = make_float2(0.f, 0.f);
+        phase();
+        fft_strided<L, false, true>(f, t, fresh(tw), acc);
+        phase();
+        t = fresh_tid<T>(t);
+        __syncthreads();
+        lds_store_strided<T>(acc, t, f);
+        __syncthreads();
+        const float2* Hs = fresh(spec) + ((int64_t)o * D + d) * L;
+        const float2* wp = fresh(wpair);
+        const float bs = bias[(int64_t)o * D + d] * bscale;
+        const float2* Gw = fresh(Gr) + (int64_t)o * L;
+        float2* Pw = fresh(Pr) + (int64_t)o * L;
+#pragma unroll
+        for (int e = 0; e < H; ++e) {
+            const uint32_t k = t + T * e;
+            const uint32_t km = k == 0 ? 0 : L - k;
+            float2 Ak, Am, Hk, Hm, Yk, Ym, Gk, Gm;
+            const float2 wk = wp[k];
+            pair_unpack(acc[k], acc[km], wk, Ak, Am);
+            if (o == N - 2) {
+                Gk = ga[e];
+                Gm = gb[e];
+            } else if (k != 0) {
+                Gk = Gw[k];
+                Gm = Gw[km];
+            } else {
+                const float2 g0 = Gw[0];
+                Gk = make_float2(g0.x, 0.f);
+                Gm = make_float2(g0.y, 0.f);
+            }
+            const float2 Pk = cmulc(Ak, Gk), Pm = cmulc(Am, Gm);
+            if (k != 0) {
+                Pw[k] = Pk;
+                Pw[km] = Pm;
+            } else {
+                Pw[0] = make_float2(Pk.x, Pm.x);
+            }
+            spec_pair(Hs, k, km, bs, Hk, Hm);
+            pair_repack(cmulc(Ak, Hk), cmulc(Am, Hm), wk, Yk, Ym);
             acc[k] = Yk;
             if (k != 0) acc[km] = Ym;
         }
         if (t == 0) {
             const uint32_t k = L / 2;
-            const float2 P = fmul2(DHw[k], sc);
-            float2 Y, Yd;
-            pair_repack(P, P, wpair[k], Y, Yd);
+            float2 A, Am, Y, Yd;
+            pair_unpack(acc[k], acc[k], wp[k], A, Am);
+            Pw[k] = cmulc(A, o == N - 2 ? gh : Gw[k]);
+            const float2 Hh = hadd(Hs[k], bs);
+            pair_repack(cmulc(A, Hh), cmulc(A, Hh), wp[k], Y, Yd);
             acc[k] = Y;
         }
         __syncthreads();
-        float2 f[E];
         lds_load_strided<T>(acc, t, f);
-        fft_strided<L, true, false>(f, t, tw, acc);
-        float* dhr = dh + ((int64_t)o * D + d) * L;
+        phase();
+        fft_strided<L, true, false>(f, t, fresh(tw), acc);
+        phase();
+        t = fresh_tid<T>(t);
+        // v_o and the gate x_{N-1-o} are fetched again here rather than held
+        // across the transforms; their raw samples also give the tap sums
+        {
+            const TIO* vr = fresh(urow[N]);
+            const TIO* xr = fresh(urow[gi]);
+            const float2* Vw = fresh(Vr) + (int64_t)(o - 1) * (L / 2);
 #pragma unroll
-        for (int e = 0; e < H; ++e) store_pair(dhr, (uint32_t)(t + T * e), f[e]);
-        // the bias gradient sum_b sum_t dv[t] g[t] is the lag-0 value of the same
-        // correlation that gives dh
-        if (t == 0) dbias[(int64_t)o * D + d] = f[0].x;
+            for (int e = 0; e < H; ++e) {
+                const uint32_t m = t + T * e;
+                float2 xp, xc;
+                raw_pairs(xr, m, xp, xc);
+                if (o == 0) {
+                    float2 vp, vc;
+                    raw_pairs(vr, m, vp, vc);
+                    dx[e] = emul(f[e], conv3_from(vp, vc, wN[0], wN[1], wN[2]));  // dg * v_0
+                    a[e] = emul(f[e], conv3_from(xp, xc, wg[0], wg[1], wg[2]));   // dv_0
+                    tap_sums(a[e], vp, vc, dws[N]);
+                } else {
+                    dx[e] = emul(f[e], Vw[m]);                                  // dg * v_o
+                    a[e] = emul(f[e], conv3_from(xp, xc, wg[0], wg[1], wg[2]));  // dv_o
+                }
+                tap_sums(dx[e], xp, xc, dws[gi]);
+            }
+            pin(dws[gi][0]);
+            pin(dws[gi][1]);
+            pin(dws[gi][2]);
+            if (o == 0) {
+                pin(dws[N][0]);
+                pin(dws[N][1]);
+                pin(dws[N][2]);
+            }
+        }
+        short_conv_back<L, E>(acc, t, dx, wg, du + ((int64_t)b * C + (int64_t)gi * D + d) * L);
     }
+    short_conv_back<L, E>(acc, t, a, wN, du + ((int64_t)b * C + (int64_t)N * D + d) * L);
 
-    // ------------------------------------------------ tap sums over the workgroup
+    // ------------------------------------------- this row's tap sums, per channel
     float* red = reinterpret_cast<float*>(lds);
     __syncthreads();
 #pragma unroll
@@ -431,23 +389,96 @@ k_lds_backward(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
         for (int j = 0; j < 3; ++j) red[(3 * i + j) * T + t] = dws[i][j];
     __syncthreads();
     for (int q = t; q < NV; q += T) {
-        float s = 0.f;
-        for (int r = 0; r < T; ++r) s += red[q * T + r];
-        dw[((int64_t)(q / 3) * D + d) * 3 + (q % 3)] = s;
+        float sum = 0.f;
+        for (int k = 0; k < T; ++k) sum += red[q * T + k];
+        TWb[((int64_t)(q / 3) * D + d) * 3 + (q % 3)] = sum;
+    }
+}
+
+// Sums over the batch: dh[o][d] and dbias[o][d] from the product spectra, and
+// (by the o = 0 workgroups) dshort_w of the N+1 channels of d from the row tap sums.
+template <int LOGL, int N>
+__global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS)
+k_lds_bwd_finish(const float2* __restrict__ ws, float* __restrict__ dw, float* __restrict__ dh,
+                 float* __restrict__ dbias, const float2* __restrict__ tw, const float2* __restrict__ wpair, int B,
+                 int D) {
+    constexpr int L = 1 << LOGL;
+    constexpr int E = LdsCfg<LOGL>::E;
+    constexpr int H = E / 2;
+    constexpr int T = L / E;
+    using W = BwdWs<LOGL, N>;
+    __shared__ float2 lds[padded_len<L>()];
+    const RowAcc acc{lds};
+    const int o = blockIdx.x / D, d = blockIdx.x % D;
+    const int t = threadIdx.x;
+    const int64_t rows = (int64_t)B * D;
+    // repack + the unnormalised L-point inverse of X gives the 2L-point inverse of
+    // 2L*X; the products carry the factor 4 of the unpacked values: X = P / (8L)
+    const float sc = 1.0f / (8.0f * (float)L);
+#pragma unroll
+    for (int e = 0; e < H; ++e) {
+        const uint32_t k = t + T * e;
+        const uint32_t km = k == 0 ? 0 : L - k;
+        float2 Ck = make_float2(0.f, 0.f), Cm = make_float2(0.f, 0.f);
+        for (int b = 0; b < B; ++b) {
+            const float2* Pw = ws + ((int64_t)b * D + d) * W::P_ROW + (int64_t)o * L;
+            Ck = cadd(Ck, Pw[k]);
+            if (k != 0) Cm = cadd(Cm, Pw[km]);
+        }
+        float2 Yk, Ym;
+        if (k != 0) {
+            pair_repack(fmul2(Ck, sc), fmul2(Cm, sc), wpair[k], Yk, Ym);
+        } else {
+            // slot 0 holds the real bins 0 and L
+            pair_repack(make_float2(Ck.x * sc, 0.f), make_float2(Ck.y * sc, 0.f), wpair[0], Yk, Ym);
+        }
+        acc[k] = Yk;
+        if (k != 0) acc[km] = Ym;
+    }
+    if (t == 0) {
+        const uint32_t k = L / 2;
+        float2 P = make_float2(0.f, 0.f);
+        for (int b = 0; b < B; ++b) P = cadd(P, ws[((int64_t)b * D + d) * W::P_ROW + (int64_t)o * L + k]);
+        P = fmul2(P, sc);
+        float2 Y, Yd;
+        pair_repack(P, P, wpair[k], Y, Yd);
+        acc[k] = Y;
+    }
+    __syncthreads();
+    float2 f[E];
+    lds_load_strided<T>(acc, t, f);
+    fft_strided<L, true, false>(f, t, tw, acc);
+    float* dhr = dh + ((int64_t)o * D + d) * L;
+#pragma unroll
+    for (int e = 0; e < H; ++e) store_pair(dhr, (uint32_t)(t + T * e), f[e]);
+    // the bias gradient sum_b sum_t dv[t] g[t] is the lag-0 value of the same
+    // correlation that gives dh
+    if (t == 0) dbias[(int64_t)o * D + d] = f[0].x;
+    if (o == 0) {
+        const float* TW = reinterpret_cast<const float*>(ws + rows * (W::P_ROW + W::G_ROW + W::V_ROW));
+        const int64_t C = (int64_t)(N + 1) * D;
+        for (int q = t; q < 3 * (N + 1); q += T) {
+            const int64_t idx = ((int64_t)(q / 3) * D + d) * 3 + (q % 3);
+            float sum = 0.f;
+            for (int b = 0; b < B; ++b) sum += TW[(int64_t)b * C * 3 + idx];
+            dw[idx] = sum;
+        }
     }
 }
 
 template <int LOGL, int N>
 inline void launch_lds_backward_n(const LdsBwdArgs& a, hipStream_t st) {
     constexpr int T = LdsCfg<LOGL>::THREADS;
+    const unsigned grid = (unsigned)(a.B * 8 * ((a.D + 7) / 8));
     if (a.bf16)
-        hipLaunchKernelGGL((k_lds_backward<LOGL, N, uint16_t>), dim3((unsigned)a.D), dim3(T), 0, st,
-                           (const uint16_t*)a.u, a.w3, a.spec, a.bias, (const uint16_t*)a.dy, (uint16_t*)a.du,
-                           a.dw, a.dh, a.dbias, a.ws, a.tw, a.wpair, a.B, a.D);
+        hipLaunchKernelGGL((k_lds_bwd_rows<LOGL, N, uint16_t>), dim3(grid), dim3(T), 0, st, (const uint16_t*)a.u,
+                           a.w3, a.spec, a.bias, (const uint16_t*)a.dy, (uint16_t*)a.du, a.ws, a.tw, a.wpair, a.B,
+                           a.D);
     else
-        hipLaunchKernelGGL((k_lds_backward<LOGL, N, float>), dim3((unsigned)a.D), dim3(T), 0, st,
-                           (const float*)a.u, a.w3, a.spec, a.bias, (const float*)a.dy, (float*)a.du, a.dw, a.dh,
-                           a.dbias, a.ws, a.tw, a.wpair, a.B, a.D);
+        hipLaunchKernelGGL((k_lds_bwd_rows<LOGL, N, float>), dim3(grid), dim3(T), 0, st, (const float*)a.u, a.w3,
+                           a.spec, a.bias, (const float*)a.dy, (float*)a.du, a.ws, a.tw, a.wpair, a.B, a.D);
+    hipLaunchKernelGGL((k_lds_bwd_finish<LOGL, N>), dim3((unsigned)((N - 1) * a.D)), dim3(T), 0, st,
+                       (const float2*)a.ws, a.dw, a.dh, a.dbias, a.tw, a.wpair, a.B, a.D);
 }
 
 template <int LOGL>

@@ -163,11 +163,13 @@ hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_p
  * HYENA_ERR_INVALID_ARG for NULL arguments, HYENA_ERR_DEVICE if the copy fails. */
 hyena_status_t hyena_fused_check(hyena_plan_t plan, const void* workspace, int* flag);
 
-/* Bytes of workspace hyena_backward needs for this plan (independent of B):
- * per channel, the N-1 running dh spectra, the gated-input spectra of steps
- * 0..N-3 and the values v_1..v_{N-2}, i.e. 8 * D * ((2N-3)*L + (N-2)*L/2).
- * Returns 0 for a NULL plan or a plan whose path has no backward (FOURSTEP). */
-size_t hyena_backward_workspace_bytes(hyena_plan_t plan);
+/* Bytes of workspace hyena_backward needs for batch B: per (b, d) row the N-1
+ * product spectra that the batch sums of dh are taken from, the gated-input
+ * spectra of steps 0..N-3 and the values v_1..v_{N-2} (8 bytes per complex or
+ * pair value), then 3 floats of short-conv tap sums per (b, channel):
+ * 8*B*D*((2N-3)*L + (N-2)*L/2) + 12*B*(N+1)*D. Returns 0 for a NULL plan, B < 1
+ * or a plan whose path has no backward (FOURSTEP). */
+size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* Backward of the forward hot path: given the upstream gradient dy of y, the
  * gradients of the same scalar loss with respect to u_proj, short_w, the long
@@ -186,10 +188,11 @@ size_t hyena_backward_workspace_bytes(hyena_plan_t plan);
  *           (outputs; the batch sums are complete, not accumulated into the
  *           buffers' previous contents)
  *   workspace / workspace_bytes: device scratch of at least
- *           hyena_backward_workspace_bytes(plan); contents on entry irrelevant.
+ *           hyena_backward_workspace_bytes(plan, B); contents on entry irrelevant.
  * Only the LDS path (L <= 16384) has a backward in this build; other plans get
- * HYENA_ERR_UNSUPPORTED. One workgroup per channel walks the batch, so every
- * sum is taken in a fixed order and results are bitwise reproducible.
+ * HYENA_ERR_UNSUPPORTED. Two launches: one workgroup per (b, d) row, then one
+ * per (o, d) that sums the rows' partial results over the batch in a fixed
+ * order (no atomics), so results are bitwise reproducible.
  * Enqueued on `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL or misaligned
  * pointers, B < 1), HYENA_ERR_UNSUPPORTED, HYENA_ERR_WORKSPACE,
  * HYENA_ERR_DEVICE (launch failure, wrong current device). Outputs must not

@@ -94,7 +94,7 @@ def test_forward_and_spectrum_reject_null_plan(lib):
 
 
 def test_backward_rejects_null_plan(lib):
-    assert lib.hyena_backward_workspace_bytes(None) == 0
+    assert lib.hyena_backward_workspace_bytes(None, 1) == 0
     assert lib.hyena_backward(None, 1, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 20, None) == 1
 
 

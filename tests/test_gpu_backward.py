@@ -132,14 +132,14 @@ def test_backward_rejects_fourstep_plan_and_small_workspace():
     g = torch.zeros((1, 2, 1024), dtype=torch.float32, device=t["u"].device)
     with Plan(1024, 2, 2, "f32", "fourstep") as p:
         spec = p.spectrum(t["h"])
-        assert p.backward_workspace_bytes() == 0
+        assert p.backward_workspace_bytes(1) == 0
         with pytest.raises(HyenaError) as e:
             p.backward(t["u"], t["w"], spec, t["bias"], g, workspace=torch.empty(16, dtype=torch.uint8,
                                                                              device=g.device))
         assert e.value.status == 2  # HYENA_ERR_UNSUPPORTED
     with Plan(1024, 2, 2, "f32", "lds") as p:
         spec = p.spectrum(t["h"])
-        small = torch.empty(p.backward_workspace_bytes() - 256, dtype=torch.uint8, device=g.device)
+        small = torch.empty(p.backward_workspace_bytes(1) - 256, dtype=torch.uint8, device=g.device)
         with pytest.raises(HyenaError) as e:
             p.backward(t["u"], t["w"], spec, t["bias"], g, workspace=small)
         assert e.value.status == 3  # HYENA_ERR_WORKSPACE
