@@ -244,6 +244,103 @@ def bench_backward(args, wl, x, torch, Plan):
     plan.close()
 
 
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+
+def cpu_baseline_operator(x, p, wl, budget_s: float):
+    """The fp64 operator oracle on the first L' tokens of every sequence (the path is
+    causal, so those outputs need only those inputs), L' a power of two sized to
+    about the time budget."""
+    import oracle
+
+    threads = oracle.max_threads()
+    Lp = min(wl.L, 1024)
+    while True:
+        t0 = time.perf_counter()
+        oracle.operator_forward(p.x[:, :Lp], p.w_in, p.b_in, x.short_w, x.h[:, :, :Lp], x.bias, p.w_out, p.b_out,
+                                wl.order, mode="fft")
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or Lp >= wl.L:
+            break
+        Lp = min(wl.L, Lp * 2)
+    return {"value": wl.B * Lp / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the first {Lp} of {wl.L} tokens of all {wl.B} sequences (causal: exact for those tokens), "
+                      f"fp64 numpy projections + fp64 FFT path, {dt:.1f} s wall"}
+
+
+def bench_operator(args, wl, x, torch, Plan):
+    from fft_long_convolution_libhyena_amd import synth
+
+    dev = torch.device("cuda", 0)
+    iot = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    p = synth.operator_params(wl)
+
+    def dv(a, dt=iot):
+        return torch.from_numpy(a).to(dev).to(dt).contiguous()
+
+    plan = Plan(wl.L, wl.D, wl.order, wl.dtype)
+    spec = plan.spectrum(dv(x.h, torch.float32))
+    N, D, L, B = wl.order, wl.D, wl.L, wl.B
+    C = (N + 1) * D
+    args_ = (dv(p.x), dv(p.w_in), dv(p.b_in), dv(x.short_w, torch.float32), spec, dv(x.bias, torch.float32),
+             dv(p.w_out), dv(p.b_out))
+    out = torch.empty((B, L, D), dtype=iot, device=dev)
+    ws = torch.empty(plan.operator_workspace_bytes(B), dtype=torch.uint8, device=dev)
+    log(f"[bench] operator workspace {ws.numel() / 2**20:.1f} MiB, path={plan.path}")
+    for _ in range(args.warmup):
+        plan.operator_forward(*args_, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for rep in range(args.reps):
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            plan.operator_forward(*args_, out=out, workspace=ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / args.steps)
+        log(f"[bench] rep {rep}: {times[-1] * 1e3:.1f} us/step")
+    ms = float(np.median(times))
+    stage = {}
+    nt = max(3, min(args.steps, 10))
+    for _ in range(nt):
+        for k, v in plan.operator_forward_timed(*args_, out=out, workspace=ws).items():
+            stage[k] = stage.get(k, 0.0) + v / nt
+    log(f"[bench] stage ms: {json.dumps({k: round(v, 4) for k, v in stage.items()})}")
+    flops = {"in_proj": 2.0 * B * L * D * C, "out_proj": 2.0 * B * L * D * D}
+    dom = max(("in_proj", "path", "out_proj"), key=lambda k: stage[k])
+    # the stages' share of the timed region (events around each stage add fence time)
+    dom_ms = ms * stage[dom] / max(stage["in_proj"] + stage["path"] + stage["out_proj"], 1e-9)
+    if dom == "path":
+        nbytes = alg_bytes_forward(wl)
+        roof = {"bound": "hbm", "achieved": round(nbytes / (dom_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "kernel": "hyena_forward", "alg_bytes_per_launch": nbytes}
+        roof["frac"] = round(roof["achieved"] / HBM_PEAK_GBS, 4)
+    else:
+        peak = MFMA_PEAK_TFLOPS[wl.dtype]
+        tf = flops[dom] / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tf, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tf / peak, 4), "kernel": f"hipBLASLt GEMM ({dom})", "alg_flops_per_launch": flops[dom]}
+    roof.update({"traffic": None, "launch_ms": round(dom_ms, 5), "launches_per_step": 1,
+                 "stage_ms": {k: round(v, 4) for k, v in stage.items()}})
+    res = {
+        "metric": "tokens/s (B·L/s), Hyena operator forward with in/out projections",
+        "value": B * L / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "f32" else "bf16",
+        "data": f"synthetic seeded ({wl.kind} activations, N(0,1/D) projection weights)",
+        "config": {"workload": wl.name, "B": B, "D": D, "L": L, "order": N, "io_dtype": wl.dtype,
+                   "path": plan.path, "pass": "operator"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (operator oracle) ...")
+        res["cpu_baseline"] = cpu_baseline_operator(x, p, wl, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    plan.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -256,6 +353,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--check", action="store_true", help="also compare sampled rows with the oracle")
+    ap.add_argument("--operator", action="store_true",
+                    help="time hyena_operator_forward (in_proj GEMM + the path + out_proj GEMM) instead")
     ap.add_argument("--backward", action="store_true",
                     help="time hyena_backward instead of the forward (LDS-path workloads, L <= 16384)")
     args = ap.parse_args()
@@ -279,6 +378,9 @@ def main():
     t0 = time.perf_counter()
     x = synth.generate(wl)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    if args.operator:
+        bench_operator(args, wl, x, torch, Plan)
+        return
     if args.backward:
         if wl.L > 16384:
             print("the backward runs on the LDS path only (L <= 16384)", file=sys.stderr)

@@ -25,6 +25,7 @@ _DTYPES = {"f32": HYENA_F32, "bf16": HYENA_BF16}
 EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_destroy", "hyena_plan_path",
            "hyena_spectrum_bytes", "hyena_workspace_bytes", "hyena_filter_spectrum", "hyena_forward",
            "hyena_forward_timed", "hyena_fused_check", "hyena_backward_workspace_bytes", "hyena_backward",
+           "hyena_operator_workspace_bytes", "hyena_operator_forward", "hyena_operator_forward_timed",
            "hyena_status_string")
 
 
@@ -72,6 +73,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_backward_workspace_bytes.restype = sz
     lib.hyena_backward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hyena_backward.restype = ci
+    lib.hyena_operator_workspace_bytes.argtypes = [vp, i64]
+    lib.hyena_operator_workspace_bytes.restype = sz
+    lib.hyena_operator_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hyena_operator_forward.restype = ci
+    lib.hyena_operator_forward_timed.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                                 ctypes.POINTER(ctypes.c_float)]
+    lib.hyena_operator_forward_timed.restype = ci
     lib.hyena_status_string.argtypes = [ci]
     lib.hyena_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -219,6 +227,55 @@ class Plan:
                                        bias.data_ptr(), dy.data_ptr(), du.data_ptr(), dw.data_ptr(), dh.data_ptr(),
                                        dbias.data_ptr(), ws_ptr, ws_bytes, _stream_handle(torch, self.device)))
         return du, dw, dh, dbias
+
+    def operator_workspace_bytes(self, B: int) -> int:
+        return int(self.lib.hyena_operator_workspace_bytes(self.handle, int(B)))
+
+    def _operator_args(self, x, w_in, b_in, short_w, spec, bias, w_out, b_out, out, workspace):
+        torch = self._torch
+        N, D, L = self.order, self.D, self.L
+        if x.dim() != 3:
+            raise ValueError("x must be [B, L, D]")
+        B = int(x.shape[0])
+        io = self.io_dtype
+        self._need(x, "x", (B, L, D), io)
+        self._need(w_in, "w_in", ((N + 1) * D, D), io)
+        self._need(b_in, "b_in", ((N + 1) * D,), io)
+        self._need(w_out, "w_out", (D, D), io)
+        self._need(b_out, "b_out", (D,), io)
+        self._need(short_w, "short_w", ((N + 1) * D, 3), torch.float32)
+        self._need(bias, "bias", (N - 1, D), torch.float32)
+        if spec.device != self.device or spec.numel() * spec.element_size() < self.spectrum_bytes():
+            raise ValueError("spec must come from Plan.spectrum of an equal plan")
+        if out is None:
+            out = torch.empty((B, L, D), dtype=io, device=self.device)
+        self._need(out, "out", (B, L, D), io)
+        if workspace is None:
+            workspace = torch.empty(self.operator_workspace_bytes(B), dtype=torch.uint8, device=self.device)
+        return B, out, workspace
+
+    def operator_forward(self, x, w_in, b_in, short_w, spec, bias, w_out, b_out, out=None, workspace=None):
+        """hyena_operator_forward: x [B,L,D] -> out [B,L,D] through in_proj, the hot path and out_proj."""
+        B, out, ws = self._operator_args(x, w_in, b_in, short_w, spec, bias, w_out, b_out, out, workspace)
+        _check("hyena_operator_forward",
+               self.lib.hyena_operator_forward(self.handle, B, x.data_ptr(), w_in.data_ptr(), b_in.data_ptr(),
+                                               short_w.data_ptr(), spec.data_ptr(), bias.data_ptr(),
+                                               w_out.data_ptr(), b_out.data_ptr(), out.data_ptr(), ws.data_ptr(),
+                                               ws.numel(), _stream_handle(self._torch, self.device)))
+        return out
+
+    def operator_forward_timed(self, x, w_in, b_in, short_w, spec, bias, w_out, b_out, out, workspace=None):
+        """hyena_operator_forward_timed: one synchronous call; returns milliseconds
+        {"in_proj", "path", "out_proj", "total"}."""
+        B, out, ws = self._operator_args(x, w_in, b_in, short_w, spec, bias, w_out, b_out, out, workspace)
+        ms = (ctypes.c_float * 4)()
+        _check("hyena_operator_forward_timed",
+               self.lib.hyena_operator_forward_timed(self.handle, B, x.data_ptr(), w_in.data_ptr(),
+                                                     b_in.data_ptr(), short_w.data_ptr(), spec.data_ptr(),
+                                                     bias.data_ptr(), w_out.data_ptr(), b_out.data_ptr(),
+                                                     out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                                     _stream_handle(self._torch, self.device), ms))
+        return dict(zip(("in_proj", "path", "out_proj", "total"), [float(v) for v in ms]))
 
     def fused_check(self, workspace) -> int:
         """hyena_fused_check: nonzero if a bounded wait of the fused kernel expired

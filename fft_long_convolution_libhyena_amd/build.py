@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhyena.so")
-SOURCES = ["hyena_api.hip", "hyena_backward.hip", "fourstep.hip", "lds_path_a.hip", "lds_path_b.hip", "lds_path_c.hip",
+SOURCES = ["hyena_api.hip", "hyena_backward.hip", "hyena_operator.hip", "fourstep.hip", "lds_path_a.hip", "lds_path_b.hip", "lds_path_c.hip",
            "lds_path_d.hip", "lds_backward_a.hip", "lds_backward_b.hip", "lds_backward_c.hip", "lds_backward_d.hip"]
 HEADERS = ["fft_core.hpp", "kernels.hpp", "pair.hpp", "plan.hpp", "lds_path.hpp", "backward.hpp", "lds_backward.hpp"]
 
@@ -60,7 +60,8 @@ def build(verbose: bool = False, jobs: int = 4, out: str = LIB, defines=()) -> s
         msg = "\n".join(f"--- {s} ---\n{t}" for s, t in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp,
+           "-L/opt/rocm/lib", "-lhipblaslt", "-Wl,-rpath,/opt/rocm/lib"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

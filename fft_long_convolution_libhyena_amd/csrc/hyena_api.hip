@@ -201,6 +201,7 @@ hyena_status_t hyena_plan_destroy(hyena_plan_t plan) {
     if (!plan) return HYENA_OK;
     hyena_status_t st = HYENA_OK;
     if (plan->dtab && hipFree(plan->dtab) != hipSuccess) st = HYENA_ERR_DEVICE;
+    if (plan->op && plan->op_free) plan->op_free(plan->op);
     delete plan;
     return st;
 }

@@ -22,6 +22,10 @@ struct hyena_plan_s {
     // four-step path
     int log1 = 0, log2 = 0;
     hy::FsTables fs{};
+    // state of the operator entry points (projection GEMM handles and descriptors),
+    // attached on their first call and released with the plan
+    void* op = nullptr;
+    void (*op_free)(void*) = nullptr;
 };
 
 namespace hy {

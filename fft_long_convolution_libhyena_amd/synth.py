@@ -148,6 +148,35 @@ def upstream_grad(wl: Workload, seed: Optional[int] = None) -> np.ndarray:
     return np.ascontiguousarray(round_to_bf16(dy) if wl.dtype == "bf16" else dy)
 
 
+@dataclasses.dataclass
+class OperatorParams:
+    x: np.ndarray      # [B, L, D] float32 (bf16 values for bf16 workloads)
+    w_in: np.ndarray   # [(N+1)D, D]
+    b_in: np.ndarray   # [(N+1)D]
+    w_out: np.ndarray  # [D, D]
+    b_out: np.ndarray  # [D]
+
+
+def operator_params(wl: Workload, seed: Optional[int] = None) -> OperatorParams:
+    """Seeded module input and projection parameters for the whole operator:
+    x ~ N(0, 1); weights ~ N(0, 1/D) (the variance of PyTorch's default Linear
+    initialisation scale); biases ~ N(0, 1/D). Drawn from their own PCG64 stream
+    (seed + 2000); rounded to bf16 for bf16 workloads (the rounded values feed
+    both sides)."""
+    rng = np.random.Generator(np.random.PCG64((wl.seed if seed is None else seed) + 2000))
+    B, D, L, C = wl.B, wl.D, wl.L, (wl.order + 1) * wl.D
+    sd = np.float32(1.0 / np.sqrt(D))
+    x = rng.standard_normal((B, L, D), dtype=np.float32)
+    w_in = rng.standard_normal((C, D), dtype=np.float32) * sd
+    b_in = rng.standard_normal(C, dtype=np.float32) * sd
+    w_out = rng.standard_normal((D, D), dtype=np.float32) * sd
+    b_out = rng.standard_normal(D, dtype=np.float32) * sd
+    arrs = [x, w_in, b_in, w_out, b_out]
+    if wl.dtype == "bf16":
+        arrs = [round_to_bf16(a) for a in arrs]
+    return OperatorParams(*[np.ascontiguousarray(a, dtype=np.float32) for a in arrs])
+
+
 def channel_subset(x: Inputs, ds) -> Inputs:
     """The inputs restricted to channels ds of every channel group (gates, value,
     filters, biases): the hot path treats channels independently, so a subset is a

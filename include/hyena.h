@@ -13,9 +13,9 @@
  *   conv(v, h)[t] = sum_{s <= t} h[s] v[t - s],
  * evaluated by FFT on the sequence zero-padded to 2L (the HyenaND summary's
  * boundary handling; the Hyena Hierarchy concept page, section 3.2, FFT
- * acceleration). The in/out projections and the b l d <-> b d l rearranges of
- * the module are outside this library; dropout is the identity; the short
- * Conv1d bias is taken as zero.
+ * acceleration). hyena_operator_forward adds the module's in/out projections and
+ * its b l d <-> b d l rearranges around the path; dropout is the identity; the
+ * short Conv1d bias is taken as zero.
  *
  * Conventions for every call:
  *  - Device pointers are plain device memory on the device that was current when
@@ -27,8 +27,9 @@
  *    synchronising; results are ready when the stream reaches that point.
  *  - Errors are reported by return value; nothing throws across this ABI.
  *    Argument errors are detected on the host before any HIP call is made.
- *  - A plan is immutable after creation and may be shared read-only between
- *    host threads; concurrent forwards need distinct workspaces and outputs.
+ *  - A plan is immutable after creation (apart from the GEMM state the operator
+ *    entry points attach under a lock) and may be shared between host threads;
+ *    concurrent calls need distinct workspaces and outputs.
  */
 #ifndef LIBHYENA_HYENA_H
 #define LIBHYENA_HYENA_H
@@ -200,6 +201,47 @@ size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B);
 hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
                               const void* spec, const float* bias, const void* dy, void* du_proj, float* dshort_w,
                               float* dh, float* dbias, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace hyena_operator_forward needs for batch B: the in-projected
+ * activation u_proj, the path output y, a broadcast input-bias matrix, 32 MiB of
+ * GEMM scratch and the path's own workspace (hyena_workspace_bytes), each
+ * 256-byte aligned. Returns 0 for a NULL plan or B < 1. */
+size_t hyena_operator_workspace_bytes(hyena_plan_t plan, int64_t B);
+
+/* The whole operator forward around the hot path (HyenaDNA walkthrough, section
+ * 2.1, HyenaOperator.forward): in_proj, b l d -> b d l, the hot path as in
+ * hyena_forward, b d l -> b l d, out_proj:
+ *   u_proj[b][c][t] = sum_k w_in[c][k] x[b][t][k] + b_in[c]
+ *   out[b][t][j]    = sum_d w_out[j][d] y[b][d][t] + b_out[j]
+ *   x     [B][L][D] of the plan dtype, device
+ *   w_in  [(N+1)*D][D], b_in [(N+1)*D], w_out [D][D], b_out [D]: the projections'
+ *         weights and biases (PyTorch nn.Linear layout), plan dtype, device
+ *   short_w, spec, bias: as in hyena_forward
+ *   out   [B][L][D] of the plan dtype, device (output)
+ *   workspace: at least hyena_operator_workspace_bytes(plan, B) bytes.
+ * The projections are plain dense GEMMs run by hipBLASLt (fp32 accumulation; with
+ * bf16 plans u_proj is rounded to bf16 between the GEMM and the path, as a bf16
+ * module would), one GEMM call per sequence. The first call on a plan attaches
+ * the GEMM state to it (a hipBLASLt handle and descriptors), so calls on one plan
+ * are serialised internally; hyena_plan_destroy releases it.
+ * Enqueued on `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL or misaligned
+ * pointers, B < 1, sizes too large), HYENA_ERR_WORKSPACE, HYENA_ERR_UNSUPPORTED
+ * (no GEMM kernel for these shapes), HYENA_ERR_DEVICE, and those of
+ * hyena_forward. Outputs must not alias inputs. */
+hyena_status_t hyena_operator_forward(hyena_plan_t plan, int64_t B, const void* x, const void* w_in,
+                                      const void* b_in, const float* short_w, const void* spec, const float* bias,
+                                      const void* w_out, const void* b_out, void* out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/* hyena_operator_forward with timing: HIP events around the three stages on
+ * `stream`; waits for the last one and writes milliseconds into ms[4]:
+ * ms[0] input projection (with the bias fill), ms[1] the hot path, ms[2] output
+ * projection, ms[3] total. HYENA_ERR_INVALID_ARG also for ms == NULL. */
+hyena_status_t hyena_operator_forward_timed(hyena_plan_t plan, int64_t B, const void* x, const void* w_in,
+                                            const void* b_in, const float* short_w, const void* spec,
+                                            const float* bias, const void* w_out, const void* b_out, void* out,
+                                            void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                            float* ms);
 
 /* Static, NUL-terminated description of a status code. */
 const char* hyena_status_string(hyena_status_t s);

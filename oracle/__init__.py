@@ -52,7 +52,7 @@ def _load():
         lib.oracle_causal_conv_fft.restype = None
         lib.oracle_fft.argtypes = [f64p, f64p, i64, ctypes.c_int]
         lib.oracle_fft.restype = ctypes.c_int
-        lib.oracle_hyena_forward.argtypes = [i64, i64, i64, ctypes.c_int, f32p, f32p, f32p, f32p,
+        lib.oracle_hyena_forward.argtypes = [i64, i64, i64, ctypes.c_int, f32p, f64p, f32p, f32p, f32p,
                                              i64p, i64, f64p, ctypes.c_int, ctypes.c_int]
         lib.oracle_hyena_forward.restype = ctypes.c_int
         lib.oracle_causal_corr_direct.argtypes = [f64p, f64p, i64, f64p]
@@ -125,15 +125,22 @@ def forward(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.nda
             threads: int = 0) -> np.ndarray:
     """Hyena operator forward hot path in fp64.
 
-    u_proj [B,(N+1)D,L], short_w [(N+1)D,3], h [N-1,D,L], bias [N-1,D] (all taken as
-    fp32 values).  Returns y as float64, [B,D,L] when ``rows`` is None, otherwise
-    [len(rows), L] for the flat rows b*D + d.
+    u_proj [B,(N+1)D,L], short_w [(N+1)D,3], h [N-1,D,L], bias [N-1,D] (parameters
+    taken as fp32 values; u_proj as fp32 values, or used as is when it is float64).
+    Returns y as float64, [B,D,L] when ``rows`` is None, otherwise [len(rows), L]
+    for the flat rows b*D + d.
     """
-    u = np.ascontiguousarray(u_proj, dtype=np.float32)
+    if np.asarray(u_proj).dtype == np.float64:
+        u = None
+        u64 = np.ascontiguousarray(u_proj)
+    else:
+        u = np.ascontiguousarray(u_proj, dtype=np.float32)
+        u64 = None
+    shape_src = u if u is not None else u64
     w = np.ascontiguousarray(short_w, dtype=np.float32)
     hh = np.ascontiguousarray(h, dtype=np.float32)
     bb = np.ascontiguousarray(bias, dtype=np.float32)
-    B, C, L = u.shape
+    B, C, L = shape_src.shape
     N = int(order)
     if C % (N + 1):
         raise ValueError("u_proj channel count must be (order+1)*D")
@@ -147,7 +154,9 @@ def forward(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.nda
         ra = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
         out = np.empty((ra.size, L), dtype=np.float64)
         rp, nr = _ptr(ra, ctypes.c_int64), ra.size
-    rc = _load().oracle_hyena_forward(B, D, L, N, _ptr(u, ctypes.c_float), _ptr(w, ctypes.c_float),
+    up = _ptr(u, ctypes.c_float) if u is not None else None
+    u64p = _ptr(u64, ctypes.c_double) if u64 is not None else None
+    rc = _load().oracle_hyena_forward(B, D, L, N, up, u64p, _ptr(w, ctypes.c_float),
                                       _ptr(hh, ctypes.c_float), _ptr(bb, ctypes.c_float), rp, nr,
                                       _ptr(out, ctypes.c_double), 0 if mode == "direct" else 1,
                                       int(threads))
@@ -187,6 +196,21 @@ def backward(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.nd
     if rc != 0:
         raise ValueError("oracle_hyena_backward rejected its arguments")
     return du, dw, dh, db
+
+
+def operator_forward(x: np.ndarray, w_in: np.ndarray, b_in: np.ndarray, short_w: np.ndarray, h: np.ndarray,
+                     bias: np.ndarray, w_out: np.ndarray, b_out: np.ndarray, order: int, mode: str = "fft",
+                     threads: int = 0) -> np.ndarray:
+    """The whole operator forward in fp64 (HyenaDNA walkthrough, section 2.1,
+    HyenaOperator.forward): u = in_proj(x) = x w_in^T + b_in on x [B, L, D]; the
+    b l d -> b d l rearrange; the hot path (``forward``); the b d l -> b l d
+    rearrange; out_proj = y w_out^T + b_out. The projections are numpy matrix
+    products in fp64. Returns [B, L, D] float64."""
+    x64 = np.asarray(x, dtype=np.float64)
+    u = x64 @ np.asarray(w_in, np.float64).T + np.asarray(b_in, np.float64)  # [B, L, (N+1)D]
+    u_proj = np.ascontiguousarray(u.transpose(0, 2, 1))                      # [B, (N+1)D, L]
+    y = forward(u_proj, short_w, h, bias, order, mode=mode, threads=threads)  # [B, D, L]
+    return y.transpose(0, 2, 1) @ np.asarray(w_out, np.float64).T + np.asarray(b_out, np.float64)
 
 
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:

@@ -51,6 +51,18 @@ void oracle_short_conv_row(const float* u, const float* w3, int64_t L, double* o
     }
 }
 
+/* The same for a row given in fp64 (an intermediate the oracle computed itself). */
+void oracle_short_conv_row64(const double* u, const float* w3, int64_t L, double* out) {
+    for (int64_t t = 0; t < L; ++t) {
+        double s = 0.0;
+        for (int j = 0; j < 3; ++j) {
+            int64_t tau = t - 2 + j;
+            if (tau >= 0) s += (double)w3[j] * u[tau];
+        }
+        out[t] = s;
+    }
+}
+
 /* Causal linear convolution by its definition: out[t] = sum_{s=0..t} h[s] v[t-s]. */
 void oracle_causal_conv_direct(const double* v, const double* h, int64_t L, double* out) {
     for (int64_t t = 0; t < L; ++t) {
@@ -155,7 +167,8 @@ void oracle_causal_conv_fft(const double* v, const double* h, int64_t L, double*
 
 /*
  * The forward hot path for a set of (b, d) rows.
- *   u     [B][(N+1)D][L]  fp32 values (bf16 inputs already widened exactly)
+ *   u     [B][(N+1)D][L]  fp32 values (bf16 inputs already widened exactly), or NULL
+ *         when u64 (the same tensor in fp64) is given instead
  *   w     [(N+1)D][3]     short conv taps in PyTorch Conv1d order
  *   h     [N-1][D][L]     long filters
  *   bias  [N-1][D]
@@ -165,9 +178,9 @@ void oracle_causal_conv_fft(const double* v, const double* h, int64_t L, double*
  * Returns 0 on success, -1 on invalid arguments.
  */
 int oracle_hyena_forward(int64_t B, int64_t D, int64_t L, int N,
-                         const float* u, const float* w, const float* h, const float* bias,
+                         const float* u, const double* u64, const float* w, const float* h, const float* bias,
                          const int64_t* rows, int64_t nrows, double* y, int mode, int nthreads) {
-    if (B < 1 || D < 1 || L < 1 || N < 2 || !u || !w || !h || !bias || !y) return -1;
+    if (B < 1 || D < 1 || L < 1 || N < 2 || (!u && !u64) || !w || !h || !bias || !y) return -1;
     if (mode != 0 && mode != 1) return -1;
     const int64_t C = (int64_t)(N + 1) * D;
     const int64_t total = rows ? nrows : B * D;
@@ -209,7 +222,8 @@ int oracle_hyena_forward(int64_t B, int64_t D, int64_t L, int N,
                 for (int i = 0; i <= N; ++i) {
                     const int64_t ch = (int64_t)i * D + d;
                     double* dst = (i < N) ? xs + (int64_t)i * L : v;
-                    oracle_short_conv_row(u + (b * C + ch) * L, w + ch * 3, L, dst);
+                    if (u64) oracle_short_conv_row64(u64 + (b * C + ch) * L, w + ch * 3, L, dst);
+                    else oracle_short_conv_row(u + (b * C + ch) * L, w + ch * 3, L, dst);
                 }
                 /* the recurrence: step o pairs gate x_{N-1-o} with k[o], bias[o] */
                 for (int o = 0; o <= N - 2; ++o) {

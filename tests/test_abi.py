@@ -93,6 +93,11 @@ def test_forward_and_spectrum_reject_null_plan(lib):
     assert lib.hyena_filter_spectrum(None, 16, 16, None) == 1
 
 
+def test_operator_rejects_null_plan(lib):
+    assert lib.hyena_operator_workspace_bytes(None, 1) == 0
+    assert lib.hyena_operator_forward(None, 1, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 20, None) == 1
+
+
 def test_backward_rejects_null_plan(lib):
     assert lib.hyena_backward_workspace_bytes(None, 1) == 0
     assert lib.hyena_backward(None, 1, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 20, None) == 1
