@@ -20,6 +20,7 @@
 
 #include <mutex>
 #include <new>
+#include <vector>
 
 #include "../../include/hyena.h"
 #include "plan.hpp"
@@ -43,6 +44,7 @@ struct Gemm {
     hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr, d = nullptr;
     hipblasLtMatmulAlgo_t algo{};
     size_t ws = 0;
+    std::vector<hipblasLtMatmulAlgo_t> cand;  // heuristic candidates, timed on first use
     void release() {
         if (desc) hipblasLtMatmulDescDestroy(desc);
         for (auto* l : {&a, &b, &c, &d})
@@ -53,11 +55,12 @@ struct Gemm {
 };
 
 // Per-plan operator state: the hipBLASLt handle and the descriptors of both GEMMs
-// (one sequence each). Built on first use, under the mutex.
+// (one sequence each). Built on first use, under the mutex; the first call also
+// times the heuristic's candidate kernels on its own buffers and keeps the fastest.
 struct OpState {
     std::mutex mu;
     hipblasLtHandle_t lt = nullptr;
-    bool built = false;
+    bool built = false, tuned = false;
     Gemm in, out;
     ~OpState() {
         in.release();
@@ -72,26 +75,65 @@ bool layout(hipblasLtMatrixLayout_t* l, hipDataType t, uint64_t rows, uint64_t c
     return hipblasLtMatrixLayoutCreate(l, t, rows, cols, ld) == HIPBLAS_STATUS_SUCCESS;
 }
 
+constexpr int kCandidates = 16;
+
 bool pick_algo(hipblasLtHandle_t lt, Gemm& g) {
     hipblasLtMatmulPreference_t pref = nullptr;
     if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) return false;
     const uint64_t maxws = kLtWorkspace;
     hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &maxws, sizeof(maxws));
-    hipblasLtMatmulHeuristicResult_t res[1];
+    hipblasLtMatmulHeuristicResult_t res[kCandidates];
     int n = 0;
-    const hipblasStatus_t st = hipblasLtMatmulAlgoGetHeuristic(lt, g.desc, g.a, g.b, g.c, g.d, pref, 1, res, &n);
+    const hipblasStatus_t st =
+        hipblasLtMatmulAlgoGetHeuristic(lt, g.desc, g.a, g.b, g.c, g.d, pref, kCandidates, res, &n);
     hipblasLtMatmulPreferenceDestroy(pref);
-    if (st != HIPBLAS_STATUS_SUCCESS || n < 1 || res[0].state != HIPBLAS_STATUS_SUCCESS) return false;
-    g.algo = res[0].algo;
-    g.ws = res[0].workspaceSize;
-    return g.ws <= kLtWorkspace;
+    if (st != HIPBLAS_STATUS_SUCCESS) return false;
+    g.cand.clear();
+    for (int i = 0; i < n; ++i)
+        if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= kLtWorkspace) g.cand.push_back(res[i].algo);
+    if (g.cand.empty()) return false;
+    g.algo = g.cand[0];  // the heuristic's first choice until timed
+    return true;
+}
+
+// Times every candidate of g on the given operands (one warm-up and three timed
+// calls each, HIP events on `stream`) and keeps the fastest. The operands are the
+// call's own buffers; the output is rewritten by the real call afterwards.
+void tune(hipblasLtHandle_t lt, Gemm& g, const void* alpha, const void* A, const void* B, const void* beta,
+          const void* C, void* Dm, void* ws, hipStream_t stream) {
+    if (g.cand.size() < 2) return;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return;
+    }
+    float best = 1e30f;
+    for (const auto& algo : g.cand) {
+        if (hipblasLtMatmul(lt, g.desc, alpha, A, g.a, B, g.b, beta, C, g.c, Dm, g.d, &algo, ws, kLtWorkspace,
+                            stream) != HIPBLAS_STATUS_SUCCESS)
+            continue;
+        (void)hipEventRecord(e0, stream);
+        bool ok = true;
+        for (int r = 0; r < 3 && ok; ++r)
+            ok = hipblasLtMatmul(lt, g.desc, alpha, A, g.a, B, g.b, beta, C, g.c, Dm, g.d, &algo, ws, kLtWorkspace,
+                                 stream) == HIPBLAS_STATUS_SUCCESS;
+        (void)hipEventRecord(e1, stream);
+        if (!ok || hipEventSynchronize(e1) != hipSuccess) continue;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, e0, e1) == hipSuccess && ms < best) {
+            best = ms;
+            g.algo = algo;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
 }
 
 // Descriptors of both GEMMs for one sequence (column-major views, see the file header).
 bool build(OpState& s, const hyena_plan_s* plan) {
     s.in.release();
     s.out.release();
-    s.built = false;
+    s.built = s.tuned = false;
     const bool bf16 = plan->dtype == HYENA_BF16;
     const hipDataType dt = bf16 ? HIP_R_16BF : HIP_R_32F;
     const int64_t L = plan->L, D = plan->D, C = (int64_t)(plan->order + 1) * plan->D;
@@ -221,6 +263,13 @@ hyena_status_t operator_impl(hyena_plan_t plan, int64_t B, const void* x, const 
         hipLaunchKernelGGL(k_bias_matrix<float>, dim3(grid), dim3(256), 0, stream, (const float*)b_in, (float*)c.cb,
                            L, C);
     if (hipGetLastError() != hipSuccess) st = HYENA_ERR_DEVICE;
+    if (st == HYENA_OK && !s.tuned) {
+        // first call on this plan: time the candidates on sequence 0's operands
+        tune(s.lt, s.in, &one, x, w_in, &one, c.cb, c.u, c.lt, stream);
+        hipblasLtMatmulDescSetAttribute(s.out.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &b_out, sizeof(b_out));
+        tune(s.lt, s.out, &one, w_out, c.y, &zero, out, out, c.lt, stream);
+        s.tuned = true;
+    }
     for (int64_t b = 0; b < B && st == HYENA_OK; ++b) {
         const char* xb = static_cast<const char*>(x) + (size_t)b * L * D * es;
         char* ub = static_cast<char*>(c.u) + (size_t)b * C * L * es;
