@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"
+
 namespace hy {
 
 struct LdsBwdArgs {
@@ -31,5 +33,55 @@ inline size_t bwd_ws_bytes(int64_t B, int64_t D, int64_t L, int N) {
 }
 
 hipError_t launch_lds_backward(int logL, const LdsBwdArgs& a, hipStream_t st);
+
+// Four-step backward (order 2): arguments and the workspace it carves.
+struct FsBwdArgs {
+    const void* u;
+    const float* w3;
+    const float2* spec;
+    const float* bias;
+    const void* dy;
+    void* du;
+    float* dw;
+    float* dh;
+    float* dbias;
+    void* ws;  // fs_bwd_ws_bytes(logL, B, D) bytes
+    FsTables tb;
+    int B, D, N;
+    bool bf16;
+};
+
+// Per (b, d) row: the L-point tile T, the gated input's spectrum G and the product
+// spectrum P (complex), the three channels' staging rows S (fp32), the tap sums
+// of every column-block workgroup; per channel d the dh tile. 256-byte aligned.
+struct FsBwdWs {
+    float2* T;
+    float2* G;
+    float2* P;
+    float* S;
+    float2* Tdh;
+    float* part;
+    size_t bytes;
+};
+inline FsBwdWs fs_bwd_ws(void* base, int64_t B, int64_t D, int64_t L, int ncb) {
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        void* r = base ? static_cast<char*>(base) + off : nullptr;
+        off += (n + 255) & ~(size_t)255;
+        return r;
+    };
+    const size_t rows = (size_t)(B * D);
+    FsBwdWs w;
+    w.T = (float2*)take(rows * (size_t)L * 8);
+    w.G = (float2*)take(rows * (size_t)L * 8);
+    w.P = (float2*)take(rows * (size_t)L * 8);
+    w.S = (float*)take(rows * 3 * (size_t)L * 4);
+    w.Tdh = (float2*)take((size_t)D * (size_t)L * 8);
+    w.part = (float*)take(rows * (size_t)ncb * 9 * 4);
+    w.bytes = off;
+    return w;
+}
+hipError_t launch_fs_backward(int logL, const FsBwdArgs& a, hipStream_t st);
+size_t fs_bwd_ws_bytes(int logL, int64_t B, int64_t D);
 
 }  // namespace hy

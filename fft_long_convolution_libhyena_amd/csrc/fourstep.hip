@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include "fft_core.hpp"
+#include "fourstep.hpp"
 #include "kernels.hpp"
 #include "pair.hpp"
 
@@ -48,292 +49,6 @@ hipError_t launch_lds_forward_t(const LdsArgs& a, hipStream_t st);
 template <int LOGL>
 hipError_t launch_lds_spectrum_t(const float* h, float2* spec, int64_t rows, const float2* tw, const float2* wpair,
                                  hipStream_t st);
-
-// ============================================================ four-step path
-//
-// Workgroups are spread over the 8 XCDs round-robin by hardware; the mapping
-// below gives every row of a chunk to one XCD (row % 8) in all three passes, so
-// the neighbouring column blocks that share conv3 halo lines, and the passes that
-// re-read a row's tile, meet in the same L2.
-__device__ __forceinline__ bool xcd_row_map(int64_t bid, int64_t nrows, int per_row, int64_t& row, int& sub) {
-    const int xcd = (int)(bid & 7);
-    const int64_t s = bid >> 3;
-    sub = (int)(s % per_row);
-    row = (s / per_row) * 8 + xcd;
-    return row < nrows;
-}
-__host__ __device__ constexpr int64_t xcd_grid(int64_t nrows, int per_row) { return ((nrows + 7) / 8) * 8 * per_row; }
-
-// The four-step twiddle W_L^(k1*m2) for k1 = t + T1*e: W_L^(t*m2) * W_L^(T1*e*m2),
-// from two tables laid out [t][m2] and [e][m2] so that the 16 columns of a pass A
-// or pass C workgroup read consecutive entries.
-template <int L2>
-__device__ __forceinline__ float2 twiddle_base(const FsTables& tb, int t, int m2) {
-    return tb.tbase[(uint32_t)t * L2 + m2];
-}
-template <int L2>
-__device__ __forceinline__ float2 twiddle_step(const FsTables& tb, float2 base, int e, int m2) {
-    return cmul(base, tb.tstep[(uint32_t)e * L2 + m2]);
-}
-
-// Pass A: column FFTs over m1 of the packed gated input (MODE 0) or of a filter
-// row (MODE 1), written to the row-major [k1][m2] tile `slot` of row `flat`.
-template <int LOG1, int LOG2, class TIO, int MODE>
-__device__ __forceinline__ void fs_colfwd_body(float2* lds, const TIO* __restrict__ u, const float* __restrict__ w3,
-                                               const float* __restrict__ h, float2* __restrict__ slot,
-                                               const FsTables& tb, int D, int N, int64_t flat, int cb) {
-    using Cfg = FsCfg<LOG1, LOG2>;
-    constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T1 = Cfg::T1, CB = Cfg::CB;
-    constexpr int64_t L = (int64_t)L1 * L2;
-    const int c = threadIdx.x % CB, t = threadIdx.x / CB;
-    const int m2 = cb * CB + c;
-    float2 v[16];
-    if constexpr (MODE == 0) {
-        const uint32_t b = (uint32_t)flat / (uint32_t)D, d = (uint32_t)flat - b * (uint32_t)D;
-        const int64_t C = (int64_t)(N + 1) * D;
-        const int64_t cv = N * D + d, cx = (N - 1) * D + d;
-        const TIO* rv = u + (b * C + cv) * L;
-        const TIO* rx = u + (b * C + cx) * L;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
-            v[e] = gated_pair(rv, rx, m, w3 + 3 * cv, w3 + 3 * cx);
-        }
-    } else {
-        const float* hr = h + flat * L;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = load_pair(hr, (uint32_t)(t + T1 * e) * L2 + m2);
-    }
-#pragma unroll
-    for (int e = 8; e < 16; ++e) v[e] = make_float2(0.f, 0.f);
-    fft_strided<L1, false, true>(v, t, tb.tw1, ColAcc<Cfg::CP>{lds + c});
-    // four-step twiddle W_L^(k1*m2), applied here so that pass B carries none
-    const float2 base = twiddle_base<L2>(tb, t, m2);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) slot[(uint32_t)(t + T1 * e) * L2 + m2] = cmul(v[e], twiddle_step<L2>(tb, base, e, m2));
-}
-
-template <int LOG1, int LOG2, class TIO, int MODE>
-__global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::COL_THREADS))
-k_fs_colfwd(const TIO* __restrict__ u, const float* __restrict__ w3, const float* __restrict__ h,
-            float2* __restrict__ ws, FsTables tb, int D, int N, int64_t row0, int64_t nrows) {
-    using Cfg = FsCfg<LOG1, LOG2>;
-    __shared__ float2 lds[Cfg::L1 * Cfg::CP];
-    int64_t r;
-    int cb;
-    if (!xcd_row_map(blockIdx.x, nrows, Cfg::L2 / Cfg::CB, r, cb)) return;
-    const int64_t L = (int64_t)Cfg::L1 * Cfg::L2;
-    float2* slot = (MODE == 0) ? ws + r * L : ws + (row0 + r) * L;
-    fs_colfwd_body<LOG1, LOG2, TIO, MODE>(lds, u, w3, h, slot, tb, D, N, row0 + r, cb);
-}
-
-// Where one pair slot of pass B lives: LDS rows/indices of its two bins, the
-// offsets of their spectrum values in the [k1][k2] spectrum tile, and W_{2L}^k.
-struct PairSlot {
-    int ra, ia, rb, ib;  // LDS row slot (0 = row a, 1 = row b of the unit) and index
-    int offa, offb;      // spectrum offsets
-    float2 w;
-    int kind;  // 0 general pair, 1 the two self-contained bins k = 0 and k = L/2
-};
-
-template <int L1, int L2>
-__device__ __forceinline__ PairSlot pair_slot(int p, int k2, const FsTables& tb) {
-    PairSlot ps;
-    ps.kind = 0;
-    if (p != 0) {
-        // k = p + L1*k2 pairs with L - k = (L1-p) + L1*(L2-1-k2)
-        ps.ra = 0; ps.ia = k2; ps.rb = 1; ps.ib = L2 - 1 - k2;
-        ps.offa = p * L2 + ps.ia;
-        ps.offb = (L1 - p) * L2 + ps.ib;
-        ps.w = cmul(tb.pa[p], tb.pb[k2]);
-    } else if (k2 == 0) {
-        // k = 0 (with L) and k = L/2, both in row 0
-        ps.kind = 1;
-        ps.ra = 0; ps.ia = 0; ps.rb = 0; ps.ib = L2 / 2;
-        ps.offa = 0;
-        ps.offb = L2 / 2;
-        ps.w = tb.pb[L2 / 2];
-    } else if (k2 < L2 / 2) {
-        // row 0: k = L1*k2 pairs with L1*(L2-k2)
-        ps.ra = 0; ps.ia = k2; ps.rb = 0; ps.ib = L2 - k2;
-        ps.offa = ps.ia;
-        ps.offb = ps.ib;
-        ps.w = tb.pb[k2];
-    } else {
-        // row L1/2: k = L1/2 + L1*j pairs with L1/2 + L1*(L2-1-j)
-        const int j = k2 - L2 / 2;
-        ps.ra = 1; ps.ia = j; ps.rb = 1; ps.ib = L2 - 1 - j;
-        ps.offa = (L1 / 2) * L2 + ps.ia;
-        ps.offb = (L1 / 2) * L2 + ps.ib;
-        ps.w = cmul(tb.pa[L1 / 2], tb.pb[j]);
-    }
-    return ps;
-}
-
-// Pass B: row FFTs over m2 (the tile already carries the W_L^(k1*m2) twiddle),
-// the pair step, then (MODE 0) the spectrum multiply and the inverse rows, in
-// place; or (MODE 1) the scaled spectrum written in place.
-// A unit is the row pair {p, L1-p} (p >= 1) or {0, L1/2} (p = 0).
-template <int LOG1, int LOG2, int MODE>
-__device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ slot, const float2* __restrict__ spec,
-                                            const float* __restrict__ bias, const FsTables& tb, int D, int o,
-                                            int64_t flat, int ug) {
-    using Cfg = FsCfg<LOG1, LOG2>;
-    constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T2 = Cfg::T2, U = Cfg::UNITS, RP = Cfg::RP;
-    constexpr int64_t L = (int64_t)L1 * L2;
-    const int tau = threadIdx.x;
-    const int rho = tau / T2, t = tau % T2;
-    const int p_row = ug * U + rho / 2;
-    const int k1 = (rho & 1) == 0 ? p_row : (p_row == 0 ? L1 / 2 : L1 - p_row);
-    float2* rowp = slot + (uint32_t)k1 * L2;
-    const RowAcc racc{lds + rho * RP};
-
-    // pair-step role of this thread: 2*T2 threads per unit, L2 pairs per unit
-    const int unit = tau / (2 * T2), tp = tau % (2 * T2);
-    const int p = ug * U + unit;
-    const float2* Hrow = nullptr;
-    float bs = 0.f;
-    float2 ha[8], hb[8];
-    if constexpr (MODE == 0) {
-        const uint32_t d = (uint32_t)flat % (uint32_t)D;
-        Hrow = spec + ((int64_t)o * D + d) * L;
-        bs = bias[(int64_t)o * D + d] * (1.0f / (4.0f * (float)L));
-    }
-
-    float2 v[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = rowp[(uint32_t)(t + T2 * e)];
-    if constexpr (MODE == 0) {
-        // the spectrum is needed only after the forward rows; fetch it now
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const PairSlot ps = pair_slot<L1, L2>(p, tp + 2 * T2 * e, tb);
-            ha[e] = Hrow[(uint32_t)ps.offa];
-            hb[e] = Hrow[(uint32_t)ps.offb];
-        }
-    }
-    fft_strided<L2, false, false>(v, t, tb.tw2, racc);
-    __syncthreads();
-    lds_store_strided<T2>(racc, t, v);
-    __syncthreads();
-
-    const RowAcc au[2] = {RowAcc{lds + (2 * unit) * RP}, RowAcc{lds + (2 * unit + 1) * RP}};
-    const float sc = 1.0f / (8.0f * (float)L);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const PairSlot ps = pair_slot<L1, L2>(p, tp + 2 * T2 * e, tb);
-        const float2 Za = au[ps.ra][ps.ia];
-        const float2 Zb = au[ps.rb][ps.ib];
-        if constexpr (MODE == 0) {
-            float2 Yk, Ym;
-            if (ps.kind == 0) {
-                pair_conv(Za, Zb, hadd(ha[e], bs), hadd(hb[e], bs), ps.w, Yk, Ym);
-                au[ps.ra][ps.ia] = Yk;
-                au[ps.rb][ps.ib] = Ym;
-            } else {
-                // bin 0 pairs with bin L (spectrum slot 0 holds (H[0], H[L]))
-                pair_conv(Za, Za, make_float2(ha[e].x + bs, 0.f), make_float2(ha[e].y + bs, 0.f),
-                          make_float2(1.f, 0.f), Yk, Ym);
-                au[ps.ra][ps.ia] = Yk;
-                const float2 Hh = hadd(hb[e], bs);  // bin L/2 pairs with itself
-                pair_conv(Zb, Zb, Hh, Hh, ps.w, Yk, Ym);
-                au[ps.rb][ps.ib] = Yk;
-            }
-        } else {
-            float2 Ak, Am;
-            if (ps.kind == 0) {
-                pair_unpack(Za, Zb, ps.w, Ak, Am);
-                slot[(uint32_t)ps.offa] = fmul2(Ak, sc);
-                slot[(uint32_t)ps.offb] = fmul2(Am, sc);
-            } else {
-                pair_unpack(Za, Za, make_float2(1.f, 0.f), Ak, Am);
-                slot[0] = make_float2(Ak.x * sc, Am.x * sc);
-                pair_unpack(Zb, Zb, ps.w, Ak, Am);
-                slot[(uint32_t)ps.offb] = fmul2(Ak, sc);
-            }
-        }
-    }
-    if constexpr (MODE == 0) {
-        __syncthreads();
-        lds_load_strided<T2>(racc, t, v);
-        fft_strided<L2, true, false>(v, t, tb.tw2, racc);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) rowp[(uint32_t)(t + T2 * e)] = v[e];
-    }
-}
-
-template <int LOG1, int LOG2, int MODE>
-__global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::ROW_THREADS))
-k_fs_row(float2* __restrict__ ws, const float2* __restrict__ spec, const float* __restrict__ bias, FsTables tb,
-         int D, int o, int64_t row0, int64_t nrows) {
-    using Cfg = FsCfg<LOG1, LOG2>;
-    __shared__ float2 lds[2 * Cfg::UNITS * Cfg::RP];
-    int64_t r;
-    int ug;
-    if (!xcd_row_map(blockIdx.x, nrows, Cfg::L1 / 2 / Cfg::UNITS, r, ug)) return;
-    const int64_t L = (int64_t)Cfg::L1 * Cfg::L2;
-    float2* slot = (MODE == 0) ? ws + r * L : ws + (row0 + r) * L;
-    fs_row_body<LOG1, LOG2, MODE>(lds, slot, spec, bias, tb, D, o, row0 + r, ug);
-}
-
-// Pass C: the conjugate four-step twiddle, inverse column FFTs over k1, then
-// the gate. The last step stores y;
-// otherwise the gated result is the next step's input and its forward column
-// FFTs (pass A of step o+1) run here, written back in place.
-template <int LOG1, int LOG2, class TIO, bool LAST>
-__device__ __forceinline__ void fs_colinv_body(float2* lds, float2* __restrict__ slot, const TIO* __restrict__ u,
-                                               const float* __restrict__ w3, TIO* __restrict__ y, const FsTables& tb,
-                                               int D, int N, int o, int64_t flat, int cb) {
-    using Cfg = FsCfg<LOG1, LOG2>;
-    constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T1 = Cfg::T1, CB = Cfg::CB;
-    constexpr int64_t L = (int64_t)L1 * L2;
-    const uint32_t b = (uint32_t)flat / (uint32_t)D, d = (uint32_t)flat - b * (uint32_t)D;
-    const int c = threadIdx.x % CB, t = threadIdx.x / CB;
-    const int m2 = cb * CB + c;
-    const ColAcc<Cfg::CP> cacc{lds + c};
-    float2 v[16];
-    const float2 base = twiddle_base<L2>(tb, t, m2);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = cmulc(slot[(uint32_t)(t + T1 * e) * L2 + m2], twiddle_step<L2>(tb, base, e, m2));
-    fft_strided<L1, true, false>(v, t, tb.tw1, cacc);
-    const int64_t C = (int64_t)(N + 1) * D;
-    const int64_t cg = (int64_t)(LAST ? 0 : N - 2 - o) * D + d;
-    const TIO* rg = u + (b * C + cg) * L;
-    const float* wg = w3 + 3 * cg;
-    if constexpr (LAST) {
-        TIO* yr = y + (b * D + d) * L;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
-            store_pair(yr, m, emul(v[e], conv3_pair(rg, m, wg[0], wg[1], wg[2])));
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
-            v[e] = emul(v[e], conv3_pair(rg, m, wg[0], wg[1], wg[2]));
-        }
-#pragma unroll
-        for (int e = 8; e < 16; ++e) v[e] = make_float2(0.f, 0.f);
-        fft_strided<L1, false, true>(v, t, tb.tw1, cacc);
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            slot[(uint32_t)(t + T1 * e) * L2 + m2] = cmul(v[e], twiddle_step<L2>(tb, base, e, m2));
-    }
-}
-
-template <int LOG1, int LOG2, class TIO, bool LAST>
-__global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::COL_THREADS))
-k_fs_colinv(float2* __restrict__ ws, const TIO* __restrict__ u, const float* __restrict__ w3, TIO* __restrict__ y,
-            FsTables tb, int D, int N, int o, int64_t row0, int64_t nrows) {
-    using Cfg = FsCfg<LOG1, LOG2>;
-    __shared__ float2 lds[Cfg::L1 * Cfg::CP];
-    int64_t r;
-    int cb;
-    if (!xcd_row_map(blockIdx.x, nrows, Cfg::L2 / Cfg::CB, r, cb)) return;
-    const int64_t L = (int64_t)Cfg::L1 * Cfg::L2;
-    fs_colinv_body<LOG1, LOG2, TIO, LAST>(lds, ws + r * L, u, w3, y, tb, D, N, o, row0 + r, cb);
-}
 
 // ====================================================== fused persistent path
 //
@@ -599,19 +314,6 @@ static hipError_t fs_spectrum_t(const float* h, float2* spec, int64_t rows, cons
                        (const float2*)nullptr, (const float*)nullptr, tb, 1, 0, (int64_t)0, rows);
     return hipGetLastError();
 }
-
-// log2 L -> (log2 L1, log2 L2). Square splits up to L1 = 512, whose pass A/C
-// tile (512 x 17 complex) still leaves room for two workgroups per CU.
-#ifndef HY_FS_LOG1_16
-#define HY_FS_LOG1_16 8
-#endif
-#ifndef HY_FS_LOG1_20
-#define HY_FS_LOG1_20 9
-#endif
-#define HY_FS_CASES(X)                                                                                   \
-    X(8, 4, 4) X(9, 4, 5) X(10, 5, 5) X(11, 5, 6) X(12, 6, 6) X(13, 6, 7) X(14, 7, 7) X(15, 7, 8)          \
-        X(16, HY_FS_LOG1_16, 16 - HY_FS_LOG1_16) X(17, 8, 9) X(18, 9, 9) X(19, 9, 10)                     \
-        X(20, HY_FS_LOG1_20, 20 - HY_FS_LOG1_20)
 
 void fs_split(int logL, int* log1, int* log2) {
     switch (logL) {

@@ -1,0 +1,325 @@
+// Backward of the order-2 hot path on the four-step sizes (L = L1 * L2 > 16384 by
+// default), for gfx950. The chain rule is the one of lds_backward.hpp (HyenaDNA
+// walkthrough, section 2.1, HyenaOperator.forward; section 2.2, fftconv): with
+// g = v0 * x1 and v1 = conv(g, h) + bias * g,
+//   dv1 = dy * x0,  dx0 = dy * v1,  dg = corr(dv1, h) + bias * dv1,
+//   dx1 = dg * v0,  dv0 = dg * x1,  dh = sum_b corr(dv1, g),  dbias = dh[0],
+// and the short conv's transpose and tap sums for the three channels.
+// corr is taken through the same zero-padded spectra with conj(H + bias).
+//
+// Nine launches over all B*D rows (each row's tile lives in the workspace):
+//  1 pass A of the forward (column FFTs of g)                       -> T
+//  2 pass B, mode 2: rows, spectrum multiply, inverse rows, A_g     -> T, G
+//  3 column pass HEAD: inverse columns = v1; dx0 -> S0; columns of dv1 -> T
+//  4 pass B, mode 3: rows, P = A_dv conj(A_g), conj(H + bias), inverse -> T, P
+//  5 column pass TAIL: inverse columns = dg; dx1 -> S1, dv0 -> S2
+//  6 du = conv3^T of S0, S1, S2 (neighbouring samples are now plain row reads)
+//  7, 8 dh: the batch sum of P per channel, repacked and inverted by rows and
+//       columns; dbias its lag-0 value
+//  9 dshort_w: the sum of the per-workgroup tap sums of passes 3 and 5
+// Every sum over the batch or over workgroups is taken in a fixed order.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "backward.hpp"
+#include "fft_core.hpp"
+#include "fourstep.hpp"
+#include "kernels.hpp"
+#include "pair.hpp"
+
+namespace hy {
+
+namespace {
+
+// Tap gradients of the short conv: dw[j] += duc[2m] u[2m-2+j] + duc[2m+1] u[2m-1+j].
+__device__ __forceinline__ void fs_tap_sums(float2 dc, float2 prev, float2 cur, float (&s)[3]) {
+    s[0] = fmaf(dc.x, prev.x, fmaf(dc.y, prev.y, s[0]));
+    s[1] = fmaf(dc.x, prev.y, fmaf(dc.y, cur.x, s[1]));
+    s[2] = fmaf(dc.x, cur.x, fmaf(dc.y, cur.y, s[2]));
+}
+
+template <class TIO>
+__device__ __forceinline__ void fs_raw_pairs(const TIO* __restrict__ row, uint32_t m, float2& prev, float2& cur) {
+    cur = load_pair(row, m);
+    prev = m > 0 ? load_pair(row, m - 1) : make_float2(0.f, 0.f);
+}
+
+}  // namespace
+
+template <int LOG1, int LOG2, int MODE>
+__global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::ROW_THREADS))
+k_fs_row_bwd(float2* __restrict__ T, const float2* __restrict__ spec, const float* __restrict__ bias,
+             float2* __restrict__ G, float2* __restrict__ P, FsTables tb, int D, int64_t nrows) {
+    using Cfg = FsCfg<LOG1, LOG2>;
+    __shared__ float2 lds[2 * Cfg::UNITS * Cfg::RP];
+    int64_t r;
+    int ug;
+    if (!xcd_row_map(blockIdx.x, nrows, Cfg::L1 / 2 / Cfg::UNITS, r, ug)) return;
+    const int64_t L = (int64_t)Cfg::L1 * Cfg::L2;
+    fs_row_body<LOG1, LOG2, MODE>(lds, T + r * L, spec, bias, tb, D, 0, r, ug, G + r * L,
+                                  P ? P + r * L : nullptr);
+}
+
+// Column pass of the backward. HEAD: the inverse columns give v1; with dy and x0,
+// dx0 = dy*v1 goes to S0 and dv1 = dy*x0 is transformed by columns back into the
+// tile. TAIL: the inverse columns give dg; with x1 and v0, dx1 = dg*v0 goes to S1
+// and dv0 = dg*x1 to S2. Both add the finished channels' tap sums into
+// part[row][column block][channel][tap].
+template <int LOG1, int LOG2, class TIO, bool HEAD>
+__global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::COL_THREADS))
+k_fs_colinv_bwd(float2* __restrict__ T, const TIO* __restrict__ u, const float* __restrict__ w3,
+                const TIO* __restrict__ dy, float* __restrict__ S, float* __restrict__ part, FsTables tb, int D,
+                int64_t nrows) {
+    using Cfg = FsCfg<LOG1, LOG2>;
+    constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T1 = Cfg::T1, CB = Cfg::CB, NCB = L2 / CB;
+    constexpr int NT = Cfg::COL_THREADS;
+    constexpr int64_t L = (int64_t)L1 * L2;
+    __shared__ float2 lds[L1 * Cfg::CP];
+    int64_t r;
+    int cb;
+    if (!xcd_row_map(blockIdx.x, nrows, NCB, r, cb)) return;
+    const uint32_t b = (uint32_t)r / (uint32_t)D, d = (uint32_t)r - b * (uint32_t)D;
+    const int64_t C = 3 * (int64_t)D;
+    const int c = threadIdx.x % CB, t = threadIdx.x / CB;
+    const int m2 = cb * CB + c;
+    const ColAcc<Cfg::CP> cacc{lds + c};
+    float2* slot = T + r * L;
+    float2 v[16];
+    const float2 base = twiddle_base<L2>(tb, t, m2);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = cmulc(slot[(uint32_t)(t + T1 * e) * L2 + m2], twiddle_step<L2>(tb, base, e, m2));
+    fft_strided<L1, true, false>(v, t, tb.tw1, cacc);
+    float* Sr = S + r * 3 * L;  // staging rows of channels 0, 1, 2 (time domain, fp32)
+    float s0[3] = {0.f, 0.f, 0.f}, s1[3] = {0.f, 0.f, 0.f};
+    if constexpr (HEAD) {
+        const TIO* dyr = dy + r * L;
+        const TIO* x0r = u + ((int64_t)b * C + d) * L;
+        const float* wx = w3 + 3 * (int64_t)d;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
+            const float2 g = load_pair(dyr, m);
+            float2 prev, cur;
+            fs_raw_pairs(x0r, m, prev, cur);
+            const float2 dx = emul(g, v[e]);  // dy * v1
+            store_pair(Sr, m, dx);
+            fs_tap_sums(dx, prev, cur, s0);
+            v[e] = emul(g, conv3_from(prev, cur, wx[0], wx[1], wx[2]));  // dv1 = dy * x0
+        }
+#pragma unroll
+        for (int e = 8; e < 16; ++e) v[e] = make_float2(0.f, 0.f);
+        fft_strided<L1, false, true>(v, t, tb.tw1, cacc);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            slot[(uint32_t)(t + T1 * e) * L2 + m2] = cmul(v[e], twiddle_step<L2>(tb, base, e, m2));
+    } else {
+        const TIO* x1r = u + ((int64_t)b * C + D + d) * L;
+        const TIO* vr = u + ((int64_t)b * C + 2 * D + d) * L;
+        const float* wx = w3 + 3 * ((int64_t)D + d);
+        const float* wv = w3 + 3 * ((int64_t)2 * D + d);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
+            float2 xp, xc, vp, vc;
+            fs_raw_pairs(x1r, m, xp, xc);
+            fs_raw_pairs(vr, m, vp, vc);
+            const float2 dx1 = emul(v[e], conv3_from(vp, vc, wv[0], wv[1], wv[2]));  // dg * v0
+            const float2 dv0 = emul(v[e], conv3_from(xp, xc, wx[0], wx[1], wx[2]));  // dg * x1
+            store_pair(Sr + L, m, dx1);
+            store_pair(Sr + 2 * L, m, dv0);
+            fs_tap_sums(dx1, xp, xc, s0);
+            fs_tap_sums(dv0, vp, vc, s1);
+        }
+    }
+    // this workgroup's tap sums
+    constexpr int NQ = HEAD ? 3 : 6;
+    static_assert(NQ * NT * 4 <= L1 * Cfg::CP * 8, "reduction buffer fits in the column tile's LDS");
+    float* red = reinterpret_cast<float*>(lds);
+    const int tid = threadIdx.x;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        red[q * NT + tid] = s0[q];
+        if constexpr (!HEAD) red[(3 + q) * NT + tid] = s1[q];
+    }
+    __syncthreads();
+    if (tid < NQ) {
+        float sum = 0.f;
+        for (int k = 0; k < NT; ++k) sum += red[tid * NT + k];
+        // channel 0 taps at 0..2 (HEAD); channels 1 and 2 at 3..8 (TAIL)
+        part[(r * NCB + cb) * 9 + (HEAD ? 0 : 3) + tid] = sum;
+    }
+}
+
+// du[b][i*D + d][t] = w2 S_i[t] + w1 S_i[t+1] + w0 S_i[t+2], one thread per pair.
+template <class TIO>
+__global__ void k_fs_bwd_du(const float* __restrict__ S, const float* __restrict__ w3, TIO* __restrict__ du,
+                            int D, int64_t L, int64_t rows) {
+    const int64_t pairs = L / 2;
+    const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (m >= pairs) return;
+    for (int64_t ri = blockIdx.y; ri < rows * 3; ri += gridDim.y) {
+        const int64_t r = ri / 3;
+        const int i = (int)(ri - r * 3);
+        const int64_t b = r / D, d = r - b * D;
+        const float* s = S + ri * L;
+        const float2 dc = make_float2(s[2 * m], s[2 * m + 1]);
+        const float2 nx = 2 * m + 2 < L ? make_float2(s[2 * m + 2], s[2 * m + 3]) : make_float2(0.f, 0.f);
+        const float* w = w3 + 3 * ((int64_t)i * D + d);
+        store_pair(du + (b * 3 * D + (int64_t)i * D + d) * L, (uint32_t)m,
+                   make_float2(fmaf(w[2], dc.x, fmaf(w[1], dc.y, w[0] * nx.x)),
+                               fmaf(w[2], dc.y, fmaf(w[1], nx.x, w[0] * nx.y))));
+    }
+}
+
+// dh by rows: the batch sum of the product spectra of channel d, scaled and
+// repacked for the inverse (the pair step's second half), then inverse rows.
+template <int LOG1, int LOG2>
+__global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::ROW_THREADS))
+k_fs_dh_row(const float2* __restrict__ P, float2* __restrict__ Tdh, FsTables tb, int B, int D) {
+    using Cfg = FsCfg<LOG1, LOG2>;
+    constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T2 = Cfg::T2, U = Cfg::UNITS, RP = Cfg::RP;
+    constexpr int64_t L = (int64_t)L1 * L2;
+    __shared__ float2 lds[2 * U * RP];
+    int64_t dd;
+    int ug;
+    if (!xcd_row_map(blockIdx.x, D, L1 / 2 / U, dd, ug)) return;
+    const int tau = threadIdx.x;
+    const int rho = tau / T2, t = tau % T2;
+    const int p_row = ug * U + rho / 2;
+    const int k1 = (rho & 1) == 0 ? p_row : (p_row == 0 ? L1 / 2 : L1 - p_row);
+    float2* rowp = Tdh + dd * L + (uint32_t)k1 * L2;
+    const RowAcc racc{lds + rho * RP};
+    const int unit = tau / (2 * T2), tp = tau % (2 * T2);
+    const int p = ug * U + unit;
+    const RowAcc au[2] = {RowAcc{lds + (2 * unit) * RP}, RowAcc{lds + (2 * unit + 1) * RP}};
+    // repack + the unnormalised inverse of X gives the 2L-point inverse of 2L*X; the
+    // products carry the factor 4 of the unpacked values: X = P / (8L)
+    const float sc = 1.0f / (8.0f * (float)L);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const PairSlot ps = pair_slot<L1, L2>(p, tp + 2 * T2 * e, tb);
+        float2 Pa = make_float2(0.f, 0.f), Pb = make_float2(0.f, 0.f);
+        for (int b = 0; b < B; ++b) {
+            const float2* Pr = P + ((int64_t)b * D + dd) * L;
+            Pa = cadd(Pa, Pr[(uint32_t)ps.offa]);
+            Pb = cadd(Pb, Pr[(uint32_t)ps.offb]);
+        }
+        float2 Yk, Ym;
+        if (ps.kind == 0) {
+            pair_repack(fmul2(Pa, sc), fmul2(Pb, sc), ps.w, Yk, Ym);
+            au[ps.ra][ps.ia] = Yk;
+            au[ps.rb][ps.ib] = Ym;
+        } else {
+            // slot 0 holds the real bins 0 and L; offb is bin L/2
+            pair_repack(make_float2(Pa.x * sc, 0.f), make_float2(Pa.y * sc, 0.f), make_float2(1.f, 0.f), Yk, Ym);
+            au[ps.ra][ps.ia] = Yk;
+            pair_repack(fmul2(Pb, sc), fmul2(Pb, sc), ps.w, Yk, Ym);
+            au[ps.rb][ps.ib] = Yk;
+        }
+    }
+    __syncthreads();
+    float2 v[16];
+    lds_load_strided<T2>(racc, t, v);
+    fft_strided<L2, true, false>(v, t, tb.tw2, racc);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) rowp[(uint32_t)(t + T2 * e)] = v[e];
+}
+
+// dh by columns: conjugate twiddle, inverse columns, the first half is dh; the
+// workgroup holding sample 0 also writes dbias = dh[0].
+template <int LOG1, int LOG2>
+__global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::COL_THREADS))
+k_fs_dh_col(const float2* __restrict__ Tdh, float* __restrict__ dh, float* __restrict__ dbias, FsTables tb, int D) {
+    using Cfg = FsCfg<LOG1, LOG2>;
+    constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T1 = Cfg::T1, CB = Cfg::CB, NCB = L2 / CB;
+    constexpr int64_t L = (int64_t)L1 * L2;
+    __shared__ float2 lds[L1 * Cfg::CP];
+    int64_t dd;
+    int cb;
+    if (!xcd_row_map(blockIdx.x, D, NCB, dd, cb)) return;
+    const int c = threadIdx.x % CB, t = threadIdx.x / CB;
+    const int m2 = cb * CB + c;
+    const float2* slot = Tdh + dd * L;
+    float2 v[16];
+    const float2 base = twiddle_base<L2>(tb, t, m2);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = cmulc(slot[(uint32_t)(t + T1 * e) * L2 + m2], twiddle_step<L2>(tb, base, e, m2));
+    fft_strided<L1, true, false>(v, t, tb.tw1, ColAcc<Cfg::CP>{lds + c});
+    float* dhr = dh + dd * L;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) store_pair(dhr, (uint32_t)(t + T1 * e) * L2 + m2, v[e]);
+    if (t == 0 && m2 == 0) dbias[dd] = v[0].x;
+}
+
+// dshort_w[i*D + d][j] = sum over b and column blocks of the tap sums.
+__global__ void k_fs_bwd_dw(const float* __restrict__ part, float* __restrict__ dw, int B, int D, int ncb) {
+    const int d = blockIdx.x, q = threadIdx.x;  // q = 3*channel + tap
+    if (q >= 9) return;
+    float s = 0.f;
+    for (int b = 0; b < B; ++b) {
+        const float* pr = part + ((int64_t)b * D + d) * ncb * 9;
+        for (int k = 0; k < ncb; ++k) s += pr[k * 9 + q];
+    }
+    dw[((int64_t)(q / 3) * D + d) * 3 + (q % 3)] = s;
+}
+
+template <int LOG1, int LOG2, class TIO>
+static void fs_backward_launch(const FsBwdArgs& a, hipStream_t st) {
+    using Cfg = FsCfg<LOG1, LOG2>;
+    constexpr int NCB = Cfg::L2 / Cfg::CB;
+    const int64_t L = (int64_t)Cfg::L1 * Cfg::L2, rows = (int64_t)a.B * a.D;
+    const FsBwdWs w = fs_bwd_ws(a.ws, a.B, a.D, L, NCB);
+    const unsigned gcol = (unsigned)xcd_grid(rows, NCB);
+    const unsigned grow = (unsigned)xcd_grid(rows, Cfg::L1 / 2 / Cfg::UNITS);
+    const dim3 bcol(Cfg::COL_THREADS), brow(Cfg::ROW_THREADS);
+    const TIO* u = (const TIO*)a.u;
+    hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, TIO, 0>), dim3(gcol), bcol, 0, st, u, a.w3, (const float*)nullptr,
+                       w.T, a.tb, a.D, 2, (int64_t)0, rows);
+    hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 2>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G,
+                       (float2*)nullptr, a.tb, a.D, rows);
+    hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, true>), dim3(gcol), bcol, 0, st, w.T, u, a.w3,
+                       (const TIO*)a.dy, w.S, w.part, a.tb, a.D, rows);
+    hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 3>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G, w.P, a.tb,
+                       a.D, rows);
+    hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, false>), dim3(gcol), bcol, 0, st, w.T, u, a.w3,
+                       (const TIO*)a.dy, w.S, w.part, a.tb, a.D, rows);
+    const int64_t pairs = L / 2;
+    const unsigned gy = (unsigned)(rows * 3 < 65535 ? rows * 3 : 65535);
+    hipLaunchKernelGGL((k_fs_bwd_du<TIO>), dim3((unsigned)((pairs + 255) / 256), gy), dim3(256), 0, st,
+                       (const float*)w.S, a.w3, (TIO*)a.du, a.D, L, rows);
+    hipLaunchKernelGGL((k_fs_dh_row<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, Cfg::L1 / 2 / Cfg::UNITS)), brow, 0,
+                       st, (const float2*)w.P, w.Tdh, a.tb, a.B, a.D);
+    hipLaunchKernelGGL((k_fs_dh_col<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, NCB)), bcol, 0, st,
+                       (const float2*)w.Tdh, a.dh, a.dbias, a.tb, a.D);
+    hipLaunchKernelGGL(k_fs_bwd_dw, dim3((unsigned)a.D), dim3(64), 0, st, (const float*)w.part, a.dw, a.B, a.D,
+                       NCB);
+}
+
+template <int LOG1, int LOG2>
+static hipError_t fs_backward_t(const FsBwdArgs& a, hipStream_t st) {
+    if (a.bf16) fs_backward_launch<LOG1, LOG2, uint16_t>(a, st);
+    else fs_backward_launch<LOG1, LOG2, float>(a, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_fs_backward(int logL, const FsBwdArgs& a, hipStream_t st) {
+    if (a.N != 2) return hipErrorInvalidValue;
+    switch (logL) {
+#define X(LG, A, B) \
+    case LG: return fs_backward_t<A, B>(a, st);
+        HY_FS_CASES(X)
+#undef X
+        default: return hipErrorInvalidValue;
+    }
+}
+
+size_t fs_bwd_ws_bytes(int logL, int64_t B, int64_t D) {
+    int l1 = 0, l2 = 0;
+    fs_split(logL, &l1, &l2);
+    const int64_t L = int64_t(1) << logL;
+    const int ncb = (1 << l2) / HY_FS_CB;
+    return fs_bwd_ws(nullptr, B, D, L, ncb).bytes;
+}
+
+}  // namespace hy

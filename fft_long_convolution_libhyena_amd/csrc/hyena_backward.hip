@@ -10,8 +10,10 @@
 extern "C" {
 
 size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B) {
-    if (!plan || B < 1 || plan->path != HYENA_PATH_LDS) return 0;
-    return hy::bwd_ws_bytes(B, plan->D, plan->L, plan->order);
+    if (!plan || B < 1) return 0;
+    if (plan->path == HYENA_PATH_LDS) return hy::bwd_ws_bytes(B, plan->D, plan->L, plan->order);
+    if (plan->path == HYENA_PATH_FOURSTEP && plan->order == 2) return hy::fs_bwd_ws_bytes(plan->logL, B, plan->D);
+    return 0;
 }
 
 hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
@@ -24,11 +26,17 @@ hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, 
         !aligned16(du_proj) || !aligned16(dshort_w) || !aligned16(dh) || !aligned16(dbias))
         return HYENA_ERR_INVALID_ARG;
     if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 26)) return HYENA_ERR_INVALID_ARG;
-    if (plan->path != HYENA_PATH_LDS) return HYENA_ERR_UNSUPPORTED;
+    const bool fs = plan->path == HYENA_PATH_FOURSTEP;
+    if (!(plan->path == HYENA_PATH_LDS || (fs && plan->order == 2))) return HYENA_ERR_UNSUPPORTED;
     if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
     if (!workspace || !aligned16(workspace) || workspace_bytes < hyena_backward_workspace_bytes(plan, B))
         return HYENA_ERR_WORKSPACE;
     if (hy::check_device(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
+    if (fs) {
+        hy::FsBwdArgs a{u_proj, short_w, (const float2*)spec, bias, dy, du_proj, dshort_w, dh, dbias, workspace,
+                        plan->fs, (int)B, (int)plan->D, plan->order, plan->dtype == HYENA_BF16};
+        return hy::launch_fs_backward(plan->logL, a, stream) == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
+    }
     hy::LdsBwdArgs a{u_proj,   short_w,   (const float2*)spec, bias,      dy,         du_proj,
                      dshort_w, dh,        dbias,               (float2*)workspace, plan->tw, plan->wpair,
                      (int)B,   (int)plan->D, plan->order,       plan->dtype == HYENA_BF16};

@@ -164,12 +164,17 @@ hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_p
  * HYENA_ERR_INVALID_ARG for NULL arguments, HYENA_ERR_DEVICE if the copy fails. */
 hyena_status_t hyena_fused_check(hyena_plan_t plan, const void* workspace, int* flag);
 
-/* Bytes of workspace hyena_backward needs for batch B: per (b, d) row the N-1
- * product spectra that the batch sums of dh are taken from, the gated-input
- * spectra of steps 0..N-3 and the values v_1..v_{N-2} (8 bytes per complex or
- * pair value), then 3 floats of short-conv tap sums per (b, channel):
- * 8*B*D*((2N-3)*L + (N-2)*L/2) + 12*B*(N+1)*D. Returns 0 for a NULL plan, B < 1
- * or a plan whose path has no backward (FOURSTEP). */
+/* Bytes of workspace hyena_backward needs for batch B.
+ * LDS path: per (b, d) row the N-1 product spectra that the batch sums of dh are
+ * taken from, the gated-input spectra of steps 0..N-3 and the values v_1..v_{N-2}
+ * (8 bytes per complex or pair value), then 3 floats of short-conv tap sums per
+ * (b, channel): 8*B*D*((2N-3)*L + (N-2)*L/2) + 12*B*(N+1)*D.
+ * Four-step path (order 2 only): per (b, d) row three L-point complex tiles (the
+ * transform, the gated input's spectrum, the product spectrum) and three fp32
+ * staging rows, per channel one complex dh tile, and 36 bytes of tap sums per
+ * (row, column block), each region 256-byte aligned.
+ * Returns 0 for a NULL plan, B < 1, or a plan without a backward (four-step with
+ * order > 2). */
 size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* Backward of the forward hot path: given the upstream gradient dy of y, the
@@ -190,10 +195,10 @@ size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B);
  *           buffers' previous contents)
  *   workspace / workspace_bytes: device scratch of at least
  *           hyena_backward_workspace_bytes(plan, B); contents on entry irrelevant.
- * Only the LDS path (L <= 16384) has a backward in this build; other plans get
- * HYENA_ERR_UNSUPPORTED. Two launches: one workgroup per (b, d) row, then one
- * per (o, d) that sums the rows' partial results over the batch in a fixed
- * order (no atomics), so results are bitwise reproducible.
+ * Both paths have a backward: the LDS path for every order, the four-step path
+ * for order 2 (other orders get HYENA_ERR_UNSUPPORTED). Every sum over the batch
+ * or over workgroups is taken in a fixed order (no atomics), so results are
+ * bitwise reproducible.
  * Enqueued on `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL or misaligned
  * pointers, B < 1), HYENA_ERR_UNSUPPORTED, HYENA_ERR_WORKSPACE,
  * HYENA_ERR_DEVICE (launch failure, wrong current device). Outputs must not

@@ -26,7 +26,7 @@ def _gpu():
     yield
 
 
-def _run_backward(x, dy, repeat=1):
+def _run_backward(x, dy, repeat=1, path="lds"):
     import torch
 
     from fft_long_convolution_libhyena_amd import Plan
@@ -38,7 +38,7 @@ def _run_backward(x, dy, repeat=1):
     if wl.dtype == "bf16":
         g = g.to(torch.bfloat16)
     outs = []
-    with Plan(wl.L, wl.D, wl.order, wl.dtype, "lds") as p:
+    with Plan(wl.L, wl.D, wl.order, wl.dtype, path) as p:
         spec = p.spectrum(t["h"])
         for _ in range(repeat):
             outs.append(p.backward(t["u"], t["w"], spec, t["bias"], g.contiguous()))
@@ -46,10 +46,10 @@ def _run_backward(x, dy, repeat=1):
     return outs
 
 
-def _compare(x, dy, label, mode="fft"):
+def _compare(x, dy, label, mode="fft", path="lds"):
     wl = x.wl
-    say(f"[backward] {label}: {wl.describe()}")
-    (du, dw, dh, db), = _run_backward(x, dy)
+    say(f"[backward] {label}: {wl.describe()} path={path}")
+    (du, dw, dh, db), = _run_backward(x, dy, path=path)
     ref = oracle.backward(x.u_proj, x.short_w, x.h, x.bias, dy, wl.order, mode=mode)
     got = [a.float().cpu().numpy().astype(np.float64) for a in (du, dw, dh, db)]
     bounds = [1e-2 if wl.dtype == "bf16" else 1e-4, 1e-4, 1e-4, 1e-4]
@@ -104,6 +104,56 @@ def test_backward_workload_channels(name, nch):
     _compare(xs, dy, f"{name} channels {list(ds[:nch])}")
 
 
+FOURSTEP = [
+    # order 2 on the four-step path: the smallest split, ragged D, bf16, the default
+    # four-step sizes (32768, 65536) and the largest split
+    (2, 3, 256, "f32"),
+    (1, 5, 4096, "f32"),
+    (3, 2, 8192, "bf16"),
+    (2, 2, 32768, "f32"),
+    (1, 2, 65536, "bf16"),
+    (1, 1, 1 << 20, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,D,L,dtype", FOURSTEP)
+def test_backward_fourstep_shapes(B, D, L, dtype):
+    wl = synth.custom(B, D, L, 2, dtype, seed=B * 100 + D + L % 97)
+    x = synth.generate(wl)
+    _compare(x, synth.upstream_grad(wl), f"four-step {B}x{D}x{L} {dtype}", mode="fft", path="fourstep")
+
+
+def test_backward_fourstep_workload_channels():
+    """long64k (the headline forward shape) on sampled channels: all of L, order 2."""
+    wl = synth.WORKLOADS["long64k"]
+    x = synth.generate(wl)
+    xs = synth.channel_subset(x, [0, 383, wl.D - 1])
+    _compare(xs, synth.upstream_grad(xs.wl), "long64k channels [0, 383, 767]", path="fourstep")
+
+
+def test_backward_fourstep_is_deterministic_and_rejects_order_3():
+    import torch
+
+    from fft_long_convolution_libhyena_amd import HyenaError, Plan
+
+    wl = synth.custom(2, 3, 1024, 2, seed=8)
+    x = synth.generate(wl)
+    dy = synth.upstream_grad(wl)
+    a, b = _run_backward(x, dy, repeat=2, path="fourstep")
+    for ta, tb in zip(a, b):
+        assert bool((ta == tb).all()), "two backward calls differ"
+    wl3 = synth.custom(1, 2, 1024, 3, seed=9)
+    x3 = synth.generate(wl3)
+    t = to_device(x3)
+    with Plan(1024, 2, 3, "f32", "fourstep") as p:
+        spec = p.spectrum(t["h"])
+        assert p.backward_workspace_bytes(1) == 0
+        with pytest.raises(HyenaError) as e:
+            p.backward(t["u"], t["w"], spec, t["bias"], torch.zeros((1, 2, 1024), device=t["u"].device),
+                       workspace=torch.empty(16, dtype=torch.uint8, device=t["u"].device))
+        assert e.value.status == 2  # HYENA_ERR_UNSUPPORTED
+
+
 def test_backward_is_deterministic():
     wl = synth.custom(3, 6, 4096, 3, seed=21)
     x = synth.generate(wl)
@@ -121,7 +171,7 @@ def test_backward_zero_upstream_gives_zero():
         assert float(t.abs().max()) == 0.0
 
 
-def test_backward_rejects_fourstep_plan_and_small_workspace():
+def test_backward_rejects_small_workspaces():
     import torch
 
     from fft_long_convolution_libhyena_amd import HyenaError, Plan
@@ -132,11 +182,10 @@ def test_backward_rejects_fourstep_plan_and_small_workspace():
     g = torch.zeros((1, 2, 1024), dtype=torch.float32, device=t["u"].device)
     with Plan(1024, 2, 2, "f32", "fourstep") as p:
         spec = p.spectrum(t["h"])
-        assert p.backward_workspace_bytes(1) == 0
         with pytest.raises(HyenaError) as e:
             p.backward(t["u"], t["w"], spec, t["bias"], g, workspace=torch.empty(16, dtype=torch.uint8,
                                                                              device=g.device))
-        assert e.value.status == 2  # HYENA_ERR_UNSUPPORTED
+        assert e.value.status == 3  # HYENA_ERR_WORKSPACE
     with Plan(1024, 2, 2, "f32", "lds") as p:
         spec = p.spectrum(t["h"])
         small = torch.empty(p.backward_workspace_bytes(1) - 256, dtype=torch.uint8, device=g.device)
