@@ -81,15 +81,21 @@ def alg_bytes_pass(wl, family: str) -> int:
 # sizes its launches (chunking, grids)
 _CSRC = os.path.join(ROOT, "fft_long_convolution_libhyena_amd", "csrc")
 KERNEL_SOURCES = {
-    "lds": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "lds_path.hpp", "lds_path_a.hip", "lds_path_b.hip",
-            "lds_path_c.hip", "lds_path_d.hip", "hyena_api.hip"],
-    "fourstep": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "fourstep.hip", "hyena_api.hip"],
-    "backward": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "backward.hpp", "lds_backward.hpp", "lds_backward_a.hip",
-                 "lds_backward_b.hip", "lds_backward_c.hip", "lds_backward_d.hip", "hyena_backward.hip"],
+    "lds": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "lds_path.hpp", "lds_path_a.hip",
+            "lds_path_b.hip", "lds_path_c.hip", "lds_path_d.hip", "hyena_api.hip"],
+    "fourstep": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "fourstep.hpp", "fourstep.hip",
+                 "hyena_api.hip"],
+    "backward": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "backward.hpp", "lds_backward.hpp",
+                 "lds_backward_a.hip", "lds_backward_b.hip", "lds_backward_c.hip", "lds_backward_d.hip",
+                 "hyena_backward.hip"],
+    "fs_backward": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "backward.hpp", "fourstep.hpp",
+                    "fourstep_backward.hip", "hyena_backward.hip"],
 }
 
 
 def kernel_family(kernel: str) -> str:
+    if kernel.startswith("fs_backward"):
+        return "fs_backward"
     if kernel.startswith("k_lds_bwd"):
         return "backward"
     return "lds" if kernel.startswith("k_lds") else "fourstep"
@@ -210,6 +216,9 @@ def bench_backward(args, wl, x, torch, Plan):
         log(f"[bench] rep {rep}: {times[-1] * 1e3:.1f} us/step")
     ms = float(np.median(times))
     nbytes = alg_bytes_backward(wl)
+    # the step's kernels taken together: k_lds_bwd_rows + k_lds_bwd_finish on the LDS
+    # path, the nine launches of the four-step backward ("fs_backward") otherwise
+    bk = "k_lds_bwd_rows" if plan.path == "lds" else "fs_backward"
     achieved = nbytes / (ms * 1e-3) / 1e9
     out = {
         "metric": "channel-tokens/s (B·D·L/s) and % HBM peak, Hyena op backward (gradients of u_proj, short_w, "
@@ -224,8 +233,8 @@ def bench_backward(args, wl, x, torch, Plan):
         # four-step path) against its algorithmic bytes
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("k_lds_bwd_rows", wl.name) if plan.path == "lds" else None,
-                     "kernel": "k_lds_bwd_rows" if plan.path == "lds" else "four-step backward (9 launches)",
+                     "traffic": measured_traffic(bk, wl.name),
+                     "kernel": bk,
                      "alg_bytes_per_launch": nbytes, "launch_ms": round(ms, 5), "launches_per_step": 1},
     }
     if args.check:
