@@ -177,6 +177,60 @@ def operator_params(wl: Workload, seed: Optional[int] = None) -> OperatorParams:
     return OperatorParams(*[np.ascontiguousarray(a, dtype=np.float32) for a in arrs])
 
 
+@dataclasses.dataclass
+class FilterMLP:
+    """Parameters of the implicit long-filter generator (HyenaDNA walkthrough,
+    section 2.2, HyenaFilter): positional bands, the Linear / Sin stack, the output
+    Linear without bias and the exponential modulation rates. With
+    E = emb_dim, K = (E-1)/2, W = width, M = num_inner and C = (N-1)*D:"""
+    band_freq: np.ndarray  # [K] frequencies of the positional sine/cosine bands
+    w_in: np.ndarray       # [W, E]
+    b_in: np.ndarray       # [W]
+    w_inner: np.ndarray    # [M, W, W]
+    b_inner: np.ndarray    # [M, W]
+    sin_freq: np.ndarray   # [W] frequency of the Sin activation (shared by all its uses)
+    w_out: np.ndarray      # [C, W]
+    alpha: np.ndarray      # [C] modulation rates, channel c = o*D + d
+
+    @property
+    def emb_dim(self) -> int:
+        return int(self.w_in.shape[1])
+
+    @property
+    def width(self) -> int:
+        return int(self.w_in.shape[0])
+
+    @property
+    def num_inner(self) -> int:
+        return int(self.w_inner.shape[0])
+
+
+def filter_mlp(wl: Workload, emb_dim: int = 3, width: int = 16, num_inner: int = 2, w: float = 1.0,
+               seed: Optional[int] = None) -> FilterMLP:
+    """Seeded parameters of the implicit filter for a workload's plan (D, order),
+    defaulting to the walkthrough's HyenaFilter defaults (emb_dim 3, MLP width 16,
+    two inner layers, Sin frequency w = 1). Band k (k = 1..K) has frequency k;
+    Linear weights and biases ~ N(0, 1/fan_in); alpha_d log-spaced over the
+    workload's [alpha_lo, alpha_hi] and shared across o. Drawn from their own PCG64
+    stream (seed + 3000)."""
+    if emb_dim < 3 or emb_dim % 2 == 0:
+        raise ValueError("emb_dim must be odd and at least 3")
+    rng = np.random.Generator(np.random.PCG64((wl.seed if seed is None else seed) + 3000))
+    E, W, M = emb_dim, width, num_inner
+    C = (wl.order - 1) * wl.D
+    K = (E - 1) // 2
+    band = np.arange(1, K + 1, dtype=np.float32)
+    w_in = rng.standard_normal((W, E), dtype=np.float32) * np.float32(1.0 / np.sqrt(E))
+    b_in = rng.standard_normal(W, dtype=np.float32) * np.float32(1.0 / np.sqrt(E))
+    w_inner = rng.standard_normal((M, W, W), dtype=np.float32) * np.float32(1.0 / np.sqrt(W))
+    b_inner = rng.standard_normal((M, W), dtype=np.float32) * np.float32(1.0 / np.sqrt(W))
+    sin_freq = np.full(W, w, dtype=np.float32)
+    w_out = rng.standard_normal((C, W), dtype=np.float32) * np.float32(1.0 / np.sqrt(W))
+    alpha = np.tile(_alphas(wl.D, wl.alpha_lo, wl.alpha_hi), wl.order - 1).astype(np.float32)
+    arrs = [band, w_in, b_in, w_inner, b_inner, sin_freq, w_out, alpha]
+    return FilterMLP(*[np.ascontiguousarray(a, dtype=np.float32) for a in arrs])
+
+
 def channel_subset(x: Inputs, ds) -> Inputs:
     """The inputs restricted to channels ds of every channel group (gates, value,
     filters, biases): the hot path treats channels independently, so a subset is a

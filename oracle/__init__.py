@@ -1,13 +1,14 @@
-"""fp64 CPU oracle for the Hyena operator forward hot path and its backward (test
-infrastructure).
+"""fp64 CPU oracle for the Hyena operator forward hot path, its backward, the whole
+operator and the implicit filter generator (test infrastructure).
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The product (the HIP library and its binding) never does.
 
-The arithmetic lives in ``hyena_oracle.c`` (plain C, fp64, OpenMP over rows);
-this wrapper only marshals numpy arrays.  See that file's header for the
+The path's arithmetic lives in ``hyena_oracle.c`` (plain C, fp64, OpenMP over
+rows), which this wrapper calls with numpy arrays; see that file's header for the
 passages of the pages each step follows and the readings taken where the pages
-are silent.
+are silent.  The operator's projections and the implicit filter generator are
+written here in numpy fp64 (their docstrings cite their passages and readings).
 """
 from __future__ import annotations
 
@@ -211,6 +212,46 @@ def operator_forward(x: np.ndarray, w_in: np.ndarray, b_in: np.ndarray, short_w:
     u_proj = np.ascontiguousarray(u.transpose(0, 2, 1))                      # [B, (N+1)D, L]
     y = forward(u_proj, short_w, h, bias, order, mode=mode, threads=threads)  # [B, D, L]
     return y.transpose(0, 2, 1) @ np.asarray(w_out, np.float64).T + np.asarray(b_out, np.float64)
+
+
+def positional_embedding(L: int, band_freq: np.ndarray):
+    """The positional features of the implicit filter (HyenaDNA walkthrough, section
+    2.2: PositionalEmbedding gives every time step sine/cosine bands plus a linear time
+    term; emb_dim odd, (emb_dim - 1)/2 bands). The pages give no formula; reading
+    taken: t = tau / L for tau = 0..L-1 and z[tau] = (t, sin(2 pi f_k t) for each band
+    k, then cos(2 pi f_k t) for each band k), with the band frequencies f_k an input.
+    Returns (z [L, 1 + 2K], t [L]) in float64."""
+    f = np.asarray(band_freq, dtype=np.float64).reshape(-1)
+    t = np.arange(L, dtype=np.float64) / L
+    ang = 2.0 * np.pi * t[:, None] * f[None, :]
+    z = np.concatenate([t[:, None], np.sin(ang), np.cos(ang)], axis=1)
+    return z, t
+
+
+def implicit_filter(L: int, D: int, order: int, p) -> np.ndarray:
+    """The implicit long filters h [N-1, D, L] in float64 (HyenaDNA walkthrough,
+    section 2.2, HyenaFilter.filter): z, t = pos_emb(L); h = implicit_filter(z), the
+    stack Linear(emb_dim -> W), Sin, then num_inner times (Linear(W -> W), Sin), then
+    Linear(W -> (N-1)*D) without bias; h = modulation(t, h); and the
+    'l (o d) -> o d l' rearrange of section 2.1, so channel c = o*D + d.
+    Readings taken where the formulas are absent: Sin(x) = sin(sin_freq * x)
+    elementwise, one frequency vector shared by every Sin of the stack (the code
+    appends the same activation module after each Linear); the modulation multiplies
+    channel c by exp(-alpha_c * t) with the same t as the embedding. `p` carries the
+    fields of synth.FilterMLP."""
+    z, t = positional_embedding(L, p.band_freq)
+    freq = np.asarray(p.sin_freq, np.float64)
+    a = z @ np.asarray(p.w_in, np.float64).T + np.asarray(p.b_in, np.float64)   # Linear(emb_dim, W)
+    a = np.sin(freq * a)                                                         # Sin
+    for m in range(np.asarray(p.w_inner).shape[0]):
+        a = a @ np.asarray(p.w_inner[m], np.float64).T + np.asarray(p.b_inner[m], np.float64)  # Linear(W, W)
+        a = np.sin(freq * a)                                                     # Sin
+    h = a @ np.asarray(p.w_out, np.float64).T                                    # Linear(W, C), no bias
+    h = h * np.exp(-np.outer(t, np.asarray(p.alpha, np.float64)))               # modulation(t, h)
+    C = (order - 1) * D
+    if h.shape != (L, C):
+        raise ValueError(f"w_out has {h.shape[1]} rows, the plan needs (order-1)*D = {C}")
+    return np.ascontiguousarray(h.T.reshape(order - 1, D, L))                    # l (o d) -> o d l
 
 
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
