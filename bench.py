@@ -90,10 +90,13 @@ KERNEL_SOURCES = {
                  "hyena_backward.hip"],
     "fs_backward": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "backward.hpp", "fourstep.hpp",
                     "fourstep_backward.hip", "hyena_backward.hip"],
+    "filter": ["plan.hpp", "implicit_filter.hip"],
 }
 
 
 def kernel_family(kernel: str) -> str:
+    if kernel.startswith("k_implicit_filter"):
+        return "filter"
     if kernel.startswith("fs_backward"):
         return "fs_backward"
     if kernel.startswith("k_lds_bwd"):
@@ -350,6 +353,107 @@ def bench_operator(args, wl, x, torch, Plan):
     plan.close()
 
 
+def cpu_baseline_filter(p, wl, budget_s: float):
+    """The fp64 implicit-filter oracle on a seeded subset of the output channels (rows
+    of w_out and alpha; channels are independent), all L time steps, the subset
+    doubled until it takes about a quarter of the time budget."""
+    import types
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    C = (wl.order - 1) * wl.D
+    n = min(C, 8)
+    rng = np.random.default_rng(11)
+    while True:
+        cs = np.sort(rng.choice(C, size=n, replace=False))
+        sub = types.SimpleNamespace(**{**vars(p), "w_out": p.w_out[cs], "alpha": p.alpha[cs]})
+        t0 = time.perf_counter()
+        oracle.implicit_filter(wl.L, n, 2, sub)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 4 or n >= C:
+            break
+        n = min(C, n * 2)
+    return {"value": n * wl.L / dt, "unit": "filter taps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {C} filter channels, all {wl.L} time steps, fp64 numpy (BLAS threads), {dt:.1f} s wall"}
+
+
+def bench_filter(args, wl, torch, Plan):
+    """hyena_implicit_filter for the workload's plan with the walkthrough's default
+    HyenaFilter shape (emb_dim 3, MLP width 16, two inner layers); the spectrum of the
+    generated filters is timed beside it."""
+    import types
+
+    from fft_long_convolution_libhyena_amd import synth
+
+    dev = torch.device("cuda", 0)
+    p = synth.filter_mlp(wl)
+    dp = types.SimpleNamespace(**{k: torch.from_numpy(v).to(dev).contiguous() for k, v in vars(p).items()})
+    plan = Plan(wl.L, wl.D, wl.order, wl.dtype)
+    N, D, L = wl.order, wl.D, wl.L
+    C = (N - 1) * D
+    h = torch.empty((N - 1, D, L), dtype=torch.float32, device=dev)
+    spec = torch.empty(plan.spectrum_bytes(), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        plan.implicit_filter(dp, out=h)
+        plan.spectrum(h, out=spec)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        times = []
+        for rep in range(args.reps):
+            torch.cuda.synchronize()
+            ev0.record()
+            for _ in range(args.steps):
+                fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            times.append(ev0.elapsed_time(ev1) / args.steps)
+        return float(np.median(times))
+
+    ms = timed(lambda: plan.implicit_filter(dp, out=h))
+    spec_ms = timed(lambda: plan.spectrum(h, out=spec))
+    log(f"[bench] implicit filter {ms * 1e3:.1f} us, spectrum of its output {spec_ms * 1e3:.1f} us")
+    W, E, M = p.width, p.emb_dim, p.num_inner
+    # written filters plus the parameters read once
+    nbytes = 4 * C * L + 4 * (p.band_freq.size + p.w_in.size + p.b_in.size + p.w_inner.size + p.b_inner.size
+                               + p.sin_freq.size + p.w_out.size + p.alpha.size)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "filter taps/s ((N-1)·D·L/s), implicit long-filter generation (positional embedding, Sin MLP, "
+                  "exponential modulation)",
+        "value": C * L / (ms * 1e-3), "unit": "filter taps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic seeded filter parameters (N(0,1/fan_in) weights, log-spaced alpha)",
+        "config": {"workload": wl.name, "D": D, "L": L, "order": N, "emb_dim": E, "width": W, "num_inner": M,
+                   "pass": "implicit_filter"},
+        "spectrum_ms": round(spec_ms, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("k_implicit_filter", wl.name),
+                     "kernel": "k_implicit_filter", "alg_bytes_per_launch": nbytes, "launch_ms": round(ms, 5),
+                     "launches_per_step": 1},
+    }
+    if args.check:
+        import oracle
+
+        got = h.cpu().numpy().astype(np.float64).reshape(C, L)
+        cs = np.array([0, C // 2, C - 1])
+        sub = types.SimpleNamespace(**{**vars(p), "w_out": p.w_out[cs], "alpha": p.alpha[cs]})
+        res["check_rel_l2"] = oracle.rel_l2(got[cs], oracle.implicit_filter(L, 3, 2, sub).reshape(3, L))
+        log(f"[bench] oracle check on channels {list(cs)}: rel_l2 {res['check_rel_l2']:.3e}")
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (implicit filter oracle) ...")
+        res["cpu_baseline"] = cpu_baseline_filter(p, wl, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+    plan.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,7 +469,9 @@ def main():
     ap.add_argument("--operator", action="store_true",
                     help="time hyena_operator_forward (in_proj GEMM + the path + out_proj GEMM) instead")
     ap.add_argument("--backward", action="store_true",
-                    help="time hyena_backward instead of the forward (LDS-path workloads, L <= 16384)")
+                    help="time hyena_backward instead of the forward (order 2 only when L > 16384)")
+    ap.add_argument("--filter", action="store_true",
+                    help="time hyena_implicit_filter (the long filters of the workload's plan) instead")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -384,6 +490,9 @@ def main():
         sys.exit(1)
     wl = synth.WORKLOADS[args.workload]
     log(f"[bench] workload {wl.name}: {wl.describe()}")
+    if args.filter:
+        bench_filter(args, wl, torch, Plan)
+        return
     t0 = time.perf_counter()
     x = synth.generate(wl)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")

@@ -26,7 +26,16 @@ EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_destroy", 
            "hyena_spectrum_bytes", "hyena_workspace_bytes", "hyena_filter_spectrum", "hyena_forward",
            "hyena_forward_timed", "hyena_fused_check", "hyena_backward_workspace_bytes", "hyena_backward",
            "hyena_operator_workspace_bytes", "hyena_operator_forward", "hyena_operator_forward_timed",
-           "hyena_status_string")
+           "hyena_implicit_filter", "hyena_status_string")
+
+
+class FilterMLPStruct(ctypes.Structure):
+    """hyena_filter_mlp_t: sizes, then device pointers of the filter generator's
+    parameters (see include/hyena.h)."""
+    _fields_ = [("emb_dim", ctypes.c_int64), ("width", ctypes.c_int64), ("num_inner", ctypes.c_int64),
+                ("band_freq", ctypes.c_void_p), ("w_in", ctypes.c_void_p), ("b_in", ctypes.c_void_p),
+                ("w_inner", ctypes.c_void_p), ("b_inner", ctypes.c_void_p), ("sin_freq", ctypes.c_void_p),
+                ("w_out", ctypes.c_void_p), ("alpha", ctypes.c_void_p)]
 
 
 class HyenaError(RuntimeError):
@@ -80,6 +89,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_operator_forward_timed.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                  ctypes.POINTER(ctypes.c_float)]
     lib.hyena_operator_forward_timed.restype = ci
+    lib.hyena_implicit_filter.argtypes = [vp, ctypes.POINTER(FilterMLPStruct), vp, vp]
+    lib.hyena_implicit_filter.restype = ci
     lib.hyena_status_string.argtypes = [ci]
     lib.hyena_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -144,6 +155,32 @@ class Plan:
             raise ValueError("spectrum buffer too small")
         _check("hyena_filter_spectrum",
                self.lib.hyena_filter_spectrum(self.handle, h.data_ptr(), out.data_ptr(),
+                                              _stream_handle(torch, self.device)))
+        return out
+
+    def implicit_filter(self, mlp, out=None):
+        """hyena_implicit_filter: the plan's long filters h [N-1, D, L] fp32 from the
+        filter generator's parameters. `mlp` has the fields of synth.FilterMLP as
+        contiguous fp32 tensors on the plan's device (band_freq [K], w_in [W, E],
+        b_in [W], w_inner [M, W, W], b_inner [M, W], sin_freq [W], w_out [C, W],
+        alpha [C])."""
+        torch = self._torch
+        N, D, L = self.order, self.D, self.L
+        C = (N - 1) * D
+        W, E = (int(v) for v in mlp.w_in.shape)
+        M = int(mlp.w_inner.shape[0])
+        K = (E - 1) // 2
+        for name, shape in (("band_freq", (K,)), ("w_in", (W, E)), ("b_in", (W,)), ("w_inner", (M, W, W)),
+                            ("b_inner", (M, W)), ("sin_freq", (W,)), ("w_out", (C, W)), ("alpha", (C,))):
+            self._need(getattr(mlp, name), name, shape, torch.float32)
+        if out is None:
+            out = torch.empty((N - 1, D, L), dtype=torch.float32, device=self.device)
+        self._need(out, "h", (N - 1, D, L), torch.float32)
+        ptr = lambda t: t.data_ptr() if t.numel() else None  # noqa: E731
+        st = FilterMLPStruct(E, W, M, ptr(mlp.band_freq), ptr(mlp.w_in), ptr(mlp.b_in), ptr(mlp.w_inner),
+                             ptr(mlp.b_inner), ptr(mlp.sin_freq), ptr(mlp.w_out), ptr(mlp.alpha))
+        _check("hyena_implicit_filter",
+               self.lib.hyena_implicit_filter(self.handle, ctypes.byref(st), out.data_ptr(),
                                               _stream_handle(torch, self.device)))
         return out
 

@@ -1,6 +1,6 @@
 /*
- * libhyena — the Hyena operator forward hot path, and its backward, on AMD
- * MI355X (gfx950).
+ * libhyena — the Hyena operator forward hot path, its backward, the whole
+ * operator forward and the implicit filter generator, on AMD MI355X (gfx950).
  *
  * The operator (HyenaDNA walkthrough, section 2.1, HyenaOperator.forward):
  *   uc  = ShortConv(u_proj)[..., :L]    depthwise Conv1d, 3 taps, padding 2
@@ -247,6 +247,48 @@ hyena_status_t hyena_operator_forward_timed(hyena_plan_t plan, int64_t B, const 
                                             const float* bias, const void* w_out, const void* b_out, void* out,
                                             void* workspace, size_t workspace_bytes, hipStream_t stream,
                                             float* ms);
+
+/* Parameters of the implicit long-filter generator (HyenaDNA walkthrough, section
+ * 2.2, HyenaFilter). With E = emb_dim (odd, 3..127), K = (E-1)/2 bands,
+ * W = width (8, 16, 32 or 64), M = num_inner (0..16) and C = (N-1)*D of the plan;
+ * all arrays fp32, row-major, device, 16-byte aligned:
+ *   band_freq [K]      frequencies f_k of the positional sine/cosine bands
+ *   w_in [W][E], b_in [W]                 first Linear (PyTorch nn.Linear layout)
+ *   w_inner [M][W][W], b_inner [M][W]     inner Linears (may be NULL when M = 0)
+ *   sin_freq [W]       frequency of the Sin activation, shared by all its uses
+ *   w_out [C][W]       output Linear, no bias; row c = o*D + d
+ *   alpha [C]          modulation rates */
+typedef struct hyena_filter_mlp_s {
+    int64_t emb_dim;
+    int64_t width;
+    int64_t num_inner;
+    const float* band_freq;
+    const float* w_in;
+    const float* b_in;
+    const float* w_inner;
+    const float* b_inner;
+    const float* sin_freq;
+    const float* w_out;
+    const float* alpha;
+} hyena_filter_mlp_t;
+
+/* The implicit long filters of the plan (HyenaDNA walkthrough, section 2.2,
+ * HyenaFilter.filter: positional embedding, the Linear/Sin stack, modulation; and
+ * the 'l (o d) -> o d l' rearrange of section 2.1). For tau = 0..L-1, t = tau/L:
+ *   z    = (t, sin(2 pi f_1 t) .. sin(2 pi f_K t), cos(2 pi f_1 t) .. cos(2 pi f_K t))
+ *   a    = sin(sin_freq * (w_in z + b_in)),  then M times  a = sin(sin_freq * (w_inner[m] a + b_inner[m]))
+ *   h[o][d][tau] = exp(-alpha[c] t) * sum_j w_out[c][j] a[j],   c = o*D + d
+ * (the pages give the structure but not these formulas: the positional features,
+ * the Sin activation and the modulation are this library's readings of them).
+ *   h [N-1][D][L] fp32, device (output): the layout hyena_filter_spectrum takes.
+ * The positional features are evaluated in fp64 and rounded once; the stack runs
+ * in fp32; exp(-alpha t) is evaluated as 2^(alpha * (-t log2 e)) with the hardware
+ * exp2 (relative error about 1e-7). Enqueued on `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL plan, mlp or
+ * h, NULL arrays, even or too small emb_dim, misaligned pointers),
+ * HYENA_ERR_UNSUPPORTED (width not 8/16/32/64, emb_dim > 127, num_inner > 16),
+ * HYENA_ERR_DEVICE. h must not alias the parameters. */
+hyena_status_t hyena_implicit_filter(hyena_plan_t plan, const hyena_filter_mlp_t* mlp, float* h,
+                                     hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* hyena_status_string(hyena_status_t s);

@@ -103,6 +103,14 @@ def test_backward_rejects_null_plan(lib):
     assert lib.hyena_backward(None, 1, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 20, None) == 1
 
 
+def test_implicit_filter_rejects_null_arguments(lib):
+    from fft_long_convolution_libhyena_amd.binding import FilterMLPStruct
+
+    st = FilterMLPStruct(3, 16, 0, 16, 16, 16, None, None, 16, 16, 16)
+    assert lib.hyena_implicit_filter(None, ctypes.byref(st), 16, None) == 1
+    assert lib.hyena_implicit_filter(None, None, 16, None) == 1
+
+
 def test_valid_plan_without_gpu_reports_device_error(lib):
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
