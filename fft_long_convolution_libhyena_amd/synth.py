@@ -140,6 +140,19 @@ def generate(wl: Workload, seed: Optional[int] = None) -> Inputs:
                   np.ascontiguousarray(h), np.ascontiguousarray(bias))
 
 
+def per_sample_filters(wl: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """Seeded long filters for every sample, h [B, N-1, D, L] fp32, drawn like the
+    shared filters of ``generate`` (N(0, 1) noise times exp(-alpha_d t / L)) from
+    their own PCG64 stream (seed + 4000)."""
+    rng = np.random.Generator(np.random.PCG64((wl.seed if seed is None else seed) + 4000))
+    B, D, L, N = wl.B, wl.D, wl.L, wl.order
+    noise = rng.standard_normal((B, N - 1, D, L), dtype=np.float32)
+    alpha = _alphas(D, wl.alpha_lo, wl.alpha_hi)
+    t = np.arange(L, dtype=np.float64) / L
+    decay = np.exp(-alpha[:, None] * t[None, :]).astype(np.float32)  # [D, L]
+    return np.ascontiguousarray((noise * decay[None, None]).astype(np.float32))
+
+
 def upstream_grad(wl: Workload, seed: Optional[int] = None) -> np.ndarray:
     """A seeded upstream gradient dy [B, D, L] ~ N(0, 1) for the backward, drawn from its
     own PCG64 stream (seed + 1000 by default) and rounded to bf16 for bf16 workloads."""

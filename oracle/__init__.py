@@ -166,6 +166,21 @@ def forward(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.nda
     return out
 
 
+def forward_per_sample(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray, order: int,
+                       mode: str = "fft", threads: int = 0) -> np.ndarray:
+    """The hot path with a filter set per sample (input-dependent long convolutions,
+    HyenaND summary, methodology: the kernel is conditioned on the whole input
+    sample): sample b of u_proj [B, (N+1)D, L] runs through ``forward`` with the
+    filters h[b] of h [B, N-1, D, L]; short_w and bias are shared. Returns
+    [B, D, L] float64."""
+    u = np.asarray(u_proj)
+    hb = np.asarray(h)
+    if hb.ndim != 4 or hb.shape[0] != u.shape[0]:
+        raise ValueError("h must be [B, N-1, D, L] with the B of u_proj")
+    return np.concatenate([forward(u[b:b + 1], short_w, hb[b], bias, order, mode=mode, threads=threads)
+                           for b in range(u.shape[0])], axis=0)
+
+
 def backward(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray, dy: np.ndarray,
              order: int, mode: str = "fft", threads: int = 0):
     """Gradients of the hot path in fp64 for upstream gradient dy [B,D,L].
