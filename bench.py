@@ -454,6 +454,96 @@ def bench_filter(args, wl, torch, Plan):
     plan.close()
 
 
+def _per_sample_rows(x, hb, wl, rows):
+    """The per-sample oracle on flat rows b*D + d (sorted): each sample's rows with its own filters."""
+    import oracle
+
+    out = []
+    for b in range(wl.B):
+        ds = [int(r) - b * wl.D for r in rows if int(r) // wl.D == b]
+        if ds:
+            out.append(oracle.forward(x.u_proj[b:b + 1], x.short_w, hb[b], x.bias, wl.order, mode="fft", rows=ds))
+    return np.concatenate(out, axis=0)
+
+
+def bench_per_sample(args, wl, x, torch, Plan):
+    """hyena_forward_per_sample: the workload with a filter set per sample (B spectra
+    read, one per sample), against its algorithmic bytes."""
+    import oracle
+    from fft_long_convolution_libhyena_amd import synth
+
+    dev = torch.device("cuda", 0)
+    iot = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    u = torch.from_numpy(x.u_proj).to(dev).to(iot).contiguous()
+    w = torch.from_numpy(x.short_w).to(dev)
+    bias = torch.from_numpy(x.bias).to(dev)
+    hb = synth.per_sample_filters(wl)
+    plan = Plan(wl.L, wl.D, wl.order, wl.dtype)
+    spec = plan.spectrum_batched(torch.from_numpy(hb).to(dev))
+    B, D, L, N = wl.B, wl.D, wl.L, wl.order
+    ws_bytes = plan.workspace_bytes(B)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    y = torch.empty((B, D, L), dtype=iot, device=dev)
+    for _ in range(args.warmup):
+        plan.forward_per_sample(u, w, spec, bias, y, ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for rep in range(args.reps):
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            plan.forward_per_sample(u, w, spec, bias, y, ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / args.steps)
+        log(f"[bench] rep {rep}: {times[-1] * 1e3:.1f} us/step")
+    ms = float(np.median(times))
+    # as the shared forward, with B filter spectra instead of one
+    nbytes = alg_bytes_forward(wl) + 8 * (B - 1) * (N - 1) * D * (L + 1)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    lds = plan.path == "lds"
+    dom = "k_lds_forward" if lds else "four-step passes (whole step)"
+    out = {
+        "metric": "channel-tokens/s (B·D·L/s) and % HBM peak, Hyena op fwd with a filter set per sample",
+        "value": B * D * L / (ms * 1e-3), "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if wl.dtype == "f32" else "bf16-io/f32",
+        "data": f"synthetic seeded ({wl.kind} activations, per-sample exponentially decaying random filters)",
+        "config": {"workload": wl.name, "B": B, "D": D, "L": L, "order": N, "io_dtype": wl.dtype,
+                   "path": plan.path, "pass": "forward_per_sample"},
+        "hbm_frac_forward": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dom, wl.name + "_per_sample") if lds else None,
+                     "kernel": dom, "alg_bytes_per_launch": nbytes, "launch_ms": round(ms, 5),
+                     "launches_per_step": 1},
+    }
+    if args.check:
+        rows = synth.sample_rows(wl, 8)
+        got = y.float().cpu().numpy().reshape(-1, L)[rows]
+        out["check_rel_l2"] = oracle.rel_l2(got, _per_sample_rows(x, hb, wl, rows))
+        log(f"[bench] oracle check on {len(rows)} rows: rel_l2 {out['check_rel_l2']:.3e}")
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (per-sample oracle) ...")
+        threads = oracle.max_threads()
+        n = max(1, min(B * D, 2 * threads))
+        while True:
+            rows = synth.sample_rows(wl, n, seed=99)
+            t0 = time.perf_counter()
+            _per_sample_rows(x, hb, wl, rows)
+            dt = time.perf_counter() - t0
+            if dt >= args.cpu_budget / 4 or n >= B * D:
+                break
+            n = int(min(B * D, max(n + 1, n * args.cpu_budget / max(dt, 1e-3) * 0.8)))
+        out["cpu_baseline"] = {"value": len(rows) * L / dt, "unit": "channel-tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"{len(rows)} of {B * D} (b,d) rows, each with its sample's filters, "
+                                         f"fp64 radix-2 FFT convolution, OpenMP over rows, {dt:.1f} s wall"}
+    print(json.dumps(out), flush=True)
+    plan.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -470,6 +560,8 @@ def main():
                     help="time hyena_operator_forward (in_proj GEMM + the path + out_proj GEMM) instead")
     ap.add_argument("--backward", action="store_true",
                     help="time hyena_backward instead of the forward (order 2 only when L > 16384)")
+    ap.add_argument("--per-sample", action="store_true",
+                    help="time hyena_forward_per_sample (a filter set per sample) instead")
     ap.add_argument("--filter", action="store_true",
                     help="time hyena_implicit_filter (the long filters of the workload's plan) instead")
     args = ap.parse_args()
@@ -498,6 +590,9 @@ def main():
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
     if args.operator:
         bench_operator(args, wl, x, torch, Plan)
+        return
+    if args.per_sample:
+        bench_per_sample(args, wl, x, torch, Plan)
         return
     if args.backward:
         if wl.L > 16384 and wl.order != 2:

@@ -26,7 +26,8 @@ EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_destroy", 
            "hyena_spectrum_bytes", "hyena_workspace_bytes", "hyena_filter_spectrum", "hyena_forward",
            "hyena_forward_timed", "hyena_fused_check", "hyena_backward_workspace_bytes", "hyena_backward",
            "hyena_operator_workspace_bytes", "hyena_operator_forward", "hyena_operator_forward_timed",
-           "hyena_implicit_filter", "hyena_status_string")
+           "hyena_implicit_filter", "hyena_filter_spectrum_batched", "hyena_forward_per_sample",
+           "hyena_status_string")
 
 
 class FilterMLPStruct(ctypes.Structure):
@@ -74,6 +75,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_filter_spectrum.restype = ci
     lib.hyena_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hyena_forward.restype = ci
+    lib.hyena_filter_spectrum_batched.argtypes = [vp, i64, vp, vp, vp]
+    lib.hyena_filter_spectrum_batched.restype = ci
+    lib.hyena_forward_per_sample.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hyena_forward_per_sample.restype = ci
     lib.hyena_forward_timed.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
     lib.hyena_forward_timed.restype = ci
     lib.hyena_fused_check.argtypes = [vp, vp, ctypes.POINTER(ci)]
@@ -184,7 +189,30 @@ class Plan:
                                               _stream_handle(torch, self.device)))
         return out
 
-    def forward(self, u_proj, short_w, spec, bias, y=None, workspace=None):
+    def spectrum_batched(self, h, out=None):
+        """hyena_filter_spectrum_batched: per-sample filters h [B, N-1, D, L] fp32 ->
+        B spectra in one opaque uint8 device buffer."""
+        torch = self._torch
+        N, D, L = self.order, self.D, self.L
+        if h.dim() != 4:
+            raise ValueError("h must be [B, N-1, D, L]")
+        B = int(h.shape[0])
+        self._need(h, "h", (B, N - 1, D, L), torch.float32)
+        if out is None:
+            out = torch.empty(B * self.spectrum_bytes(), dtype=torch.uint8, device=self.device)
+        elif out.numel() * out.element_size() < B * self.spectrum_bytes():
+            raise ValueError("spectrum buffer too small")
+        _check("hyena_filter_spectrum_batched",
+               self.lib.hyena_filter_spectrum_batched(self.handle, B, h.data_ptr(), out.data_ptr(),
+                                                      _stream_handle(torch, self.device)))
+        return out
+
+    def forward_per_sample(self, u_proj, short_w, spec, bias, y=None, workspace=None):
+        """hyena_forward_per_sample: as forward, with spec holding one spectrum per
+        sample (from spectrum_batched)."""
+        return self.forward(u_proj, short_w, spec, bias, y, workspace, per_sample=True)
+
+    def forward(self, u_proj, short_w, spec, bias, y=None, workspace=None, per_sample=False):
         """hyena_forward: u_proj [B,(N+1)D,L], short_w [(N+1)D,3], bias [N-1,D] -> y [B,D,L]."""
         torch = self._torch
         N, D, L = self.order, self.D, self.L
@@ -194,8 +222,10 @@ class Plan:
         self._need(u_proj, "u_proj", (B, (N + 1) * D, L), self.io_dtype)
         self._need(short_w, "short_w", ((N + 1) * D, 3), torch.float32)
         self._need(bias, "bias", (N - 1, D), torch.float32)
-        if spec.device != self.device or spec.numel() * spec.element_size() < self.spectrum_bytes():
-            raise ValueError("spec must come from Plan.spectrum of an equal plan")
+        nspec = B if per_sample else 1
+        if spec.device != self.device or spec.numel() * spec.element_size() < nspec * self.spectrum_bytes():
+            raise ValueError("spec must come from Plan.spectrum (spectrum_batched for per-sample filters) "
+                             "of an equal plan")
         if y is None:
             y = torch.empty((B, D, L), dtype=self.io_dtype, device=self.device)
         self._need(y, "y", (B, D, L), self.io_dtype)
@@ -205,10 +235,10 @@ class Plan:
             if workspace is None:
                 workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-        _check("hyena_forward",
-               self.lib.hyena_forward(self.handle, B, u_proj.data_ptr(), short_w.data_ptr(), spec.data_ptr(),
-                                      bias.data_ptr(), y.data_ptr(), ws_ptr or None, ws_bytes,
-                                      _stream_handle(torch, self.device)))
+        fn, name = ((self.lib.hyena_forward_per_sample, "hyena_forward_per_sample") if per_sample
+                    else (self.lib.hyena_forward, "hyena_forward"))
+        _check(name, fn(self.handle, B, u_proj.data_ptr(), short_w.data_ptr(), spec.data_ptr(), bias.data_ptr(),
+                        y.data_ptr(), ws_ptr or None, ws_bytes, _stream_handle(torch, self.device)))
         return y
 
     def forward_timed(self, u_proj, short_w, spec, bias, y, workspace=None):

@@ -280,7 +280,7 @@ static hipError_t fs_forward_chunk(const FsArgs& a, int64_t row0, int64_t nrows,
     mark();
     for (int o = 0; o < a.N - 1; ++o) {
         hipLaunchKernelGGL((k_fs_row<LOG1, LOG2, 0>), dim3(grow), brow, 0, st, a.ws, a.spec, a.bias, a.tb, a.D, o,
-                           row0, nrows);
+                           row0, nrows, a.sbs);
         mark();
         const bool last = (o == a.N - 2);
         if (a.bf16) {
@@ -311,7 +311,7 @@ static hipError_t fs_spectrum_t(const float* h, float2* spec, int64_t rows, cons
     hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, float, 1>), dim3(gcol), dim3(Cfg::COL_THREADS), 0, st,
                        (const float*)nullptr, (const float*)nullptr, h, spec, tb, 1, 2, (int64_t)0, rows);
     hipLaunchKernelGGL((k_fs_row<LOG1, LOG2, 1>), dim3(grow), dim3(Cfg::ROW_THREADS), 0, st, spec,
-                       (const float2*)nullptr, (const float*)nullptr, tb, 1, 0, (int64_t)0, rows);
+                       (const float2*)nullptr, (const float*)nullptr, tb, 1, 0, (int64_t)0, rows, (int64_t)0);
     return hipGetLastError();
 }
 

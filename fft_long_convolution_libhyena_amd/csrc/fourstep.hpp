@@ -145,7 +145,7 @@ template <int LOG1, int LOG2, int MODE>
 __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ slot, const float2* __restrict__ spec,
                                             const float* __restrict__ bias, const FsTables& tb, int D, int o,
                                             int64_t flat, int ug, float2* __restrict__ gt = nullptr,
-                                            float2* __restrict__ pt = nullptr) {
+                                            float2* __restrict__ pt = nullptr, int64_t sbs = 0) {
     constexpr bool CONV = MODE == 0 || MODE == 2 || MODE == 3;  // multiply by the filter spectrum
     using Cfg = FsCfg<LOG1, LOG2>;
     constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T2 = Cfg::T2, U = Cfg::UNITS, RP = Cfg::RP;
@@ -164,8 +164,8 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
     float bs = 0.f;
     float2 ha[8], hb[8];
     if constexpr (CONV) {
-        const uint32_t d = (uint32_t)flat % (uint32_t)D;
-        Hrow = spec + ((int64_t)o * D + d) * L;
+        const uint32_t b = (uint32_t)flat / (uint32_t)D, d = (uint32_t)flat - b * (uint32_t)D;
+        Hrow = spec + (int64_t)b * sbs + ((int64_t)o * D + d) * L;
         bs = bias[(int64_t)o * D + d] * (1.0f / (4.0f * (float)L));
     }
 
@@ -271,7 +271,7 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
 template <int LOG1, int LOG2, int MODE>
 __global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::ROW_THREADS))
 k_fs_row(float2* __restrict__ ws, const float2* __restrict__ spec, const float* __restrict__ bias, FsTables tb,
-         int D, int o, int64_t row0, int64_t nrows) {
+         int D, int o, int64_t row0, int64_t nrows, int64_t sbs) {
     using Cfg = FsCfg<LOG1, LOG2>;
     __shared__ float2 lds[2 * Cfg::UNITS * Cfg::RP];
     int64_t r;
@@ -279,7 +279,7 @@ k_fs_row(float2* __restrict__ ws, const float2* __restrict__ spec, const float* 
     if (!xcd_row_map(blockIdx.x, nrows, Cfg::L1 / 2 / Cfg::UNITS, r, ug)) return;
     const int64_t L = (int64_t)Cfg::L1 * Cfg::L2;
     float2* slot = (MODE == 0) ? ws + r * L : ws + (row0 + r) * L;
-    fs_row_body<LOG1, LOG2, MODE>(lds, slot, spec, bias, tb, D, o, row0 + r, ug);
+    fs_row_body<LOG1, LOG2, MODE>(lds, slot, spec, bias, tb, D, o, row0 + r, ug, nullptr, nullptr, sbs);
 }
 
 // Pass C: the conjugate four-step twiddle, inverse column FFTs over k1, then

@@ -225,17 +225,23 @@ size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B) {
     return (size_t)want * per_row;
 }
 
-hyena_status_t hyena_filter_spectrum(hyena_plan_t plan, const float* h, void* spec, hipStream_t stream) {
-    if (!plan || !h || !spec) return HYENA_ERR_INVALID_ARG;
+hyena_status_t hyena_filter_spectrum_batched(hyena_plan_t plan, int64_t B, const float* h, void* spec,
+                                             hipStream_t stream) {
+    if (!plan || B < 1 || !h || !spec) return HYENA_ERR_INVALID_ARG;
     if (!aligned16(h) || !aligned16(spec)) return HYENA_ERR_INVALID_ARG;
+    if (B > (int64_t(1) << 24) || B * (plan->order - 1) * plan->D > (int64_t(1) << 24)) return HYENA_ERR_INVALID_ARG;
     if (check_device(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
-    const int64_t rows = (int64_t)(plan->order - 1) * plan->D;
+    const int64_t rows = B * (plan->order - 1) * plan->D;
     hipError_t e;
     if (plan->path == HYENA_PATH_LDS)
         e = hy::launch_lds_spectrum(plan->logL, h, (float2*)spec, rows, plan->tw, plan->wpair, stream);
     else
         e = hy::launch_fs_spectrum(plan->logL, h, (float2*)spec, rows, plan->fs, stream);
     return e == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
+}
+
+hyena_status_t hyena_filter_spectrum(hyena_plan_t plan, const float* h, void* spec, hipStream_t stream) {
+    return hyena_filter_spectrum_batched(plan, 1, h, spec, stream);
 }
 
 }  // extern "C"
@@ -247,7 +253,7 @@ namespace {
 // elapsed milliseconds are summed per kernel family (see hyena_forward_timed).
 hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
                             const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream, float* ms) {
+                            hipStream_t stream, float* ms, bool per_sample = false) {
     if (!plan || B < 1 || !u_proj || !short_w || !spec || !bias || !y) return HYENA_ERR_INVALID_ARG;
     if (!aligned16(u_proj) || !aligned16(spec) || !aligned16(y) || !aligned16(short_w) || !aligned16(bias))
         return HYENA_ERR_INVALID_ARG;
@@ -256,6 +262,9 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
     const bool bf16 = plan->dtype == HYENA_BF16;
     const int64_t rows = B * plan->D;
     int64_t chunk = 0;
+    if (per_sample && plan->path == HYENA_PATH_FUSED) return HYENA_ERR_UNSUPPORTED;
+    // sample b reads spectrum b when every sample has its own filters
+    const int64_t sbs = per_sample ? (int64_t)(plan->order - 1) * plan->D * plan->L : 0;
     if (plan->path == HYENA_PATH_FUSED) {
         if (!workspace || !aligned16(workspace)) return HYENA_ERR_WORKSPACE;
         if (workspace_bytes < hy::fused_workspace_bytes(plan->logL, rows, kFusedG, kFusedS)) return HYENA_ERR_WORKSPACE;
@@ -293,13 +302,13 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
     } else if (plan->path == HYENA_PATH_LDS) {
         if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
         hy::LdsArgs a{u_proj, short_w, (const float2*)spec, bias, y, plan->tw, plan->wpair,
-                      (int)B, (int)plan->D, plan->order, bf16};
+                      (int)B, (int)plan->D, plan->order, bf16, sbs};
         if (ms) (void)hipEventRecord(ev[0], stream);
         if (hy::launch_lds_forward(plan->logL, a, stream) != hipSuccess) st = HYENA_ERR_DEVICE;
         if (ms) (void)hipEventRecord(ev[1], stream);
     } else {
         hy::FsArgs a{u_proj, short_w, (const float2*)spec, bias, y, (float2*)workspace, plan->fs,
-                     (int)plan->D, plan->order, bf16};
+                     (int)plan->D, plan->order, bf16, sbs};
         int64_t ci = 0;
         for (int64_t r0 = 0; r0 < rows && st == HYENA_OK; r0 += chunk, ++ci) {
             const int64_t n = (rows - r0) < chunk ? (rows - r0) : chunk;
@@ -354,6 +363,12 @@ hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, c
                              const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,
                              hipStream_t stream) {
     return forward_impl(plan, B, u_proj, short_w, spec, bias, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+hyena_status_t hyena_forward_per_sample(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                                        const void* spec, const float* bias, void* y, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    return forward_impl(plan, B, u_proj, short_w, spec, bias, y, workspace, workspace_bytes, stream, nullptr, true);
 }
 
 hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,

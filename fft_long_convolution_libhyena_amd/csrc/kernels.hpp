@@ -63,6 +63,7 @@ struct LdsArgs {
     const float2* wpair;  // W_{2L}^k, k = 0..L/2
     int B, D, N;
     bool bf16;
+    int64_t sbs = 0;      // spectrum batch stride (complex values): 0 = one spectrum for every b
 };
 
 struct FsTables {
@@ -84,6 +85,7 @@ struct FsArgs {
     FsTables tb;
     int D, N;
     bool bf16;
+    int64_t sbs = 0;  // spectrum batch stride (complex values): 0 = one spectrum for every b
 };
 
 hipError_t launch_lds_forward(int logL, const LdsArgs& a, hipStream_t st);

@@ -48,7 +48,7 @@ template <int LOGL, int N, class TIO>
 __global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS)
 k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const float2* __restrict__ spec,
               const float* __restrict__ bias, TIO* __restrict__ y, const float2* __restrict__ tw,
-              const float2* __restrict__ wpair, int B, int D) {
+              const float2* __restrict__ wpair, int B, int D, int64_t sbs) {
     constexpr int L = 1 << LOGL;
     constexpr int E = LdsCfg<LOGL>::E;
     constexpr int H = E / 2;
@@ -82,7 +82,7 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
         // keep each step's loads inside its step: hoisting the next step's
         // spectrum fetch across a transform raises register pressure
         __builtin_amdgcn_sched_barrier(0);
-        const float2* Hs = spec + ((int64_t)o * D + d) * L;
+        const float2* Hs = spec + (int64_t)b * sbs + ((int64_t)o * D + d) * L;
         // spectrum values of this thread's pairs, fetched before the transform
         float2 hk[H], hm[H];
         if constexpr (HY_LDS_PREFETCH) {
@@ -224,10 +224,10 @@ inline void launch_lds_forward_n(const LdsArgs& a, hipStream_t st) {
     const unsigned grid = (unsigned)(a.B * 8 * dgroups);
     if (a.bf16)
         hipLaunchKernelGGL((k_lds_forward<LOGL, N, uint16_t>), dim3(grid), dim3(T), 0, st, (const uint16_t*)a.u,
-                           a.w3, a.spec, a.bias, (uint16_t*)a.y, a.tw, a.wpair, a.B, a.D);
+                           a.w3, a.spec, a.bias, (uint16_t*)a.y, a.tw, a.wpair, a.B, a.D, a.sbs);
     else
         hipLaunchKernelGGL((k_lds_forward<LOGL, N, float>), dim3(grid), dim3(T), 0, st, (const float*)a.u, a.w3,
-                           a.spec, a.bias, (float*)a.y, a.tw, a.wpair, a.B, a.D);
+                           a.spec, a.bias, (float*)a.y, a.tw, a.wpair, a.B, a.D, a.sbs);
 }
 
 template <int LOGL>

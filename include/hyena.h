@@ -123,6 +123,17 @@ size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B);
  * current. */
 hyena_status_t hyena_filter_spectrum(hyena_plan_t plan, const float* h, void* spec, hipStream_t stream);
 
+/* Spectra of per-sample long filters, for input-dependent convolutions (the
+ * HyenaND summary's methodology: kernels conditioned on each input sample, one
+ * global FFT path). hyena_filter_spectrum for B filter sets at once:
+ *   h    [B][N-1][D][L] fp32, device: the filters of sample b at h + b*(N-1)*D*L
+ *   spec device buffer of B * hyena_spectrum_bytes(plan) bytes; sample b's
+ *        spectrum starts at byte b * hyena_spectrum_bytes(plan).
+ * Errors as hyena_filter_spectrum; HYENA_ERR_INVALID_ARG also for B < 1 or
+ * B*(N-1)*D > 2^24. */
+hyena_status_t hyena_filter_spectrum_batched(hyena_plan_t plan, int64_t B, const float* h, void* spec,
+                                             hipStream_t stream);
+
 /* The forward hot path for a batch of B sequences.
  *   u_proj  [B][(N+1)*D][L] of the plan dtype, device: channel i*D + d is gate
  *           x_i for i < N and channel N*D + d is the value v (the in-projected,
@@ -142,6 +153,15 @@ hyena_status_t hyena_filter_spectrum(hyena_plan_t plan, const float* h, void* sp
 hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
                              const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* hyena_forward with a filter set per sample (input-dependent long convolutions,
+ * the HyenaND summary's methodology): sample b is convolved with the filters whose
+ * spectrum hyena_filter_spectrum_batched wrote at byte b * hyena_spectrum_bytes
+ * of `spec` (B spectra, B as in this call); short_w and bias stay shared. Same
+ * arguments, workspace, results and errors as hyena_forward otherwise. */
+hyena_status_t hyena_forward_per_sample(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                                        const void* spec, const float* bias, void* y, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
 
 /* hyena_forward with per-kernel timing, for measurement. HIP events are
  * recorded on `stream` around every kernel launch of this forward; the call
