@@ -166,6 +166,46 @@ def forward(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.nda
     return out
 
 
+def circular_conv(v: np.ndarray, h: np.ndarray, mode: str = "fft") -> np.ndarray:
+    """Circular convolution along the last axis in fp64: out[t] = sum_{s<L} h[s]
+    v[(t - s) mod L] (the HyenaND summary's circular boundary mode, for periodic
+    data). ``direct`` is that sum written out; ``fft`` multiplies numpy real FFTs of
+    length L (no zero padding) and inverts."""
+    v = np.asarray(v, dtype=np.float64)
+    h = np.asarray(h, dtype=np.float64)
+    L = v.shape[-1]
+    if mode == "direct":
+        idx = (np.arange(L)[:, None] - np.arange(L)[None, :]) % L  # [t, s] -> (t - s) mod L
+        return np.einsum("...s,...ts->...t", h, v[..., idx])
+    return np.fft.irfft(np.fft.rfft(v, axis=-1) * np.fft.rfft(h, axis=-1), n=L, axis=-1)
+
+
+def forward_circular(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray, order: int,
+                     mode: str = "fft") -> np.ndarray:
+    """The hot path with circular long convolutions in fp64 (HyenaDNA walkthrough,
+    section 2.1, the gated recurrence; HyenaND summary, circular boundary handling):
+    the short conv keeps its causal zero padding (``short_conv_row``), then for
+    o = 0..N-2: v = v * x_{N-1-o}; v = circular_conv(v, h[o]) + bias[o] * v; and
+    y = v * x_0. Returns [B, D, L] float64."""
+    u = np.asarray(u_proj, dtype=np.float32)
+    B, C, L = u.shape
+    N = int(order)
+    D = C // (N + 1)
+    w = np.asarray(short_w, dtype=np.float32)
+    uc = np.empty((B, C, L), dtype=np.float64)
+    for b in range(B):
+        for c in range(C):
+            uc[b, c] = short_conv_row(u[b, c], w[c])
+    x = [uc[:, i * D:(i + 1) * D] for i in range(N)]
+    v = uc[:, N * D:]
+    hh = np.asarray(h, dtype=np.float32).astype(np.float64)
+    bb = np.asarray(bias, dtype=np.float32).astype(np.float64)
+    for o in range(N - 1):
+        v = v * x[N - 1 - o]
+        v = circular_conv(v, hh[o][None], mode=mode) + bb[o][None, :, None] * v
+    return v * x[0]
+
+
 def forward_per_sample(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray, order: int,
                        mode: str = "fft", threads: int = 0) -> np.ndarray:
     """The hot path with a filter set per sample (input-dependent long convolutions,
