@@ -544,6 +544,87 @@ def bench_per_sample(args, wl, x, torch, Plan):
     plan.close()
 
 
+def bench_circular(args, wl, x, torch, Plan):
+    """hyena_forward on a circular plan (HYENA_FLAG_CIRCULAR: circular long
+    convolution of the L samples, an L-point real transform), against its
+    algorithmic bytes (the spectrum holds L/2 + 1 bins per filter)."""
+    import oracle
+    from fft_long_convolution_libhyena_amd import synth
+
+    dev = torch.device("cuda", 0)
+    iot = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    u = torch.from_numpy(x.u_proj).to(dev).to(iot).contiguous()
+    w = torch.from_numpy(x.short_w).to(dev)
+    bias = torch.from_numpy(x.bias).to(dev)
+    plan = Plan(wl.L, wl.D, wl.order, wl.dtype, circular=True)
+    spec = plan.spectrum(torch.from_numpy(x.h).to(dev))
+    B, D, L, N = wl.B, wl.D, wl.L, wl.order
+    ws_bytes = plan.workspace_bytes(B)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    y = torch.empty((B, D, L), dtype=iot, device=dev)
+    for _ in range(args.warmup):
+        plan.forward(u, w, spec, bias, y, ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for rep in range(args.reps):
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            plan.forward(u, w, spec, bias, y, ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        times.append(ev0.elapsed_time(ev1) / args.steps)
+        log(f"[bench] rep {rep}: {times[-1] * 1e3:.1f} us/step")
+    ms = float(np.median(times))
+    s = io_bytes(wl)
+    nbytes = (s * B * (N + 1) * D * L + s * B * D * L + 8 * (N - 1) * D * (L // 2 + 1)
+              + 4 * (N + 1) * D * 3 + 4 * (N - 1) * D)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    lds = plan.path == "lds"
+    dom = "k_lds_forward" if lds else "four-step passes (whole step)"
+    out = {
+        "metric": "channel-tokens/s (B·D·L/s) and % HBM peak, Hyena op fwd with circular long convolutions",
+        "value": B * D * L / (ms * 1e-3), "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if wl.dtype == "f32" else "bf16-io/f32",
+        "data": f"synthetic seeded ({wl.kind} activations, exponentially decaying random filters)",
+        "config": {"workload": wl.name, "B": B, "D": D, "L": L, "order": N, "io_dtype": wl.dtype,
+                   "path": plan.path, "pass": "forward_circular"},
+        "hbm_frac_forward": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(dom, wl.name + "_circular") if lds else None,
+                     "kernel": dom, "alg_bytes_per_launch": nbytes, "launch_ms": round(ms, 5),
+                     "launches_per_step": 1},
+    }
+    if args.check:
+        ds = [0, D // 2, D - 1]
+        xs = synth.channel_subset(x, ds)
+        ref = oracle.forward_circular(xs.u_proj, xs.short_w, xs.h, xs.bias, N)
+        got = y.float().cpu().numpy()[:, ds]
+        out["check_rel_l2"] = oracle.rel_l2(got, ref)
+        log(f"[bench] oracle check on channels {ds}: rel_l2 {out['check_rel_l2']:.3e}")
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (circular oracle) ...")
+        rng = np.random.default_rng(99)
+        n = 1
+        while True:
+            ds = np.sort(rng.choice(D, size=n, replace=False))
+            xs = synth.channel_subset(x, ds)
+            t0 = time.perf_counter()
+            oracle.forward_circular(xs.u_proj, xs.short_w, xs.h, xs.bias, N)
+            dt = time.perf_counter() - t0
+            if dt >= args.cpu_budget / 4 or n >= D:
+                break
+            n = int(min(D, max(n + 1, n * args.cpu_budget / max(dt, 1e-3) * 0.8)))
+        out["cpu_baseline"] = {"value": B * n * L / dt, "unit": "channel-tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} of {D} channels at every b and t, fp64 numpy (one thread), "
+                                         f"{dt:.1f} s wall"}
+    print(json.dumps(out), flush=True)
+    plan.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -560,6 +641,8 @@ def main():
                     help="time hyena_operator_forward (in_proj GEMM + the path + out_proj GEMM) instead")
     ap.add_argument("--backward", action="store_true",
                     help="time hyena_backward instead of the forward (order 2 only when L > 16384)")
+    ap.add_argument("--circular", action="store_true",
+                    help="time hyena_forward on a circular plan (circular long convolutions) instead")
     ap.add_argument("--per-sample", action="store_true",
                     help="time hyena_forward_per_sample (a filter set per sample) instead")
     ap.add_argument("--filter", action="store_true",
@@ -593,6 +676,9 @@ def main():
         return
     if args.per_sample:
         bench_per_sample(args, wl, x, torch, Plan)
+        return
+    if args.circular:
+        bench_circular(args, wl, x, torch, Plan)
         return
     if args.backward:
         if wl.L > 16384 and wl.order != 2:

@@ -22,7 +22,9 @@ _PATHS = {"auto": PATH_AUTO, "lds": PATH_LDS, "fourstep": PATH_FOURSTEP, "fused"
 _DTYPES = {"f32": HYENA_F32, "bf16": HYENA_BF16}
 
 # every symbol include/hyena.h declares
-EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_destroy", "hyena_plan_path",
+FLAG_CIRCULAR = 1  # HYENA_FLAG_CIRCULAR
+
+EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_create_ex", "hyena_plan_destroy", "hyena_plan_path",
            "hyena_spectrum_bytes", "hyena_workspace_bytes", "hyena_filter_spectrum", "hyena_forward",
            "hyena_forward_timed", "hyena_fused_check", "hyena_backward_workspace_bytes", "hyena_backward",
            "hyena_operator_workspace_bytes", "hyena_operator_forward", "hyena_operator_forward_timed",
@@ -63,6 +65,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_plan_create.restype = ci
     lib.hyena_plan_create_path.argtypes = [ctypes.POINTER(vp), i64, i64, ci, ci, ci]
     lib.hyena_plan_create_path.restype = ci
+    lib.hyena_plan_create_ex.argtypes = [ctypes.POINTER(vp), i64, i64, ci, ci, ci, ctypes.c_uint32]
+    lib.hyena_plan_create_ex.restype = ci
     lib.hyena_plan_destroy.argtypes = [vp]
     lib.hyena_plan_destroy.restype = ci
     lib.hyena_plan_path.argtypes = [vp]
@@ -115,19 +119,21 @@ def _stream_handle(torch, device) -> int:
 class Plan:
     """A libhyena plan: fixed L, D, order and I/O dtype ("f32" or "bf16")."""
 
-    def __init__(self, L: int, D: int, order: int, dtype: str = "f32", path: str = "auto"):
+    def __init__(self, L: int, D: int, order: int, dtype: str = "f32", path: str = "auto",
+                 circular: bool = False):
         import torch  # device memory and streams only
 
         self._torch = torch
         self.lib = load_library()
         self.L, self.D, self.order, self.dtype = int(L), int(D), int(order), dtype
+        self.circular = bool(circular)
         if dtype not in _DTYPES or path not in _PATHS:
             raise ValueError(f"dtype must be one of {list(_DTYPES)}, path one of {list(_PATHS)}")
         self.device = torch.device("cuda", torch.cuda.current_device())
         h = ctypes.c_void_p()
-        _check("hyena_plan_create_path",
-               self.lib.hyena_plan_create_path(ctypes.byref(h), self.L, self.D, self.order, _DTYPES[dtype],
-                                               _PATHS[path]))
+        _check("hyena_plan_create_ex",
+               self.lib.hyena_plan_create_ex(ctypes.byref(h), self.L, self.D, self.order, _DTYPES[dtype],
+                                             _PATHS[path], FLAG_CIRCULAR if self.circular else 0))
         self.handle = h
         self.path = {PATH_LDS: "lds", PATH_FOURSTEP: "fourstep", PATH_FUSED: "fused"}[self.lib.hyena_plan_path(h)]
 

@@ -48,7 +48,7 @@ template <int LOGL>
 hipError_t launch_lds_forward_t(const LdsArgs& a, hipStream_t st);
 template <int LOGL>
 hipError_t launch_lds_spectrum_t(const float* h, float2* spec, int64_t rows, const float2* tw, const float2* wpair,
-                                 hipStream_t st);
+                                 hipStream_t st, bool circ);
 
 // ====================================================== fused persistent path
 //
@@ -240,28 +240,28 @@ hipError_t launch_lds_forward(int logL, const LdsArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_lds_spectrum(int logL, const float* h, float2* spec, int64_t rows, const float2* tw,
-                               const float2* wpair, hipStream_t st) {
+                               const float2* wpair, hipStream_t st, bool circ) {
     switch (logL) {
-        case 4: return launch_lds_spectrum_t<4>(h, spec, rows, tw, wpair, st);
-        case 5: return launch_lds_spectrum_t<5>(h, spec, rows, tw, wpair, st);
-        case 6: return launch_lds_spectrum_t<6>(h, spec, rows, tw, wpair, st);
-        case 7: return launch_lds_spectrum_t<7>(h, spec, rows, tw, wpair, st);
-        case 8: return launch_lds_spectrum_t<8>(h, spec, rows, tw, wpair, st);
-        case 9: return launch_lds_spectrum_t<9>(h, spec, rows, tw, wpair, st);
-        case 10: return launch_lds_spectrum_t<10>(h, spec, rows, tw, wpair, st);
-        case 11: return launch_lds_spectrum_t<11>(h, spec, rows, tw, wpair, st);
-        case 12: return launch_lds_spectrum_t<12>(h, spec, rows, tw, wpair, st);
-        case 13: return launch_lds_spectrum_t<13>(h, spec, rows, tw, wpair, st);
-        case 14: return launch_lds_spectrum_t<14>(h, spec, rows, tw, wpair, st);
+        case 4: return launch_lds_spectrum_t<4>(h, spec, rows, tw, wpair, st, circ);
+        case 5: return launch_lds_spectrum_t<5>(h, spec, rows, tw, wpair, st, circ);
+        case 6: return launch_lds_spectrum_t<6>(h, spec, rows, tw, wpair, st, circ);
+        case 7: return launch_lds_spectrum_t<7>(h, spec, rows, tw, wpair, st, circ);
+        case 8: return launch_lds_spectrum_t<8>(h, spec, rows, tw, wpair, st, circ);
+        case 9: return launch_lds_spectrum_t<9>(h, spec, rows, tw, wpair, st, circ);
+        case 10: return launch_lds_spectrum_t<10>(h, spec, rows, tw, wpair, st, circ);
+        case 11: return launch_lds_spectrum_t<11>(h, spec, rows, tw, wpair, st, circ);
+        case 12: return launch_lds_spectrum_t<12>(h, spec, rows, tw, wpair, st, circ);
+        case 13: return launch_lds_spectrum_t<13>(h, spec, rows, tw, wpair, st, circ);
+        case 14: return launch_lds_spectrum_t<14>(h, spec, rows, tw, wpair, st, circ);
         default: return hipErrorInvalidValue;
     }
 }
 
 // Launches the passes of one chunk of rows. With `marks`, an event is recorded
 // before the first launch and after every launch (1 + 2*(N-1) launches).
-template <int LOG1, int LOG2>
-static hipError_t fs_forward_chunk(const FsArgs& a, int64_t row0, int64_t nrows, hipStream_t st,
-                                   hipEvent_t* marks) {
+template <int LOG1, int LOG2, bool CIRC>
+static hipError_t fs_forward_chunk_c(const FsArgs& a, int64_t row0, int64_t nrows, hipStream_t st,
+                                     hipEvent_t* marks) {
     using Cfg = FsCfg<LOG1, LOG2>;
     int mi = 0;
     auto mark = [&]() {
@@ -272,10 +272,10 @@ static hipError_t fs_forward_chunk(const FsArgs& a, int64_t row0, int64_t nrows,
     const unsigned grow = (unsigned)xcd_grid(nrows, Cfg::L1 / 2 / Cfg::UNITS);
     const dim3 bcol(Cfg::COL_THREADS), brow(Cfg::ROW_THREADS);
     if (a.bf16)
-        hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, uint16_t, 0>), dim3(gcol), bcol, 0, st, (const uint16_t*)a.u,
+        hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, uint16_t, 0, CIRC>), dim3(gcol), bcol, 0, st, (const uint16_t*)a.u,
                            a.w3, (const float*)nullptr, a.ws, a.tb, a.D, a.N, row0, nrows);
     else
-        hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, float, 0>), dim3(gcol), bcol, 0, st, (const float*)a.u, a.w3,
+        hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, float, 0, CIRC>), dim3(gcol), bcol, 0, st, (const float*)a.u, a.w3,
                            (const float*)nullptr, a.ws, a.tb, a.D, a.N, row0, nrows);
     mark();
     for (int o = 0; o < a.N - 1; ++o) {
@@ -285,17 +285,17 @@ static hipError_t fs_forward_chunk(const FsArgs& a, int64_t row0, int64_t nrows,
         const bool last = (o == a.N - 2);
         if (a.bf16) {
             if (last)
-                hipLaunchKernelGGL((k_fs_colinv<LOG1, LOG2, uint16_t, true>), dim3(gcol), bcol, 0, st, a.ws,
+                hipLaunchKernelGGL((k_fs_colinv<LOG1, LOG2, uint16_t, true, CIRC>), dim3(gcol), bcol, 0, st, a.ws,
                                    (const uint16_t*)a.u, a.w3, (uint16_t*)a.y, a.tb, a.D, a.N, o, row0, nrows);
             else
-                hipLaunchKernelGGL((k_fs_colinv<LOG1, LOG2, uint16_t, false>), dim3(gcol), bcol, 0, st, a.ws,
+                hipLaunchKernelGGL((k_fs_colinv<LOG1, LOG2, uint16_t, false, CIRC>), dim3(gcol), bcol, 0, st, a.ws,
                                    (const uint16_t*)a.u, a.w3, (uint16_t*)a.y, a.tb, a.D, a.N, o, row0, nrows);
         } else {
             if (last)
-                hipLaunchKernelGGL((k_fs_colinv<LOG1, LOG2, float, true>), dim3(gcol), bcol, 0, st, a.ws,
+                hipLaunchKernelGGL((k_fs_colinv<LOG1, LOG2, float, true, CIRC>), dim3(gcol), bcol, 0, st, a.ws,
                                    (const float*)a.u, a.w3, (float*)a.y, a.tb, a.D, a.N, o, row0, nrows);
             else
-                hipLaunchKernelGGL((k_fs_colinv<LOG1, LOG2, float, false>), dim3(gcol), bcol, 0, st, a.ws,
+                hipLaunchKernelGGL((k_fs_colinv<LOG1, LOG2, float, false, CIRC>), dim3(gcol), bcol, 0, st, a.ws,
                                    (const float*)a.u, a.w3, (float*)a.y, a.tb, a.D, a.N, o, row0, nrows);
         }
         mark();
@@ -304,12 +304,24 @@ static hipError_t fs_forward_chunk(const FsArgs& a, int64_t row0, int64_t nrows,
 }
 
 template <int LOG1, int LOG2>
-static hipError_t fs_spectrum_t(const float* h, float2* spec, int64_t rows, const FsTables& tb, hipStream_t st) {
+static hipError_t fs_forward_chunk(const FsArgs& a, int64_t row0, int64_t nrows, hipStream_t st,
+                                   hipEvent_t* marks) {
+    return a.circ ? fs_forward_chunk_c<LOG1, LOG2, true>(a, row0, nrows, st, marks)
+                  : fs_forward_chunk_c<LOG1, LOG2, false>(a, row0, nrows, st, marks);
+}
+
+template <int LOG1, int LOG2>
+static hipError_t fs_spectrum_t(const float* h, float2* spec, int64_t rows, const FsTables& tb, hipStream_t st,
+                                bool circ) {
     using Cfg = FsCfg<LOG1, LOG2>;
     const unsigned gcol = (unsigned)xcd_grid(rows, Cfg::L2 / Cfg::CB);
     const unsigned grow = (unsigned)xcd_grid(rows, Cfg::L1 / 2 / Cfg::UNITS);
-    hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, float, 1>), dim3(gcol), dim3(Cfg::COL_THREADS), 0, st,
-                       (const float*)nullptr, (const float*)nullptr, h, spec, tb, 1, 2, (int64_t)0, rows);
+    if (circ)
+        hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, float, 1, true>), dim3(gcol), dim3(Cfg::COL_THREADS), 0, st,
+                           (const float*)nullptr, (const float*)nullptr, h, spec, tb, 1, 2, (int64_t)0, rows);
+    else
+        hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, float, 1, false>), dim3(gcol), dim3(Cfg::COL_THREADS), 0, st,
+                           (const float*)nullptr, (const float*)nullptr, h, spec, tb, 1, 2, (int64_t)0, rows);
     hipLaunchKernelGGL((k_fs_row<LOG1, LOG2, 1>), dim3(grow), dim3(Cfg::ROW_THREADS), 0, st, spec,
                        (const float2*)nullptr, (const float*)nullptr, tb, 1, 0, (int64_t)0, rows, (int64_t)0);
     return hipGetLastError();
@@ -337,10 +349,10 @@ hipError_t launch_fs_forward_chunk(int logL, const FsArgs& a, int64_t row0, int6
 }
 
 hipError_t launch_fs_spectrum(int logL, const float* h, float2* spec, int64_t rows, const FsTables& tb,
-                              hipStream_t st) {
+                              hipStream_t st, bool circ) {
     switch (logL) {
 #define X(LG, A, B) \
-    case LG: return fs_spectrum_t<A, B>(h, spec, rows, tb, st);
+    case LG: return fs_spectrum_t<A, B>(h, spec, rows, tb, st, circ);
         HY_FS_CASES(X)
 #undef X
         default: return hipErrorInvalidValue;

@@ -40,13 +40,17 @@ __device__ __forceinline__ float2 twiddle_step(const FsTables& tb, float2 base, 
 
 // Pass A: column FFTs over m1 of the packed gated input (MODE 0) or of a filter
 // row (MODE 1), written to the row-major [k1][m2] tile `slot` of row `flat`.
-template <int LOG1, int LOG2, class TIO, int MODE>
+// CIRC: rows of 2L samples with no zero padding (circular mode): all of every
+// column holds data and the first radix pass is not pruned.
+template <int LOG1, int LOG2, class TIO, int MODE, bool CIRC = false>
 __device__ __forceinline__ void fs_colfwd_body(float2* lds, const TIO* __restrict__ u, const float* __restrict__ w3,
                                                const float* __restrict__ h, float2* __restrict__ slot,
                                                const FsTables& tb, int D, int N, int64_t flat, int cb) {
     using Cfg = FsCfg<LOG1, LOG2>;
     constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T1 = Cfg::T1, CB = Cfg::CB;
     constexpr int64_t L = (int64_t)L1 * L2;
+    constexpr int64_t S = CIRC ? 2 * L : L;  // samples per input row
+    constexpr int LD = CIRC ? 16 : 8;        // column slots holding data
     const int c = threadIdx.x % CB, t = threadIdx.x / CB;
     const int m2 = cb * CB + c;
     float2 v[16];
@@ -54,28 +58,28 @@ __device__ __forceinline__ void fs_colfwd_body(float2* lds, const TIO* __restric
         const uint32_t b = (uint32_t)flat / (uint32_t)D, d = (uint32_t)flat - b * (uint32_t)D;
         const int64_t C = (int64_t)(N + 1) * D;
         const int64_t cv = N * D + d, cx = (N - 1) * D + d;
-        const TIO* rv = u + (b * C + cv) * L;
-        const TIO* rx = u + (b * C + cx) * L;
+        const TIO* rv = u + (b * C + cv) * S;
+        const TIO* rx = u + (b * C + cx) * S;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < LD; ++e) {
             const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
             v[e] = gated_pair(rv, rx, m, w3 + 3 * cv, w3 + 3 * cx);
         }
     } else {
-        const float* hr = h + flat * L;
+        const float* hr = h + flat * S;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = load_pair(hr, (uint32_t)(t + T1 * e) * L2 + m2);
+        for (int e = 0; e < LD; ++e) v[e] = load_pair(hr, (uint32_t)(t + T1 * e) * L2 + m2);
     }
 #pragma unroll
-    for (int e = 8; e < 16; ++e) v[e] = make_float2(0.f, 0.f);
-    fft_strided<L1, false, true>(v, t, tb.tw1, ColAcc<Cfg::CP>{lds + c});
+    for (int e = LD; e < 16; ++e) v[e] = make_float2(0.f, 0.f);
+    fft_strided<L1, false, !CIRC>(v, t, tb.tw1, ColAcc<Cfg::CP>{lds + c});
     // four-step twiddle W_L^(k1*m2), applied here so that pass B carries none
     const float2 base = twiddle_base<L2>(tb, t, m2);
 #pragma unroll
     for (int e = 0; e < 16; ++e) slot[(uint32_t)(t + T1 * e) * L2 + m2] = cmul(v[e], twiddle_step<L2>(tb, base, e, m2));
 }
 
-template <int LOG1, int LOG2, class TIO, int MODE>
+template <int LOG1, int LOG2, class TIO, int MODE, bool CIRC = false>
 __global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::COL_THREADS))
 k_fs_colfwd(const TIO* __restrict__ u, const float* __restrict__ w3, const float* __restrict__ h,
             float2* __restrict__ ws, FsTables tb, int D, int N, int64_t row0, int64_t nrows) {
@@ -86,7 +90,7 @@ k_fs_colfwd(const TIO* __restrict__ u, const float* __restrict__ w3, const float
     if (!xcd_row_map(blockIdx.x, nrows, Cfg::L2 / Cfg::CB, r, cb)) return;
     const int64_t L = (int64_t)Cfg::L1 * Cfg::L2;
     float2* slot = (MODE == 0) ? ws + r * L : ws + (row0 + r) * L;
-    fs_colfwd_body<LOG1, LOG2, TIO, MODE>(lds, u, w3, h, slot, tb, D, N, row0 + r, cb);
+    fs_colfwd_body<LOG1, LOG2, TIO, MODE, CIRC>(lds, u, w3, h, slot, tb, D, N, row0 + r, cb);
 }
 
 // Where one pair slot of pass B lives: LDS rows/indices of its two bins, the
@@ -286,13 +290,15 @@ k_fs_row(float2* __restrict__ ws, const float2* __restrict__ spec, const float* 
 // the gate. The last step stores y;
 // otherwise the gated result is the next step's input and its forward column
 // FFTs (pass A of step o+1) run here, written back in place.
-template <int LOG1, int LOG2, class TIO, bool LAST>
+template <int LOG1, int LOG2, class TIO, bool LAST, bool CIRC = false>
 __device__ __forceinline__ void fs_colinv_body(float2* lds, float2* __restrict__ slot, const TIO* __restrict__ u,
                                                const float* __restrict__ w3, TIO* __restrict__ y, const FsTables& tb,
                                                int D, int N, int o, int64_t flat, int cb) {
     using Cfg = FsCfg<LOG1, LOG2>;
     constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T1 = Cfg::T1, CB = Cfg::CB;
     constexpr int64_t L = (int64_t)L1 * L2;
+    constexpr int64_t S = CIRC ? 2 * L : L;  // samples per row of u_proj and y
+    constexpr int LD = CIRC ? 16 : 8;        // column slots holding data
     const uint32_t b = (uint32_t)flat / (uint32_t)D, d = (uint32_t)flat - b * (uint32_t)D;
     const int c = threadIdx.x % CB, t = threadIdx.x / CB;
     const int m2 = cb * CB + c;
@@ -304,31 +310,31 @@ __device__ __forceinline__ void fs_colinv_body(float2* lds, float2* __restrict__
     fft_strided<L1, true, false>(v, t, tb.tw1, cacc);
     const int64_t C = (int64_t)(N + 1) * D;
     const int64_t cg = (int64_t)(LAST ? 0 : N - 2 - o) * D + d;
-    const TIO* rg = u + (b * C + cg) * L;
+    const TIO* rg = u + (b * C + cg) * S;
     const float* wg = w3 + 3 * cg;
     if constexpr (LAST) {
-        TIO* yr = y + (b * D + d) * L;
+        TIO* yr = y + (b * D + d) * S;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < LD; ++e) {
             const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
             store_pair(yr, m, emul(v[e], conv3_pair(rg, m, wg[0], wg[1], wg[2])));
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < LD; ++e) {
             const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
             v[e] = emul(v[e], conv3_pair(rg, m, wg[0], wg[1], wg[2]));
         }
 #pragma unroll
-        for (int e = 8; e < 16; ++e) v[e] = make_float2(0.f, 0.f);
-        fft_strided<L1, false, true>(v, t, tb.tw1, cacc);
+        for (int e = LD; e < 16; ++e) v[e] = make_float2(0.f, 0.f);
+        fft_strided<L1, false, !CIRC>(v, t, tb.tw1, cacc);
 #pragma unroll
         for (int e = 0; e < 16; ++e)
             slot[(uint32_t)(t + T1 * e) * L2 + m2] = cmul(v[e], twiddle_step<L2>(tb, base, e, m2));
     }
 }
 
-template <int LOG1, int LOG2, class TIO, bool LAST>
+template <int LOG1, int LOG2, class TIO, bool LAST, bool CIRC = false>
 __global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::COL_THREADS))
 k_fs_colinv(float2* __restrict__ ws, const TIO* __restrict__ u, const float* __restrict__ w3, TIO* __restrict__ y,
             FsTables tb, int D, int N, int o, int64_t row0, int64_t nrows) {
@@ -338,7 +344,7 @@ k_fs_colinv(float2* __restrict__ ws, const TIO* __restrict__ u, const float* __r
     int cb;
     if (!xcd_row_map(blockIdx.x, nrows, Cfg::L2 / Cfg::CB, r, cb)) return;
     const int64_t L = (int64_t)Cfg::L1 * Cfg::L2;
-    fs_colinv_body<LOG1, LOG2, TIO, LAST>(lds, ws + r * L, u, w3, y, tb, D, N, o, row0 + r, cb);
+    fs_colinv_body<LOG1, LOG2, TIO, LAST, CIRC>(lds, ws + r * L, u, w3, y, tb, D, N, o, row0 + r, cb);
 }
 
 // log2 L -> (log2 L1, log2 L2). Square splits up to L1 = 512, whose pass A/C

@@ -72,7 +72,7 @@ size_t stockham_size(int logn) {
 }
 
 int64_t chunk_rows(const hyena_plan_t plan, int64_t rows, size_t ws_bytes) {
-    const size_t per_row = (size_t)plan->L * sizeof(float2);
+    const size_t per_row = ((size_t)1 << plan->logT) * sizeof(float2);
     int64_t n = (int64_t)(ws_bytes / per_row);
     if (n > rows) n = rows;
     if (n > kMaxChunkRows) n = kMaxChunkRows;  // keeps every grid dimension far below 2^31
@@ -94,9 +94,11 @@ const char* hyena_status_string(hyena_status_t s) {
     }
 }
 
-hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype,
-                                      hyena_path_t path) {
+hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype,
+                                    hyena_path_t path, uint32_t flags) {
     if (!out) return HYENA_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)HYENA_FLAG_CIRCULAR) return HYENA_ERR_INVALID_ARG;
+    const bool circ = (flags & HYENA_FLAG_CIRCULAR) != 0;
     if (D < 1 || L < 1 || order < 2) return HYENA_ERR_INVALID_ARG;
     if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
     if (path != HYENA_PATH_AUTO && path != HYENA_PATH_LDS && path != HYENA_PATH_FOURSTEP && path != HYENA_PATH_FUSED)
@@ -104,15 +106,20 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
     if (!is_pow2(L) || L < 16 || L > (int64_t(1) << kMaxLog) || order > 8) return HYENA_ERR_UNSUPPORTED;
     if (D > (int64_t(1) << 24)) return HYENA_ERR_UNSUPPORTED;
     const int logL = ilog2_64(L);
+    // a zero-padded plan transforms 2L real samples as L complex values; a circular
+    // plan transforms its L samples as L/2 complex values
+    const int logT = circ ? logL - 1 : logL;
+    const int64_t T = int64_t(1) << logT;
+    if (logT < hy::kLdsMinLog) return HYENA_ERR_UNSUPPORTED;
     hyena_path_t p = path;
     if (p == HYENA_PATH_AUTO) {
-        if (logL <= hy::kLdsMaxLog) p = HYENA_PATH_LDS;
-        else if (kAutoFused && order == 2 && hy::fused_supported(logL)) p = HYENA_PATH_FUSED;
+        if (logT <= hy::kLdsMaxLog) p = HYENA_PATH_LDS;
+        else if (!circ && kAutoFused && order == 2 && hy::fused_supported(logT)) p = HYENA_PATH_FUSED;
         else p = HYENA_PATH_FOURSTEP;
     }
-    if (p == HYENA_PATH_LDS && logL > hy::kLdsMaxLog) return HYENA_ERR_UNSUPPORTED;
-    if (p == HYENA_PATH_FOURSTEP && logL < hy::kFsMinLog) return HYENA_ERR_UNSUPPORTED;
-    if (p == HYENA_PATH_FUSED && !(order == 2 && hy::fused_supported(logL))) return HYENA_ERR_UNSUPPORTED;
+    if (p == HYENA_PATH_LDS && logT > hy::kLdsMaxLog) return HYENA_ERR_UNSUPPORTED;
+    if (p == HYENA_PATH_FOURSTEP && logT < hy::kFsMinLog) return HYENA_ERR_UNSUPPORTED;
+    if (p == HYENA_PATH_FUSED && (circ || !(order == 2 && hy::fused_supported(logT)))) return HYENA_ERR_UNSUPPORTED;
 
     // host tables (fp64 -> fp32)
     std::vector<float2> tab;
@@ -120,11 +127,11 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
     int log1 = 0, log2 = 0;
     if (p == HYENA_PATH_LDS) {
         o_tw = tab.size();
-        append_stockham(tab, logL);
+        append_stockham(tab, logT);
         o_wpair = tab.size();
-        for (int64_t k = 0; k <= L / 2; ++k) tab.push_back(wfwd(k, 2 * L));
+        for (int64_t k = 0; k <= T / 2; ++k) tab.push_back(wfwd(k, 2 * T));
     } else {
-        hy::fs_split(logL, &log1, &log2);
+        hy::fs_split(logT, &log1, &log2);
         const int64_t L1 = int64_t(1) << log1, L2 = int64_t(1) << log2;
         o_tw1 = tab.size();
         append_stockham(tab, log1);
@@ -135,14 +142,14 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
         const int64_t T1 = L1 / 16;
         o_lo = tab.size();
         for (int64_t t = 0; t < T1; ++t)
-            for (int64_t m2 = 0; m2 < L2; ++m2) tab.push_back(wfwd(t * m2, L));
+            for (int64_t m2 = 0; m2 < L2; ++m2) tab.push_back(wfwd(t * m2, T));
         o_hi = tab.size();
         for (int64_t e = 0; e < 16; ++e)
-            for (int64_t m2 = 0; m2 < L2; ++m2) tab.push_back(wfwd(T1 * e * m2, L));
+            for (int64_t m2 = 0; m2 < L2; ++m2) tab.push_back(wfwd(T1 * e * m2, T));
         o_pa = tab.size();
-        for (int64_t k1 = 0; k1 < L1; ++k1) tab.push_back(wfwd(k1, 2 * L));
+        for (int64_t k1 = 0; k1 < L1; ++k1) tab.push_back(wfwd(k1, 2 * T));
         o_pb = tab.size();
-        for (int64_t k2 = 0; k2 < L2; ++k2) tab.push_back(wfwd(L1 * k2, 2 * L));
+        for (int64_t k2 = 0; k2 < L2; ++k2) tab.push_back(wfwd(L1 * k2, 2 * T));
     }
 
     int dev = -1;
@@ -152,7 +159,7 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
             return HYENA_ERR_DEVICE;
-        const int per_cu = hy::fused_blocks_per_cu(logL);
+        const int per_cu = hy::fused_blocks_per_cu(logT);
         if (per_cu < 1) return HYENA_ERR_DEVICE;
         fused_blocks = (cus * per_cu) / 8 * 8;  // a multiple of 8: every XCD gets the same share
     }
@@ -171,6 +178,8 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
     plan->D = D;
     plan->order = order;
     plan->logL = logL;
+    plan->logT = logT;
+    plan->circular = circ;
     plan->dtype = dtype;
     plan->path = p;
     plan->device = dev;
@@ -193,6 +202,11 @@ hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, i
     return HYENA_OK;
 }
 
+hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype,
+                                      hyena_path_t path) {
+    return hyena_plan_create_ex(out, L, D, order, dtype, path, 0);
+}
+
 hyena_status_t hyena_plan_create(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype) {
     return hyena_plan_create_path(out, L, D, order, dtype, HYENA_PATH_AUTO);
 }
@@ -210,14 +224,14 @@ hyena_path_t hyena_plan_path(hyena_plan_t plan) { return plan ? plan->path : HYE
 
 size_t hyena_spectrum_bytes(hyena_plan_t plan) {
     if (!plan) return 0;
-    return (size_t)(plan->order - 1) * (size_t)plan->D * (size_t)plan->L * sizeof(float2);
+    return (size_t)(plan->order - 1) * (size_t)plan->D * ((size_t)1 << plan->logT) * sizeof(float2);
 }
 
 size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B) {
     if (!plan || B < 1) return 0;
     if (plan->path == HYENA_PATH_LDS) return 0;
-    if (plan->path == HYENA_PATH_FUSED) return hy::fused_workspace_bytes(plan->logL, B * plan->D, kFusedG, kFusedS);
-    const size_t per_row = (size_t)plan->L * sizeof(float2);
+    if (plan->path == HYENA_PATH_FUSED) return hy::fused_workspace_bytes(plan->logT, B * plan->D, kFusedG, kFusedS);
+    const size_t per_row = ((size_t)1 << plan->logT) * sizeof(float2);
     int64_t rows = B * plan->D;
     int64_t want = (int64_t)(kChunkTargetBytes / per_row);
     if (want < 1) want = 1;
@@ -234,9 +248,9 @@ hyena_status_t hyena_filter_spectrum_batched(hyena_plan_t plan, int64_t B, const
     const int64_t rows = B * (plan->order - 1) * plan->D;
     hipError_t e;
     if (plan->path == HYENA_PATH_LDS)
-        e = hy::launch_lds_spectrum(plan->logL, h, (float2*)spec, rows, plan->tw, plan->wpair, stream);
+        e = hy::launch_lds_spectrum(plan->logT, h, (float2*)spec, rows, plan->tw, plan->wpair, stream, plan->circular);
     else
-        e = hy::launch_fs_spectrum(plan->logL, h, (float2*)spec, rows, plan->fs, stream);
+        e = hy::launch_fs_spectrum(plan->logT, h, (float2*)spec, rows, plan->fs, stream, plan->circular);
     return e == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
 }
 
@@ -264,10 +278,10 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
     int64_t chunk = 0;
     if (per_sample && plan->path == HYENA_PATH_FUSED) return HYENA_ERR_UNSUPPORTED;
     // sample b reads spectrum b when every sample has its own filters
-    const int64_t sbs = per_sample ? (int64_t)(plan->order - 1) * plan->D * plan->L : 0;
+    const int64_t sbs = per_sample ? (int64_t)(plan->order - 1) * plan->D * (int64_t(1) << plan->logT) : 0;
     if (plan->path == HYENA_PATH_FUSED) {
         if (!workspace || !aligned16(workspace)) return HYENA_ERR_WORKSPACE;
-        if (workspace_bytes < hy::fused_workspace_bytes(plan->logL, rows, kFusedG, kFusedS)) return HYENA_ERR_WORKSPACE;
+        if (workspace_bytes < hy::fused_workspace_bytes(plan->logT, rows, kFusedG, kFusedS)) return HYENA_ERR_WORKSPACE;
     }
     if (plan->path == HYENA_PATH_FOURSTEP) {
         if (!workspace || !aligned16(workspace)) return HYENA_ERR_WORKSPACE;
@@ -296,24 +310,24 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
         hy::FsArgs a{u_proj, short_w, (const float2*)spec, bias, y, (float2*)workspace, plan->fs,
                      (int)plan->D, plan->order, bf16};
         if (ms) (void)hipEventRecord(ev[0], stream);
-        if (hy::launch_fs_fused(plan->logL, a, rows, kFusedG, kFusedS, plan->fused_blocks, stream) != hipSuccess)
+        if (hy::launch_fs_fused(plan->logT, a, rows, kFusedG, kFusedS, plan->fused_blocks, stream) != hipSuccess)
             st = HYENA_ERR_DEVICE;
         if (ms) (void)hipEventRecord(ev[1], stream);
     } else if (plan->path == HYENA_PATH_LDS) {
         if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
         hy::LdsArgs a{u_proj, short_w, (const float2*)spec, bias, y, plan->tw, plan->wpair,
-                      (int)B, (int)plan->D, plan->order, bf16, sbs};
+                      (int)B, (int)plan->D, plan->order, bf16, sbs, plan->circular};
         if (ms) (void)hipEventRecord(ev[0], stream);
-        if (hy::launch_lds_forward(plan->logL, a, stream) != hipSuccess) st = HYENA_ERR_DEVICE;
+        if (hy::launch_lds_forward(plan->logT, a, stream) != hipSuccess) st = HYENA_ERR_DEVICE;
         if (ms) (void)hipEventRecord(ev[1], stream);
     } else {
         hy::FsArgs a{u_proj, short_w, (const float2*)spec, bias, y, (float2*)workspace, plan->fs,
-                     (int)plan->D, plan->order, bf16, sbs};
+                     (int)plan->D, plan->order, bf16, sbs, plan->circular};
         int64_t ci = 0;
         for (int64_t r0 = 0; r0 < rows && st == HYENA_OK; r0 += chunk, ++ci) {
             const int64_t n = (rows - r0) < chunk ? (rows - r0) : chunk;
             hipEvent_t* marks = ms ? ev.data() + ci * (per_chunk + 1) : nullptr;
-            if (hy::launch_fs_forward_chunk(plan->logL, a, r0, n, stream, marks) != hipSuccess)
+            if (hy::launch_fs_forward_chunk(plan->logT, a, r0, n, stream, marks) != hipSuccess)
                 st = HYENA_ERR_DEVICE;
         }
     }

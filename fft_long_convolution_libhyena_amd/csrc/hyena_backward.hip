@@ -10,7 +10,7 @@
 extern "C" {
 
 size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B) {
-    if (!plan || B < 1) return 0;
+    if (!plan || B < 1 || plan->circular) return 0;
     if (plan->path == HYENA_PATH_LDS) return hy::bwd_ws_bytes(B, plan->D, plan->L, plan->order);
     if (plan->path == HYENA_PATH_FOURSTEP && plan->order == 2) return hy::fs_bwd_ws_bytes(plan->logL, B, plan->D);
     return 0;
@@ -27,7 +27,7 @@ hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, 
         return HYENA_ERR_INVALID_ARG;
     if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 26)) return HYENA_ERR_INVALID_ARG;
     const bool fs = plan->path == HYENA_PATH_FOURSTEP;
-    if (!(plan->path == HYENA_PATH_LDS || (fs && plan->order == 2))) return HYENA_ERR_UNSUPPORTED;
+    if (plan->circular || !(plan->path == HYENA_PATH_LDS || (fs && plan->order == 2))) return HYENA_ERR_UNSUPPORTED;
     if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
     if (!workspace || !aligned16(workspace) || workspace_bytes < hyena_backward_workspace_bytes(plan, B))
         return HYENA_ERR_WORKSPACE;

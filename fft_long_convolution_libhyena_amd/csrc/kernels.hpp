@@ -33,6 +33,7 @@ struct LdsCfg {
     static constexpr int E = LOGL >= HY_LDS_E32_FROM ? 32 : 16;
     static constexpr int THREADS = L / E;
 };
+constexpr int kLdsMinLog = 4;   // L = 16: one thread per 16 values
 constexpr int kLdsMaxLog = 14;  // L = 16384: 139,264 bytes of LDS
 
 // Four-step path geometry for L = L1 * L2.
@@ -64,6 +65,7 @@ struct LdsArgs {
     int B, D, N;
     bool bf16;
     int64_t sbs = 0;      // spectrum batch stride (complex values): 0 = one spectrum for every b
+    bool circ = false;    // circular convolution of 2L-sample rows (no zero padding)
 };
 
 struct FsTables {
@@ -86,15 +88,16 @@ struct FsArgs {
     int D, N;
     bool bf16;
     int64_t sbs = 0;  // spectrum batch stride (complex values): 0 = one spectrum for every b
+    bool circ = false;  // circular convolution of 2L-sample rows (no zero padding)
 };
 
 hipError_t launch_lds_forward(int logL, const LdsArgs& a, hipStream_t st);
 hipError_t launch_lds_spectrum(int logL, const float* h, float2* spec, int64_t rows, const float2* tw,
-                               const float2* wpair, hipStream_t st);
+                               const float2* wpair, hipStream_t st, bool circ = false);
 hipError_t launch_fs_forward_chunk(int logL, const FsArgs& a, int64_t row0, int64_t nrows, hipStream_t st,
                                    hipEvent_t* marks = nullptr);
 hipError_t launch_fs_spectrum(int logL, const float* h, float2* spec, int64_t rows, const FsTables& tb,
-                              hipStream_t st);
+                              hipStream_t st, bool circ = false);
 void fs_split(int logL, int* log1, int* log2);
 
 // Fused persistent four-step (order 2): one launch per forward, per-XCD pipelines.

@@ -44,7 +44,10 @@ namespace hy {
 // N (the recurrence order) is a template parameter so the step loop unrolls:
 // with a run-time trip count the compiler keeps both transforms' state live
 // across the loop and needs about twice the registers.
-template <int LOGL, int N, class TIO>
+// CIRC: circular convolution of sequences of 2L samples (the HyenaND summary's
+// circular boundary mode): the same L-point packed transform with every slot
+// holding data (no zero-padded half, no pruned first pass) and every output kept.
+template <int LOGL, int N, class TIO, bool CIRC = false>
 __global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS)
 k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const float2* __restrict__ spec,
               const float* __restrict__ bias, TIO* __restrict__ y, const float2* __restrict__ tw,
@@ -53,6 +56,9 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
     constexpr int E = LdsCfg<LOGL>::E;
     constexpr int H = E / 2;
     constexpr int T = L / E;
+    constexpr int64_t S = CIRC ? 2 * (int64_t)L : L;  // samples per row of u_proj and y
+    constexpr int LD = CIRC ? E : H;                  // slots holding data
+    constexpr bool PF_GATE = HY_LDS_PREFETCH_GATE && !CIRC;
     __shared__ float2 lds[padded_len<L>()];
     const RowAcc acc{lds};
     // Consecutive workgroups go to different XCDs; the B batch rows of channel d
@@ -64,17 +70,17 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
     if (d >= D) return;
     const int t = threadIdx.x;
     const int64_t C = (int64_t)(N + 1) * D;
-    const TIO* ub = u + (int64_t)b * C * L;
+    const TIO* ub = u + (int64_t)b * C * S;
 
     float2 v[E];
     {
         const int cv = N * D + d, cx = (N - 1) * D + d;
-        const TIO* rv = ub + (int64_t)cv * L;
-        const TIO* rx = ub + (int64_t)cx * L;
+        const TIO* rv = ub + (int64_t)cv * S;
+        const TIO* rx = ub + (int64_t)cx * S;
 #pragma unroll
-        for (int e = 0; e < H; ++e) v[e] = gated_pair(rv, rx, (uint32_t)(t + T * e), w3 + 3 * cv, w3 + 3 * cx);
+        for (int e = 0; e < LD; ++e) v[e] = gated_pair(rv, rx, (uint32_t)(t + T * e), w3 + 3 * cv, w3 + 3 * cx);
 #pragma unroll
-        for (int e = H; e < E; ++e) v[e] = make_float2(0.f, 0.f);
+        for (int e = LD; e < E; ++e) v[e] = make_float2(0.f, 0.f);
     }
     const float bscale = 1.0f / (4.0f * (float)L);
 #pragma unroll
@@ -93,7 +99,7 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
                 hm[e] = Hs[k == 0 ? 0u : (uint32_t)L - k];
             }
         }
-        fft_strided<L, false, true>(v, t, tw, acc);
+        fft_strided<L, false, !CIRC>(v, t, tw, acc);
         __syncthreads();
         lds_store_strided<T>(acc, t, v);
         __syncthreads();
@@ -131,12 +137,12 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
         lds_load_strided<T>(acc, t, v);
         const bool last = (o == N - 2);
         const int cg = (last ? 0 : N - 2 - o) * D + d;
-        const TIO* rg = ub + (int64_t)cg * L;
+        const TIO* rg = ub + (int64_t)cg * S;
         const float* wg = w3 + 3 * cg;
         // the gate's input samples, fetched before the inverse transform so that
         // their latency hides behind it
         typename RawPair<TIO>::type gcur[H], gprev[H];
-        if constexpr (HY_LDS_PREFETCH_GATE) {
+        if constexpr (PF_GATE) {
             if (last) {
 #pragma unroll
                 for (int e = 0; e < H; ++e) {
@@ -149,12 +155,12 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
         fft_strided<L, true, false>(v, t, tw, acc);
         // v[e], e < E/2, holds (c[2m], c[2m+1]) = conv + bias*v at m = t + T*e
         if (last) {
-            TIO* yr = y + ((int64_t)b * D + d) * L;
+            TIO* yr = y + ((int64_t)b * D + d) * S;
 #pragma unroll
-            for (int e = 0; e < H; ++e) {
+            for (int e = 0; e < LD; ++e) {
                 const uint32_t m = t + T * e;
                 float2 g;
-                if constexpr (HY_LDS_PREFETCH_GATE)
+                if constexpr (PF_GATE)
                     g = conv3_from(unpack_raw(gprev[e]), unpack_raw(gcur[e]), wg[0], wg[1], wg[2]);
                 else
                     g = conv3_pair(rg, m, wg[0], wg[1], wg[2]);
@@ -162,16 +168,17 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < H; ++e) v[e] = emul(v[e], conv3_pair(rg, (uint32_t)(t + T * e), wg[0], wg[1], wg[2]));
+            for (int e = 0; e < LD; ++e) v[e] = emul(v[e], conv3_pair(rg, (uint32_t)(t + T * e), wg[0], wg[1], wg[2]));
 #pragma unroll
-            for (int e = H; e < E; ++e) v[e] = make_float2(0.f, 0.f);
+            for (int e = LD; e < E; ++e) v[e] = make_float2(0.f, 0.f);
         }
     }
 }
 
 // Filter spectrum for the LDS path: natural-order bins, slot 0 = (A[0], A[L]),
 // every value scaled by 1/(4L).
-template <int LOGL>
+// CIRC: the filter has 2L samples and no zero padding (circular mode).
+template <int LOGL, bool CIRC = false>
 __global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS)
 k_lds_spectrum(const float* __restrict__ h, float2* __restrict__ spec, const float2* __restrict__ tw,
                const float2* __restrict__ wpair) {
@@ -179,18 +186,20 @@ k_lds_spectrum(const float* __restrict__ h, float2* __restrict__ spec, const flo
     constexpr int E = LdsCfg<LOGL>::E;
     constexpr int H = E / 2;
     constexpr int T = L / E;
+    constexpr int64_t S = CIRC ? 2 * (int64_t)L : L;
+    constexpr int LD = CIRC ? E : H;
     __shared__ float2 lds[padded_len<L>()];
     const RowAcc acc{lds};
     const int64_t row = blockIdx.x;
     const int t = threadIdx.x;
-    const float* hr = h + row * L;
+    const float* hr = h + row * S;
     float2* out = spec + row * L;
     float2 v[E];
 #pragma unroll
-    for (int e = 0; e < H; ++e) v[e] = load_pair(hr, (uint32_t)(t + T * e));
+    for (int e = 0; e < LD; ++e) v[e] = load_pair(hr, (uint32_t)(t + T * e));
 #pragma unroll
-    for (int e = H; e < E; ++e) v[e] = make_float2(0.f, 0.f);
-    fft_strided<L, false, true>(v, t, tw, acc);
+    for (int e = LD; e < E; ++e) v[e] = make_float2(0.f, 0.f);
+    fft_strided<L, false, !CIRC>(v, t, tw, acc);
     __syncthreads();
     lds_store_strided<T>(acc, t, v);
     __syncthreads();
@@ -217,17 +226,26 @@ k_lds_spectrum(const float* __restrict__ h, float2* __restrict__ spec, const flo
     }
 }
 
-template <int LOGL, int N>
-inline void launch_lds_forward_n(const LdsArgs& a, hipStream_t st) {
+template <int LOGL, int N, bool CIRC>
+inline void launch_lds_forward_c(const LdsArgs& a, hipStream_t st) {
     constexpr int T = LdsCfg<LOGL>::THREADS;
     const int dgroups = (a.D + 7) / 8;
     const unsigned grid = (unsigned)(a.B * 8 * dgroups);
     if (a.bf16)
-        hipLaunchKernelGGL((k_lds_forward<LOGL, N, uint16_t>), dim3(grid), dim3(T), 0, st, (const uint16_t*)a.u,
-                           a.w3, a.spec, a.bias, (uint16_t*)a.y, a.tw, a.wpair, a.B, a.D, a.sbs);
+        hipLaunchKernelGGL((k_lds_forward<LOGL, N, uint16_t, CIRC>), dim3(grid), dim3(T), 0, st,
+                           (const uint16_t*)a.u, a.w3, a.spec, a.bias, (uint16_t*)a.y, a.tw, a.wpair, a.B, a.D,
+                           a.sbs);
     else
-        hipLaunchKernelGGL((k_lds_forward<LOGL, N, float>), dim3(grid), dim3(T), 0, st, (const float*)a.u, a.w3,
-                           a.spec, a.bias, (float*)a.y, a.tw, a.wpair, a.B, a.D, a.sbs);
+        hipLaunchKernelGGL((k_lds_forward<LOGL, N, float, CIRC>), dim3(grid), dim3(T), 0, st, (const float*)a.u,
+                           a.w3, a.spec, a.bias, (float*)a.y, a.tw, a.wpair, a.B, a.D, a.sbs);
+}
+
+template <int LOGL, int N>
+inline void launch_lds_forward_n(const LdsArgs& a, hipStream_t st) {
+    if (a.circ)
+        launch_lds_forward_c<LOGL, N, true>(a, st);
+    else
+        launch_lds_forward_c<LOGL, N, false>(a, st);
 }
 
 template <int LOGL>
@@ -247,9 +265,13 @@ hipError_t launch_lds_forward_t(const LdsArgs& a, hipStream_t st) {
 
 template <int LOGL>
 hipError_t launch_lds_spectrum_t(const float* h, float2* spec, int64_t rows, const float2* tw,
-                                        const float2* wpair, hipStream_t st) {
-    hipLaunchKernelGGL((k_lds_spectrum<LOGL>), dim3((unsigned)rows), dim3(LdsCfg<LOGL>::THREADS), 0, st, h, spec,
-                       tw, wpair);
+                                        const float2* wpair, hipStream_t st, bool circ) {
+    if (circ)
+        hipLaunchKernelGGL((k_lds_spectrum<LOGL, true>), dim3((unsigned)rows), dim3(LdsCfg<LOGL>::THREADS), 0, st,
+                           h, spec, tw, wpair);
+    else
+        hipLaunchKernelGGL((k_lds_spectrum<LOGL, false>), dim3((unsigned)rows), dim3(LdsCfg<LOGL>::THREADS), 0,
+                           st, h, spec, tw, wpair);
     return hipGetLastError();
 }
 

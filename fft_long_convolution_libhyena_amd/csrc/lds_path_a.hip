@@ -3,17 +3,17 @@
 
 namespace hy {
 template hipError_t launch_lds_forward_t<4>(const LdsArgs&, hipStream_t);
-template hipError_t launch_lds_spectrum_t<4>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t);
+template hipError_t launch_lds_spectrum_t<4>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t, bool);
 template hipError_t launch_lds_forward_t<5>(const LdsArgs&, hipStream_t);
-template hipError_t launch_lds_spectrum_t<5>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t);
+template hipError_t launch_lds_spectrum_t<5>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t, bool);
 template hipError_t launch_lds_forward_t<6>(const LdsArgs&, hipStream_t);
-template hipError_t launch_lds_spectrum_t<6>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t);
+template hipError_t launch_lds_spectrum_t<6>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t, bool);
 template hipError_t launch_lds_forward_t<7>(const LdsArgs&, hipStream_t);
-template hipError_t launch_lds_spectrum_t<7>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t);
+template hipError_t launch_lds_spectrum_t<7>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t, bool);
 template hipError_t launch_lds_forward_t<8>(const LdsArgs&, hipStream_t);
-template hipError_t launch_lds_spectrum_t<8>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t);
+template hipError_t launch_lds_spectrum_t<8>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t, bool);
 template hipError_t launch_lds_forward_t<9>(const LdsArgs&, hipStream_t);
-template hipError_t launch_lds_spectrum_t<9>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t);
+template hipError_t launch_lds_spectrum_t<9>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t, bool);
 template hipError_t launch_lds_forward_t<10>(const LdsArgs&, hipStream_t);
-template hipError_t launch_lds_spectrum_t<10>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t);
+template hipError_t launch_lds_spectrum_t<10>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t, bool);
 }  // namespace hy

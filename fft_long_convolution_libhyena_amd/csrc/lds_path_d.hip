@@ -3,5 +3,5 @@
 
 namespace hy {
 template hipError_t launch_lds_forward_t<14>(const LdsArgs&, hipStream_t);
-template hipError_t launch_lds_spectrum_t<14>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t);
+template hipError_t launch_lds_spectrum_t<14>(const float*, float2*, int64_t, const float2*, const float2*, hipStream_t, bool);
 }  // namespace hy

@@ -10,7 +10,9 @@
 struct hyena_plan_s {
     int64_t L = 0, D = 0;
     int order = 0;
-    int logL = 0;
+    int logL = 0;            // log2 of the sequence length
+    int logT = 0;            // log2 of the packed complex transform length (logL - circular)
+    bool circular = false;   // circular convolution instead of zero padding to 2L
     hyena_dtype_t dtype = HYENA_F32;
     hyena_path_t path = HYENA_PATH_AUTO;
     int device = -1;

@@ -92,6 +92,23 @@ hyena_status_t hyena_plan_create(hyena_plan_t* out, int64_t L, int64_t D, int or
 hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype,
                                       hyena_path_t path);
 
+/* Plan options (bit flags for hyena_plan_create_ex). */
+enum {
+    /* Circular long convolution (the HyenaND summary's boundary handling offers
+     * circular convolution for periodic data besides zero padding to double the
+     * grid):  conv(v, h)[t] = sum_{s < L} h[s] v[(t - s) mod L]. The L samples are
+     * transformed as they are (an L-point real transform, no zero padding); the
+     * short conv keeps its causal zero padding. Requires L >= 32; the LDS path
+     * serves L <= 32768. hyena_backward does not support circular plans. */
+    HYENA_FLAG_CIRCULAR = 1
+};
+
+/* As hyena_plan_create_path, with option flags (0 or HYENA_FLAG_CIRCULAR).
+ * HYENA_ERR_INVALID_ARG for unknown flag bits; HYENA_ERR_UNSUPPORTED for a
+ * circular plan with L < 32 or on the fused path. */
+hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype,
+                                    hyena_path_t path, uint32_t flags);
+
 /* Release a plan and its device tables. NULL is a no-op returning HYENA_OK.
  * The caller must ensure no enqueued work still uses the plan. */
 hyena_status_t hyena_plan_destroy(hyena_plan_t plan);
@@ -101,7 +118,8 @@ hyena_status_t hyena_plan_destroy(hyena_plan_t plan);
 hyena_path_t hyena_plan_path(hyena_plan_t plan);
 
 /* Bytes of the opaque spectrum buffer: (N-1) * D * L complex fp32 values, i.e.
- * 8 * (N-1) * D * L. Returns 0 for a NULL plan. */
+ * 8 * (N-1) * D * L (L/2 complex values per filter for a circular plan).
+ * Returns 0 for a NULL plan. */
 size_t hyena_spectrum_bytes(hyena_plan_t plan);
 
 /* Workspace for a forward over batch B: 0 on the LDS path. On the four-step

@@ -1,0 +1,115 @@
+"""GPU parity of circular plans (HYENA_FLAG_CIRCULAR: circular long convolution of
+L samples, causal short conv) against the circular-mode oracle, on both paths.
+
+Bounds as for the zero-padded forward: relative L2 1e-4 (fp32 I/O), 1e-2 (bf16 I/O).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from fft_long_convolution_libhyena_amd import synth
+from tests._hy import say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fft_long_convolution_libhyena_amd import load_library
+
+    load_library()
+    yield
+
+
+CASES = [
+    # B, D, L, order, dtype, path
+    (2, 3, 32, 2, "f32", "lds"),          # the smallest circular plan (16-point transform)
+    (1, 5, 256, 3, "f32", "lds"),
+    (2, 4, 2048, 2, "bf16", "lds"),
+    (2, 3, 8192, 4, "f32", "lds"),
+    (1, 3, 32768, 2, "f32", "lds"),       # the largest LDS circular plan (16384-point transform)
+    (2, 3, 512, 2, "f32", "fourstep"),    # the smallest four-step circular plan
+    (1, 2, 65536, 3, "f32", "fourstep"),
+    (2, 2, 16384, 2, "bf16", "fourstep"),
+    (1, 2, 1 << 20, 2, "f32", "fourstep"),
+]
+
+
+@pytest.mark.parametrize("B,D,L,order,dtype,path", CASES)
+def test_circular_matches_oracle(B, D, L, order, dtype, path):
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan
+
+    wl = synth.custom(B, D, L, order, dtype, seed=L % 101 + D)
+    x = synth.generate(wl)
+    t = to_device(x)
+    with Plan(L, D, order, dtype, path, circular=True) as p:
+        y = p.forward(t["u"], t["w"], p.spectrum(t["h"]), t["bias"])
+        torch.cuda.synchronize()
+        assert p.path == path
+    ref = oracle.forward_circular(x.u_proj, x.short_w, x.h, x.bias, order, mode="direct" if L <= 256 else "fft")
+    got = y.float().cpu().numpy().astype(np.float64)
+    err = oracle.rel_l2(got, ref)
+    bound = 1e-2 if dtype == "bf16" else 1e-4
+    # the zero-padded result differs: the comparison is not satisfied by accident
+    causal = oracle.forward(x.u_proj, x.short_w, x.h, x.bias, order, mode="direct" if L <= 256 else "fft")
+    gap = oracle.rel_l2(causal, ref)
+    say(f"[circular] {wl.describe()} {path}: rel_l2 {err:.3e} (zero-padded result differs by {gap:.1e})")
+    assert err <= bound
+    assert gap > 10 * bound
+
+
+@pytest.mark.parametrize("L,path", [(64, "lds"), (4096, "lds"), (1024, "fourstep"), (65536, "fourstep")])
+def test_circular_spectrum_matches_numpy_rfft(L, path):
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan
+
+    wl = synth.custom(1, 3, L, 2, seed=L)
+    x = synth.generate(wl)
+    T = L // 2
+    with Plan(L, wl.D, 2, "f32", path, circular=True) as p:
+        spec = p.spectrum(torch.from_numpy(x.h).cuda())
+        torch.cuda.synchronize()
+        assert p.spectrum_bytes() == 8 * wl.D * T
+        s = spec.cpu().numpy().view(np.complex64).reshape(wl.D, T).astype(np.complex128)
+    s *= 4 * T  # stored spectra carry an exact 2^-(log2 T + 2) scale
+    if path == "fourstep":
+        log = T.bit_length() - 1
+        l1 = min(log // 2, 9)
+        L1, L2 = 1 << l1, 1 << (log - l1)
+        s = s.reshape(wl.D, L1, L2).transpose(0, 2, 1).reshape(wl.D, T)
+    want = np.fft.rfft(x.h[0].astype(np.float64), axis=-1)  # L-point, no zero padding: T + 1 bins
+    full = np.empty_like(want)
+    full[:, 1:T] = s[:, 1:T]
+    full[:, 0] = s[:, 0].real
+    full[:, T] = s[:, 0].imag
+    err = np.linalg.norm(full - want) / np.linalg.norm(want)
+    say(f"[circular spectrum] L={L} {path}: rel_l2 {err:.3e}")
+    assert err < 2e-6
+
+
+def test_circular_plan_limits_and_backward():
+    import torch
+
+    from fft_long_convolution_libhyena_amd import HyenaError, Plan
+
+    with pytest.raises(HyenaError) as e:
+        Plan(16, 2, 2, circular=True)  # an 8-point transform is below the smallest
+    assert e.value.status == 2
+    with pytest.raises(HyenaError) as e:
+        Plan(65536, 2, 2, "f32", "lds", circular=True)  # beyond the LDS path
+    assert e.value.status == 2
+    wl = synth.custom(1, 2, 1024, 2, seed=1)
+    x = synth.generate(wl)
+    t = to_device(x)
+    with Plan(1024, 2, 2, circular=True) as p:
+        assert p.backward_workspace_bytes(1) == 0
+        with pytest.raises(HyenaError) as e:
+            p.backward(t["u"], t["w"], p.spectrum(t["h"]), t["bias"], torch.zeros((1, 2, 1024), device="cuda"),
+                       workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+        assert e.value.status == 2
