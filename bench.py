@@ -220,7 +220,7 @@ def bench_backward(args, wl, x, torch, Plan):
     ms = float(np.median(times))
     nbytes = alg_bytes_backward(wl)
     # the step's kernels taken together: k_lds_bwd_rows + k_lds_bwd_finish on the LDS
-    # path, the nine launches of the four-step backward ("fs_backward") otherwise
+    # path, the launches of the four-step backward ("fs_backward") otherwise
     bk = "k_lds_bwd_rows" if plan.path == "lds" else "fs_backward"
     achieved = nbytes / (ms * 1e-3) / 1e9
     out = {
@@ -640,7 +640,7 @@ def main():
     ap.add_argument("--operator", action="store_true",
                     help="time hyena_operator_forward (in_proj GEMM + the path + out_proj GEMM) instead")
     ap.add_argument("--backward", action="store_true",
-                    help="time hyena_backward instead of the forward (order 2 only when L > 16384)")
+                    help="time hyena_backward instead of the forward")
     ap.add_argument("--circular", action="store_true",
                     help="time hyena_forward on a circular plan (circular long convolutions) instead")
     ap.add_argument("--per-sample", action="store_true",
@@ -681,9 +681,6 @@ def main():
         bench_circular(args, wl, x, torch, Plan)
         return
     if args.backward:
-        if wl.L > 16384 and wl.order != 2:
-            print("on the four-step sizes (L > 16384) the backward supports order 2 only", file=sys.stderr)
-            sys.exit(2)
         bench_backward(args, wl, x, torch, Plan)
         return
     dev = torch.device("cuda", 0)

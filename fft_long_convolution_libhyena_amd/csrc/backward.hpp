@@ -51,19 +51,21 @@ struct FsBwdArgs {
     bool bf16;
 };
 
-// Per (b, d) row: the L-point tile T, the gated input's spectrum G and the product
-// spectrum P (complex), the three channels' staging rows S (fp32), the tap sums
-// of every column-block workgroup; per channel d the dh tile. 256-byte aligned.
+// Per (b, d) row: the L-point tile T, the gated input's spectra G_o of the N-1
+// steps and the product spectrum P (complex), the recomputed values v_1..v_{N-2}
+// V (fp32), the N+1 channels' staging rows S (fp32), the tap sums of every
+// column-block workgroup; per channel d the dh tile. 256-byte aligned.
 struct FsBwdWs {
     float2* T;
     float2* G;
     float2* P;
+    float* V;
     float* S;
     float2* Tdh;
     float* part;
     size_t bytes;
 };
-inline FsBwdWs fs_bwd_ws(void* base, int64_t B, int64_t D, int64_t L, int ncb) {
+inline FsBwdWs fs_bwd_ws(void* base, int64_t B, int64_t D, int64_t L, int ncb, int N) {
     size_t off = 0;
     auto take = [&](size_t n) {
         void* r = base ? static_cast<char*>(base) + off : nullptr;
@@ -73,15 +75,16 @@ inline FsBwdWs fs_bwd_ws(void* base, int64_t B, int64_t D, int64_t L, int ncb) {
     const size_t rows = (size_t)(B * D);
     FsBwdWs w;
     w.T = (float2*)take(rows * (size_t)L * 8);
-    w.G = (float2*)take(rows * (size_t)L * 8);
+    w.G = (float2*)take((size_t)(N - 1) * rows * (size_t)L * 8);
     w.P = (float2*)take(rows * (size_t)L * 8);
-    w.S = (float*)take(rows * 3 * (size_t)L * 4);
+    w.V = (float*)take((size_t)(N > 2 ? N - 2 : 0) * rows * (size_t)L * 4);
+    w.S = (float*)take(rows * (size_t)(N + 1) * (size_t)L * 4);
     w.Tdh = (float2*)take((size_t)D * (size_t)L * 8);
-    w.part = (float*)take(rows * (size_t)ncb * 9 * 4);
+    w.part = (float*)take(rows * (size_t)ncb * 3 * (size_t)(N + 1) * 4);
     w.bytes = off;
     return w;
 }
 hipError_t launch_fs_backward(int logL, const FsBwdArgs& a, hipStream_t st);
-size_t fs_bwd_ws_bytes(int logL, int64_t B, int64_t D);
+size_t fs_bwd_ws_bytes(int logL, int64_t B, int64_t D, int N);
 
 }  // namespace hy

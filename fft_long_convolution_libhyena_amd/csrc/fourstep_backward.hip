@@ -1,22 +1,24 @@
-// Backward of the order-2 hot path on the four-step sizes (L = L1 * L2 > 16384 by
-// default), for gfx950. The chain rule is the one of lds_backward.hpp (HyenaDNA
-// walkthrough, section 2.1, HyenaOperator.forward; section 2.2, fftconv): with
-// g = v0 * x1 and v1 = conv(g, h) + bias * g,
-//   dv1 = dy * x0,  dx0 = dy * v1,  dg = corr(dv1, h) + bias * dv1,
-//   dx1 = dg * v0,  dv0 = dg * x1,  dh = sum_b corr(dv1, g),  dbias = dh[0],
-// and the short conv's transpose and tap sums for the three channels.
-// corr is taken through the same zero-padded spectra with conj(H + bias).
+// Backward of the hot path on the four-step sizes (L = L1 * L2 > 16384 by
+// default), for gfx950, any order N. The chain rule is the one of
+// lds_backward.hpp (HyenaDNA walkthrough, section 2.1, HyenaOperator.forward;
+// section 2.2, fftconv): with g_o = v_o * x_{N-1-o} and
+// v_{o+1} = conv(g_o, h_o) + bias_o * g_o,
+//   dv_{N-1} = dy * x_0,  dx_0 = dy * v_{N-1},  and for o = N-2 .. 0:
+//   dg_o = corr(dv_{o+1}, h_o) + bias_o * dv_{o+1},  dh_o = sum_b corr(dv_{o+1}, g_o),
+//   dbias_o = dh_o[0],  dx_{N-1-o} = dg_o * v_o,  dv_o = dg_o * x_{N-1-o},
+// then the short conv's transpose and tap sums for the N+1 channels. corr is taken
+// through the same zero-padded spectra with conj(H + bias).
 //
-// Nine launches over all B*D rows (each row's tile lives in the workspace):
-//  1 pass A of the forward (column FFTs of g)                       -> T
-//  2 pass B, mode 2: rows, spectrum multiply, inverse rows, A_g     -> T, G
-//  3 column pass HEAD: inverse columns = v1; dx0 -> S0; columns of dv1 -> T
-//  4 pass B, mode 3: rows, P = A_dv conj(A_g), conj(H + bias), inverse -> T, P
-//  5 column pass TAIL: inverse columns = dg; dx1 -> S1, dv0 -> S2
-//  6 du = conv3^T of S0, S1, S2 (neighbouring samples are now plain row reads)
-//  7, 8 dh: the batch sum of P per channel, repacked and inverted by rows and
-//       columns; dbias its lag-0 value
-//  9 dshort_w: the sum of the per-workgroup tap sums of passes 3 and 5
+// Launches over all B*D rows (each row's tiles live in the workspace):
+//  pass A of g_0 -> T; for o = 0 .. N-2: pass B mode 2 (rows, multiply, inverse
+//  rows; keeps A_{g_o} in G_o) -> T, then a column pass: MID (v_{o+1} -> V, the
+//  next gated input by columns -> T) or, after the last step, HEAD (dx_0 -> S_0,
+//  dv_{N-1} by columns -> T);
+//  for o = N-2 .. 0: pass B mode 3 (P = A_dv conj(A_{g_o}), conj(H + bias), inverse
+//  rows) -> T, P; dh_o by rows and columns from the fixed-order batch sum of P
+//  (dbias_o its lag-0 value); then TAILMID (dx_{N-1-o} -> S, dv_o by columns -> T)
+//  or, at o = 0, TAIL0 (dx_{N-1} and dv_0 -> S);
+//  du = conv3^T of the N+1 staged channels; dshort_w from the tap sums.
 // Every sum over the batch or over workgroups is taken in a fixed order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,30 +48,42 @@ __device__ __forceinline__ void fs_raw_pairs(const TIO* __restrict__ row, uint32
 
 }  // namespace
 
+// Pass B of step o: MODE 2 keeps the gated input's spectrum in G_o (forward
+// recompute), MODE 3 forms the dh product in P with G_o and applies
+// conj(H_o + bias_o) (the adjoint), both then inverting the rows in T.
 template <int LOG1, int LOG2, int MODE>
 __global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::ROW_THREADS))
 k_fs_row_bwd(float2* __restrict__ T, const float2* __restrict__ spec, const float* __restrict__ bias,
-             float2* __restrict__ G, float2* __restrict__ P, FsTables tb, int D, int64_t nrows) {
+             float2* __restrict__ G, float2* __restrict__ P, FsTables tb, int D, int o, int64_t nrows) {
     using Cfg = FsCfg<LOG1, LOG2>;
     __shared__ float2 lds[2 * Cfg::UNITS * Cfg::RP];
     int64_t r;
     int ug;
     if (!xcd_row_map(blockIdx.x, nrows, Cfg::L1 / 2 / Cfg::UNITS, r, ug)) return;
     const int64_t L = (int64_t)Cfg::L1 * Cfg::L2;
-    fs_row_body<LOG1, LOG2, MODE>(lds, T + r * L, spec, bias, tb, D, 0, r, ug, G + r * L,
+    fs_row_body<LOG1, LOG2, MODE>(lds, T + r * L, spec, bias, tb, D, o, r, ug, G + ((int64_t)o * nrows + r) * L,
                                   P ? P + r * L : nullptr);
 }
 
-// Column pass of the backward. HEAD: the inverse columns give v1; with dy and x0,
-// dx0 = dy*v1 goes to S0 and dv1 = dy*x0 is transformed by columns back into the
-// tile. TAIL: the inverse columns give dg; with x1 and v0, dx1 = dg*v0 goes to S1
-// and dv0 = dg*x1 to S2. Both add the finished channels' tap sums into
+// Column passes of the backward (inverse columns of the tile first, then):
+//  MID (forward recompute after step o < N-2): v_{o+1} is stored in V_{o+1};
+//      g_{o+1} = v_{o+1} * x_{N-2-o} is transformed by columns back into the tile.
+//  HEAD (after the last step): with dy and x_0, dx_0 = dy * v_{N-1} goes to S_0 and
+//      dv_{N-1} = dy * x_0 is transformed by columns back into the tile.
+//  TAILMID (step o >= 1 of the adjoint): the columns give dg_o; with a = N-1-o,
+//      dx_a = dg_o * v_o (v_o from V_o) goes to S_a and dv_o = dg_o * x_a is
+//      transformed by columns back into the tile.
+//  TAIL0 (step 0): dx_{N-1} = dg_0 * v_0 goes to S_{N-1} and dv_0 = dg_0 * x_{N-1}
+//      to S_N (v_0 and x_{N-1} by the short conv of their raw rows).
+// Every pass that finishes a channel adds its tap sums into
 // part[row][column block][channel][tap].
-template <int LOG1, int LOG2, class TIO, bool HEAD>
+constexpr int kColMid = 0, kColHead = 1, kColTailMid = 2, kColTail0 = 3;
+
+template <int LOG1, int LOG2, class TIO, int KIND>
 __global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::COL_THREADS))
 k_fs_colinv_bwd(float2* __restrict__ T, const TIO* __restrict__ u, const float* __restrict__ w3,
-                const TIO* __restrict__ dy, float* __restrict__ S, float* __restrict__ part, FsTables tb, int D,
-                int64_t nrows) {
+                const TIO* __restrict__ dy, float* __restrict__ S, float* __restrict__ V, float* __restrict__ part,
+                FsTables tb, int D, int N, int o, int64_t nrows) {
     using Cfg = FsCfg<LOG1, LOG2>;
     constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T1 = Cfg::T1, CB = Cfg::CB, NCB = L2 / CB;
     constexpr int NT = Cfg::COL_THREADS;
@@ -79,7 +93,7 @@ k_fs_colinv_bwd(float2* __restrict__ T, const TIO* __restrict__ u, const float* 
     int cb;
     if (!xcd_row_map(blockIdx.x, nrows, NCB, r, cb)) return;
     const uint32_t b = (uint32_t)r / (uint32_t)D, d = (uint32_t)r - b * (uint32_t)D;
-    const int64_t C = 3 * (int64_t)D;
+    const int64_t C = (int64_t)(N + 1) * D;
     const int c = threadIdx.x % CB, t = threadIdx.x / CB;
     const int m2 = cb * CB + c;
     const ColAcc<Cfg::CP> cacc{lds + c};
@@ -89,50 +103,86 @@ k_fs_colinv_bwd(float2* __restrict__ T, const TIO* __restrict__ u, const float* 
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = cmulc(slot[(uint32_t)(t + T1 * e) * L2 + m2], twiddle_step<L2>(tb, base, e, m2));
     fft_strided<L1, true, false>(v, t, tb.tw1, cacc);
-    float* Sr = S + r * 3 * L;  // staging rows of channels 0, 1, 2 (time domain, fp32)
+    float* Sr = S + r * (N + 1) * L;  // staging rows of the N+1 channels (time domain, fp32)
+    auto chan = [&](int i) { return u + ((int64_t)b * C + (int64_t)i * D + d) * L; };
+    auto taps = [&](int i) { return w3 + 3 * ((int64_t)i * D + d); };
     float s0[3] = {0.f, 0.f, 0.f}, s1[3] = {0.f, 0.f, 0.f};
-    if constexpr (HEAD) {
+    int ch0 = 0;  // channel of s0 (s1 is channel N, TAIL0 only)
+    bool refill = true;
+    if constexpr (KIND == kColMid) {
+        const int a = N - 2 - o;
+        const TIO* xr = chan(a);
+        const float* wx = taps(a);
+        float* Vr = V + ((int64_t)o * nrows + r) * L;  // V_{o+1} at slot o
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
+            store_pair(Vr, m, v[e]);
+            v[e] = emul(v[e], conv3_pair(xr, m, wx[0], wx[1], wx[2]));
+        }
+    } else if constexpr (KIND == kColHead) {
         const TIO* dyr = dy + r * L;
-        const TIO* x0r = u + ((int64_t)b * C + d) * L;
-        const float* wx = w3 + 3 * (int64_t)d;
+        const TIO* x0r = chan(0);
+        const float* wx = taps(0);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
             const float2 g = load_pair(dyr, m);
             float2 prev, cur;
             fs_raw_pairs(x0r, m, prev, cur);
-            const float2 dx = emul(g, v[e]);  // dy * v1
+            const float2 dx = emul(g, v[e]);  // dy * v_{N-1}
             store_pair(Sr, m, dx);
             fs_tap_sums(dx, prev, cur, s0);
-            v[e] = emul(g, conv3_from(prev, cur, wx[0], wx[1], wx[2]));  // dv1 = dy * x0
+            v[e] = emul(g, conv3_from(prev, cur, wx[0], wx[1], wx[2]));  // dv_{N-1} = dy * x_0
         }
+    } else if constexpr (KIND == kColTailMid) {
+        const int a = N - 1 - o;
+        ch0 = a;
+        const TIO* xr = chan(a);
+        const float* wx = taps(a);
+        const float* Vr = V + ((int64_t)(o - 1) * nrows + r) * L;  // v_o
 #pragma unroll
-        for (int e = 8; e < 16; ++e) v[e] = make_float2(0.f, 0.f);
-        fft_strided<L1, false, true>(v, t, tb.tw1, cacc);
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            slot[(uint32_t)(t + T1 * e) * L2 + m2] = cmul(v[e], twiddle_step<L2>(tb, base, e, m2));
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
+            float2 xp, xc;
+            fs_raw_pairs(xr, m, xp, xc);
+            const float2 dx = emul(v[e], load_pair(Vr, m));  // dg_o * v_o
+            store_pair(Sr + (int64_t)a * L, m, dx);
+            fs_tap_sums(dx, xp, xc, s0);
+            v[e] = emul(v[e], conv3_from(xp, xc, wx[0], wx[1], wx[2]));  // dv_o = dg_o * x_a
+        }
     } else {
-        const TIO* x1r = u + ((int64_t)b * C + D + d) * L;
-        const TIO* vr = u + ((int64_t)b * C + 2 * D + d) * L;
-        const float* wx = w3 + 3 * ((int64_t)D + d);
-        const float* wv = w3 + 3 * ((int64_t)2 * D + d);
+        refill = false;
+        ch0 = N - 1;
+        const TIO* x1r = chan(N - 1);
+        const TIO* vr = chan(N);
+        const float* wx = taps(N - 1);
+        const float* wv = taps(N);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t m = (uint32_t)(t + T1 * e) * L2 + m2;
             float2 xp, xc, vp, vc;
             fs_raw_pairs(x1r, m, xp, xc);
             fs_raw_pairs(vr, m, vp, vc);
-            const float2 dx1 = emul(v[e], conv3_from(vp, vc, wv[0], wv[1], wv[2]));  // dg * v0
-            const float2 dv0 = emul(v[e], conv3_from(xp, xc, wx[0], wx[1], wx[2]));  // dg * x1
-            store_pair(Sr + L, m, dx1);
-            store_pair(Sr + 2 * L, m, dv0);
+            const float2 dx1 = emul(v[e], conv3_from(vp, vc, wv[0], wv[1], wv[2]));  // dg_0 * v_0
+            const float2 dv0 = emul(v[e], conv3_from(xp, xc, wx[0], wx[1], wx[2]));  // dg_0 * x_{N-1}
+            store_pair(Sr + (int64_t)(N - 1) * L, m, dx1);
+            store_pair(Sr + (int64_t)N * L, m, dv0);
             fs_tap_sums(dx1, xp, xc, s0);
             fs_tap_sums(dv0, vp, vc, s1);
         }
     }
+    if (refill) {  // (uniform) the next transform's input goes back into the tile
+#pragma unroll
+        for (int e = 8; e < 16; ++e) v[e] = make_float2(0.f, 0.f);
+        fft_strided<L1, false, true>(v, t, tb.tw1, cacc);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            slot[(uint32_t)(t + T1 * e) * L2 + m2] = cmul(v[e], twiddle_step<L2>(tb, base, e, m2));
+    }
+    if constexpr (KIND == kColMid) return;
     // this workgroup's tap sums
-    constexpr int NQ = HEAD ? 3 : 6;
+    constexpr int NQ = KIND == kColTail0 ? 6 : 3;
     static_assert(NQ * NT * 4 <= L1 * Cfg::CP * 8, "reduction buffer fits in the column tile's LDS");
     float* red = reinterpret_cast<float*>(lds);
     const int tid = threadIdx.x;
@@ -140,33 +190,35 @@ k_fs_colinv_bwd(float2* __restrict__ T, const TIO* __restrict__ u, const float* 
 #pragma unroll
     for (int q = 0; q < 3; ++q) {
         red[q * NT + tid] = s0[q];
-        if constexpr (!HEAD) red[(3 + q) * NT + tid] = s1[q];
+        if constexpr (KIND == kColTail0) red[(3 + q) * NT + tid] = s1[q];
     }
     __syncthreads();
     if (tid < NQ) {
         float sum = 0.f;
         for (int k = 0; k < NT; ++k) sum += red[tid * NT + k];
-        // channel 0 taps at 0..2 (HEAD); channels 1 and 2 at 3..8 (TAIL)
-        part[(r * NCB + cb) * 9 + (HEAD ? 0 : 3) + tid] = sum;
+        // taps of channel ch0 at 3*ch0 + 0..2; TAIL0 also channel N right after (N = ch0 + 1)
+        part[(r * NCB + cb) * 3 * (N + 1) + 3 * ch0 + tid] = sum;
     }
 }
 
-// du[b][i*D + d][t] = w2 S_i[t] + w1 S_i[t+1] + w0 S_i[t+2], one thread per pair.
+// du[b][i*D + d][t] = w2 S_i[t] + w1 S_i[t+1] + w0 S_i[t+2] for the N+1 channels,
+// one thread per pair.
 template <class TIO>
 __global__ void k_fs_bwd_du(const float* __restrict__ S, const float* __restrict__ w3, TIO* __restrict__ du,
-                            int D, int64_t L, int64_t rows) {
+                            int D, int N, int64_t L, int64_t rows) {
     const int64_t pairs = L / 2;
     const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (m >= pairs) return;
-    for (int64_t ri = blockIdx.y; ri < rows * 3; ri += gridDim.y) {
-        const int64_t r = ri / 3;
-        const int i = (int)(ri - r * 3);
+    const int nc = N + 1;
+    for (int64_t ri = blockIdx.y; ri < rows * nc; ri += gridDim.y) {
+        const int64_t r = ri / nc;
+        const int i = (int)(ri - r * nc);
         const int64_t b = r / D, d = r - b * D;
         const float* s = S + ri * L;
         const float2 dc = make_float2(s[2 * m], s[2 * m + 1]);
         const float2 nx = 2 * m + 2 < L ? make_float2(s[2 * m + 2], s[2 * m + 3]) : make_float2(0.f, 0.f);
         const float* w = w3 + 3 * ((int64_t)i * D + d);
-        store_pair(du + (b * 3 * D + (int64_t)i * D + d) * L, (uint32_t)m,
+        store_pair(du + (b * nc * D + (int64_t)i * D + d) * L, (uint32_t)m,
                    make_float2(fmaf(w[2], dc.x, fmaf(w[1], dc.y, w[0] * nx.x)),
                                fmaf(w[2], dc.y, fmaf(w[1], nx.x, w[0] * nx.y))));
     }
@@ -252,14 +304,15 @@ k_fs_dh_col(const float2* __restrict__ Tdh, float* __restrict__ dh, float* __res
     if (t == 0 && m2 == 0) dbias[dd] = v[0].x;
 }
 
-// dshort_w[i*D + d][j] = sum over b and column blocks of the tap sums.
-__global__ void k_fs_bwd_dw(const float* __restrict__ part, float* __restrict__ dw, int B, int D, int ncb) {
+// dshort_w[i*D + d][j] = sum over b and column blocks of the tap sums (fixed order).
+__global__ void k_fs_bwd_dw(const float* __restrict__ part, float* __restrict__ dw, int B, int D, int N, int ncb) {
     const int d = blockIdx.x, q = threadIdx.x;  // q = 3*channel + tap
-    if (q >= 9) return;
+    const int nq = 3 * (N + 1);
+    if (q >= nq) return;
     float s = 0.f;
     for (int b = 0; b < B; ++b) {
-        const float* pr = part + ((int64_t)b * D + d) * ncb * 9;
-        for (int k = 0; k < ncb; ++k) s += pr[k * 9 + q];
+        const float* pr = part + ((int64_t)b * D + d) * ncb * nq;
+        for (int k = 0; k < ncb; ++k) s += pr[k * nq + q];
     }
     dw[((int64_t)(q / 3) * D + d) * 3 + (q % 3)] = s;
 }
@@ -268,31 +321,50 @@ template <int LOG1, int LOG2, class TIO>
 static void fs_backward_launch(const FsBwdArgs& a, hipStream_t st) {
     using Cfg = FsCfg<LOG1, LOG2>;
     constexpr int NCB = Cfg::L2 / Cfg::CB;
+    const int N = a.N;
     const int64_t L = (int64_t)Cfg::L1 * Cfg::L2, rows = (int64_t)a.B * a.D;
-    const FsBwdWs w = fs_bwd_ws(a.ws, a.B, a.D, L, NCB);
+    const FsBwdWs w = fs_bwd_ws(a.ws, a.B, a.D, L, NCB, N);
     const unsigned gcol = (unsigned)xcd_grid(rows, NCB);
     const unsigned grow = (unsigned)xcd_grid(rows, Cfg::L1 / 2 / Cfg::UNITS);
     const dim3 bcol(Cfg::COL_THREADS), brow(Cfg::ROW_THREADS);
     const TIO* u = (const TIO*)a.u;
+    const TIO* dy = (const TIO*)a.dy;
+    // forward recompute: pass A of g_0, then per step pass B (keeping G_o) and a
+    // column pass (MID: store v_{o+1}, next input; HEAD after the last step)
     hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, TIO, 0>), dim3(gcol), bcol, 0, st, u, a.w3, (const float*)nullptr,
-                       w.T, a.tb, a.D, 2, (int64_t)0, rows);
-    hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 2>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G,
-                       (float2*)nullptr, a.tb, a.D, rows);
-    hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, true>), dim3(gcol), bcol, 0, st, w.T, u, a.w3,
-                       (const TIO*)a.dy, w.S, w.part, a.tb, a.D, rows);
-    hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 3>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G, w.P, a.tb,
-                       a.D, rows);
-    hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, false>), dim3(gcol), bcol, 0, st, w.T, u, a.w3,
-                       (const TIO*)a.dy, w.S, w.part, a.tb, a.D, rows);
+                       w.T, a.tb, a.D, N, (int64_t)0, rows);
+    for (int o = 0; o < N - 1; ++o) {
+        hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 2>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G,
+                           (float2*)nullptr, a.tb, a.D, o, rows);
+        if (o < N - 2)
+            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColMid>), dim3(gcol), bcol, 0, st, w.T, u, a.w3,
+                               dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
+        else
+            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColHead>), dim3(gcol), bcol, 0, st, w.T, u,
+                               a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
+    }
+    // the adjoint, last step first: pass B (dh product, conj(H + bias)), dh of the
+    // step, then the column pass that finishes the step's gate channel
+    for (int o = N - 2; o >= 0; --o) {
+        hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 3>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G, w.P,
+                           a.tb, a.D, o, rows);
+        hipLaunchKernelGGL((k_fs_dh_row<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, Cfg::L1 / 2 / Cfg::UNITS)), brow,
+                           0, st, (const float2*)w.P, w.Tdh, a.tb, a.B, a.D);
+        hipLaunchKernelGGL((k_fs_dh_col<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, NCB)), bcol, 0, st,
+                           (const float2*)w.Tdh, a.dh + (int64_t)o * a.D * L, a.dbias + (int64_t)o * a.D, a.tb, a.D);
+        if (o > 0)
+            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColTailMid>), dim3(gcol), bcol, 0, st, w.T, u,
+                               a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
+        else
+            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColTail0>), dim3(gcol), bcol, 0, st, w.T, u,
+                               a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
+    }
     const int64_t pairs = L / 2;
-    const unsigned gy = (unsigned)(rows * 3 < 65535 ? rows * 3 : 65535);
+    const int64_t nrc = rows * (N + 1);
+    const unsigned gy = (unsigned)(nrc < 65535 ? nrc : 65535);
     hipLaunchKernelGGL((k_fs_bwd_du<TIO>), dim3((unsigned)((pairs + 255) / 256), gy), dim3(256), 0, st,
-                       (const float*)w.S, a.w3, (TIO*)a.du, a.D, L, rows);
-    hipLaunchKernelGGL((k_fs_dh_row<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, Cfg::L1 / 2 / Cfg::UNITS)), brow, 0,
-                       st, (const float2*)w.P, w.Tdh, a.tb, a.B, a.D);
-    hipLaunchKernelGGL((k_fs_dh_col<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, NCB)), bcol, 0, st,
-                       (const float2*)w.Tdh, a.dh, a.dbias, a.tb, a.D);
-    hipLaunchKernelGGL(k_fs_bwd_dw, dim3((unsigned)a.D), dim3(64), 0, st, (const float*)w.part, a.dw, a.B, a.D,
+                       (const float*)w.S, a.w3, (TIO*)a.du, a.D, N, L, rows);
+    hipLaunchKernelGGL(k_fs_bwd_dw, dim3((unsigned)a.D), dim3(64), 0, st, (const float*)w.part, a.dw, a.B, a.D, N,
                        NCB);
 }
 
@@ -304,7 +376,7 @@ static hipError_t fs_backward_t(const FsBwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_fs_backward(int logL, const FsBwdArgs& a, hipStream_t st) {
-    if (a.N != 2) return hipErrorInvalidValue;
+    if (a.N < 2 || a.N > 8) return hipErrorInvalidValue;
     switch (logL) {
 #define X(LG, A, B) \
     case LG: return fs_backward_t<A, B>(a, st);
@@ -314,12 +386,12 @@ hipError_t launch_fs_backward(int logL, const FsBwdArgs& a, hipStream_t st) {
     }
 }
 
-size_t fs_bwd_ws_bytes(int logL, int64_t B, int64_t D) {
+size_t fs_bwd_ws_bytes(int logL, int64_t B, int64_t D, int N) {
     int l1 = 0, l2 = 0;
     fs_split(logL, &l1, &l2);
     const int64_t L = int64_t(1) << logL;
     const int ncb = (1 << l2) / HY_FS_CB;
-    return fs_bwd_ws(nullptr, B, D, L, ncb).bytes;
+    return fs_bwd_ws(nullptr, B, D, L, ncb, N).bytes;
 }
 
 }  // namespace hy

@@ -12,7 +12,7 @@ extern "C" {
 size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B) {
     if (!plan || B < 1 || plan->circular) return 0;
     if (plan->path == HYENA_PATH_LDS) return hy::bwd_ws_bytes(B, plan->D, plan->L, plan->order);
-    if (plan->path == HYENA_PATH_FOURSTEP && plan->order == 2) return hy::fs_bwd_ws_bytes(plan->logL, B, plan->D);
+    if (plan->path == HYENA_PATH_FOURSTEP) return hy::fs_bwd_ws_bytes(plan->logT, B, plan->D, plan->order);
     return 0;
 }
 
@@ -27,7 +27,7 @@ hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, 
         return HYENA_ERR_INVALID_ARG;
     if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 26)) return HYENA_ERR_INVALID_ARG;
     const bool fs = plan->path == HYENA_PATH_FOURSTEP;
-    if (plan->circular || !(plan->path == HYENA_PATH_LDS || (fs && plan->order == 2))) return HYENA_ERR_UNSUPPORTED;
+    if (plan->circular || !(plan->path == HYENA_PATH_LDS || fs)) return HYENA_ERR_UNSUPPORTED;
     if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
     if (!workspace || !aligned16(workspace) || workspace_bytes < hyena_backward_workspace_bytes(plan, B))
         return HYENA_ERR_WORKSPACE;
@@ -35,7 +35,7 @@ hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, 
     if (fs) {
         hy::FsBwdArgs a{u_proj, short_w, (const float2*)spec, bias, dy, du_proj, dshort_w, dh, dbias, workspace,
                         plan->fs, (int)B, (int)plan->D, plan->order, plan->dtype == HYENA_BF16};
-        return hy::launch_fs_backward(plan->logL, a, stream) == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
+        return hy::launch_fs_backward(plan->logT, a, stream) == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
     }
     hy::LdsBwdArgs a{u_proj,   short_w,   (const float2*)spec, bias,      dy,         du_proj,
                      dshort_w, dh,        dbias,               (float2*)workspace, plan->tw, plan->wpair,

@@ -207,12 +207,11 @@ hyena_status_t hyena_fused_check(hyena_plan_t plan, const void* workspace, int* 
  * taken from, the gated-input spectra of steps 0..N-3 and the values v_1..v_{N-2}
  * (8 bytes per complex or pair value), then 3 floats of short-conv tap sums per
  * (b, channel): 8*B*D*((2N-3)*L + (N-2)*L/2) + 12*B*(N+1)*D.
- * Four-step path (order 2 only): per (b, d) row three L-point complex tiles (the
- * transform, the gated input's spectrum, the product spectrum) and three fp32
- * staging rows, per channel one complex dh tile, and 36 bytes of tap sums per
- * (row, column block), each region 256-byte aligned.
- * Returns 0 for a NULL plan, B < 1, or a plan without a backward (four-step with
- * order > 2). */
+ * Four-step path: per (b, d) row N+1 L-point complex tiles (the transform, the
+ * N-1 gated inputs' spectra, the product spectrum), N-2 fp32 rows of recomputed
+ * values and N+1 fp32 staging rows; per channel one complex dh tile; and
+ * 12*(N+1) bytes of tap sums per (row, column block); each region 256-byte
+ * aligned. Returns 0 for a NULL plan, B < 1, or a circular plan. */
 size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* Backward of the forward hot path: given the upstream gradient dy of y, the
@@ -233,8 +232,8 @@ size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B);
  *           buffers' previous contents)
  *   workspace / workspace_bytes: device scratch of at least
  *           hyena_backward_workspace_bytes(plan, B); contents on entry irrelevant.
- * Both paths have a backward: the LDS path for every order, the four-step path
- * for order 2 (other orders get HYENA_ERR_UNSUPPORTED). Every sum over the batch
+ * Both paths have a backward for every order; circular plans have none
+ * (HYENA_ERR_UNSUPPORTED). Every sum over the batch
  * or over workgroups is taken in a fixed order (no atomics), so results are
  * bitwise reproducible.
  * Enqueued on `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL or misaligned
