@@ -206,6 +206,45 @@ def forward_circular(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bia
     return v * x[0]
 
 
+def conv2d_forward(v: np.ndarray, k: np.ndarray, bias: np.ndarray, g: Optional[np.ndarray] = None,
+                   x: Optional[np.ndarray] = None, mode: str = "fft") -> np.ndarray:
+    """One gated 2-D long-convolution step in fp64 (HyenaND summary, methodology:
+    global convolution on the native N-d grid, evaluated by N-d FFT, the input
+    zero-padded to double the grid in every dimension for the non-circular mode).
+    v, g, x [B, D, H, W]; k [D, 2H, 2W], the kernel on the doubled grid (row i >= H
+    and column j >= W hold the offsets i - 2H, j - 2W, so causal and centred kernels
+    are both expressible); bias [D]. With s = v * g (s = v when g is None):
+      c[p, q] = sum_{i < 2H, j < 2W} k[i, j] s_pad[(p - i) mod 2H, (q - j) mod 2W],
+    p < H, q < W, s_pad being s zero-padded to 2H x 2W; y = (c + bias * s) * x (no
+    factor when x is None). ``direct`` is that sum written out; ``fft`` multiplies
+    numpy's rfft2 of the padded input and of the kernel and inverts.
+    Returns [B, D, H, W] float64."""
+    s = np.asarray(v, dtype=np.float64)
+    if g is not None:
+        s = s * np.asarray(g, dtype=np.float64)
+    B, D, H, W = s.shape
+    kk = np.asarray(k, dtype=np.float64)
+    if kk.shape != (D, 2 * H, 2 * W):
+        raise ValueError("k must be [D, 2H, 2W]")
+    if mode == "direct":
+        sp = np.zeros((B, D, 2 * H, 2 * W))
+        sp[:, :, :H, :W] = s
+        c = np.zeros((B, D, H, W))
+        for i in range(2 * H):
+            for j in range(2 * W):
+                # shifted copy: entry (p, q) holds s_pad[(p - i) mod 2H, (q - j) mod 2W]
+                sh = np.roll(np.roll(sp, i, axis=2), j, axis=3)[:, :, :H, :W]
+                c += kk[None, :, i, j, None, None] * sh
+    else:
+        S = np.fft.rfft2(s, s=(2 * H, 2 * W))
+        Kh = np.fft.rfft2(kk)
+        c = np.fft.irfft2(S * Kh[None], s=(2 * H, 2 * W))[:, :, :H, :W]
+    y = c + np.asarray(bias, dtype=np.float64)[None, :, None, None] * s
+    if x is not None:
+        y = y * np.asarray(x, dtype=np.float64)
+    return y
+
+
 def forward_per_sample(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray, order: int,
                        mode: str = "fft", threads: int = 0) -> np.ndarray:
     """The hot path with a filter set per sample (input-dependent long convolutions,
