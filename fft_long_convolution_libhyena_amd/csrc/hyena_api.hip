@@ -12,13 +12,15 @@
 #include "fft_core.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
+#include "tables.hpp"
 
 using hy::aligned16;
+using hy::append_stockham;
 using hy::check_device;
+using hy::wfwd;
 
 namespace {
 
-constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr int64_t kMaxLog = 20;
 constexpr size_t kChunkTargetBytes = 128u << 20;  // in-flight four-step intermediates per launch
 constexpr int64_t kMaxChunkRows = 65536;
@@ -40,29 +42,6 @@ int ilog2_64(int64_t x) {
     int l = 0;
     while ((int64_t(1) << l) < x) ++l;
     return l;
-}
-
-// exp(-2 pi i num / den) computed in fp64 after an exact integer reduction.
-float2 wfwd(int64_t num, int64_t den) {
-    int64_t r = num % den;
-    if (r < 0) r += den;
-    const double a = -kTwoPi * (double)r / (double)den;
-    return make_float2((float)cos(a), (float)sin(a));
-}
-
-// Stockham per-pass tables for a length-n transform, in the order the device
-// schedule reads them: pass p (radix R, NS = 16^p) holds W_{NS*R}^{r*k} at
-// [(r-1)*NS + k], r = 1..R-1, k = 0..NS-1.
-void append_stockham(std::vector<float2>& out, int logn) {
-    const int full = logn / 4, rem = logn % 4;
-    const int npass = full + (rem ? 1 : 0);
-    int64_t ns = 1;
-    for (int p = 0; p < npass; ++p) {
-        const int R = p < full ? 16 : (1 << rem);
-        for (int r = 1; r < R; ++r)
-            for (int64_t k = 0; k < ns; ++k) out.push_back(wfwd((int64_t)r * k, ns * R));
-        ns *= R;
-    }
 }
 
 size_t stockham_size(int logn) {

@@ -244,6 +244,48 @@ def filter_mlp(wl: Workload, emb_dim: int = 3, width: int = 16, num_inner: int =
     return FilterMLP(*[np.ascontiguousarray(a, dtype=np.float32) for a in arrs])
 
 
+@dataclasses.dataclass
+class Conv2dInputs:
+    """Inputs of one gated 2-D long-convolution step (all fp32; bf16 values for bf16)."""
+    v: np.ndarray     # [B, D, H, W]
+    g: np.ndarray     # [B, D, H, W] pre-gate
+    x: np.ndarray     # [B, D, H, W] post-gate
+    k: np.ndarray     # [D, 2H, 2W] kernel on the doubled grid
+    bias: np.ndarray  # [D]
+
+
+def conv2d_inputs(B: int, D: int, H: int, W: int, dtype: str = "f32", seed: int = 0,
+                  centred: bool = True) -> Conv2dInputs:
+    """Seeded inputs for the 2-D step: v, g, x ~ N(0, 1); a kernel k[d][i][j] =
+    N(0, 1) * exp(-alpha_d * r / max(H, W)) with r the length of the offset the
+    doubled-grid position stands for (negative offsets in the upper rows and
+    columns when ``centred``; otherwise zero outside [0, H) x [0, W), a causal
+    kernel), alpha_d log-spaced over [0.3, 30]; bias ~ N(0, 1). Drawn from one
+    PCG64 stream; the activations are rounded to bf16 for bf16 (those values feed
+    both sides)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 5000))
+    v = rng.standard_normal((B, D, H, W), dtype=np.float32)
+    g = rng.standard_normal((B, D, H, W), dtype=np.float32)
+    x = rng.standard_normal((B, D, H, W), dtype=np.float32)
+    noise = rng.standard_normal((D, 2 * H, 2 * W), dtype=np.float32)
+    bias = rng.standard_normal(D, dtype=np.float32)
+    di = np.arange(2 * H)
+    dj = np.arange(2 * W)
+    if centred:
+        di = np.where(di < H, di, di - 2 * H)
+        dj = np.where(dj < W, dj, dj - 2 * W)
+    r = np.sqrt(di[:, None].astype(np.float64) ** 2 + dj[None, :].astype(np.float64) ** 2) / max(H, W)
+    alpha = _alphas(D, 0.3, 30.0)
+    k = noise * np.exp(-alpha[:, None, None] * r[None]).astype(np.float32)
+    if not centred:
+        k[:, H:, :] = 0.0
+        k[:, :, W:] = 0.0
+    arrs = [v, g, x]
+    if dtype == "bf16":
+        arrs = [round_to_bf16(a) for a in arrs]
+    return Conv2dInputs(*[np.ascontiguousarray(a, dtype=np.float32) for a in arrs + [k, bias]])
+
+
 def channel_subset(x: Inputs, ds) -> Inputs:
     """The inputs restricted to channels ds of every channel group (gates, value,
     filters, biases): the hot path treats channels independently, so a subset is a

@@ -327,6 +327,62 @@ typedef struct hyena_filter_mlp_s {
 hyena_status_t hyena_implicit_filter(hyena_plan_t plan, const hyena_filter_mlp_t* mlp, float* h,
                                      hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * 2-D long convolution (HyenaND summary, methodology: global convolution on the
+ * native N-d grid by an N-d FFT; the non-circular mode zero-pads the input to
+ * double the grid in every dimension). One gated step per (b, d) image, as one
+ * step of the 1-D recurrence above:
+ *   s = v * g            (g optional: s = v when NULL)
+ *   c[p][q] = sum_{i < 2H, j < 2W} k[i][j] s_pad[(p - i) mod 2H][(q - j) mod 2W]
+ *   y = (c + bias * s) * x   (x optional),     p < H, q < W,
+ * where s_pad is s zero-padded to 2H x 2W and the kernel k is given on the
+ * doubled grid: rows i >= H and columns j >= W hold the negative offsets i - 2H
+ * and j - 2W, so a causal kernel (zero outside [0,H) x [0,W)) and a centred one
+ * are both expressible. (How the HyenaND operator synthesises its kernels and
+ * what short convolution it applies on a grid are not on the pages; this is the
+ * convolution step on its own.)
+ * ------------------------------------------------------------------------ */
+typedef struct hyena_plan2d_s* hyena_plan2d_t; /* opaque */
+
+/* Plan for H x W images (powers of two, 16 <= H <= 512, 32 <= W <= 512) of D
+ * channels; dtype of v, g, x and y as for the 1-D plans. The plan owns its
+ * twiddle tables on the current device. Errors as hyena_plan_create. */
+hyena_status_t hyena_plan2d_create(hyena_plan2d_t* out, int64_t H, int64_t W, int64_t D, hyena_dtype_t dtype);
+
+/* Release a 2-D plan. NULL is a no-op. */
+hyena_status_t hyena_plan2d_destroy(hyena_plan2d_t plan);
+
+/* Bytes of a 2-D kernel spectrum: D * 2H * (W + 1) complex fp32 values, the
+ * doubled grid's real-transform bins (numpy.fft.rfft2 layout) of each channel,
+ * scaled by 1/(4 * 2H * W). Returns 0 for a NULL plan. */
+size_t hyena_spectrum2d_bytes(hyena_plan2d_t plan);
+
+/* Workspace for hyena_conv2d_forward over batch B: any size of at least one
+ * image tile (8 * H * W bytes) is accepted; this is the recommended size (up to
+ * 128 MiB of tiles per launch). Returns 0 for a NULL plan or B < 1. */
+size_t hyena_workspace2d_bytes(hyena_plan2d_t plan, int64_t B);
+
+/* Kernel spectra, once per plan.
+ *   k    [D][2H][2W] fp32, device: the kernels on the doubled grid
+ *   spec device buffer of hyena_spectrum2d_bytes(plan) bytes (output)
+ * Enqueued on `stream`. HYENA_ERR_INVALID_ARG for NULL or misaligned pointers,
+ * HYENA_ERR_DEVICE for launch failures or a wrong current device. */
+hyena_status_t hyena_filter_spectrum2d(hyena_plan2d_t plan, const float* k, void* spec, hipStream_t stream);
+
+/* The gated 2-D long convolution above for B x D images.
+ *   v    [B][D][H][W] of the plan dtype, device
+ *   g, x [B][D][H][W] of the plan dtype, device, or NULL (no gate)
+ *   spec from hyena_filter_spectrum2d of this plan; bias [D] fp32, device
+ *   y    [B][D][H][W] of the plan dtype, device (output; must not alias inputs)
+ *   workspace / workspace_bytes: at least 8*H*W bytes (see hyena_workspace2d_bytes)
+ * Three passes per chunk of images: column FFTs of the gated image, row FFTs with
+ * the spectrum multiply and the inverse rows, inverse columns with the gate; all
+ * intermediates fp32. Enqueued on `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL or
+ * misaligned pointers, B < 1, B*D > 2^24), HYENA_ERR_WORKSPACE, HYENA_ERR_DEVICE. */
+hyena_status_t hyena_conv2d_forward(hyena_plan2d_t plan, int64_t B, const void* v, const void* g, const void* x,
+                                    const void* spec, const float* bias, void* y, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* hyena_status_string(hyena_status_t s);
 

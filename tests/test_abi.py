@@ -26,7 +26,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(hyena_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(hyena_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_binding_exports():
@@ -109,6 +109,22 @@ def test_implicit_filter_rejects_null_arguments(lib):
     st = FilterMLPStruct(3, 16, 0, 16, 16, 16, None, None, 16, 16, 16)
     assert lib.hyena_implicit_filter(None, ctypes.byref(st), 16, None) == 1
     assert lib.hyena_implicit_filter(None, None, 16, None) == 1
+
+
+def test_conv2d_entry_points_reject_bad_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.hyena_plan2d_create(None, 64, 64, 4, 0) == 1
+    assert lib.hyena_plan2d_create(ctypes.byref(h), 0, 64, 4, 0) == 1
+    assert lib.hyena_plan2d_create(ctypes.byref(h), 64, 64, 4, 5) == 1     # bad dtype
+    assert lib.hyena_plan2d_create(ctypes.byref(h), 48, 64, 4, 0) == 2     # H not a power of two
+    assert lib.hyena_plan2d_create(ctypes.byref(h), 8, 64, 4, 0) == 2      # H below 16
+    assert lib.hyena_plan2d_create(ctypes.byref(h), 64, 16, 4, 0) == 2     # W below 32
+    assert lib.hyena_plan2d_create(ctypes.byref(h), 64, 1024, 4, 0) == 2   # W above 512
+    assert h.value is None
+    assert lib.hyena_plan2d_destroy(None) == 0
+    assert lib.hyena_spectrum2d_bytes(None) == 0 and lib.hyena_workspace2d_bytes(None, 1) == 0
+    assert lib.hyena_filter_spectrum2d(None, 16, 16, None) == 1
+    assert lib.hyena_conv2d_forward(None, 1, 16, None, None, 16, 16, 16, 16, 1 << 20, None) == 1
 
 
 def test_valid_plan_without_gpu_reports_device_error(lib):
