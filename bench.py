@@ -77,6 +77,23 @@ def alg_bytes_pass(wl, family: str) -> int:
     raise ValueError(family)
 
 
+def alg_bytes_part(wl, family: str) -> int:
+    """Bytes each pass of the partitioned path must move by design, per forward
+    (all rows): pass 1 reads the step's input (two u_proj rows at the first step,
+    the previous step's fp32 output after it) and writes the window spectra (8L
+    per row); pass 2 reads the window spectra, the filter block spectra (8L per
+    channel and step) and one gate row, and writes y (last step) or the fp32
+    input of the next step."""
+    s = io_bytes(wl)
+    B, D, L, N = wl.B, wl.D, wl.L, wl.order
+    rows = B * D
+    if family == "pass_1":
+        return rows * (2 * s * L + 8 * L) + (N - 2) * rows * (4 * L + 8 * L)
+    if family == "pass_2":
+        return (N - 1) * (rows * (8 * L + s * L) + 8 * D * L) + rows * s * L + (N - 2) * rows * 4 * L
+    raise ValueError(family)
+
+
 # the sources each kernel family is compiled from, including the host code that
 # sizes its launches (chunking, grids)
 _CSRC = os.path.join(ROOT, "fft_long_convolution_libhyena_amd", "csrc")
@@ -92,6 +109,7 @@ KERNEL_SOURCES = {
                     "fourstep_backward.hip", "hyena_backward.hip"],
     "filter": ["plan.hpp", "implicit_filter.hip"],
     "conv2d": ["fft_core.hpp", "pair.hpp", "fourstep.hpp", "kernels.hpp", "plan.hpp", "tables.hpp", "conv2d.hip"],
+    "partitioned": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "partitioned.hip", "hyena_api.hip"],
 }
 
 
@@ -104,6 +122,8 @@ def kernel_family(kernel: str) -> str:
         return "fs_backward"
     if kernel.startswith("k_lds_bwd"):
         return "backward"
+    if kernel.startswith("k_part"):
+        return "partitioned"
     return "lds" if kernel.startswith("k_lds") else "fourstep"
 
 
@@ -703,7 +723,9 @@ def main():
     ap.add_argument("--workload", default="long64k")
     ap.add_argument("--reps", type=int, default=5, help="timed repetitions of --steps; the median is reported")
     ap.add_argument("--workspace-mb", type=float, default=0.0,
-                    help="four-step workspace (0 = the library's recommendation)")
+                    help="four-step / partitioned workspace (0 = the library's recommendation)")
+    ap.add_argument("--path", default="auto", choices=["auto", "lds", "fourstep", "partitioned"],
+                    help="kernel family of the forward plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--check", action="store_true", help="also compare sampled rows with the oracle")
@@ -767,7 +789,7 @@ def main():
     h = torch.from_numpy(x.h).to(dev)
     bias = torch.from_numpy(x.bias).to(dev)
 
-    plan = Plan(wl.L, wl.D, wl.order, wl.dtype)
+    plan = Plan(wl.L, wl.D, wl.order, wl.dtype, args.path)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     spec = plan.spectrum(h)
@@ -811,6 +833,16 @@ def main():
         # (events around a single launch add their own fence time)
         dom, dom_ms, dom_bytes = "k_lds_forward", ms, fwd_bytes
         launches = 1
+    elif plan.path == "partitioned":
+        # hyena_forward_timed reports pass 1 in the pass_a slot and pass 2 in pass_b
+        fam = max(("pass_a", "pass_b"), key=lambda k: fam_ms[k])
+        dom = {"pass_a": "k_part_fwd", "pass_b": "k_part_inv"}[fam]
+        dom_ms = fam_ms[fam]
+        dom_bytes = alg_bytes_part(wl, {"pass_a": "pass_1", "pass_b": "pass_2"}[fam])
+        rows = wl.B * wl.D
+        per_row = 8 * wl.L + (4 * wl.L if wl.order > 2 else 0)
+        chunk = max(1, min(rows, ws_bytes // per_row))
+        launches = math.ceil(rows / chunk) * (wl.order - 1)
     else:
         fam = max(("pass_a", "pass_b", "pass_c"), key=lambda k: fam_ms[k])
         dom = {"pass_a": "k_fs_colfwd", "pass_b": "k_fs_row", "pass_c": "k_fs_colinv"}[fam]

@@ -15,10 +15,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhyena.so")
 
 HYENA_F32, HYENA_BF16 = 0, 1
-PATH_AUTO, PATH_LDS, PATH_FOURSTEP, PATH_FUSED = 0, 1, 2, 3
+PATH_AUTO, PATH_LDS, PATH_FOURSTEP, PATH_FUSED, PATH_PARTITIONED = 0, 1, 2, 3, 4
 STATUS = {0: "HYENA_OK", 1: "HYENA_ERR_INVALID_ARG", 2: "HYENA_ERR_UNSUPPORTED",
           3: "HYENA_ERR_WORKSPACE", 4: "HYENA_ERR_DEVICE"}
-_PATHS = {"auto": PATH_AUTO, "lds": PATH_LDS, "fourstep": PATH_FOURSTEP, "fused": PATH_FUSED}
+_PATHS = {"auto": PATH_AUTO, "lds": PATH_LDS, "fourstep": PATH_FOURSTEP, "fused": PATH_FUSED,
+          "partitioned": PATH_PARTITIONED}
 _DTYPES = {"f32": HYENA_F32, "bf16": HYENA_BF16}
 
 # every symbol include/hyena.h declares
@@ -148,7 +149,8 @@ class Plan:
                self.lib.hyena_plan_create_ex(ctypes.byref(h), self.L, self.D, self.order, _DTYPES[dtype],
                                              _PATHS[path], FLAG_CIRCULAR if self.circular else 0))
         self.handle = h
-        self.path = {PATH_LDS: "lds", PATH_FOURSTEP: "fourstep", PATH_FUSED: "fused"}[self.lib.hyena_plan_path(h)]
+        self.path = {PATH_LDS: "lds", PATH_FOURSTEP: "fourstep", PATH_FUSED: "fused",
+                     PATH_PARTITIONED: "partitioned"}[self.lib.hyena_plan_path(h)]
 
     @property
     def io_dtype(self):

@@ -50,8 +50,17 @@ size_t stockham_size(int logn) {
     return tmp.size();
 }
 
+// Workspace bytes one (b, d) row needs in flight: its transposed tile on the
+// four-step path; its window spectra, plus the gated output of a step above order
+// 2, on the partitioned path.
+size_t ws_per_row(const hyena_plan_t plan) {
+    const size_t T = (size_t)1 << plan->logT;
+    if (plan->path == HYENA_PATH_PARTITIONED) return T * sizeof(float2) + (plan->order > 2 ? T * sizeof(float) : 0);
+    return T * sizeof(float2);
+}
+
 int64_t chunk_rows(const hyena_plan_t plan, int64_t rows, size_t ws_bytes) {
-    const size_t per_row = ((size_t)1 << plan->logT) * sizeof(float2);
+    const size_t per_row = ws_per_row(plan);
     int64_t n = (int64_t)(ws_bytes / per_row);
     if (n > rows) n = rows;
     if (n > kMaxChunkRows) n = kMaxChunkRows;  // keeps every grid dimension far below 2^31
@@ -80,7 +89,8 @@ hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int
     const bool circ = (flags & HYENA_FLAG_CIRCULAR) != 0;
     if (D < 1 || L < 1 || order < 2) return HYENA_ERR_INVALID_ARG;
     if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
-    if (path != HYENA_PATH_AUTO && path != HYENA_PATH_LDS && path != HYENA_PATH_FOURSTEP && path != HYENA_PATH_FUSED)
+    if (path != HYENA_PATH_AUTO && path != HYENA_PATH_LDS && path != HYENA_PATH_FOURSTEP && path != HYENA_PATH_FUSED &&
+        path != HYENA_PATH_PARTITIONED)
         return HYENA_ERR_INVALID_ARG;
     if (!is_pow2(L) || L < 16 || L > (int64_t(1) << kMaxLog) || order > 8) return HYENA_ERR_UNSUPPORTED;
     if (D > (int64_t(1) << 24)) return HYENA_ERR_UNSUPPORTED;
@@ -99,16 +109,21 @@ hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int
     if (p == HYENA_PATH_LDS && logT > hy::kLdsMaxLog) return HYENA_ERR_UNSUPPORTED;
     if (p == HYENA_PATH_FOURSTEP && logT < hy::kFsMinLog) return HYENA_ERR_UNSUPPORTED;
     if (p == HYENA_PATH_FUSED && (circ || !(order == 2 && hy::fused_supported(logT)))) return HYENA_ERR_UNSUPPORTED;
+    if (p == HYENA_PATH_PARTITIONED && (circ || logT < hy::kPartMinLog || logT > hy::kPartMaxLog))
+        return HYENA_ERR_UNSUPPORTED;
 
     // host tables (fp64 -> fp32)
     std::vector<float2> tab;
     size_t o_tw = 0, o_wpair = 0, o_tw1 = 0, o_tw2 = 0, o_lo = 0, o_hi = 0, o_pa = 0, o_pb = 0;
     int log1 = 0, log2 = 0;
-    if (p == HYENA_PATH_LDS) {
+    if (p == HYENA_PATH_LDS || p == HYENA_PATH_PARTITIONED) {
+        // the partitioned path transforms 2Q-sample windows: the LDS tables for length Q
+        const int lt = p == HYENA_PATH_LDS ? logT : hy::kPartLogQ;
+        const int64_t Tl = int64_t(1) << lt;
         o_tw = tab.size();
-        append_stockham(tab, logT);
+        append_stockham(tab, lt);
         o_wpair = tab.size();
-        for (int64_t k = 0; k <= T / 2; ++k) tab.push_back(wfwd(k, 2 * T));
+        for (int64_t k = 0; k <= Tl / 2; ++k) tab.push_back(wfwd(k, 2 * Tl));
     } else {
         hy::fs_split(logT, &log1, &log2);
         const int64_t L1 = int64_t(1) << log1, L2 = int64_t(1) << log2;
@@ -164,7 +179,7 @@ hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int
     plan->device = dev;
     plan->fused_blocks = fused_blocks;
     plan->dtab = dtab;
-    if (p == HYENA_PATH_LDS) {
+    if (p == HYENA_PATH_LDS || p == HYENA_PATH_PARTITIONED) {
         plan->tw = dtab + o_tw;
         plan->wpair = dtab + o_wpair;
     } else {
@@ -210,7 +225,7 @@ size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B) {
     if (!plan || B < 1) return 0;
     if (plan->path == HYENA_PATH_LDS) return 0;
     if (plan->path == HYENA_PATH_FUSED) return hy::fused_workspace_bytes(plan->logT, B * plan->D, kFusedG, kFusedS);
-    const size_t per_row = ((size_t)1 << plan->logT) * sizeof(float2);
+    const size_t per_row = ws_per_row(plan);
     int64_t rows = B * plan->D;
     int64_t want = (int64_t)(kChunkTargetBytes / per_row);
     if (want < 1) want = 1;
@@ -228,6 +243,10 @@ hyena_status_t hyena_filter_spectrum_batched(hyena_plan_t plan, int64_t B, const
     hipError_t e;
     if (plan->path == HYENA_PATH_LDS)
         e = hy::launch_lds_spectrum(plan->logT, h, (float2*)spec, rows, plan->tw, plan->wpair, stream, plan->circular);
+    else if (plan->path == HYENA_PATH_PARTITIONED)
+        // each filter row is L / Q consecutive blocks of Q taps: LDS spectra of Q-sample rows
+        e = hy::launch_lds_spectrum(hy::kPartLogQ, h, (float2*)spec, rows << (plan->logT - hy::kPartLogQ), plan->tw,
+                                    plan->wpair, stream, false);
     else
         e = hy::launch_fs_spectrum(plan->logT, h, (float2*)spec, rows, plan->fs, stream, plan->circular);
     return e == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
@@ -262,19 +281,22 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
         if (!workspace || !aligned16(workspace)) return HYENA_ERR_WORKSPACE;
         if (workspace_bytes < hy::fused_workspace_bytes(plan->logT, rows, kFusedG, kFusedS)) return HYENA_ERR_WORKSPACE;
     }
-    if (plan->path == HYENA_PATH_FOURSTEP) {
+    const bool part = plan->path == HYENA_PATH_PARTITIONED;
+    const bool chunked = plan->path == HYENA_PATH_FOURSTEP || part;
+    if (chunked) {
         if (!workspace || !aligned16(workspace)) return HYENA_ERR_WORKSPACE;
         chunk = chunk_rows(plan, rows, workspace_bytes);
         if (chunk < 1) return HYENA_ERR_WORKSPACE;
     }
     if (check_device(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
 
-    const int per_chunk = 2 * plan->order - 1;  // launches per chunk on the four-step path
-    const int64_t nchunks = plan->path == HYENA_PATH_FOURSTEP ? (rows + chunk - 1) / chunk : 1;
+    // launches per chunk: four-step 2N-1, partitioned 2(N-1)
+    const int per_chunk = part ? 2 * (plan->order - 1) : 2 * plan->order - 1;
+    const int64_t nchunks = chunked ? (rows + chunk - 1) / chunk : 1;
     std::vector<hipEvent_t> ev;
     if (ms) {
         for (int i = 0; i < 5; ++i) ms[i] = 0.f;
-        const int64_t n = plan->path == HYENA_PATH_FOURSTEP ? nchunks * (per_chunk + 1) : 2;  // LDS, FUSED: 2
+        const int64_t n = chunked ? nchunks * (per_chunk + 1) : 2;  // LDS, FUSED: 2
         if (n > 4096) return HYENA_ERR_INVALID_ARG;  // timing is for bounded chunk counts
         ev.resize((size_t)n, nullptr);
         for (auto& e : ev)
@@ -299,6 +321,18 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
         if (ms) (void)hipEventRecord(ev[0], stream);
         if (hy::launch_lds_forward(plan->logT, a, stream) != hipSuccess) st = HYENA_ERR_DEVICE;
         if (ms) (void)hipEventRecord(ev[1], stream);
+    } else if (part) {
+        // window spectra of the chunk's rows first, then the gated outputs of a step
+        const int64_t T = int64_t(1) << plan->logT;
+        float* vb = plan->order > 2 ? (float*)((float2*)workspace + chunk * T) : nullptr;
+        hy::PartArgs a{u_proj, short_w, (const float2*)spec, bias, y, (float2*)workspace, vb, plan->tw, plan->wpair,
+                       (int)plan->D, plan->order, (int)(T >> hy::kPartLogQ), bf16, sbs};
+        int64_t ci = 0;
+        for (int64_t r0 = 0; r0 < rows && st == HYENA_OK; r0 += chunk, ++ci) {
+            const int64_t n = (rows - r0) < chunk ? (rows - r0) : chunk;
+            hipEvent_t* marks = ms ? ev.data() + ci * (per_chunk + 1) : nullptr;
+            if (hy::launch_part_forward_chunk(a, r0, n, stream, marks) != hipSuccess) st = HYENA_ERR_DEVICE;
+        }
     } else {
         hy::FsArgs a{u_proj, short_w, (const float2*)spec, bias, y, (float2*)workspace, plan->fs,
                      (int)plan->D, plan->order, bf16, sbs, plan->circular};
@@ -314,9 +348,17 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
         if (st == HYENA_OK && hipEventSynchronize(ev.back()) != hipSuccess) st = HYENA_ERR_DEVICE;
         if (st == HYENA_OK) {
             float t = 0.f;
-            if (plan->path != HYENA_PATH_FOURSTEP) {
+            if (!chunked) {
                 (void)hipEventElapsedTime(&t, ev[0], ev[1]);
                 ms[0] = t;
+            } else if (part) {
+                for (int64_t c = 0; c < nchunks; ++c) {
+                    hipEvent_t* m = ev.data() + c * (per_chunk + 1);
+                    for (int i = 0; i < per_chunk; ++i) {
+                        (void)hipEventElapsedTime(&t, m[i], m[i + 1]);
+                        ms[1 + (i & 1)] += t;  // pass 1, pass 2 alternate
+                    }
+                }
             } else {
                 for (int64_t c = 0; c < nchunks; ++c) {
                     hipEvent_t* m = ev.data() + c * (per_chunk + 1);

@@ -27,6 +27,10 @@ namespace hy {
 #ifndef HY_FS_CB
 #define HY_FS_CB 16
 #endif
+// HY_PART_G         output blocks per workgroup of the partitioned path's pass 2
+#ifndef HY_PART_G
+#define HY_PART_G 4
+#endif
 template <int LOGL>
 struct LdsCfg {
     static constexpr int L = 1 << LOGL;
@@ -103,6 +107,27 @@ void fs_split(int logL, int* log1, int* log2);
 // Fused persistent four-step (order 2): one launch per forward, per-XCD pipelines.
 bool fused_supported(int logL);
 int fused_blocks_per_cu(int logL);
+// Partitioned path: blocks of Q = 2^kPartLogQ taps, L from 2Q to 2^kPartMaxLog.
+constexpr int kPartLogQ = 12;
+constexpr int kPartMinLog = kPartLogQ + 1;
+constexpr int kPartMaxLog = 17;
+struct PartArgs {
+    const void* u;
+    const float* w3;
+    const float2* spec;  // [o][d][block][Q] filter block spectra (the LDS layout for Q samples)
+    const float* bias;
+    void* y;
+    float2* X;           // window spectra of the chunk's rows, [row][window][Q]
+    float* vb;           // gated output of the previous step, [row][L] (order > 2)
+    const float2* tw;    // Stockham twiddles for length Q
+    const float2* wpair; // W_{2Q}^k, k = 0..Q/2
+    int D, N, P;         // P = L / Q
+    bool bf16;
+    int64_t sbs;         // spectrum batch stride (complex values): 0 = one spectrum for every b
+};
+hipError_t launch_part_forward_chunk(const PartArgs& a, int64_t row0, int64_t n, hipStream_t st, hipEvent_t* marks);
+int part_group(int P);  // output blocks per pass 2 workgroup
+
 size_t fused_workspace_bytes(int logL, int64_t nrows, int G, int S);
 hipError_t launch_fs_fused(int logL, const FsArgs& a, int64_t nrows, int G, int S, int blocks, hipStream_t st);
 uint32_t fused_error_offset(int x);

@@ -67,12 +67,20 @@ typedef enum {
  *             intermediate tiles kept in each XCD's L2 (order 2, L = 65536).
  *             Not available in this build: plans asking for it get
  *             HYENA_ERR_UNSUPPORTED.
+ *   PARTITIONED  the same causal convolution with the filter cut into
+ *             blocks of Q = 4096 taps (uniformly partitioned overlap-save):
+ *             two LDS-resident launches per recurrence step (transforms of
+ *             2Q-sample windows of v; block-Toeplitz sums of window and
+ *             filter-block spectra, inverse transforms and the gate), no
+ *             transposed tile. Zero-padded plans with 8192 <= L <= 131072;
+ *             hyena_backward does not take these plans.
  * AUTO picks LDS when L <= 16384 and FOURSTEP otherwise. */
 typedef enum {
     HYENA_PATH_AUTO = 0,
     HYENA_PATH_LDS = 1,
     HYENA_PATH_FOURSTEP = 2,
-    HYENA_PATH_FUSED = 3
+    HYENA_PATH_FUSED = 3,
+    HYENA_PATH_PARTITIONED = 4
 } hyena_path_t;
 
 /* Create a plan for sequence length L, operator width D and recurrence order
@@ -85,10 +93,13 @@ typedef enum {
 hyena_status_t hyena_plan_create(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype);
 
 /* As hyena_plan_create, with an explicit kernel family. HYENA_PATH_LDS needs
- * L <= 16384; HYENA_PATH_FOURSTEP needs L >= 256; HYENA_PATH_FUSED is not
- * available in this build (HYENA_ERR_UNSUPPORTED otherwise). The spectrum layout
- * depends on the path (FOURSTEP and FUSED share one), so a spectrum must be made
- * by a plan whose path uses the same layout as the plan that consumes it. */
+ * L <= 16384; HYENA_PATH_FOURSTEP needs L >= 256; HYENA_PATH_PARTITIONED needs
+ * 8192 <= L <= 131072 and no flags; HYENA_PATH_FUSED is not available in this
+ * build (HYENA_ERR_UNSUPPORTED otherwise). The spectrum layout depends on the
+ * path (FOURSTEP and FUSED share one; PARTITIONED holds the 2Q-point spectra of
+ * each filter's L/Q blocks, [o][d][block][Q], in the LDS layout), so a spectrum
+ * must be made by a plan whose path uses the same layout as the plan that
+ * consumes it. */
 hyena_status_t hyena_plan_create_path(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype,
                                       hyena_path_t path);
 
@@ -113,8 +124,8 @@ hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int
  * The caller must ensure no enqueued work still uses the plan. */
 hyena_status_t hyena_plan_destroy(hyena_plan_t plan);
 
-/* The path a plan resolved to (HYENA_PATH_LDS or HYENA_PATH_FOURSTEP), or
- * HYENA_PATH_AUTO for a NULL plan. */
+/* The path a plan resolved to (HYENA_PATH_LDS, HYENA_PATH_FOURSTEP or
+ * HYENA_PATH_PARTITIONED), or HYENA_PATH_AUTO for a NULL plan. */
 hyena_path_t hyena_plan_path(hyena_plan_t plan);
 
 /* Bytes of the opaque spectrum buffer: (N-1) * D * L complex fp32 values, i.e.
@@ -125,7 +136,9 @@ size_t hyena_spectrum_bytes(hyena_plan_t plan);
 /* Workspace for a forward over batch B: 0 on the LDS path. On the four-step
  * path this is the recommended size (8*L bytes per (b, d) row held in flight);
  * any workspace of at least 8*L bytes (one row) is accepted, a larger one lets
- * more rows run per launch. On the fused path it is the exact minimum: a control
+ * more rows run per launch. The partitioned path likewise, with 8*L bytes per
+ * row at order 2 and 12*L bytes per row above (the gated output of a step is
+ * held for the next). On the fused path it is the exact minimum: a control
  * block, per-row counters and a ring of tiles per XCD. Returns 0 for a NULL plan
  * or B < 1. */
 size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B);
@@ -163,8 +176,9 @@ hyena_status_t hyena_filter_spectrum_batched(hyena_plan_t plan, int64_t B, const
  *   y       [B][D][L] of the plan dtype, device (output, before the b d l ->
  *           b l d rearrange)
  *   workspace / workspace_bytes: device scratch, at least 8*L bytes on the
- *           four-step path (see hyena_workspace_bytes); ignored (may be NULL)
- *           on the LDS path. Contents on entry are irrelevant.
+ *           four-step path and 8*L (order 2) or 12*L bytes on the partitioned
+ *           path (see hyena_workspace_bytes); ignored (may be NULL) on the LDS
+ *           path. Contents on entry are irrelevant.
  * Enqueued on `stream`; no host synchronisation. Errors: HYENA_ERR_INVALID_ARG
  * (NULL/misaligned pointers, B < 1 or B*D*L too large), HYENA_ERR_WORKSPACE,
  * HYENA_ERR_DEVICE (launch failure, wrong current device). */
@@ -188,7 +202,9 @@ hyena_status_t hyena_forward_per_sample(hyena_plan_t plan, int64_t B, const void
  *   ms[0] the single kernel of the LDS or fused path, ms[1] four-step pass A (column FFTs of the
  *   gated input), ms[2] pass B (row FFTs, spectrum multiply, inverse rows),
  *   ms[3] pass C (inverse columns and gate; for order > 2 it also carries the
- *   next step's pass A), ms[4] first event to last event.
+ *   next step's pass A), ms[4] first event to last event. On the partitioned
+ *   path ms[1] is pass 1 (window transforms) and ms[2] pass 2 (block sums,
+ *   inverse transforms, gate).
  * Same arguments, results and errors as hyena_forward; HYENA_ERR_INVALID_ARG
  * also for ms == NULL or more than 4096 events. */
 hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
