@@ -791,8 +791,10 @@ def main():
 
     plan = Plan(wl.L, wl.D, wl.order, wl.dtype, args.path)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spec = plan.spectrum(h)  # first call: allocates the buffer and loads the kernels
+    torch.cuda.synchronize()
     ev0.record()
-    spec = plan.spectrum(h)
+    plan.spectrum(h, out=spec)
     ev1.record()
     torch.cuda.synchronize()
     spectrum_ms = ev0.elapsed_time(ev1)
