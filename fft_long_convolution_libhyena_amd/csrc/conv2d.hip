@@ -69,7 +69,7 @@ struct C2Row {
     static constexpr int W = 1 << LOGW;
     static constexpr int T2 = W / 16;                     // threads per row
     static constexpr int U0 = 2048 / W;
-    static constexpr int UNITS = U0 > 16 ? 16 : U0;       // row pairs per workgroup (<= H / 1)
+    static constexpr int UNITS = U0 > 16 ? 16 : U0;       // row pairs per workgroup (an image has H >= 16)
     static constexpr int THREADS = UNITS * 2 * T2;
     static constexpr int RP = W + W / 16;                 // padded LDS row
 };

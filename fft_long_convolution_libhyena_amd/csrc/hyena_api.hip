@@ -44,12 +44,6 @@ int ilog2_64(int64_t x) {
     return l;
 }
 
-size_t stockham_size(int logn) {
-    std::vector<float2> tmp;
-    append_stockham(tmp, logn);
-    return tmp.size();
-}
-
 // Workspace bytes one (b, d) row needs in flight: its transposed tile on the
 // four-step path; its window spectra, plus the gated output of a step above order
 // 2, on the partitioned path.
