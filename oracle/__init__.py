@@ -245,6 +245,45 @@ def conv2d_forward(v: np.ndarray, k: np.ndarray, bias: np.ndarray, g: Optional[n
     return y
 
 
+def conv3d_forward(v: np.ndarray, k: np.ndarray, bias: np.ndarray, g: Optional[np.ndarray] = None,
+                   x: Optional[np.ndarray] = None, mode: str = "fft") -> np.ndarray:
+    """One gated 3-D long-convolution step in fp64: ``conv2d_forward`` with one more
+    grid axis (HyenaND summary, methodology: global convolution on the native N-d
+    grid by an N-d FFT, the input zero-padded to double the grid in every dimension
+    for the non-circular mode). v, g, x [B, D, A, H, W]; k [D, 2A, 2H, 2W] on the
+    doubled grid (index >= the axis length holds the negative offset, as in 2-D);
+    bias [D]. With s = v * g:
+      c[a, p, q] = sum_{l < 2A, i < 2H, j < 2W} k[l, i, j]
+                   s_pad[(a - l) mod 2A, (p - i) mod 2H, (q - j) mod 2W],
+    a < A, p < H, q < W; y = (c + bias * s) * x. ``direct`` is that sum written out;
+    ``fft`` multiplies numpy's rfftn of the padded input and of the kernel.
+    Returns [B, D, A, H, W] float64."""
+    s = np.asarray(v, dtype=np.float64)
+    if g is not None:
+        s = s * np.asarray(g, dtype=np.float64)
+    B, D, A, H, W = s.shape
+    kk = np.asarray(k, dtype=np.float64)
+    if kk.shape != (D, 2 * A, 2 * H, 2 * W):
+        raise ValueError("k must be [D, 2A, 2H, 2W]")
+    if mode == "direct":
+        sp = np.zeros((B, D, 2 * A, 2 * H, 2 * W))
+        sp[:, :, :A, :H, :W] = s
+        c = np.zeros((B, D, A, H, W))
+        for l in range(2 * A):
+            for i in range(2 * H):
+                for j in range(2 * W):
+                    sh = np.roll(sp, (l, i, j), axis=(2, 3, 4))[:, :, :A, :H, :W]
+                    c += kk[None, :, l, i, j, None, None, None] * sh
+    else:
+        S = np.fft.rfftn(s, s=(2 * A, 2 * H, 2 * W), axes=(2, 3, 4))
+        Kh = np.fft.rfftn(kk, axes=(1, 2, 3))
+        c = np.fft.irfftn(S * Kh[None], s=(2 * A, 2 * H, 2 * W), axes=(2, 3, 4))[:, :, :A, :H, :W]
+    y = c + np.asarray(bias, dtype=np.float64)[None, :, None, None, None] * s
+    if x is not None:
+        y = y * np.asarray(x, dtype=np.float64)
+    return y
+
+
 def forward_per_sample(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray, order: int,
                        mode: str = "fft", threads: int = 0) -> np.ndarray:
     """The hot path with a filter set per sample (input-dependent long convolutions,
