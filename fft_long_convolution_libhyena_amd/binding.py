@@ -31,7 +31,9 @@ EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_create_ex"
            "hyena_operator_workspace_bytes", "hyena_operator_forward", "hyena_operator_forward_timed",
            "hyena_implicit_filter", "hyena_filter_spectrum_batched", "hyena_forward_per_sample",
            "hyena_plan2d_create", "hyena_plan2d_destroy", "hyena_spectrum2d_bytes", "hyena_workspace2d_bytes",
-           "hyena_filter_spectrum2d", "hyena_conv2d_forward", "hyena_status_string")
+           "hyena_filter_spectrum2d", "hyena_conv2d_forward", "hyena_plan3d_create", "hyena_plan3d_destroy",
+           "hyena_spectrum3d_bytes", "hyena_workspace3d_bytes", "hyena_filter_spectrum3d", "hyena_conv3d_forward",
+           "hyena_status_string")
 
 
 class FilterMLPStruct(ctypes.Structure):
@@ -114,6 +116,18 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_filter_spectrum2d.restype = ci
     lib.hyena_conv2d_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hyena_conv2d_forward.restype = ci
+    lib.hyena_plan3d_create.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i64, ci]
+    lib.hyena_plan3d_create.restype = ci
+    lib.hyena_plan3d_destroy.argtypes = [vp]
+    lib.hyena_plan3d_destroy.restype = ci
+    lib.hyena_spectrum3d_bytes.argtypes = [vp]
+    lib.hyena_spectrum3d_bytes.restype = sz
+    lib.hyena_workspace3d_bytes.argtypes = [vp, i64]
+    lib.hyena_workspace3d_bytes.restype = sz
+    lib.hyena_filter_spectrum3d.argtypes = [vp, vp, vp, vp]
+    lib.hyena_filter_spectrum3d.restype = ci
+    lib.hyena_conv3d_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hyena_conv3d_forward.restype = ci
     lib.hyena_status_string.argtypes = [ci]
     lib.hyena_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -392,80 +406,84 @@ class Plan:
         self.close()
 
 
-class Plan2D:
-    """A 2-D plan: H x W images of D channels, I/O dtype "f32" or "bf16"
-    (hyena_plan2d_create; the gated 2-D long convolution of include/hyena.h)."""
+class _GridPlan:
+    """Shared body of the N-d plans (Plan2D, Plan3D): the grid dims, D channels,
+    I/O dtype "f32" or "bf16"; the C calls are hyena_plan{2d,3d}_create, ... ."""
+    _SFX = ""
 
-    def __init__(self, H: int, W: int, D: int, dtype: str = "f32"):
+    def __init__(self, dims, D: int, dtype: str = "f32"):
         import torch
 
         self._torch = torch
         self.lib = load_library()
-        self.H, self.W, self.D, self.dtype = int(H), int(W), int(D), dtype
+        self.dims, self.D, self.dtype = tuple(int(n) for n in dims), int(D), dtype
         if dtype not in _DTYPES:
             raise ValueError(f"dtype must be one of {list(_DTYPES)}")
         self.device = torch.device("cuda", torch.cuda.current_device())
         h = ctypes.c_void_p()
-        _check("hyena_plan2d_create",
-               self.lib.hyena_plan2d_create(ctypes.byref(h), self.H, self.W, self.D, _DTYPES[dtype]))
+        name = f"hyena_plan{self._SFX}_create"
+        _check(name, getattr(self.lib, name)(ctypes.byref(h), *self.dims, self.D, _DTYPES[dtype]))
         self.handle = h
+
+    def _fn(self, stem, tail=""):
+        return getattr(self.lib, f"hyena_{stem}{self._SFX}{tail}")
 
     @property
     def io_dtype(self):
         return self._torch.bfloat16 if self.dtype == "bf16" else self._torch.float32
 
     def spectrum_bytes(self) -> int:
-        return int(self.lib.hyena_spectrum2d_bytes(self.handle))
+        return int(self._fn("spectrum", "_bytes")(self.handle))
 
     def workspace_bytes(self, B: int) -> int:
-        return int(self.lib.hyena_workspace2d_bytes(self.handle, int(B)))
+        return int(self._fn("workspace", "_bytes")(self.handle, int(B)))
 
     def _need(self, t, name, shape, dtype):
         Plan._need(self, t, name, shape, dtype)
 
     def spectrum(self, k, out=None):
-        """hyena_filter_spectrum2d: k [D, 2H, 2W] fp32 -> opaque uint8 device buffer."""
+        """hyena_filter_spectrum{2d,3d}: k [D, *doubled grid] fp32 -> opaque uint8 device buffer."""
         torch = self._torch
-        self._need(k, "k", (self.D, 2 * self.H, 2 * self.W), torch.float32)
+        self._need(k, "k", (self.D, *[2 * n for n in self.dims]), torch.float32)
         if out is None:
             out = torch.empty(self.spectrum_bytes(), dtype=torch.uint8, device=self.device)
         elif out.numel() * out.element_size() < self.spectrum_bytes():
             raise ValueError("spectrum buffer too small")
-        _check("hyena_filter_spectrum2d",
-               self.lib.hyena_filter_spectrum2d(self.handle, k.data_ptr(), out.data_ptr(),
-                                                _stream_handle(torch, self.device)))
+        _check(f"hyena_filter_spectrum{self._SFX}",
+               self._fn("filter_spectrum")(self.handle, k.data_ptr(), out.data_ptr(),
+                                           _stream_handle(torch, self.device)))
         return out
 
     def forward(self, v, spec, bias, g=None, x=None, y=None, workspace=None):
-        """hyena_conv2d_forward: v (and the optional gates g, x) [B, D, H, W] -> y."""
+        """hyena_conv{2d,3d}_forward: v (and the optional gates g, x) [B, D, *grid] -> y."""
         torch = self._torch
-        if v.dim() != 4:
-            raise ValueError("v must be [B, D, H, W]")
+        if v.dim() != 2 + len(self.dims):
+            raise ValueError(f"v must be [B, D, {', '.join(str(n) for n in self.dims)}]")
         B = int(v.shape[0])
-        shape = (B, self.D, self.H, self.W)
+        shape = (B, self.D, *self.dims)
         self._need(v, "v", shape, self.io_dtype)
         for name, t in (("g", g), ("x", x)):
             if t is not None:
                 self._need(t, name, shape, self.io_dtype)
         self._need(bias, "bias", (self.D,), torch.float32)
         if spec.device != self.device or spec.numel() * spec.element_size() < self.spectrum_bytes():
-            raise ValueError("spec must come from Plan2D.spectrum of an equal plan")
+            raise ValueError(f"spec must come from {type(self).__name__}.spectrum of an equal plan")
         if y is None:
             y = torch.empty(shape, dtype=self.io_dtype, device=self.device)
         self._need(y, "y", shape, self.io_dtype)
         if workspace is None:
             workspace = torch.empty(self.workspace_bytes(B), dtype=torch.uint8, device=self.device)
-        _check("hyena_conv2d_forward",
-               self.lib.hyena_conv2d_forward(self.handle, B, v.data_ptr(), g.data_ptr() if g is not None else None,
-                                             x.data_ptr() if x is not None else None, spec.data_ptr(),
-                                             bias.data_ptr(), y.data_ptr(), workspace.data_ptr(),
-                                             workspace.numel() * workspace.element_size(),
-                                             _stream_handle(torch, self.device)))
+        _check(f"hyena_conv{self._SFX}_forward",
+               getattr(self.lib, f"hyena_conv{self._SFX}_forward")(
+                   self.handle, B, v.data_ptr(), g.data_ptr() if g is not None else None,
+                   x.data_ptr() if x is not None else None, spec.data_ptr(), bias.data_ptr(), y.data_ptr(),
+                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                   _stream_handle(torch, self.device)))
         return y
 
     def close(self):
         if getattr(self, "handle", None) is not None and self.handle.value:
-            self.lib.hyena_plan2d_destroy(self.handle)
+            getattr(self.lib, f"hyena_plan{self._SFX}_destroy")(self.handle)
             self.handle = ctypes.c_void_p()
 
     def __del__(self):
@@ -479,3 +497,23 @@ class Plan2D:
 
     def __exit__(self, *exc):
         self.close()
+
+
+class Plan2D(_GridPlan):
+    """A 2-D plan: H x W images of D channels (hyena_plan2d_create; the gated 2-D
+    long convolution of include/hyena.h)."""
+    _SFX = "2d"
+
+    def __init__(self, H: int, W: int, D: int, dtype: str = "f32"):
+        self.H, self.W = int(H), int(W)
+        super().__init__((H, W), D, dtype)
+
+
+class Plan3D(_GridPlan):
+    """A 3-D plan: A x H x W volumes of D channels (hyena_plan3d_create; the gated
+    3-D long convolution of include/hyena.h)."""
+    _SFX = "3d"
+
+    def __init__(self, A: int, H: int, W: int, D: int, dtype: str = "f32"):
+        self.A, self.H, self.W = int(A), int(H), int(W)
+        super().__init__((A, H, W), D, dtype)

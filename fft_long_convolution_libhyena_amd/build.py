@@ -14,9 +14,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhyena.so")
-SOURCES = ["hyena_api.hip", "hyena_backward.hip", "hyena_operator.hip", "fourstep.hip", "fourstep_backward.hip", "implicit_filter.hip", "conv2d.hip", "partitioned.hip", "lds_path_a.hip", "lds_path_b.hip", "lds_path_c.hip",
+SOURCES = ["hyena_api.hip", "hyena_backward.hip", "hyena_operator.hip", "fourstep.hip", "fourstep_backward.hip", "implicit_filter.hip", "conv2d.hip", "conv3d.hip", "partitioned.hip", "lds_path_a.hip", "lds_path_b.hip", "lds_path_c.hip",
            "lds_path_d.hip", "lds_backward_a.hip", "lds_backward_b.hip", "lds_backward_c.hip", "lds_backward_d.hip"]
-HEADERS = ["fft_core.hpp", "kernels.hpp", "pair.hpp", "plan.hpp", "tables.hpp", "lds_path.hpp", "fourstep.hpp", "backward.hpp",
+HEADERS = ["fft_core.hpp", "kernels.hpp", "pair.hpp", "plan.hpp", "tables.hpp", "conv_nd.hpp", "lds_path.hpp", "fourstep.hpp", "backward.hpp",
            "lds_backward.hpp"]
 
 HIPCC_FLAGS = [

@@ -286,6 +286,47 @@ def conv2d_inputs(B: int, D: int, H: int, W: int, dtype: str = "f32", seed: int 
     return Conv2dInputs(*[np.ascontiguousarray(a, dtype=np.float32) for a in arrs + [k, bias]])
 
 
+@dataclasses.dataclass
+class Conv3dInputs:
+    """Inputs of one gated 3-D long-convolution step (all fp32; bf16 values for bf16)."""
+    v: np.ndarray     # [B, D, A, H, W]
+    g: np.ndarray     # [B, D, A, H, W] pre-gate
+    x: np.ndarray     # [B, D, A, H, W] post-gate
+    k: np.ndarray     # [D, 2A, 2H, 2W] kernel on the doubled grid
+    bias: np.ndarray  # [D]
+
+
+def conv3d_inputs(B: int, D: int, A: int, H: int, W: int, dtype: str = "f32", seed: int = 0,
+                  centred: bool = True) -> Conv3dInputs:
+    """Seeded inputs for the 3-D step, drawn as for ``conv2d_inputs`` with one more
+    axis: v, g, x ~ N(0, 1); k = N(0, 1) * exp(-alpha_d * r / max(A, H, W)), r the
+    length of the offset each doubled-grid position stands for (centred: the upper
+    half of every axis holds negative offsets; otherwise a causal kernel, zero
+    outside [0, A) x [0, H) x [0, W)); bias ~ N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 6000))
+    v = rng.standard_normal((B, D, A, H, W), dtype=np.float32)
+    g = rng.standard_normal((B, D, A, H, W), dtype=np.float32)
+    x = rng.standard_normal((B, D, A, H, W), dtype=np.float32)
+    noise = rng.standard_normal((D, 2 * A, 2 * H, 2 * W), dtype=np.float32)
+    bias = rng.standard_normal(D, dtype=np.float32)
+    offs = []
+    for n in (A, H, W):
+        o = np.arange(2 * n)
+        offs.append(np.where(o < n, o, o - 2 * n) if centred else o)
+    r = np.sqrt(offs[0][:, None, None].astype(np.float64) ** 2 + offs[1][None, :, None] ** 2
+                + offs[2][None, None, :] ** 2) / max(A, H, W)
+    alpha = _alphas(D, 0.3, 30.0)
+    k = noise * np.exp(-alpha[:, None, None, None] * r[None]).astype(np.float32)
+    if not centred:
+        k[:, A:] = 0.0
+        k[:, :, H:] = 0.0
+        k[:, :, :, W:] = 0.0
+    arrs = [v, g, x]
+    if dtype == "bf16":
+        arrs = [round_to_bf16(a) for a in arrs]
+    return Conv3dInputs(*[np.ascontiguousarray(a, dtype=np.float32) for a in arrs + [k, bias]])
+
+
 def channel_subset(x: Inputs, ds) -> Inputs:
     """The inputs restricted to channels ds of every channel group (gates, value,
     filters, biases): the hot path treats channels independently, so a subset is a

@@ -399,6 +399,61 @@ hyena_status_t hyena_conv2d_forward(hyena_plan2d_t plan, int64_t B, const void* 
                                     const void* spec, const float* bias, void* y, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * 3-D long convolution: the 2-D step above with one more grid axis (HyenaND
+ * summary, methodology: the N-d FFT convolution on the native grid, zero-padded
+ * to double the grid in every dimension). One gated step per (b, d) volume:
+ *   s = v * g            (g optional)
+ *   c[a][p][q] = sum_{l < 2A, i < 2H, j < 2W} k[l][i][j]
+ *                s_pad[(a - l) mod 2A][(p - i) mod 2H][(q - j) mod 2W]
+ *   y = (c + bias * s) * x   (x optional),     a < A, p < H, q < W,
+ * with the kernel given on the doubled grid (an index >= the axis length holds
+ * the negative offset, as in 2-D).
+ * ------------------------------------------------------------------------ */
+typedef struct hyena_plan3d_s* hyena_plan3d_t; /* opaque */
+
+/* Plan for A x H x W volumes (powers of two, 16 <= A, H <= 512, 32 <= W <= 512,
+ * A*H*W <= 2^24) of D channels; dtype of v, g, x and y as for the 1-D plans. The
+ * plan owns its twiddle tables on the current device. Errors as
+ * hyena_plan_create. */
+hyena_status_t hyena_plan3d_create(hyena_plan3d_t* out, int64_t A, int64_t H, int64_t W, int64_t D,
+                                   hyena_dtype_t dtype);
+
+/* Release a 3-D plan. NULL is a no-op. */
+hyena_status_t hyena_plan3d_destroy(hyena_plan3d_t plan);
+
+/* Bytes of a 3-D kernel spectrum: D * 2A * 2H * (W + 1) complex fp32 values, the
+ * doubled grid's real-transform bins (numpy.fft.rfftn layout) of each channel,
+ * scaled by 1/(4 * 2A * 2H * W). Returns 0 for a NULL plan. */
+size_t hyena_spectrum3d_bytes(hyena_plan3d_t plan);
+
+/* Workspace for hyena_conv3d_forward over batch B: any size of at least one
+ * volume's two tiles (24 * A * H * W bytes) is accepted; this is the recommended
+ * size (up to 192 MiB of tiles per launch). Returns 0 for a NULL plan or B < 1. */
+size_t hyena_workspace3d_bytes(hyena_plan3d_t plan, int64_t B);
+
+/* Kernel spectra, once per plan.
+ *   k    [D][2A][2H][2W] fp32, device: the kernels on the doubled grid
+ *   spec device buffer of hyena_spectrum3d_bytes(plan) bytes (output)
+ * Enqueued on `stream`. HYENA_ERR_INVALID_ARG for NULL or misaligned pointers,
+ * HYENA_ERR_DEVICE for launch failures or a wrong current device. */
+hyena_status_t hyena_filter_spectrum3d(hyena_plan3d_t plan, const float* k, void* spec, hipStream_t stream);
+
+/* The gated 3-D long convolution above for B x D volumes.
+ *   v    [B][D][A][H][W] of the plan dtype, device
+ *   g, x [B][D][A][H][W] of the plan dtype, device, or NULL (no gate)
+ *   spec from hyena_filter_spectrum3d of this plan; bias [D] fp32, device
+ *   y    [B][D][A][H][W] of the plan dtype, device (output; must not alias inputs)
+ *   workspace / workspace_bytes: at least 24*A*H*W bytes (hyena_workspace3d_bytes)
+ * Five passes per chunk of volumes: column FFTs over a of the gated volume and
+ * over h, row FFTs over w with the spectrum multiply and the inverse rows, inverse
+ * columns over h and over a with the gate; all intermediates fp32. Enqueued on
+ * `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL or misaligned pointers, B < 1,
+ * B*D > 2^24), HYENA_ERR_WORKSPACE, HYENA_ERR_DEVICE. */
+hyena_status_t hyena_conv3d_forward(hyena_plan3d_t plan, int64_t B, const void* v, const void* g, const void* x,
+                                    const void* spec, const float* bias, void* y, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* hyena_status_string(hyena_status_t s);
 

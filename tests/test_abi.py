@@ -127,6 +127,23 @@ def test_conv2d_entry_points_reject_bad_arguments(lib):
     assert lib.hyena_conv2d_forward(None, 1, 16, None, None, 16, 16, 16, 16, 1 << 20, None) == 1
 
 
+def test_conv3d_entry_points_reject_bad_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.hyena_plan3d_create(None, 32, 32, 32, 4, 0) == 1
+    assert lib.hyena_plan3d_create(ctypes.byref(h), 32, 0, 32, 4, 0) == 1
+    assert lib.hyena_plan3d_create(ctypes.byref(h), 32, 32, 32, 4, 5) == 1   # bad dtype
+    assert lib.hyena_plan3d_create(ctypes.byref(h), 24, 32, 32, 4, 0) == 2   # A not a power of two
+    assert lib.hyena_plan3d_create(ctypes.byref(h), 8, 32, 32, 4, 0) == 2    # A below 16
+    assert lib.hyena_plan3d_create(ctypes.byref(h), 32, 8, 32, 4, 0) == 2    # H below 16
+    assert lib.hyena_plan3d_create(ctypes.byref(h), 32, 32, 16, 4, 0) == 2   # W below 32
+    assert lib.hyena_plan3d_create(ctypes.byref(h), 512, 512, 512, 4, 0) == 2  # more than 2^24 points
+    assert h.value is None
+    assert lib.hyena_plan3d_destroy(None) == 0
+    assert lib.hyena_spectrum3d_bytes(None) == 0 and lib.hyena_workspace3d_bytes(None, 1) == 0
+    assert lib.hyena_filter_spectrum3d(None, 16, 16, None) == 1
+    assert lib.hyena_conv3d_forward(None, 1, 16, None, None, 16, 16, 16, 16, 1 << 20, None) == 1
+
+
 def test_valid_plan_without_gpu_reports_device_error(lib):
     torch = pytest.importorskip("torch")
     if torch.cuda.is_available():
