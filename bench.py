@@ -108,7 +108,10 @@ KERNEL_SOURCES = {
     "fs_backward": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "backward.hpp", "fourstep.hpp",
                     "fourstep_backward.hip", "hyena_backward.hip"],
     "filter": ["plan.hpp", "implicit_filter.hip"],
-    "conv2d": ["fft_core.hpp", "pair.hpp", "fourstep.hpp", "kernels.hpp", "plan.hpp", "tables.hpp", "conv2d.hip"],
+    "conv2d": ["fft_core.hpp", "pair.hpp", "fourstep.hpp", "kernels.hpp", "plan.hpp", "tables.hpp", "conv_nd.hpp",
+               "conv2d.hip"],
+    "conv3d": ["fft_core.hpp", "pair.hpp", "fourstep.hpp", "kernels.hpp", "plan.hpp", "tables.hpp", "conv_nd.hpp",
+               "conv3d.hip"],
     "partitioned": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "partitioned.hip", "hyena_api.hip"],
 }
 
@@ -116,6 +119,8 @@ KERNEL_SOURCES = {
 def kernel_family(kernel: str) -> str:
     if kernel.startswith("k_implicit_filter"):
         return "filter"
+    if kernel.startswith("k_c3"):
+        return "conv3d"
     if kernel.startswith("k_c2"):
         return "conv2d"
     if kernel.startswith("fs_backward"):
@@ -648,18 +653,26 @@ def bench_circular(args, wl, x, torch, Plan):
     plan.close()
 
 
-def bench_conv2d(args, torch):
-    """hyena_conv2d_forward: one gated 2-D long-convolution step on a 256 x 256 grid
-    (65536 tokens per channel, as in long64k) of 768 channels, both gates, a
-    centred kernel; against its algorithmic bytes (v, g, x read once, y written
-    once, the kernel spectrum read once)."""
+def bench_convnd(args, torch, nd: int):
+    """hyena_conv2d_forward / hyena_conv3d_forward: one gated N-d long-convolution
+    step on a 256 x 256 grid (2-D) or a 32 x 32 x 64 grid (3-D) -- 65536 tokens per
+    channel, as in long64k -- of 768 channels, both gates, a centred kernel; against
+    its algorithmic bytes (v, g, x read once, y written once, the kernel spectrum
+    read once)."""
     import oracle
-    from fft_long_convolution_libhyena_amd import Plan2D, synth
+    from fft_long_convolution_libhyena_amd import Plan2D, Plan3D, synth
 
-    B, D, H, W = 1, 768, 256, 256
+    B, D = 1, 768
+    dims = (256, 256) if nd == 2 else (32, 32, 64)
     dev = torch.device("cuda", 0)
-    inp = synth.conv2d_inputs(B, D, H, W, seed=3)
-    plan = Plan2D(H, W, D)
+    if nd == 2:
+        inp = synth.conv2d_inputs(B, D, *dims, seed=3)
+        plan = Plan2D(*dims, D)
+        ref_fn = oracle.conv2d_forward
+    else:
+        inp = synth.conv3d_inputs(B, D, *dims, seed=3)
+        plan = Plan3D(*dims, D)
+        ref_fn = oracle.conv3d_forward
     spec = plan.spectrum(torch.from_numpy(inp.k).to(dev))
     v, g, x = (torch.from_numpy(a).to(dev) for a in (inp.v, inp.g, inp.x))
     bias = torch.from_numpy(inp.bias).to(dev)
@@ -680,23 +693,27 @@ def bench_conv2d(args, torch):
         times.append(ev0.elapsed_time(ev1) / args.steps)
         log(f"[bench] rep {rep}: {times[-1] * 1e3:.1f} us/step")
     ms = float(np.median(times))
-    nbytes = 4 * 4 * B * D * H * W + 8 * D * 2 * H * (W + 1) + 4 * D
+    pts = int(np.prod(dims))
+    spec_bins = int(np.prod([2 * n for n in dims[:-1]])) * (dims[-1] + 1)
+    nbytes = 4 * 4 * B * D * pts + 8 * D * spec_bins + 4 * D
     achieved = nbytes / (ms * 1e-3) / 1e9
+    grid = "x".join(str(n) for n in dims)
+    names = "B·D·H·W" if nd == 2 else "B·D·A·H·W"
     out = {
-        "metric": "channel-tokens/s (B·D·H·W/s) and % HBM peak, gated 2-D long convolution (grid doubled)",
-        "value": B * D * H * W / (ms * 1e-3), "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "metric": f"channel-tokens/s ({names}/s) and % HBM peak, gated {nd}-D long convolution (grid doubled)",
+        "value": B * D * pts / (ms * 1e-3), "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic seeded (N(0,1) images and gates, centred decaying random kernels)",
-        "config": {"workload": f"conv2d {H}x{W}", "B": B, "D": D, "H": H, "W": W, "pass": "conv2d_forward"},
+        "dtype": "f32", "data": "synthetic seeded (N(0,1) grids and gates, centred decaying random kernels)",
+        "config": {"workload": f"conv{nd}d {grid}", "B": B, "D": D, "grid": list(dims), "pass": f"conv{nd}d_forward"},
         "hbm_frac_forward": round(achieved / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "2-D passes (whole step)", "alg_bytes_per_launch": nbytes, "launch_ms": round(ms, 5),
-                     "launches_per_step": 1},
+                     "kernel": f"{nd}-D passes (whole step)", "alg_bytes_per_launch": nbytes,
+                     "launch_ms": round(ms, 5), "launches_per_step": 1},
     }
     if args.check:
         ds = [0, D // 2, D - 1]
-        ref = oracle.conv2d_forward(inp.v[:, ds], inp.k[ds], inp.bias[ds], inp.g[:, ds], inp.x[:, ds])
+        ref = ref_fn(inp.v[:, ds], inp.k[ds], inp.bias[ds], inp.g[:, ds], inp.x[:, ds])
         out["check_rel_l2"] = oracle.rel_l2(y.cpu().numpy()[:, ds], ref)
         log(f"[bench] oracle check on channels {ds}: rel_l2 {out['check_rel_l2']:.3e}")
     if not args.no_cpu_baseline:
@@ -704,13 +721,13 @@ def bench_conv2d(args, torch):
         while True:
             ds = list(range(n))
             t0 = time.perf_counter()
-            oracle.conv2d_forward(inp.v[:, ds], inp.k[ds], inp.bias[ds], inp.g[:, ds], inp.x[:, ds])
+            ref_fn(inp.v[:, ds], inp.k[ds], inp.bias[ds], inp.g[:, ds], inp.x[:, ds])
             dt = time.perf_counter() - t0
             if dt >= args.cpu_budget / 4 or n >= D:
                 break
             n = int(min(D, max(n + 1, n * args.cpu_budget / max(dt, 1e-3) * 0.8)))
-        out["cpu_baseline"] = {"value": B * n * H * W / dt, "unit": "channel-tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"{n} of {D} channels, fp64 numpy rfft2 (one thread), {dt:.1f} s wall"}
+        out["cpu_baseline"] = {"value": B * n * pts / dt, "unit": "channel-tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"{n} of {D} channels, fp64 numpy rfftn (one thread), {dt:.1f} s wall"}
     print(json.dumps(out), flush=True)
     plan.close()
 
@@ -735,6 +752,8 @@ def main():
                     help="time hyena_backward instead of the forward")
     ap.add_argument("--conv2d", action="store_true",
                     help="time hyena_conv2d_forward (gated 2-D long convolution, 256 x 256 x 768) instead")
+    ap.add_argument("--conv3d", action="store_true",
+                    help="time hyena_conv3d_forward (gated 3-D long convolution, 32 x 32 x 64 x 768) instead")
     ap.add_argument("--circular", action="store_true",
                     help="time hyena_forward on a circular plan (circular long convolutions) instead")
     ap.add_argument("--per-sample", action="store_true",
@@ -757,8 +776,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.conv2d:
-        bench_conv2d(args, torch)
+    if args.conv2d or args.conv3d:
+        bench_convnd(args, torch, 2 if args.conv2d else 3)
         return
     wl = synth.WORKLOADS[args.workload]
     log(f"[bench] workload {wl.name}: {wl.describe()}")
