@@ -33,7 +33,8 @@ EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_create_ex"
            "hyena_plan2d_create", "hyena_plan2d_destroy", "hyena_spectrum2d_bytes", "hyena_workspace2d_bytes",
            "hyena_filter_spectrum2d", "hyena_conv2d_forward", "hyena_plan3d_create", "hyena_plan3d_destroy",
            "hyena_spectrum3d_bytes", "hyena_workspace3d_bytes", "hyena_filter_spectrum3d", "hyena_conv3d_forward",
-           "hyena_status_string")
+           "hyena_filter_spectrum2d_batched", "hyena_conv2d_forward_per_sample", "hyena_filter_spectrum3d_batched",
+           "hyena_conv3d_forward_per_sample", "hyena_status_string")
 
 
 class FilterMLPStruct(ctypes.Structure):
@@ -128,6 +129,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_filter_spectrum3d.restype = ci
     lib.hyena_conv3d_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hyena_conv3d_forward.restype = ci
+    for nd in ("2d", "3d"):
+        getattr(lib, f"hyena_filter_spectrum{nd}_batched").argtypes = [vp, i64, vp, vp, vp]
+        getattr(lib, f"hyena_filter_spectrum{nd}_batched").restype = ci
+        getattr(lib, f"hyena_conv{nd}_forward_per_sample").argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        getattr(lib, f"hyena_conv{nd}_forward_per_sample").restype = ci
     lib.hyena_status_string.argtypes = [ci]
     lib.hyena_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -454,7 +460,29 @@ class _GridPlan:
                                            _stream_handle(torch, self.device)))
         return out
 
-    def forward(self, v, spec, bias, g=None, x=None, y=None, workspace=None):
+    def spectrum_batched(self, k, out=None):
+        """hyena_filter_spectrum{2d,3d}_batched: k [B, D, *doubled grid] fp32 (a kernel
+        set per sample) -> B spectra in one uint8 device buffer."""
+        torch = self._torch
+        if k.dim() != 2 + len(self.dims):
+            raise ValueError("k must be [B, D, *doubled grid]")
+        B = int(k.shape[0])
+        self._need(k, "k", (B, self.D, *[2 * n for n in self.dims]), torch.float32)
+        if out is None:
+            out = torch.empty(B * self.spectrum_bytes(), dtype=torch.uint8, device=self.device)
+        elif out.numel() * out.element_size() < B * self.spectrum_bytes():
+            raise ValueError("spectrum buffer too small")
+        _check(f"hyena_filter_spectrum{self._SFX}_batched",
+               self._fn("filter_spectrum", "_batched")(self.handle, B, k.data_ptr(), out.data_ptr(),
+                                                       _stream_handle(torch, self.device)))
+        return out
+
+    def forward_per_sample(self, v, spec, bias, g=None, x=None, y=None, workspace=None):
+        """hyena_conv{2d,3d}_forward_per_sample: as forward, with spec holding one
+        spectrum per sample (from spectrum_batched)."""
+        return self.forward(v, spec, bias, g, x, y, workspace, per_sample=True)
+
+    def forward(self, v, spec, bias, g=None, x=None, y=None, workspace=None, per_sample=False):
         """hyena_conv{2d,3d}_forward: v (and the optional gates g, x) [B, D, *grid] -> y."""
         torch = self._torch
         if v.dim() != 2 + len(self.dims):
@@ -466,15 +494,18 @@ class _GridPlan:
             if t is not None:
                 self._need(t, name, shape, self.io_dtype)
         self._need(bias, "bias", (self.D,), torch.float32)
-        if spec.device != self.device or spec.numel() * spec.element_size() < self.spectrum_bytes():
-            raise ValueError(f"spec must come from {type(self).__name__}.spectrum of an equal plan")
+        nspec = B if per_sample else 1
+        if spec.device != self.device or spec.numel() * spec.element_size() < nspec * self.spectrum_bytes():
+            raise ValueError(f"spec must come from {type(self).__name__}.spectrum (spectrum_batched for a kernel "
+                             "set per sample) of an equal plan")
         if y is None:
             y = torch.empty(shape, dtype=self.io_dtype, device=self.device)
         self._need(y, "y", shape, self.io_dtype)
         if workspace is None:
             workspace = torch.empty(self.workspace_bytes(B), dtype=torch.uint8, device=self.device)
-        _check(f"hyena_conv{self._SFX}_forward",
-               getattr(self.lib, f"hyena_conv{self._SFX}_forward")(
+        name = f"hyena_conv{self._SFX}_forward" + ("_per_sample" if per_sample else "")
+        _check(name,
+               getattr(self.lib, name)(
                    self.handle, B, v.data_ptr(), g.data_ptr() if g is not None else None,
                    x.data_ptr() if x is not None else None, spec.data_ptr(), bias.data_ptr(), y.data_ptr(),
                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),

@@ -174,22 +174,29 @@ size_t hyena_workspace2d_bytes(hyena_plan2d_t plan, int64_t B) {
     return (size_t)want * per;
 }
 
-hyena_status_t hyena_filter_spectrum2d(hyena_plan2d_t plan, const float* k, void* spec, hipStream_t stream) {
+hyena_status_t hyena_filter_spectrum2d_batched(hyena_plan2d_t plan, int64_t B, const float* k, void* spec,
+                                               hipStream_t stream) {
     using hy::aligned16;
-    if (!plan || !k || !spec || !aligned16(k) || !aligned16(spec)) return HYENA_ERR_INVALID_ARG;
+    if (!plan || B < 1 || !k || !spec || !aligned16(k) || !aligned16(spec)) return HYENA_ERR_INVALID_ARG;
+    if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 24)) return HYENA_ERR_INVALID_ARG;
     if (hy::check2d(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
     const int W = (int)plan->W;
+    const int64_t n = B * plan->D;  // the B kernel sets are B*D consecutive kernels
     float2* sp = (float2*)spec;
-    hipError_t e = hy::spec_cols(plan->logH, k, sp, plan->tw1, W, plan->D, stream);
+    hipError_t e = hy::spec_cols(plan->logH, k, sp, plan->tw1, W, n, stream);
     if (e == hipSuccess)
         e = hy::rows(plan->logW, 1, sp, nullptr, nullptr, plan->tw2, plan->wpair, hy::PairMap2{(int)plan->H},
-                     (int)plan->H, (int)plan->D, 0, plan->D, stream);
+                     (int)plan->H, (int)plan->D, 0, n, false, stream);
     return e == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
 }
 
-hyena_status_t hyena_conv2d_forward(hyena_plan2d_t plan, int64_t B, const void* v, const void* g, const void* x,
-                                    const void* spec, const float* bias, void* y, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+hyena_status_t hyena_filter_spectrum2d(hyena_plan2d_t plan, const float* k, void* spec, hipStream_t stream) {
+    return hyena_filter_spectrum2d_batched(plan, 1, k, spec, stream);
+}
+
+static hyena_status_t conv2d_impl(hyena_plan2d_t plan, int64_t B, const void* v, const void* g, const void* x,
+                                  const void* spec, const float* bias, void* y, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream, bool per_sample) {
     using hy::aligned16;
     if (!plan || B < 1 || !v || !spec || !bias || !y) return HYENA_ERR_INVALID_ARG;
     if (!aligned16(v) || !aligned16(spec) || !aligned16(bias) || !aligned16(y) || (g && !aligned16(g)) ||
@@ -211,12 +218,24 @@ hyena_status_t hyena_conv2d_forward(hyena_plan2d_t plan, int64_t B, const void* 
         hipError_t e = hy::cols(plan->logH, true, bf16, v, g, nullptr, tile, nullptr, plan->tw1, W, r0, n, stream);
         if (e == hipSuccess)
             e = hy::rows(plan->logW, 0, tile, (const float2*)spec, bias, plan->tw2, plan->wpair,
-                         hy::PairMap2{(int)plan->H}, (int)plan->H, (int)plan->D, r0, n, stream);
+                         hy::PairMap2{(int)plan->H}, (int)plan->H, (int)plan->D, r0, n, per_sample, stream);
         if (e == hipSuccess)
             e = hy::cols(plan->logH, false, bf16, nullptr, nullptr, x, tile, y, plan->tw1, W, r0, n, stream);
         if (e != hipSuccess) return HYENA_ERR_DEVICE;
     }
     return HYENA_OK;
+}
+
+hyena_status_t hyena_conv2d_forward(hyena_plan2d_t plan, int64_t B, const void* v, const void* g, const void* x,
+                                    const void* spec, const float* bias, void* y, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    return conv2d_impl(plan, B, v, g, x, spec, bias, y, workspace, workspace_bytes, stream, false);
+}
+
+hyena_status_t hyena_conv2d_forward_per_sample(hyena_plan2d_t plan, int64_t B, const void* v, const void* g,
+                                               const void* x, const void* spec, const float* bias, void* y,
+                                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return conv2d_impl(plan, B, v, g, x, spec, bias, y, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -186,11 +186,14 @@ size_t hyena_workspace3d_bytes(hyena_plan3d_t plan, int64_t B) {
     return (size_t)want * per;
 }
 
-hyena_status_t hyena_filter_spectrum3d(hyena_plan3d_t plan, const float* k, void* spec, hipStream_t stream) {
+hyena_status_t hyena_filter_spectrum3d_batched(hyena_plan3d_t plan, int64_t B, const float* k, void* spec,
+                                               hipStream_t stream) {
     using hy::aligned16;
-    if (!plan || !k || !spec || !aligned16(k) || !aligned16(spec)) return HYENA_ERR_INVALID_ARG;
+    if (!plan || B < 1 || !k || !spec || !aligned16(k) || !aligned16(spec)) return HYENA_ERR_INVALID_ARG;
+    if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 24)) return HYENA_ERR_INVALID_ARG;
     if (hy::check3d(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
-    const int64_t A2 = 2 * plan->A, H2 = 2 * plan->H, W = plan->W, D = plan->D;
+    // the B kernel sets are B*D consecutive kernels
+    const int64_t A2 = 2 * plan->A, H2 = 2 * plan->H, W = plan->W, D = B * plan->D;
     float2* sp = (float2*)spec;
     // over a: the packed kernel rows [ka][h][m < W] (pitch 2H*W) into spectrum rows of pitch W + 1
     hipError_t e = hy::ccol(plan->logA + 1, hy::kColFwdFull, (const float2*)k, sp, plan->twa, D, (int)(H2 * W),
@@ -202,13 +205,18 @@ hyena_status_t hyena_filter_spectrum3d(hyena_plan3d_t plan, const float* k, void
                      (int)W, (int)W, H2 * (W + 1), W + 1, (int)W, (int)W, stream);
     if (e == hipSuccess)
         e = hy::rows(plan->logW, 1, sp, nullptr, nullptr, plan->tww, plan->wpair,
-                     hy::PairMap3{(int)plan->A, (int)plan->H}, (int)(plan->A * H2), (int)D, 0, D, stream);
+                     hy::PairMap3{(int)plan->A, (int)plan->H}, (int)(plan->A * H2), (int)plan->D, 0, D, false,
+                     stream);
     return e == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
 }
 
-hyena_status_t hyena_conv3d_forward(hyena_plan3d_t plan, int64_t B, const void* v, const void* g, const void* x,
-                                    const void* spec, const float* bias, void* y, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+hyena_status_t hyena_filter_spectrum3d(hyena_plan3d_t plan, const float* k, void* spec, hipStream_t stream) {
+    return hyena_filter_spectrum3d_batched(plan, 1, k, spec, stream);
+}
+
+static hyena_status_t conv3d_impl(hyena_plan3d_t plan, int64_t B, const void* v, const void* g, const void* x,
+                                  const void* spec, const float* bias, void* y, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream, bool per_sample) {
     using hy::aligned16;
     if (!plan || B < 1 || !v || !spec || !bias || !y) return HYENA_ERR_INVALID_ARG;
     if (!aligned16(v) || !aligned16(spec) || !aligned16(bias) || !aligned16(y) || (g && !aligned16(g)) ||
@@ -235,7 +243,8 @@ hyena_status_t hyena_conv3d_forward(hyena_plan3d_t plan, int64_t B, const void* 
                          (int)(W / 2), (int)(W / 2), 2 * HW2, W / 2, (int)(W / 2), (int)(W / 2), stream);
         if (e == hipSuccess)
             e = hy::rows(plan->logW, 0, t2, (const float2*)spec, bias, plan->tww, plan->wpair,
-                         hy::PairMap3{(int)plan->A, (int)H}, (int)(plan->A * 2 * H), (int)plan->D, r0, n, stream);
+                         hy::PairMap3{(int)plan->A, (int)H}, (int)(plan->A * 2 * H), (int)plan->D, r0, n, per_sample,
+                         stream);
         if (e == hipSuccess)
             e = hy::ccol(plan->logH + 1, hy::kColInvHalf, t2, t1, plan->twh, n * A2, (int)(W / 2), 2 * HW2, W / 2,
                          (int)(W / 2), (int)(W / 2), HW2, W / 2, (int)(W / 2), (int)(W / 2), stream);
@@ -244,6 +253,18 @@ hyena_status_t hyena_conv3d_forward(hyena_plan3d_t plan, int64_t B, const void* 
         if (e != hipSuccess) return HYENA_ERR_DEVICE;
     }
     return HYENA_OK;
+}
+
+hyena_status_t hyena_conv3d_forward(hyena_plan3d_t plan, int64_t B, const void* v, const void* g, const void* x,
+                                    const void* spec, const float* bias, void* y, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+    return conv3d_impl(plan, B, v, g, x, spec, bias, y, workspace, workspace_bytes, stream, false);
+}
+
+hyena_status_t hyena_conv3d_forward_per_sample(hyena_plan3d_t plan, int64_t B, const void* v, const void* g,
+                                               const void* x, const void* spec, const float* bias, void* y,
+                                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return conv3d_impl(plan, B, v, g, x, spec, bias, y, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

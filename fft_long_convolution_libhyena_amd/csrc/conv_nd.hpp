@@ -184,11 +184,13 @@ struct PairMap3 {
 //   real spectrum's bins 0..W of both rows, scaled, written over the same rows.
 // The stored spectrum is scaled by 1/(4 * rows * W), rows * W being the complex
 // transform's size, so that the pair step also applies the inverse normalisation.
+// per_sample (MODE 0): image b*D + d reads spectrum b*D + d (a kernel set per
+// sample) instead of spectrum d.
 template <int LOGW, int MODE, class MAP>
 __global__ void __launch_bounds__(C2Row<LOGW>::THREADS)
 k_cnd_row(float2* __restrict__ buf, const float2* __restrict__ spec, const float* __restrict__ bias,
           const float2* __restrict__ tw2, const float2* __restrict__ wpair, MAP map, int D, int64_t row0,
-          int64_t nrows) {
+          int64_t nrows, bool per_sample) {
     using R = C2Row<LOGW>;
     constexpr int W = R::W, T2 = R::T2, U = R::UNITS, RP = R::RP, HW = W / 2;
     __shared__ float2 lds[2 * U * RP];
@@ -230,7 +232,7 @@ k_cnd_row(float2* __restrict__ buf, const float2* __restrict__ spec, const float
     const RowAcc au[2] = {RowAcc{lds + (2 * unit) * RP}, RowAcc{lds + (2 * unit + 1) * RP}};
     const int64_t flat = row0 + r;
     const int d = (int)(flat % D);
-    const float2* S = MODE == 0 ? spec + (int64_t)d * NR * (W + 1) : nullptr;
+    const float2* S = MODE == 0 ? spec + (per_sample ? flat : (int64_t)d) * NR * (W + 1) : nullptr;
     const float nscale = 1.0f / (4.0f * (float)NR * (float)W);
     const float bs = MODE == 0 ? bias[d] * nscale : 0.f;
     const float sc = 0.5f * nscale;  // the unpacked values are twice the spectrum
@@ -346,27 +348,29 @@ inline hipError_t cols(int logH, bool fwd, bool bf16, const void* v, const void*
 
 template <int LOGW, class MAP>
 void launch_rows(int mode, float2* buf, const float2* spec, const float* bias, const float2* tw2,
-                 const float2* wpair, MAP map, int units, int D, int64_t row0, int64_t nrows, hipStream_t st) {
+                 const float2* wpair, MAP map, int units, int D, int64_t row0, int64_t nrows, bool per_sample,
+                 hipStream_t st) {
     using R = C2Row<LOGW>;
     const unsigned grid = (unsigned)xcd_grid(nrows, units / R::UNITS);
     if (mode == 0)
         hipLaunchKernelGGL((k_cnd_row<LOGW, 0, MAP>), dim3(grid), dim3(R::THREADS), 0, st, buf, spec, bias, tw2,
-                           wpair, map, D, row0, nrows);
+                           wpair, map, D, row0, nrows, per_sample);
     else
         hipLaunchKernelGGL((k_cnd_row<LOGW, 1, MAP>), dim3(grid), dim3(R::THREADS), 0, st, buf, spec, bias, tw2,
-                           wpair, map, D, row0, nrows);
+                           wpair, map, D, row0, nrows, false);
 }
 
 // Row pass over W-sample rows (MODE 0: the forward's tile; MODE 1: the spectrum).
 template <class MAP>
 hipError_t rows(int logW, int mode, float2* buf, const float2* spec, const float* bias, const float2* tw2,
-                const float2* wpair, MAP map, int units, int D, int64_t row0, int64_t nrows, hipStream_t st) {
+                const float2* wpair, MAP map, int units, int D, int64_t row0, int64_t nrows, bool per_sample,
+                hipStream_t st) {
     switch (logW) {
-        case 5: launch_rows<5>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, st); break;
-        case 6: launch_rows<6>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, st); break;
-        case 7: launch_rows<7>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, st); break;
-        case 8: launch_rows<8>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, st); break;
-        case 9: launch_rows<9>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, st); break;
+        case 5: launch_rows<5>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, st); break;
+        case 6: launch_rows<6>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, st); break;
+        case 7: launch_rows<7>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, st); break;
+        case 8: launch_rows<8>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, st); break;
+        case 9: launch_rows<9>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -399,6 +399,18 @@ hyena_status_t hyena_conv2d_forward(hyena_plan2d_t plan, int64_t B, const void* 
                                     const void* spec, const float* bias, void* y, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
 
+/* Input-dependent kernels (the HyenaND summary's methodology: a kernel set per
+ * input sample): hyena_filter_spectrum2d for B kernel sets at once,
+ *   k    [B][D][2H][2W] fp32, device; spec: B * hyena_spectrum2d_bytes(plan) bytes,
+ *        sample b's spectrum at byte b * hyena_spectrum2d_bytes(plan),
+ * and the forward in which image (b, d) uses sample b's kernel d (bias shared).
+ * Errors as the calls above; HYENA_ERR_INVALID_ARG also for B < 1 or B*D > 2^24. */
+hyena_status_t hyena_filter_spectrum2d_batched(hyena_plan2d_t plan, int64_t B, const float* k, void* spec,
+                                               hipStream_t stream);
+hyena_status_t hyena_conv2d_forward_per_sample(hyena_plan2d_t plan, int64_t B, const void* v, const void* g,
+                                               const void* x, const void* spec, const float* bias, void* y,
+                                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * 3-D long convolution: the 2-D step above with one more grid axis (HyenaND
  * summary, methodology: the N-d FFT convolution on the native grid, zero-padded
@@ -453,6 +465,15 @@ hyena_status_t hyena_filter_spectrum3d(hyena_plan3d_t plan, const float* k, void
 hyena_status_t hyena_conv3d_forward(hyena_plan3d_t plan, int64_t B, const void* v, const void* g, const void* x,
                                     const void* spec, const float* bias, void* y, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream);
+
+/* A kernel set per input sample, as for 2-D: k [B][D][2A][2H][2W] fp32 gives B
+ * spectra of hyena_spectrum3d_bytes(plan) bytes each; volume (b, d) uses sample
+ * b's kernel d. */
+hyena_status_t hyena_filter_spectrum3d_batched(hyena_plan3d_t plan, int64_t B, const float* k, void* spec,
+                                               hipStream_t stream);
+hyena_status_t hyena_conv3d_forward_per_sample(hyena_plan3d_t plan, int64_t B, const void* v, const void* g,
+                                               const void* x, const void* spec, const float* bias, void* y,
+                                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* hyena_status_string(hyena_status_t s);

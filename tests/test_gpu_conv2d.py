@@ -127,3 +127,53 @@ def test_conv2d_error_paths():
             p.forward(v[:, :1].contiguous(), spec, bias)
         with pytest.raises(ValueError):
             p.spectrum(torch.from_numpy(inp.k[:, :32]).contiguous().cuda())
+
+
+def _kernel_sets(B, D, dims, seed, nd):
+    """B seeded kernel sets [B, D, *doubled grid] (sample b drawn with seed + b)."""
+    make = synth.conv2d_inputs if nd == 2 else synth.conv3d_inputs
+    return np.stack([make(1, D, *dims, seed=seed + b).k for b in range(B)])
+
+
+@pytest.mark.parametrize("B,D,H,W,dtype", [(3, 2, 32, 64, "f32"), (2, 3, 64, 32, "bf16")])
+def test_conv2d_per_sample_matches_oracle(B, D, H, W, dtype):
+    """A kernel set per sample (input-dependent kernels): image (b, d) uses kernel
+    d of sample b."""
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan2D
+
+    inp = synth.conv2d_inputs(B, D, H, W, dtype, seed=21)
+    kb = _kernel_sets(B, D, (H, W), 300, 2)
+    with Plan2D(H, W, D, dtype) as p:
+        spec = p.spectrum_batched(torch.from_numpy(kb).cuda())
+        y = p.forward_per_sample(_dev(inp.v, dtype), spec, torch.from_numpy(inp.bias).cuda(),
+                                 g=_dev(inp.g, dtype), x=_dev(inp.x, dtype))
+        torch.cuda.synchronize()
+    ref = np.concatenate([oracle.conv2d_forward(inp.v[b:b + 1], kb[b], inp.bias, inp.g[b:b + 1], inp.x[b:b + 1])
+                          for b in range(B)])
+    got = y.float().cpu().numpy().astype(np.float64)
+    err = oracle.rel_l2(got, ref)
+    per = [oracle.rel_l2(got[b], ref[b]) for b in range(B)]
+    bound = 1e-2 if dtype == "bf16" else 1e-4
+    say(f"[conv2d per-sample] B={B} D={D} {H}x{W} {dtype}: rel_l2 {err:.3e}, per sample {max(per):.2e}")
+    assert err <= bound and max(per) <= 10 * bound
+
+
+def test_conv2d_equal_kernel_sets_reproduce_the_shared_step():
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan2D
+
+    B, D, H, W = 3, 2, 32, 32
+    inp = synth.conv2d_inputs(B, D, H, W, seed=22)
+    kb = np.repeat(inp.k[None], B, axis=0)
+    with Plan2D(H, W, D) as p:
+        v, g, x = (torch.from_numpy(a).cuda() for a in (inp.v, inp.g, inp.x))
+        bias = torch.from_numpy(inp.bias).cuda()
+        a = p.forward_per_sample(v, p.spectrum_batched(torch.from_numpy(kb).cuda()), bias, g=g, x=x)
+        b = p.forward(v, p.spectrum(torch.from_numpy(inp.k).cuda()), bias, g=g, x=x)
+        torch.cuda.synchronize()
+        with pytest.raises(ValueError):  # one spectrum is too small for B = 3
+            p.forward_per_sample(v, p.spectrum(torch.from_numpy(inp.k).cuda()), bias)
+    assert bool((a == b).all())
