@@ -207,7 +207,7 @@ def forward_circular(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bia
 
 
 def conv2d_forward(v: np.ndarray, k: np.ndarray, bias: np.ndarray, g: Optional[np.ndarray] = None,
-                   x: Optional[np.ndarray] = None, mode: str = "fft") -> np.ndarray:
+                   x: Optional[np.ndarray] = None, mode: str = "fft", circular: bool = False) -> np.ndarray:
     """One gated 2-D long-convolution step in fp64 (HyenaND summary, methodology:
     global convolution on the native N-d grid, evaluated by N-d FFT, the input
     zero-padded to double the grid in every dimension for the non-circular mode).
@@ -218,15 +218,28 @@ def conv2d_forward(v: np.ndarray, k: np.ndarray, bias: np.ndarray, g: Optional[n
     p < H, q < W, s_pad being s zero-padded to 2H x 2W; y = (c + bias * s) * x (no
     factor when x is None). ``direct`` is that sum written out; ``fft`` multiplies
     numpy's rfft2 of the padded input and of the kernel and inverts.
+    ``circular`` (the summary's boundary handling for periodic systems): no padding,
+    k [D, H, W] on the grid itself, c[p, q] = sum_{i < H, j < W} k[i, j]
+    s[(p - i) mod H, (q - j) mod W].
     Returns [B, D, H, W] float64."""
     s = np.asarray(v, dtype=np.float64)
     if g is not None:
         s = s * np.asarray(g, dtype=np.float64)
     B, D, H, W = s.shape
     kk = np.asarray(k, dtype=np.float64)
-    if kk.shape != (D, 2 * H, 2 * W):
+    if circular:
+        if kk.shape != (D, H, W):
+            raise ValueError("k must be [D, H, W] for a circular step")
+        if mode == "direct":
+            c = np.zeros((B, D, H, W))
+            for i in range(H):
+                for j in range(W):
+                    c += kk[None, :, i, j, None, None] * np.roll(s, (i, j), axis=(2, 3))
+        else:
+            c = np.fft.irfft2(np.fft.rfft2(s) * np.fft.rfft2(kk)[None], s=(H, W))
+    elif kk.shape != (D, 2 * H, 2 * W):
         raise ValueError("k must be [D, 2H, 2W]")
-    if mode == "direct":
+    elif mode == "direct":
         sp = np.zeros((B, D, 2 * H, 2 * W))
         sp[:, :, :H, :W] = s
         c = np.zeros((B, D, H, W))
@@ -246,7 +259,7 @@ def conv2d_forward(v: np.ndarray, k: np.ndarray, bias: np.ndarray, g: Optional[n
 
 
 def conv3d_forward(v: np.ndarray, k: np.ndarray, bias: np.ndarray, g: Optional[np.ndarray] = None,
-                   x: Optional[np.ndarray] = None, mode: str = "fft") -> np.ndarray:
+                   x: Optional[np.ndarray] = None, mode: str = "fft", circular: bool = False) -> np.ndarray:
     """One gated 3-D long-convolution step in fp64: ``conv2d_forward`` with one more
     grid axis (HyenaND summary, methodology: global convolution on the native N-d
     grid by an N-d FFT, the input zero-padded to double the grid in every dimension
@@ -257,15 +270,29 @@ def conv3d_forward(v: np.ndarray, k: np.ndarray, bias: np.ndarray, g: Optional[n
                    s_pad[(a - l) mod 2A, (p - i) mod 2H, (q - j) mod 2W],
     a < A, p < H, q < W; y = (c + bias * s) * x. ``direct`` is that sum written out;
     ``fft`` multiplies numpy's rfftn of the padded input and of the kernel.
+    ``circular``: no padding, k [D, A, H, W] on the grid itself, every index taken
+    modulo its own axis length.
     Returns [B, D, A, H, W] float64."""
     s = np.asarray(v, dtype=np.float64)
     if g is not None:
         s = s * np.asarray(g, dtype=np.float64)
     B, D, A, H, W = s.shape
     kk = np.asarray(k, dtype=np.float64)
-    if kk.shape != (D, 2 * A, 2 * H, 2 * W):
+    if circular:
+        if kk.shape != (D, A, H, W):
+            raise ValueError("k must be [D, A, H, W] for a circular step")
+        if mode == "direct":
+            c = np.zeros((B, D, A, H, W))
+            for l in range(A):
+                for i in range(H):
+                    for j in range(W):
+                        c += kk[None, :, l, i, j, None, None, None] * np.roll(s, (l, i, j), axis=(2, 3, 4))
+        else:
+            c = np.fft.irfftn(np.fft.rfftn(s, axes=(2, 3, 4)) * np.fft.rfftn(kk, axes=(1, 2, 3))[None],
+                              s=(A, H, W), axes=(2, 3, 4))
+    elif kk.shape != (D, 2 * A, 2 * H, 2 * W):
         raise ValueError("k must be [D, 2A, 2H, 2W]")
-    if mode == "direct":
+    elif mode == "direct":
         sp = np.zeros((B, D, 2 * A, 2 * H, 2 * W))
         sp[:, :, :A, :H, :W] = s
         c = np.zeros((B, D, A, H, W))

@@ -80,3 +80,51 @@ def test_rejects_a_kernel_not_on_the_doubled_grid():
     v, g, x, k, bias = _inputs()
     with pytest.raises(ValueError):
         oracle.conv2d_forward(v, k[:, :4], bias)
+
+
+# ---------------------------------------------------------------- circular mode
+
+@pytest.mark.parametrize("H,W", [(1, 1), (2, 4), (4, 8), (8, 2), (3, 5)])
+def test_circular_direct_and_fft_agree(H, W):
+    v, g, x, _, bias = _inputs(H=H, W=W, seed=H * 7 + W)
+    k = np.random.default_rng(H + W).standard_normal((v.shape[1], H, W))
+    a = oracle.conv2d_forward(v, k, bias, g, x, mode="direct", circular=True)
+    b = oracle.conv2d_forward(v, k, bias, g, x, mode="fft", circular=True)
+    assert np.allclose(a, b, rtol=1e-11, atol=1e-11)
+
+
+def test_circular_single_row_is_the_1d_circular_convolution():
+    """H = 1: each image row is the separately pinned 1-D circular convolution."""
+    v, _, _, _, _ = _inputs(H=1, W=16, seed=8)
+    k = np.random.default_rng(9).standard_normal((v.shape[1], 1, 16))
+    y = oracle.conv2d_forward(v, k, np.zeros(v.shape[1]), mode="direct", circular=True)
+    for b in range(v.shape[0]):
+        for d in range(v.shape[1]):
+            assert np.allclose(y[b, d, 0], oracle.circular_conv(v[b, d, 0], k[d, 0], "direct"), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_circular_step_on_the_doubled_grid_is_the_zero_padded_step():
+    """The zero-padded step is the circular step on the doubled grid of the padded
+    image, truncated: this ties the two modes' kernel conventions together."""
+    v, g, x, k, bias = _inputs(H=4, W=8, seed=10)
+    B, D, H, W = v.shape
+    pad = np.zeros((B, D, 2 * H, 2 * W))
+    pad[:, :, :H, :W] = v * g
+    xp = np.ones((B, D, 2 * H, 2 * W))
+    xp[:, :, :H, :W] = x
+    y = oracle.conv2d_forward(pad, k, bias, None, xp, mode="direct", circular=True)[:, :, :H, :W]
+    want = oracle.conv2d_forward(v, k, bias, g, x, mode="direct")
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-12)
+
+
+def test_circular_shift_kernel_wraps_around():
+    v, _, _, _, _ = _inputs(B=1, D=1, H=4, W=8, seed=11)
+    k = np.zeros((1, 4, 8))
+    k[0, 1, 0] = 1.0  # one row forward: the last row comes back as the first
+    y = oracle.conv2d_forward(v, k, np.zeros(1), mode="fft", circular=True)
+    assert np.allclose(y, np.roll(v, 1, axis=2), rtol=1e-12, atol=1e-12)
+    k[:] = 0.0
+    k[0, 0, 7] = 1.0  # one column back, wrapped
+    y = oracle.conv2d_forward(v, k, np.zeros(1), mode="fft", circular=True)
+    assert np.allclose(y, np.roll(v, -1, axis=3), rtol=1e-12, atol=1e-12)

@@ -84,3 +84,43 @@ def test_shift_kernels_move_the_input_by_one_step(mode, axis):
             dst[2 + axis], src[2 + axis] = slice(0, n - 1), slice(1, None)
         want[tuple(dst)] = v[tuple(src)]
         assert np.allclose(y, want, rtol=1e-12, atol=1e-12), (axis, off)
+
+
+# ---------------------------------------------------------------- circular mode
+
+@pytest.mark.parametrize("A,H,W", [(1, 1, 1), (2, 2, 4), (4, 2, 2), (3, 2, 5)])
+def test_circular_direct_and_fft_agree(A, H, W):
+    v, g, x, _, bias = _inputs(A=A, H=H, W=W, seed=A * 50 + H * 7 + W)
+    k = np.random.default_rng(A + H + W).standard_normal((v.shape[1], A, H, W))
+    a = oracle.conv3d_forward(v, k, bias, g, x, mode="direct", circular=True)
+    b = oracle.conv3d_forward(v, k, bias, g, x, mode="fft", circular=True)
+    assert np.allclose(a, b, rtol=1e-11, atol=1e-11)
+
+
+def test_circular_first_slice_kernel_is_the_circular_2d_step_on_every_slice():
+    v, g, x, _, bias = _inputs(A=3, H=4, W=8, seed=13)
+    k = np.zeros((v.shape[1], 3, 4, 8))
+    k[:, 0] = np.random.default_rng(14).standard_normal((v.shape[1], 4, 8))
+    y = oracle.conv3d_forward(v, k, bias, g, x, mode="direct", circular=True)
+    for a in range(3):
+        want = oracle.conv2d_forward(v[:, :, a], k[:, 0], bias, g[:, :, a], x[:, :, a], mode="direct",
+                                     circular=True)
+        assert np.allclose(y[:, :, a], want, rtol=1e-12, atol=1e-12)
+
+
+def test_circular_step_on_the_doubled_grid_is_the_zero_padded_step():
+    v, g, x, k, bias = _inputs(A=2, H=4, W=4, seed=15)
+    B, D, A, H, W = v.shape
+    pad = np.zeros((B, D, 2 * A, 2 * H, 2 * W))
+    pad[:, :, :A, :H, :W] = v * g
+    y = oracle.conv3d_forward(pad, k, bias, mode="fft", circular=True)[:, :, :A, :H, :W] * x
+    want = oracle.conv3d_forward(v, k, bias, g, x, mode="direct")
+    assert np.allclose(y, want, rtol=1e-11, atol=1e-11)
+
+
+def test_circular_depth_shift_wraps_around():
+    v, _, _, _, _ = _inputs(B=1, D=1, A=4, H=2, W=4, seed=16)
+    k = np.zeros((1, 4, 2, 4))
+    k[0, 1, 0, 0] = 1.0
+    y = oracle.conv3d_forward(v, k, np.zeros(1), mode="fft", circular=True)
+    assert np.allclose(y, np.roll(v, 1, axis=2), rtol=1e-12, atol=1e-12)
