@@ -664,15 +664,22 @@ def bench_convnd(args, torch, nd: int):
 
     B, D = 1, 768
     dims = (256, 256) if nd == 2 else (32, 32, 64)
+    circ = bool(args.circular)
     dev = torch.device("cuda", 0)
     if nd == 2:
         inp = synth.conv2d_inputs(B, D, *dims, seed=3)
-        plan = Plan2D(*dims, D)
-        ref_fn = oracle.conv2d_forward
+        plan = Plan2D(*dims, D, circular=circ)
+        base_fn = oracle.conv2d_forward
     else:
         inp = synth.conv3d_inputs(B, D, *dims, seed=3)
-        plan = Plan3D(*dims, D)
-        ref_fn = oracle.conv3d_forward
+        plan = Plan3D(*dims, D, circular=circ)
+        base_fn = oracle.conv3d_forward
+    if circ:  # a kernel on the grid itself: the leading corner of the doubled-grid draw
+        inp.k = np.ascontiguousarray(inp.k[(slice(None),) + tuple(slice(0, n) for n in dims)])
+
+    def ref_fn(*a):
+        return base_fn(*a, circular=circ)
+
     spec = plan.spectrum(torch.from_numpy(inp.k).to(dev))
     v, g, x = (torch.from_numpy(a).to(dev) for a in (inp.v, inp.g, inp.x))
     bias = torch.from_numpy(inp.bias).to(dev)
@@ -694,17 +701,22 @@ def bench_convnd(args, torch, nd: int):
         log(f"[bench] rep {rep}: {times[-1] * 1e3:.1f} us/step")
     ms = float(np.median(times))
     pts = int(np.prod(dims))
-    spec_bins = int(np.prod([2 * n for n in dims[:-1]])) * (dims[-1] + 1)
+    if circ:
+        spec_bins = int(np.prod(dims[:-1])) * (dims[-1] // 2 + 1)
+    else:
+        spec_bins = int(np.prod([2 * n for n in dims[:-1]])) * (dims[-1] + 1)
     nbytes = 4 * 4 * B * D * pts + 8 * D * spec_bins + 4 * D
     achieved = nbytes / (ms * 1e-3) / 1e9
     grid = "x".join(str(n) for n in dims)
     names = "B·D·H·W" if nd == 2 else "B·D·A·H·W"
     out = {
-        "metric": f"channel-tokens/s ({names}/s) and % HBM peak, gated {nd}-D long convolution (grid doubled)",
+        "metric": f"channel-tokens/s ({names}/s) and % HBM peak, gated {nd}-D long convolution "
+                  + ("(circular)" if circ else "(grid doubled)"),
         "value": B * D * pts / (ms * 1e-3), "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic seeded (N(0,1) grids and gates, centred decaying random kernels)",
-        "config": {"workload": f"conv{nd}d {grid}", "B": B, "D": D, "grid": list(dims), "pass": f"conv{nd}d_forward"},
+        "config": {"workload": f"conv{nd}d {grid}" + (" circular" if circ else ""), "B": B, "D": D,
+                   "grid": list(dims), "pass": f"conv{nd}d_forward"},
         "hbm_frac_forward": round(achieved / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
@@ -755,7 +767,8 @@ def main():
     ap.add_argument("--conv3d", action="store_true",
                     help="time hyena_conv3d_forward (gated 3-D long convolution, 32 x 32 x 64 x 768) instead")
     ap.add_argument("--circular", action="store_true",
-                    help="time hyena_forward on a circular plan (circular long convolutions) instead")
+                    help="time hyena_forward on a circular plan (circular long convolutions) instead; with "
+                         "--conv2d or --conv3d, a circular N-d plan")
     ap.add_argument("--per-sample", action="store_true",
                     help="time hyena_forward_per_sample (a filter set per sample) instead")
     ap.add_argument("--filter", action="store_true",
@@ -776,7 +789,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.conv2d or args.conv3d:
+    if args.conv2d or args.conv3d:  # with --circular: a circular N-d plan
         bench_convnd(args, torch, 2 if args.conv2d else 3)
         return
     wl = synth.WORKLOADS[args.workload]

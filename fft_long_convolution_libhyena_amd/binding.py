@@ -34,7 +34,8 @@ EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_create_ex"
            "hyena_filter_spectrum2d", "hyena_conv2d_forward", "hyena_plan3d_create", "hyena_plan3d_destroy",
            "hyena_spectrum3d_bytes", "hyena_workspace3d_bytes", "hyena_filter_spectrum3d", "hyena_conv3d_forward",
            "hyena_filter_spectrum2d_batched", "hyena_conv2d_forward_per_sample", "hyena_filter_spectrum3d_batched",
-           "hyena_conv3d_forward_per_sample", "hyena_status_string")
+           "hyena_conv3d_forward_per_sample", "hyena_plan2d_create_ex", "hyena_plan3d_create_ex",
+           "hyena_status_string")
 
 
 class FilterMLPStruct(ctypes.Structure):
@@ -129,6 +130,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_filter_spectrum3d.restype = ci
     lib.hyena_conv3d_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hyena_conv3d_forward.restype = ci
+    lib.hyena_plan2d_create_ex.argtypes = [ctypes.POINTER(vp), i64, i64, i64, ci, ctypes.c_uint32]
+    lib.hyena_plan2d_create_ex.restype = ci
+    lib.hyena_plan3d_create_ex.argtypes = [ctypes.POINTER(vp), i64, i64, i64, i64, ci, ctypes.c_uint32]
+    lib.hyena_plan3d_create_ex.restype = ci
     for nd in ("2d", "3d"):
         getattr(lib, f"hyena_filter_spectrum{nd}_batched").argtypes = [vp, i64, vp, vp, vp]
         getattr(lib, f"hyena_filter_spectrum{nd}_batched").restype = ci
@@ -417,19 +422,25 @@ class _GridPlan:
     I/O dtype "f32" or "bf16"; the C calls are hyena_plan{2d,3d}_create, ... ."""
     _SFX = ""
 
-    def __init__(self, dims, D: int, dtype: str = "f32"):
+    def __init__(self, dims, D: int, dtype: str = "f32", circular: bool = False):
         import torch
 
         self._torch = torch
         self.lib = load_library()
         self.dims, self.D, self.dtype = tuple(int(n) for n in dims), int(D), dtype
+        self.circular = bool(circular)
         if dtype not in _DTYPES:
             raise ValueError(f"dtype must be one of {list(_DTYPES)}")
         self.device = torch.device("cuda", torch.cuda.current_device())
         h = ctypes.c_void_p()
-        name = f"hyena_plan{self._SFX}_create"
-        _check(name, getattr(self.lib, name)(ctypes.byref(h), *self.dims, self.D, _DTYPES[dtype]))
+        name = f"hyena_plan{self._SFX}_create_ex"
+        _check(name, getattr(self.lib, name)(ctypes.byref(h), *self.dims, self.D, _DTYPES[dtype],
+                                             FLAG_CIRCULAR if self.circular else 0))
         self.handle = h
+
+    def kernel_shape(self):
+        """Per-channel kernel grid: the doubled grid, or the grid itself when circular."""
+        return tuple(self.dims) if self.circular else tuple(2 * n for n in self.dims)
 
     def _fn(self, stem, tail=""):
         return getattr(self.lib, f"hyena_{stem}{self._SFX}{tail}")
@@ -448,9 +459,9 @@ class _GridPlan:
         Plan._need(self, t, name, shape, dtype)
 
     def spectrum(self, k, out=None):
-        """hyena_filter_spectrum{2d,3d}: k [D, *doubled grid] fp32 -> opaque uint8 device buffer."""
+        """hyena_filter_spectrum{2d,3d}: k [D, *kernel grid] fp32 -> opaque uint8 device buffer."""
         torch = self._torch
-        self._need(k, "k", (self.D, *[2 * n for n in self.dims]), torch.float32)
+        self._need(k, "k", (self.D, *self.kernel_shape()), torch.float32)
         if out is None:
             out = torch.empty(self.spectrum_bytes(), dtype=torch.uint8, device=self.device)
         elif out.numel() * out.element_size() < self.spectrum_bytes():
@@ -467,7 +478,7 @@ class _GridPlan:
         if k.dim() != 2 + len(self.dims):
             raise ValueError("k must be [B, D, *doubled grid]")
         B = int(k.shape[0])
-        self._need(k, "k", (B, self.D, *[2 * n for n in self.dims]), torch.float32)
+        self._need(k, "k", (B, self.D, *self.kernel_shape()), torch.float32)
         if out is None:
             out = torch.empty(B * self.spectrum_bytes(), dtype=torch.uint8, device=self.device)
         elif out.numel() * out.element_size() < B * self.spectrum_bytes():
@@ -535,9 +546,9 @@ class Plan2D(_GridPlan):
     long convolution of include/hyena.h)."""
     _SFX = "2d"
 
-    def __init__(self, H: int, W: int, D: int, dtype: str = "f32"):
+    def __init__(self, H: int, W: int, D: int, dtype: str = "f32", circular: bool = False):
         self.H, self.W = int(H), int(W)
-        super().__init__((H, W), D, dtype)
+        super().__init__((H, W), D, dtype, circular)
 
 
 class Plan3D(_GridPlan):
@@ -545,6 +556,6 @@ class Plan3D(_GridPlan):
     3-D long convolution of include/hyena.h)."""
     _SFX = "3d"
 
-    def __init__(self, A: int, H: int, W: int, D: int, dtype: str = "f32"):
+    def __init__(self, A: int, H: int, W: int, D: int, dtype: str = "f32", circular: bool = False):
         self.A, self.H, self.W = int(A), int(H), int(W)
-        super().__init__((A, H, W), D, dtype)
+        super().__init__((A, H, W), D, dtype, circular)

@@ -23,7 +23,10 @@
 // [2H][W+1] bins of the doubled-grid real transform (numpy's rfft2 layout),
 // scaled by 1/(4 * 2H * W) so that the pair step also applies the inverse
 // normalisation, like the 1-D path's spectrum.
-// The pass kernels are shared with the 3-D step (conv_nd.hpp).
+// The pass kernels are shared with the 3-D step (conv_nd.hpp). A circular plan
+// (periodic grid, kernel on the H x W grid itself) runs the same passes on
+// transforms of the grid's own size: columns of length H, rows of W/2 packed
+// points, nothing pruned and every output kept.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,6 +41,10 @@
 struct hyena_plan2d_s {
     int64_t H = 0, W = 0, D = 0;
     int logH = 0, logW = 0;
+    bool circular = false;
+    // transform geometry: column transforms of 2^(lc+1) points, row transforms of
+    // 2^lr packed points, rows paired as PairMap2{pm}
+    int lc = 0, lr = 0, pm = 0;
     hyena_dtype_t dtype = HYENA_F32;
     int device = -1;
     float2* dtab = nullptr;
@@ -111,20 +118,26 @@ hyena_status_t check2d(const hyena_plan2d_t plan) {
 
 extern "C" {
 
-hyena_status_t hyena_plan2d_create(hyena_plan2d_t* out, int64_t H, int64_t W, int64_t D, hyena_dtype_t dtype) {
+hyena_status_t hyena_plan2d_create_ex(hyena_plan2d_t* out, int64_t H, int64_t W, int64_t D, hyena_dtype_t dtype,
+                                      uint32_t flags) {
     if (!out) return HYENA_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)HYENA_FLAG_CIRCULAR) return HYENA_ERR_INVALID_ARG;
     if (H < 1 || W < 1 || D < 1) return HYENA_ERR_INVALID_ARG;
     if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
     if (!hy::pow2(H) || !hy::pow2(W) || D > (int64_t(1) << 24)) return HYENA_ERR_UNSUPPORTED;
+    const bool circ = (flags & HYENA_FLAG_CIRCULAR) != 0;
     const int logH = hy::log2i(H), logW = hy::log2i(W);
-    if (logH < hy::kC2MinLogH || logH > hy::kC2MaxLogH || logW < hy::kC2MinLogW || logW > hy::kC2MaxLogW)
+    // circular: transforms of the grid's own size (H columns, W/2 packed points)
+    const int lc = circ ? logH - 1 : logH, lr = circ ? logW - 1 : logW;
+    if (lc < hy::kC2MinLogH || lc > hy::kC2MaxLogH || lr < hy::kC2MinLogW || lr > hy::kC2MaxLogW)
         return HYENA_ERR_UNSUPPORTED;
+    const int64_t Wr = int64_t(1) << lr;  // packed row transform length
     std::vector<float2> tab;
-    hy::append_stockham(tab, logH + 1);
+    hy::append_stockham(tab, lc + 1);
     const size_t o_tw2 = tab.size();
-    hy::append_stockham(tab, logW);
+    hy::append_stockham(tab, lr);
     const size_t o_wp = tab.size();
-    for (int64_t k = 0; k < W; ++k) tab.push_back(hy::wfwd(k, 2 * W));
+    for (int64_t k = 0; k < Wr; ++k) tab.push_back(hy::wfwd(k, 2 * Wr));
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return HYENA_ERR_DEVICE;
     float2* dtab = nullptr;
@@ -143,6 +156,10 @@ hyena_status_t hyena_plan2d_create(hyena_plan2d_t* out, int64_t H, int64_t W, in
     plan->D = D;
     plan->logH = logH;
     plan->logW = logW;
+    plan->circular = circ;
+    plan->lc = lc;
+    plan->lr = lr;
+    plan->pm = circ ? (int)(H / 2) : (int)H;
     plan->dtype = dtype;
     plan->device = dev;
     plan->dtab = dtab;
@@ -151,6 +168,10 @@ hyena_status_t hyena_plan2d_create(hyena_plan2d_t* out, int64_t H, int64_t W, in
     plan->wpair = dtab + o_wp;
     *out = plan;
     return HYENA_OK;
+}
+
+hyena_status_t hyena_plan2d_create(hyena_plan2d_t* out, int64_t H, int64_t W, int64_t D, hyena_dtype_t dtype) {
+    return hyena_plan2d_create_ex(out, H, W, D, dtype, 0);
 }
 
 hyena_status_t hyena_plan2d_destroy(hyena_plan2d_t plan) {
@@ -162,12 +183,17 @@ hyena_status_t hyena_plan2d_destroy(hyena_plan2d_t plan) {
 
 size_t hyena_spectrum2d_bytes(hyena_plan2d_t plan) {
     if (!plan) return 0;
-    return (size_t)plan->D * (size_t)(2 * plan->H) * (size_t)(plan->W + 1) * sizeof(float2);
+    return (size_t)plan->D * ((size_t)2 << plan->lc) * (((size_t)1 << plan->lr) + 1) * sizeof(float2);
+}
+
+// the tile of one image: the column transform's rows x W/2 packed columns
+static size_t tile2d_bytes(const hyena_plan2d_t plan) {
+    return ((size_t)2 << plan->lc) * (size_t)(plan->W / 2) * sizeof(float2);
 }
 
 size_t hyena_workspace2d_bytes(hyena_plan2d_t plan, int64_t B) {
     if (!plan || B < 1) return 0;
-    const size_t per = (size_t)plan->H * (size_t)plan->W * sizeof(float2);  // 2H x W/2 complex
+    const size_t per = tile2d_bytes(plan);
     int64_t want = (int64_t)(hy::kC2ChunkBytes / per);
     if (want < 1) want = 1;
     if (want > B * plan->D) want = B * plan->D;
@@ -180,13 +206,13 @@ hyena_status_t hyena_filter_spectrum2d_batched(hyena_plan2d_t plan, int64_t B, c
     if (!plan || B < 1 || !k || !spec || !aligned16(k) || !aligned16(spec)) return HYENA_ERR_INVALID_ARG;
     if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 24)) return HYENA_ERR_INVALID_ARG;
     if (hy::check2d(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
-    const int W = (int)plan->W;
     const int64_t n = B * plan->D;  // the B kernel sets are B*D consecutive kernels
     float2* sp = (float2*)spec;
-    hipError_t e = hy::spec_cols(plan->logH, k, sp, plan->tw1, W, n, stream);
+    // kernel rows of 2^(lr+1) samples (2W zero-padded, W circular)
+    hipError_t e = hy::spec_cols(plan->lc, k, sp, plan->tw1, 1 << plan->lr, n, stream);
     if (e == hipSuccess)
-        e = hy::rows(plan->logW, 1, sp, nullptr, nullptr, plan->tw2, plan->wpair, hy::PairMap2{(int)plan->H},
-                     (int)plan->H, (int)plan->D, 0, n, false, stream);
+        e = hy::rows(plan->lr, 1, sp, nullptr, nullptr, plan->tw2, plan->wpair, hy::PairMap2{plan->pm}, plan->pm,
+                     (int)plan->D, 0, n, false, stream);
     return e == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
 }
 
@@ -203,7 +229,7 @@ static hyena_status_t conv2d_impl(hyena_plan2d_t plan, int64_t B, const void* v,
         (x && !aligned16(x)))
         return HYENA_ERR_INVALID_ARG;
     if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 24)) return HYENA_ERR_INVALID_ARG;
-    const size_t per = (size_t)plan->H * (size_t)plan->W * sizeof(float2);
+    const size_t per = tile2d_bytes(plan);
     if (!workspace || !aligned16(workspace) || workspace_bytes < per) return HYENA_ERR_WORKSPACE;
     if (hy::check2d(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
     const int64_t nr = B * plan->D;
@@ -215,12 +241,14 @@ static hyena_status_t conv2d_impl(hyena_plan2d_t plan, int64_t B, const void* v,
     float2* tile = (float2*)workspace;
     for (int64_t r0 = 0; r0 < nr; r0 += chunk) {
         const int64_t n = nr - r0 < chunk ? nr - r0 : chunk;
-        hipError_t e = hy::cols(plan->logH, true, bf16, v, g, nullptr, tile, nullptr, plan->tw1, W, r0, n, stream);
+        const bool circ = plan->circular;
+        hipError_t e =
+            hy::cols(plan->lc, true, bf16, v, g, nullptr, tile, nullptr, plan->tw1, W, r0, n, stream, circ);
         if (e == hipSuccess)
-            e = hy::rows(plan->logW, 0, tile, (const float2*)spec, bias, plan->tw2, plan->wpair,
-                         hy::PairMap2{(int)plan->H}, (int)plan->H, (int)plan->D, r0, n, per_sample, stream);
+            e = hy::rows(plan->lr, 0, tile, (const float2*)spec, bias, plan->tw2, plan->wpair, hy::PairMap2{plan->pm},
+                         plan->pm, (int)plan->D, r0, n, per_sample, stream, circ);
         if (e == hipSuccess)
-            e = hy::cols(plan->logH, false, bf16, nullptr, nullptr, x, tile, y, plan->tw1, W, r0, n, stream);
+            e = hy::cols(plan->lc, false, bf16, nullptr, nullptr, x, tile, y, plan->tw1, W, r0, n, stream, circ);
         if (e != hipSuccess) return HYENA_ERR_DEVICE;
     }
     return HYENA_OK;

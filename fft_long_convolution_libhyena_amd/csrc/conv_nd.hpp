@@ -44,12 +44,15 @@ struct C2Row {
 // First column pass of an image of H rows of W real samples: column FFTs (length
 // 2H, first radix pass pruned) of the packed gated image; tile row kh, column
 // m < W/2. (3-D: H is the depth axis and W the flattened H x W plane.)
-template <int LOGH, class TIO>
+// CIRC (circular mode): the image has 2H rows, all transformed (no padding).
+template <int LOGH, class TIO, bool CIRC = false>
 __global__ void __launch_bounds__(C2Col<LOGH>::THREADS)
 k_c2_colfwd(const TIO* __restrict__ v, const TIO* __restrict__ g, float2* __restrict__ tile,
             const float2* __restrict__ tw1, int W, int64_t row0, int64_t nrows) {
     using C = C2Col<LOGH>;
-    constexpr int H = C::H, C1 = C::C1, T1 = C::T1, CB = kC2CB;
+    constexpr int C1 = C::C1, T1 = C::T1, CB = kC2CB;
+    constexpr int H = CIRC ? C1 : C::H;  // image rows
+    constexpr int LD = CIRC ? 16 : 8;    // values per thread holding data
     __shared__ float2 lds[C1 * C::CP];
     const int half = W / 2;
     int64_t r;
@@ -62,27 +65,30 @@ k_c2_colfwd(const TIO* __restrict__ v, const TIO* __restrict__ g, float2* __rest
     const TIO* gr = g ? g + img : nullptr;
     float2 a[16];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < LD; ++e) {
         const int h = t + T1 * e;  // < H
         float2 s = load_pair(vr + (int64_t)h * W, (uint32_t)m);
         if (gr) s = emul(s, load_pair(gr + (int64_t)h * W, (uint32_t)m));
         a[e] = s;
     }
 #pragma unroll
-    for (int e = 8; e < 16; ++e) a[e] = make_float2(0.f, 0.f);
-    fft_strided<C1, false, true>(a, t, tw1, ColAcc<C::CP>{lds + c});
+    for (int e = LD; e < 16; ++e) a[e] = make_float2(0.f, 0.f);
+    fft_strided<C1, false, !CIRC>(a, t, tw1, ColAcc<C::CP>{lds + c});
     float2* tr = tile + r * (int64_t)C1 * half;
 #pragma unroll
     for (int e = 0; e < 16; ++e) tr[(int64_t)(t + T1 * e) * half + m] = a[e];
 }
 
 // Last column pass: inverse column FFTs, rows h < H, the gate, y.
-template <int LOGH, class TIO>
+// CIRC: the image has 2H rows, all kept.
+template <int LOGH, class TIO, bool CIRC = false>
 __global__ void __launch_bounds__(C2Col<LOGH>::THREADS)
 k_c2_colinv(const float2* __restrict__ tile, const TIO* __restrict__ x, TIO* __restrict__ y,
             const float2* __restrict__ tw1, int W, int64_t row0, int64_t nrows) {
     using C = C2Col<LOGH>;
-    constexpr int H = C::H, C1 = C::C1, T1 = C::T1, CB = kC2CB;
+    constexpr int C1 = C::C1, T1 = C::T1, CB = kC2CB;
+    constexpr int H = CIRC ? C1 : C::H;
+    constexpr int LD = CIRC ? 16 : 8;
     __shared__ float2 lds[C1 * C::CP];
     const int half = W / 2;
     int64_t r;
@@ -99,7 +105,7 @@ k_c2_colinv(const float2* __restrict__ tile, const TIO* __restrict__ x, TIO* __r
     const TIO* xr = x ? x + img : nullptr;
     TIO* yr = y + img;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < LD; ++e) {
         const int h = t + T1 * e;
         float2 o = a[e];
         if (xr) o = emul(o, load_pair(xr + (int64_t)h * W, (uint32_t)m));
@@ -186,13 +192,17 @@ struct PairMap3 {
 // transform's size, so that the pair step also applies the inverse normalisation.
 // per_sample (MODE 0): image b*D + d reads spectrum b*D + d (a kernel set per
 // sample) instead of spectrum d.
-template <int LOGW, int MODE, class MAP>
+// CIRC (circular mode, MODE 0): the tile rows hold all W packed columns; the
+// row transform is not pruned and every column is kept.
+template <int LOGW, int MODE, class MAP, bool CIRC = false>
 __global__ void __launch_bounds__(C2Row<LOGW>::THREADS)
 k_cnd_row(float2* __restrict__ buf, const float2* __restrict__ spec, const float* __restrict__ bias,
           const float2* __restrict__ tw2, const float2* __restrict__ wpair, MAP map, int D, int64_t row0,
           int64_t nrows, bool per_sample) {
     using R = C2Row<LOGW>;
     constexpr int W = R::W, T2 = R::T2, U = R::UNITS, RP = R::RP, HW = W / 2;
+    constexpr int TP = CIRC ? W : HW;  // tile pitch (MODE 0)
+    constexpr int LD = CIRC ? 16 : 8;  // values per thread holding data (MODE 0)
     __shared__ float2 lds[2 * U * RP];
     const int NR = map.rows();
     int64_t r;
@@ -206,20 +216,20 @@ k_cnd_row(float2* __restrict__ buf, const float2* __restrict__ spec, const float
     const int kh = (rho & 1) == 0 ? my_a : my_b;
     const RowAcc racc{lds + rho * RP};
     // MODE 0 works on the chunk's tile; MODE 1 in place on the spectrum rows
-    const int64_t pitch = MODE == 0 ? HW : W + 1;
-    float2* img = MODE == 0 ? buf + r * (int64_t)NR * HW : buf + (row0 + r) * (int64_t)NR * (W + 1);
+    const int64_t pitch = MODE == 0 ? TP : W + 1;
+    float2* img = MODE == 0 ? buf + r * (int64_t)NR * TP : buf + (row0 + r) * (int64_t)NR * (W + 1);
     float2* rowp = img + (int64_t)kh * pitch;
     float2 a[16];
     if constexpr (MODE == 0) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = rowp[t + T2 * e];
+        for (int e = 0; e < LD; ++e) a[e] = rowp[t + T2 * e];
 #pragma unroll
-        for (int e = 8; e < 16; ++e) a[e] = make_float2(0.f, 0.f);
+        for (int e = LD; e < 16; ++e) a[e] = make_float2(0.f, 0.f);
     } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) a[e] = rowp[t + T2 * e];
     }
-    fft_strided<W, false, MODE == 0>(a, t, tw2, racc);
+    fft_strided<W, false, MODE == 0 && !CIRC>(a, t, tw2, racc);
     __syncthreads();
     lds_store_strided<T2>(racc, t, a);
     __syncthreads();
@@ -303,44 +313,53 @@ k_cnd_row(float2* __restrict__ buf, const float2* __restrict__ spec, const float
         lds_load_strided<T2>(racc, t, a);
         fft_strided<W, true, false>(a, t, tw2, racc);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rowp[t + T2 * e] = a[e];
+        for (int e = 0; e < LD; ++e) rowp[t + T2 * e] = a[e];
     }
 }
 
 // ------------------------------------------------------------- launch helpers
 
-template <int LOGH>
-void launch_cols(bool fwd, bool bf16, const void* v, const void* g, const void* x, float2* tile, void* y,
-                 const float2* tw1, int W, int64_t row0, int64_t nrows, hipStream_t st) {
+template <int LOGH, bool CIRC>
+void launch_cols_c(bool fwd, bool bf16, const void* v, const void* g, const void* x, float2* tile, void* y,
+                   const float2* tw1, int W, int64_t row0, int64_t nrows, hipStream_t st) {
     using C = C2Col<LOGH>;
     const unsigned grid = (unsigned)xcd_grid(nrows, (W / 2) / kC2CB);
     if (fwd) {
         if (bf16)
-            hipLaunchKernelGGL((k_c2_colfwd<LOGH, uint16_t>), dim3(grid), dim3(C::THREADS), 0, st,
+            hipLaunchKernelGGL((k_c2_colfwd<LOGH, uint16_t, CIRC>), dim3(grid), dim3(C::THREADS), 0, st,
                                (const uint16_t*)v, (const uint16_t*)g, tile, tw1, W, row0, nrows);
         else
-            hipLaunchKernelGGL((k_c2_colfwd<LOGH, float>), dim3(grid), dim3(C::THREADS), 0, st, (const float*)v,
-                               (const float*)g, tile, tw1, W, row0, nrows);
+            hipLaunchKernelGGL((k_c2_colfwd<LOGH, float, CIRC>), dim3(grid), dim3(C::THREADS), 0, st,
+                               (const float*)v, (const float*)g, tile, tw1, W, row0, nrows);
     } else {
         if (bf16)
-            hipLaunchKernelGGL((k_c2_colinv<LOGH, uint16_t>), dim3(grid), dim3(C::THREADS), 0, st, tile,
+            hipLaunchKernelGGL((k_c2_colinv<LOGH, uint16_t, CIRC>), dim3(grid), dim3(C::THREADS), 0, st, tile,
                                (const uint16_t*)x, (uint16_t*)y, tw1, W, row0, nrows);
         else
-            hipLaunchKernelGGL((k_c2_colinv<LOGH, float>), dim3(grid), dim3(C::THREADS), 0, st, tile,
+            hipLaunchKernelGGL((k_c2_colinv<LOGH, float, CIRC>), dim3(grid), dim3(C::THREADS), 0, st, tile,
                                (const float*)x, (float*)y, tw1, W, row0, nrows);
     }
 }
 
-// First (fwd) or last (!fwd) column pass over images of 2^logH rows of W samples.
+template <int LOGH>
+void launch_cols(bool fwd, bool bf16, const void* v, const void* g, const void* x, float2* tile, void* y,
+                 const float2* tw1, int W, int64_t row0, int64_t nrows, bool circ, hipStream_t st) {
+    if (circ) launch_cols_c<LOGH, true>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, st);
+    else launch_cols_c<LOGH, false>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, st);
+}
+
+// First (fwd) or last (!fwd) column pass with transforms of length 2^(logH+1):
+// over images of 2^logH rows (zero-padded) or 2^(logH+1) rows (circ) of W samples.
 inline hipError_t cols(int logH, bool fwd, bool bf16, const void* v, const void* g, const void* x, float2* tile,
-                       void* y, const float2* tw1, int W, int64_t row0, int64_t nrows, hipStream_t st) {
+                       void* y, const float2* tw1, int W, int64_t row0, int64_t nrows, hipStream_t st,
+                       bool circ = false) {
     switch (logH) {
-        case 4: launch_cols<4>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, st); break;
-        case 5: launch_cols<5>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, st); break;
-        case 6: launch_cols<6>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, st); break;
-        case 7: launch_cols<7>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, st); break;
-        case 8: launch_cols<8>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, st); break;
-        case 9: launch_cols<9>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, st); break;
+        case 4: launch_cols<4>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, circ, st); break;
+        case 5: launch_cols<5>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, circ, st); break;
+        case 6: launch_cols<6>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, circ, st); break;
+        case 7: launch_cols<7>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, circ, st); break;
+        case 8: launch_cols<8>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, circ, st); break;
+        case 9: launch_cols<9>(fwd, bf16, v, g, x, tile, y, tw1, W, row0, nrows, circ, st); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -349,30 +368,39 @@ inline hipError_t cols(int logH, bool fwd, bool bf16, const void* v, const void*
 template <int LOGW, class MAP>
 void launch_rows(int mode, float2* buf, const float2* spec, const float* bias, const float2* tw2,
                  const float2* wpair, MAP map, int units, int D, int64_t row0, int64_t nrows, bool per_sample,
-                 hipStream_t st) {
+                 bool circ, hipStream_t st) {
     using R = C2Row<LOGW>;
     const unsigned grid = (unsigned)xcd_grid(nrows, units / R::UNITS);
-    if (mode == 0)
-        hipLaunchKernelGGL((k_cnd_row<LOGW, 0, MAP>), dim3(grid), dim3(R::THREADS), 0, st, buf, spec, bias, tw2,
-                           wpair, map, D, row0, nrows, per_sample);
-    else
+    if (mode == 1)
         hipLaunchKernelGGL((k_cnd_row<LOGW, 1, MAP>), dim3(grid), dim3(R::THREADS), 0, st, buf, spec, bias, tw2,
                            wpair, map, D, row0, nrows, false);
+    else if (circ)
+        hipLaunchKernelGGL((k_cnd_row<LOGW, 0, MAP, true>), dim3(grid), dim3(R::THREADS), 0, st, buf, spec, bias,
+                           tw2, wpair, map, D, row0, nrows, per_sample);
+    else
+        hipLaunchKernelGGL((k_cnd_row<LOGW, 0, MAP>), dim3(grid), dim3(R::THREADS), 0, st, buf, spec, bias, tw2,
+                           wpair, map, D, row0, nrows, per_sample);
 }
 
-// Row pass over W-sample rows (MODE 0: the forward's tile; MODE 1: the spectrum).
+// Row pass with transforms of 2^logW packed points (MODE 0: the forward's tile,
+// half of each row holding data, or all of it when circ; MODE 1: the spectrum).
 template <class MAP>
 hipError_t rows(int logW, int mode, float2* buf, const float2* spec, const float* bias, const float2* tw2,
                 const float2* wpair, MAP map, int units, int D, int64_t row0, int64_t nrows, bool per_sample,
-                hipStream_t st) {
+                hipStream_t st, bool circ = false) {
+#define CND_ROWS(n)                                                                                         \
+    case n:                                                                                                 \
+        launch_rows<n>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, circ, st); \
+        break;
     switch (logW) {
-        case 5: launch_rows<5>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, st); break;
-        case 6: launch_rows<6>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, st); break;
-        case 7: launch_rows<7>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, st); break;
-        case 8: launch_rows<8>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, st); break;
-        case 9: launch_rows<9>(mode, buf, spec, bias, tw2, wpair, map, units, D, row0, nrows, per_sample, st); break;
+        CND_ROWS(5)
+        CND_ROWS(6)
+        CND_ROWS(7)
+        CND_ROWS(8)
+        CND_ROWS(9)
         default: return hipErrorInvalidValue;
     }
+#undef CND_ROWS
     return hipGetLastError();
 }
 

@@ -365,6 +365,16 @@ typedef struct hyena_plan2d_s* hyena_plan2d_t; /* opaque */
  * twiddle tables on the current device. Errors as hyena_plan_create. */
 hyena_status_t hyena_plan2d_create(hyena_plan2d_t* out, int64_t H, int64_t W, int64_t D, hyena_dtype_t dtype);
 
+/* As hyena_plan2d_create, with option flags (0 or HYENA_FLAG_CIRCULAR). A circular
+ * plan convolves the grid periodically (the HyenaND summary's boundary handling
+ * for periodic systems), with the kernel k[D][H][W] on the grid itself:
+ *   c[p][q] = sum_{i < H, j < W} k[i][j] s[(p - i) mod H][(q - j) mod W];
+ * its spectrum is D * H * (W/2 + 1) complex values (rfft2 of the H x W kernel,
+ * scaled by 1/(2 * H * W)), its workspace 4*H*W bytes per image; 32 <= H <= 1024,
+ * 64 <= W <= 1024. HYENA_ERR_INVALID_ARG for unknown flag bits. */
+hyena_status_t hyena_plan2d_create_ex(hyena_plan2d_t* out, int64_t H, int64_t W, int64_t D, hyena_dtype_t dtype,
+                                      uint32_t flags);
+
 /* Release a 2-D plan. NULL is a no-op. */
 hyena_status_t hyena_plan2d_destroy(hyena_plan2d_t plan);
 
@@ -430,6 +440,14 @@ typedef struct hyena_plan3d_s* hyena_plan3d_t; /* opaque */
  * hyena_plan_create. */
 hyena_status_t hyena_plan3d_create(hyena_plan3d_t* out, int64_t A, int64_t H, int64_t W, int64_t D,
                                    hyena_dtype_t dtype);
+
+/* As hyena_plan3d_create, with option flags (0 or HYENA_FLAG_CIRCULAR): a
+ * circular plan convolves the volume periodically with the kernel k[D][A][H][W]
+ * on the grid itself; its spectrum is D * A * H * (W/2 + 1) complex values
+ * (rfftn of the kernel, scaled by 1/(2 * A * H * W)), its workspace 4*A*H*W
+ * bytes per volume; 32 <= A, H <= 1024, 64 <= W <= 1024. */
+hyena_status_t hyena_plan3d_create_ex(hyena_plan3d_t* out, int64_t A, int64_t H, int64_t W, int64_t D,
+                                      hyena_dtype_t dtype, uint32_t flags);
 
 /* Release a 3-D plan. NULL is a no-op. */
 hyena_status_t hyena_plan3d_destroy(hyena_plan3d_t plan);

@@ -142,6 +142,12 @@ def test_conv3d_entry_points_reject_bad_arguments(lib):
     assert lib.hyena_spectrum3d_bytes(None) == 0 and lib.hyena_workspace3d_bytes(None, 1) == 0
     assert lib.hyena_filter_spectrum3d(None, 16, 16, None) == 1
     assert lib.hyena_conv3d_forward(None, 1, 16, None, None, 16, 16, 16, 16, 1 << 20, None) == 1
+    assert lib.hyena_plan2d_create_ex(ctypes.byref(h), 64, 64, 4, 0, 2) == 1       # unknown flag bit
+    assert lib.hyena_plan3d_create_ex(ctypes.byref(h), 32, 32, 64, 4, 0, 2) == 1   # unknown flag bit
+    assert lib.hyena_plan2d_create_ex(ctypes.byref(h), 16, 64, 4, 0, 1) == 2       # circular H below 32
+    assert lib.hyena_plan2d_create_ex(ctypes.byref(h), 64, 32, 4, 0, 1) == 2       # circular W below 64
+    assert lib.hyena_plan3d_create_ex(ctypes.byref(h), 16, 32, 64, 4, 0, 1) == 2   # circular A below 32
+    assert h.value is None
     for nd in ("2d", "3d"):
         assert getattr(lib, f"hyena_filter_spectrum{nd}_batched")(None, 1, 16, 16, None) == 1
         assert getattr(lib, f"hyena_conv{nd}_forward_per_sample")(None, 1, 16, None, None, 16, 16, 16, 16,

@@ -177,3 +177,54 @@ def test_conv2d_equal_kernel_sets_reproduce_the_shared_step():
         with pytest.raises(ValueError):  # one spectrum is too small for B = 3
             p.forward_per_sample(v, p.spectrum(torch.from_numpy(inp.k).cuda()), bias)
     assert bool((a == b).all())
+
+
+CIRC_CASES = [
+    # B, D, H, W, dtype: the smallest circular plan, non-square, bf16, the largest axes
+    (1, 2, 32, 64, "f32"),
+    (2, 2, 64, 128, "f32"),
+    (1, 3, 128, 64, "bf16"),
+    (1, 1, 1024, 64, "f32"),
+    (1, 1, 32, 1024, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,D,H,W,dtype", CIRC_CASES)
+def test_conv2d_circular_matches_oracle(B, D, H, W, dtype):
+    """Circular plans (periodic grid, kernel on the grid itself) against the
+    circular oracle; the zero-padded result differs by far more than the bound."""
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan2D
+
+    inp = synth.conv2d_inputs(B, D, H, W, dtype, seed=H + W + 3)
+    kc = np.ascontiguousarray(inp.k[:, :H, :W])  # a kernel on the H x W grid
+    with Plan2D(H, W, D, dtype, circular=True) as p:
+        assert p.spectrum_bytes() == 8 * D * H * (W // 2 + 1)
+        y = p.forward(_dev(inp.v, dtype), p.spectrum(torch.from_numpy(kc).cuda()), torch.from_numpy(inp.bias).cuda(),
+                      g=_dev(inp.g, dtype), x=_dev(inp.x, dtype))
+        torch.cuda.synchronize()
+    ref = oracle.conv2d_forward(inp.v, kc, inp.bias, inp.g, inp.x, circular=True)
+    got = y.float().cpu().numpy().astype(np.float64)
+    err = oracle.rel_l2(got, ref)
+    bound = 1e-2 if dtype == "bf16" else 1e-4
+    kz = np.zeros((D, 2 * H, 2 * W), np.float32)
+    kz[:, :H, :W] = kc
+    gap = oracle.rel_l2(oracle.conv2d_forward(inp.v, kz, inp.bias, inp.g, inp.x), ref)
+    say(f"[conv2d circular] B={B} D={D} {H}x{W} {dtype}: rel_l2 {err:.3e} (zero-padded differs by {gap:.1e})")
+    assert err <= bound and gap > 10 * bound
+
+
+def test_conv2d_circular_spectrum_matches_numpy_rfft2():
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan2D
+
+    D, H, W = 2, 64, 128
+    k = synth.conv2d_inputs(1, D, H, W, seed=4).k[:, :H, :W].copy()
+    with Plan2D(H, W, D, circular=True) as p:
+        s = p.spectrum(torch.from_numpy(k).cuda())
+        torch.cuda.synchronize()
+        s = s.cpu().numpy().view(np.complex64).reshape(D, H, W // 2 + 1).astype(np.complex128) * (2.0 * H * W)
+    want = np.fft.rfft2(k.astype(np.float64))
+    assert np.linalg.norm(s - want) / np.linalg.norm(want) < 2e-6

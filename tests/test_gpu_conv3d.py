@@ -177,3 +177,45 @@ def test_conv3d_per_sample_matches_oracle():
     say(f"[conv3d per-sample] B={B} D={D} {A}x{H}x{W}: rel_l2 {err:.3e}")
     assert err <= 1e-4
     assert bool((y_eq == y_sh).all())
+
+
+@pytest.mark.parametrize("B,D,A,H,W,dtype", [(1, 2, 32, 32, 64, "f32"), (2, 1, 64, 32, 128, "f32"),
+                                             (1, 2, 32, 64, 64, "bf16"), (1, 1, 1024, 32, 64, "f32")])
+def test_conv3d_circular_matches_oracle(B, D, A, H, W, dtype):
+    """Circular plans (periodic volume, kernel on the grid itself) against the
+    circular oracle; the zero-padded result differs by far more than the bound."""
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan3D
+
+    inp = synth.conv3d_inputs(B, D, A, H, W, dtype, seed=A + H + W + 5)
+    kc = np.ascontiguousarray(inp.k[:, :A, :H, :W])
+    with Plan3D(A, H, W, D, dtype, circular=True) as p:
+        assert p.spectrum_bytes() == 8 * D * A * H * (W // 2 + 1)
+        y = p.forward(_dev(inp.v, dtype), p.spectrum(torch.from_numpy(kc).cuda()), torch.from_numpy(inp.bias).cuda(),
+                      g=_dev(inp.g, dtype), x=_dev(inp.x, dtype))
+        torch.cuda.synchronize()
+    ref = oracle.conv3d_forward(inp.v, kc, inp.bias, inp.g, inp.x, circular=True)
+    got = y.float().cpu().numpy().astype(np.float64)
+    err = oracle.rel_l2(got, ref)
+    bound = 1e-2 if dtype == "bf16" else 1e-4
+    kz = np.zeros((D, 2 * A, 2 * H, 2 * W), np.float32)
+    kz[:, :A, :H, :W] = kc
+    gap = oracle.rel_l2(oracle.conv3d_forward(inp.v, kz, inp.bias, inp.g, inp.x), ref)
+    say(f"[conv3d circular] B={B} D={D} {A}x{H}x{W} {dtype}: rel_l2 {err:.3e} (zero-padded differs by {gap:.1e})")
+    assert err <= bound and gap > 10 * bound
+
+
+def test_conv3d_circular_spectrum_matches_numpy_rfftn():
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan3D
+
+    D, A, H, W = 2, 32, 64, 64
+    k = synth.conv3d_inputs(1, D, A, H, W, seed=4).k[:, :A, :H, :W].copy()
+    with Plan3D(A, H, W, D, circular=True) as p:
+        s = p.spectrum(torch.from_numpy(k).cuda())
+        torch.cuda.synchronize()
+        s = s.cpu().numpy().view(np.complex64).reshape(D, A, H, W // 2 + 1).astype(np.complex128) * (2.0 * A * H * W)
+    want = np.fft.rfftn(k.astype(np.float64), axes=(1, 2, 3))
+    assert np.linalg.norm(s - want) / np.linalg.norm(want) < 2e-6
