@@ -1,6 +1,8 @@
 /*
  * libhyena — the Hyena operator forward hot path, its backward, the whole
- * operator forward and the implicit filter generator, on AMD MI355X (gfx950).
+ * operator forward, the implicit filter generator, and the HyenaND variants
+ * (per-sample filters, circular plans, gated 2-D and 3-D long convolutions), on
+ * AMD MI355X (gfx950).
  *
  * The operator (HyenaDNA walkthrough, section 2.1, HyenaOperator.forward):
  *   uc  = ShortConv(u_proj)[..., :L]    depthwise Conv1d, 3 taps, padding 2
