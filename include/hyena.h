@@ -54,7 +54,7 @@ typedef enum { HYENA_F32 = 0, HYENA_BF16 = 1 } hyena_dtype_t;
 typedef enum {
     HYENA_OK = 0,
     HYENA_ERR_INVALID_ARG = 1, /* NULL pointer, bad size or shape, misaligned pointer */
-    HYENA_ERR_UNSUPPORTED = 2, /* valid request outside what this build implements */
+    HYENA_ERR_UNSUPPORTED = 2, /* valid request outside what the library implements */
     HYENA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
     HYENA_ERR_DEVICE = 4       /* no usable HIP device, allocation or launch failure */
 } hyena_status_t;
@@ -67,7 +67,7 @@ typedef enum {
  *             256 <= L <= 2^20.
  *   FUSED     one persistent launch for the whole four-step forward, with the
  *             intermediate tiles kept in each XCD's L2 (order 2, L = 65536).
- *             Not available in this build: plans asking for it get
+ *             Switched off: plans asking for it get
  *             HYENA_ERR_UNSUPPORTED.
  *   PARTITIONED  the same causal convolution with the filter cut into
  *             blocks of Q = 4096 taps (uniformly partitioned overlap-save):
@@ -96,8 +96,8 @@ hyena_status_t hyena_plan_create(hyena_plan_t* out, int64_t L, int64_t D, int or
 
 /* As hyena_plan_create, with an explicit kernel family. HYENA_PATH_LDS needs
  * L <= 16384; HYENA_PATH_FOURSTEP needs L >= 256; HYENA_PATH_PARTITIONED needs
- * 8192 <= L <= 131072 and no flags; HYENA_PATH_FUSED is not available in this
- * build (HYENA_ERR_UNSUPPORTED otherwise). The spectrum layout depends on the
+ * 8192 <= L <= 131072 and no flags; HYENA_PATH_FUSED is switched off
+ * (HYENA_ERR_UNSUPPORTED). The spectrum layout depends on the
  * path (FOURSTEP and FUSED share one; PARTITIONED holds the 2Q-point spectra of
  * each filter's L/Q blocks, [o][d][block][Q], in the LDS layout), so a spectrum
  * must be made by a plan whose path uses the same layout as the plan that

@@ -76,7 +76,7 @@ def _create(lib, L, D, order, dtype=0, path=0):
     (1024, 4, 9, 0, 0, 2),        # order above 8
     (1 << 15, 4, 2, 0, 1, 2),     # LDS path beyond 16384
     (128, 4, 2, 0, 2, 2),         # four-step below 256
-    (65536, 4, 2, 0, 3, 2),       # fused path is switched off in this build
+    (65536, 4, 2, 0, 3, 2),       # the fused path is switched off
 ])
 def test_plan_argument_errors_before_any_device_call(lib, L, D, order, dtype, path, want):
     st, h = _create(lib, L, D, order, dtype, path)
