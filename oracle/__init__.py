@@ -359,6 +359,26 @@ def backward(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.nd
     return du, dw, dh, db
 
 
+def backward_per_sample(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray, dy: np.ndarray,
+                        order: int, mode: str = "fft", threads: int = 0):
+    """Gradients of ``forward_per_sample`` (a filter set per sample, HyenaND summary,
+    methodology): sample b runs through ``backward`` with its own filters h[b] of
+    h [B, N-1, D, L]; the shared parameters' gradients are summed over the samples.
+    Returns (du_proj [B,(N+1)D,L], dshort_w [(N+1)D,3], dh [B,N-1,D,L], dbias [N-1,D])."""
+    u = np.asarray(u_proj)
+    hb = np.asarray(h)
+    g = np.asarray(dy)
+    if hb.ndim != 4 or hb.shape[0] != u.shape[0]:
+        raise ValueError("h must be [B, N-1, D, L] with the B of u_proj")
+    parts = [backward(u[b:b + 1], short_w, hb[b], bias, g[b:b + 1], order, mode=mode, threads=threads)
+             for b in range(u.shape[0])]
+    du = np.concatenate([p[0] for p in parts], axis=0)
+    dw = np.sum([p[1] for p in parts], axis=0)
+    dh = np.stack([p[2] for p in parts])
+    db = np.sum([p[3] for p in parts], axis=0)
+    return du, dw, dh, db
+
+
 def operator_forward(x: np.ndarray, w_in: np.ndarray, b_in: np.ndarray, short_w: np.ndarray, h: np.ndarray,
                      bias: np.ndarray, w_out: np.ndarray, b_out: np.ndarray, order: int, mode: str = "fft",
                      threads: int = 0) -> np.ndarray:
