@@ -28,6 +28,7 @@ FLAG_CIRCULAR = 1  # HYENA_FLAG_CIRCULAR
 EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_create_ex", "hyena_plan_destroy", "hyena_plan_path",
            "hyena_spectrum_bytes", "hyena_workspace_bytes", "hyena_filter_spectrum", "hyena_forward",
            "hyena_forward_timed", "hyena_fused_check", "hyena_backward_workspace_bytes", "hyena_backward",
+           "hyena_backward_per_sample_workspace_bytes", "hyena_backward_per_sample",
            "hyena_operator_workspace_bytes", "hyena_operator_forward", "hyena_operator_forward_timed",
            "hyena_implicit_filter", "hyena_filter_spectrum_batched", "hyena_forward_per_sample",
            "hyena_plan2d_create", "hyena_plan2d_destroy", "hyena_spectrum2d_bytes", "hyena_workspace2d_bytes",
@@ -97,6 +98,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_backward_workspace_bytes.restype = sz
     lib.hyena_backward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hyena_backward.restype = ci
+    lib.hyena_backward_per_sample_workspace_bytes.argtypes = [vp, i64]
+    lib.hyena_backward_per_sample_workspace_bytes.restype = sz
+    lib.hyena_backward_per_sample.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hyena_backward_per_sample.restype = ci
     lib.hyena_operator_workspace_bytes.argtypes = [vp, i64]
     lib.hyena_operator_workspace_bytes.restype = sz
     lib.hyena_operator_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -304,10 +309,18 @@ class Plan:
                                             ws_bytes, _stream_handle(torch, self.device), ms))
         return dict(zip(("lds", "pass_a", "pass_b", "pass_c", "total"), [float(v) for v in ms]))
 
-    def backward_workspace_bytes(self, B: int) -> int:
-        return int(self.lib.hyena_backward_workspace_bytes(self.handle, int(B)))
+    def backward_workspace_bytes(self, B: int, per_sample: bool = False) -> int:
+        fn = self.lib.hyena_backward_per_sample_workspace_bytes if per_sample else self.lib.hyena_backward_workspace_bytes
+        return int(fn(self.handle, int(B)))
 
-    def backward(self, u_proj, short_w, spec, bias, dy, du=None, dw=None, dh=None, dbias=None, workspace=None):
+    def backward_per_sample(self, u_proj, short_w, spec, bias, dy, du=None, dw=None, dh=None, dbias=None,
+                            workspace=None):
+        """hyena_backward_per_sample: as backward, with spec holding one spectrum per
+        sample (from spectrum_batched) and dh [B,N-1,D,L] one filter gradient per sample."""
+        return self.backward(u_proj, short_w, spec, bias, dy, du, dw, dh, dbias, workspace, per_sample=True)
+
+    def backward(self, u_proj, short_w, spec, bias, dy, du=None, dw=None, dh=None, dbias=None, workspace=None,
+                 per_sample=False):
         """hyena_backward: gradients (du_proj [B,(N+1)D,L] io dtype, dshort_w [(N+1)D,3],
         dh [N-1,D,L], dbias [N-1,D] fp32) of the forward for upstream gradient dy [B,D,L]."""
         torch = self._torch
@@ -319,24 +332,28 @@ class Plan:
         self._need(short_w, "short_w", ((N + 1) * D, 3), torch.float32)
         self._need(bias, "bias", (N - 1, D), torch.float32)
         self._need(dy, "dy", (B, D, L), self.io_dtype)
-        if spec.device != self.device or spec.numel() * spec.element_size() < self.spectrum_bytes():
-            raise ValueError("spec must come from Plan.spectrum of an equal plan")
+        nspec = B if per_sample else 1
+        if spec.device != self.device or spec.numel() * spec.element_size() < nspec * self.spectrum_bytes():
+            raise ValueError("spec must come from Plan.spectrum (spectrum_batched for per-sample filters) "
+                             "of an equal plan")
         f32 = torch.float32
+        dh_shape = (B, N - 1, D, L) if per_sample else (N - 1, D, L)
         du = torch.empty((B, (N + 1) * D, L), dtype=self.io_dtype, device=self.device) if du is None else du
         dw = torch.empty(((N + 1) * D, 3), dtype=f32, device=self.device) if dw is None else dw
-        dh = torch.empty((N - 1, D, L), dtype=f32, device=self.device) if dh is None else dh
+        dh = torch.empty(dh_shape, dtype=f32, device=self.device) if dh is None else dh
         dbias = torch.empty((N - 1, D), dtype=f32, device=self.device) if dbias is None else dbias
         self._need(du, "du", (B, (N + 1) * D, L), self.io_dtype)
         self._need(dw, "dw", ((N + 1) * D, 3), f32)
-        self._need(dh, "dh", (N - 1, D, L), f32)
+        self._need(dh, "dh", dh_shape, f32)
         self._need(dbias, "dbias", (N - 1, D), f32)
-        need = self.backward_workspace_bytes(B)
+        need = self.backward_workspace_bytes(B, per_sample)
         if workspace is None and need:
             workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-        _check("hyena_backward",
-               self.lib.hyena_backward(self.handle, B, u_proj.data_ptr(), short_w.data_ptr(), spec.data_ptr(),
+        name = "hyena_backward_per_sample" if per_sample else "hyena_backward"
+        _check(name,
+               getattr(self.lib, name)(self.handle, B, u_proj.data_ptr(), short_w.data_ptr(), spec.data_ptr(),
                                        bias.data_ptr(), dy.data_ptr(), du.data_ptr(), dw.data_ptr(), dh.data_ptr(),
                                        dbias.data_ptr(), ws_ptr, ws_bytes, _stream_handle(torch, self.device)))
         return du, dw, dh, dbias

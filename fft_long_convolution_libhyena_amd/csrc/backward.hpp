@@ -22,6 +22,8 @@ struct LdsBwdArgs {
     const float2* wpair;  // W_{2L}^k, k = 0..L/2
     int B, D, N;
     bool bf16;
+    int64_t sbs = 0;          // spectrum batch stride (complex values): 0 = one spectrum for every b
+    bool per_sample = false;  // dh per sample ([B][N-1][D][L]) instead of the batch sum
 };
 
 // Bytes of backward workspace for batch B: per (b, d) row the N-1 product
@@ -45,16 +47,19 @@ struct FsBwdArgs {
     float* dw;
     float* dh;
     float* dbias;
-    void* ws;  // fs_bwd_ws_bytes(logL, B, D) bytes
+    void* ws;  // fs_bwd_ws_bytes(logL, B, D, N, per_sample) bytes
     FsTables tb;
     int B, D, N;
     bool bf16;
+    int64_t sbs = 0;          // spectrum batch stride (complex values): 0 = one spectrum for every b
+    bool per_sample = false;  // dh per sample ([B][N-1][D][L]) instead of the batch sum
 };
 
 // Per (b, d) row: the L-point tile T, the gated input's spectra G_o of the N-1
 // steps and the product spectrum P (complex), the recomputed values v_1..v_{N-2}
 // V (fp32), the N+1 channels' staging rows S (fp32), the tap sums of every
-// column-block workgroup; per channel d the dh tile. 256-byte aligned.
+// column-block workgroup; per channel d the dh tile (per row with a filter set per
+// sample, which also keeps every row's lag-0 value). 256-byte aligned.
 struct FsBwdWs {
     float2* T;
     float2* G;
@@ -63,9 +68,10 @@ struct FsBwdWs {
     float* S;
     float2* Tdh;
     float* part;
+    float* lag;
     size_t bytes;
 };
-inline FsBwdWs fs_bwd_ws(void* base, int64_t B, int64_t D, int64_t L, int ncb, int N) {
+inline FsBwdWs fs_bwd_ws(void* base, int64_t B, int64_t D, int64_t L, int ncb, int N, bool per_sample = false) {
     size_t off = 0;
     auto take = [&](size_t n) {
         void* r = base ? static_cast<char*>(base) + off : nullptr;
@@ -79,12 +85,13 @@ inline FsBwdWs fs_bwd_ws(void* base, int64_t B, int64_t D, int64_t L, int ncb, i
     w.P = (float2*)take(rows * (size_t)L * 8);
     w.V = (float*)take((size_t)(N > 2 ? N - 2 : 0) * rows * (size_t)L * 4);
     w.S = (float*)take(rows * (size_t)(N + 1) * (size_t)L * 4);
-    w.Tdh = (float2*)take((size_t)D * (size_t)L * 8);
+    w.Tdh = (float2*)take((per_sample ? rows : (size_t)D) * (size_t)L * 8);
     w.part = (float*)take(rows * (size_t)ncb * 3 * (size_t)(N + 1) * 4);
+    w.lag = per_sample ? (float*)take(rows * 4) : nullptr;
     w.bytes = off;
     return w;
 }
 hipError_t launch_fs_backward(int logL, const FsBwdArgs& a, hipStream_t st);
-size_t fs_bwd_ws_bytes(int logL, int64_t B, int64_t D, int N);
+size_t fs_bwd_ws_bytes(int logL, int64_t B, int64_t D, int N, bool per_sample = false);
 
 }  // namespace hy

@@ -54,7 +54,7 @@ __device__ __forceinline__ void fs_raw_pairs(const TIO* __restrict__ row, uint32
 template <int LOG1, int LOG2, int MODE>
 __global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::ROW_THREADS))
 k_fs_row_bwd(float2* __restrict__ T, const float2* __restrict__ spec, const float* __restrict__ bias,
-             float2* __restrict__ G, float2* __restrict__ P, FsTables tb, int D, int o, int64_t nrows) {
+             float2* __restrict__ G, float2* __restrict__ P, FsTables tb, int D, int o, int64_t nrows, int64_t sbs) {
     using Cfg = FsCfg<LOG1, LOG2>;
     __shared__ float2 lds[2 * Cfg::UNITS * Cfg::RP];
     int64_t r;
@@ -62,7 +62,7 @@ k_fs_row_bwd(float2* __restrict__ T, const float2* __restrict__ spec, const floa
     if (!xcd_row_map(blockIdx.x, nrows, Cfg::L1 / 2 / Cfg::UNITS, r, ug)) return;
     const int64_t L = (int64_t)Cfg::L1 * Cfg::L2;
     fs_row_body<LOG1, LOG2, MODE>(lds, T + r * L, spec, bias, tb, D, o, r, ug, G + ((int64_t)o * nrows + r) * L,
-                                  P ? P + r * L : nullptr);
+                                  P ? P + r * L : nullptr, sbs);
 }
 
 // Column passes of the backward (inverse columns of the tile first, then):
@@ -282,7 +282,8 @@ k_fs_dh_row(const float2* __restrict__ P, float2* __restrict__ Tdh, FsTables tb,
 // workgroup holding sample 0 also writes dbias = dh[0].
 template <int LOG1, int LOG2>
 __global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::COL_THREADS))
-k_fs_dh_col(const float2* __restrict__ Tdh, float* __restrict__ dh, float* __restrict__ dbias, FsTables tb, int D) {
+k_fs_dh_col(const float2* __restrict__ Tdh, float* __restrict__ dh, float* __restrict__ dbias, FsTables tb, int D,
+            int Dch, int64_t bstride) {
     using Cfg = FsCfg<LOG1, LOG2>;
     constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T1 = Cfg::T1, CB = Cfg::CB, NCB = L2 / CB;
     constexpr int64_t L = (int64_t)L1 * L2;
@@ -298,10 +299,21 @@ k_fs_dh_col(const float2* __restrict__ Tdh, float* __restrict__ dh, float* __res
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = cmulc(slot[(uint32_t)(t + T1 * e) * L2 + m2], twiddle_step<L2>(tb, base, e, m2));
     fft_strided<L1, true, false>(v, t, tb.tw1, ColAcc<Cfg::CP>{lds + c});
-    float* dhr = dh + dd * L;
+    // row dd of the tile is filter d = dd mod Dch of sample b = dd / Dch
+    const int64_t b = dd / Dch;
+    float* dhr = dh + b * bstride + (dd - b * Dch) * L;
 #pragma unroll
     for (int e = 0; e < 8; ++e) store_pair(dhr, (uint32_t)(t + T1 * e) * L2 + m2, v[e]);
-    if (t == 0 && m2 == 0) dbias[dd] = v[0].x;
+    if (t == 0 && m2 == 0) dbias[dd] = v[0].x;  // lag 0
+}
+
+// dbias[d] = sum over the samples of the per-sample lag-0 values (fixed order).
+__global__ void k_fs_dbias_sum(const float* __restrict__ lag, float* __restrict__ dbias, int B, int D) {
+    const int d = blockIdx.x * blockDim.x + threadIdx.x;
+    if (d >= D) return;
+    float s = 0.f;
+    for (int b = 0; b < B; ++b) s += lag[(int64_t)b * D + d];
+    dbias[d] = s;
 }
 
 // dshort_w[i*D + d][j] = sum over b and column blocks of the tap sums (fixed order).
@@ -323,7 +335,7 @@ static void fs_backward_launch(const FsBwdArgs& a, hipStream_t st) {
     constexpr int NCB = Cfg::L2 / Cfg::CB;
     const int N = a.N;
     const int64_t L = (int64_t)Cfg::L1 * Cfg::L2, rows = (int64_t)a.B * a.D;
-    const FsBwdWs w = fs_bwd_ws(a.ws, a.B, a.D, L, NCB, N);
+    const FsBwdWs w = fs_bwd_ws(a.ws, a.B, a.D, L, NCB, N, a.per_sample);
     const unsigned gcol = (unsigned)xcd_grid(rows, NCB);
     const unsigned grow = (unsigned)xcd_grid(rows, Cfg::L1 / 2 / Cfg::UNITS);
     const dim3 bcol(Cfg::COL_THREADS), brow(Cfg::ROW_THREADS);
@@ -335,7 +347,7 @@ static void fs_backward_launch(const FsBwdArgs& a, hipStream_t st) {
                        w.T, a.tb, a.D, N, (int64_t)0, rows);
     for (int o = 0; o < N - 1; ++o) {
         hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 2>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G,
-                           (float2*)nullptr, a.tb, a.D, o, rows);
+                           (float2*)nullptr, a.tb, a.D, o, rows, a.sbs);
         if (o < N - 2)
             hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColMid>), dim3(gcol), bcol, 0, st, w.T, u, a.w3,
                                dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
@@ -347,11 +359,24 @@ static void fs_backward_launch(const FsBwdArgs& a, hipStream_t st) {
     // step, then the column pass that finishes the step's gate channel
     for (int o = N - 2; o >= 0; --o) {
         hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 3>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G, w.P,
-                           a.tb, a.D, o, rows);
-        hipLaunchKernelGGL((k_fs_dh_row<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, Cfg::L1 / 2 / Cfg::UNITS)), brow,
-                           0, st, (const float2*)w.P, w.Tdh, a.tb, a.B, a.D);
-        hipLaunchKernelGGL((k_fs_dh_col<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, NCB)), bcol, 0, st,
-                           (const float2*)w.Tdh, a.dh + (int64_t)o * a.D * L, a.dbias + (int64_t)o * a.D, a.tb, a.D);
+                           a.tb, a.D, o, rows, a.sbs);
+        if (!a.per_sample) {
+            // the batch sum of the product spectra, then dh[o][d] and its lag 0
+            hipLaunchKernelGGL((k_fs_dh_row<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, Cfg::L1 / 2 / Cfg::UNITS)),
+                               brow, 0, st, (const float2*)w.P, w.Tdh, a.tb, a.B, a.D);
+            hipLaunchKernelGGL((k_fs_dh_col<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, NCB)), bcol, 0, st,
+                               (const float2*)w.Tdh, a.dh + (int64_t)o * a.D * L, a.dbias + (int64_t)o * a.D, a.tb,
+                               a.D, a.D, (int64_t)0);
+        } else {
+            // every row's own product spectrum: dh[b][o][d]; dbias sums the samples' lag 0
+            hipLaunchKernelGGL((k_fs_dh_row<LOG1, LOG2>), dim3((unsigned)xcd_grid(rows, Cfg::L1 / 2 / Cfg::UNITS)),
+                               brow, 0, st, (const float2*)w.P, w.Tdh, a.tb, 1, (int)rows);
+            hipLaunchKernelGGL((k_fs_dh_col<LOG1, LOG2>), dim3((unsigned)xcd_grid(rows, NCB)), bcol, 0, st,
+                               (const float2*)w.Tdh, a.dh + (int64_t)o * a.D * L, w.lag, a.tb, (int)rows, a.D,
+                               (int64_t)(N - 1) * a.D * L);
+            hipLaunchKernelGGL(k_fs_dbias_sum, dim3((unsigned)((a.D + 255) / 256)), dim3(256), 0, st,
+                               (const float*)w.lag, a.dbias + (int64_t)o * a.D, a.B, a.D);
+        }
         if (o > 0)
             hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColTailMid>), dim3(gcol), bcol, 0, st, w.T, u,
                                a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
@@ -386,12 +411,12 @@ hipError_t launch_fs_backward(int logL, const FsBwdArgs& a, hipStream_t st) {
     }
 }
 
-size_t fs_bwd_ws_bytes(int logL, int64_t B, int64_t D, int N) {
+size_t fs_bwd_ws_bytes(int logL, int64_t B, int64_t D, int N, bool per_sample) {
     int l1 = 0, l2 = 0;
     fs_split(logL, &l1, &l2);
     const int64_t L = int64_t(1) << logL;
     const int ncb = (1 << l2) / HY_FS_CB;
-    return fs_bwd_ws(nullptr, B, D, L, ncb, N).bytes;
+    return fs_bwd_ws(nullptr, B, D, L, ncb, N, per_sample).bytes;
 }
 
 }  // namespace hy

@@ -262,6 +262,27 @@ hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, 
                               const void* spec, const float* bias, const void* dy, void* du_proj, float* dshort_w,
                               float* dh, float* dbias, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of workspace hyena_backward_per_sample needs for batch B: as
+ * hyena_backward_workspace_bytes, except on the four-step path, where the complex
+ * dh tiles are kept per (b, d) row instead of per channel and B*D floats of
+ * per-sample dbias terms are added. Returns 0 for a NULL plan, B < 1, or a
+ * circular plan. */
+size_t hyena_backward_per_sample_workspace_bytes(hyena_plan_t plan, int64_t B);
+
+/* Backward of hyena_forward_per_sample (a filter set per sample, the HyenaND
+ * summary's input-dependent convolutions): spec holds the B spectra of
+ * hyena_filter_spectrum_batched, and sample b's filter gradient is its own, so
+ *   dh      [B][N-1][D][L] fp32, device (output): dh[b] is the gradient with
+ *           respect to sample b's filters h[b] [N-1][D][L]
+ * while dshort_w and dbias, whose parameters every sample shares, are batch sums
+ * as in hyena_backward. Every other argument, the workspace (of at least
+ * hyena_backward_per_sample_workspace_bytes(plan, B)), the fixed summation order
+ * and the errors are those of hyena_backward. */
+hyena_status_t hyena_backward_per_sample(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                                         const void* spec, const float* bias, const void* dy, void* du_proj,
+                                         float* dshort_w, float* dh, float* dbias, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace hyena_operator_forward needs for batch B: the in-projected
  * activation u_proj, the path output y, a broadcast input-bias matrix, 32 MiB of
  * GEMM scratch and the path's own workspace (hyena_workspace_bytes), each

@@ -101,6 +101,8 @@ def test_operator_rejects_null_plan(lib):
 def test_backward_rejects_null_plan(lib):
     assert lib.hyena_backward_workspace_bytes(None, 1) == 0
     assert lib.hyena_backward(None, 1, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 20, None) == 1
+    assert lib.hyena_backward_per_sample_workspace_bytes(None, 1) == 0
+    assert lib.hyena_backward_per_sample(None, 1, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 20, None) == 1
 
 
 def test_implicit_filter_rejects_null_arguments(lib):

@@ -187,3 +187,108 @@ def test_backward_rejects_small_workspaces():
         with pytest.raises(HyenaError) as e:
             p.backward(t["u"], t["w"], spec, t["bias"], g, workspace=small)
         assert e.value.status == 3  # HYENA_ERR_WORKSPACE
+
+
+def _run_backward_per_sample(x, hb, dy, path):
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan
+
+    wl = x.wl
+    t = to_device(x)
+    g = torch.from_numpy(dy).to(t["u"].device)
+    if wl.dtype == "bf16":
+        g = g.to(torch.bfloat16)
+    with Plan(wl.L, wl.D, wl.order, wl.dtype, path) as p:
+        spec = p.spectrum_batched(torch.from_numpy(hb).to(g.device))
+        out = p.backward_per_sample(t["u"], t["w"], spec, t["bias"], g.contiguous())
+        torch.cuda.synchronize()
+    return out
+
+
+PER_SAMPLE = [
+    # B, D, L, order, dtype, path: both paths, orders 2..4, ragged D, bf16 I/O
+    (3, 3, 256, 2, "f32", "lds"),
+    (3, 3, 1024, 2, "f32", "lds"),
+    (2, 5, 4096, 3, "f32", "lds"),
+    (2, 3, 8192, 3, "bf16", "lds"),
+    (2, 2, 16384, 4, "f32", "lds"),
+    (3, 3, 256, 2, "f32", "fourstep"),
+    (3, 3, 1024, 3, "f32", "fourstep"),
+    (2, 3, 8192, 4, "bf16", "fourstep"),
+    (2, 2, 32768, 3, "f32", "fourstep"),
+    (2, 1, 1 << 18, 2, "f32", "fourstep"),
+]
+
+
+@pytest.mark.parametrize("B,D,L,order,dtype,path", PER_SAMPLE)
+def test_backward_per_sample_matches_oracle(B, D, L, order, dtype, path):
+    """hyena_backward_per_sample against the oracle's per-sample backward: every
+    gradient by relative L2, and each sample's filter gradient dh[b] on its own,
+    since a sample reading another sample's spectrum would hide in the global norm."""
+    wl = synth.custom(B, D, L, order, dtype, seed=B * 31 + D + L % 89 + order)
+    x = synth.generate(wl)
+    hb = synth.per_sample_filters(wl)
+    dy = synth.upstream_grad(wl)
+    say(f"[backward per-sample] {wl.describe()} path={path}")
+    got = [a.float().cpu().numpy().astype(np.float64) for a in _run_backward_per_sample(x, hb, dy, path)]
+    ref = oracle.backward_per_sample(x.u_proj, x.short_w, hb, x.bias, dy, order,
+                                     mode="direct" if L <= 256 else "fft")
+    bounds = [1e-2 if dtype == "bf16" else 1e-4, 1e-4, 1e-4, 1e-4]
+    for name, g, r, bound in zip(("du_proj", "dshort_w", "dh", "dbias"), got, ref, bounds):
+        assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+        err = oracle.rel_l2(g, r)
+        say(f"   {name:9s} rel_l2={err:.3e} (bound {bound:.0e})")
+        assert err <= bound, f"{name}: rel L2 {err:.3e} exceeds {bound:.0e}"
+    per = [oracle.rel_l2(got[2][b], ref[2][b]) for b in range(B)]
+    say(f"   dh per sample {', '.join(f'{e:.2e}' for e in per)}")
+    assert max(per) <= 1e-4
+
+
+@pytest.mark.parametrize("path,L,order", [("lds", 2048, 3), ("fourstep", 4096, 3), ("fourstep", 1024, 2)])
+def test_backward_per_sample_equal_sets_match_shared(path, L, order):
+    """With every sample given the shared filters, du_proj and dshort_w are the shared
+    backward's bit for bit (the same arithmetic on the same spectra), the per-sample
+    filter gradients sum to the shared one, and dbias agrees to rounding."""
+    import torch
+
+    wl = synth.custom(3, 4, L, order, seed=77 + order)
+    x = synth.generate(wl)
+    dy = synth.upstream_grad(wl)
+    same = np.ascontiguousarray(np.repeat(x.h[None], wl.B, axis=0))
+    du, dw, dh, db = _run_backward_per_sample(x, same, dy, path)
+    (du0, dw0, dh0, db0), = _run_backward(x, dy, path=path)
+    assert bool((du == du0).all()) and bool((dw == dw0).all())
+    e_dh = oracle.rel_l2(dh.double().sum(0).cpu().numpy(), dh0.double().cpu().numpy())
+    e_db = oracle.rel_l2(db.double().cpu().numpy(), db0.double().cpu().numpy())
+    say(f"[backward per-sample] equal sets, {path} L={L} N={order}: sum dh vs shared {e_dh:.2e}, dbias {e_db:.2e}")
+    assert e_dh <= 1e-5 and e_db <= 1e-5
+    torch.cuda.synchronize()
+
+
+def test_backward_per_sample_workspace_and_errors():
+    import torch
+
+    from fft_long_convolution_libhyena_amd import HyenaError, Plan
+
+    wl = synth.custom(2, 2, 1024, 2, seed=6)
+    x = synth.generate(wl)
+    t = to_device(x)
+    g = torch.zeros((2, 2, 1024), dtype=torch.float32, device=t["u"].device)
+    hb = torch.from_numpy(synth.per_sample_filters(wl)).to(g.device)
+    with Plan(1024, 2, 2, "f32", "fourstep") as p:
+        assert p.backward_workspace_bytes(2, per_sample=True) > p.backward_workspace_bytes(2)
+        spec = p.spectrum_batched(hb)
+        small = torch.empty(p.backward_workspace_bytes(2), dtype=torch.uint8, device=g.device)
+        with pytest.raises(HyenaError) as e:  # the shared backward's workspace is too small here
+            p.backward_per_sample(t["u"], t["w"], spec, t["bias"], g, workspace=small)
+        assert e.value.status == 3
+        with pytest.raises(ValueError):  # one spectrum where two are needed
+            p.backward_per_sample(t["u"], t["w"], p.spectrum(t["h"]), t["bias"], g)
+    with Plan(1024, 2, 2, "f32", "lds") as p:
+        assert p.backward_workspace_bytes(2, per_sample=True) == p.backward_workspace_bytes(2)
+        du, dw, dh, db = p.backward_per_sample(t["u"], t["w"], p.spectrum_batched(hb), t["bias"], g)
+        torch.cuda.synchronize()
+        assert tuple(dh.shape) == (2, 1, 2, 1024)
+        for a in (du, dw, dh, db):
+            assert float(a.abs().max()) == 0.0
