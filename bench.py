@@ -184,9 +184,10 @@ def cpu_baseline(x, wl, budget_s: float):
                       f"convolution, OpenMP over rows, {dt:.1f} s wall"}
 
 
-def cpu_baseline_backward(x, wl, budget_s: float):
+def cpu_baseline_backward(x, wl, budget_s: float, hb=None):
     """The fp64 backward oracle (FFT mode) on a bounded, seeded sample of channels
-    (all b and t of each); channels are independent, so this is a smaller instance."""
+    (all b and t of each); channels are independent, so this is a smaller instance.
+    With per-sample filters hb [B, N-1, D, L], the per-sample backward oracle."""
     import oracle
     from fft_long_convolution_libhyena_amd import synth
 
@@ -198,17 +199,24 @@ def cpu_baseline_backward(x, wl, budget_s: float):
         xs = synth.channel_subset(x, ds)
         dy = synth.upstream_grad(xs.wl)
         t0 = time.perf_counter()
-        oracle.backward(xs.u_proj, xs.short_w, xs.h, xs.bias, dy, wl.order, mode="fft")
+        if hb is None:
+            oracle.backward(xs.u_proj, xs.short_w, xs.h, xs.bias, dy, wl.order, mode="fft")
+        else:
+            oracle.backward_per_sample(xs.u_proj, xs.short_w, np.ascontiguousarray(hb[:, :, ds]), xs.bias, dy,
+                                       wl.order, mode="fft")
         dt = time.perf_counter() - t0
         if dt >= budget_s / 4 or n >= wl.D:
             break
         n = int(min(wl.D, max(n + 1, n * budget_s / max(dt, 1e-3) * 0.8)))
     return {"value": wl.B * n * wl.L / dt, "unit": "channel-tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of {wl.D} channels (all {wl.B} batch rows, all L) of the same inputs, fp64 radix-2 "
-                      f"FFT backward, OpenMP over channels, {dt:.1f} s wall"}
+                      f"FFT backward{' with a filter set per sample' if hb is not None else ''}, OpenMP over "
+                      f"channels, {dt:.1f} s wall"}
 
 
-def bench_backward(args, wl, x, torch, Plan):
+def bench_backward(args, wl, x, torch, Plan, per_sample=False):
+    """hyena_backward, or with per_sample hyena_backward_per_sample (a filter set per
+    sample: B spectra read, B filter gradients written)."""
     from fft_long_convolution_libhyena_amd import synth
 
     dev = torch.device("cuda", 0)
@@ -219,17 +227,18 @@ def bench_backward(args, wl, x, torch, Plan):
     bias = torch.from_numpy(x.bias).to(dev)
     dy = torch.from_numpy(synth.upstream_grad(wl)).to(dev).to(iot).contiguous()
     plan = Plan(wl.L, wl.D, wl.order, wl.dtype)
-    spec = plan.spectrum(h)
+    hb = synth.per_sample_filters(wl) if per_sample else None
+    spec = plan.spectrum_batched(torch.from_numpy(hb).to(dev)) if per_sample else plan.spectrum(h)
     N, D, L, B = wl.order, wl.D, wl.L, wl.B
-    ws = torch.empty(plan.backward_workspace_bytes(B), dtype=torch.uint8, device=dev)
+    ws = torch.empty(plan.backward_workspace_bytes(B, per_sample), dtype=torch.uint8, device=dev)
     outs = (torch.empty((B, (N + 1) * D, L), dtype=iot, device=dev),
             torch.empty(((N + 1) * D, 3), dtype=torch.float32, device=dev),
-            torch.empty((N - 1, D, L), dtype=torch.float32, device=dev),
+            torch.empty(((B,) if per_sample else ()) + (N - 1, D, L), dtype=torch.float32, device=dev),
             torch.empty((N - 1, D), dtype=torch.float32, device=dev))
     log(f"[bench] backward workspace {ws.numel() / 2**20:.1f} MiB")
 
     def step():
-        plan.backward(u, w, spec, bias, dy, *outs, workspace=ws)
+        plan.backward(u, w, spec, bias, dy, *outs, workspace=ws, per_sample=per_sample)
 
     for _ in range(args.warmup):
         step()
@@ -247,24 +256,27 @@ def bench_backward(args, wl, x, torch, Plan):
         log(f"[bench] rep {rep}: {times[-1] * 1e3:.1f} us/step")
     ms = float(np.median(times))
     nbytes = alg_bytes_backward(wl)
+    if per_sample:  # B filter spectra read and B filter gradients written instead of one each
+        nbytes += (B - 1) * (N - 1) * D * (8 * (L + 1) + 4 * L)
     # the step's kernels taken together: k_lds_bwd_rows + k_lds_bwd_finish on the LDS
     # path, the launches of the four-step backward ("fs_backward") otherwise
     bk = "k_lds_bwd_rows" if plan.path == "lds" else "fs_backward"
     achieved = nbytes / (ms * 1e-3) / 1e9
     out = {
         "metric": "channel-tokens/s (B·D·L/s) and % HBM peak, Hyena op backward (gradients of u_proj, short_w, "
-                  "h, bias)",
+                  "h, bias)" + (" with a filter set per sample" if per_sample else ""),
         "value": B * D * L / (ms * 1e-3), "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32" if wl.dtype == "f32" else "bf16-io/f32",
-        "data": f"synthetic seeded ({wl.kind} activations, N(0,1) upstream gradient)",
+        "data": f"synthetic seeded ({wl.kind} activations, N(0,1) upstream gradient"
+                f"{', per-sample exponentially decaying random filters' if per_sample else ''})",
         "config": {"workload": wl.name, "B": B, "D": D, "L": L, "order": N, "io_dtype": wl.dtype,
-                   "path": plan.path, "pass": "backward"},
+                   "path": plan.path, "pass": "backward_per_sample" if per_sample else "backward"},
         # the whole backward step (two launches on the LDS path, nine on the
         # four-step path) against its algorithmic bytes
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(bk, wl.name),
+                     "traffic": measured_traffic(bk, wl.name + ("_per_sample" if per_sample else "")),
                      "kernel": bk,
                      "alg_bytes_per_launch": nbytes, "launch_ms": round(ms, 5), "launches_per_step": 1},
     }
@@ -273,13 +285,19 @@ def bench_backward(args, wl, x, torch, Plan):
 
         ds = [0, D // 2, D - 1]
         xs = synth.channel_subset(x, ds)
-        ref = oracle.backward(xs.u_proj, xs.short_w, xs.h, xs.bias, synth.upstream_grad(wl)[:, ds], N)
+        g = synth.upstream_grad(wl)[:, ds]
+        if per_sample:
+            ref = oracle.backward_per_sample(xs.u_proj, xs.short_w, np.ascontiguousarray(hb[:, :, ds]), xs.bias, g, N)
+        else:
+            ref = oracle.backward(xs.u_proj, xs.short_w, xs.h, xs.bias, g, N)
         got = outs[0].float().cpu().numpy().reshape(B, N + 1, D, L)[:, :, ds].reshape(B, -1, L)
         out["check_rel_l2_du"] = oracle.rel_l2(got, ref[0])
-        log(f"[bench] oracle check of du on channels {ds}: rel_l2 {out['check_rel_l2_du']:.3e}")
+        out["check_rel_l2_dh"] = oracle.rel_l2(outs[2].double().cpu().numpy()[..., ds, :], ref[2])
+        log(f"[bench] oracle check on channels {ds}: du rel_l2 {out['check_rel_l2_du']:.3e}, "
+            f"dh rel_l2 {out['check_rel_l2_dh']:.3e}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (backward oracle) ...")
-        out["cpu_baseline"] = cpu_baseline_backward(x, wl, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline_backward(x, wl, args.cpu_budget, hb)
     print(json.dumps(out), flush=True)
     plan.close()
 
@@ -770,7 +788,8 @@ def main():
                     help="time hyena_forward on a circular plan (circular long convolutions) instead; with "
                          "--conv2d or --conv3d, a circular N-d plan")
     ap.add_argument("--per-sample", action="store_true",
-                    help="time hyena_forward_per_sample (a filter set per sample) instead")
+                    help="time hyena_forward_per_sample (a filter set per sample) instead; with --backward, "
+                         "hyena_backward_per_sample")
     ap.add_argument("--filter", action="store_true",
                     help="time hyena_implicit_filter (the long filters of the workload's plan) instead")
     args = ap.parse_args()
@@ -803,14 +822,14 @@ def main():
     if args.operator:
         bench_operator(args, wl, x, torch, Plan)
         return
+    if args.backward:
+        bench_backward(args, wl, x, torch, Plan, per_sample=args.per_sample)
+        return
     if args.per_sample:
         bench_per_sample(args, wl, x, torch, Plan)
         return
     if args.circular:
         bench_circular(args, wl, x, torch, Plan)
-        return
-    if args.backward:
-        bench_backward(args, wl, x, torch, Plan)
         return
     dev = torch.device("cuda", 0)
     u = torch.from_numpy(x.u_proj).to(dev)

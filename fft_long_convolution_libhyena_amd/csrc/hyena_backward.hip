@@ -29,6 +29,8 @@ hyena_status_t backward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, c
     const bool fs = plan->path == HYENA_PATH_FOURSTEP;
     if (plan->circular || !(plan->path == HYENA_PATH_LDS || fs)) return HYENA_ERR_UNSUPPORTED;
     if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
+    // per sample, dh alone is 4*B*(N-1)*D*L bytes; the bound keeps every grid below 2^32 work-items
+    if (per_sample && B * (plan->order - 1) * plan->D * plan->L > (int64_t(1) << 35)) return HYENA_ERR_INVALID_ARG;
     if (!workspace || !aligned16(workspace) || workspace_bytes < backward_ws(plan, B, per_sample))
         return HYENA_ERR_WORKSPACE;
     if (hy::check_device(plan) != HYENA_OK) return HYENA_ERR_DEVICE;

@@ -397,13 +397,13 @@ k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
 
 // Sums over the batch: dh[o][d] and dbias[o][d] from the product spectra, and
 // (by the o = 0 workgroups) dshort_w of the N+1 channels of d from the row tap sums.
-// per_sample (a filter set per sample): dh[b][o][d] from sample b's product
-// spectrum alone, one inverse per sample in turn; dbias still sums the samples.
-template <int LOGL, int N>
+// PER_SAMPLE (a filter set per sample): one workgroup per (b, o, d) inverts sample
+// b's product spectrum alone into dh[b][o][d]; dbias is left to k_lds_bwd_dbias.
+template <int LOGL, int N, bool PER_SAMPLE>
 __global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS)
 k_lds_bwd_finish(const float2* __restrict__ ws, float* __restrict__ dw, float* __restrict__ dh,
                  float* __restrict__ dbias, const float2* __restrict__ tw, const float2* __restrict__ wpair, int B,
-                 int D, bool per_sample) {
+                 int D) {
     constexpr int L = 1 << LOGL;
     constexpr int E = LdsCfg<LOGL>::E;
     constexpr int H = E / 2;
@@ -411,62 +411,57 @@ k_lds_bwd_finish(const float2* __restrict__ ws, float* __restrict__ dw, float* _
     using W = BwdWs<LOGL, N>;
     __shared__ float2 lds[padded_len<L>()];
     const RowAcc acc{lds};
-    const int o = blockIdx.x / D, d = blockIdx.x % D;
+    const int nod = (N - 1) * D;
+    const int bs = PER_SAMPLE ? (int)(blockIdx.x / nod) : 0;  // the sample whose dh this is
+    const int od = PER_SAMPLE ? (int)(blockIdx.x % nod) : (int)blockIdx.x;
+    const int o = od / D, d = od % D;
     const int t = threadIdx.x;
     const int64_t rows = (int64_t)B * D;
+    const int b_lo = PER_SAMPLE ? bs : 0, b_hi = PER_SAMPLE ? bs + 1 : B;
     // repack + the unnormalised L-point inverse of X gives the 2L-point inverse of
     // 2L*X; the products carry the factor 4 of the unpacked values: X = P / (8L)
     const float sc = 1.0f / (8.0f * (float)L);
-    // one output (the batch sum) or one per sample, in turn
-    const int nout = per_sample ? B : 1;
-    float lag0 = 0.f;
-#pragma unroll 1
-    for (int ob = 0; ob < nout; ++ob) {
-        const int b_lo = per_sample ? ob : 0, b_hi = per_sample ? ob + 1 : B;
-        __syncthreads();  // the previous output's transform is done with the LDS
 #pragma unroll
-        for (int e = 0; e < H; ++e) {
-            const uint32_t k = t + T * e;
-            const uint32_t km = k == 0 ? 0 : L - k;
-            float2 Ck = make_float2(0.f, 0.f), Cm = make_float2(0.f, 0.f);
-            for (int b = b_lo; b < b_hi; ++b) {
-                const float2* Pw = ws + ((int64_t)b * D + d) * W::P_ROW + (int64_t)o * L;
-                Ck = cadd(Ck, Pw[k]);
-                if (k != 0) Cm = cadd(Cm, Pw[km]);
-            }
-            float2 Yk, Ym;
-            if (k != 0) {
-                pair_repack(fmul2(Ck, sc), fmul2(Cm, sc), wpair[k], Yk, Ym);
-            } else {
-                // slot 0 holds the real bins 0 and L
-                pair_repack(make_float2(Ck.x * sc, 0.f), make_float2(Ck.y * sc, 0.f), wpair[0], Yk, Ym);
-            }
-            acc[k] = Yk;
-            if (k != 0) acc[km] = Ym;
+    for (int e = 0; e < H; ++e) {
+        const uint32_t k = t + T * e;
+        const uint32_t km = k == 0 ? 0 : L - k;
+        float2 Ck = make_float2(0.f, 0.f), Cm = make_float2(0.f, 0.f);
+        for (int b = b_lo; b < b_hi; ++b) {
+            const float2* Pw = ws + ((int64_t)b * D + d) * W::P_ROW + (int64_t)o * L;
+            Ck = cadd(Ck, Pw[k]);
+            if (k != 0) Cm = cadd(Cm, Pw[km]);
         }
-        if (t == 0) {
-            const uint32_t k = L / 2;
-            float2 P = make_float2(0.f, 0.f);
-            for (int b = b_lo; b < b_hi; ++b) P = cadd(P, ws[((int64_t)b * D + d) * W::P_ROW + (int64_t)o * L + k]);
-            P = fmul2(P, sc);
-            float2 Y, Yd;
-            pair_repack(P, P, wpair[k], Y, Yd);
-            acc[k] = Y;
+        float2 Yk, Ym;
+        if (k != 0) {
+            pair_repack(fmul2(Ck, sc), fmul2(Cm, sc), wpair[k], Yk, Ym);
+        } else {
+            // slot 0 holds the real bins 0 and L
+            pair_repack(make_float2(Ck.x * sc, 0.f), make_float2(Ck.y * sc, 0.f), wpair[0], Yk, Ym);
         }
-        __syncthreads();
-        float2 f[E];
-        lds_load_strided<T>(acc, t, f);
-        fft_strided<L, true, false>(f, t, tw, acc);
-        // shared filters: dh[o][d]; per sample: dh[b][o][d]
-        float* dhr = dh + (((int64_t)ob * (N - 1) + o) * D + d) * L;
-#pragma unroll
-        for (int e = 0; e < H; ++e) store_pair(dhr, (uint32_t)(t + T * e), f[e]);
-        // the bias gradient sum_b sum_t dv[t] g[t] is the lag-0 value of the same
-        // correlation that gives dh
-        lag0 += f[0].x;
+        acc[k] = Yk;
+        if (k != 0) acc[km] = Ym;
     }
-    if (t == 0) dbias[(int64_t)o * D + d] = lag0;
-    if (o == 0) {
+    if (t == 0) {
+        const uint32_t k = L / 2;
+        float2 P = make_float2(0.f, 0.f);
+        for (int b = b_lo; b < b_hi; ++b) P = cadd(P, ws[((int64_t)b * D + d) * W::P_ROW + (int64_t)o * L + k]);
+        P = fmul2(P, sc);
+        float2 Y, Yd;
+        pair_repack(P, P, wpair[k], Y, Yd);
+        acc[k] = Y;
+    }
+    __syncthreads();
+    float2 f[E];
+    lds_load_strided<T>(acc, t, f);
+    fft_strided<L, true, false>(f, t, tw, acc);
+    // shared filters: dh[o][d]; per sample: dh[b][o][d]
+    float* dhr = dh + ((int64_t)bs * nod + od) * L;
+#pragma unroll
+    for (int e = 0; e < H; ++e) store_pair(dhr, (uint32_t)(t + T * e), f[e]);
+    // the bias gradient sum_b sum_t dv[t] g[t] is the lag-0 value of the same
+    // correlation that gives dh
+    if (!PER_SAMPLE && t == 0) dbias[od] = f[0].x;
+    if (o == 0 && bs == 0) {
         const float* TW = reinterpret_cast<const float*>(ws + rows * (W::P_ROW + W::G_ROW + W::V_ROW));
         const int64_t C = (int64_t)(N + 1) * D;
         for (int q = t; q < 3 * (N + 1); q += T) {
@@ -476,6 +471,18 @@ k_lds_bwd_finish(const float2* __restrict__ ws, float* __restrict__ dw, float* _
             dw[idx] = sum;
         }
     }
+}
+
+// With a filter set per sample: dbias[o][d] = sum over b (in order) of the lag-0
+// values dh[b][o][d][0], each sample's share of the shared bias's gradient.
+template <int LOGL>
+__global__ void k_lds_bwd_dbias(const float* __restrict__ dh, float* __restrict__ dbias, int B, int nod) {
+    constexpr int64_t L = int64_t(1) << LOGL;
+    const int od = blockIdx.x * blockDim.x + threadIdx.x;
+    if (od >= nod) return;
+    float s = 0.f;
+    for (int b = 0; b < B; ++b) s += dh[((int64_t)b * nod + od) * L];
+    dbias[od] = s;
 }
 
 template <int LOGL, int N>
@@ -489,8 +496,15 @@ inline void launch_lds_backward_n(const LdsBwdArgs& a, hipStream_t st) {
     else
         hipLaunchKernelGGL((k_lds_bwd_rows<LOGL, N, float>), dim3(grid), dim3(T), 0, st, (const float*)a.u, a.w3,
                            a.spec, a.bias, (const float*)a.dy, (float*)a.du, a.ws, a.tw, a.wpair, a.B, a.D, a.sbs);
-    hipLaunchKernelGGL((k_lds_bwd_finish<LOGL, N>), dim3((unsigned)((N - 1) * a.D)), dim3(T), 0, st,
-                       (const float2*)a.ws, a.dw, a.dh, a.dbias, a.tw, a.wpair, a.B, a.D, a.per_sample);
+    if (a.per_sample) {
+        const int nod = (N - 1) * a.D;
+        hipLaunchKernelGGL((k_lds_bwd_finish<LOGL, N, true>), dim3((unsigned)(a.B * nod)), dim3(T), 0, st,
+                           (const float2*)a.ws, a.dw, a.dh, a.dbias, a.tw, a.wpair, a.B, a.D);
+        hipLaunchKernelGGL((k_lds_bwd_dbias<LOGL>), dim3((unsigned)((nod + 255) / 256)), dim3(256), 0, st,
+                           (const float*)a.dh, a.dbias, a.B, nod);
+    } else
+        hipLaunchKernelGGL((k_lds_bwd_finish<LOGL, N, false>), dim3((unsigned)((N - 1) * a.D)), dim3(T), 0, st,
+                           (const float2*)a.ws, a.dw, a.dh, a.dbias, a.tw, a.wpair, a.B, a.D);
 }
 
 template <int LOGL>

@@ -277,7 +277,8 @@ size_t hyena_backward_per_sample_workspace_bytes(hyena_plan_t plan, int64_t B);
  * while dshort_w and dbias, whose parameters every sample shares, are batch sums
  * as in hyena_backward. Every other argument, the workspace (of at least
  * hyena_backward_per_sample_workspace_bytes(plan, B)), the fixed summation order
- * and the errors are those of hyena_backward. */
+ * and the errors are those of hyena_backward; in addition HYENA_ERR_INVALID_ARG
+ * when B*(N-1)*D*L exceeds 2^35 (dh alone would pass 128 GiB). */
 hyena_status_t hyena_backward_per_sample(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
                                          const void* spec, const float* bias, const void* dy, void* du_proj,
                                          float* dshort_w, float* dh, float* dbias, void* workspace,
