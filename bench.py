@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "channel-tokens/s (B·D·L/s) and % HBM peak, Hyena op fwd at L=64K order 2"
 HBM_PEAK_GBS = 8000.0
+VALU_F32_PEAK_TFLOPS = 157.3  # 256 CUs x 4 SIMD x 16 lanes x 2 (FMA) x 2.4 GHz
 
 
 def log(*a):
@@ -47,6 +48,35 @@ def alg_bytes_forward(wl) -> int:
     B, D, L, N = wl.B, wl.D, wl.L, wl.order
     return (s * B * (N + 1) * D * L + s * B * D * L + 8 * (N - 1) * D * (L + 1)
             + 4 * (N + 1) * D * 3 + 4 * (N - 1) * D)
+
+
+def alg_flops_forward(wl) -> float:
+    """Algorithmic flops of one forward: per (b, d) and step a real forward and a real
+    inverse FFT of size 2L at 2.5 n log2 n each, the complex product (6 per bin) and
+    the bias skip (2 per point); per (b, d) the gates (N per point) and the width-3
+    conv of the N+1 channels (5 per point)."""
+    B, D, L, N = wl.B, wl.D, wl.L, wl.order
+    per_step = 10.0 * L * math.log2(2 * L) + 6.0 * (L + 1) + 2.0 * L
+    return B * D * ((N - 1) * per_step + N * L + 5.0 * (N + 1) * L)
+
+
+def device_copy_gbs(torch, dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Bandwidth of a plain device-to-device copy of nbytes (read + write counted),
+    the median of reps copies timed with HIP events: the practical HBM ceiling."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        ev0.record()
+        b.copy_(a)
+        ev1.record()
+        torch.cuda.synchronize()
+        ts.append(ev0.elapsed_time(ev1))
+    del a, b
+    return 2 * nbytes / (float(np.median(ts)) * 1e-3) / 1e9
 
 
 def alg_bytes_backward(wl) -> int:
@@ -872,6 +902,9 @@ def main():
     value = wl.B * wl.D * wl.L / (ms * 1e-3)
     fwd_bytes = alg_bytes_forward(wl)
     hbm_frac = fwd_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)
+    valu_frac = alg_flops_forward(wl) / (ms * 1e-3) / (VALU_F32_PEAK_TFLOPS * 1e12)
+    copy_gbs = device_copy_gbs(torch, dev)
+    log(f"[bench] device copy {copy_gbs:.0f} GB/s")
 
     # per-kernel durations, HIP events on the library's stream around every launch
     fam_ms = {}
@@ -928,6 +961,11 @@ def main():
                    "io_dtype": wl.dtype, "path": plan.path},
         "hbm_frac_forward": round(hbm_frac, 4),
         "alg_bytes_per_step": fwd_bytes,
+        # the same step against the measured copy bandwidth and the fp32 vector peak
+        "copy_gbs": round(copy_gbs, 1),
+        "copy_frac_forward": round(fwd_bytes / (ms * 1e-3) / 1e9 / copy_gbs, 4),
+        "alg_flops_per_step": int(alg_flops_forward(wl)),
+        "valu_frac_forward": round(valu_frac, 4),
         "spectrum_ms": round(spectrum_ms, 4),
         "roofline": roofline,
     }
