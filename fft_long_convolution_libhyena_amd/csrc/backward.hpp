@@ -56,14 +56,13 @@ struct FsBwdArgs {
 };
 
 // Per (b, d) row: the L-point tile T, the gated input's spectra G_o of the N-1
-// steps and the product spectrum P (complex), the recomputed values v_1..v_{N-2}
-// V (fp32), the N+1 channels' staging rows S (fp32), the tap sums of every
-// column-block workgroup; per channel d the dh tile (per row with a filter set per
-// sample, which also keeps every row's lag-0 value). 256-byte aligned.
+// steps and the row's dh tile Tdh (the inverse rows of A_dv * conj(A_g); complex),
+// the recomputed values v_1..v_{N-2} V (fp32), the N+1 channels' staging rows S
+// (fp32), the tap sums of every column-block workgroup; with a filter set per
+// sample also every row's lag-0 value. 256-byte aligned.
 struct FsBwdWs {
     float2* T;
     float2* G;
-    float2* P;
     float* V;
     float* S;
     float2* Tdh;
@@ -82,10 +81,9 @@ inline FsBwdWs fs_bwd_ws(void* base, int64_t B, int64_t D, int64_t L, int ncb, i
     FsBwdWs w;
     w.T = (float2*)take(rows * (size_t)L * 8);
     w.G = (float2*)take((size_t)(N - 1) * rows * (size_t)L * 8);
-    w.P = (float2*)take(rows * (size_t)L * 8);
+    w.Tdh = (float2*)take(rows * (size_t)L * 8);
     w.V = (float*)take((size_t)(N > 2 ? N - 2 : 0) * rows * (size_t)L * 4);
     w.S = (float*)take(rows * (size_t)(N + 1) * (size_t)L * 4);
-    w.Tdh = (float2*)take((per_sample ? rows : (size_t)D) * (size_t)L * 8);
     w.part = (float*)take(rows * (size_t)ncb * 3 * (size_t)(N + 1) * 4);
     w.lag = per_sample ? (float*)take(rows * 4) : nullptr;
     w.bytes = off;

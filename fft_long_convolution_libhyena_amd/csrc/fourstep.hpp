@@ -141,9 +141,10 @@ __device__ __forceinline__ PairSlot pair_slot(int p, int k2, const FsTables& tb)
 // place; or (MODE 1) the scaled spectrum written in place. Backward modes:
 // MODE 2 is MODE 0 that also stores the unpacked spectrum A of the row in `gt`
 // (the gated input's spectrum, in the filter spectrum's layout); MODE 3 takes the
-// row as A_dv, stores A_dv * conj(A_g) in `pt` (A_g read from `gt`) and applies
-// conj(H + bias) instead of H + bias (the correlation that is the adjoint of the
-// convolution).
+// row as A_dv, applies conj(H + bias) instead of H + bias (the correlation that is
+// the adjoint of the convolution) and also takes the product A_dv * conj(A_g) (A_g
+// read from `gt`, the spectrum of dh's correlation) through the same repack and
+// inverse rows into the tile `pt` of the row.
 // A unit is the row pair {p, L1-p} (p >= 1) or {0, L1/2} (p = 0).
 template <int LOG1, int LOG2, int MODE>
 __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ slot, const float2* __restrict__ spec,
@@ -167,6 +168,7 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
     const float2* Hrow = nullptr;
     float bs = 0.f;
     float2 ha[8], hb[8];
+    float2 qa[8], qb[8];  // MODE 3: the repacked dh product of this thread's pairs
     if constexpr (CONV) {
         const uint32_t b = (uint32_t)flat / (uint32_t)D, d = (uint32_t)flat - b * (uint32_t)D;
         Hrow = spec + (int64_t)b * sbs + ((int64_t)o * D + d) * L;
@@ -223,8 +225,8 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
                     gt[(uint32_t)ps.offa] = Ak;
                     gt[(uint32_t)ps.offb] = Am;
                 } else {
-                    pt[(uint32_t)ps.offa] = cmulc(Ak, gt[(uint32_t)ps.offa]);
-                    pt[(uint32_t)ps.offb] = cmulc(Am, gt[(uint32_t)ps.offb]);
+                    const float2 Pk = cmulc(Ak, gt[(uint32_t)ps.offa]), Pm = cmulc(Am, gt[(uint32_t)ps.offb]);
+                    pair_repack(fmul2(Pk, sc), fmul2(Pm, sc), ps.w, qa[e], qb[e]);
                 }
                 pair_repack(hmul(Ak, hadd(ha[e], bs)), hmul(Am, hadd(hb[e], bs)), ps.w, Yk, Ym);
                 au[ps.ra][ps.ia] = Yk;
@@ -232,19 +234,25 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
             } else {
                 float2 A0, AL;  // bins 0 and L (real)
                 pair_unpack(Za, Za, make_float2(1.f, 0.f), A0, AL);
+                [[maybe_unused]] float2 Yd;
                 if constexpr (MODE == 2) {
                     gt[0] = make_float2(A0.x, AL.x);
                 } else {
                     const float2 g0 = gt[0];
-                    pt[0] = make_float2(A0.x * g0.x, AL.x * g0.y);
+                    pair_repack(make_float2(A0.x * g0.x * sc, 0.f), make_float2(AL.x * g0.y * sc, 0.f),
+                                make_float2(1.f, 0.f), qa[e], Yd);
                 }
                 pair_repack(make_float2(A0.x * (ha[e].x + bs), 0.f), make_float2(AL.x * (ha[e].y + bs), 0.f),
                             make_float2(1.f, 0.f), Yk, Ym);
                 au[ps.ra][ps.ia] = Yk;
                 float2 Ah, Ad;  // bin L/2 pairs with itself
                 pair_unpack(Zb, Zb, ps.w, Ah, Ad);
-                if constexpr (MODE == 2) gt[(uint32_t)ps.offb] = Ah;
-                else pt[(uint32_t)ps.offb] = cmulc(Ah, gt[(uint32_t)ps.offb]);
+                if constexpr (MODE == 2) {
+                    gt[(uint32_t)ps.offb] = Ah;
+                } else {
+                    const float2 Ph = cmulc(Ah, gt[(uint32_t)ps.offb]);
+                    pair_repack(fmul2(Ph, sc), fmul2(Ph, sc), ps.w, qb[e], Yd);
+                }
                 const float2 Ch = hmul(Ah, hadd(hb[e], bs));
                 pair_repack(Ch, Ch, ps.w, Yk, Ym);
                 au[ps.rb][ps.ib] = Yk;
@@ -269,6 +277,22 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
         fft_strided<L2, true, false>(v, t, tb.tw2, racc);
 #pragma unroll
         for (int e = 0; e < 16; ++e) rowp[(uint32_t)(t + T2 * e)] = v[e];
+    }
+    if constexpr (MODE == 3) {
+        // the dh product through the same inverse rows, into the row's dh tile
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const PairSlot ps = pair_slot<L1, L2>(p, tp + 2 * T2 * e, tb);
+            au[ps.ra][ps.ia] = qa[e];
+            au[ps.rb][ps.ib] = qb[e];
+        }
+        __syncthreads();
+        lds_load_strided<T2>(racc, t, v);
+        fft_strided<L2, true, false>(v, t, tb.tw2, racc);
+        float2* prow = pt + (uint32_t)k1 * L2;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) prow[(uint32_t)(t + T2 * e)] = v[e];
     }
 }
 

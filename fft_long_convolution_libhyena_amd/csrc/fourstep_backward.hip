@@ -224,66 +224,14 @@ __global__ void k_fs_bwd_du(const float* __restrict__ S, const float* __restrict
     }
 }
 
-// dh by rows: the batch sum of the product spectra of channel d, scaled and
-// repacked for the inverse (the pair step's second half), then inverse rows.
-template <int LOG1, int LOG2>
-__global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::ROW_THREADS))
-k_fs_dh_row(const float2* __restrict__ P, float2* __restrict__ Tdh, FsTables tb, int B, int D) {
-    using Cfg = FsCfg<LOG1, LOG2>;
-    constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T2 = Cfg::T2, U = Cfg::UNITS, RP = Cfg::RP;
-    constexpr int64_t L = (int64_t)L1 * L2;
-    __shared__ float2 lds[2 * U * RP];
-    int64_t dd;
-    int ug;
-    if (!xcd_row_map(blockIdx.x, D, L1 / 2 / U, dd, ug)) return;
-    const int tau = threadIdx.x;
-    const int rho = tau / T2, t = tau % T2;
-    const int p_row = ug * U + rho / 2;
-    const int k1 = (rho & 1) == 0 ? p_row : (p_row == 0 ? L1 / 2 : L1 - p_row);
-    float2* rowp = Tdh + dd * L + (uint32_t)k1 * L2;
-    const RowAcc racc{lds + rho * RP};
-    const int unit = tau / (2 * T2), tp = tau % (2 * T2);
-    const int p = ug * U + unit;
-    const RowAcc au[2] = {RowAcc{lds + (2 * unit) * RP}, RowAcc{lds + (2 * unit + 1) * RP}};
-    // repack + the unnormalised inverse of X gives the 2L-point inverse of 2L*X; the
-    // products carry the factor 4 of the unpacked values: X = P / (8L)
-    const float sc = 1.0f / (8.0f * (float)L);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const PairSlot ps = pair_slot<L1, L2>(p, tp + 2 * T2 * e, tb);
-        float2 Pa = make_float2(0.f, 0.f), Pb = make_float2(0.f, 0.f);
-        for (int b = 0; b < B; ++b) {
-            const float2* Pr = P + ((int64_t)b * D + dd) * L;
-            Pa = cadd(Pa, Pr[(uint32_t)ps.offa]);
-            Pb = cadd(Pb, Pr[(uint32_t)ps.offb]);
-        }
-        float2 Yk, Ym;
-        if (ps.kind == 0) {
-            pair_repack(fmul2(Pa, sc), fmul2(Pb, sc), ps.w, Yk, Ym);
-            au[ps.ra][ps.ia] = Yk;
-            au[ps.rb][ps.ib] = Ym;
-        } else {
-            // slot 0 holds the real bins 0 and L; offb is bin L/2
-            pair_repack(make_float2(Pa.x * sc, 0.f), make_float2(Pa.y * sc, 0.f), make_float2(1.f, 0.f), Yk, Ym);
-            au[ps.ra][ps.ia] = Yk;
-            pair_repack(fmul2(Pb, sc), fmul2(Pb, sc), ps.w, Yk, Ym);
-            au[ps.rb][ps.ib] = Yk;
-        }
-    }
-    __syncthreads();
-    float2 v[16];
-    lds_load_strided<T2>(racc, t, v);
-    fft_strided<L2, true, false>(v, t, tb.tw2, racc);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) rowp[(uint32_t)(t + T2 * e)] = v[e];
-}
-
-// dh by columns: conjugate twiddle, inverse columns, the first half is dh; the
-// workgroup holding sample 0 also writes dbias = dh[0].
+// dh by columns from the rows' dh tiles (pass B's inverse rows of the products):
+// the fixed-order sum of the nb tiles tstride apart (the samples of a channel; one
+// tile with a filter set per sample), conjugate twiddle, inverse columns, the first
+// half is dh; the workgroup holding column 0 also writes dbias = dh[0].
 template <int LOG1, int LOG2>
 __global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::COL_THREADS))
 k_fs_dh_col(const float2* __restrict__ Tdh, float* __restrict__ dh, float* __restrict__ dbias, FsTables tb, int D,
-            int Dch, int64_t bstride) {
+            int Dch, int64_t bstride, int nb, int64_t tstride) {
     using Cfg = FsCfg<LOG1, LOG2>;
     constexpr int L1 = Cfg::L1, L2 = Cfg::L2, T1 = Cfg::T1, CB = Cfg::CB, NCB = L2 / CB;
     constexpr int64_t L = (int64_t)L1 * L2;
@@ -297,7 +245,12 @@ k_fs_dh_col(const float2* __restrict__ Tdh, float* __restrict__ dh, float* __res
     float2 v[16];
     const float2 base = twiddle_base<L2>(tb, t, m2);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = cmulc(slot[(uint32_t)(t + T1 * e) * L2 + m2], twiddle_step<L2>(tb, base, e, m2));
+    for (int e = 0; e < 16; ++e) {
+        const uint32_t i = (uint32_t)(t + T1 * e) * L2 + m2;
+        float2 s = slot[i];
+        for (int b = 1; b < nb; ++b) s = cadd(s, slot[b * tstride + i]);
+        v[e] = cmulc(s, twiddle_step<L2>(tb, base, e, m2));
+    }
     fft_strided<L1, true, false>(v, t, tb.tw1, ColAcc<Cfg::CP>{lds + c});
     // row dd of the tile is filter d = dd mod Dch of sample b = dd / Dch
     const int64_t b = dd / Dch;
@@ -358,22 +311,18 @@ static void fs_backward_launch(const FsBwdArgs& a, hipStream_t st) {
     // the adjoint, last step first: pass B (dh product, conj(H + bias)), dh of the
     // step, then the column pass that finishes the step's gate channel
     for (int o = N - 2; o >= 0; --o) {
-        hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 3>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G, w.P,
-                           a.tb, a.D, o, rows, a.sbs);
+        hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 3>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G,
+                           w.Tdh, a.tb, a.D, o, rows, a.sbs);
         if (!a.per_sample) {
-            // the batch sum of the product spectra, then dh[o][d] and its lag 0
-            hipLaunchKernelGGL((k_fs_dh_row<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, Cfg::L1 / 2 / Cfg::UNITS)),
-                               brow, 0, st, (const float2*)w.P, w.Tdh, a.tb, a.B, a.D);
+            // the fixed-order batch sum of the rows' dh tiles, then dh[o][d] and its lag 0
             hipLaunchKernelGGL((k_fs_dh_col<LOG1, LOG2>), dim3((unsigned)xcd_grid(a.D, NCB)), bcol, 0, st,
                                (const float2*)w.Tdh, a.dh + (int64_t)o * a.D * L, a.dbias + (int64_t)o * a.D, a.tb,
-                               a.D, a.D, (int64_t)0);
+                               a.D, a.D, (int64_t)0, a.B, (int64_t)a.D * L);
         } else {
-            // every row's own product spectrum: dh[b][o][d]; dbias sums the samples' lag 0
-            hipLaunchKernelGGL((k_fs_dh_row<LOG1, LOG2>), dim3((unsigned)xcd_grid(rows, Cfg::L1 / 2 / Cfg::UNITS)),
-                               brow, 0, st, (const float2*)w.P, w.Tdh, a.tb, 1, (int)rows);
+            // every row's own dh tile: dh[b][o][d]; dbias sums the samples' lag 0
             hipLaunchKernelGGL((k_fs_dh_col<LOG1, LOG2>), dim3((unsigned)xcd_grid(rows, NCB)), bcol, 0, st,
                                (const float2*)w.Tdh, a.dh + (int64_t)o * a.D * L, w.lag, a.tb, (int)rows, a.D,
-                               (int64_t)(N - 1) * a.D * L);
+                               (int64_t)(N - 1) * a.D * L, 1, (int64_t)0);
             hipLaunchKernelGGL(k_fs_dbias_sum, dim3((unsigned)((a.D + 255) / 256)), dim3(256), 0, st,
                                (const float*)w.lag, a.dbias + (int64_t)o * a.D, a.B, a.D);
         }

@@ -226,10 +226,9 @@ hyena_status_t hyena_fused_check(hyena_plan_t plan, const void* workspace, int* 
  * (8 bytes per complex or pair value), then 3 floats of short-conv tap sums per
  * (b, channel): 8*B*D*((2N-3)*L + (N-2)*L/2) + 12*B*(N+1)*D.
  * Four-step path: per (b, d) row N+1 L-point complex tiles (the transform, the
- * N-1 gated inputs' spectra, the product spectrum), N-2 fp32 rows of recomputed
- * values and N+1 fp32 staging rows; per channel one complex dh tile; and
- * 12*(N+1) bytes of tap sums per (row, column block); each region 256-byte
- * aligned. Returns 0 for a NULL plan, B < 1, or a circular plan. */
+ * N-1 gated inputs' spectra, the row's share of dh after the inverse rows), N-2
+ * fp32 rows of recomputed values and N+1 fp32 staging rows; and 12*(N+1) bytes
+ * of tap sums per (row, column block); each region 256-byte aligned. Returns 0 for a NULL plan, B < 1, or a circular plan. */
 size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* Backward of the forward hot path: given the upstream gradient dy of y, the
@@ -263,9 +262,8 @@ hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, 
                               float* dh, float* dbias, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace hyena_backward_per_sample needs for batch B: as
- * hyena_backward_workspace_bytes, except on the four-step path, where the complex
- * dh tiles are kept per (b, d) row instead of per channel and B*D floats of
- * per-sample dbias terms are added. Returns 0 for a NULL plan, B < 1, or a
+ * hyena_backward_workspace_bytes, except on the four-step path, where B*D floats
+ * of per-sample dbias terms are added. Returns 0 for a NULL plan, B < 1, or a
  * circular plan. */
 size_t hyena_backward_per_sample_workspace_bytes(hyena_plan_t plan, int64_t B);
 
