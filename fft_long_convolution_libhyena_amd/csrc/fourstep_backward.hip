@@ -202,25 +202,36 @@ k_fs_colinv_bwd(float2* __restrict__ T, const TIO* __restrict__ u, const float* 
 }
 
 // du[b][i*D + d][t] = w2 S_i[t] + w1 S_i[t+1] + w0 S_i[t+2] for the N+1 channels,
-// one thread per pair.
+// four consecutive t per thread (one 16-byte load of S, the next two values for
+// the taps that reach past them, one wide store).
+__device__ __forceinline__ void store_quad(float* __restrict__ row, int64_t q, float4 v) {
+    reinterpret_cast<float4*>(row)[q] = v;
+}
+__device__ __forceinline__ void store_quad(uint16_t* __restrict__ row, int64_t q, float4 v) {
+    reinterpret_cast<uint2*>(row)[q] = make_uint2(f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16),
+                                                  f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16));
+}
+
 template <class TIO>
-__global__ void k_fs_bwd_du(const float* __restrict__ S, const float* __restrict__ w3, TIO* __restrict__ du,
-                            int D, int N, int64_t L, int64_t rows) {
-    const int64_t pairs = L / 2;
-    const int64_t m = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (m >= pairs) return;
+__global__ void __launch_bounds__(256)
+k_fs_bwd_du(const float* __restrict__ S, const float* __restrict__ w3, TIO* __restrict__ du, int D, int N,
+            int64_t L, int64_t rows) {
+    const int64_t quads = L / 4;
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= quads) return;
     const int nc = N + 1;
     for (int64_t ri = blockIdx.y; ri < rows * nc; ri += gridDim.y) {
         const int64_t r = ri / nc;
         const int i = (int)(ri - r * nc);
         const int64_t b = r / D, d = r - b * D;
         const float* s = S + ri * L;
-        const float2 dc = make_float2(s[2 * m], s[2 * m + 1]);
-        const float2 nx = 2 * m + 2 < L ? make_float2(s[2 * m + 2], s[2 * m + 3]) : make_float2(0.f, 0.f);
+        const float4 c = reinterpret_cast<const float4*>(s)[q];
+        const float2 nx = q + 1 < quads ? reinterpret_cast<const float2*>(s)[2 * q + 2] : make_float2(0.f, 0.f);
         const float* w = w3 + 3 * ((int64_t)i * D + d);
-        store_pair(du + (b * nc * D + (int64_t)i * D + d) * L, (uint32_t)m,
-                   make_float2(fmaf(w[2], dc.x, fmaf(w[1], dc.y, w[0] * nx.x)),
-                               fmaf(w[2], dc.y, fmaf(w[1], nx.x, w[0] * nx.y))));
+        const float w0 = w[0], w1 = w[1], w2 = w[2];
+        store_quad(du + (b * nc * D + (int64_t)i * D + d) * L, q,
+                   make_float4(fmaf(w2, c.x, fmaf(w1, c.y, w0 * c.z)), fmaf(w2, c.y, fmaf(w1, c.z, w0 * c.w)),
+                               fmaf(w2, c.z, fmaf(w1, c.w, w0 * nx.x)), fmaf(w2, c.w, fmaf(w1, nx.x, w0 * nx.y))));
     }
 }
 
@@ -333,10 +344,10 @@ static void fs_backward_launch(const FsBwdArgs& a, hipStream_t st) {
             hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColTail0>), dim3(gcol), bcol, 0, st, w.T, u,
                                a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
     }
-    const int64_t pairs = L / 2;
+    const int64_t quads = L / 4;
     const int64_t nrc = rows * (N + 1);
     const unsigned gy = (unsigned)(nrc < 65535 ? nrc : 65535);
-    hipLaunchKernelGGL((k_fs_bwd_du<TIO>), dim3((unsigned)((pairs + 255) / 256), gy), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_fs_bwd_du<TIO>), dim3((unsigned)((quads + 255) / 256), gy), dim3(256), 0, st,
                        (const float*)w.S, a.w3, (TIO*)a.du, a.D, N, L, rows);
     hipLaunchKernelGGL(k_fs_bwd_dw, dim3((unsigned)a.D), dim3(64), 0, st, (const float*)w.part, a.dw, a.B, a.D, N,
                        NCB);
