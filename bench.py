@@ -422,6 +422,16 @@ def bench_operator(args, wl, x, torch, Plan):
                    "path": plan.path, "pass": "operator"},
         "roofline": roof,
     }
+    if args.check:
+        import oracle
+
+        # the first tokens of the first sequence: the operator is causal, so they
+        # depend on those tokens alone
+        Lp = min(L, 1024)
+        ref = oracle.operator_forward(p.x[:1, :Lp], p.w_in, p.b_in, x.short_w, x.h[:, :, :Lp], x.bias, p.w_out,
+                                      p.b_out, N)
+        res["check_rel_l2"] = oracle.rel_l2(out[:1, :Lp].double().cpu().numpy(), ref)
+        log(f"[bench] oracle check on the first {Lp} tokens of sequence 0: rel_l2 {res['check_rel_l2']:.3e}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (operator oracle) ...")
         res["cpu_baseline"] = cpu_baseline_operator(x, p, wl, args.cpu_budget)
