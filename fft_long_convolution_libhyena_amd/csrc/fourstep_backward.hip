@@ -256,12 +256,14 @@ k_fs_dh_col(const float2* __restrict__ Tdh, float* __restrict__ dh, float* __res
     float2 v[16];
     const float2 base = twiddle_base<L2>(tb, t, m2);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const uint32_t i = (uint32_t)(t + T1 * e) * L2 + m2;
-        float2 s = slot[i];
-        for (int b = 1; b < nb; ++b) s = cadd(s, slot[b * tstride + i]);
-        v[e] = cmulc(s, twiddle_step<L2>(tb, base, e, m2));
+    for (int e = 0; e < 16; ++e) v[e] = slot[(uint32_t)(t + T1 * e) * L2 + m2];
+    for (int b = 1; b < nb; ++b) {  // the other samples' tiles, each loaded together
+        const float2* sb = slot + b * tstride;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = cadd(v[e], sb[(uint32_t)(t + T1 * e) * L2 + m2]);
     }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = cmulc(v[e], twiddle_step<L2>(tb, base, e, m2));
     fft_strided<L1, true, false>(v, t, tb.tw1, ColAcc<Cfg::CP>{lds + c});
     // row dd of the tile is filter d = dd mod Dch of sample b = dd / Dch
     const int64_t b = dd / Dch;

@@ -421,22 +421,29 @@ k_lds_bwd_finish(const float2* __restrict__ ws, float* __restrict__ dw, float* _
     // repack + the unnormalised L-point inverse of X gives the 2L-point inverse of
     // 2L*X; the products carry the factor 4 of the unpacked values: X = P / (8L)
     const float sc = 1.0f / (8.0f * (float)L);
+    // the sum over the samples, each sample's values of this thread loaded together
+    float2 Ck[H], Cm[H];
+#pragma unroll
+    for (int e = 0; e < H; ++e) Ck[e] = Cm[e] = make_float2(0.f, 0.f);
+    for (int b = b_lo; b < b_hi; ++b) {
+        const float2* Pw = ws + ((int64_t)b * D + d) * W::P_ROW + (int64_t)o * L;
+#pragma unroll
+        for (int e = 0; e < H; ++e) {
+            const uint32_t k = t + T * e;
+            Ck[e] = cadd(Ck[e], Pw[k]);
+            if (k != 0) Cm[e] = cadd(Cm[e], Pw[L - k]);
+        }
+    }
 #pragma unroll
     for (int e = 0; e < H; ++e) {
         const uint32_t k = t + T * e;
         const uint32_t km = k == 0 ? 0 : L - k;
-        float2 Ck = make_float2(0.f, 0.f), Cm = make_float2(0.f, 0.f);
-        for (int b = b_lo; b < b_hi; ++b) {
-            const float2* Pw = ws + ((int64_t)b * D + d) * W::P_ROW + (int64_t)o * L;
-            Ck = cadd(Ck, Pw[k]);
-            if (k != 0) Cm = cadd(Cm, Pw[km]);
-        }
         float2 Yk, Ym;
         if (k != 0) {
-            pair_repack(fmul2(Ck, sc), fmul2(Cm, sc), wpair[k], Yk, Ym);
+            pair_repack(fmul2(Ck[e], sc), fmul2(Cm[e], sc), wpair[k], Yk, Ym);
         } else {
             // slot 0 holds the real bins 0 and L
-            pair_repack(make_float2(Ck.x * sc, 0.f), make_float2(Ck.y * sc, 0.f), wpair[0], Yk, Ym);
+            pair_repack(make_float2(Ck[e].x * sc, 0.f), make_float2(Ck[e].y * sc, 0.f), wpair[0], Yk, Ym);
         }
         acc[k] = Yk;
         if (k != 0) acc[km] = Ym;
