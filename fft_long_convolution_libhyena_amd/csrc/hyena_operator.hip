@@ -1,6 +1,6 @@
 // The whole Hyena operator forward around the hot path (HyenaDNA walkthrough,
-// section 2.1, HyenaOperator.forward): the input projection, the b l d -> b d l
-// rearrange, the hot path (hyena_forward), the b d l -> b l d rearrange and the
+// section 2.1, HyenaOperator.forward): the input projection, the (B, L, D) ->
+// (B, D, L) transpose, the hot path (hyena_forward), the transpose back and the
 // output projection. The two projections are plain dense GEMMs and run in
 // hipBLASLt (bf16 or fp32 operands, fp32 accumulation); the rearranges cost
 // nothing because both GEMMs read and write the layouts the path uses directly:

@@ -2,7 +2,7 @@
 // HyenaFilter.filter and its constructor): the positional features of every time
 // step, a Linear(emb_dim -> W) / Sin stack with num_inner further Linear(W -> W) /
 // Sin layers, a Linear(W -> (N-1)*D) without bias, the exponential modulation, and
-// the 'l (o d) -> o d l' rearrange of section 2.1, written straight into the
+// the [L, (N-1)*D] -> [N-1][D][L] reshape of section 2.1, written straight into the
 // h[o][d][t] layout that hyena_filter_spectrum reads.
 //
 // Readings where the pages give no formula: t = tau / L; the features are

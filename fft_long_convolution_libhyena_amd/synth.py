@@ -6,7 +6,7 @@ fp64 oracle and the HIP library consume exactly the arrays produced here.
 
 Shapes follow the operator as written in the HyenaDNA walkthrough (page "HyenaDNA
 model architecture", section 2.1, HyenaOperator code): ``u_proj`` is the
-in-projected activation after the ``b l d -> b d l`` rearrange, of shape
+in-projected activation after the (B, L, D) -> (B, D, L) transpose, of shape
 [B, (N+1)*D, L]; the long filters are ``k`` rearranged to [N-1, D, L]; the
 long-filter bias is [N-1, D] (HyenaFilter code, section 2.2: ``torch.randn``
 initialisation); the short depthwise Conv1d weight is [(N+1)*D, 3].

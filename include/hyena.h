@@ -16,7 +16,7 @@
  * evaluated by FFT on the sequence zero-padded to 2L (the HyenaND summary's
  * boundary handling; the Hyena Hierarchy concept page, section 3.2, FFT
  * acceleration). hyena_operator_forward adds the module's in/out projections and
- * its b l d <-> b d l rearranges around the path; dropout is the identity; the
+ * its (B, L, D) <-> (B, D, L) transposes around the path; dropout is the identity; the
  * short Conv1d bias is taken as zero.
  *
  * Conventions for every call:
@@ -175,8 +175,8 @@ hyena_status_t hyena_filter_spectrum_batched(hyena_plan_t plan, int64_t B, const
  *           w[0]*u[t-2] + w[1]*u[t-1] + w[2]*u[t] with u[t<0] = 0
  *   spec    from hyena_filter_spectrum of a plan with the same L, D, order, path
  *   bias    [N-1][D] fp32, device: the bias skip term of step o is bias[o][d]*v
- *   y       [B][D][L] of the plan dtype, device (output, before the b d l ->
- *           b l d rearrange)
+ *   y       [B][D][L] of the plan dtype, device (output, before the transpose
+ *           to [B][L][D])
  *   workspace / workspace_bytes: device scratch, at least 8*L bytes on the
  *           four-step path and 8*L (order 2) or 12*L bytes on the partitioned
  *           path (see hyena_workspace_bytes); ignored (may be NULL) on the LDS
@@ -289,8 +289,8 @@ hyena_status_t hyena_backward_per_sample(hyena_plan_t plan, int64_t B, const voi
 size_t hyena_operator_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* The whole operator forward around the hot path (HyenaDNA walkthrough, section
- * 2.1, HyenaOperator.forward): in_proj, b l d -> b d l, the hot path as in
- * hyena_forward, b d l -> b l d, out_proj:
+ * 2.1, HyenaOperator.forward): in_proj, the (B, L, D) -> (B, D, L) transpose, the
+ * hot path as in hyena_forward, the transpose back, out_proj:
  *   u_proj[b][c][t] = sum_k w_in[c][k] x[b][t][k] + b_in[c]
  *   out[b][t][j]    = sum_d w_out[j][d] y[b][d][t] + b_out[j]
  *   x     [B][L][D] of the plan dtype, device
@@ -349,7 +349,7 @@ typedef struct hyena_filter_mlp_s {
 
 /* The implicit long filters of the plan (HyenaDNA walkthrough, section 2.2,
  * HyenaFilter.filter: positional embedding, the Linear/Sin stack, modulation; and
- * the 'l (o d) -> o d l' rearrange of section 2.1). For tau = 0..L-1, t = tau/L:
+ * the [L, (N-1)*D] -> [N-1][D][L] reshape of section 2.1). For tau = 0..L-1, t = tau/L:
  *   z    = (t, sin(2 pi f_1 t) .. sin(2 pi f_K t), cos(2 pi f_1 t) .. cos(2 pi f_K t))
  *   a    = sin(sin_freq * (w_in z + b_in)),  then M times  a = sin(sin_freq * (w_inner[m] a + b_inner[m]))
  *   h[o][d][tau] = exp(-alpha[c] t) * sum_j w_out[c][j] a[j],   c = o*D + d

@@ -384,7 +384,7 @@ def operator_forward(x: np.ndarray, w_in: np.ndarray, b_in: np.ndarray, short_w:
                      threads: int = 0) -> np.ndarray:
     """The whole operator forward in fp64 (HyenaDNA walkthrough, section 2.1,
     HyenaOperator.forward): u = in_proj(x) = x w_in^T + b_in on x [B, L, D]; the
-    b l d -> b d l rearrange; the hot path (``forward``); the b d l -> b l d
+    (B, L, D) -> (B, D, L) transpose; the hot path (``forward``); the (B, D, L) -> (B, L, D)
     rearrange; out_proj = y w_out^T + b_out. The projections are numpy matrix
     products in fp64. Returns [B, L, D] float64."""
     x64 = np.asarray(x, dtype=np.float64)
@@ -413,7 +413,7 @@ def implicit_filter(L: int, D: int, order: int, p) -> np.ndarray:
     section 2.2, HyenaFilter.filter): z, t = pos_emb(L); h = implicit_filter(z), the
     stack Linear(emb_dim -> W), Sin, then num_inner times (Linear(W -> W), Sin), then
     Linear(W -> (N-1)*D) without bias; h = modulation(t, h); and the
-    'l (o d) -> o d l' rearrange of section 2.1, so channel c = o*D + d.
+    reshape of section 2.1 from [L, (N-1)*D] to [N-1][D][L], so channel c = o*D + d.
     Readings taken where the formulas are absent: Sin(x) = sin(sin_freq * x)
     elementwise, one frequency vector shared by every Sin of the stack (the code
     appends the same activation module after each Linear); the modulation multiplies
@@ -431,7 +431,7 @@ def implicit_filter(L: int, D: int, order: int, p) -> np.ndarray:
     C = (order - 1) * D
     if h.shape != (L, C):
         raise ValueError(f"w_out has {h.shape[1]} rows, the plan needs (order-1)*D = {C}")
-    return np.ascontiguousarray(h.T.reshape(order - 1, D, L))                    # l (o d) -> o d l
+    return np.ascontiguousarray(h.T.reshape(order - 1, D, L))                    # [L, (N-1)*D] -> [N-1][D][L]
 
 
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:

@@ -7,15 +7,16 @@
  *
  * What it computes (sources are the pages' own sections):
  *   - HyenaDNA walkthrough, section 2.1 (HyenaOperator code): the short filter is
- *     nn.Conv1d(C, C, 3, padding=2, groups=C) whose output is cut to the first L
- *     samples, then split into gates x_0..x_{N-1} and the value v (last chunk);
- *     then for o = 0..N-2 the value is gated by x_{N-1-o} (the reversed x[1:]
- *     list) and passed through the long filter k[o] with bias[o]; finally
- *     y = v * x_0.
+ *     a depthwise width-3 convolution over every channel, padded by two and cut
+ *     to the first L samples; its output splits into gates x_0..x_{N-1} and the
+ *     value v (the last group of D channels); then for o = 0..N-2 the value is
+ *     gated by x_{N-1-o} (the gates x_{N-1}..x_1 taken last to first) and passed
+ *     through the long filter k[o] with bias[o]; finally y = v * x_0.
  *   - HyenaDNA walkthrough, section 2.2 (HyenaFilter code): the long filter step
- *     is fftconv(x, k, bias), described as equivalent to Conv1d(x, k): a
- *     per-channel long convolution plus a bias term.
- *   - HyenaND summary, methodology ("boundary handling"): the non-circular
+ *     is an FFT convolution of the value with the filter and a bias, which the
+ *     page equates with a per-channel Conv1d: a per-channel long convolution plus
+ *     a bias term.
+ *   - HyenaND summary, methodology (its boundary-handling item): the non-circular
  *     convolution is obtained by zero-padding to twice the length.
  * Readings taken where the pages are silent: the convolution is causal with zero
  * initial state, conv(v,h)[t] = sum_{s<=t} h[s] v[t-s]; the bias is a skip term

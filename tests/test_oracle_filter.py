@@ -1,6 +1,6 @@
 """Pins of the fp64 implicit-filter oracle (HyenaDNA walkthrough, section 2.2,
 HyenaFilter: positional embedding -> Linear/Sin stack -> Linear without bias ->
-exponential modulation -> 'l (o d) -> o d l'), CPU only.
+exponential modulation -> the [L, (N-1)*D] to [N-1][D][L] reshape), CPU only.
 
 Closed forms fix each stage on its own: a stack whose hidden units are all exactly
 one leaves only the output weights, the modulation and the layout; identity weights
@@ -131,7 +131,7 @@ def test_matches_float64_torch_module(E, W, M, order):
         t = torch.arange(L, dtype=f64) / L
         ang = 2 * torch.pi * t[:, None] * torch.tensor(p.band_freq)[None, :]
         z = torch.cat([t[:, None], torch.sin(ang), torch.cos(ang)], dim=1)
-        k = net(z) * torch.exp(-t[:, None] * torch.tensor(p.alpha)[None, :])  # [L, (o d)]
+        k = net(z) * torch.exp(-t[:, None] * torch.tensor(p.alpha)[None, :])  # [L, (N-1)*D]
         want = k.T.reshape(order - 1, D, L).numpy()
     got = oracle.implicit_filter(L, D, order, p)
     assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
