@@ -77,3 +77,12 @@ def test_kernel_families_cover_the_summaries():
                                       "k_implicit_filter", "k_part_inv") if f[4:].startswith(k))
             for src in bench.KERNEL_SOURCES[bench.kernel_family(kernel)]:
                 assert os.path.exists(os.path.join(bench._CSRC, src)), src
+
+
+def test_cpu_baseline_of_the_small_workload_times_the_direct_definition():
+    """At L <= 1024 the CPU baseline also times the O(L^2) oracle over the whole input."""
+    w = synth.WORKLOADS["tiny"]
+    x = synth.generate(w)
+    res = bench.cpu_baseline(x, w, 1.0)
+    assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
+    assert res["direct"]["value"] > 0 and "direct" in res["direct"]["sample"]
