@@ -49,9 +49,13 @@ class FilterMLPStruct(ctypes.Structure):
 
 
 class HyenaError(RuntimeError):
-    def __init__(self, call: str, status: int):
+    def __init__(self, call: str, status: int, detail: str = ""):
         self.status = status
-        super().__init__(f"{call} failed: {STATUS.get(status, status)}")
+        super().__init__(f"{call} failed: {STATUS.get(status, status)}" + (f" ({detail})" if detail else ""))
+
+
+def _env_flag(name: str) -> bool:
+    return os.environ.get(name, "") not in ("", "0")
 
 
 _lib = None
@@ -152,8 +156,20 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 
 def _check(call: str, st: int) -> None:
+    """Raise HyenaError for a failed call. With HYENA_DEBUG_SYNC set (debugging
+    only), every call that queued work is also followed by a device
+    synchronisation, so that an asynchronous kernel error is reported against the
+    call that launched it (as HYENA_ERR_DEVICE) instead of a later one."""
     if st != 0:
         raise HyenaError(call, st)
+    if _env_flag("HYENA_DEBUG_SYNC"):
+        import torch
+
+        if torch.cuda.is_available():
+            try:
+                torch.cuda.synchronize()
+            except RuntimeError as e:
+                raise HyenaError(call, 4, f"after synchronisation: {e}") from e
 
 
 def _stream_handle(torch, device) -> int:
@@ -165,7 +181,14 @@ class Plan:
 
     def __init__(self, L: int, D: int, order: int, dtype: str = "f32", path: str = "auto",
                  circular: bool = False):
+        """path "auto" lets the library choose; the environment variable
+        HYENA_FORCE_PATH (lds, fourstep or partitioned) overrides that choice for
+        plans created with path "auto" (a debugging switch, e.g. to run the four-step
+        passes at sizes the LDS kernel would take)."""
         import torch  # device memory and streams only
+
+        if path == "auto" and os.environ.get("HYENA_FORCE_PATH"):
+            path = os.environ["HYENA_FORCE_PATH"]
 
         self._torch = torch
         self.lib = load_library()

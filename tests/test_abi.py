@@ -167,3 +167,21 @@ def test_valid_plan_without_gpu_reports_device_error(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError):
         binding.load_library(str(tmp_path / "missing.so"))
+
+
+def test_debug_switches_on_the_host(monkeypatch):
+    """HYENA_DEBUG_SYNC leaves successful calls alone where no device is present and
+    still raises for failed ones; HYENA_FORCE_PATH must name a path."""
+    from fft_long_convolution_libhyena_amd import HyenaError, Plan, binding
+
+    monkeypatch.setenv("HYENA_DEBUG_SYNC", "1")
+    assert binding._env_flag("HYENA_DEBUG_SYNC")
+    binding._check("hyena_forward", 0)
+    with pytest.raises(HyenaError) as e:
+        binding._check("hyena_forward", 3)
+    assert e.value.status == 3 and "hyena_forward" in str(e.value)
+    monkeypatch.setenv("HYENA_DEBUG_SYNC", "0")
+    assert not binding._env_flag("HYENA_DEBUG_SYNC")
+    monkeypatch.setenv("HYENA_FORCE_PATH", "no-such-path")
+    with pytest.raises(ValueError):
+        Plan(1024, 4, 2)
