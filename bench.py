@@ -784,8 +784,10 @@ def bench_convnd(args, torch, nd: int):
         "config": {"workload": f"conv{nd}d {grid}" + (" circular" if circ else ""), "B": B, "D": D,
                    "grid": list(dims), "pass": f"conv{nd}d_forward"},
         "hbm_frac_forward": round(achieved / HBM_PEAK_GBS, 4),
+        # traffic: the committed counter summary of the zero-padded step (all launches of one step)
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if circ else measured_traffic(f"k_c{nd}_conv{nd}d", grid),
                      "kernel": f"{nd}-D passes (whole step)", "alg_bytes_per_launch": nbytes,
                      "launch_ms": round(ms, 5), "launches_per_step": 1},
     }

@@ -74,7 +74,8 @@ def test_kernel_families_cover_the_summaries():
     for f in os.listdir(os.path.join(ROOT, "profiles")):
         if f.startswith("pmc_"):
             kernel = next(k for k in ("k_fs_row", "k_lds_forward", "k_lds_bwd_rows", "fs_backward",
-                                      "k_implicit_filter", "k_part_inv") if f[4:].startswith(k))
+                                      "k_implicit_filter", "k_part_inv", "k_c2_conv2d", "k_c3_conv3d")
+                          if f[4:].startswith(k))
             for src in bench.KERNEL_SOURCES[bench.kernel_family(kernel)]:
                 assert os.path.exists(os.path.join(bench._CSRC, src)), src
 
