@@ -14,10 +14,11 @@
 //  rows; keeps A_{g_o} in G_o) -> T, then a column pass: MID (v_{o+1} -> V, the
 //  next gated input by columns -> T) or, after the last step, HEAD (dx_0 -> S_0,
 //  dv_{N-1} by columns -> T);
-//  for o = N-2 .. 0: pass B mode 3 (P = A_dv conj(A_{g_o}), conj(H + bias), inverse
-//  rows) -> T, P; dh_o by rows and columns from the fixed-order batch sum of P
-//  (dbias_o its lag-0 value); then TAILMID (dx_{N-1-o} -> S, dv_o by columns -> T)
-//  or, at o = 0, TAIL0 (dx_{N-1} and dv_0 -> S);
+//  for o = N-2 .. 0: pass B mode 3 (conj(H + bias), inverse rows -> T; the product
+//  A_dv conj(A_{g_o}) through the same inverse rows -> the row's dh tile); dh_o by
+//  columns from the fixed-order sum of a channel's dh tiles over the batch (dbias_o
+//  its lag-0 value); then TAILMID (dx_{N-1-o} -> S, dv_o by columns -> T) or, at
+//  o = 0, TAIL0 (dx_{N-1} and dv_0 -> S);
 //  du = conv3^T of the N+1 staged channels; dshort_w from the tap sums.
 // Every sum over the batch or over workgroups is taken in a fixed order.
 #include <hip/hip_runtime.h>
