@@ -39,7 +39,10 @@ def _run(args):
 @pytest.mark.parametrize("mode,workload", [
     ([], "tiny"), ([], "dna_small"), (["--backward"], "tiny"), (["--backward", "--per-sample"], "tiny"),
     (["--per-sample"], "tiny"), (["--circular"], "tiny"), (["--operator"], "tiny"), (["--filter"], "tiny"),
-    (["--path", "fourstep"], "tiny"), (["--conv2d"], None), (["--conv3d", "--circular"], None)])
+    (["--path", "fourstep"], "tiny"), (["--conv2d"], None), (["--conv3d", "--circular"], None),
+    # full workloads in the launch configuration the benchmark times, checked on sampled outputs
+    (["--circular"], "long64k"), (["--circular"], "lm125m"), (["--path", "partitioned"], "long64k"),
+    (["--operator"], "lm125m"), (["--per-sample"], "long64k"), (["--backward", "--per-sample"], "lm125m")])
 def test_bench_line(mode, workload):
     args = mode + COMMON + (["--workload", workload] if workload else [])
     out = _run(args)
