@@ -185,3 +185,25 @@ def test_debug_switches_on_the_host(monkeypatch):
     monkeypatch.setenv("HYENA_FORCE_PATH", "no-such-path")
     with pytest.raises(ValueError):
         Plan(1024, 4, 2)
+
+
+def test_plain_c_client_compiles_links_and_runs(tmp_path):
+    """include/hyena.h is a C header: a C99 program includes it, links against the
+    built libhyena.so and gets the documented statuses from the host-checked calls."""
+    import shutil
+    import subprocess
+
+    from fft_long_convolution_libhyena_amd import binding
+
+    if shutil.which("gcc") is None or not os.path.exists(binding.LIB_PATH):
+        pytest.skip("gcc or the built library is missing")
+    libdir = os.path.dirname(binding.LIB_PATH)
+    exe = tmp_path / "c_client"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                    "-I", os.path.join(ROOT, "include"), "-isystem", "/opt/rocm/include",
+                    os.path.join(ROOT, "tests", "sanitize", "c_client.c"), "-o", str(exe),
+                    "-L", libdir, "-lhyena", "-Wl,-rpath," + libdir], check=True, capture_output=True,
+                   text=True, timeout=120)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 unexpected" in r.stdout
