@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "channel-tokens/s (B·D·L/s) and % HBM peak, Hyena op fwd at L=64K order 2"
 HBM_PEAK_GBS = 8000.0
-VALU_F32_PEAK_TFLOPS = 157.3  # 256 CUs x 4 SIMD x 16 lanes x 2 (FMA) x 2.4 GHz
+VALU_F32_PEAK_TFLOPS = 157.3  # published: 256 CUs x 128 fp32 lanes/clk (packed) x 2 (FMA) x 2.4 GHz
 
 
 def log(*a):
