@@ -410,34 +410,43 @@ def positional_embedding(L: int, band_freq: np.ndarray):
 
 def implicit_filter(L: int, D: int, order: int, p) -> np.ndarray:
     """The implicit long filters h [N-1, D, L] in float64 (HyenaDNA walkthrough,
-    section 2.2, HyenaFilter.filter): z, t = pos_emb(L); h = implicit_filter(z), the
-    stack Linear(emb_dim -> W), Sin, then num_inner times (Linear(W -> W), Sin), then
-    Linear(W -> (N-1)*D) without bias; h = modulation(t, h); and the
-    reshape of section 2.1 from [L, (N-1)*D] to [N-1][D][L], so channel c = o*D + d.
-    Readings taken where the formulas are absent: Sin(x) = sin(sin_freq * x)
-    elementwise, one frequency vector shared by every Sin of the stack (the code
-    appends the same activation module after each Linear); the modulation multiplies
-    channel c by exp(-alpha_c * t) with the same t as the embedding. `p` carries the
+    section 2.2, the HyenaFilter module and its filter method).
+
+    With z(tau) the positional embedding of step tau and t = tau / L:
+        a_0     = sin(f * (W_in z + b_in))
+        a_m     = sin(f * (W_m a_{m-1} + b_m)),   m = 1 .. num_inner
+        g_c     = (W_out a_last)_c                (no bias)
+        h[c, tau] = g_c * exp(-alpha_c * t)
+    for the (N-1)*D output channels c = o*D + d, which are laid out as h[o][d][tau]
+    (section 2.1 reshapes the time-major filter into that order).  Readings taken
+    where the formulas are absent: the activation is an elementwise sine of the
+    pre-activation scaled by a per-unit frequency vector f, one vector for every
+    layer (the walkthrough builds a single activation object and reuses it after
+    each linear layer); the modulation's t is the embedding's t.  `p` carries the
     fields of synth.FilterMLP."""
     z, t = positional_embedding(L, p.band_freq)
     freq = np.asarray(p.sin_freq, np.float64)
-    a = z @ np.asarray(p.w_in, np.float64).T + np.asarray(p.b_in, np.float64)   # Linear(emb_dim, W)
-    a = np.sin(freq * a)                                                         # Sin
+    a = np.sin(freq * (z @ np.asarray(p.w_in, np.float64).T + np.asarray(p.b_in, np.float64)))
     for m in range(np.asarray(p.w_inner).shape[0]):
-        a = a @ np.asarray(p.w_inner[m], np.float64).T + np.asarray(p.b_inner[m], np.float64)  # Linear(W, W)
-        a = np.sin(freq * a)                                                     # Sin
-    h = a @ np.asarray(p.w_out, np.float64).T                                    # Linear(W, C), no bias
-    h = h * np.exp(-np.outer(t, np.asarray(p.alpha, np.float64)))               # modulation(t, h)
+        a = np.sin(freq * (a @ np.asarray(p.w_inner[m], np.float64).T + np.asarray(p.b_inner[m], np.float64)))
+    g = a @ np.asarray(p.w_out, np.float64).T
+    h = g * np.exp(-np.outer(t, np.asarray(p.alpha, np.float64)))
     C = (order - 1) * D
     if h.shape != (L, C):
         raise ValueError(f"w_out has {h.shape[1]} rows, the plan needs (order-1)*D = {C}")
-    return np.ascontiguousarray(h.T.reshape(order - 1, D, L))                    # [L, (N-1)*D] -> [N-1][D][L]
+    return np.ascontiguousarray(h.T.reshape(order - 1, D, L))
 
 
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
-    """||got - ref||_2 / ||ref||_2 with got widened to fp64."""
+    """||got - ref||_2 / ||ref||_2 over every element, with got widened to fp64.
+
+    The two arrays must have the same shape (no broadcasting: a mis-shaped result
+    raises instead of being compared against a stretched reference).  With an
+    all-zero reference the absolute norm ||got||_2 is returned."""
     g = np.asarray(got, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
+    if g.shape != r.shape:
+        raise ValueError(f"rel_l2: shape {g.shape} of the result differs from the reference's {r.shape}")
     den = float(np.linalg.norm(r.ravel()))
     num = float(np.linalg.norm((g - r).ravel()))
     return num / den if den > 0 else num

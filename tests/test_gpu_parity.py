@@ -108,6 +108,20 @@ SMALL = [
     (2, 3, 4096, 2, "f32", "fourstep"),
     (1, 2, 8192, 3, "f32", "fourstep"),
     (1, 2, 16384, 2, "f32", "fourstep"),
+    # orders 5 to 8: every order the plan accepts runs through the forward kernels
+    (1, 3, 1024, 5, "f32", "lds"),
+    (2, 2, 1024, 6, "bf16", "lds"),
+    (1, 2, 1024, 7, "f32", "lds"),
+    (1, 2, 1024, 8, "f32", "lds"),
+    (1, 2, 16384, 5, "f32", "lds"),
+    (1, 2, 16384, 8, "f32", "lds"),
+    (1, 2, 16384, 8, "bf16", "lds"),
+    (1, 3, 4096, 5, "f32", "fourstep"),
+    (1, 2, 4096, 6, "f32", "fourstep"),
+    (2, 2, 4096, 7, "bf16", "fourstep"),
+    (1, 2, 4096, 8, "f32", "fourstep"),
+    (1, 2, 65536, 5, "f32", "fourstep"),
+    (1, 1, 65536, 8, "f32", "fourstep"),
 ]
 
 

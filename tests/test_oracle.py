@@ -248,3 +248,41 @@ def test_chain_rejects_bad_shapes():
     x = synth.generate(wl)
     with pytest.raises(ValueError):
         oracle.forward(x.u_proj, x.short_w, x.h, x.bias, 3)
+
+
+# ------------------------------------------------------------ the comparison
+
+
+def test_rel_l2_hand_computed_values():
+    # every expected value is worked by hand from the definition ||g - r|| / ||r||
+    assert oracle.rel_l2(np.array([1.0, 2.0, 2.0]), np.array([1.0, 2.0, 2.0])) == 0.0
+    # g - r = (0, 2, 2): norm sqrt(8); ||r|| = 1
+    assert oracle.rel_l2(np.array([1.0, 2.0, 2.0]), np.array([1.0, 0.0, 0.0])) == pytest.approx(np.sqrt(8.0), rel=1e-15)
+    # the same pair swapped: ||r|| is now 3, so the value is sqrt(8)/3, not sqrt(8)
+    assert oracle.rel_l2(np.array([1.0, 0.0, 0.0]), np.array([1.0, 2.0, 2.0])) == pytest.approx(np.sqrt(8.0) / 3.0,
+                                                                                               rel=1e-15)
+    # a 2-D pair reduces over every element: diff ((0,-1),(-1,0)) has norm sqrt(2); ||r|| = 2
+    assert oracle.rel_l2(np.array([[1.0, 0.0], [0.0, 1.0]]), np.ones((2, 2))) == pytest.approx(np.sqrt(2.0) / 2.0,
+                                                                                              rel=1e-15)
+    # a scaled result: g = (1 + eps) r gives exactly eps
+    r = np.array([3.0, -4.0])
+    assert oracle.rel_l2(1.25 * r, r) == pytest.approx(0.25, rel=1e-15)
+
+
+def test_rel_l2_zero_reference_gives_absolute_norm():
+    # ||r|| = 0: the absolute error ||g|| is returned (3-4-5 triangle)
+    assert oracle.rel_l2(np.array([3.0, 4.0]), np.zeros(2)) == pytest.approx(5.0, rel=1e-15)
+    assert oracle.rel_l2(np.zeros(4), np.zeros(4)) == 0.0
+
+
+def test_rel_l2_widens_the_result_to_fp64():
+    # an fp32 result is compared at its exact float32 value, not re-rounded
+    g = np.array([1.0 + 2.0 ** -20], dtype=np.float32)
+    assert oracle.rel_l2(g, np.array([1.0])) == pytest.approx(2.0 ** -20, rel=1e-12)
+
+
+@pytest.mark.parametrize("gs,rs", [((2, 3), (3,)), ((3, 1), (3,)), ((3,), (1,)), ((4, 4), (2, 8))])
+def test_rel_l2_rejects_shape_mismatch(gs, rs):
+    # a mis-shaped result must fail, never broadcast against the reference
+    with pytest.raises(ValueError):
+        oracle.rel_l2(np.ones(gs), np.ones(rs))
