@@ -31,6 +31,13 @@ if ROOT not in sys.path:
 METRIC = "channel-tokens/s (B·D·L/s) and % HBM peak, Hyena op fwd at L=64K order 2"
 HBM_PEAK_GBS = 8000.0
 VALU_F32_PEAK_TFLOPS = 157.3  # published: 256 CUs x 128 fp32 lanes/clk (packed) x 2 (FMA) x 2.4 GHz
+# The kernels are built without packed fp32 instructions, so the vector rate they
+# can reach is half the published one: 256 CUs x 64 fp32 lanes/clk x 2 (FMA) x 2.4 GHz.
+VALU_F32_UNPACKED_TFLOPS = 78.6
+# flop per byte above which a kernel is priced against the vector-ALU roof instead of HBM
+RIDGE_FLOP_PER_BYTE = VALU_F32_UNPACKED_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+# rows per chunk of the pipelined four-step forward (mirrors the library's rule)
+PIPE_ROWS, PIPE_MIN_ROWS = 128, 32
 
 
 def log(*a):
@@ -58,6 +65,37 @@ def alg_flops_forward(wl) -> float:
     B, D, L, N = wl.B, wl.D, wl.L, wl.order
     per_step = 10.0 * L * math.log2(2 * L) + 6.0 * (L + 1) + 2.0 * L
     return B * D * ((N - 1) * per_step + N * L + 5.0 * (N + 1) * L)
+
+
+def roofline(kernel: str, launches: int, launch_ms: float, bytes_per_launch: float, flops_per_launch: float,
+             traffic=None, step_traffic=None, step_alg_bytes=None) -> dict:
+    """The roofline object of one kernel: HBM-bound (algorithmic bytes per launch
+    against 8 TB/s) when its algorithmic intensity is at or below the ridge of the
+    unpacked fp32 vector rate and HBM, else ALU-bound (algorithmic flops against
+    78.6 TFLOP/s). `traffic` is the measured HBM bytes per launch and
+    `step_traffic` per step, both from committed counter summaries, or None."""
+    sec = launch_ms * 1e-3
+    intensity = flops_per_launch / bytes_per_launch
+    if intensity > RIDGE_FLOP_PER_BYTE:
+        achieved, peak, unit, bound = flops_per_launch / sec / 1e12, VALU_F32_UNPACKED_TFLOPS, "TFLOP/s", "alu"
+    else:
+        achieved, peak, unit, bound = bytes_per_launch / sec / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    out = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel,
+           "alg_bytes_per_launch": int(bytes_per_launch), "alg_flops_per_launch": int(flops_per_launch),
+           "flop_per_byte": round(intensity, 2), "ridge_flop_per_byte": round(RIDGE_FLOP_PER_BYTE, 2),
+           "launch_ms": round(launch_ms, 5), "launches_per_step": launches,
+           "step_traffic": step_traffic}
+    if step_traffic is not None and step_alg_bytes:
+        out["step_traffic_over_alg"] = round(step_traffic / step_alg_bytes, 3)
+    return out
+
+
+def pipe_chunk_rows(rows: int, ws_bytes: int, tile_bytes: int) -> int:
+    """Rows per chunk of a pipelined order-2 four-step forward with this workspace
+    (three tile slots), or 0 when the library runs the chunks one by one."""
+    R = min(PIPE_ROWS, ws_bytes // (3 * tile_bytes), rows)
+    return R if R >= min(rows, PIPE_MIN_ROWS) else 0
 
 
 def device_copy_gbs(torch, dev, nbytes: int = 1 << 30, reps: int = 5) -> float:
@@ -190,6 +228,19 @@ def measured_traffic(kernel: str, workload: str):
         return int(float(kv["fetch_bytes_per_dispatch"]) + float(kv["write_bytes_per_dispatch"]))
     except (KeyError, ValueError):
         return None
+
+
+def measured_step_traffic(kernel: str, workload: str):
+    """HBM bytes of one whole forward (every kernel it launches) from the committed
+    counter summary of `kernel`, or None (see measured_traffic)."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.txt")
+    if measured_traffic(kernel, workload) is None:
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("step_bytes:"):
+                return int(float(line.split(":", 1)[1]))
+    return None
 
 
 def cpu_baseline(x, wl, budget_s: float):
@@ -812,6 +863,149 @@ def bench_convnd(args, torch, nd: int):
     plan.close()
 
 
+# ------------------------------------------------------------ profile summaries
+
+def _csv_rows(d: str, suffix: str):
+    """Rows of every rocprofv3 csv file under directory d whose name ends with suffix."""
+    import csv
+    import glob
+
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def _short_name(name: str) -> str:
+    """'void hy::k_fs_row<8, 8, 0>(...)' -> 'k_fs_row<8, 8, 0>'."""
+    n = name.split("(")[0].replace("void ", "").strip()
+    return n.split("hy::")[-1]
+
+
+def _is_forward_kernel(short: str) -> bool:
+    """Kernels one forward launches (not the once-per-plan spectrum kernels)."""
+    base, _, targs = short.partition("<")
+    a = [t.strip() for t in targs.rstrip(">").split(",")] if targs else []
+    if base in ("k_fs_pipe", "k_lds_forward", "k_fs_colinv", "k_part_fwd", "k_part_inv"):
+        return True
+    if base == "k_fs_colfwd":
+        return len(a) > 3 and a[3] == "0"
+    if base == "k_fs_row":
+        return len(a) > 2 and a[2] == "0"
+    return False
+
+
+def _calibration():
+    kv = {}
+    with open(os.path.join(ROOT, "profiles", "copy_calibration_1GiB.txt")) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    return float(kv["fetch_scale"]), float(kv["write_scale"])
+
+
+def summarize_pmc(args):
+    """Counter summary (profiles/pmc_<kernel>_<workload>.txt) from a FETCH_SIZE run and
+    a WRITE_SIZE run of `bench.py --profile-forwards F`: per-dispatch HBM bytes of the
+    dominant kernel and the bytes of one whole forward, scaled by the copy calibration."""
+    from fft_long_convolution_libhyena_amd import synth
+
+    fdir, wdir = args.summarize_pmc
+    fs, ws = _calibration()
+    per = {}
+    for d, cname, key in ((fdir, "FETCH_SIZE", "fetch"), (wdir, "WRITE_SIZE", "write")):
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if r.get("Counter_Name") != cname:
+                continue
+            k = _short_name(r["Kernel_Name"])
+            e = per.setdefault(k, {"fetch": [], "write": []})
+            e[key].append(float(r["Counter_Value"]))
+    F = args.forwards
+    kern = args.kernel
+    dom = [k for k in per if k.split("<")[0] == kern]
+    if not dom:
+        raise SystemExit(f"kernel {kern} not in the counters: {sorted(per)}")
+    wl = synth.WORKLOADS[args.workload]
+    alg = alg_bytes_forward(wl)
+    step = 0.0
+    lines = []
+    for k in sorted(per, key=lambda k: -sum(per[k]["fetch"])):
+        e = per[k]
+        fb = sum(e["fetch"]) * 1024 * fs
+        wb = sum(e["write"]) * 1024 * ws
+        n = max(len(e["fetch"]), len(e["write"]))
+        fwd = _is_forward_kernel(k)
+        if fwd:
+            step += (fb + wb) / F
+        lines.append(f"#   {k}: dispatches {n}, fetch {fb / max(n, 1):.0f}, write {wb / max(n, 1):.0f} bytes per dispatch"
+                     + ("" if fwd else " (not part of the forward)"))
+    d0 = dom[0]
+    e = per[d0]
+    nd = max(len(e["fetch"]), len(e["write"]))
+    fk = sum(e["fetch"]) / len(e["fetch"])
+    wk = sum(e["write"]) / len(e["write"])
+    cmd = args.command or ""
+    out = [f"# rocprofv3 HBM byte counters per dispatch: {kern} on {wl.name} ({wl.describe()})",
+           "# commands (from the repository root):"]
+    out += [f"#   {c.strip()}" for c in cmd.split(";;") if c.strip()]
+    out += ["# scaled with the factors of copy_calibration_1GiB.txt; the forward's kernels summed over "
+            f"{F} forwards give step_bytes",
+            f"kernel: {kern}", f"instance: {d0}", f"workload: {wl.name}",
+            f"sources_sha256: {kernel_sources_hash(kern)}", f"dispatches: {nd}",
+            f"fetch_size_kib_per_dispatch: {fk:.1f}", f"write_size_kib_per_dispatch: {wk:.1f}",
+            f"fetch_scale: {fs:.4f}", f"write_scale: {ws:.4f}",
+            f"fetch_bytes_per_dispatch: {fk * 1024 * fs:.0f}", f"write_bytes_per_dispatch: {wk * 1024 * ws:.0f}",
+            f"step_bytes: {step:.0f}", f"alg_bytes_per_step: {alg}", f"step_traffic_over_alg: {step / alg:.3f}",
+            "# every kernel of the run (scaled bytes per dispatch):"] + lines
+    print("\n".join(out))
+
+
+def summarize_trace(args):
+    """Kernel-trace summary (profiles/trace_<kernel>_<workload>.txt) from a
+    `rocprofv3 --kernel-trace --stats` run."""
+    from fft_long_convolution_libhyena_amd import synth
+
+    rows = _csv_rows(args.summarize_trace, "kernel_stats.csv")
+    wl = synth.WORKLOADS[args.workload]
+    cmd = args.command or ""
+    out = [f"# rocprofv3 kernel-trace statistics: {args.kernel} on {wl.name} ({wl.describe()})",
+           "# command (from the repository root):"]
+    out += [f"#   {c.strip()}" for c in cmd.split(";;") if c.strip()]
+    out += [f"# kernel sources sha256[:16]: {kernel_sources_hash(args.kernel)}",
+            f"{'kernel':60s} {'calls':>7s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}"]
+    for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+        out.append(f"{_short_name(r['Name'])[:60]:60s} {int(r['Calls']):7d} {float(r['AverageNs']) / 1e3:10.2f} "
+                   f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} "
+                   f"{float(r['Percentage']):6.2f}")
+    if args.note:
+        out.append(f"# {args.note}")
+    print("\n".join(out))
+
+
+def profile_forwards(args, wl, x, torch, Plan):
+    """Plan, spectrum and exactly args.profile_forwards forwards, for counter runs."""
+    dev = torch.device("cuda", 0)
+    u = torch.from_numpy(x.u_proj).to(dev)
+    if wl.dtype == "bf16":
+        u = u.to(torch.bfloat16)
+    plan = Plan(wl.L, wl.D, wl.order, wl.dtype, args.path)
+    spec = plan.spectrum(torch.from_numpy(x.h).to(dev))
+    w, bias = torch.from_numpy(x.short_w).to(dev), torch.from_numpy(x.bias).to(dev)
+    ws_bytes = int(args.workspace_mb * 2 ** 20) if args.workspace_mb > 0 else plan.workspace_bytes(wl.B)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev) if ws_bytes else None
+    y = torch.empty((wl.B, wl.D, wl.L), dtype=plan.io_dtype, device=dev)
+    torch.cuda.synchronize()
+    for i in range(args.profile_forwards):
+        plan.forward(u, w, spec, bias, y, ws)
+        torch.cuda.synchronize()
+        log(f"[profile] forward {i + 1} of {args.profile_forwards} done")
+    plan.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -825,7 +1019,8 @@ def main():
                     help="kernel family of the forward plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
-    ap.add_argument("--check", action="store_true", help="also compare sampled rows with the oracle")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the oracle comparison of sampled outputs (run by default, after the timed region)")
     ap.add_argument("--operator", action="store_true",
                     help="time hyena_operator_forward (in_proj GEMM + the path + out_proj GEMM) instead")
     ap.add_argument("--backward", action="store_true",
@@ -842,7 +1037,24 @@ def main():
                          "hyena_backward_per_sample")
     ap.add_argument("--filter", action="store_true",
                     help="time hyena_implicit_filter (the long filters of the workload's plan) instead")
+    ap.add_argument("--profile-forwards", type=int, default=0,
+                    help="run plan, spectrum and exactly this many forwards, then exit (for counter runs)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print a counter summary from rocprofv3 FETCH_SIZE and WRITE_SIZE csv output")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a kernel-trace summary from rocprofv3 --kernel-trace --stats csv output")
+    ap.add_argument("--kernel", default="k_fs_pipe", help="kernel a summary is about")
+    ap.add_argument("--forwards", type=int, default=5, help="forwards in the profiled run (--summarize-pmc)")
+    ap.add_argument("--command", default="", help="the profiling commands, ';;'-separated, for the summary header")
+    ap.add_argument("--note", default="", help="a closing note line for a trace summary")
     args = ap.parse_args()
+    args.check = not args.no_check
+    if args.summarize_pmc:
+        summarize_pmc(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -880,6 +1092,9 @@ def main():
         return
     if args.circular:
         bench_circular(args, wl, x, torch, Plan)
+        return
+    if args.profile_forwards > 0:
+        profile_forwards(args, wl, x, torch, Plan)
         return
     dev = torch.device("cuda", 0)
     u = torch.from_numpy(x.u_proj).to(dev)
@@ -938,35 +1153,53 @@ def main():
         for k, v in r.items():
             fam_ms[k] = fam_ms.get(k, 0.0) + v / nt
     log(f"[bench] per-forward kernel-family ms: {json.dumps({k: round(v, 4) for k, v in fam_ms.items()})}")
+    fwd_flops = alg_flops_forward(wl)
+    rows = wl.B * wl.D
+    dominant = None
     if plan.path == "lds":
         # the step is this one launch: the timed region itself gives its duration
         # (events around a single launch add their own fence time)
-        dom, dom_ms, dom_bytes = "k_lds_forward", ms, fwd_bytes
-        launches = 1
-    elif plan.path == "partitioned":
-        # hyena_forward_timed reports pass 1 in the pass_a slot and pass 2 in pass_b
-        fam = max(("pass_a", "pass_b"), key=lambda k: fam_ms[k])
-        dom = {"pass_a": "k_part_fwd", "pass_b": "k_part_inv"}[fam]
-        dom_ms = fam_ms[fam]
-        dom_bytes = alg_bytes_part(wl, {"pass_a": "pass_1", "pass_b": "pass_2"}[fam])
-        rows = wl.B * wl.D
-        per_row = 8 * wl.L + (4 * wl.L if wl.order > 2 else 0)
-        chunk = max(1, min(rows, ws_bytes // per_row))
-        launches = math.ceil(rows / chunk) * (wl.order - 1)
+        kernel, launches, kms = "k_lds_forward", 1, ms
+    elif fam_ms.get("pipe", 0.0) > 0:
+        # pipelined four-step: every launch runs the three passes on three chunks, so
+        # the forward's algorithmic bytes spread over its launches
+        # (the launches follow each other with no gap, so the timed region divided by
+        # the launch count is the average launch; events around each launch would add
+        # their own fence time)
+        T = wl.L // 2 if getattr(plan, "circular", False) else wl.L
+        R = pipe_chunk_rows(rows, ws_bytes, 8 * T)
+        launches = math.ceil(rows / R) + 2 * wl.order - 2
+        kernel, kms = "k_fs_pipe", ms / launches
     else:
-        fam = max(("pass_a", "pass_b", "pass_c"), key=lambda k: fam_ms[k])
-        dom = {"pass_a": "k_fs_colfwd", "pass_b": "k_fs_row", "pass_c": "k_fs_colinv"}[fam]
-        dom_ms, dom_bytes = fam_ms[fam], alg_bytes_pass(wl, fam)
-        rows = wl.B * wl.D
-        chunk = max(1, min(rows, (ws_bytes // (8 * wl.L)) if ws_bytes else rows))
-        launches = math.ceil(rows / chunk) * (1 if fam == "pass_a" else wl.order - 1)
-    per_launch_ms = dom_ms / launches
-    per_launch_bytes = dom_bytes / launches
-    achieved = per_launch_bytes / (per_launch_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(dom, wl.name),
-                "kernel": dom, "alg_bytes_per_launch": int(per_launch_bytes),
-                "launch_ms": round(per_launch_ms, 5), "launches_per_step": launches}
+        # several kernel families: the forward's algorithmic bytes over all its launches;
+        # the slowest family is reported on its own under "dominant_kernel"
+        if plan.path == "partitioned":
+            fams = {"pass_a": "k_part_fwd", "pass_b": "k_part_inv"}
+            per_row = 8 * wl.L + (4 * wl.L if wl.order > 2 else 0)
+            chunk = max(1, min(rows, ws_bytes // per_row))
+            nper = {"pass_a": wl.order - 1, "pass_b": wl.order - 1}
+            design = lambda f: alg_bytes_part(wl, {"pass_a": "pass_1", "pass_b": "pass_2"}[f])  # noqa: E731
+        else:
+            fams = {"pass_a": "k_fs_colfwd", "pass_b": "k_fs_row", "pass_c": "k_fs_colinv"}
+            chunk = max(1, min(rows, (ws_bytes // (8 * wl.L)) if ws_bytes else rows))
+            nper = {"pass_a": 1, "pass_b": wl.order - 1, "pass_c": wl.order - 1}
+            design = lambda f: alg_bytes_pass(wl, f)  # noqa: E731
+        nch = math.ceil(rows / chunk)
+        launches = nch * sum(nper.values())
+        kernel = "+".join(fams.values())
+        kms = sum(fam_ms[f] for f in fams) / launches
+        fam = max(fams, key=lambda k: fam_ms[k])
+        dl = nch * nper[fam]
+        dominant = {"kernel": fams[fam], "launches_per_step": dl, "launch_ms": round(fam_ms[fam] / dl, 5),
+                    "design_bytes_per_launch": int(design(fam) / dl),
+                    "design_frac": round(design(fam) / (fam_ms[fam] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(fams[fam], wl.name)}
+    per_launch = measured_traffic(kernel, wl.name)
+    step_traffic = measured_step_traffic(kernel, wl.name)
+    roof = roofline(kernel, launches, kms, fwd_bytes / launches, fwd_flops / launches, per_launch, step_traffic,
+                    fwd_bytes)
+    if dominant:
+        roof["dominant_kernel"] = dominant
 
     out = {
         "metric": METRIC,
@@ -992,10 +1225,10 @@ def main():
         "valu_frac_forward": round(valu_frac, 4),
         "plan_ms": round(plan_ms, 3),
         "spectrum_ms": round(spectrum_ms, 4),
-        "roofline": roofline,
+        "roofline": roof,
     }
 
-    if args.check:
+    if not args.no_check:
         import oracle
 
         rows = synth.sample_rows(wl, 8)

@@ -4,6 +4,6 @@ The compute runs in ``libhyena.so`` (HIP kernels for gfx950 behind the C ABI in
 ``include/hyena.h``); this package only loads it and marshals torch tensors.
 """
 from .binding import (EXPORTS, HyenaError, Plan, Plan2D, Plan3D, LIB_PATH, load_library,  # noqa: F401
-                      HYENA_F32, HYENA_BF16, PATH_AUTO, PATH_LDS, PATH_FOURSTEP, PATH_FUSED, PATH_PARTITIONED)
+                      HYENA_F32, HYENA_BF16, PATH_AUTO, PATH_LDS, PATH_FOURSTEP, PATH_PARTITIONED)
 
 __all__ = ["Plan", "Plan2D", "Plan3D", "HyenaError", "load_library", "LIB_PATH", "EXPORTS"]

@@ -15,11 +15,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libhyena.so")
 
 HYENA_F32, HYENA_BF16 = 0, 1
-PATH_AUTO, PATH_LDS, PATH_FOURSTEP, PATH_FUSED, PATH_PARTITIONED = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_LDS, PATH_FOURSTEP, PATH_PARTITIONED = 0, 1, 2, 4
 STATUS = {0: "HYENA_OK", 1: "HYENA_ERR_INVALID_ARG", 2: "HYENA_ERR_UNSUPPORTED",
           3: "HYENA_ERR_WORKSPACE", 4: "HYENA_ERR_DEVICE"}
-_PATHS = {"auto": PATH_AUTO, "lds": PATH_LDS, "fourstep": PATH_FOURSTEP, "fused": PATH_FUSED,
-          "partitioned": PATH_PARTITIONED}
+_PATHS = {"auto": PATH_AUTO, "lds": PATH_LDS, "fourstep": PATH_FOURSTEP, "partitioned": PATH_PARTITIONED}
 _DTYPES = {"f32": HYENA_F32, "bf16": HYENA_BF16}
 
 # every symbol include/hyena.h declares
@@ -27,7 +26,7 @@ FLAG_CIRCULAR = 1  # HYENA_FLAG_CIRCULAR
 
 EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_create_ex", "hyena_plan_destroy", "hyena_plan_path",
            "hyena_spectrum_bytes", "hyena_workspace_bytes", "hyena_filter_spectrum", "hyena_forward",
-           "hyena_forward_timed", "hyena_fused_check", "hyena_backward_workspace_bytes", "hyena_backward",
+           "hyena_forward_timed", "hyena_backward_workspace_bytes", "hyena_backward",
            "hyena_backward_per_sample_workspace_bytes", "hyena_backward_per_sample",
            "hyena_operator_workspace_bytes", "hyena_operator_forward", "hyena_operator_forward_timed",
            "hyena_implicit_filter", "hyena_filter_spectrum_batched", "hyena_forward_per_sample",
@@ -96,8 +95,6 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_forward_per_sample.restype = ci
     lib.hyena_forward_timed.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
     lib.hyena_forward_timed.restype = ci
-    lib.hyena_fused_check.argtypes = [vp, vp, ctypes.POINTER(ci)]
-    lib.hyena_fused_check.restype = ci
     lib.hyena_backward_workspace_bytes.argtypes = [vp, i64]
     lib.hyena_backward_workspace_bytes.restype = sz
     lib.hyena_backward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -202,7 +199,7 @@ class Plan:
                self.lib.hyena_plan_create_ex(ctypes.byref(h), self.L, self.D, self.order, _DTYPES[dtype],
                                              _PATHS[path], FLAG_CIRCULAR if self.circular else 0))
         self.handle = h
-        self.path = {PATH_LDS: "lds", PATH_FOURSTEP: "fourstep", PATH_FUSED: "fused",
+        self.path = {PATH_LDS: "lds", PATH_FOURSTEP: "fourstep",
                      PATH_PARTITIONED: "partitioned"}[self.lib.hyena_plan_path(h)]
 
     @property
@@ -317,7 +314,9 @@ class Plan:
 
     def forward_timed(self, u_proj, short_w, spec, bias, y, workspace=None):
         """hyena_forward_timed: runs one forward (synchronously) and returns the
-        per-kernel-family milliseconds {"lds", "pass_a", "pass_b", "pass_c", "total"}."""
+        per-kernel-family milliseconds {"lds", "pass_a", "pass_b", "pass_c", "total",
+        "pipe"} ("pipe": the pipelined four-step launches, each running all three
+        passes on consecutive chunks)."""
         torch = self._torch
         B = int(u_proj.shape[0])
         ws_ptr, ws_bytes = 0, 0
@@ -325,12 +324,12 @@ class Plan:
             if workspace is None:
                 workspace = torch.empty(self.workspace_bytes(B), dtype=torch.uint8, device=self.device)
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-        ms = (ctypes.c_float * 5)()
+        ms = (ctypes.c_float * 6)()
         _check("hyena_forward_timed",
                self.lib.hyena_forward_timed(self.handle, B, u_proj.data_ptr(), short_w.data_ptr(),
                                             spec.data_ptr(), bias.data_ptr(), y.data_ptr(), ws_ptr or None,
                                             ws_bytes, _stream_handle(torch, self.device), ms))
-        return dict(zip(("lds", "pass_a", "pass_b", "pass_c", "total"), [float(v) for v in ms]))
+        return dict(zip(("lds", "pass_a", "pass_b", "pass_c", "total", "pipe"), [float(v) for v in ms]))
 
     def backward_workspace_bytes(self, B: int, per_sample: bool = False) -> int:
         fn = self.lib.hyena_backward_per_sample_workspace_bytes if per_sample else self.lib.hyena_backward_workspace_bytes
@@ -429,15 +428,6 @@ class Plan:
                                                      out.data_ptr(), ws.data_ptr(), ws.numel(),
                                                      _stream_handle(self._torch, self.device), ms))
         return dict(zip(("in_proj", "path", "out_proj", "total"), [float(v) for v in ms]))
-
-    def fused_check(self, workspace) -> int:
-        """hyena_fused_check: nonzero if a bounded wait of the fused kernel expired
-        in the last forward that used `workspace` (synchronous)."""
-        flag = ctypes.c_int(0)
-        _check("hyena_fused_check",
-               self.lib.hyena_fused_check(self.handle, workspace.data_ptr() if workspace is not None else None,
-                                          ctypes.byref(flag)))
-        return int(flag.value)
 
     def close(self):
         if getattr(self, "handle", None) is not None and self.handle.value:

@@ -28,7 +28,10 @@
 //    m = L2*m1 + m2 and k = k1 + L1*k2. Pass A takes column FFTs over m1,
 //    pass B takes row FFTs over m2 (with the L-point twiddle), the pair step and
 //    the inverse rows, pass C takes the inverse columns and the gate. Pass C of
-//    step o is fused with pass A of step o+1.
+//    step o is fused with pass A of step o+1. Rows are processed in chunks
+//    whose tiles live in the workspace; at order 2 the chunks are pipelined
+//    (k_fs_pipe: one launch runs pass C of chunk k-2, pass B of chunk k-1 and
+//    pass A of chunk k), otherwise each chunk takes 2N-1 launches of its own.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,9 +40,6 @@
 #include "kernels.hpp"
 #include "pair.hpp"
 
-#ifndef HY_EXPERIMENTAL_FUSED
-#define HY_EXPERIMENTAL_FUSED 0
-#endif
 
 namespace hy {
 
@@ -49,176 +49,6 @@ hipError_t launch_lds_forward_t(const LdsArgs& a, hipStream_t st);
 template <int LOGL>
 hipError_t launch_lds_spectrum_t(const float* h, float2* spec, int64_t rows, const float2* tw, const float2* wpair,
                                  hipStream_t st, bool circ);
-
-// ====================================================== fused persistent path
-//
-// One launch for a whole order-2 forward. Workgroups are dispatched to the 8 XCDs
-// round-robin; each reads its XCD from the XCC_ID hardware register and serves
-// that XCD's rows (r = xcd + 8*i) through the XCD's own ticket counter. Each
-// ticket names one work item (a pass A column block, a pass B unit group or a
-// pass C column block of one row). Tickets are issued per step s as
-//   [A items of group s][B items of group s-1][C items of group s-2],
-// and an item only waits for items holding earlier tickets (B waits for its
-// row's A items, C for its row's B items, A of group j for C of group j - S,
-// whose tile slot it reuses), so every wait ends even when not all workgroups
-// are resident. Tiles live in a ring of S * G rows per XCD sized to stay in that
-// XCD's L2, and every hand-off happens between CUs of one XCD: a producer waits
-// for its stores to complete (they are then in the L2), then bumps a counter with
-// an atomic in the same L2; a consumer polls the counter with atomics, then
-// invalidates its L1 before reading the tile. Waits are bounded in time (see
-// kWaitTicks, kKernelTicks): an expired wait records an error in the control
-// block and the kernel runs to its end.
-// Time bounds, on the 100 MHz real-time counter: one wait may last 20 ms, and no
-// workgroup takes a new ticket more than 1 s after it started.
-constexpr uint64_t kWaitTicks = 2000000;
-constexpr uint64_t kKernelTicks = 100000000;
-
-// One 128-byte line per XCD: [0] ticket counter, [1] error flag, [2] waits that
-// had to poll, [3] longest wait in real-time ticks. Each line is only touched by
-// the workgroups of its XCD, so it lives in that XCD's L2.
-struct FusedCtl {
-    uint32_t x[8][32];
-};
-
-__device__ __forceinline__ uint32_t hw_xcc_id() {
-    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (15 << 11)) & 7u;  // HW_REG_XCC_ID
-}
-
-__device__ __forceinline__ uint64_t rt_now() { return __builtin_amdgcn_s_memrealtime(); }
-
-// read a counter where its increments are performed: an atomic add of a value
-// the compiler cannot see is zero (it would turn an add of 0 into a plain load)
-__device__ __forceinline__ uint32_t ctr_read(uint32_t* ctr, uint32_t zero) {
-    return __hip_atomic_fetch_add(ctr, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// all threads of the block: make this block's global stores visible in the L2,
-// then count the item as done
-__device__ __forceinline__ void fused_signal(uint32_t* ctr) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// all threads of the block: wait until *ctr >= target, then drop stale L1 lines.
-// A wait that outlasts kWaitTicks sets the XCD's error flag; once the flag is set
-// every wait of that XCD returns at once (the forward's output is then invalid).
-__device__ __forceinline__ void fused_wait(uint32_t* ctr, uint32_t target, uint32_t* line, uint32_t zero) {
-    if (threadIdx.x == 0) {
-        uint32_t* err = line + 1;
-        if (ctr_read(ctr, zero) < target) {
-            const uint64_t t0 = rt_now();
-            uint32_t polls = 0;
-            for (;;) {
-                __builtin_amdgcn_s_sleep(8);
-                if (ctr_read(ctr, zero) >= target) break;
-                if ((++polls & 15u) == 0 && ctr_read(err, zero) != 0) break;
-                if (rt_now() - t0 > kWaitTicks) {
-                    __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
-                }
-            }
-            __hip_atomic_fetch_add(line + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_max(line + 3, (uint32_t)(rt_now() - t0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-    __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
-
-template <int LOG1, int LOG2>
-struct FusedCfg {
-    using Cfg = FsCfg<LOG1, LOG2>;
-    static constexpr int NA = Cfg::L2 / Cfg::CB;              // pass A / C items per row
-    static constexpr int NB = Cfg::L1 / 2 / Cfg::UNITS;       // pass B items per row
-    static constexpr int THREADS = Cfg::COL_THREADS;
-    static_assert(Cfg::COL_THREADS == Cfg::ROW_THREADS, "one block shape for all passes");
-    static constexpr int LDS_A = Cfg::L1 * Cfg::CP;
-    static constexpr int LDS_B = 2 * Cfg::UNITS * Cfg::RP;
-    static constexpr int LDS = LDS_A > LDS_B ? LDS_A : LDS_B;
-};
-
-template <int LOG1, int LOG2, class TIO>
-__global__ void __launch_bounds__((FusedCfg<LOG1, LOG2>::THREADS))
-k_fs_fused(const TIO* __restrict__ u, const float* __restrict__ w3, const float2* __restrict__ spec,
-           const float* __restrict__ bias, TIO* __restrict__ y, FsTables tb, FusedCtl* __restrict__ ctl,
-           uint32_t* __restrict__ cnt, float2* __restrict__ ring, int D, int64_t nrows, int G, int S, int ngmax,
-           uint32_t zero) {
-    using F = FusedCfg<LOG1, LOG2>;
-    constexpr int NA = F::NA, NB = F::NB;
-    constexpr int64_t L = (int64_t)FsCfg<LOG1, LOG2>::L1 * FsCfg<LOG1, LOG2>::L2;
-    __shared__ float2 lds[F::LDS];
-    __shared__ uint32_t s_ticket;
-    const uint32_t x = hw_xcc_id();
-    const uint32_t nr = (uint32_t)nrows;
-    const uint32_t nx = nr > x ? (nr - 1 - x) / 8 + 1 : 0;  // rows of this XCD
-    const uint32_t ng = (nx + G - 1) / G;
-    const uint32_t seg_a = G * NA, seg_b = G * NB, seg = 2 * seg_a + seg_b;
-    const uint32_t total = (ng + 2) * seg;
-    // per-XCD counters: A and B per local row, C per group
-    uint32_t* cA = cnt + (size_t)x * (2 * (size_t)ngmax * G + ngmax + 64);
-    uint32_t* cB = cA + (size_t)ngmax * G;
-    uint32_t* cC = cB + (size_t)ngmax * G;
-    float2* xring = ring + (size_t)x * S * G * L;
-    const uint64_t kstart = rt_now();
-    for (;;) {
-        if (threadIdx.x == 0) {
-            if (rt_now() - kstart > kKernelTicks) {
-                __hip_atomic_fetch_or(&ctl->x[x][1], 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                s_ticket = 0xffffffffu;  // give up: no further tickets
-            } else {
-                s_ticket = __hip_atomic_fetch_add(&ctl->x[x][0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-        __syncthreads();
-        const uint32_t tk = __builtin_amdgcn_readfirstlane(s_ticket);
-        __syncthreads();
-        if (tk >= total) break;
-        const uint32_t step = tk / seg;
-        uint32_t rem = tk - step * seg;
-        if (rem < seg_a) {  // pass A of group `step`
-            const uint32_t j = step;
-            if (j >= ng) continue;
-            const uint32_t rl = rem / NA, sub = rem % NA;
-            const uint32_t i = j * G + rl;
-            if (j >= (uint32_t)S) fused_wait(cC + (j - S), seg_a, ctl->x[x], zero);
-            if (i < nx) {
-                float2* slot = xring + ((size_t)(j % S) * G + rl) * L;
-                fs_colfwd_body<LOG1, LOG2, TIO, 0>(lds, u, w3, nullptr, slot, tb, D, 2, x + 8 * i, (int)sub);
-                fused_signal(cA + i);
-            }
-        } else if (rem < seg_a + seg_b) {  // pass B of group step-1
-            if (step < 1 || step - 1 >= ng) continue;
-            const uint32_t j = step - 1;
-            rem -= seg_a;
-            const uint32_t rl = rem / NB, sub = rem % NB;
-            const uint32_t i = j * G + rl;
-            if (i >= nx) continue;
-            fused_wait(cA + i, NA, ctl->x[x], zero);
-            float2* slot = xring + ((size_t)(j % S) * G + rl) * L;
-            fs_row_body<LOG1, LOG2, 0>(lds, slot, spec, bias, tb, D, 0, x + 8 * i, (int)sub);
-            fused_signal(cB + i);
-        } else {  // pass C of group step-2
-            if (step < 2 || step - 2 >= ng) continue;
-            const uint32_t j = step - 2;
-            rem -= seg_a + seg_b;
-            const uint32_t rl = rem / NA, sub = rem % NA;
-            const uint32_t i = j * G + rl;
-            if (i < nx) {
-                fused_wait(cB + i, NB, ctl->x[x], zero);
-                float2* slot = xring + ((size_t)(j % S) * G + rl) * L;
-                fs_colinv_body<LOG1, LOG2, TIO, true>(lds, slot, u, w3, y, tb, D, 2, 0, x + 8 * i, (int)sub);
-            }
-            fused_signal(cC + j);
-        }
-    }
-}
-
-// zero the control block and counters (a fill kernel, so the forward can be
-// captured in a graph)
-__global__ void k_fill_u32(uint32_t* p, size_t n) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
-}
 
 // ================================================================== launchers
 
@@ -310,6 +140,64 @@ static hipError_t fs_forward_chunk(const FsArgs& a, int64_t row0, int64_t nrows,
                   : fs_forward_chunk_c<LOG1, LOG2, false>(a, row0, nrows, st, marks);
 }
 
+// Pipelined launches over chunks of R rows (see k_fs_pipe): launch k runs stage s
+// on chunk k - s for every stage s < 2N-1 whose chunk exists.
+template <int LOG1, int LOG2, class TIO, bool CIRC>
+static hipError_t fs_forward_pipe_t(const FsArgs& a, int64_t rows, int64_t R, hipStream_t st, hipEvent_t* marks) {
+    using P = FsPipeCfg<LOG1, LOG2>;
+    if constexpr (!P::OK) {
+        return hipErrorInvalidValue;
+    } else {
+        constexpr int64_t L = (int64_t)FsCfg<LOG1, LOG2>::L1 * FsCfg<LOG1, LOG2>::L2;
+        const int S = 2 * a.N - 1;
+        const int64_t nch = (rows + R - 1) / R;
+        if (marks) (void)hipEventRecord(marks[0], st);
+        for (int64_t k = 0; k < nch + S - 1; ++k) {
+            FsPipe pp{};
+            int64_t blk = 0;
+            // oldest chunk first: its workgroups are dispatched first
+            for (int s = S - 1; s >= 0; --s) {
+                const int64_t c = k - s;
+                if (c < 0 || c >= nch) continue;
+                FsStage& g = pp.s[pp.n++];
+                g.row0 = c * R;
+                g.nrows = (rows - g.row0) < R ? (rows - g.row0) : R;
+                g.slot = a.ws + (c % S) * R * L;
+                g.blk0 = (uint32_t)blk;
+                if (s == 0) {
+                    g.kind = 0;
+                    g.o = 0;
+                } else if (s % 2 == 1) {
+                    g.kind = 1;
+                    g.o = (s - 1) / 2;
+                } else {
+                    g.o = (s - 2) / 2;
+                    g.kind = g.o == a.N - 2 ? 3 : 2;
+                }
+                blk += xcd_grid(g.nrows, g.kind == 1 ? P::ROW_PER_ROW : P::COL_PER_ROW);
+            }
+            if (blk > 0x7fffffff) return hipErrorInvalidValue;
+            if (a.N > 2)
+                hipLaunchKernelGGL((k_fs_pipe<LOG1, LOG2, TIO, CIRC, true>), dim3((unsigned)blk), dim3(P::THREADS), 0,
+                                   st, (const TIO*)a.u, a.w3, a.spec, a.bias, (TIO*)a.y, a.tb, a.D, a.N, a.sbs, pp);
+            else
+                hipLaunchKernelGGL((k_fs_pipe<LOG1, LOG2, TIO, CIRC, false>), dim3((unsigned)blk), dim3(P::THREADS), 0,
+                                   st, (const TIO*)a.u, a.w3, a.spec, a.bias, (TIO*)a.y, a.tb, a.D, a.N, a.sbs, pp);
+            if (marks) (void)hipEventRecord(marks[k + 1], st);
+        }
+        return hipGetLastError();
+    }
+}
+
+template <int LOG1, int LOG2>
+static hipError_t fs_forward_pipe(const FsArgs& a, int64_t rows, int64_t R, hipStream_t st, hipEvent_t* marks) {
+    if (a.bf16)
+        return a.circ ? fs_forward_pipe_t<LOG1, LOG2, uint16_t, true>(a, rows, R, st, marks)
+                      : fs_forward_pipe_t<LOG1, LOG2, uint16_t, false>(a, rows, R, st, marks);
+    return a.circ ? fs_forward_pipe_t<LOG1, LOG2, float, true>(a, rows, R, st, marks)
+                  : fs_forward_pipe_t<LOG1, LOG2, float, false>(a, rows, R, st, marks);
+}
+
 template <int LOG1, int LOG2>
 static hipError_t fs_spectrum_t(const float* h, float2* spec, int64_t rows, const FsTables& tb, hipStream_t st,
                                 bool circ) {
@@ -348,6 +236,28 @@ hipError_t launch_fs_forward_chunk(int logL, const FsArgs& a, int64_t row0, int6
     }
 }
 
+bool fs_pipe_supported(int logL) {
+    switch (logL) {
+#define X(LG, A, B) \
+    case LG: return FsPipeCfg<A, B>::OK;
+        HY_FS_CASES(X)
+#undef X
+        default: return false;
+    }
+}
+
+hipError_t launch_fs_forward_pipelined(int logL, const FsArgs& a, int64_t rows, int64_t R, hipStream_t st,
+                                       hipEvent_t* marks) {
+    if (R < 1 || rows < 1 || a.N < 2 || 2 * a.N - 1 > kFsMaxStages) return hipErrorInvalidValue;
+    switch (logL) {
+#define X(LG, A, B) \
+    case LG: return fs_forward_pipe<A, B>(a, rows, R, st, marks);
+        HY_FS_CASES(X)
+#undef X
+        default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_fs_spectrum(int logL, const float* h, float2* spec, int64_t rows, const FsTables& tb,
                               hipStream_t st, bool circ) {
     switch (logL) {
@@ -368,82 +278,5 @@ int fs_row_units(int logL) {
         default: return 0;
     }
 }
-
-}  // namespace hy
-
-namespace hy {
-
-// ------------------------------------------------------ fused path launchers
-
-static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
-
-static int64_t fused_ngmax(int64_t nrows, int G) { return ((nrows + 7) / 8 + G - 1) / G; }
-
-static size_t fused_counter_words(int64_t nrows, int G) {
-    const int64_t ngmax = fused_ngmax(nrows, G);
-    return 8 * (size_t)(2 * ngmax * G + ngmax + 64);
-}
-
-size_t fused_workspace_bytes(int logL, int64_t nrows, int G, int S) {
-    const size_t L = (size_t)1 << logL;
-    return align256(sizeof(FusedCtl)) + align256(fused_counter_words(nrows, G) * 4) +
-           (size_t)8 * S * G * L * sizeof(float2);
-}
-
-template <int LOG1, int LOG2>
-static hipError_t fused_launch_t(const FsArgs& a, int64_t nrows, int G, int S, int blocks, hipStream_t st) {
-    using F = FusedCfg<LOG1, LOG2>;
-    char* base = (char*)a.ws;
-    FusedCtl* ctl = (FusedCtl*)base;
-    uint32_t* cnt = (uint32_t*)(base + align256(sizeof(FusedCtl)));
-    float2* ring = (float2*)(base + align256(sizeof(FusedCtl)) + align256(fused_counter_words(nrows, G) * 4));
-    const size_t nzero = (align256(sizeof(FusedCtl)) + align256(fused_counter_words(nrows, G) * 4)) / 4;
-    hipLaunchKernelGGL(k_fill_u32, dim3(64), dim3(256), 0, st, (uint32_t*)base, nzero);
-    const int ngmax = (int)fused_ngmax(nrows, G);
-    if (a.bf16)
-        hipLaunchKernelGGL((k_fs_fused<LOG1, LOG2, uint16_t>), dim3(blocks), dim3(F::THREADS), 0, st,
-                           (const uint16_t*)a.u, a.w3, a.spec, a.bias, (uint16_t*)a.y, a.tb, ctl, cnt, ring, a.D,
-                           nrows, G, S, ngmax, 0u);
-    else
-        hipLaunchKernelGGL((k_fs_fused<LOG1, LOG2, float>), dim3(blocks), dim3(F::THREADS), 0, st,
-                           (const float*)a.u, a.w3, a.spec, a.bias, (float*)a.y, a.tb, ctl, cnt, ring, a.D, nrows, G,
-                           S, ngmax, 0u);
-    return hipGetLastError();
-}
-
-template <int LOG1, int LOG2>
-static int fused_occupancy_t() {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_fs_fused<LOG1, LOG2, float>, FusedCfg<LOG1, LOG2>::THREADS,
-                                                     0) != hipSuccess)
-        return 0;
-    return n;
-}
-
-// The fused path is switched off: its first two runs on MI355X did not finish
-// (the second one with every wait bounded in time), while a CPU emulation of the
-// same ticket and counter logic completes for every tested shape. Until the cause
-// is found it is only built for experiments (HY_EXPERIMENTAL_FUSED=1) and plans
-// asking for it get HYENA_ERR_UNSUPPORTED.
-bool fused_supported(int logL) { return HY_EXPERIMENTAL_FUSED && logL == 16; }
-
-int fused_blocks_per_cu(int logL) {
-#if HY_EXPERIMENTAL_FUSED
-    if (logL == 16) return fused_occupancy_t<8, 8>();
-#endif
-    (void)logL;
-    return 0;
-}
-
-hipError_t launch_fs_fused(int logL, const FsArgs& a, int64_t nrows, int G, int S, int blocks, hipStream_t st) {
-#if HY_EXPERIMENTAL_FUSED
-    if (logL == 16) return fused_launch_t<8, 8>(a, nrows, G, S, blocks, st);
-#endif
-    (void)logL; (void)a; (void)nrows; (void)G; (void)S; (void)blocks; (void)st;
-    return hipErrorInvalidValue;
-}
-
-// byte offset of XCD x's error flag in the workspace
-uint32_t fused_error_offset(int x) { return (uint32_t)(x * 128 + 4); }
 
 }  // namespace hy

@@ -371,6 +371,74 @@ k_fs_colinv(float2* __restrict__ ws, const TIO* __restrict__ u, const float* __r
     fs_colinv_body<LOG1, LOG2, TIO, LAST, CIRC>(lds, ws + r * L, u, w3, y, tb, D, N, o, row0 + r, cb);
 }
 
+// ============================================================ pipelined launches
+//
+// The passes of consecutive chunks of rows are independent, so one launch can
+// run pass A of chunk k, the passes of step 0 of chunk k-1, ... together: stage s
+// of a launch takes chunk k - s. Each chunk owns one tile slot of a ring of
+// 2N-1 slots, so the tile a stage writes is read by the next stage of the same
+// chunk in the next launch; the launch boundary is the only synchronisation.
+// This keeps every launch full (no per-pass tail per chunk) and keeps the time
+// between a tile's write and its re-read to one launch.
+struct FsStage {
+    float2* slot;   // the chunk's tile slot (nrows tiles of L complex values)
+    int64_t row0;   // first flat (b, d) row of the chunk
+    int64_t nrows;  // rows of the chunk
+    uint32_t blk0;  // first workgroup of this stage in the launch
+    int kind;       // 0 pass A, 1 pass B, 2 pass C followed by another step, 3 pass C of the last step
+    int o;          // the step of a pass B or pass C
+};
+constexpr int kFsMaxStages = 15;  // 2 * 8 - 1 stages at order 8
+struct FsPipe {
+    FsStage s[kFsMaxStages];
+    int n;  // stages in this launch
+};
+
+template <int LOG1, int LOG2>
+struct FsPipeCfg {
+    using Cfg = FsCfg<LOG1, LOG2>;
+    // one block size for every stage: the column and row passes must agree
+    static constexpr bool OK = Cfg::COL_THREADS == Cfg::ROW_THREADS;
+    static constexpr int THREADS = Cfg::COL_THREADS;
+    static constexpr int LDS_COL = Cfg::L1 * Cfg::CP;
+    static constexpr int LDS_ROW = 2 * Cfg::UNITS * Cfg::RP;
+    static constexpr int LDS = LDS_COL > LDS_ROW ? LDS_COL : LDS_ROW;
+    static constexpr int COL_PER_ROW = Cfg::L2 / Cfg::CB;         // pass A / C workgroups per row
+    static constexpr int ROW_PER_ROW = Cfg::L1 / 2 / Cfg::UNITS;  // pass B workgroups per row
+};
+
+// MID: the launch may hold a pass C followed by another step (order > 2); that
+// body needs more registers than the others, so order-2 launches leave it out.
+template <int LOG1, int LOG2, class TIO, bool CIRC, bool MID>
+__global__ void __launch_bounds__((FsPipeCfg<LOG1, LOG2>::THREADS))
+k_fs_pipe(const TIO* __restrict__ u, const float* __restrict__ w3, const float2* __restrict__ spec,
+          const float* __restrict__ bias, TIO* __restrict__ y, FsTables tb, int D, int N, int64_t sbs, FsPipe pp) {
+    using P = FsPipeCfg<LOG1, LOG2>;
+    static_assert(P::OK, "pipelined launches need equal column and row block sizes");
+    __shared__ float2 lds[P::LDS];
+    constexpr int64_t L = (int64_t)FsCfg<LOG1, LOG2>::L1 * FsCfg<LOG1, LOG2>::L2;
+    const uint32_t bid = blockIdx.x;
+    int i = 0;
+    while (i + 1 < pp.n && bid >= pp.s[i + 1].blk0) ++i;  // workgroup-uniform
+    const FsStage& g = pp.s[i];
+    const int64_t local = (int64_t)(bid - g.blk0);
+    int64_t r;
+    int sub;
+    if (g.kind == 1) {
+        if (!xcd_row_map(local, g.nrows, P::ROW_PER_ROW, r, sub)) return;
+        fs_row_body<LOG1, LOG2, 0>(lds, g.slot + r * L, spec, bias, tb, D, g.o, g.row0 + r, sub, nullptr, nullptr,
+                                   sbs);
+        return;
+    }
+    if (!xcd_row_map(local, g.nrows, P::COL_PER_ROW, r, sub)) return;
+    if (g.kind == 0)
+        fs_colfwd_body<LOG1, LOG2, TIO, 0, CIRC>(lds, u, w3, nullptr, g.slot + r * L, tb, D, N, g.row0 + r, sub);
+    else if (MID && g.kind == 2)
+        fs_colinv_body<LOG1, LOG2, TIO, false, CIRC>(lds, g.slot + r * L, u, w3, y, tb, D, N, g.o, g.row0 + r, sub);
+    else
+        fs_colinv_body<LOG1, LOG2, TIO, true, CIRC>(lds, g.slot + r * L, u, w3, y, tb, D, N, g.o, g.row0 + r, sub);
+}
+
 // log2 L -> (log2 L1, log2 L2). Square splits up to L1 = 512, whose pass A/C
 // tile (512 x 17 complex) still leaves room for two workgroups per CU.
 #ifndef HY_FS_LOG1_16

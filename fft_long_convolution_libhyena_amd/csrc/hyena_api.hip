@@ -22,20 +22,15 @@ using hy::wfwd;
 namespace {
 
 constexpr int64_t kMaxLog = 20;
-constexpr size_t kChunkTargetBytes = 128u << 20;  // in-flight four-step intermediates per launch
+constexpr size_t kChunkTargetBytes = 128u << 20;  // in-flight four-step intermediates per sequential chunk
 constexpr int64_t kMaxChunkRows = 65536;
-#ifndef HY_AUTO_FUSED
-#define HY_AUTO_FUSED 0
-#endif
-constexpr bool kAutoFused = HY_AUTO_FUSED != 0;
-#ifndef HY_FUSED_G
-#define HY_FUSED_G 2
-#endif
-#ifndef HY_FUSED_S
-#define HY_FUSED_S 3
-#endif
-constexpr int kFusedG = HY_FUSED_G;  // rows per group of the fused pipeline
-constexpr int kFusedS = HY_FUSED_S;  // tile slots (groups) per XCD ring; >= 3
+// Order-2 four-step forwards run as pipelined launches (one launch per chunk of
+// rows plus two) when the workspace holds three tile slots of at least
+// min(rows, kPipeMinRows) rows; chunks are capped at kPipeRows rows (measured
+// on MI355X at L = 65536: 128-row chunks were fastest; chunks of 32 rows or
+// fewer leave the launches too small to fill the GPU).
+constexpr int64_t kPipeRows = 128;
+constexpr int64_t kPipeMinRows = 32;
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 int ilog2_64(int64_t x) {
@@ -61,6 +56,18 @@ int64_t chunk_rows(const hyena_plan_t plan, int64_t rows, size_t ws_bytes) {
     return n;
 }
 
+// Rows per chunk of a pipelined four-step forward with this workspace, or 0 when
+// the forward runs as sequential chunks instead.
+int64_t pipe_rows(const hyena_plan_t plan, int64_t rows, size_t ws_bytes) {
+    if (plan->path != HYENA_PATH_FOURSTEP || plan->order != 2 || !hy::fs_pipe_supported(plan->logT)) return 0;
+    const size_t slots = (size_t)(2 * plan->order - 1);
+    int64_t R = (int64_t)(ws_bytes / (slots * ws_per_row(plan)));
+    if (R > kPipeRows) R = kPipeRows;
+    if (R > rows) R = rows;
+    const int64_t need = rows < kPipeMinRows ? rows : kPipeMinRows;
+    return R >= need ? R : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -83,7 +90,7 @@ hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int
     const bool circ = (flags & HYENA_FLAG_CIRCULAR) != 0;
     if (D < 1 || L < 1 || order < 2) return HYENA_ERR_INVALID_ARG;
     if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_ERR_INVALID_ARG;
-    if (path != HYENA_PATH_AUTO && path != HYENA_PATH_LDS && path != HYENA_PATH_FOURSTEP && path != HYENA_PATH_FUSED &&
+    if (path != HYENA_PATH_AUTO && path != HYENA_PATH_LDS && path != HYENA_PATH_FOURSTEP &&
         path != HYENA_PATH_PARTITIONED)
         return HYENA_ERR_INVALID_ARG;
     if (!is_pow2(L) || L < 16 || L > (int64_t(1) << kMaxLog) || order > 8) return HYENA_ERR_UNSUPPORTED;
@@ -97,12 +104,10 @@ hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int
     hyena_path_t p = path;
     if (p == HYENA_PATH_AUTO) {
         if (logT <= hy::kLdsMaxLog) p = HYENA_PATH_LDS;
-        else if (!circ && kAutoFused && order == 2 && hy::fused_supported(logT)) p = HYENA_PATH_FUSED;
         else p = HYENA_PATH_FOURSTEP;
     }
     if (p == HYENA_PATH_LDS && logT > hy::kLdsMaxLog) return HYENA_ERR_UNSUPPORTED;
     if (p == HYENA_PATH_FOURSTEP && logT < hy::kFsMinLog) return HYENA_ERR_UNSUPPORTED;
-    if (p == HYENA_PATH_FUSED && (circ || !(order == 2 && hy::fused_supported(logT)))) return HYENA_ERR_UNSUPPORTED;
     if (p == HYENA_PATH_PARTITIONED && (circ || logT < hy::kPartMinLog || logT > hy::kPartMaxLog))
         return HYENA_ERR_UNSUPPORTED;
 
@@ -142,15 +147,6 @@ hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int
 
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return HYENA_ERR_DEVICE;
-    int fused_blocks = 0;
-    if (p == HYENA_PATH_FUSED) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
-            return HYENA_ERR_DEVICE;
-        const int per_cu = hy::fused_blocks_per_cu(logT);
-        if (per_cu < 1) return HYENA_ERR_DEVICE;
-        fused_blocks = (cus * per_cu) / 8 * 8;  // a multiple of 8: every XCD gets the same share
-    }
     float2* dtab = nullptr;
     if (hipMalloc((void**)&dtab, tab.size() * sizeof(float2)) != hipSuccess) return HYENA_ERR_DEVICE;
     if (hipMemcpy(dtab, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
@@ -171,7 +167,6 @@ hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int
     plan->dtype = dtype;
     plan->path = p;
     plan->device = dev;
-    plan->fused_blocks = fused_blocks;
     plan->dtab = dtab;
     if (p == HYENA_PATH_LDS || p == HYENA_PATH_PARTITIONED) {
         plan->tw = dtab + o_tw;
@@ -218,9 +213,12 @@ size_t hyena_spectrum_bytes(hyena_plan_t plan) {
 size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B) {
     if (!plan || B < 1) return 0;
     if (plan->path == HYENA_PATH_LDS) return 0;
-    if (plan->path == HYENA_PATH_FUSED) return hy::fused_workspace_bytes(plan->logT, B * plan->D, kFusedG, kFusedS);
     const size_t per_row = ws_per_row(plan);
     int64_t rows = B * plan->D;
+    if (pipe_rows(plan, rows, (size_t)-1) > 0) {
+        const int64_t R = rows < kPipeRows ? rows : kPipeRows;
+        return (size_t)(2 * plan->order - 1) * (size_t)R * per_row;
+    }
     int64_t want = (int64_t)(kChunkTargetBytes / per_row);
     if (want < 1) want = 1;
     if (want > rows) want = rows;
@@ -267,30 +265,28 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
     if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 26)) return HYENA_ERR_INVALID_ARG;
     const bool bf16 = plan->dtype == HYENA_BF16;
     const int64_t rows = B * plan->D;
-    int64_t chunk = 0;
-    if (per_sample && plan->path == HYENA_PATH_FUSED) return HYENA_ERR_UNSUPPORTED;
     // sample b reads spectrum b when every sample has its own filters
     const int64_t sbs = per_sample ? (int64_t)(plan->order - 1) * plan->D * (int64_t(1) << plan->logT) : 0;
-    if (plan->path == HYENA_PATH_FUSED) {
-        if (!workspace || !aligned16(workspace)) return HYENA_ERR_WORKSPACE;
-        if (workspace_bytes < hy::fused_workspace_bytes(plan->logT, rows, kFusedG, kFusedS)) return HYENA_ERR_WORKSPACE;
-    }
     const bool part = plan->path == HYENA_PATH_PARTITIONED;
     const bool chunked = plan->path == HYENA_PATH_FOURSTEP || part;
+    int64_t chunk = 0, pipe = 0;
     if (chunked) {
         if (!workspace || !aligned16(workspace)) return HYENA_ERR_WORKSPACE;
-        chunk = chunk_rows(plan, rows, workspace_bytes);
+        pipe = pipe_rows(plan, rows, workspace_bytes);
+        chunk = pipe > 0 ? pipe : chunk_rows(plan, rows, workspace_bytes);
         if (chunk < 1) return HYENA_ERR_WORKSPACE;
     }
     if (check_device(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
 
-    // launches per chunk: four-step 2N-1, partitioned 2(N-1)
+    // launches per chunk: four-step 2N-1, partitioned 2(N-1); pipelined: one per
+    // chunk plus 2N-2
     const int per_chunk = part ? 2 * (plan->order - 1) : 2 * plan->order - 1;
     const int64_t nchunks = chunked ? (rows + chunk - 1) / chunk : 1;
+    const int64_t nlaunch = pipe > 0 ? nchunks + 2 * plan->order - 2 : chunked ? nchunks * per_chunk : 1;
     std::vector<hipEvent_t> ev;
     if (ms) {
-        for (int i = 0; i < 5; ++i) ms[i] = 0.f;
-        const int64_t n = chunked ? nchunks * (per_chunk + 1) : 2;  // LDS, FUSED: 2
+        for (int i = 0; i < 6; ++i) ms[i] = 0.f;
+        const int64_t n = pipe > 0 ? nlaunch + 1 : chunked ? nchunks * (per_chunk + 1) : 2;
         if (n > 4096) return HYENA_ERR_INVALID_ARG;  // timing is for bounded chunk counts
         ev.resize((size_t)n, nullptr);
         for (auto& e : ev)
@@ -301,14 +297,7 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
             }
     }
     hyena_status_t st = HYENA_OK;
-    if (plan->path == HYENA_PATH_FUSED) {
-        hy::FsArgs a{u_proj, short_w, (const float2*)spec, bias, y, (float2*)workspace, plan->fs,
-                     (int)plan->D, plan->order, bf16};
-        if (ms) (void)hipEventRecord(ev[0], stream);
-        if (hy::launch_fs_fused(plan->logT, a, rows, kFusedG, kFusedS, plan->fused_blocks, stream) != hipSuccess)
-            st = HYENA_ERR_DEVICE;
-        if (ms) (void)hipEventRecord(ev[1], stream);
-    } else if (plan->path == HYENA_PATH_LDS) {
+    if (plan->path == HYENA_PATH_LDS) {
         if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
         hy::LdsArgs a{u_proj, short_w, (const float2*)spec, bias, y, plan->tw, plan->wpair,
                       (int)B, (int)plan->D, plan->order, bf16, sbs, plan->circular};
@@ -327,6 +316,12 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
             hipEvent_t* marks = ms ? ev.data() + ci * (per_chunk + 1) : nullptr;
             if (hy::launch_part_forward_chunk(a, r0, n, stream, marks) != hipSuccess) st = HYENA_ERR_DEVICE;
         }
+    } else if (pipe > 0) {
+        hy::FsArgs a{u_proj, short_w, (const float2*)spec, bias, y, (float2*)workspace, plan->fs,
+                     (int)plan->D, plan->order, bf16, sbs, plan->circular};
+        if (hy::launch_fs_forward_pipelined(plan->logT, a, rows, pipe, stream, ms ? ev.data() : nullptr) !=
+            hipSuccess)
+            st = HYENA_ERR_DEVICE;
     } else {
         hy::FsArgs a{u_proj, short_w, (const float2*)spec, bias, y, (float2*)workspace, plan->fs,
                      (int)plan->D, plan->order, bf16, sbs, plan->circular};
@@ -345,6 +340,11 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
             if (!chunked) {
                 (void)hipEventElapsedTime(&t, ev[0], ev[1]);
                 ms[0] = t;
+            } else if (pipe > 0) {
+                for (int64_t i = 0; i < nlaunch; ++i) {
+                    (void)hipEventElapsedTime(&t, ev[i], ev[i + 1]);
+                    ms[5] += t;
+                }
             } else if (part) {
                 for (int64_t c = 0; c < nchunks; ++c) {
                     hipEvent_t* m = ev.data() + c * (per_chunk + 1);
@@ -375,18 +375,6 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
 }  // namespace
 
 extern "C" {
-
-hyena_status_t hyena_fused_check(hyena_plan_t plan, const void* workspace, int* flag) {
-    if (!plan || !flag) return HYENA_ERR_INVALID_ARG;
-    *flag = 0;
-    if (plan->path != HYENA_PATH_FUSED) return HYENA_OK;
-    if (!workspace) return HYENA_ERR_INVALID_ARG;
-    uint32_t ctl[8 * 32];
-    if (hipMemcpy(ctl, workspace, sizeof(ctl), hipMemcpyDeviceToHost) != hipSuccess) return HYENA_ERR_DEVICE;
-    for (int x = 0; x < 8; ++x)
-        if (ctl[hy::fused_error_offset(x) / 4] != 0) *flag = 1;
-    return HYENA_OK;
-}
 
 hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
                              const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,

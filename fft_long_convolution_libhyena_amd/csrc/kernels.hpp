@@ -100,13 +100,16 @@ hipError_t launch_lds_spectrum(int logL, const float* h, float2* spec, int64_t r
                                const float2* wpair, hipStream_t st, bool circ = false);
 hipError_t launch_fs_forward_chunk(int logL, const FsArgs& a, int64_t row0, int64_t nrows, hipStream_t st,
                                    hipEvent_t* marks = nullptr);
+// Pipelined four-step forward over chunks of R rows: one launch per chunk plus
+// 2N-2, the workspace holding 2N-1 tile slots of R rows each. With `marks`, an
+// event is recorded before the first launch and after every launch.
+bool fs_pipe_supported(int logL);
+hipError_t launch_fs_forward_pipelined(int logL, const FsArgs& a, int64_t rows, int64_t R, hipStream_t st,
+                                       hipEvent_t* marks = nullptr);
 hipError_t launch_fs_spectrum(int logL, const float* h, float2* spec, int64_t rows, const FsTables& tb,
                               hipStream_t st, bool circ = false);
 void fs_split(int logL, int* log1, int* log2);
 
-// Fused persistent four-step (order 2): one launch per forward, per-XCD pipelines.
-bool fused_supported(int logL);
-int fused_blocks_per_cu(int logL);
 // Partitioned path: blocks of Q = 2^kPartLogQ taps, L from 2Q to 2^kPartMaxLog.
 constexpr int kPartLogQ = 12;
 constexpr int kPartMinLog = kPartLogQ + 1;
@@ -128,9 +131,6 @@ struct PartArgs {
 hipError_t launch_part_forward_chunk(const PartArgs& a, int64_t row0, int64_t n, hipStream_t st, hipEvent_t* marks);
 int part_group(int P);  // output blocks per pass 2 workgroup
 
-size_t fused_workspace_bytes(int logL, int64_t nrows, int G, int S);
-hipError_t launch_fs_fused(int logL, const FsArgs& a, int64_t nrows, int G, int S, int blocks, hipStream_t st);
-uint32_t fused_error_offset(int x);
 int fs_row_units(int logL);
 
 }  // namespace hy

@@ -16,7 +16,6 @@ struct hyena_plan_s {
     hyena_dtype_t dtype = HYENA_F32;
     hyena_path_t path = HYENA_PATH_AUTO;
     int device = -1;
-    int fused_blocks = 0;    // persistent grid of the fused path
     float2* dtab = nullptr;  // all twiddle tables, one device allocation
     // LDS path
     const float2* tw = nullptr;

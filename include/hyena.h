@@ -62,13 +62,11 @@ typedef enum {
 /* Which kernel family runs a plan.
  *   LDS       one launch; the whole transform of a (b, d) row stays in LDS
  *             (L <= 16384).
- *   FOURSTEP  three launches per recurrence step (column FFTs, row FFTs with
- *             the spectrum multiply, inverse columns with the gate); any order,
- *             256 <= L <= 2^20.
- *   FUSED     one persistent launch for the whole four-step forward, with the
- *             intermediate tiles kept in each XCD's L2 (order 2, L = 65536).
- *             Switched off: plans asking for it get
- *             HYENA_ERR_UNSUPPORTED.
+ *   FOURSTEP  three passes per recurrence step (column FFTs, row FFTs with
+ *             the spectrum multiply, inverse columns with the gate) over
+ *             chunks of rows; any order, 256 <= L <= 2^20. At order 2 with
+ *             L = 2^16 or 2^17 the chunks are pipelined: one launch runs the
+ *             three passes on three consecutive chunks.
  *   PARTITIONED  the same causal convolution with the filter cut into
  *             blocks of Q = 4096 taps (uniformly partitioned overlap-save):
  *             two LDS-resident launches per recurrence step (transforms of
@@ -81,7 +79,7 @@ typedef enum {
     HYENA_PATH_AUTO = 0,
     HYENA_PATH_LDS = 1,
     HYENA_PATH_FOURSTEP = 2,
-    HYENA_PATH_FUSED = 3,
+    /* 3 is unused (HYENA_ERR_INVALID_ARG) */
     HYENA_PATH_PARTITIONED = 4
 } hyena_path_t;
 
@@ -96,9 +94,8 @@ hyena_status_t hyena_plan_create(hyena_plan_t* out, int64_t L, int64_t D, int or
 
 /* As hyena_plan_create, with an explicit kernel family. HYENA_PATH_LDS needs
  * L <= 16384; HYENA_PATH_FOURSTEP needs L >= 256; HYENA_PATH_PARTITIONED needs
- * 8192 <= L <= 131072 and no flags; HYENA_PATH_FUSED is switched off
- * (HYENA_ERR_UNSUPPORTED). The spectrum layout depends on the
- * path (FOURSTEP and FUSED share one; PARTITIONED holds the 2Q-point spectra of
+ * 8192 <= L <= 131072 and no flags. The spectrum layout depends on the
+ * path (PARTITIONED holds the 2Q-point spectra of
  * each filter's L/Q blocks, [o][d][block][Q], in the LDS layout), so a spectrum
  * must be made by a plan whose path uses the same layout as the plan that
  * consumes it. */
@@ -118,7 +115,7 @@ enum {
 
 /* As hyena_plan_create_path, with option flags (0 or HYENA_FLAG_CIRCULAR).
  * HYENA_ERR_INVALID_ARG for unknown flag bits; HYENA_ERR_UNSUPPORTED for a
- * circular plan with L < 32 or on the fused path. */
+ * circular plan with L < 32 or on the partitioned path. */
 hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int order, hyena_dtype_t dtype,
                                     hyena_path_t path, uint32_t flags);
 
@@ -136,13 +133,16 @@ hyena_path_t hyena_plan_path(hyena_plan_t plan);
 size_t hyena_spectrum_bytes(hyena_plan_t plan);
 
 /* Workspace for a forward over batch B: 0 on the LDS path. On the four-step
- * path this is the recommended size (8*L bytes per (b, d) row held in flight);
- * any workspace of at least 8*L bytes (one row) is accepted, a larger one lets
- * more rows run per launch. The partitioned path likewise, with 8*L bytes per
- * row at order 2 and 12*L bytes per row above (the gated output of a step is
- * held for the next). On the fused path it is the exact minimum: a control
- * block, per-row counters and a ring of tiles per XCD. Returns 0 for a NULL plan
- * or B < 1. */
+ * path this is the recommended size, in tiles of 8*L bytes per (b, d) row held
+ * in flight: at order 2 with L = 2^16 or 2^17, three tile slots of
+ * min(B*D, 128) rows (the pipelined launches); otherwise up to 128 MiB of
+ * tiles. Any workspace of at least 8*L bytes (one row) is accepted: a
+ * pipelined forward needs three slots of min(B*D, 32) rows and otherwise runs
+ * chunk by chunk, and a larger one lets more rows run per launch. The
+ * partitioned path likewise, with 8*L bytes per row at order 2 and 12*L bytes
+ * per row above (the gated output of a step is held for the next). The choice
+ * of chunks never changes the result: every chunking gives the same bits.
+ * Returns 0 for a NULL plan or B < 1. */
 size_t hyena_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* The real FFT of the long filters, once per plan (the filter spectrum of the
@@ -200,25 +200,19 @@ hyena_status_t hyena_forward_per_sample(hyena_plan_t plan, int64_t B, const void
 /* hyena_forward with per-kernel timing, for measurement. HIP events are
  * recorded on `stream` around every kernel launch of this forward; the call
  * then waits for the last event (so it is synchronous), and writes elapsed
- * milliseconds summed per kernel family into ms[5]:
- *   ms[0] the single kernel of the LDS or fused path, ms[1] four-step pass A (column FFTs of the
- *   gated input), ms[2] pass B (row FFTs, spectrum multiply, inverse rows),
- *   ms[3] pass C (inverse columns and gate; for order > 2 it also carries the
- *   next step's pass A), ms[4] first event to last event. On the partitioned
- *   path ms[1] is pass 1 (window transforms) and ms[2] pass 2 (block sums,
- *   inverse transforms, gate).
+ * milliseconds summed per kernel family into ms[6]:
+ *   ms[0] the single kernel of the LDS path, ms[1] four-step pass A (column
+ *   FFTs of the gated input), ms[2] pass B (row FFTs, spectrum multiply,
+ *   inverse rows), ms[3] pass C (inverse columns and gate; for order > 2 it
+ *   also carries the next step's pass A), ms[4] first event to last event,
+ *   ms[5] the pipelined four-step launches (each runs all three passes, on
+ *   different chunks). On the partitioned path ms[1] is pass 1 (window
+ *   transforms) and ms[2] pass 2 (block sums, inverse transforms, gate).
  * Same arguments, results and errors as hyena_forward; HYENA_ERR_INVALID_ARG
  * also for ms == NULL or more than 4096 events. */
 hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
                                    const void* spec, const float* bias, void* y, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream, float* ms);
-
-/* Diagnostic for the fused path: after the stream has reached the end of a
- * forward that used `workspace`, reports in *flag whether any of the kernel's
- * bounded waits expired (nonzero: the output of that forward is invalid). Copies
- * the 1 KiB control block to the host synchronously. *flag = 0 on other paths. Errors:
- * HYENA_ERR_INVALID_ARG for NULL arguments, HYENA_ERR_DEVICE if the copy fails. */
-hyena_status_t hyena_fused_check(hyena_plan_t plan, const void* workspace, int* flag);
 
 /* Bytes of workspace hyena_backward needs for batch B.
  * LDS path: per (b, d) row the N-1 product spectra that the batch sums of dh are

@@ -1,6 +1,6 @@
 """bench.py end to end on the GPU, every mode on a small workload: one JSON line
 with the fields the measurement contract names, a roofline object, and (with
---check) the oracle comparison within the parity bound of the mode."""
+by default) the oracle comparison within the parity bound of the mode."""
 import json
 import os
 import subprocess
@@ -13,7 +13,7 @@ from tests._hy import say
 pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-COMMON = ["--steps", "2", "--reps", "1", "--warmup", "1", "--no-cpu-baseline", "--check"]
+COMMON = ["--steps", "2", "--reps", "1", "--warmup", "1", "--no-cpu-baseline"]
 KEYS = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
         "vs_baseline", "dtype", "data", "config", "roofline"}
 ROOF = {"bound", "achieved", "peak", "unit", "frac", "traffic"}
@@ -42,7 +42,8 @@ def _run(args):
     (["--path", "fourstep"], "tiny"), (["--conv2d"], None), (["--conv3d", "--circular"], None),
     # full workloads in the launch configuration the benchmark times, checked on sampled outputs
     (["--circular"], "long64k"), (["--circular"], "lm125m"), (["--path", "partitioned"], "long64k"),
-    (["--operator"], "lm125m"), (["--per-sample"], "long64k"), (["--backward", "--per-sample"], "lm125m")])
+    (["--operator"], "lm125m"), (["--per-sample"], "long64k"), (["--backward", "--per-sample"], "lm125m"),
+    ([], "long64k"), ([], "long64k_o3"), ([], "lm125m")])
 def test_bench_line(mode, workload):
     args = mode + COMMON + (["--workload", workload] if workload else [])
     out = _run(args)
@@ -52,6 +53,8 @@ def test_bench_line(mode, workload):
     assert out["n_gpus"] == 1 and out["steps"] == 2 and out["warmup"] == 1
     assert out["value"] > 0 and out["ms_per_step"] > 0 and out["higher_is_better"] is True
     assert out["roofline"]["peak"] > 0 and 0 < out["roofline"]["frac"] < 1.5
+    assert (out["roofline"]["bound"], out["roofline"]["unit"]) in {("hbm", "GB/s"), ("alu", "TFLOP/s"),
+                                                                   ("mfma", "TFLOP/s")}
     assert "workload" in out["config"]
     checks = {k: v for k, v in out.items() if k.startswith("check_rel_l2")}
     if "--filter" not in mode:
