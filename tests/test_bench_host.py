@@ -73,7 +73,7 @@ def test_kernel_families_cover_the_summaries():
     """Every committed counter summary names a kernel whose family lists real sources."""
     for f in os.listdir(os.path.join(ROOT, "profiles")):
         if f.startswith("pmc_"):
-            kernel = next(k for k in ("k_fs_row", "k_lds_forward", "k_lds_bwd_rows", "fs_backward",
+            kernel = next(k for k in ("k_fs_pipe", "k_fs_row", "k_lds_forward", "k_lds_bwd_rows", "fs_backward",
                                       "k_implicit_filter", "k_part_inv", "k_c2_conv2d", "k_c3_conv3d")
                           if f[4:].startswith(k))
             for src in bench.KERNEL_SOURCES[bench.kernel_family(kernel)]:
@@ -87,3 +87,66 @@ def test_cpu_baseline_of_the_small_workload_times_the_direct_definition():
     res = bench.cpu_baseline(x, w, 1.0)
     assert res["kind"] == "oracle" and res["value"] > 0 and res["cores"] >= 1
     assert res["direct"]["value"] > 0 and "direct" in res["direct"]["sample"]
+
+
+def test_roofline_bound_follows_the_ridge():
+    """Intensity at or below 78.6 TFLOP/s / 8 TB/s = 9.83 flop/B prices against HBM,
+    above it against the unpacked fp32 vector rate; worked by hand."""
+    assert bench.RIDGE_FLOP_PER_BYTE == pytest.approx(9.825, abs=1e-3)
+    r = bench.roofline("k", 1, 1.0, 4e9, 32e9)  # 8 flop/B, 4 GB in 1 ms = 4000 GB/s
+    assert (r["bound"], r["unit"], r["peak"]) == ("hbm", "GB/s", 8000.0)
+    assert r["achieved"] == pytest.approx(4000.0) and r["frac"] == pytest.approx(0.5)
+    r = bench.roofline("k", 1, 1.0, 1e9, 20e9)  # 20 flop/B, 20 GFLOP in 1 ms = 20 TFLOP/s
+    assert (r["bound"], r["unit"], r["peak"]) == ("alu", "TFLOP/s", 78.6)
+    assert r["frac"] == pytest.approx(20.0 / 78.6, abs=1e-4)
+    r = bench.roofline("k", 2, 0.5, 1e9, 1e9, traffic=3e9, step_traffic=6e9, step_alg_bytes=2e9)
+    assert r["step_traffic_over_alg"] == 3.0 and r["launches_per_step"] == 2
+
+
+@pytest.mark.parametrize("name,bound", [("tiny", "hbm"), ("dna_small", "hbm"), ("lm125m", "alu"),
+                                        ("long64k_o3", "alu"), ("long64k", "hbm"), ("dna_1m", "hbm")])
+def test_workload_bounds(name, bound):
+    w = synth.WORKLOADS[name]
+    b, f = bench.alg_bytes_forward(w), bench.alg_flops_forward(w)
+    assert bench.roofline("k", 1, 1.0, b, f)["bound"] == bound
+
+
+def test_pipe_chunk_rows_mirrors_the_library_rule():
+    tile = 8 * 65536
+    assert bench.pipe_chunk_rows(768, 3 * 128 * tile, tile) == 128   # the recommended workspace
+    assert bench.pipe_chunk_rows(768, 3 * 500 * tile, tile) == 128   # capped at 128 rows
+    assert bench.pipe_chunk_rows(768, 3 * 42 * tile, tile) == 42
+    assert bench.pipe_chunk_rows(768, 3 * 31 * tile, tile) == 0      # below 32 rows: chunk by chunk
+    assert bench.pipe_chunk_rows(20, 3 * 20 * tile, tile) == 20      # fewer rows than 32: all of them
+    assert bench.pipe_chunk_rows(20, 3 * 19 * tile, tile) == 0
+
+
+def test_pmc_summary_from_csv(tmp_path, capsys):
+    """--summarize-pmc on hand-made rocprofv3 csv rows: per-dispatch bytes of the kernel
+    scaled by the copy calibration, the forward's kernels summed over the forwards."""
+    import argparse
+    import csv
+
+    def write(d, counter, vals):
+        d.mkdir()
+        with open(d / "x_counter_collection.csv", "w", newline="") as fh:
+            w = csv.DictWriter(fh, ["Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for name, v in vals:
+                w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+
+    pipe = "void hy::k_fs_pipe<8, 8, float, false, false>(float const*)"
+    spec = "void hy::k_fs_row<8, 8, 1>(float2*)"
+    write(tmp_path / "fe", "FETCH_SIZE", [(pipe, 100.0), (pipe, 300.0), (spec, 999.0)])
+    write(tmp_path / "wr", "WRITE_SIZE", [(pipe, 50.0), (pipe, 50.0), (spec, 999.0)])
+    args = argparse.Namespace(summarize_pmc=[str(tmp_path / "fe"), str(tmp_path / "wr")], kernel="k_fs_pipe",
+                              workload="long64k", forwards=2, command="cmd one;;cmd two")
+    bench.summarize_pmc(args)
+    text = capsys.readouterr().out
+    kv = dict(ln.split(": ", 1) for ln in text.splitlines() if ": " in ln and not ln.startswith("#"))
+    fs, ws = bench._calibration()
+    assert float(kv["fetch_bytes_per_dispatch"]) == pytest.approx(200 * 1024 * fs, rel=1e-5)
+    assert float(kv["write_bytes_per_dispatch"]) == pytest.approx(50 * 1024 * ws, rel=1e-5)
+    # two dispatches over two forwards; the spectrum kernel is not part of the forward
+    assert float(kv["step_bytes"]) == pytest.approx((400 * fs + 100 * ws) * 1024 / 2, rel=1e-5)
+    assert "#   cmd one" in text and "#   cmd two" in text
