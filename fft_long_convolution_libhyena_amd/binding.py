@@ -35,7 +35,7 @@ EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_create_ex"
            "hyena_spectrum3d_bytes", "hyena_workspace3d_bytes", "hyena_filter_spectrum3d", "hyena_conv3d_forward",
            "hyena_filter_spectrum2d_batched", "hyena_conv2d_forward_per_sample", "hyena_filter_spectrum3d_batched",
            "hyena_conv3d_forward_per_sample", "hyena_plan2d_create_ex", "hyena_plan3d_create_ex",
-           "hyena_status_string")
+           "hyena_forward_noalloc", "hyena_status_string")
 
 
 class FilterMLPStruct(ctypes.Structure):
@@ -93,6 +93,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_filter_spectrum_batched.restype = ci
     lib.hyena_forward_per_sample.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hyena_forward_per_sample.restype = ci
+    lib.hyena_forward_noalloc.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp]
+    lib.hyena_forward_noalloc.restype = ci
     lib.hyena_forward_timed.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
     lib.hyena_forward_timed.restype = ci
     lib.hyena_backward_workspace_bytes.argtypes = [vp, i64]
@@ -310,6 +312,24 @@ class Plan:
                     else (self.lib.hyena_forward, "hyena_forward"))
         _check(name, fn(self.handle, B, u_proj.data_ptr(), short_w.data_ptr(), spec.data_ptr(), bias.data_ptr(),
                         y.data_ptr(), ws_ptr or None, ws_bytes, _stream_handle(torch, self.device)))
+        return y
+
+    def forward_noalloc(self, u_proj, short_w, spec, bias, y):
+        """hyena_forward_noalloc: as forward into a caller-given y, with no workspace
+        and no allocation (the library's per-device scratch array holds the tiles;
+        calls that overlap on one GPU race)."""
+        torch = self._torch
+        N, D, L = self.order, self.D, self.L
+        B = int(u_proj.shape[0])
+        self._need(u_proj, "u_proj", (B, (N + 1) * D, L), self.io_dtype)
+        self._need(short_w, "short_w", ((N + 1) * D, 3), torch.float32)
+        self._need(bias, "bias", (N - 1, D), torch.float32)
+        self._need(y, "y", (B, D, L), self.io_dtype)
+        if spec.device != self.device or spec.numel() * spec.element_size() < self.spectrum_bytes():
+            raise ValueError("spec must come from Plan.spectrum of an equal plan")
+        _check("hyena_forward_noalloc",
+               self.lib.hyena_forward_noalloc(self.handle, B, u_proj.data_ptr(), short_w.data_ptr(), spec.data_ptr(),
+                                              bias.data_ptr(), y.data_ptr(), _stream_handle(torch, self.device)))
         return y
 
     def forward_timed(self, u_proj, short_w, spec, bias, y, workspace=None):

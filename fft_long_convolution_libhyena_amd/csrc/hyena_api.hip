@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -374,7 +375,52 @@ hyena_status_t forward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, co
 
 }  // namespace
 
+// ----------------------------------------------- forward without allocation
+//
+// The four-step and partitioned paths keep their tiles in a workspace. For
+// callers that cannot allocate, hyena_forward_noalloc uses this file-scope
+// device array instead. Host code never passes the array's name to a kernel or
+// a copy (on the host it is only a stand-in for the symbol): the device address
+// is looked up once per device with hipGetSymbolAddress, with that device
+// current, and kept in g_scratch_ptr.
+static constexpr size_t kScratchBytes = HYENA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, or nullptr.
+void* scratch_on_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
+
+hyena_status_t hyena_forward_noalloc(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                                     const void* spec, const float* bias, void* y, hipStream_t stream) {
+    if (!plan) return HYENA_ERR_INVALID_ARG;
+    if (plan->path == HYENA_PATH_LDS)  // no scratch on the LDS path
+        return forward_impl(plan, B, u_proj, short_w, spec, bias, y, nullptr, 0, stream, nullptr);
+    // the smallest workspace the path accepts: one row's tiles
+    if (ws_per_row(plan) > kScratchBytes) return HYENA_ERR_WORKSPACE;
+    if (check_device(plan) != HYENA_OK) return HYENA_ERR_DEVICE;
+    void* ws = scratch_on_current_device();
+    if (!ws) return HYENA_ERR_DEVICE;
+    return forward_impl(plan, B, u_proj, short_w, spec, bias, y, ws, kScratchBytes, stream, nullptr);
+}
 
 hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
                              const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,

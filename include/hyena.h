@@ -188,6 +188,25 @@ hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, c
                              const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): hyena_forward with no
+ * workspace argument and no allocation of any kind. The four-step and
+ * partitioned paths keep their tiles in a scratch array of
+ * HYENA_NOALLOC_SCRATCH_BYTES bytes that the library holds in device memory on
+ * every GPU it runs on, from load until the process ends (the LDS path needs
+ * none); chunks of rows are sized to it, so long rows run fewer rows per launch
+ * than with the recommended workspace (the results are the same bits).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time on
+ * one GPU (on different streams, or from different host threads without
+ * ordering) race and give undefined results. The array's contents on entry are
+ * irrelevant. Same arguments, results and errors as hyena_forward otherwise;
+ * HYENA_ERR_WORKSPACE if one row's tiles exceed the array (not reachable with
+ * the supported sizes), HYENA_ERR_DEVICE if the array's address cannot be
+ * obtained on the current device. */
+#define HYENA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hyena_status_t hyena_forward_noalloc(hyena_plan_t plan, int64_t B, const void* u_proj, const float* short_w,
+                                     const void* spec, const float* bias, void* y, hipStream_t stream);
+
 /* hyena_forward with a filter set per sample (input-dependent long convolutions,
  * the HyenaND summary's methodology): sample b is convolved with the filters whose
  * spectrum hyena_filter_spectrum_batched wrote at byte b * hyena_spectrum_bytes
