@@ -4,15 +4,19 @@
  * (per-sample filters, circular plans, gated 2-D and 3-D long convolutions), on
  * AMD MI355X (gfx950).
  *
- * The operator (HyenaDNA walkthrough, section 2.1, HyenaOperator.forward):
- *   uc  = ShortConv(u_proj)[..., :L]    depthwise Conv1d, 3 taps, padding 2
- *   x_0 .. x_{N-1}, v = split(uc, D)    gates first, the value v is the last chunk
- *   for o in 0 .. N-2:                  gates taken from reversed(x[1:])
- *       v = v * x_{N-1-o}
- *       v = conv(v, h[o]) + bias[o] * v (HyenaFilter.forward -> fftconv, section 2.2)
- *   y = v * x_0
- * where conv is the causal per-channel long convolution
- *   conv(v, h)[t] = sum_{s <= t} h[s] v[t - s],
+ * The operator (HyenaDNA walkthrough, section 2.1, the Hyena operator module and
+ * its forward pass; section 2.2, the long-filter module and its FFT convolution).
+ * For each channel d < D and time t < L, with u the in-projected activation of
+ * (N+1)*D channels:
+ *   uc[c][t] = w[c][0] u[c][t-2] + w[c][1] u[c][t-1] + w[c][2] u[c][t],
+ *              u[c][t'] = 0 for t' < 0 (a causal width-3 depthwise filter);
+ *   x_i[d] = uc[i*D + d] for i < N (the gates), v_0[d] = uc[N*D + d] (the value);
+ *   for o = 0 .. N-2 (the gates taken from x_{N-1} down to x_1):
+ *       g_o     = v_o (.) x_{N-1-o}
+ *       v_{o+1} = h[o] * g_o + bias[o] g_o
+ *   y = v_{N-1} (.) x_0,
+ * with (.) the elementwise product and * the causal per-channel long convolution
+ *   (h * g)[t] = sum_{s <= t} h[s] g[t - s],
  * evaluated by FFT on the sequence zero-padded to 2L (the HyenaND summary's
  * boundary handling; the Hyena Hierarchy concept page, section 3.2, FFT
  * acceleration). hyena_operator_forward adds the module's in/out projections and
