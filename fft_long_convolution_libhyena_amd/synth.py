@@ -245,6 +245,69 @@ def filter_mlp(wl: Workload, emb_dim: int = 3, width: int = 16, num_inner: int =
 
 
 @dataclasses.dataclass
+class SynthParams:
+    """Parameters of the input-dependent kernel synthesis (a FiLM-modulated
+    coordinate SIREN times a Gaussian window), all fp32. A = len(grid) axes,
+    W hidden units, M layers, Z control values, C output kernels."""
+    grid: tuple          # kernel grid size per axis (axis 0 slowest)
+    signed: tuple        # per axis: True for signed (wrapped) offsets, False for causal ones
+    w_first: np.ndarray  # [W, A]
+    w_hidden: np.ndarray  # [M-1, W, W]
+    b_layer: np.ndarray  # [M, W]
+    omega: np.ndarray    # [M, W] sine frequencies
+    film_g: np.ndarray   # [M, W, Z]  gamma = film_g z + film_gb
+    film_gb: np.ndarray  # [M, W]
+    film_b: np.ndarray   # [M, W, Z]  beta = film_b z + film_bb
+    film_bb: np.ndarray  # [M, W]
+    w_out: np.ndarray    # [C, W]
+    b_out: np.ndarray    # [C]
+    win_mu: np.ndarray   # [C, A] window centres (coordinate units)
+    win_sigma: np.ndarray  # [C, A] window widths (coordinate units)
+
+
+def synthesis_params(grid, signed, channels: int, width: int = 16, layers: int = 2, zdim: int = 8,
+                     seed: int = 0) -> SynthParams:
+    """Seeded synthesis parameters. SIREN-style draws: first layer U(-1/A, 1/A),
+    hidden layers U(-sqrt(6/W)/omega, sqrt(6/W)/omega) per unit, biases U(-1/fan_in,
+    1/fan_in); the sine frequencies come in blocks of units with frequencies 1, 4,
+    12 and 30 (the multi-frequency initialisation); FiLM maps near the identity
+    (gamma = 1 + 0.1 N(0,1) z-terms, beta = 0.1 N(0,1) z-terms); output weights
+    N(0, 1/W); window centres U(0, 0.3) on causal axes and U(-0.3, 0.3) on signed
+    ones, widths U(0.15, 0.6). Drawn from their own PCG64 stream (seed + 5000)."""
+    grid = tuple(int(n) for n in grid)
+    signed = tuple(bool(x) for x in signed)
+    if not 1 <= len(grid) <= 3 or len(signed) != len(grid):
+        raise ValueError("1 to 3 axes, one signed flag per axis")
+    rng = np.random.Generator(np.random.PCG64(seed + 5000))
+    A, W, M, Z, C = len(grid), width, layers, zdim, channels
+    blocks = np.array([1.0, 4.0, 12.0, 30.0])
+    omega = np.tile(blocks[(np.arange(W) * len(blocks)) // W], (M, 1))
+    w_first = rng.uniform(-1.0 / A, 1.0 / A, (W, A))
+    lim = np.sqrt(6.0 / W) / omega[1:, :, None]
+    w_hidden = rng.uniform(-1.0, 1.0, (M - 1, W, W)) * lim
+    b_layer = np.concatenate([rng.uniform(-1.0 / A, 1.0 / A, (1, W)), rng.uniform(-1.0 / W, 1.0 / W, (M - 1, W))])
+    film_g = 0.1 * rng.standard_normal((M, W, Z))
+    film_gb = np.ones((M, W))
+    film_b = 0.1 * rng.standard_normal((M, W, Z))
+    film_bb = np.zeros((M, W))
+    w_out = rng.standard_normal((C, W)) / np.sqrt(W)
+    b_out = 0.1 * rng.standard_normal(C)
+    lo = np.array([-0.3 if sg else 0.0 for sg in signed])
+    win_mu = lo + rng.uniform(0.0, 1.0, (C, A)) * (0.3 - lo)
+    win_sigma = rng.uniform(0.15, 0.6, (C, A))
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)  # noqa: E731
+    return SynthParams(grid, signed, f32(w_first), f32(w_hidden), f32(b_layer), f32(omega), f32(film_g),
+                       f32(film_gb), f32(film_b), f32(film_bb), f32(w_out), f32(b_out), f32(win_mu),
+                       f32(win_sigma))
+
+
+def synthesis_controls(B: int, zdim: int, seed: int = 0) -> np.ndarray:
+    """Per-sample control vectors z [B, Z] ~ N(0, 1), fp32 (seed + 6000)."""
+    rng = np.random.Generator(np.random.PCG64(seed + 6000))
+    return rng.standard_normal((B, zdim), dtype=np.float32)
+
+
+@dataclasses.dataclass
 class Conv2dInputs:
     """Inputs of one gated 2-D long-convolution step (all fp32; bf16 values for bf16)."""
     v: np.ndarray     # [B, D, H, W]

@@ -437,6 +437,68 @@ def implicit_filter(L: int, D: int, order: int, p) -> np.ndarray:
     return np.ascontiguousarray(h.T.reshape(order - 1, D, L))
 
 
+def synthesis_coords(grid, signed) -> np.ndarray:
+    """Coordinates of the points of a kernel grid, [P, A] float64 with the points in
+    row-major order (axis 0 slowest). Reading taken (the HyenaND summary, method,
+    kernel parametrisation, defines the kernel on a continuous coordinate grid but
+    gives no mapping): index j of a causal axis of n points sits at c = j / n in
+    [0, 1); a signed axis of n points holds the offsets j for j < n/2 and j - n
+    above (the wrapped layout of a kernel on a doubled or periodic grid), at
+    c = 2 * offset / n in [-1, 1)."""
+    axes = []
+    for n, sg in zip(grid, signed):
+        j = np.arange(n, dtype=np.float64)
+        if sg:
+            off = np.where(j < n // 2, j, j - n)
+            axes.append(2.0 * off / n)
+        else:
+            axes.append(j / n)
+    mesh = np.meshgrid(*axes, indexing="ij")
+    return np.stack([m.reshape(-1) for m in mesh], axis=1)
+
+
+def kernel_synthesis(p, z: np.ndarray) -> np.ndarray:
+    """Input-dependent kernels K [B, C, *grid] in float64 (HyenaND summary, method:
+    input-dependent kernels through registers and FiLM, kernel synthesis, kernel
+    parametrisation): K_b = w(c) * f(c; z_b) at every grid coordinate c, where f is
+    a coordinate SIREN whose layers are modulated by FiLM from the sample's control
+    vector z_b, and w is a Gaussian window per output kernel.
+
+    With h_0 = c and, for layers l = 0 .. M-1 (W_0 = w_first, W_l = w_hidden[l-1]):
+        a_l     = W_l h_l + b_l
+        gamma_l = G_l z_b + g_l,   beta_l = E_l z_b + e_l
+        h_{l+1} = sin(omega_l * (gamma_l * a_l + beta_l))
+    f = W_out h_M + b_out, and for kernel k
+        w_k(c)  = exp(-1/2 sum_i ((c_i - mu_{k,i}) / sigma_{k,i})^2).
+    Readings taken where the summary gives no formula: the SIREN activation is
+    sin(omega * x) with a frequency per hidden unit (the multi-frequency
+    initialisation gives blocks of units different frequencies); FiLM scales and
+    shifts the pre-activation inside the sine, with gamma and beta affine in z per
+    layer; the output layer is affine with no sine; the window is an axis-aligned
+    Gaussian per output kernel; z_b is given (the register tokens and their softmax
+    pooling belong to the model around the operator). `p` carries the fields of
+    synth.SynthParams; z is [B, Z]."""
+    c = synthesis_coords(p.grid, p.signed)
+    z = np.asarray(z, np.float64)
+    M = np.asarray(p.b_layer).shape[0]
+    f64 = lambda a: np.asarray(a, np.float64)  # noqa: E731
+    mu, sigma = f64(p.win_mu), f64(p.win_sigma)
+    win = np.exp(-0.5 * np.sum(((c[:, None, :] - mu[None]) / sigma[None]) ** 2, axis=2))  # [P, C]
+    C = mu.shape[0]
+    out = np.empty((z.shape[0], C) + tuple(p.grid))
+    for b in range(z.shape[0]):
+        h = c
+        for layer in range(M):
+            Wl = f64(p.w_first) if layer == 0 else f64(p.w_hidden)[layer - 1]
+            a = h @ Wl.T + f64(p.b_layer)[layer]
+            gamma = f64(p.film_g)[layer] @ z[b] + f64(p.film_gb)[layer]
+            beta = f64(p.film_b)[layer] @ z[b] + f64(p.film_bb)[layer]
+            h = np.sin(f64(p.omega)[layer] * (gamma * a + beta))
+        f = h @ f64(p.w_out).T + f64(p.b_out)  # [P, C]
+        out[b] = (win * f).T.reshape((C,) + tuple(p.grid))
+    return out
+
+
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
     """||got - ref||_2 / ||ref||_2 over every element, with got widened to fp64.
 
