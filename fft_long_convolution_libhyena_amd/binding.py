@@ -35,7 +35,7 @@ EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_create_ex"
            "hyena_spectrum3d_bytes", "hyena_workspace3d_bytes", "hyena_filter_spectrum3d", "hyena_conv3d_forward",
            "hyena_filter_spectrum2d_batched", "hyena_conv2d_forward_per_sample", "hyena_filter_spectrum3d_batched",
            "hyena_conv3d_forward_per_sample", "hyena_plan2d_create_ex", "hyena_plan3d_create_ex",
-           "hyena_forward_noalloc", "hyena_status_string")
+           "hyena_forward_noalloc", "hyena_kernel_synthesis", "hyena_status_string")
 
 
 class FilterMLPStruct(ctypes.Structure):
@@ -45,6 +45,16 @@ class FilterMLPStruct(ctypes.Structure):
                 ("band_freq", ctypes.c_void_p), ("w_in", ctypes.c_void_p), ("b_in", ctypes.c_void_p),
                 ("w_inner", ctypes.c_void_p), ("b_inner", ctypes.c_void_p), ("sin_freq", ctypes.c_void_p),
                 ("w_out", ctypes.c_void_p), ("alpha", ctypes.c_void_p)]
+
+
+class SynthParamsStruct(ctypes.Structure):
+    """hyena_synth_params_t: sizes, then device pointers of the kernel-synthesis
+    parameters (see include/hyena.h)."""
+    _fields_ = [("axes", ctypes.c_int64), ("grid", ctypes.c_int64 * 3), ("signed_axes", ctypes.c_uint32),
+                ("width", ctypes.c_int64), ("layers", ctypes.c_int64), ("zdim", ctypes.c_int64),
+                ("channels", ctypes.c_int64)] + [(n, ctypes.c_void_p) for n in (
+                    "w_first", "w_hidden", "b_layer", "omega", "film_g", "film_gb", "film_b", "film_bb", "w_out",
+                    "b_out", "win_mu", "win_sigma")]
 
 
 class HyenaError(RuntimeError):
@@ -93,6 +103,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_filter_spectrum_batched.restype = ci
     lib.hyena_forward_per_sample.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hyena_forward_per_sample.restype = ci
+    lib.hyena_kernel_synthesis.argtypes = [ctypes.POINTER(SynthParamsStruct), i64, vp, vp, vp]
+    lib.hyena_kernel_synthesis.restype = ci
     lib.hyena_forward_noalloc.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp]
     lib.hyena_forward_noalloc.restype = ci
     lib.hyena_forward_timed.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, sz, vp, ctypes.POINTER(ctypes.c_float)]
@@ -173,6 +185,47 @@ def _check(call: str, st: int) -> None:
 
 def _stream_handle(torch, device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def kernel_synthesis(params, z, out=None):
+    """hyena_kernel_synthesis: the input-dependent kernels of B samples.
+    `params` has the fields of synth.SynthParams as fp32 device tensors (grid and
+    signed as tuples); z is [B, Z] fp32 on the device. Returns k [B, C, *grid]."""
+    import torch
+
+    lib = load_library()
+    z = z.contiguous()
+    B, Z = int(z.shape[0]), int(z.shape[1])
+    grid = tuple(int(n) for n in params.grid)
+    A = len(grid)
+    C, W = int(params.w_out.shape[0]), int(params.w_out.shape[1])
+    M = int(params.b_layer.shape[0])
+    dev = z.device
+    want = {"w_first": (W, A), "w_hidden": (M - 1, W, W), "b_layer": (M, W), "omega": (M, W), "film_g": (M, W, Z),
+            "film_gb": (M, W), "film_b": (M, W, Z), "film_bb": (M, W), "w_out": (C, W), "b_out": (C,),
+            "win_mu": (C, A), "win_sigma": (C, A)}
+    ptrs = {}
+    for name, shape in want.items():
+        t = getattr(params, name)
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous fp32 device tensor of shape {shape}")
+        ptrs[name] = t.data_ptr() if t.numel() else None
+    if z.dtype != torch.float32:
+        raise ValueError("z must be fp32")
+    if out is None:
+        out = torch.empty((B, C) + grid, dtype=torch.float32, device=dev)
+    if tuple(out.shape) != (B, C) + grid or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor [B, C, *grid]")
+    st = SynthParamsStruct()
+    st.axes, st.width, st.layers, st.zdim, st.channels = A, W, M, Z, C
+    for i in range(3):
+        st.grid[i] = grid[i] if i < A else 1
+    st.signed_axes = sum(1 << i for i, sg in enumerate(params.signed) if sg)
+    for name, ptr in ptrs.items():
+        setattr(st, name, ptr)
+    _check("hyena_kernel_synthesis",
+           lib.hyena_kernel_synthesis(ctypes.byref(st), B, z.data_ptr(), out.data_ptr(), _stream_handle(torch, dev)))
+    return out
 
 
 class Plan:

@@ -192,6 +192,64 @@ hyena_status_t hyena_forward(hyena_plan_t plan, int64_t B, const void* u_proj, c
                              const void* spec, const float* bias, void* y, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+/* Parameters of the input-dependent kernel synthesis (HyenaND summary, method:
+ * input-dependent kernels through registers and FiLM, kernel synthesis, kernel
+ * parametrisation). With A = axes, W = width, M = layers, Z = zdim and
+ * C = channels; all arrays fp32, row-major, device, 16-byte aligned:
+ *   w_first  [W][A]      first layer, on the coordinates
+ *   w_hidden [M-1][W][W] further layers (may be NULL when M = 1); row = output unit
+ *   b_layer  [M][W]      layer biases
+ *   omega    [M][W]      sine frequency of every hidden unit
+ *   film_g [M][W][Z], film_gb [M][W]   FiLM scale  gamma_l = film_g[l] z + film_gb[l]
+ *   film_b [M][W][Z], film_bb [M][W]   FiLM shift  beta_l  = film_b[l] z + film_bb[l]
+ *   w_out [C][W], b_out [C]            affine output layer, one row per kernel
+ *   win_mu [C][A], win_sigma [C][A]    Gaussian window of every kernel
+ * Layer l maps h_l to h_{l+1} = sin(omega_l * (gamma_l * (W_l h_l + b_l) + beta_l))
+ * with h_0 the coordinate c of a grid point; the kernel is
+ *   K_k(c) = exp(-1/2 sum_i ((c_i - mu_ki) / sigma_ki)^2) * (w_out[k] . h_M + b_out[k]).
+ * The grid has grid[i] points on axis i (axis 0 slowest; grid[i] for i >= axes is
+ * ignored). Point j of a causal axis of n points sits at c = j / n; a signed axis
+ * (bit i of signed_axes set) holds the wrapped offsets j (j < n/2) and j - n
+ * (j >= n/2) at c = 2 * offset / n. 1-D Hyena filters use one causal axis of L
+ * points with C = (N-1)*D (kernel o*D + d is filter o of channel d); the 2-D and
+ * 3-D steps use signed axes on their kernel grid (2H x 2W, or H x W for a
+ * circular plan) with C = D. */
+typedef struct hyena_synth_params_s {
+    int64_t axes;          /* 1, 2 or 3 */
+    int64_t grid[3];       /* points per axis; at most 2^28 points in all */
+    uint32_t signed_axes;  /* bit i: axis i holds signed offsets */
+    int64_t width;         /* W: 8, 16, 32 or 64 */
+    int64_t layers;        /* M: 1 .. 16 */
+    int64_t zdim;          /* Z: 1 .. 256 */
+    int64_t channels;      /* C: 1 .. 2^24 */
+    const float* w_first;
+    const float* w_hidden;
+    const float* b_layer;
+    const float* omega;
+    const float* film_g;
+    const float* film_gb;
+    const float* film_b;
+    const float* film_bb;
+    const float* w_out;
+    const float* b_out;
+    const float* win_mu;
+    const float* win_sigma;
+} hyena_synth_params_t;
+
+/* Synthesise B samples' kernels from their control vectors:
+ *   z [B][Z] fp32, device: the control vector of every sample (derived by the
+ *     model from its register tokens)
+ *   k [B][C][grid points] fp32, device (output): kernel kk of sample b at
+ *     k + (b*C + kk) * points, points in row-major grid order; for 1-D filters this
+ *     is the [B][N-1][D][L] input of hyena_filter_spectrum_batched.
+ * Enqueued on `stream` on the current device (no plan). HYENA_ERR_INVALID_ARG for
+ * NULL or misaligned pointers, B < 1, sizes below 1 or signed bits beyond the axes;
+ * HYENA_ERR_UNSUPPORTED for a width other than 8/16/32/64, more than 16 layers,
+ * Z > 256, more than 2^28 grid points, B > 65535 or C > 2^24; HYENA_ERR_DEVICE if
+ * the launch fails. */
+hyena_status_t hyena_kernel_synthesis(const hyena_synth_params_t* params, int64_t B, const float* z, float* k,
+                                      hipStream_t stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): hyena_forward with no
  * workspace argument and no allocation of any kind. The four-step and
