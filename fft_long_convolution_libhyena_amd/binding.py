@@ -28,7 +28,7 @@ EXPORTS = ("hyena_plan_create", "hyena_plan_create_path", "hyena_plan_create_ex"
            "hyena_spectrum_bytes", "hyena_workspace_bytes", "hyena_filter_spectrum", "hyena_forward",
            "hyena_forward_timed", "hyena_backward_workspace_bytes", "hyena_backward",
            "hyena_backward_per_sample_workspace_bytes", "hyena_backward_per_sample",
-           "hyena_operator_workspace_bytes", "hyena_operator_forward", "hyena_operator_forward_timed",
+           "hyena_operator_workspace_bytes", "hyena_operator_forward", "hyena_operator_forward_timed", "hyena_operator_tune",
            "hyena_implicit_filter", "hyena_filter_spectrum_batched", "hyena_forward_per_sample",
            "hyena_plan2d_create", "hyena_plan2d_destroy", "hyena_spectrum2d_bytes", "hyena_workspace2d_bytes",
            "hyena_filter_spectrum2d", "hyena_conv2d_forward", "hyena_plan3d_create", "hyena_plan3d_destroy",
@@ -121,6 +121,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.hyena_operator_workspace_bytes.restype = sz
     lib.hyena_operator_forward.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hyena_operator_forward.restype = ci
+    lib.hyena_operator_tune.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hyena_operator_tune.restype = ci
     lib.hyena_operator_forward_timed.argtypes = [vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                                  ctypes.POINTER(ctypes.c_float)]
     lib.hyena_operator_forward_timed.restype = ci
@@ -488,6 +490,16 @@ class Plan:
                                                w_out.data_ptr(), b_out.data_ptr(), out.data_ptr(), ws.data_ptr(),
                                                ws.numel(), _stream_handle(self._torch, self.device)))
         return out
+
+    def operator_tune(self, x, w_in, b_in, short_w, spec, bias, w_out, b_out, out=None, workspace=None):
+        """hyena_operator_tune: times the projection GEMMs' candidate kernels on these
+        buffers and keeps the fastest for later calls (blocking; `out` is scratch)."""
+        B, out, ws = self._operator_args(x, w_in, b_in, short_w, spec, bias, w_out, b_out, out, workspace)
+        _check("hyena_operator_tune",
+               self.lib.hyena_operator_tune(self.handle, B, x.data_ptr(), w_in.data_ptr(), b_in.data_ptr(),
+                                            short_w.data_ptr(), spec.data_ptr(), bias.data_ptr(), w_out.data_ptr(),
+                                            b_out.data_ptr(), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                            _stream_handle(self._torch, self.device)))
 
     def operator_forward_timed(self, x, w_in, b_in, short_w, spec, bias, w_out, b_out, out, workspace=None):
         """hyena_operator_forward_timed: one synchronous call; returns milliseconds

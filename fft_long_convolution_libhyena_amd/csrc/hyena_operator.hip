@@ -1,19 +1,29 @@
 // The whole Hyena operator forward around the hot path (HyenaDNA walkthrough,
-// section 2.1, HyenaOperator.forward): the input projection, the (B, L, D) ->
-// (B, D, L) transpose, the hot path (hyena_forward), the transpose back and the
-// output projection. The two projections are plain dense GEMMs and run in
-// hipBLASLt (bf16 or fp32 operands, fp32 accumulation); the rearranges cost
-// nothing because both GEMMs read and write the layouts the path uses directly:
-//   in_proj : u_proj[b] (row-major [(N+1)D][L]) = W_in x[b]^T + b_in
-//             column-major view: U (L x C) = X^T (L x D) * W_in^T (D x C) + 1 b_in^T
-//   out_proj: out[b] (row-major [L][D])      = y[b]^T W_out^T + b_out
-//             column-major view: O (D x L) = W_out (D x D) * Y (D x L) + b_out 1^T
-// The output bias is hipBLASLt's bias epilogue (one value per row of O). The
-// input bias varies along the columns of U, where that epilogue does not apply,
-// so it enters as the C operand (beta = 1) of a bias matrix that a small kernel
-// fills once per call. Each sequence b is one ordinary (non-batched) GEMM call:
-// the weights and the bias matrix are shared by all b, and sharing them through
-// a batch stride of 0 is not a documented hipBLASLt mode.
+// section 2.1, the operator's forward pass): the input projection, the (B, L, D) ->
+// (B, D, L) transpose, the short conv and the hot path, the transpose back and the
+// output projection.
+//
+// bf16 plans (D a multiple of 64): the input projection runs in this library's
+// own matrix-core kernel (inproj.hip), one launch over every sequence, whose
+// epilogue adds b_in, applies the short conv along t to the fp32 sums and writes
+// the channels-first uc that the hot path reads; the path then runs with the
+// identity taps (0, 0, 1), which a fill kernel writes into the workspace.
+//
+// Otherwise (fp32 plans), the input projection is a hipBLASLt GEMM per sequence:
+//   column-major view: U (L x C) = X^T (L x D) * W_in^T (D x C) + 1 b_in^T
+// with the input bias (constant along the columns of U, where hipBLASLt's bias
+// epilogue does not apply) entering as the C operand (beta = 1) of a bias matrix
+// that a small kernel fills once per call; the path applies the short conv.
+//
+// The output projection is a hipBLASLt GEMM per sequence in both cases, with the
+// bias epilogue (one value per row):
+//   out[b] (row-major [L][D]) = y[b]^T W_out^T + b_out
+//   column-major view: O (D x L) = W_out (D x D) * Y (D x L) + b_out 1^T
+// Each sequence is one ordinary (non-batched) GEMM call: the weights are shared
+// by all b, and sharing them through a batch stride of 0 is not a documented
+// hipBLASLt mode. hipBLASLt's heuristic picks the kernel; hyena_operator_tune
+// times its candidates on the caller's buffers and keeps the fastest (a blocking
+// call made once, outside the forward, which never waits on the device).
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 #include <stdint.h>
@@ -23,6 +33,7 @@
 #include <vector>
 
 #include "../../include/hyena.h"
+#include "kernels.hpp"
 #include "plan.hpp"
 
 namespace {
@@ -30,6 +41,12 @@ namespace {
 constexpr size_t kLtWorkspace = 32u << 20;  // scratch offered to hipBLASLt
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// identity short-conv taps (0, 0, 1) for the C channels the path reads
+__global__ void k_identity_taps(float* __restrict__ w3, int64_t C) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < 3 * C) w3[i] = (i % 3 == 2) ? 1.f : 0.f;
+}
 
 template <class T>
 __global__ void k_bias_matrix(const T* __restrict__ b_in, T* __restrict__ cb, int64_t L, int64_t C) {
@@ -54,13 +71,12 @@ struct Gemm {
     }
 };
 
-// Per-plan operator state: the hipBLASLt handle and the descriptors of both GEMMs
-// (one sequence each). Built on first use, under the mutex; the first call also
-// times the heuristic's candidate kernels on its own buffers and keeps the fastest.
+// Per-plan operator state: the hipBLASLt handle and the descriptors of the GEMMs
+// it runs (one sequence each). Built on first use, under the mutex.
 struct OpState {
     std::mutex mu;
     hipblasLtHandle_t lt = nullptr;
-    bool built = false, tuned = false;
+    bool built = false;
     Gemm in, out;
     ~OpState() {
         in.release();
@@ -130,24 +146,32 @@ void tune(hipblasLtHandle_t lt, Gemm& g, const void* alpha, const void* A, const
 }
 
 // Descriptors of both GEMMs for one sequence (column-major views, see the file header).
+// bf16 plans whose width the matrix-core kernel tiles take the fused in_proj
+bool custom_inproj(const hyena_plan_s* plan) { return plan->dtype == HYENA_BF16 && hy::inproj_supported(plan->D); }
+
 bool build(OpState& s, const hyena_plan_s* plan) {
     s.in.release();
     s.out.release();
-    s.built = s.tuned = false;
+    s.built = false;
     const bool bf16 = plan->dtype == HYENA_BF16;
     const hipDataType dt = bf16 ? HIP_R_16BF : HIP_R_32F;
     const int64_t L = plan->L, D = plan->D, C = (int64_t)(plan->order + 1) * plan->D;
     const hipblasOperation_t T = HIPBLAS_OP_T, N = HIPBLAS_OP_N;
     // in_proj: U (L x C, ld L) = op_T(X: D x L, ld D) * W (D x C, ld D) + CB (L x C, ld L)
-    Gemm& g1 = s.in;
-    if (hipblasLtMatmulDescCreate(&g1.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) return false;
-    if (hipblasLtMatmulDescSetAttribute(g1.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &T, sizeof(T)) != HIPBLAS_STATUS_SUCCESS ||
-        hipblasLtMatmulDescSetAttribute(g1.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &N, sizeof(N)) != HIPBLAS_STATUS_SUCCESS)
-        return false;
-    if (!layout(&g1.a, dt, D, L, D) || !layout(&g1.b, dt, D, C, D) || !layout(&g1.c, dt, L, C, L) ||
-        !layout(&g1.d, dt, L, C, L))
-        return false;
-    if (!pick_algo(s.lt, g1)) return false;
+    if (!custom_inproj(plan)) {
+        Gemm& g1 = s.in;
+        if (hipblasLtMatmulDescCreate(&g1.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS)
+            return false;
+        if (hipblasLtMatmulDescSetAttribute(g1.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &T, sizeof(T)) !=
+                HIPBLAS_STATUS_SUCCESS ||
+            hipblasLtMatmulDescSetAttribute(g1.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &N, sizeof(N)) !=
+                HIPBLAS_STATUS_SUCCESS)
+            return false;
+        if (!layout(&g1.a, dt, D, L, D) || !layout(&g1.b, dt, D, C, D) || !layout(&g1.c, dt, L, C, L) ||
+            !layout(&g1.d, dt, L, C, L))
+            return false;
+        if (!pick_algo(s.lt, g1)) return false;
+    }
     // out_proj: O (D x L, ld D) = op_T(Wo: D x D, ld D) * op_T(Y: L x D, ld L) + b_out (bias epilogue, one
     //           value per row of O)
     Gemm& g2 = s.out;
@@ -174,7 +198,8 @@ bool build(OpState& s, const hyena_plan_s* plan) {
 struct Carve {
     void* u;
     void* y;
-    void* cb;
+    void* cb;    // broadcast input-bias matrix (hipBLASLt in_proj only)
+    void* taps;  // identity short-conv taps (fused in_proj only)
     void* lt;
     void* path;
     size_t path_bytes;
@@ -193,7 +218,13 @@ Carve carve(const hyena_plan_s* plan, int64_t B, void* base) {
     };
     c.u = take((size_t)B * C * L * s);
     c.y = take((size_t)B * D * L * s);
-    c.cb = take(L * C * s);
+    if (custom_inproj(plan)) {
+        c.cb = nullptr;
+        c.taps = take(C * 3 * sizeof(float));
+    } else {
+        c.cb = take(L * C * s);
+        c.taps = nullptr;
+    }
     c.lt = take(kLtWorkspace);
     c.path_bytes = hyena_workspace_bytes(const_cast<hyena_plan_s*>(plan), B);
     c.path = c.path_bytes ? take(c.path_bytes) : nullptr;
@@ -204,7 +235,7 @@ Carve carve(const hyena_plan_s* plan, int64_t B, void* base) {
 hyena_status_t operator_impl(hyena_plan_t plan, int64_t B, const void* x, const void* w_in, const void* b_in,
                              const float* short_w, const void* spec, const float* bias, const void* w_out,
                              const void* b_out, void* out, void* workspace, size_t workspace_bytes,
-                             hipStream_t stream, float* ms) {
+                             hipStream_t stream, float* ms, bool tune_only = false) {
     using hy::aligned16;
     if (!plan || B < 1 || !x || !w_in || !b_in || !short_w || !spec || !bias || !w_out || !b_out || !out)
         return HYENA_ERR_INVALID_ARG;
@@ -241,6 +272,14 @@ hyena_status_t operator_impl(hyena_plan_t plan, int64_t B, const void* x, const 
     const bool bf16 = plan->dtype == HYENA_BF16;
     const size_t es = bf16 ? 2 : 4;
     const int64_t L = plan->L, D = plan->D, C = (int64_t)(plan->order + 1) * plan->D;
+    if (tune_only) {
+        // time the hipBLASLt candidates on sequence 0's operands (outputs are scratch)
+        const float one = 1.f, zero = 0.f;
+        if (!custom_inproj(plan)) tune(s.lt, s.in, &one, x, w_in, &one, c.cb, c.u, c.lt, stream);
+        hipblasLtMatmulDescSetAttribute(s.out.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &b_out, sizeof(b_out));
+        tune(s.lt, s.out, &one, w_out, c.y, &zero, out, out, c.lt, stream);
+        return hipStreamSynchronize(stream) == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
+    }
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     if (ms) {
         for (auto& e : ev)
@@ -253,34 +292,39 @@ hyena_status_t operator_impl(hyena_plan_t plan, int64_t B, const void* x, const 
     }
     hyena_status_t st = HYENA_OK;
     const float one = 1.f, zero = 0.f;
-    // input projection, with b_in broadcast through the C operand
-    const int64_t n = L * C;
-    const unsigned grid = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-    if (bf16)
-        hipLaunchKernelGGL(k_bias_matrix<uint16_t>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)b_in,
-                           (uint16_t*)c.cb, L, C);
-    else
-        hipLaunchKernelGGL(k_bias_matrix<float>, dim3(grid), dim3(256), 0, stream, (const float*)b_in, (float*)c.cb,
-                           L, C);
-    if (hipGetLastError() != hipSuccess) st = HYENA_ERR_DEVICE;
-    if (st == HYENA_OK && !s.tuned) {
-        // first call on this plan: time the candidates on sequence 0's operands
-        tune(s.lt, s.in, &one, x, w_in, &one, c.cb, c.u, c.lt, stream);
-        hipblasLtMatmulDescSetAttribute(s.out.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &b_out, sizeof(b_out));
-        tune(s.lt, s.out, &one, w_out, c.y, &zero, out, out, c.lt, stream);
-        s.tuned = true;
-    }
-    for (int64_t b = 0; b < B && st == HYENA_OK; ++b) {
-        const char* xb = static_cast<const char*>(x) + (size_t)b * L * D * es;
-        char* ub = static_cast<char*>(c.u) + (size_t)b * C * L * es;
-        if (hipblasLtMatmul(s.lt, s.in.desc, &one, xb, s.in.a, w_in, s.in.b, &one, c.cb, s.in.c, ub, s.in.d,
-                            &s.in.algo, c.lt, kLtWorkspace, stream) != HIPBLAS_STATUS_SUCCESS)
+    const float* path_taps = short_w;
+    if (custom_inproj(plan)) {
+        // fused in_proj + b_in + short conv on the matrix cores; the path gets identity taps
+        hipLaunchKernelGGL(k_identity_taps, dim3((unsigned)((3 * C + 255) / 256)), dim3(256), 0, stream,
+                           (float*)c.taps, C);
+        if (hipGetLastError() != hipSuccess ||
+            hy::launch_inproj_conv3((const uint16_t*)x, (const uint16_t*)w_in, (const uint16_t*)b_in, short_w,
+                                    (uint16_t*)c.u, B, L, D, C, stream) != hipSuccess)
             st = HYENA_ERR_DEVICE;
+        path_taps = (const float*)c.taps;
+    } else {
+        // input projection, with b_in broadcast through the C operand
+        const int64_t n = L * C;
+        const unsigned grid = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+        if (bf16)
+            hipLaunchKernelGGL(k_bias_matrix<uint16_t>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)b_in,
+                               (uint16_t*)c.cb, L, C);
+        else
+            hipLaunchKernelGGL(k_bias_matrix<float>, dim3(grid), dim3(256), 0, stream, (const float*)b_in,
+                               (float*)c.cb, L, C);
+        if (hipGetLastError() != hipSuccess) st = HYENA_ERR_DEVICE;
+        for (int64_t b = 0; b < B && st == HYENA_OK; ++b) {
+            const char* xb = static_cast<const char*>(x) + (size_t)b * L * D * es;
+            char* ub = static_cast<char*>(c.u) + (size_t)b * C * L * es;
+            if (hipblasLtMatmul(s.lt, s.in.desc, &one, xb, s.in.a, w_in, s.in.b, &one, c.cb, s.in.c, ub, s.in.d,
+                                &s.in.algo, c.lt, kLtWorkspace, stream) != HIPBLAS_STATUS_SUCCESS)
+                st = HYENA_ERR_DEVICE;
+        }
     }
     if (ms) (void)hipEventRecord(ev[1], stream);
     // the hot path
     if (st == HYENA_OK)
-        st = hyena_forward(plan, B, c.u, short_w, spec, bias, c.y, c.path, c.path_bytes, stream);
+        st = hyena_forward(plan, B, c.u, path_taps, spec, bias, c.y, c.path, c.path_bytes, stream);
     if (ms) (void)hipEventRecord(ev[2], stream);
     // output projection with the bias epilogue
     if (st == HYENA_OK)
@@ -319,6 +363,14 @@ hyena_status_t hyena_operator_forward(hyena_plan_t plan, int64_t B, const void* 
                                       size_t workspace_bytes, hipStream_t stream) {
     return operator_impl(plan, B, x, w_in, b_in, short_w, spec, bias, w_out, b_out, out, workspace,
                          workspace_bytes, stream, nullptr);
+}
+
+hyena_status_t hyena_operator_tune(hyena_plan_t plan, int64_t B, const void* x, const void* w_in, const void* b_in,
+                                   const float* short_w, const void* spec, const float* bias, const void* w_out,
+                                   const void* b_out, void* out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    return operator_impl(plan, B, x, w_in, b_in, short_w, spec, bias, w_out, b_out, out, workspace,
+                         workspace_bytes, stream, nullptr, true);
 }
 
 hyena_status_t hyena_operator_forward_timed(hyena_plan_t plan, int64_t B, const void* x, const void* w_in,

@@ -133,4 +133,10 @@ int part_group(int P);  // output blocks per pass 2 workgroup
 
 int fs_row_units(int logL);
 
+// Fused input projection and short conv on the bf16 matrix cores (inproj.hip):
+// uc[b][c][t] = short_conv_c(x[b] w_in^T + b_in)[t] for C = (N+1)*D channels.
+bool inproj_supported(int64_t D);
+hipError_t launch_inproj_conv3(const uint16_t* x, const uint16_t* w, const uint16_t* b, const float* w3,
+                               uint16_t* u, int64_t B, int64_t L, int64_t D, int64_t C, hipStream_t st);
+
 }  // namespace hy

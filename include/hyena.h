@@ -358,9 +358,11 @@ hyena_status_t hyena_backward_per_sample(hyena_plan_t plan, int64_t B, const voi
                                          size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of workspace hyena_operator_forward needs for batch B: the in-projected
- * activation u_proj, the path output y, a broadcast input-bias matrix, 32 MiB of
- * GEMM scratch and the path's own workspace (hyena_workspace_bytes), each
- * 256-byte aligned. Returns 0 for a NULL plan or B < 1. */
+ * activation u_proj, the path output y, either the identity short-conv taps
+ * (bf16 plans with D a multiple of 64, whose input projection is fused with the
+ * short conv) or a broadcast input-bias matrix (other plans), 32 MiB of GEMM
+ * scratch and the path's own workspace (hyena_workspace_bytes), each 256-byte
+ * aligned. Returns 0 for a NULL plan or B < 1. */
 size_t hyena_operator_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* The whole operator forward around the hot path (HyenaDNA walkthrough, section
@@ -374,11 +376,17 @@ size_t hyena_operator_workspace_bytes(hyena_plan_t plan, int64_t B);
  *   short_w, spec, bias: as in hyena_forward
  *   out   [B][L][D] of the plan dtype, device (output)
  *   workspace: at least hyena_operator_workspace_bytes(plan, B) bytes.
- * The projections are plain dense GEMMs run by hipBLASLt (fp32 accumulation; with
- * bf16 plans u_proj is rounded to bf16 between the GEMM and the path, as a bf16
- * module would), one GEMM call per sequence. The first call on a plan attaches
- * the GEMM state to it (a hipBLASLt handle and descriptors), so calls on one plan
- * are serialised internally; hyena_plan_destroy releases it.
+ * bf16 plans with D a multiple of 64: the input projection runs in libhyena's own
+ * bf16 matrix-core kernel, one launch over every sequence, fused with b_in and
+ * the short conv (applied to the fp32 sums, then rounded once to bf16); the path
+ * then runs with identity taps. Other plans: the input projection is a hipBLASLt
+ * GEMM per sequence (u_proj rounded to the plan dtype) and the path applies the
+ * short conv. The output projection is a hipBLASLt GEMM per sequence (fp32
+ * accumulation). hipBLASLt's heuristic choice of kernel is used unless
+ * hyena_operator_tune has run on the plan. The first call on a plan attaches the
+ * GEMM state to it (a hipBLASLt handle and descriptors), so calls on one plan are
+ * serialised internally; hyena_plan_destroy releases it. The call never waits on
+ * the device.
  * Enqueued on `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL or misaligned
  * pointers, B < 1, sizes too large), HYENA_ERR_WORKSPACE, HYENA_ERR_UNSUPPORTED
  * (no GEMM kernel for these shapes), HYENA_ERR_DEVICE, and those of
@@ -388,9 +396,20 @@ hyena_status_t hyena_operator_forward(hyena_plan_t plan, int64_t B, const void* 
                                       const void* w_out, const void* b_out, void* out, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream);
 
+/* Times hipBLASLt's candidate kernels for this plan's projection GEMMs on the
+ * given buffers (a few calls each) and keeps the fastest for later calls on the
+ * plan. Same arguments and errors as hyena_operator_forward; it overwrites `out`
+ * and the workspace with scratch values and returns after the stream has finished
+ * (a blocking call, made once before timing-sensitive use). */
+hyena_status_t hyena_operator_tune(hyena_plan_t plan, int64_t B, const void* x, const void* w_in, const void* b_in,
+                                   const float* short_w, const void* spec, const float* bias, const void* w_out,
+                                   const void* b_out, void* out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 /* hyena_operator_forward with timing: HIP events around the three stages on
  * `stream`; waits for the last one and writes milliseconds into ms[4]:
- * ms[0] input projection (with the bias fill), ms[1] the hot path, ms[2] output
+ * ms[0] input projection (with the bias or tap fill; the short conv as well on the
+ * fused bf16 path), ms[1] the hot path, ms[2] output
  * projection, ms[3] total. HYENA_ERR_INVALID_ARG also for ms == NULL. */
 hyena_status_t hyena_operator_forward_timed(hyena_plan_t plan, int64_t B, const void* x, const void* w_in,
                                             const void* b_in, const float* short_w, const void* spec,

@@ -43,7 +43,7 @@ def _run(args):
     # full workloads in the launch configuration the benchmark times, checked on sampled outputs
     (["--circular"], "long64k"), (["--circular"], "lm125m"), (["--path", "partitioned"], "long64k"),
     (["--operator"], "lm125m"), (["--per-sample"], "long64k"), (["--backward", "--per-sample"], "lm125m"),
-    ([], "long64k"), ([], "long64k_o3"), ([], "lm125m")])
+    ([], "long64k"), ([], "long64k_o3"), ([], "lm125m"), (["--synthesis"], "lm125m")])
 def test_bench_line(mode, workload):
     args = mode + COMMON + (["--workload", workload] if workload else [])
     out = _run(args)

@@ -54,6 +54,10 @@ CASES = [
     (2, 32, 2048, 2, "bf16", "auto"),
     (1, 16, 32768, 2, "f32", "auto"),
     (1, 64, 8192, 4, "bf16", "auto"),
+    # bf16 with D a multiple of 64: the fused matrix-core in_proj + short conv
+    (3, 64, 1024, 2, "bf16", "auto"),      # five 254-step tiles per sequence, the last one partial
+    (2, 320, 512, 3, "bf16", "auto"),      # C = 1280: five full channel tiles
+    (1, 192, 65536, 2, "bf16", "auto"),    # C = 576: a partial channel tile; four-step path
 ]
 
 
@@ -104,3 +108,42 @@ def test_operator_reuses_state_across_batch_sizes():
                                         f(p.w_out), f(p.b_out))
             ref = oracle.operator_forward(p.x[:B], p.w_in, p.b_in, x.short_w, x.h, x.bias, p.w_out, p.b_out, 2)
             assert oracle.rel_l2(out.cpu().numpy(), ref) <= 1e-4
+
+
+def test_operator_fused_inproj_every_time_step():
+    """Per time step over all sequences and channels: the fused in_proj writes tiles of
+    254 steps that each recompute two steps of history, so a wrong seam would show
+    in single time steps that a global norm hides."""
+    wl = synth.custom(2, 128, 2048, 2, "bf16", seed=5)
+    x, p, got, used, _ = _run(wl)
+    ref = oracle.operator_forward(p.x, p.w_in, p.b_in, x.short_w, x.h, x.bias, p.w_out, p.b_out, 2)
+    per_t = np.linalg.norm(got - ref, axis=(0, 2)) / np.linalg.norm(ref, axis=(0, 2))
+    say(f"[operator] fused in_proj: worst time step rel_l2 {per_t.max():.3e} at t={int(per_t.argmax())}")
+    assert per_t.max() <= 2e-2
+    assert oracle.rel_l2(got, ref) <= 1e-2
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 16)])
+def test_operator_tune_keeps_results(dtype, D):
+    """hyena_operator_tune picks among hipBLASLt's candidates; the results stay within
+    the parity bound afterwards."""
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan
+
+    wl = synth.custom(2, D, 1024, 2, dtype, seed=9)
+    x = synth.generate(wl)
+    p = synth.operator_params(wl)
+    io = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dv = lambda a, dt=io: torch.from_numpy(a).cuda().to(dt).contiguous()  # noqa: E731
+    with Plan(wl.L, wl.D, 2, dtype) as plan:
+        spec = plan.spectrum(dv(x.h, torch.float32))
+        args = (dv(p.x), dv(p.w_in), dv(p.b_in), dv(x.short_w, torch.float32), spec, dv(x.bias, torch.float32),
+                dv(p.w_out), dv(p.b_out))
+        plan.operator_tune(*args)
+        out = plan.operator_forward(*args)
+        torch.cuda.synchronize()
+    ref = oracle.operator_forward(p.x, p.w_in, p.b_in, x.short_w, x.h, x.bias, p.w_out, p.b_out, 2)
+    err = oracle.rel_l2(out.float().cpu().numpy().astype(np.float64), ref)
+    say(f"[operator] after tuning ({dtype}): rel_l2={err:.3e}")
+    assert err <= (1e-2 if dtype == "bf16" else 1e-4)
