@@ -181,10 +181,16 @@ KERNEL_SOURCES = {
     "conv3d": ["fft_core.hpp", "pair.hpp", "fourstep.hpp", "kernels.hpp", "plan.hpp", "tables.hpp", "conv_nd.hpp",
                "conv3d.hip"],
     "partitioned": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "partitioned.hip", "hyena_api.hip"],
+    "operator": ["kernels.hpp", "inproj.hip", "hyena_operator.hip"],
+    "synthesis": ["plan.hpp", "kernel_synthesis.hip"],
 }
 
 
 def kernel_family(kernel: str) -> str:
+    if kernel.startswith("k_inproj"):
+        return "operator"
+    if kernel.startswith("k_kernel_synthesis"):
+        return "synthesis"
     if kernel.startswith("k_implicit_filter"):
         return "filter"
     if kernel.startswith("k_c3"):
@@ -968,7 +974,7 @@ def _csv_rows(d: str, suffix: str):
 
 def _short_name(name: str) -> str:
     """'void hy::k_fs_row<8, 8, 0>(...)' -> 'k_fs_row<8, 8, 0>'."""
-    n = name.split("(")[0].replace("void ", "").strip()
+    n = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
     return n.split("hy::")[-1]
 
 
