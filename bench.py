@@ -371,7 +371,8 @@ def bench_backward(args, wl, x, torch, Plan, per_sample=False):
         # four-step path) against its algorithmic bytes
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(bk, wl.name + ("_per_sample" if per_sample else "")),
+                     # the whole step's HBM bytes (every launch of one backward step)
+                     "traffic": measured_step_traffic(bk, wl.name + ("_per_sample" if per_sample else "")),
                      "kernel": bk,
                      "alg_bytes_per_launch": nbytes, "launch_ms": round(ms, 5), "launches_per_step": 1},
     }
@@ -991,6 +992,16 @@ def _is_forward_kernel(short: str) -> bool:
     return False
 
 
+def _is_backward_kernel(short: str) -> bool:
+    """Kernels one backward launches (the forward recompute's column pass included)."""
+    base, _, targs = short.partition("<")
+    a = [t.strip() for t in targs.rstrip(">").split(",")] if targs else []
+    if base == "k_fs_colfwd":
+        return len(a) > 3 and a[3] == "0"
+    return base.startswith(("k_fs_row_bwd", "k_fs_colinv_bwd", "k_fs_dh_col", "k_fs_bwd_", "k_fs_dbias",
+                            "k_lds_bwd"))
+
+
 def _calibration():
     kv = {}
     with open(os.path.join(ROOT, "profiles", "copy_calibration_1GiB.txt")) as fh:
@@ -1019,11 +1030,15 @@ def summarize_pmc(args):
             e[key].append(float(r["Counter_Value"]))
     F = args.forwards
     kern = args.kernel
-    dom = [k for k in per if k.split("<")[0] == kern]
+    # a family name (k_fs_passes, k_part_passes; fs_backward) stands for every kernel of
+    # the forward (of the backward)
+    family = kern in ("k_fs_passes", "k_part_passes", "fs_backward")
+    member = _is_backward_kernel if kern == "fs_backward" else _is_forward_kernel
+    dom = [k for k in per if (member(k) if family else k.split("<")[0] == kern)]
     if not dom:
         raise SystemExit(f"kernel {kern} not in the counters: {sorted(per)}")
     wl = synth.WORKLOADS[args.workload]
-    alg = alg_bytes_forward(wl)
+    alg = alg_bytes_backward(wl) if kern == "fs_backward" else alg_bytes_forward(wl)
     step = 0.0
     lines = []
     for k in sorted(per, key=lambda k: -sum(per[k]["fetch"])):
@@ -1031,22 +1046,23 @@ def summarize_pmc(args):
         fb = sum(e["fetch"]) * 1024 * fs
         wb = sum(e["write"]) * 1024 * ws
         n = max(len(e["fetch"]), len(e["write"]))
-        fwd = _is_forward_kernel(k)
+        fwd = member(k)
         if fwd:
             step += (fb + wb) / F
         lines.append(f"#   {k}: dispatches {n}, fetch {fb / max(n, 1):.0f}, write {wb / max(n, 1):.0f} bytes per dispatch"
-                     + ("" if fwd else " (not part of the forward)"))
-    d0 = dom[0]
-    e = per[d0]
-    nd = max(len(e["fetch"]), len(e["write"]))
-    fk = sum(e["fetch"]) / len(e["fetch"])
-    wk = sum(e["write"]) / len(e["write"])
+                     + ("" if fwd else " (not part of the step)"))
+    d0 = dom[0] if not family else ", ".join(sorted(dom))
+    fe_all = [v for k in dom for v in per[k]["fetch"]]
+    wr_all = [v for k in dom for v in per[k]["write"]]
+    nd = max(len(fe_all), len(wr_all))
+    fk = sum(fe_all) / len(fe_all)
+    wk = sum(wr_all) / len(wr_all)
     cmd = args.command or ""
     out = [f"# rocprofv3 HBM byte counters per dispatch: {kern} on {wl.name} ({wl.describe()})",
            "# commands (from the repository root):"]
     out += [f"#   {c.strip()}" for c in cmd.split(";;") if c.strip()]
-    out += ["# scaled with the factors of copy_calibration_1GiB.txt; the forward's kernels summed over "
-            f"{F} forwards give step_bytes",
+    out += ["# scaled with the factors of copy_calibration_1GiB.txt; the kernels of one step (forward or backward) summed over "
+            f"{F} steps give step_bytes",
             f"kernel: {kern}", f"instance: {d0}", f"workload: {wl.name}",
             f"sources_sha256: {kernel_sources_hash(kern)}", f"dispatches: {nd}",
             f"fetch_size_kib_per_dispatch: {fk:.1f}", f"write_size_kib_per_dispatch: {wk:.1f}",
@@ -1054,6 +1070,42 @@ def summarize_pmc(args):
             f"fetch_bytes_per_dispatch: {fk * 1024 * fs:.0f}", f"write_bytes_per_dispatch: {wk * 1024 * ws:.0f}",
             f"step_bytes: {step:.0f}", f"alg_bytes_per_step: {alg}", f"step_traffic_over_alg: {step / alg:.3f}",
             "# every kernel of the run (scaled bytes per dispatch):"] + lines
+    print("\n".join(out))
+
+
+def summarize_sq(args):
+    """Instruction-counter summary (profiles/sq_<kernel>_<workload>.txt) from one
+    rocprofv3 --pmc run of `bench.py --profile-forwards F` with SQ counters: every
+    counter of the forward's kernels summed over the run, per forward and per
+    channel-token (b, d, t) point. SQ_INSTS_* count wave instructions (64 lanes)."""
+    from fft_long_convolution_libhyena_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    tot = {}
+    disp = {}
+    for r in _csv_rows(args.summarize_sq, "counter_collection.csv"):
+        k = _short_name(r["Kernel_Name"])
+        if not _is_forward_kernel(k):
+            continue
+        tot[r["Counter_Name"]] = tot.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        disp[k] = disp.get(k, 0) + 1
+    F = args.forwards
+    pts = wl.B * wl.D * wl.L
+    cmd = args.command or ""
+    out = [f"# rocprofv3 SQ counters: {args.kernel} on {wl.name} ({wl.describe()})",
+           "# command (from the repository root):"]
+    out += [f"#   {c.strip()}" for c in cmd.split(";;") if c.strip()]
+    out += [f"# kernel sources sha256[:16]: {kernel_sources_hash(args.kernel)}",
+            f"# forward kernels and counter rows: {dict(sorted(disp.items()))}; {F} forwards; "
+            f"{pts} channel-token points per forward",
+            "# wave instructions (64 lanes each) per forward, and lane instructions per point (x 64 / points)",
+            f"{'counter':28s} {'per_forward':>16s} {'lane_instr_per_point':>22s}"]
+    for name in sorted(tot):
+        pf = tot[name] / F
+        per = pf * 64 / pts if name.startswith("SQ_INSTS") else float("nan")
+        out.append(f"{name:28s} {pf:16.0f} {per:22.2f}")
+    if args.note:
+        out.append(f"# {args.note}")
     print("\n".join(out))
 
 
@@ -1136,6 +1188,8 @@ def main():
                     help="run plan, spectrum and exactly this many forwards, then exit (for counter runs)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print a counter summary from rocprofv3 FETCH_SIZE and WRITE_SIZE csv output")
+    ap.add_argument("--summarize-sq", metavar="DIR",
+                    help="print an instruction-counter summary from rocprofv3 SQ counter csv output")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print a kernel-trace summary from rocprofv3 --kernel-trace --stats csv output")
     ap.add_argument("--kernel", default="k_fs_pipe", help="kernel a summary is about")
@@ -1149,6 +1203,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.summarize_sq:
+        summarize_sq(args)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -1284,7 +1341,7 @@ def main():
             design = lambda f: alg_bytes_pass(wl, f)  # noqa: E731
         nch = math.ceil(rows / chunk)
         launches = nch * sum(nper.values())
-        kernel = "+".join(fams.values())
+        kernel = "k_part_passes" if plan.path == "partitioned" else "k_fs_passes"  # every launch of the forward
         kms = sum(fam_ms[f] for f in fams) / launches
         fam = max(fams, key=lambda k: fam_ms[k])
         dl = nch * nper[fam]
@@ -1297,6 +1354,7 @@ def main():
     roof = roofline(kernel, launches, kms, fwd_bytes / launches, fwd_flops / launches, per_launch, step_traffic,
                     fwd_bytes)
     if dominant:
+        roof["kernels"] = list(fams.values())
         roof["dominant_kernel"] = dominant
 
     out = {

@@ -73,7 +73,7 @@ def test_kernel_families_cover_the_summaries():
     """Every committed counter summary names a kernel whose family lists real sources."""
     for f in os.listdir(os.path.join(ROOT, "profiles")):
         if f.startswith("pmc_"):
-            kernel = next(k for k in ("k_fs_pipe", "k_fs_row", "k_lds_forward", "k_lds_bwd_rows", "fs_backward",
+            kernel = next(k for k in ("k_fs_pipe", "k_fs_passes", "k_part_passes", "k_fs_row", "k_lds_forward", "k_lds_bwd_rows", "fs_backward",
                                       "k_implicit_filter", "k_part_inv", "k_c2_conv2d", "k_c3_conv3d")
                           if f[4:].startswith(k))
             for src in bench.KERNEL_SOURCES[bench.kernel_family(kernel)]:
