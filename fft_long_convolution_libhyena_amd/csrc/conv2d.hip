@@ -133,9 +133,8 @@ hyena_status_t hyena_plan2d_create_ex(hyena_plan2d_t* out, int64_t H, int64_t W,
         return HYENA_ERR_UNSUPPORTED;
     const int64_t Wr = int64_t(1) << lr;  // packed row transform length
     std::vector<float2> tab;
-    hy::append_stockham(tab, lc + 1);
-    const size_t o_tw2 = tab.size();
-    hy::append_stockham(tab, lr);
+    const size_t o_tw1 = hy::append_stockham(tab, lc + 1);
+    const size_t o_tw2 = hy::append_stockham(tab, lr);
     const size_t o_wp = tab.size();
     for (int64_t k = 0; k < Wr; ++k) tab.push_back(hy::wfwd(k, 2 * Wr));
     int dev = -1;
@@ -163,7 +162,7 @@ hyena_status_t hyena_plan2d_create_ex(hyena_plan2d_t* out, int64_t H, int64_t W,
     plan->dtype = dtype;
     plan->device = dev;
     plan->dtab = dtab;
-    plan->tw1 = dtab;
+    plan->tw1 = dtab + o_tw1;
     plan->tw2 = dtab + o_tw2;
     plan->wpair = dtab + o_wp;
     *out = plan;

@@ -148,11 +148,9 @@ hyena_status_t hyena_plan3d_create_ex(hyena_plan3d_t* out, int64_t A, int64_t H,
         return HYENA_ERR_UNSUPPORTED;
     const int64_t Wr = int64_t(1) << lr;  // packed row transform length
     std::vector<float2> tab;
-    hy::append_stockham(tab, la + 1);
-    const size_t o_twh = tab.size();
-    hy::append_stockham(tab, lh);
-    const size_t o_tww = tab.size();
-    hy::append_stockham(tab, lr);
+    const size_t o_twa = hy::append_stockham(tab, la + 1);
+    const size_t o_twh = hy::append_stockham(tab, lh);
+    const size_t o_tww = hy::append_stockham(tab, lr);
     const size_t o_wp = tab.size();
     for (int64_t k = 0; k < Wr; ++k) tab.push_back(hy::wfwd(k, 2 * Wr));
     int dev = -1;
@@ -184,7 +182,7 @@ hyena_status_t hyena_plan3d_create_ex(hyena_plan3d_t* out, int64_t A, int64_t H,
     plan->dtype = dtype;
     plan->device = dev;
     plan->dtab = dtab;
-    plan->twa = dtab;
+    plan->twa = dtab + o_twa;
     plan->twh = dtab + o_twh;
     plan->tww = dtab + o_tww;
     plan->wpair = dtab + o_wp;

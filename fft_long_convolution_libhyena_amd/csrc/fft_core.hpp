@@ -15,7 +15,8 @@
 // except a final 2/4/8 pass when s is not a multiple of 4.
 //
 // Twiddles come from tables built on the host in fp64 and rounded once to fp32
-// (per pass: W_{NS*R}^{r*k} at [(r-1)*NS + k]); inverse transforms use their
+// (pass 0 needs none; pass p >= 1 holds W_{NS*R}^{r*k} at [(r-1)*NS + k], so the
+// lanes of a wave read consecutive values); inverse transforms use their
 // conjugates. The in-register DFT constants are fp32 roundings of cos/sin of
 // multiples of pi/8. No fast sin/cos intrinsics are used anywhere.
 #pragma once
@@ -25,6 +26,29 @@
 #include <utility>
 
 namespace hy {
+
+// Raw buffer access to read-only tables: a resource descriptor built from a
+// uniform base (gfx9 layout: no stride, byte-sized records, 32-bit data format),
+// a per-lane byte offset and a scalar byte offset.
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+__device__ __forceinline__ BufRsrc buf_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ float2 buf_load_f2(BufRsrc rs, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)voff, (int)soff, 0));
+}
+
+// Element i of an array at a workgroup-uniform base, addressed by a 32-bit byte
+// offset (i * sizeof(T) below 2^32): the access then takes the scalar base plus a
+// per-lane 32-bit offset, with no 64-bit address arithmetic per lane.
+template <class T>
+__device__ __forceinline__ const T& ld32(const T* __restrict__ base, uint32_t i) {
+    return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + i * (uint32_t)sizeof(T));
+}
+template <class T>
+__device__ __forceinline__ T& st32(T* __restrict__ base, uint32_t i) {
+    return *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + i * (uint32_t)sizeof(T));
+}
 
 __device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
 __device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
@@ -171,7 +195,7 @@ struct Sched {
     // offset of pass p's twiddles inside this size's table
     static constexpr int twoff(int p) {
         int off = 0;
-        for (int i = 0; i < p; ++i) off += (radix(i) - 1) * ns(i);
+        for (int i = 1; i < p; ++i) off += (radix(i) - 1) * ns(i);
         return off;
     }
     static constexpr int twsize() { return twoff(NPASS); }
@@ -250,9 +274,13 @@ __device__ __forceinline__ void fft_pass(float2 (&v)[E], int t, const float2* __
 #pragma unroll
         for (int r = 0; r < R; ++r) a[r] = v[q + r * Q];
         if constexpr (NS > 1) {
-            const uint32_t tk = S::twoff(P) + k;
+            // buffer loads: one per-lane offset for all R - 1 twiddles, the row of
+            // each r a scalar offset (no per-lane 64-bit addresses)
+            const BufRsrc rs = buf_rsrc(tw);
+            const uint32_t vo = k * 8u;
 #pragma unroll
-            for (int r = 1; r < R; ++r) a[r] = twmul<INV>(a[r], tw[tk + (r - 1) * NS]);
+            for (int r = 1; r < R; ++r)
+                a[r] = twmul<INV>(a[r], buf_load_f2(rs, vo, (uint32_t)(S::twoff(P) + (r - 1) * NS) * 8u));
         }
         if constexpr (HALF_IN && P == 0 && R == 16)
             dft16<INV, true>(a);  // a[8..15] are the zero padding
@@ -307,16 +335,17 @@ __device__ __forceinline__ float2 load_pair(const uint16_t* __restrict__ row, ui
     uint32_t bits = reinterpret_cast<const uint32_t*>(row)[m];
     return make_float2(__uint_as_float(bits << 16), __uint_as_float(bits & 0xffff0000u));
 }
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // quiet NaN
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Two floats to packed bf16 (lo in bits 0..15), rounded to nearest even by the
+// hardware conversion; a NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 __device__ __forceinline__ void store_pair(float* __restrict__ row, uint32_t m, float2 v) {
     reinterpret_cast<float2*>(row)[m] = v;
 }
 __device__ __forceinline__ void store_pair(uint16_t* __restrict__ row, uint32_t m, float2 v) {
-    reinterpret_cast<uint32_t*>(row)[m] = f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16);
+    reinterpret_cast<uint32_t*>(row)[m] = pack_bf16x2(v.x, v.y);
 }
 
 // A pair of samples as stored (fp32 pair or two packed bf16), for fetching ahead

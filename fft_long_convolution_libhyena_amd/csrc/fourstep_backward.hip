@@ -209,8 +209,7 @@ __device__ __forceinline__ void store_quad(float* __restrict__ row, int64_t q, f
     reinterpret_cast<float4*>(row)[q] = v;
 }
 __device__ __forceinline__ void store_quad(uint16_t* __restrict__ row, int64_t q, float4 v) {
-    reinterpret_cast<uint2*>(row)[q] = make_uint2(f32_to_bf16_rne(v.x) | (f32_to_bf16_rne(v.y) << 16),
-                                                  f32_to_bf16_rne(v.z) | (f32_to_bf16_rne(v.w) << 16));
+    reinterpret_cast<uint2*>(row)[q] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
 }
 
 template <class TIO>

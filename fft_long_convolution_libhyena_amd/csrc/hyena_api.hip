@@ -120,17 +120,14 @@ hyena_status_t hyena_plan_create_ex(hyena_plan_t* out, int64_t L, int64_t D, int
         // the partitioned path transforms 2Q-sample windows: the LDS tables for length Q
         const int lt = p == HYENA_PATH_LDS ? logT : hy::kPartLogQ;
         const int64_t Tl = int64_t(1) << lt;
-        o_tw = tab.size();
-        append_stockham(tab, lt);
+        o_tw = append_stockham(tab, lt);
         o_wpair = tab.size();
         for (int64_t k = 0; k <= Tl / 2; ++k) tab.push_back(wfwd(k, 2 * Tl));
     } else {
         hy::fs_split(logT, &log1, &log2);
         const int64_t L1 = int64_t(1) << log1, L2 = int64_t(1) << log2;
-        o_tw1 = tab.size();
-        append_stockham(tab, log1);
-        o_tw2 = tab.size();
-        append_stockham(tab, log2);
+        o_tw1 = append_stockham(tab, log1);
+        o_tw2 = append_stockham(tab, log2);
         // the four-step twiddle W_L^(k1*m2) with k1 = t + T1*e is the product of
         // W_L^(t*m2) and W_L^(T1*e*m2): two small tables, both read with m2 fastest
         const int64_t T1 = L1 / 16;

@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fft_core.hpp"
 #include "kernels.hpp"
 
 namespace hy {
@@ -54,11 +55,6 @@ static_assert(kRoundCols * kEP * 4 + kRoundCols * 16 <= kLdsBytes,
               "one epilogue round and its column parameters fit the staging buffers");
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-// two floats to packed bf16, round to nearest even (the hardware conversion)
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
 
 struct Inproj {
     const uint16_t* x;   // [B*L][D]
@@ -203,8 +199,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_inproj_conv3(Inproj a) {
             const float o2 = fmaf(w0, u4, fmaf(w1, u5, w2 * u6));
             const float o3 = fmaf(w0, u5, fmaf(w1, u6, w2 * u7));
             if (lane < kTO / 4 && t < a.L)  // L is a multiple of 4: all four times are in range
-                *reinterpret_cast<uint2*>(a.u + (seq * a.C + c) * a.L + t) = make_uint2(pack_bf16(o0, o1),
-                                                                                         pack_bf16(o2, o3));
+                *reinterpret_cast<uint2*>(a.u + (seq * a.C + c) * a.L + t) = make_uint2(pack_bf16x2(o0, o1),
+                                                                                         pack_bf16x2(o2, o3));
         }
     }
 }

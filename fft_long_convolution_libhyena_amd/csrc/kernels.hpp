@@ -36,6 +36,13 @@ struct LdsCfg {
     static constexpr int L = 1 << LOGL;
     static constexpr int E = LOGL >= HY_LDS_E32_FROM ? 32 : 16;
     static constexpr int THREADS = L / E;
+    // waves per SIMD when as many workgroups share a CU as its 160 KB of LDS
+    // allows (one padded transform each), capped at 8: the register budget asked
+    // of the compiler is the one that keeps them all resident
+    static constexpr int LDS_BYTES = (L + L / 16) * 8;
+    static constexpr int BLOCKS = (160 * 1024) / LDS_BYTES;
+    static constexpr int WAVES_RAW = BLOCKS * (THREADS / 64) / 4;
+    static constexpr int MIN_WAVES = WAVES_RAW < 1 ? 1 : (WAVES_RAW > 8 ? 8 : WAVES_RAW);
 };
 constexpr int kLdsMinLog = 4;   // L = 16: one thread per 16 values
 constexpr int kLdsMaxLog = 14;  // L = 16384: 139,264 bytes of LDS

@@ -47,8 +47,11 @@ namespace hy {
 // CIRC: circular convolution of sequences of 2L samples (the HyenaND summary's
 // circular boundary mode): the same L-point packed transform with every slot
 // holding data (no zero-padded half, no pruned first pass) and every output kept.
+// At order 2 the register budget is the one that keeps every workgroup the LDS
+// allows resident (it fits without spills); higher orders keep more state live
+// across the step loop and get the compiler's default.
 template <int LOGL, int N, class TIO, bool CIRC = false>
-__global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS)
+__global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS, N == 2 ? LdsCfg<LOGL>::MIN_WAVES : 1)
 k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const float2* __restrict__ spec,
               const float* __restrict__ bias, TIO* __restrict__ y, const float2* __restrict__ tw,
               const float2* __restrict__ wpair, int B, int D, int64_t sbs) {
@@ -95,8 +98,8 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
 #pragma unroll
             for (int e = 0; e < H; ++e) {
                 const uint32_t k = t + T * e;
-                hk[e] = Hs[k];
-                hm[e] = Hs[k == 0 ? 0u : (uint32_t)L - k];
+                hk[e] = ld32(Hs, k);
+                hm[e] = ld32(Hs, k == 0 ? 0u : (uint32_t)L - k);
             }
         }
         fft_strided<L, false, !CIRC>(v, t, tw, acc);
@@ -109,8 +112,8 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
             const uint32_t k = t + T * e;  // k in [0, L/2)
             const uint32_t km = k == 0 ? 0 : L - k;
             if constexpr (!HY_LDS_PREFETCH) {
-                hk[e] = Hs[k];
-                hm[e] = Hs[km];
+                hk[e] = ld32(Hs, k);
+                hm[e] = ld32(Hs, km);
             }
             float2 Hk, Hm;
             if (k == 0) {
@@ -121,7 +124,7 @@ k_lds_forward(const TIO* __restrict__ u, const float* __restrict__ w3, const flo
                 Hm = hadd(hm[e], bs);
             }
             float2 Yk, Ym;
-            pair_conv(acc[k], acc[km], Hk, Hm, wpair[k], Yk, Ym);
+            pair_conv(acc[k], acc[km], Hk, Hm, ld32(wpair, k), Yk, Ym);
             acc[k] = Yk;
             if (k != 0) acc[km] = Ym;
         }

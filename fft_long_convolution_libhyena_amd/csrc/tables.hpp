@@ -20,18 +20,22 @@ inline float2 wfwd(int64_t num, int64_t den) {
 }
 
 // Stockham per-pass tables for a length-n transform, in the order the device
-// schedule reads them: pass p (radix R, NS = 16^p) holds W_{NS*R}^{r*k} at
-// [(r-1)*NS + k], r = 1..R-1, k = 0..NS-1.
-inline void append_stockham(std::vector<float2>& out, int logn) {
+// schedule reads them: pass 0 (NS = 1) needs none; pass p >= 1 (radix R,
+// NS = 16^p) holds W_{NS*R}^{r*k} at [(r-1)*NS + k], r = 1..R-1, k = 0..NS-1.
+// Returns the index at which the table starts.
+inline size_t append_stockham(std::vector<float2>& out, int logn) {
+    const size_t start = out.size();
     const int full = logn / 4, rem = logn % 4;
     const int npass = full + (rem ? 1 : 0);
     int64_t ns = 1;
     for (int p = 0; p < npass; ++p) {
         const int R = p < full ? 16 : (1 << rem);
-        for (int r = 1; r < R; ++r)
-            for (int64_t k = 0; k < ns; ++k) out.push_back(wfwd((int64_t)r * k, ns * R));
+        if (p > 0)
+            for (int r = 1; r < R; ++r)
+                for (int64_t k = 0; k < ns; ++k) out.push_back(wfwd((int64_t)r * k, ns * R));
         ns *= R;
     }
+    return start;
 }
 
 }  // namespace hy
