@@ -45,10 +45,6 @@ template <class T>
 __device__ __forceinline__ const T& ld32(const T* __restrict__ base, uint32_t i) {
     return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + i * (uint32_t)sizeof(T));
 }
-template <class T>
-__device__ __forceinline__ T& st32(T* __restrict__ base, uint32_t i) {
-    return *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + i * (uint32_t)sizeof(T));
-}
 
 __device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
 __device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }

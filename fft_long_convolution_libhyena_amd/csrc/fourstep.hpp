@@ -192,27 +192,29 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
     lds_store_strided<T2>(racc, t, v);
     __syncthreads();
 
-    const RowAcc au[2] = {RowAcc{lds + (2 * unit) * RP}, RowAcc{lds + (2 * unit + 1) * RP}};
+    // row ri (0 or 1) of this thread's unit, computed rather than taken from an array,
+    // so that a run-time ri leaves a plain LDS address (no private array)
+    auto au = [&](int ri) { return RowAcc{lds + (2 * unit + ri) * RP}; };
     const float sc = 1.0f / (8.0f * (float)L);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const PairSlot ps = pair_slot<L1, L2>(p, tp + 2 * T2 * e, tb);
-        const float2 Za = au[ps.ra][ps.ia];
-        const float2 Zb = au[ps.rb][ps.ib];
+        const float2 Za = au(ps.ra)[ps.ia];
+        const float2 Zb = au(ps.rb)[ps.ib];
         if constexpr (MODE == 0) {
             float2 Yk, Ym;
             if (ps.kind == 0) {
                 pair_conv(Za, Zb, hadd(ha[e], bs), hadd(hb[e], bs), ps.w, Yk, Ym);
-                au[ps.ra][ps.ia] = Yk;
-                au[ps.rb][ps.ib] = Ym;
+                au(ps.ra)[ps.ia] = Yk;
+                au(ps.rb)[ps.ib] = Ym;
             } else {
                 // bin 0 pairs with bin L (spectrum slot 0 holds (H[0], H[L]))
                 pair_conv(Za, Za, make_float2(ha[e].x + bs, 0.f), make_float2(ha[e].y + bs, 0.f),
                           make_float2(1.f, 0.f), Yk, Ym);
-                au[ps.ra][ps.ia] = Yk;
+                au(ps.ra)[ps.ia] = Yk;
                 const float2 Hh = hadd(hb[e], bs);  // bin L/2 pairs with itself
                 pair_conv(Zb, Zb, Hh, Hh, ps.w, Yk, Ym);
-                au[ps.rb][ps.ib] = Yk;
+                au(ps.rb)[ps.ib] = Yk;
             }
         } else if constexpr (MODE == 2 || MODE == 3) {
             // conj(H + bias) in MODE 3; bins 0 and L of slot 0 are real either way
@@ -229,8 +231,8 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
                     pair_repack(fmul2(Pk, sc), fmul2(Pm, sc), ps.w, qa[e], qb[e]);
                 }
                 pair_repack(hmul(Ak, hadd(ha[e], bs)), hmul(Am, hadd(hb[e], bs)), ps.w, Yk, Ym);
-                au[ps.ra][ps.ia] = Yk;
-                au[ps.rb][ps.ib] = Ym;
+                au(ps.ra)[ps.ia] = Yk;
+                au(ps.rb)[ps.ib] = Ym;
             } else {
                 float2 A0, AL;  // bins 0 and L (real)
                 pair_unpack(Za, Za, make_float2(1.f, 0.f), A0, AL);
@@ -244,7 +246,7 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
                 }
                 pair_repack(make_float2(A0.x * (ha[e].x + bs), 0.f), make_float2(AL.x * (ha[e].y + bs), 0.f),
                             make_float2(1.f, 0.f), Yk, Ym);
-                au[ps.ra][ps.ia] = Yk;
+                au(ps.ra)[ps.ia] = Yk;
                 float2 Ah, Ad;  // bin L/2 pairs with itself
                 pair_unpack(Zb, Zb, ps.w, Ah, Ad);
                 if constexpr (MODE == 2) {
@@ -255,7 +257,7 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
                 }
                 const float2 Ch = hmul(Ah, hadd(hb[e], bs));
                 pair_repack(Ch, Ch, ps.w, Yk, Ym);
-                au[ps.rb][ps.ib] = Yk;
+                au(ps.rb)[ps.ib] = Yk;
             }
         } else {
             float2 Ak, Am;
@@ -284,8 +286,8 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const PairSlot ps = pair_slot<L1, L2>(p, tp + 2 * T2 * e, tb);
-            au[ps.ra][ps.ia] = qa[e];
-            au[ps.rb][ps.ib] = qb[e];
+            au(ps.ra)[ps.ia] = qa[e];
+            au(ps.rb)[ps.ib] = qb[e];
         }
         __syncthreads();
         lds_load_strided<T2>(racc, t, v);
