@@ -55,8 +55,9 @@ struct FsBwdArgs {
     bool per_sample = false;  // dh per sample ([B][N-1][D][L]) instead of the batch sum
 };
 
-// Per (b, d) row: the L-point tile T, the gated input's spectra G_o of the N-1
-// steps and the row's dh tile Tdh (the inverse rows of A_dv * conj(A_g); complex),
+// Per (b, d) row: the L-point tile T, the column-transformed gated inputs G_o of
+// the N-1 steps and the row's dh tile Tdh (the inverse rows of A_dv * conj(A_g);
+// complex),
 // the recomputed values v_1..v_{N-2} V (fp32), the N+1 channels' staging rows S
 // (fp32), the tap sums of every column-block workgroup; with a filter set per
 // sample also every row's lag-0 value. 256-byte aligned.

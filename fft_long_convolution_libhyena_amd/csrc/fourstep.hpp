@@ -139,17 +139,18 @@ __device__ __forceinline__ PairSlot pair_slot(int p, int k2, const FsTables& tb)
 // Pass B: row FFTs over m2 (the tile already carries the W_L^(k1*m2) twiddle),
 // the pair step, then (MODE 0) the spectrum multiply and the inverse rows, in
 // place; or (MODE 1) the scaled spectrum written in place. Backward modes:
-// MODE 2 is MODE 0 that also stores the unpacked spectrum A of the row in `gt`
-// (the gated input's spectrum, in the filter spectrum's layout); MODE 3 takes the
+// MODE 2 is MODE 0 with the result written to the tile `aux` (the column-
+// transformed gated input in `slot` is kept for the adjoint); MODE 3 takes the
 // row as A_dv, applies conj(H + bias) instead of H + bias (the correlation that is
-// the adjoint of the convolution) and also takes the product A_dv * conj(A_g) (A_g
-// read from `gt`, the spectrum of dh's correlation) through the same repack and
-// inverse rows into the tile `pt` of the row.
+// the adjoint of the convolution) and also takes the product A_dv * conj(A_g)
+// through the same repack and inverse rows into the tile `pt` of the row, A_g
+// being the row transform of the kept column-transformed gated input in `aux`
+// (the same arithmetic as in MODE 2, so the same values).
 // A unit is the row pair {p, L1-p} (p >= 1) or {0, L1/2} (p = 0).
 template <int LOG1, int LOG2, int MODE>
 __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ slot, const float2* __restrict__ spec,
                                             const float* __restrict__ bias, const FsTables& tb, int D, int o,
-                                            int64_t flat, int ug, float2* __restrict__ gt = nullptr,
+                                            int64_t flat, int ug, float2* __restrict__ aux = nullptr,
                                             float2* __restrict__ pt = nullptr, int64_t sbs = 0) {
     constexpr bool CONV = MODE == 0 || MODE == 2 || MODE == 3;  // multiply by the filter spectrum
     using Cfg = FsCfg<LOG1, LOG2>;
@@ -175,7 +176,37 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
         bs = bias[(int64_t)o * D + d] * (1.0f / (4.0f * (float)L));
     }
 
+    // row ri (0 or 1) of this thread's unit, computed rather than taken from an array,
+    // so that a run-time ri leaves a plain LDS address (no private array)
+    auto au = [&](int ri) { return RowAcc{lds + (2 * unit + ri) * RP}; };
+
     float2 v[16];
+    [[maybe_unused]] float2 ga[8], gb[8];  // MODE 3: A_g at this thread's pairs
+    if constexpr (MODE == 3) {
+        // A_g: the forward rows of the kept gated input, unpacked at this thread's pairs
+        const float2* grow = aux + (uint32_t)k1 * L2;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = grow[(uint32_t)(t + T2 * e)];
+        fft_strided<L2, false, false>(v, t, tb.tw2, racc);
+        __syncthreads();
+        lds_store_strided<T2>(racc, t, v);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const PairSlot ps = pair_slot<L1, L2>(p, tp + 2 * T2 * e, tb);
+            const float2 Za = au(ps.ra)[ps.ia];
+            const float2 Zb = au(ps.rb)[ps.ib];
+            if (ps.kind == 0) {
+                pair_unpack(Za, Zb, ps.w, ga[e], gb[e]);
+            } else {
+                float2 A0, AL, Ad;  // bins 0 and L (real), then L/2
+                pair_unpack(Za, Za, make_float2(1.f, 0.f), A0, AL);
+                ga[e] = make_float2(A0.x, AL.x);
+                pair_unpack(Zb, Zb, ps.w, gb[e], Ad);
+            }
+        }
+        // the next transform begins with a barrier before it writes the LDS
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = rowp[(uint32_t)(t + T2 * e)];
     if constexpr (CONV) {
@@ -192,9 +223,6 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
     lds_store_strided<T2>(racc, t, v);
     __syncthreads();
 
-    // row ri (0 or 1) of this thread's unit, computed rather than taken from an array,
-    // so that a run-time ri leaves a plain LDS address (no private array)
-    auto au = [&](int ri) { return RowAcc{lds + (2 * unit + ri) * RP}; };
     const float sc = 1.0f / (8.0f * (float)L);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -223,11 +251,8 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
             if (ps.kind == 0) {
                 float2 Ak, Am;
                 pair_unpack(Za, Zb, ps.w, Ak, Am);
-                if constexpr (MODE == 2) {
-                    gt[(uint32_t)ps.offa] = Ak;
-                    gt[(uint32_t)ps.offb] = Am;
-                } else {
-                    const float2 Pk = cmulc(Ak, gt[(uint32_t)ps.offa]), Pm = cmulc(Am, gt[(uint32_t)ps.offb]);
+                if constexpr (MODE == 3) {
+                    const float2 Pk = cmulc(Ak, ga[e]), Pm = cmulc(Am, gb[e]);
                     pair_repack(fmul2(Pk, sc), fmul2(Pm, sc), ps.w, qa[e], qb[e]);
                 }
                 pair_repack(hmul(Ak, hadd(ha[e], bs)), hmul(Am, hadd(hb[e], bs)), ps.w, Yk, Ym);
@@ -237,10 +262,8 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
                 float2 A0, AL;  // bins 0 and L (real)
                 pair_unpack(Za, Za, make_float2(1.f, 0.f), A0, AL);
                 [[maybe_unused]] float2 Yd;
-                if constexpr (MODE == 2) {
-                    gt[0] = make_float2(A0.x, AL.x);
-                } else {
-                    const float2 g0 = gt[0];
+                if constexpr (MODE == 3) {
+                    const float2 g0 = ga[e];
                     pair_repack(make_float2(A0.x * g0.x * sc, 0.f), make_float2(AL.x * g0.y * sc, 0.f),
                                 make_float2(1.f, 0.f), qa[e], Yd);
                 }
@@ -249,10 +272,8 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
                 au(ps.ra)[ps.ia] = Yk;
                 float2 Ah, Ad;  // bin L/2 pairs with itself
                 pair_unpack(Zb, Zb, ps.w, Ah, Ad);
-                if constexpr (MODE == 2) {
-                    gt[(uint32_t)ps.offb] = Ah;
-                } else {
-                    const float2 Ph = cmulc(Ah, gt[(uint32_t)ps.offb]);
+                if constexpr (MODE == 3) {
+                    const float2 Ph = cmulc(Ah, gb[e]);
                     pair_repack(fmul2(Ph, sc), fmul2(Ph, sc), ps.w, qb[e], Yd);
                 }
                 const float2 Ch = hmul(Ah, hadd(hb[e], bs));
@@ -277,8 +298,9 @@ __device__ __forceinline__ void fs_row_body(float2* lds, float2* __restrict__ sl
         __syncthreads();
         lds_load_strided<T2>(racc, t, v);
         fft_strided<L2, true, false>(v, t, tb.tw2, racc);
+        float2* orow = MODE == 2 ? aux + (uint32_t)k1 * L2 : rowp;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) rowp[(uint32_t)(t + T2 * e)] = v[e];
+        for (int e = 0; e < 16; ++e) orow[(uint32_t)(t + T2 * e)] = v[e];
     }
     if constexpr (MODE == 3) {
         // the dh product through the same inverse rows, into the row's dh tile

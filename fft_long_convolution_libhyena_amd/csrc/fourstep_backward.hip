@@ -10,12 +10,13 @@
 // through the same zero-padded spectra with conj(H + bias).
 //
 // Launches over all B*D rows (each row's tiles live in the workspace):
-//  pass A of g_0 -> T; for o = 0 .. N-2: pass B mode 2 (rows, multiply, inverse
-//  rows; keeps A_{g_o} in G_o) -> T, then a column pass: MID (v_{o+1} -> V, the
-//  next gated input by columns -> T) or, after the last step, HEAD (dx_0 -> S_0,
+//  pass A of g_0 -> G_0; for o = 0 .. N-2: pass B mode 2 (rows of G_o, multiply,
+//  inverse rows) -> T, G_o kept, then a column pass: MID (v_{o+1} -> V, the next
+//  gated input by columns -> G_{o+1}) or, after the last step, HEAD (dx_0 -> S_0,
 //  dv_{N-1} by columns -> T);
-//  for o = N-2 .. 0: pass B mode 3 (conj(H + bias), inverse rows -> T; the product
-//  A_dv conj(A_{g_o}) through the same inverse rows -> the row's dh tile); dh_o by
+//  for o = N-2 .. 0: pass B mode 3 (conj(H + bias), inverse rows -> T; A_{g_o} from
+//  the rows of G_o, the product A_dv conj(A_{g_o}) through the same inverse rows ->
+//  the row's dh tile); dh_o by
 //  columns from the fixed-order sum of a channel's dh tiles over the batch (dbias_o
 //  its lag-0 value); then TAILMID (dx_{N-1-o} -> S, dv_o by columns -> T) or, at
 //  o = 0, TAIL0 (dx_{N-1} and dv_0 -> S);
@@ -49,9 +50,11 @@ __device__ __forceinline__ void fs_raw_pairs(const TIO* __restrict__ row, uint32
 
 }  // namespace
 
-// Pass B of step o: MODE 2 keeps the gated input's spectrum in G_o (forward
-// recompute), MODE 3 forms the dh product in P with G_o and applies
-// conj(H_o + bias_o) (the adjoint), both then inverting the rows in T.
+// Pass B of step o on the tile T and the kept column-transformed gated input G_o:
+// MODE 2 (forward recompute) transforms G_o and writes the inverse rows to T;
+// MODE 3 (the adjoint) transforms T (dv), applies conj(H_o + bias_o), and takes the
+// dh product with A_g, the rows of G_o transformed again, into P; both invert the
+// rows in T.
 template <int LOG1, int LOG2, int MODE>
 __global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::ROW_THREADS))
 k_fs_row_bwd(float2* __restrict__ T, const float2* __restrict__ spec, const float* __restrict__ bias,
@@ -62,13 +65,17 @@ k_fs_row_bwd(float2* __restrict__ T, const float2* __restrict__ spec, const floa
     int ug;
     if (!xcd_row_map(blockIdx.x, nrows, Cfg::L1 / 2 / Cfg::UNITS, r, ug)) return;
     const int64_t L = (int64_t)Cfg::L1 * Cfg::L2;
-    fs_row_body<LOG1, LOG2, MODE>(lds, T + r * L, spec, bias, tb, D, o, r, ug, G + ((int64_t)o * nrows + r) * L,
-                                  P ? P + r * L : nullptr, sbs);
+    float2* trow = T + r * L;
+    float2* grow = G + ((int64_t)o * nrows + r) * L;
+    if constexpr (MODE == 2)
+        fs_row_body<LOG1, LOG2, MODE>(lds, grow, spec, bias, tb, D, o, r, ug, trow, nullptr, sbs);
+    else
+        fs_row_body<LOG1, LOG2, MODE>(lds, trow, spec, bias, tb, D, o, r, ug, grow, P + r * L, sbs);
 }
 
 // Column passes of the backward (inverse columns of the tile first, then):
 //  MID (forward recompute after step o < N-2): v_{o+1} is stored in V_{o+1};
-//      g_{o+1} = v_{o+1} * x_{N-2-o} is transformed by columns back into the tile.
+//      g_{o+1} = v_{o+1} * x_{N-2-o} is transformed by columns into G_{o+1} (Tout).
 //  HEAD (after the last step): with dy and x_0, dx_0 = dy * v_{N-1} goes to S_0 and
 //      dv_{N-1} = dy * x_0 is transformed by columns back into the tile.
 //  TAILMID (step o >= 1 of the adjoint): the columns give dg_o; with a = N-1-o,
@@ -82,7 +89,8 @@ constexpr int kColMid = 0, kColHead = 1, kColTailMid = 2, kColTail0 = 3;
 
 template <int LOG1, int LOG2, class TIO, int KIND>
 __global__ void __launch_bounds__((FsCfg<LOG1, LOG2>::COL_THREADS))
-k_fs_colinv_bwd(float2* __restrict__ T, const TIO* __restrict__ u, const float* __restrict__ w3,
+k_fs_colinv_bwd(const float2* __restrict__ T, float2* __restrict__ Tout, const TIO* __restrict__ u,
+                const float* __restrict__ w3,
                 const TIO* __restrict__ dy, float* __restrict__ S, float* __restrict__ V, float* __restrict__ part,
                 FsTables tb, int D, int N, int o, int64_t nrows) {
     using Cfg = FsCfg<LOG1, LOG2>;
@@ -98,7 +106,8 @@ k_fs_colinv_bwd(float2* __restrict__ T, const TIO* __restrict__ u, const float* 
     const int c = threadIdx.x % CB, t = threadIdx.x / CB;
     const int m2 = cb * CB + c;
     const ColAcc<Cfg::CP> cacc{lds + c};
-    float2* slot = T + r * L;
+    const float2* slot = T + r * L;
+    float2* oslot = Tout + r * L;  // the refill's tile (T itself except for MID)
     float2 v[16];
     const float2 base = twiddle_base<L2>(tb, t, m2);
 #pragma unroll
@@ -179,7 +188,7 @@ k_fs_colinv_bwd(float2* __restrict__ T, const TIO* __restrict__ u, const float* 
         fft_strided<L1, false, true>(v, t, tb.tw1, cacc);
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-            slot[(uint32_t)(t + T1 * e) * L2 + m2] = cmul(v[e], twiddle_step<L2>(tb, base, e, m2));
+            oslot[(uint32_t)(t + T1 * e) * L2 + m2] = cmul(v[e], twiddle_step<L2>(tb, base, e, m2));
     }
     if constexpr (KIND == kColMid) return;
     // this workgroup's tap sums
@@ -310,16 +319,17 @@ static void fs_backward_launch(const FsBwdArgs& a, hipStream_t st) {
     // forward recompute: pass A of g_0, then per step pass B (keeping G_o) and a
     // column pass (MID: store v_{o+1}, next input; HEAD after the last step)
     hipLaunchKernelGGL((k_fs_colfwd<LOG1, LOG2, TIO, 0>), dim3(gcol), bcol, 0, st, u, a.w3, (const float*)nullptr,
-                       w.T, a.tb, a.D, N, (int64_t)0, rows);
+                       w.G, a.tb, a.D, N, (int64_t)0, rows);
     for (int o = 0; o < N - 1; ++o) {
         hipLaunchKernelGGL((k_fs_row_bwd<LOG1, LOG2, 2>), dim3(grow), brow, 0, st, w.T, a.spec, a.bias, w.G,
                            (float2*)nullptr, a.tb, a.D, o, rows, a.sbs);
         if (o < N - 2)
-            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColMid>), dim3(gcol), bcol, 0, st, w.T, u, a.w3,
-                               dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
+            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColMid>), dim3(gcol), bcol, 0, st,
+                               (const float2*)w.T, w.G + (int64_t)(o + 1) * rows * L, u, a.w3, dy, w.S, w.V, w.part,
+                               a.tb, a.D, N, o, rows);
         else
-            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColHead>), dim3(gcol), bcol, 0, st, w.T, u,
-                               a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
+            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColHead>), dim3(gcol), bcol, 0, st,
+                               (const float2*)w.T, w.T, u, a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
     }
     // the adjoint, last step first: pass B (dh product, conj(H + bias)), dh of the
     // step, then the column pass that finishes the step's gate channel
@@ -340,11 +350,11 @@ static void fs_backward_launch(const FsBwdArgs& a, hipStream_t st) {
                                (const float*)w.lag, a.dbias + (int64_t)o * a.D, a.B, a.D);
         }
         if (o > 0)
-            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColTailMid>), dim3(gcol), bcol, 0, st, w.T, u,
-                               a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
+            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColTailMid>), dim3(gcol), bcol, 0, st,
+                               (const float2*)w.T, w.T, u, a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
         else
-            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColTail0>), dim3(gcol), bcol, 0, st, w.T, u,
-                               a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
+            hipLaunchKernelGGL((k_fs_colinv_bwd<LOG1, LOG2, TIO, kColTail0>), dim3(gcol), bcol, 0, st,
+                               (const float2*)w.T, w.T, u, a.w3, dy, w.S, w.V, w.part, a.tb, a.D, N, o, rows);
     }
     const int64_t quads = L / 4;
     const int64_t nrc = rows * (N + 1);

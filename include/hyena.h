@@ -301,7 +301,8 @@ hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_p
  * (8 bytes per complex or pair value), then 3 floats of short-conv tap sums per
  * (b, channel): 8*B*D*((2N-3)*L + (N-2)*L/2) + 12*B*(N+1)*D.
  * Four-step path: per (b, d) row N+1 L-point complex tiles (the transform, the
- * N-1 gated inputs' spectra, the row's share of dh after the inverse rows), N-2
+ * N-1 gated inputs after their column transforms, the row's share of dh after the
+ * inverse rows), N-2
  * fp32 rows of recomputed values and N+1 fp32 staging rows; and 12*(N+1) bytes
  * of tap sums per (row, column block); each region 256-byte aligned. Returns 0 for a NULL plan, B < 1, or a circular plan. */
 size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B);
