@@ -974,9 +974,11 @@ def _csv_rows(d: str, suffix: str):
 
 
 def _short_name(name: str) -> str:
-    """'void hy::k_fs_row<8, 8, 0>(...)' -> 'k_fs_row<8, 8, 0>'."""
+    """'void hy::k_fs_row<8, 8, 0>(...)' -> 'k_fs_row<8, 8, 0>'; namespaces inside the
+    template arguments go too ('k_cnd_row<8, 0, hy::PairMap2, false>' -> '... PairMap2 ...')."""
     n = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").strip()
-    return n.split("hy::")[-1]
+    head, lt, rest = n.partition("<")
+    return head.split("hy::")[-1] + lt + rest.replace("hy::", "")
 
 
 def _is_forward_kernel(short: str) -> bool:
@@ -1030,15 +1032,33 @@ def summarize_pmc(args):
             e[key].append(float(r["Counter_Value"]))
     F = args.forwards
     kern = args.kernel
-    # a family name (k_fs_passes, k_part_passes; fs_backward) stands for every kernel of
-    # the forward (of the backward)
-    family = kern in ("k_fs_passes", "k_part_passes", "fs_backward")
-    member = _is_backward_kernel if kern == "fs_backward" else _is_forward_kernel
+    # a family name stands for every kernel of one step: k_fs_passes, k_part_passes
+    # (the forward); fs_backward, k_lds_bwd_rows (the backward); k_c2_conv2d, k_c3_conv3d
+    # (the N-d step: its kernels run at least once per step, the spectrum's once per plan)
+    family = kern in ("k_fs_passes", "k_part_passes", "fs_backward", "k_lds_bwd_rows", "k_c2_conv2d",
+                      "k_c3_conv3d")
+    if kern in ("fs_backward", "k_lds_bwd_rows"):
+        member = _is_backward_kernel
+    elif kern in ("k_c2_conv2d", "k_c3_conv3d"):
+        def member(k):
+            e = per[k]
+            return k.startswith(("k_c2_", "k_c3_", "k_cnd_")) and max(len(e["fetch"]), len(e["write"])) >= F
+    else:
+        # the forward's kernels, and the kernel itself when it is not one (the filter's)
+        def member(k):
+            return _is_forward_kernel(k) or k.split("<")[0] == kern
     dom = [k for k in per if (member(k) if family else k.split("<")[0] == kern)]
     if not dom:
         raise SystemExit(f"kernel {kern} not in the counters: {sorted(per)}")
-    wl = synth.WORKLOADS[args.workload]
-    alg = alg_bytes_backward(wl) if kern == "fs_backward" else alg_bytes_forward(wl)
+    wl = synth.WORKLOADS.get(args.workload)
+    label = getattr(args, "label", "") or args.workload
+    what = getattr(args, "what", "") or (f"{wl.name} ({wl.describe()})" if wl else label)
+    if getattr(args, "alg_bytes", 0):
+        alg = args.alg_bytes
+    elif wl is None:
+        raise SystemExit("--alg-bytes is needed for a workload that is not one of the synthetic workloads")
+    else:
+        alg = alg_bytes_backward(wl) if kern in ("fs_backward", "k_lds_bwd_rows") else alg_bytes_forward(wl)
     step = 0.0
     lines = []
     for k in sorted(per, key=lambda k: -sum(per[k]["fetch"])):
@@ -1057,13 +1077,15 @@ def summarize_pmc(args):
     nd = max(len(fe_all), len(wr_all))
     fk = sum(fe_all) / len(fe_all)
     wk = sum(wr_all) / len(wr_all)
+    if kern in ("k_c2_conv2d", "k_c3_conv3d"):  # a dispatch of the N-d step is the whole step
+        nd, fk, wk = F, sum(fe_all) / F, sum(wr_all) / F
     cmd = args.command or ""
-    out = [f"# rocprofv3 HBM byte counters per dispatch: {kern} on {wl.name} ({wl.describe()})",
+    out = [f"# rocprofv3 HBM byte counters per dispatch: {kern} on {what}",
            "# commands (from the repository root):"]
     out += [f"#   {c.strip()}" for c in cmd.split(";;") if c.strip()]
     out += ["# scaled with the factors of copy_calibration_1GiB.txt; the kernels of one step (forward or backward) summed over "
             f"{F} steps give step_bytes",
-            f"kernel: {kern}", f"instance: {d0}", f"workload: {wl.name}",
+            f"kernel: {kern}", f"instance: {d0}", f"workload: {label}",
             f"sources_sha256: {kernel_sources_hash(kern)}", f"dispatches: {nd}",
             f"fetch_size_kib_per_dispatch: {fk:.1f}", f"write_size_kib_per_dispatch: {wk:.1f}",
             f"fetch_scale: {fs:.4f}", f"write_scale: {ws:.4f}",
@@ -1115,9 +1137,11 @@ def summarize_trace(args):
     from fft_long_convolution_libhyena_amd import synth
 
     rows = _csv_rows(args.summarize_trace, "kernel_stats.csv")
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS.get(args.workload)
+    what = getattr(args, "what", "") or (f"{wl.name} ({wl.describe()})" if wl else
+                                         (getattr(args, "label", "") or args.workload))
     cmd = args.command or ""
-    out = [f"# rocprofv3 kernel-trace statistics: {args.kernel} on {wl.name} ({wl.describe()})",
+    out = [f"# rocprofv3 kernel-trace statistics: {args.kernel} on {what}",
            "# command (from the repository root):"]
     out += [f"#   {c.strip()}" for c in cmd.split(";;") if c.strip()]
     out += [f"# kernel sources sha256[:16]: {kernel_sources_hash(args.kernel)}",
@@ -1196,6 +1220,13 @@ def main():
     ap.add_argument("--forwards", type=int, default=5, help="forwards in the profiled run (--summarize-pmc)")
     ap.add_argument("--command", default="", help="the profiling commands, ';;'-separated, for the summary header")
     ap.add_argument("--note", default="", help="a closing note line for a trace summary")
+    ap.add_argument("--label", default="", help="workload label of a summary (default: --workload), e.g. "
+                    "long64k_per_sample or 256x256")
+    ap.add_argument("--what", default="", help="what a summary covers, for its first line (default: the "
+                    "workload's description)")
+    ap.add_argument("--alg-bytes", type=int, default=0,
+                    help="algorithmic bytes of one step for a counter summary (default: the forward's or "
+                         "backward's of --workload)")
     args = ap.parse_args()
     args.check = not args.no_check
     if args.summarize_pmc:

@@ -150,3 +150,48 @@ def test_pmc_summary_from_csv(tmp_path, capsys):
     # two dispatches over two forwards; the spectrum kernel is not part of the forward
     assert float(kv["step_bytes"]) == pytest.approx((400 * fs + 100 * ws) * 1024 / 2, rel=1e-5)
     assert "#   cmd one" in text and "#   cmd two" in text
+
+
+def test_short_name_drops_namespaces_inside_template_arguments():
+    assert bench._short_name("void hy::(anonymous namespace)::k_cnd_row<8, 0, hy::PairMap2, false>(float2*, int)") \
+        == "k_cnd_row<8, 0, PairMap2, false>"
+    assert bench._short_name("void hy::k_fs_row<8, 8, 0>(HIP_vector_type<float, 2u>*)") == "k_fs_row<8, 8, 0>"
+    assert bench._short_name("hy::k_fs_bwd_dw(float const*, float*, int)") == "k_fs_bwd_dw"
+
+
+def test_pmc_summary_of_an_nd_step(tmp_path, capsys):
+    import argparse
+    """A conv family: every kernel run at least once per step is part of the step; the
+    spectrum's kernels (once per plan) are not; a dispatch is one whole step."""
+    import csv
+
+    def write(d, counter, vals):
+        d.mkdir(parents=True, exist_ok=True)
+        with open(d / "x_counter_collection.csv", "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            for name, v in vals:
+                w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+
+    col = "void hy::k_c2_colfwd<8, float, false>(float const*)"
+    row = "void hy::(anonymous namespace)::k_cnd_row<8, 0, hy::PairMap2, false>(float2*)"
+    spec = "void hy::(anonymous namespace)::k_cnd_row<8, 1, hy::PairMap2, false>(float2*)"
+    # two steps of three chunks each; the spectrum once
+    write(tmp_path / "fe", "FETCH_SIZE", [(col, 10.0)] * 6 + [(row, 20.0)] * 6 + [(spec, 999.0)])
+    write(tmp_path / "wr", "WRITE_SIZE", [(col, 1.0)] * 6 + [(row, 2.0)] * 6 + [(spec, 999.0)])
+    args = argparse.Namespace(summarize_pmc=[str(tmp_path / "fe"), str(tmp_path / "wr")], kernel="k_c2_conv2d",
+                              workload="conv2d", label="256x256", what="a 2-D step", alg_bytes=1000,
+                              forwards=2, command="")
+    bench.summarize_pmc(args)
+    text = capsys.readouterr().out
+    kv = dict(ln.split(": ", 1) for ln in text.splitlines() if ": " in ln and not ln.startswith("#"))
+    fs, ws = bench._calibration()
+    assert kv["workload"] == "256x256" and int(kv["dispatches"]) == 2
+    assert float(kv["fetch_bytes_per_dispatch"]) == pytest.approx(3 * 30 * 1024 * fs, rel=1e-5)
+    assert float(kv["write_bytes_per_dispatch"]) == pytest.approx(3 * 3 * 1024 * ws, rel=1e-5)
+    assert float(kv["step_bytes"]) == pytest.approx(3 * (30 * fs + 3 * ws) * 1024, rel=1e-5)
+    assert "k_cnd_row<8, 1, PairMap2, false>: dispatches 1" in text and "(not part of the step)" in text
+    # a workload outside the synthetic set needs its algorithmic bytes
+    args.alg_bytes = 0
+    with pytest.raises(SystemExit):
+        bench.summarize_pmc(args)
