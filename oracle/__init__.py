@@ -206,6 +206,87 @@ def forward_circular(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bia
     return v * x[0]
 
 
+def circular_corr(a: np.ndarray, k: np.ndarray, mode: str = "fft") -> np.ndarray:
+    """Circular correlation along the last axis in fp64: out[t] = sum_{s<S}
+    k[(s - t) mod S] a[s], the adjoint of v -> circular_conv(v, k) (and of
+    k -> circular_conv(v, k) with v in the role of k). ``direct`` writes the sum
+    out; ``fft`` multiplies a's real FFT by the conjugate of k's and inverts."""
+    a = np.asarray(a, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    S = a.shape[-1]
+    if mode == "direct":
+        idx = (np.arange(S)[None, :] - np.arange(S)[:, None]) % S  # [t, s] -> (s - t) mod S
+        return np.einsum("...s,...ts->...t", a, k[..., idx])
+    return np.fft.irfft(np.fft.rfft(a, axis=-1) * np.conj(np.fft.rfft(k, axis=-1)), n=S, axis=-1)
+
+
+def backward_circular(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray, dy: np.ndarray,
+                      order: int, mode: str = "fft"):
+    """Gradients of ``forward_circular`` in fp64 for upstream gradient dy [B,D,S]
+    (the chain rule of the gated recurrence, HyenaDNA walkthrough section 2.1, with
+    the circular long convolution of the HyenaND summary's boundary handling):
+    dv_{N-1} = dy * x_0, dx_0 = dy * v_{N-1}; for o = N-2 .. 0 with a = dv_{o+1}:
+    dg_o = circular_corr(a, h_o) + bias_o * a, dh_o = sum_b circular_corr(a, g_o),
+    dbias_o = sum_b sum_t a g_o, dx_{N-1-o} = dg_o * v_o, dv_o = dg_o * x_{N-1-o};
+    then the causal short conv's transpose du[s] = sum_j w_j duc[s + 2 - j] (duc = 0
+    past the end) and dw_j = sum_t duc[t] u[t - 2 + j] for every channel.
+    Returns (du_proj [B,(N+1)D,S], dshort_w [(N+1)D,3], dh [N-1,D,S], dbias [N-1,D])."""
+    u = np.asarray(u_proj, dtype=np.float32).astype(np.float64)
+    w = np.asarray(short_w, dtype=np.float32).astype(np.float64)
+    hh = np.asarray(h, dtype=np.float32).astype(np.float64)
+    bb = np.asarray(bias, dtype=np.float32).astype(np.float64)
+    g_up = np.asarray(dy, dtype=np.float32).astype(np.float64)
+    B, C, S = u.shape
+    N = int(order)
+    if C % (N + 1):
+        raise ValueError("u_proj channel count must be (order+1)*D")
+    D = C // (N + 1)
+    if w.shape != (C, 3) or hh.shape != (N - 1, D, S) or bb.shape != (N - 1, D) or g_up.shape != (B, D, S):
+        raise ValueError("parameter shapes do not match u_proj")
+    # the short conv (causal, zero before t = 0): uc[t] = sum_j w_j u[t - 2 + j]
+    upad = np.concatenate([np.zeros((B, C, 2)), u], axis=-1)
+    uc = sum(w[None, :, j, None] * upad[:, :, j:j + S] for j in range(3))
+    x = [uc[:, i * D:(i + 1) * D] for i in range(N)]
+    vs = [uc[:, N * D:]]
+    gs = []
+    for o in range(N - 1):
+        g = vs[o] * x[N - 1 - o]
+        gs.append(g)
+        vs.append(circular_conv(g, hh[o][None], mode=mode) + bb[o][None, :, None] * g)
+    duc = np.zeros((B, C, S))
+    duc[:, 0:D] = g_up * vs[N - 1]
+    a = g_up * x[0]
+    dh = np.zeros((N - 1, D, S))
+    db = np.zeros((N - 1, D))
+    for o in range(N - 2, -1, -1):
+        dh[o] = circular_corr(a, gs[o], mode=mode).sum(axis=0)
+        db[o] = (a * gs[o]).sum(axis=(0, 2))
+        dg = circular_corr(a, hh[o][None], mode=mode) + bb[o][None, :, None] * a
+        gi = N - 1 - o
+        duc[:, gi * D:(gi + 1) * D] += dg * vs[o]
+        a = dg * x[gi]
+    duc[:, N * D:] = a
+    # the short conv's transpose and its taps' gradients
+    dpad = np.concatenate([duc, np.zeros((B, C, 2))], axis=-1)
+    du = sum(w[None, :, j, None] * dpad[:, :, 2 - j:2 - j + S] for j in range(3))
+    dw = np.stack([(duc * upad[:, :, j:j + S]).sum(axis=(0, 2)) for j in range(3)], axis=1)
+    return du, dw, dh, db
+
+
+def backward_circular_per_sample(u_proj: np.ndarray, short_w: np.ndarray, h: np.ndarray, bias: np.ndarray,
+                                 dy: np.ndarray, order: int, mode: str = "fft"):
+    """``backward_circular`` with a filter set per sample (h [B, N-1, D, S]): sample b
+    through its own filters; the shared parameters' gradients summed over the samples.
+    Returns (du_proj, dshort_w, dh [B,N-1,D,S], dbias)."""
+    u = np.asarray(u_proj)
+    hb = np.asarray(h)
+    g = np.asarray(dy)
+    parts = [backward_circular(u[b:b + 1], short_w, hb[b], bias, g[b:b + 1], order, mode=mode)
+             for b in range(u.shape[0])]
+    return (np.concatenate([p[0] for p in parts], axis=0), np.sum([p[1] for p in parts], axis=0),
+            np.stack([p[2] for p in parts]), np.sum([p[3] for p in parts], axis=0))
+
+
 def conv2d_forward(v: np.ndarray, k: np.ndarray, bias: np.ndarray, g: Optional[np.ndarray] = None,
                    x: Optional[np.ndarray] = None, mode: str = "fft", circular: bool = False) -> np.ndarray:
     """One gated 2-D long-convolution step in fp64 (HyenaND summary, methodology:
