@@ -172,7 +172,7 @@ KERNEL_SOURCES = {
                  "hyena_api.hip"],
     "backward": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "backward.hpp", "lds_backward.hpp",
                  "lds_backward_a.hip", "lds_backward_b.hip", "lds_backward_c.hip", "lds_backward_d.hip",
-                 "hyena_backward.hip"],
+                 "lds_backward_e.hip", "lds_backward_f.hip", "hyena_backward.hip"],
     "fs_backward": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "backward.hpp", "fourstep.hpp",
                     "fourstep_backward.hip", "hyena_backward.hip"],
     "filter": ["plan.hpp", "implicit_filter.hip"],

@@ -24,13 +24,15 @@ struct LdsBwdArgs {
     bool bf16;
     int64_t sbs = 0;          // spectrum batch stride (complex values): 0 = one spectrum for every b
     bool per_sample = false;  // dh per sample ([B][N-1][D][L]) instead of the batch sum
+    bool circ = false;        // circular plan: rows of 2L samples, no zero padding
 };
 
-// Bytes of backward workspace for batch B: per (b, d) row the N-1 product
-// spectra, the gated-input spectra of steps 0..N-3 and the values v_1..v_{N-2}
-// (float2), then the per-row tap sums of the short conv (3 floats per channel).
-inline size_t bwd_ws_bytes(int64_t B, int64_t D, int64_t L, int N) {
-    const int64_t per_row = (int64_t)(2 * N - 3) * L + (int64_t)(N - 2) * (L / 2);
+// Bytes of backward workspace for batch B and transform length L: per (b, d) row
+// the N-1 product spectra, the gated-input spectra of steps 0..N-3 and the values
+// v_1..v_{N-2} (float2; L/2 pairs per value, L for the 2L-sample rows of a
+// circular plan), then the per-row tap sums of the short conv (3 floats per channel).
+inline size_t bwd_ws_bytes(int64_t B, int64_t D, int64_t L, int N, bool circ = false) {
+    const int64_t per_row = (int64_t)(2 * N - 3) * L + (int64_t)(N - 2) * (circ ? L : L / 2);
     return (size_t)(B * D * per_row) * 8 + (size_t)(B * (N + 1) * D * 3) * 4;
 }
 

@@ -10,9 +10,12 @@
 namespace {
 
 size_t backward_ws(hyena_plan_t plan, int64_t B, bool per_sample) {
-    if (!plan || B < 1 || plan->circular) return 0;
-    if (plan->path == HYENA_PATH_LDS) return hy::bwd_ws_bytes(B, plan->D, plan->L, plan->order);
-    if (plan->path == HYENA_PATH_FOURSTEP) return hy::fs_bwd_ws_bytes(plan->logT, B, plan->D, plan->order, per_sample);
+    if (!plan || B < 1) return 0;
+    // circular plans: the LDS path only (transform length L/2 for rows of L samples)
+    if (plan->path == HYENA_PATH_LDS)
+        return hy::bwd_ws_bytes(B, plan->D, int64_t(1) << plan->logT, plan->order, plan->circular);
+    if (plan->path == HYENA_PATH_FOURSTEP && !plan->circular)
+        return hy::fs_bwd_ws_bytes(plan->logT, B, plan->D, plan->order, per_sample);
     return 0;
 }
 
@@ -27,7 +30,7 @@ hyena_status_t backward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, c
         return HYENA_ERR_INVALID_ARG;
     if (B > (int64_t(1) << 24) || B * plan->D > (int64_t(1) << 26)) return HYENA_ERR_INVALID_ARG;
     const bool fs = plan->path == HYENA_PATH_FOURSTEP;
-    if (plan->circular || !(plan->path == HYENA_PATH_LDS || fs)) return HYENA_ERR_UNSUPPORTED;
+    if (!(plan->path == HYENA_PATH_LDS || fs) || (fs && plan->circular)) return HYENA_ERR_UNSUPPORTED;
     if ((int64_t)B * 8 * ((plan->D + 7) / 8) > 0x7fffffff) return HYENA_ERR_INVALID_ARG;
     // per sample, dh alone is 4*B*(N-1)*D*L bytes; the bound keeps every grid below 2^32 work-items
     if (per_sample && B * (plan->order - 1) * plan->D * plan->L > (int64_t(1) << 35)) return HYENA_ERR_INVALID_ARG;
@@ -43,8 +46,9 @@ hyena_status_t backward_impl(hyena_plan_t plan, int64_t B, const void* u_proj, c
     }
     hy::LdsBwdArgs a{u_proj,   short_w,   (const float2*)spec, bias,      dy,         du_proj,
                      dshort_w, dh,        dbias,               (float2*)workspace, plan->tw, plan->wpair,
-                     (int)B,   (int)plan->D, plan->order,       plan->dtype == HYENA_BF16, sbs, per_sample};
-    return hy::launch_lds_backward(plan->logL, a, stream) == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
+                     (int)B,   (int)plan->D, plan->order,       plan->dtype == HYENA_BF16, sbs, per_sample,
+                     plan->circular};
+    return hy::launch_lds_backward(plan->logT, a, stream) == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
 }
 
 }  // namespace

@@ -16,6 +16,12 @@
 // correlation is a product with a conjugate spectrum: dg_o comes from
 // A_dv * conj(H_o + bias_o) and dh_o from sum_b A_dv * conj(A_g).
 //
+// Circular plans (CIRC; the HyenaND summary's circular boundary handling): the
+// rows hold 2L samples and the same L-point packed transform carries them with no
+// zero half; conv and corr are then circular (corr(a, k)[t] = sum_s k[(s-t) mod 2L]
+// a[s]), the same products with the same conjugate spectra, and every output of
+// the inverse is kept. The short conv stays causal.
+//
 // Two kernels. k_lds_bwd_rows: one workgroup per (b, d) row (the B rows of a
 // channel on one XCD, sharing its filter spectrum in L2) recomputes the forward
 // chain on chip (2(N-1) transforms), undoes it (2(N-1) transforms), writes the
@@ -81,26 +87,28 @@ __device__ __forceinline__ void spec_pair(const float2* __restrict__ Hs, uint32_
 
 // Input gradient through the short conv of one channel row:
 // du[t] = w2 duc[t] + w1 duc[t+1] + w0 duc[t+2]. duc[e] holds the pair
-// (duc[2m], duc[2m+1]) at m = t + T*e; the pairs go through LDS (each thread
-// then reads its own pair and the next one back, so duc need not stay live).
-template <int L, int E, class TIO>
-__device__ __forceinline__ void short_conv_back(const RowAcc& acc, int t, const float2 (&duc)[E / 2],
+// (duc[2m], duc[2m+1]) at m = t + T*e, e < LD (LD = E/2, or E for the 2L-sample
+// rows of a circular plan); the pairs go through LDS (each thread then reads its
+// own pair and the next one back, so duc need not stay live).
+template <int L, int E, int LD, class TIO>
+__device__ __forceinline__ void short_conv_back(const RowAcc& acc, int t, const float2 (&duc)[LD],
                                                 const float* __restrict__ w, TIO* __restrict__ durow) {
-    constexpr int H = E / 2, T = L / E;
+    constexpr int T = L / E;
+    constexpr uint32_t NP = (uint32_t)LD * T;  // pairs of the row
     phase();
     t = fresh_tid<T>(t);
     __syncthreads();  // the previous readers of LDS are done
 #pragma unroll
-    for (int e = 0; e < H; ++e) acc[t + T * e] = duc[e];
+    for (int e = 0; e < LD; ++e) acc[t + T * e] = duc[e];
     __syncthreads();
     phase();
     t = fresh_tid<T>(t);
     const float w0 = w[0], w1 = w[1], w2 = w[2];
 #pragma unroll
-    for (int e = 0; e < H; ++e) {
+    for (int e = 0; e < LD; ++e) {
         const uint32_t m = t + T * e;
         const float2 dc = acc[m];
-        const float2 nx = (m + 1 < (uint32_t)(L / 2)) ? acc[m + 1] : make_float2(0.f, 0.f);
+        const float2 nx = (m + 1 < NP) ? acc[m + 1] : make_float2(0.f, 0.f);
         store_pair(durow, m, make_float2(fmaf(w2, dc.x, fmaf(w1, dc.y, w0 * nx.x)),
                                          fmaf(w2, dc.y, fmaf(w1, nx.x, w0 * nx.y))));
     }
@@ -125,18 +133,18 @@ __device__ __forceinline__ void tap_sums(float2 dc, float2 prev, float2 cur, flo
 //                      filter spectrum (slot 0 holds the real bins 0 and L)
 //   G  [B*D][N-2][L]   unpacked spectra A_g of steps o < N-2 (the last step's stays
 //                      in registers from the recomputed forward to its undoing)
-//   V  [B*D][N-2][L/2] v_o of steps 1..N-2 as sample pairs
+//   V  [B*D][N-2][S/2] v_o of steps 1..N-2 as sample pairs (S = L, 2L circular)
 //   TW [B][(N+1)*D][3] (floats) per-row tap sums of the short conv
 // G and V are written and read back by the same thread.
-template <int LOGL, int N>
+template <int LOGL, int N, bool CIRC = false>
 struct BwdWs {
     static constexpr int64_t L = int64_t(1) << LOGL;
     static constexpr int64_t P_ROW = (N - 1) * L;
     static constexpr int64_t G_ROW = (N - 2) * L;
-    static constexpr int64_t V_ROW = (N - 2) * (L / 2);
+    static constexpr int64_t V_ROW = (N - 2) * (CIRC ? L : L / 2);
 };
 
-template <int LOGL, int N, class TIO>
+template <int LOGL, int N, class TIO, bool CIRC = false>
 __global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS)
 k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const float2* __restrict__ spec,
                const float* __restrict__ bias, const TIO* __restrict__ dy, TIO* __restrict__ du,
@@ -146,9 +154,11 @@ k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
     constexpr int E = LdsCfg<LOGL>::E;
     constexpr int H = E / 2;
     constexpr int T = L / E;
+    constexpr int LD = CIRC ? E : H;                  // pairs of data per thread
+    constexpr int64_t S = CIRC ? 2 * (int64_t)L : L;  // samples per row
     constexpr int NV = 3 * (N + 1);  // tap sums per thread
     static_assert(T * NV * 4 <= padded_len<L>() * 8, "reduction buffer fits in the transform's LDS");
-    using W = BwdWs<LOGL, N>;
+    using W = BwdWs<LOGL, N, CIRC>;
     __shared__ float2 lds[padded_len<L>()];
     const RowAcc acc{lds};
     // as in the forward: consecutive workgroups go to different XCDs, and the B
@@ -174,16 +184,16 @@ k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
 #pragma unroll
     for (int i = 0; i <= N; ++i) dws[i][0] = dws[i][1] = dws[i][2] = 0.f;
 
-    const TIO* ub = u + (int64_t)b * C * L;
+    const TIO* ub = u + (int64_t)b * C * S;
     const TIO* urow[N + 1];
 #pragma unroll
-    for (int i = 0; i <= N; ++i) urow[i] = ub + ((int64_t)i * D + d) * L;
+    for (int i = 0; i <= N; ++i) urow[i] = ub + ((int64_t)i * D + d) * S;
     const float* wN = w3 + 3 * ((int64_t)N * D + d);
 
     // -------------------------------------------------- forward chain, recomputed
-    float2 v[H];
+    float2 v[LD];
 #pragma unroll
-    for (int e = 0; e < H; ++e) v[e] = conv3_pair(urow[N], (uint32_t)(t + T * e), wN[0], wN[1], wN[2]);
+    for (int e = 0; e < LD; ++e) v[e] = conv3_pair(urow[N], (uint32_t)(t + T * e), wN[0], wN[1], wN[2]);
     float2 ga[H], gb[H];  // A_g at k and L-k of the last step
     float2 gh = make_float2(0.f, 0.f);
 #pragma unroll
@@ -193,18 +203,18 @@ k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
         const int gi = N - 1 - o;
         const float* wg = w3 + 3 * ((int64_t)gi * D + d);
         if (o >= 1) {
-            float2* Vw = fresh(Vr) + (int64_t)(o - 1) * (L / 2);
+            float2* Vw = fresh(Vr) + (int64_t)(o - 1) * (S / 2);
 #pragma unroll
-            for (int e = 0; e < H; ++e) Vw[t + T * e] = v[e];
+            for (int e = 0; e < LD; ++e) Vw[t + T * e] = v[e];
         }
         float2 f[E];
         const TIO* xr = fresh(urow[gi]);
 #pragma unroll
-        for (int e = 0; e < H; ++e) f[e] = emul(v[e], conv3_pair(xr, (uint32_t)(t + T * e), wg[0], wg[1], wg[2]));
+        for (int e = 0; e < LD; ++e) f[e] = emul(v[e], conv3_pair(xr, (uint32_t)(t + T * e), wg[0], wg[1], wg[2]));
 #pragma unroll
-        for (int e = H; e < E; ++e) f[e] = make_float2(0.f, 0.f);
+        for (int e = LD; e < E; ++e) f[e] = make_float2(0.f, 0.f);
         phase();
-        fft_strided<L, false, true>(f, t, fresh(tw), acc);
+        fft_strided<L, false, !CIRC>(f, t, fresh(tw), acc);
         phase();
         t = fresh_tid<T>(t);
         __syncthreads();
@@ -252,17 +262,17 @@ k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
         phase();
         t = fresh_tid<T>(t);
 #pragma unroll
-        for (int e = 0; e < H; ++e) v[e] = f[e];  // v_{o+1}
+        for (int e = 0; e < LD; ++e) v[e] = f[e];  // v_{o+1}
     }
 
     // ------------------------------------------------------------------ backward
-    float2 a[H], dx[H];
+    float2 a[LD], dx[LD];
     {
-        const TIO* dyr = dy + r * L;
+        const TIO* dyr = dy + r * S;
         const float* w0p = w3 + 3 * (int64_t)d;
         const TIO* x0r = fresh(urow[0]);
 #pragma unroll
-        for (int e = 0; e < H; ++e) {
+        for (int e = 0; e < LD; ++e) {
             const uint32_t m = t + T * e;
             const float2 g = load_pair(dyr, m);
             float2 prev, cur;
@@ -274,7 +284,7 @@ k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
         pin(dws[0][0]);
         pin(dws[0][1]);
         pin(dws[0][2]);
-        short_conv_back<L, E>(acc, t, dx, w0p, du + ((int64_t)b * C + d) * L);
+        short_conv_back<L, E>(acc, t, dx, w0p, du + ((int64_t)b * C + d) * S);
     }
 #pragma unroll
     for (int o = N - 2; o >= 0; --o) {
@@ -284,11 +294,11 @@ k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
         const float* wg = w3 + 3 * ((int64_t)gi * D + d);
         float2 f[E];
 #pragma unroll
-        for (int e = 0; e < H; ++e) f[e] = a[e];
+        for (int e = 0; e < LD; ++e) f[e] = a[e];
 #pragma unroll
-        for (int e = H; e < E; ++e) f[e] = make_float2(0.f, 0.f);
+        for (int e = LD; e < E; ++e) f[e] = make_float2(0.f, 0.f);
         phase();
-        fft_strided<L, false, true>(f, t, fresh(tw), acc);
+        fft_strided<L, false, !CIRC>(f, t, fresh(tw), acc);
         phase();
         t = fresh_tid<T>(t);
         __syncthreads();
@@ -349,9 +359,9 @@ k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
         {
             const TIO* vr = fresh(urow[N]);
             const TIO* xr = fresh(urow[gi]);
-            const float2* Vw = fresh(Vr) + (int64_t)(o - 1) * (L / 2);
+            const float2* Vw = fresh(Vr) + (int64_t)(o - 1) * (S / 2);
 #pragma unroll
-            for (int e = 0; e < H; ++e) {
+            for (int e = 0; e < LD; ++e) {
                 const uint32_t m = t + T * e;
                 float2 xp, xc;
                 raw_pairs(xr, m, xp, xc);
@@ -376,9 +386,9 @@ k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
                 pin(dws[N][2]);
             }
         }
-        short_conv_back<L, E>(acc, t, dx, wg, du + ((int64_t)b * C + (int64_t)gi * D + d) * L);
+        short_conv_back<L, E>(acc, t, dx, wg, du + ((int64_t)b * C + (int64_t)gi * D + d) * S);
     }
-    short_conv_back<L, E>(acc, t, a, wN, du + ((int64_t)b * C + (int64_t)N * D + d) * L);
+    short_conv_back<L, E>(acc, t, a, wN, du + ((int64_t)b * C + (int64_t)N * D + d) * S);
 
     // ------------------------------------------- this row's tap sums, per channel
     float* red = reinterpret_cast<float*>(lds);
@@ -399,7 +409,7 @@ k_lds_bwd_rows(const TIO* __restrict__ u, const float* __restrict__ w3, const fl
 // (by the o = 0 workgroups) dshort_w of the N+1 channels of d from the row tap sums.
 // PER_SAMPLE (a filter set per sample): one workgroup per (b, o, d) inverts sample
 // b's product spectrum alone into dh[b][o][d]; dbias is left to k_lds_bwd_dbias.
-template <int LOGL, int N, bool PER_SAMPLE>
+template <int LOGL, int N, bool PER_SAMPLE, bool CIRC = false>
 __global__ void __launch_bounds__(LdsCfg<LOGL>::THREADS)
 k_lds_bwd_finish(const float2* __restrict__ ws, float* __restrict__ dw, float* __restrict__ dh,
                  float* __restrict__ dbias, const float2* __restrict__ tw, const float2* __restrict__ wpair, int B,
@@ -408,7 +418,9 @@ k_lds_bwd_finish(const float2* __restrict__ ws, float* __restrict__ dw, float* _
     constexpr int E = LdsCfg<LOGL>::E;
     constexpr int H = E / 2;
     constexpr int T = L / E;
-    using W = BwdWs<LOGL, N>;
+    constexpr int LD = CIRC ? E : H;                  // pairs of dh per thread
+    constexpr int64_t S = CIRC ? 2 * (int64_t)L : L;  // taps per filter
+    using W = BwdWs<LOGL, N, CIRC>;
     __shared__ float2 lds[padded_len<L>()];
     const RowAcc acc{lds};
     const int nod = (N - 1) * D;
@@ -462,9 +474,9 @@ k_lds_bwd_finish(const float2* __restrict__ ws, float* __restrict__ dw, float* _
     lds_load_strided<T>(acc, t, f);
     fft_strided<L, true, false>(f, t, tw, acc);
     // shared filters: dh[o][d]; per sample: dh[b][o][d]
-    float* dhr = dh + ((int64_t)bs * nod + od) * L;
+    float* dhr = dh + ((int64_t)bs * nod + od) * S;
 #pragma unroll
-    for (int e = 0; e < H; ++e) store_pair(dhr, (uint32_t)(t + T * e), f[e]);
+    for (int e = 0; e < LD; ++e) store_pair(dhr, (uint32_t)(t + T * e), f[e]);
     // the bias gradient sum_b sum_t dv[t] g[t] is the lag-0 value of the same
     // correlation that gives dh
     if (!PER_SAMPLE && t == 0) dbias[od] = f[0].x;
@@ -482,36 +494,46 @@ k_lds_bwd_finish(const float2* __restrict__ ws, float* __restrict__ dw, float* _
 
 // With a filter set per sample: dbias[o][d] = sum over b (in order) of the lag-0
 // values dh[b][o][d][0], each sample's share of the shared bias's gradient.
-template <int LOGL>
+// (dh rows of S taps: L, or 2L for a circular plan)
+template <int LOGL, bool CIRC>
 __global__ void k_lds_bwd_dbias(const float* __restrict__ dh, float* __restrict__ dbias, int B, int nod) {
-    constexpr int64_t L = int64_t(1) << LOGL;
+    constexpr int64_t S = (int64_t(1) << LOGL) * (CIRC ? 2 : 1);
     const int od = blockIdx.x * blockDim.x + threadIdx.x;
     if (od >= nod) return;
     float s = 0.f;
-    for (int b = 0; b < B; ++b) s += dh[((int64_t)b * nod + od) * L];
+    for (int b = 0; b < B; ++b) s += dh[((int64_t)b * nod + od) * S];
     dbias[od] = s;
+}
+
+template <int LOGL, int N, bool CIRC>
+inline void launch_lds_backward_c(const LdsBwdArgs& a, hipStream_t st) {
+    constexpr int T = LdsCfg<LOGL>::THREADS;
+    const unsigned grid = (unsigned)(a.B * 8 * ((a.D + 7) / 8));
+    if (a.bf16)
+        hipLaunchKernelGGL((k_lds_bwd_rows<LOGL, N, uint16_t, CIRC>), dim3(grid), dim3(T), 0, st,
+                           (const uint16_t*)a.u, a.w3, a.spec, a.bias, (const uint16_t*)a.dy, (uint16_t*)a.du, a.ws,
+                           a.tw, a.wpair, a.B, a.D, a.sbs);
+    else
+        hipLaunchKernelGGL((k_lds_bwd_rows<LOGL, N, float, CIRC>), dim3(grid), dim3(T), 0, st, (const float*)a.u,
+                           a.w3, a.spec, a.bias, (const float*)a.dy, (float*)a.du, a.ws, a.tw, a.wpair, a.B, a.D,
+                           a.sbs);
+    if (a.per_sample) {
+        const int nod = (N - 1) * a.D;
+        hipLaunchKernelGGL((k_lds_bwd_finish<LOGL, N, true, CIRC>), dim3((unsigned)(a.B * nod)), dim3(T), 0, st,
+                           (const float2*)a.ws, a.dw, a.dh, a.dbias, a.tw, a.wpair, a.B, a.D);
+        hipLaunchKernelGGL((k_lds_bwd_dbias<LOGL, CIRC>), dim3((unsigned)((nod + 255) / 256)), dim3(256), 0, st,
+                           (const float*)a.dh, a.dbias, a.B, nod);
+    } else
+        hipLaunchKernelGGL((k_lds_bwd_finish<LOGL, N, false, CIRC>), dim3((unsigned)((N - 1) * a.D)), dim3(T), 0,
+                           st, (const float2*)a.ws, a.dw, a.dh, a.dbias, a.tw, a.wpair, a.B, a.D);
 }
 
 template <int LOGL, int N>
 inline void launch_lds_backward_n(const LdsBwdArgs& a, hipStream_t st) {
-    constexpr int T = LdsCfg<LOGL>::THREADS;
-    const unsigned grid = (unsigned)(a.B * 8 * ((a.D + 7) / 8));
-    if (a.bf16)
-        hipLaunchKernelGGL((k_lds_bwd_rows<LOGL, N, uint16_t>), dim3(grid), dim3(T), 0, st, (const uint16_t*)a.u,
-                           a.w3, a.spec, a.bias, (const uint16_t*)a.dy, (uint16_t*)a.du, a.ws, a.tw, a.wpair, a.B,
-                           a.D, a.sbs);
+    if (a.circ)
+        launch_lds_backward_c<LOGL, N, true>(a, st);
     else
-        hipLaunchKernelGGL((k_lds_bwd_rows<LOGL, N, float>), dim3(grid), dim3(T), 0, st, (const float*)a.u, a.w3,
-                           a.spec, a.bias, (const float*)a.dy, (float*)a.du, a.ws, a.tw, a.wpair, a.B, a.D, a.sbs);
-    if (a.per_sample) {
-        const int nod = (N - 1) * a.D;
-        hipLaunchKernelGGL((k_lds_bwd_finish<LOGL, N, true>), dim3((unsigned)(a.B * nod)), dim3(T), 0, st,
-                           (const float2*)a.ws, a.dw, a.dh, a.dbias, a.tw, a.wpair, a.B, a.D);
-        hipLaunchKernelGGL((k_lds_bwd_dbias<LOGL>), dim3((unsigned)((nod + 255) / 256)), dim3(256), 0, st,
-                           (const float*)a.dh, a.dbias, a.B, nod);
-    } else
-        hipLaunchKernelGGL((k_lds_bwd_finish<LOGL, N, false>), dim3((unsigned)((N - 1) * a.D)), dim3(T), 0, st,
-                           (const float2*)a.ws, a.dw, a.dh, a.dbias, a.tw, a.wpair, a.B, a.D);
+        launch_lds_backward_c<LOGL, N, false>(a, st);
 }
 
 template <int LOGL>

@@ -1,9 +1,13 @@
-// Instantiations of the LDS-path backward for log2 L in {4, ..., 10}, and the
+// Instantiations of the LDS-path backward for log2 L in {4, 5, 6}, and the
 // dispatch over sizes.
 #include "lds_backward.hpp"
 
 namespace hy {
-// instantiated in lds_backward_b.hip .. lds_backward_d.hip
+// instantiated in lds_backward_b.hip .. lds_backward_f.hip
+extern template hipError_t launch_lds_backward_t<7>(const LdsBwdArgs&, hipStream_t);
+extern template hipError_t launch_lds_backward_t<8>(const LdsBwdArgs&, hipStream_t);
+extern template hipError_t launch_lds_backward_t<9>(const LdsBwdArgs&, hipStream_t);
+extern template hipError_t launch_lds_backward_t<10>(const LdsBwdArgs&, hipStream_t);
 extern template hipError_t launch_lds_backward_t<11>(const LdsBwdArgs&, hipStream_t);
 extern template hipError_t launch_lds_backward_t<12>(const LdsBwdArgs&, hipStream_t);
 extern template hipError_t launch_lds_backward_t<13>(const LdsBwdArgs&, hipStream_t);
@@ -12,10 +16,6 @@ extern template hipError_t launch_lds_backward_t<14>(const LdsBwdArgs&, hipStrea
 template hipError_t launch_lds_backward_t<4>(const LdsBwdArgs&, hipStream_t);
 template hipError_t launch_lds_backward_t<5>(const LdsBwdArgs&, hipStream_t);
 template hipError_t launch_lds_backward_t<6>(const LdsBwdArgs&, hipStream_t);
-template hipError_t launch_lds_backward_t<7>(const LdsBwdArgs&, hipStream_t);
-template hipError_t launch_lds_backward_t<8>(const LdsBwdArgs&, hipStream_t);
-template hipError_t launch_lds_backward_t<9>(const LdsBwdArgs&, hipStream_t);
-template hipError_t launch_lds_backward_t<10>(const LdsBwdArgs&, hipStream_t);
 
 hipError_t launch_lds_backward(int logL, const LdsBwdArgs& a, hipStream_t st) {
     switch (logL) {

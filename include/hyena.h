@@ -113,7 +113,7 @@ enum {
      * grid):  conv(v, h)[t] = sum_{s < L} h[s] v[(t - s) mod L]. The L samples are
      * transformed as they are (an L-point real transform, no zero padding); the
      * short conv keeps its causal zero padding. Requires L >= 32; the LDS path
-     * serves L <= 32768. hyena_backward does not support circular plans. */
+     * serves L <= 32768. hyena_backward takes circular plans on the LDS path. */
     HYENA_FLAG_CIRCULAR = 1
 };
 
@@ -304,7 +304,9 @@ hyena_status_t hyena_forward_timed(hyena_plan_t plan, int64_t B, const void* u_p
  * N-1 gated inputs after their column transforms, the row's share of dh after the
  * inverse rows), N-2
  * fp32 rows of recomputed values and N+1 fp32 staging rows; and 12*(N+1) bytes
- * of tap sums per (row, column block); each region 256-byte aligned. Returns 0 for a NULL plan, B < 1, or a circular plan. */
+ * of tap sums per (row, column block); each region 256-byte aligned. A circular
+ * plan (LDS path only) counts L/2-point transforms and L sample pairs per value.
+ * Returns 0 for a NULL plan, B < 1, or a circular four-step plan. */
 size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* Backward of the forward hot path: given the upstream gradient dy of y, the
@@ -325,8 +327,10 @@ size_t hyena_backward_workspace_bytes(hyena_plan_t plan, int64_t B);
  *           buffers' previous contents)
  *   workspace / workspace_bytes: device scratch of at least
  *           hyena_backward_workspace_bytes(plan, B); contents on entry irrelevant.
- * Both paths have a backward for every order; circular plans have none
- * (HYENA_ERR_UNSUPPORTED). Every sum over the batch
+ * Both paths have a backward for every order. For a circular plan (LDS path
+ * only; a circular four-step plan gives HYENA_ERR_UNSUPPORTED) the correlations
+ * are circular too (corr(a, k)[t] = sum_s k[(s - t) mod L] a[s]), dh has L taps
+ * per filter and the short conv's transpose keeps its causal form. Every sum over the batch
  * or over workgroups is taken in a fixed order (no atomics), so results are
  * bitwise reproducible.
  * Enqueued on `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL or misaligned
@@ -340,7 +344,7 @@ hyena_status_t hyena_backward(hyena_plan_t plan, int64_t B, const void* u_proj, 
 /* Bytes of workspace hyena_backward_per_sample needs for batch B: as
  * hyena_backward_workspace_bytes, except on the four-step path, where B*D floats
  * of per-sample dbias terms are added. Returns 0 for a NULL plan, B < 1, or a
- * circular plan. */
+ * circular four-step plan. */
 size_t hyena_backward_per_sample_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* Backward of hyena_forward_per_sample (a filter set per sample, the HyenaND

@@ -1,5 +1,6 @@
 """GPU parity of circular plans (HYENA_FLAG_CIRCULAR: circular long convolution of
-L samples, causal short conv) against the circular-mode oracle, on both paths.
+L samples, causal short conv) against the circular-mode oracle, on both paths, and
+of their backward (LDS path) against the circular backward oracle.
 
 Bounds as for the zero-padded forward: relative L2 1e-4 (fp32 I/O), 1e-2 (bf16 I/O).
 """
@@ -104,12 +105,74 @@ def test_circular_plan_limits_and_backward():
     with pytest.raises(HyenaError) as e:
         Plan(65536, 2, 2, "f32", "lds", circular=True)  # beyond the LDS path
     assert e.value.status == 2
+    # the backward of a circular plan runs on the LDS path only
     wl = synth.custom(1, 2, 1024, 2, seed=1)
     x = synth.generate(wl)
     t = to_device(x)
-    with Plan(1024, 2, 2, circular=True) as p:
+    with Plan(1024, 2, 2, "f32", "fourstep", circular=True) as p:
         assert p.backward_workspace_bytes(1) == 0
         with pytest.raises(HyenaError) as e:
             p.backward(t["u"], t["w"], p.spectrum(t["h"]), t["bias"], torch.zeros((1, 2, 1024), device="cuda"),
                        workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
         assert e.value.status == 2
+    with Plan(1024, 2, 2, "f32", "lds", circular=True) as p:
+        # 2L-sample rows: v_1..v_{N-2} take L pairs per row instead of L/2
+        assert p.backward_workspace_bytes(3) > 0
+
+
+BWD_CASES = [
+    # B, D, L (samples per row), order, dtype, per_sample
+    (2, 3, 32, 2, "f32", False),      # the smallest circular plan (16-point transform)
+    (1, 5, 256, 3, "f32", False),
+    (2, 4, 2048, 2, "bf16", False),
+    (2, 3, 8192, 4, "f32", False),
+    (2, 2, 1024, 8, "f32", False),
+    (1, 3, 32768, 2, "f32", False),   # the largest LDS circular plan (32 values per thread)
+    (2, 3, 512, 2, "f32", True),
+    (3, 2, 4096, 3, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("B,D,L,order,dtype,per_sample", BWD_CASES)
+def test_circular_backward_matches_oracle(B, D, L, order, dtype, per_sample):
+    import torch
+
+    from fft_long_convolution_libhyena_amd import Plan
+
+    wl = synth.custom(B, D, L, order, dtype, seed=L % 97 + 3 * D + order)
+    x = synth.generate(wl)
+    t = to_device(x)
+    dy = synth.upstream_grad(wl)
+    g = torch.from_numpy(dy).cuda()
+    if dtype == "bf16":
+        g = g.to(torch.bfloat16)
+    hb = synth.per_sample_filters(wl) if per_sample else None
+    say(f"[circular backward] {wl.describe()} per_sample={per_sample}")
+    with Plan(L, D, order, dtype, "lds", circular=True) as p:
+        if per_sample:
+            spec = p.spectrum_batched(torch.from_numpy(hb).cuda())
+            outs = p.backward_per_sample(t["u"], t["w"], spec, t["bias"], g.contiguous())
+        else:
+            outs = p.backward(t["u"], t["w"], p.spectrum(t["h"]), t["bias"], g.contiguous())
+        torch.cuda.synchronize()
+    mode = "direct" if L <= 256 else "fft"
+    if per_sample:
+        ref = oracle.backward_circular_per_sample(x.u_proj, x.short_w, hb, x.bias, dy, order, mode=mode)
+    else:
+        ref = oracle.backward_circular(x.u_proj, x.short_w, x.h, x.bias, dy, order, mode=mode)
+    got = [a.float().cpu().numpy().astype(np.float64) for a in outs]
+    bounds = [1e-2 if dtype == "bf16" else 1e-4, 1e-4, 1e-4, 1e-4]
+    for name, gv, r, bound in zip(("du_proj", "dshort_w", "dh", "dbias"), got, ref, bounds):
+        assert np.all(np.isfinite(gv)), f"{name}: non-finite values"
+        err = oracle.rel_l2(gv, r)
+        say(f"   {name:9s} rel_l2={err:.3e} (bound {bound:.0e})")
+        assert err <= bound, f"{name}: rel L2 {err:.3e} exceeds {bound:.0e}"
+    # the causal backward differs: the comparison is not satisfied by accident
+    if not per_sample:
+        causal = oracle.backward(x.u_proj, x.short_w, x.h, x.bias, dy, order, mode=mode)
+        assert oracle.rel_l2(causal[2], ref[2]) > 10 * bounds[2]
+    # per-channel check of du
+    g2 = got[0].reshape(-1, L)
+    r2 = ref[0].reshape(-1, L)
+    row = np.linalg.norm(g2 - r2, axis=1) / np.maximum(np.linalg.norm(r2, axis=1), 1e-30)
+    assert row.max() <= 10 * bounds[0], f"worst du row rel L2 {row.max():.3e}"
