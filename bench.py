@@ -311,9 +311,11 @@ def cpu_baseline_backward(x, wl, budget_s: float, hb=None):
 
 def bench_backward(args, wl, x, torch, Plan, per_sample=False):
     """hyena_backward, or with per_sample hyena_backward_per_sample (a filter set per
-    sample: B spectra read, B filter gradients written)."""
+    sample: B spectra read, B filter gradients written); with --circular on a
+    circular plan (circular correlations, L/2 + 1 spectrum bins per filter)."""
     from fft_long_convolution_libhyena_amd import synth
 
+    circ = bool(getattr(args, "circular", False))
     dev = torch.device("cuda", 0)
     iot = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     u = torch.from_numpy(x.u_proj).to(dev).to(iot).contiguous()
@@ -321,7 +323,7 @@ def bench_backward(args, wl, x, torch, Plan, per_sample=False):
     h = torch.from_numpy(x.h).to(dev)
     bias = torch.from_numpy(x.bias).to(dev)
     dy = torch.from_numpy(synth.upstream_grad(wl)).to(dev).to(iot).contiguous()
-    plan = Plan(wl.L, wl.D, wl.order, wl.dtype)
+    plan = Plan(wl.L, wl.D, wl.order, wl.dtype, circular=circ)
     hb = synth.per_sample_filters(wl) if per_sample else None
     spec = plan.spectrum_batched(torch.from_numpy(hb).to(dev)) if per_sample else plan.spectrum(h)
     N, D, L, B = wl.order, wl.D, wl.L, wl.B
@@ -351,28 +353,34 @@ def bench_backward(args, wl, x, torch, Plan, per_sample=False):
         log(f"[bench] rep {rep}: {times[-1] * 1e3:.1f} us/step")
     ms = float(np.median(times))
     nbytes = alg_bytes_backward(wl)
+    spec_bins = L // 2 + 1 if circ else L + 1  # spectrum bins per filter
+    if circ:
+        nbytes -= 8 * (N - 1) * D * (L + 1 - spec_bins)
     if per_sample:  # B filter spectra read and B filter gradients written instead of one each
-        nbytes += (B - 1) * (N - 1) * D * (8 * (L + 1) + 4 * L)
+        nbytes += (B - 1) * (N - 1) * D * (8 * spec_bins + 4 * L)
     # the step's kernels taken together: k_lds_bwd_rows + k_lds_bwd_finish on the LDS
     # path, the launches of the four-step backward ("fs_backward") otherwise
     bk = "k_lds_bwd_rows" if plan.path == "lds" else "fs_backward"
     achieved = nbytes / (ms * 1e-3) / 1e9
     out = {
         "metric": "channel-tokens/s (B·D·L/s) and % HBM peak, Hyena op backward (gradients of u_proj, short_w, "
-                  "h, bias)" + (" with a filter set per sample" if per_sample else ""),
+                  "h, bias)" + (" with a filter set per sample" if per_sample else "")
+                  + (", circular plan" if circ else ""),
         "value": B * D * L / (ms * 1e-3), "unit": "channel-tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32" if wl.dtype == "f32" else "bf16-io/f32",
         "data": f"synthetic seeded ({wl.kind} activations, N(0,1) upstream gradient"
                 f"{', per-sample exponentially decaying random filters' if per_sample else ''})",
         "config": {"workload": wl.name, "B": B, "D": D, "L": L, "order": N, "io_dtype": wl.dtype,
-                   "path": plan.path, "pass": "backward_per_sample" if per_sample else "backward"},
+                   "path": plan.path, "pass": ("backward_per_sample" if per_sample else "backward")
+                   + ("_circular" if circ else "")},
         # the whole backward step (two launches on the LDS path, nine on the
         # four-step path) against its algorithmic bytes
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      # the whole step's HBM bytes (every launch of one backward step)
-                     "traffic": measured_step_traffic(bk, wl.name + ("_per_sample" if per_sample else "")),
+                     "traffic": measured_step_traffic(bk, wl.name + ("_per_sample" if per_sample else "")
+                                                      + ("_circular" if circ else "")),
                      "kernel": bk,
                      "alg_bytes_per_launch": nbytes, "launch_ms": round(ms, 5), "launches_per_step": 1},
     }
@@ -382,7 +390,12 @@ def bench_backward(args, wl, x, torch, Plan, per_sample=False):
         ds = [0, D // 2, D - 1]
         xs = synth.channel_subset(x, ds)
         g = synth.upstream_grad(wl)[:, ds]
-        if per_sample:
+        if circ and per_sample:
+            ref = oracle.backward_circular_per_sample(xs.u_proj, xs.short_w, np.ascontiguousarray(hb[:, :, ds]),
+                                                      xs.bias, g, N)
+        elif circ:
+            ref = oracle.backward_circular(xs.u_proj, xs.short_w, xs.h, xs.bias, g, N)
+        elif per_sample:
             ref = oracle.backward_per_sample(xs.u_proj, xs.short_w, np.ascontiguousarray(hb[:, :, ds]), xs.bias, g, N)
         else:
             ref = oracle.backward(xs.u_proj, xs.short_w, xs.h, xs.bias, g, N)
@@ -391,7 +404,7 @@ def bench_backward(args, wl, x, torch, Plan, per_sample=False):
         out["check_rel_l2_dh"] = oracle.rel_l2(outs[2].double().cpu().numpy()[..., ds, :], ref[2])
         log(f"[bench] oracle check on channels {ds}: du rel_l2 {out['check_rel_l2_du']:.3e}, "
             f"dh rel_l2 {out['check_rel_l2_dh']:.3e}")
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not circ:
         log("[bench] cpu baseline (backward oracle) ...")
         out["cpu_baseline"] = cpu_baseline_backward(x, wl, args.cpu_budget, hb)
     print(json.dumps(out), flush=True)
