@@ -38,11 +38,13 @@ def _run(args):
 
 @pytest.mark.parametrize("mode,workload", [
     ([], "tiny"), ([], "dna_small"), (["--backward"], "tiny"), (["--backward", "--per-sample"], "tiny"),
-    (["--per-sample"], "tiny"), (["--circular"], "tiny"), (["--operator"], "tiny"), (["--filter"], "tiny"),
+    (["--backward", "--circular"], "tiny"), (["--per-sample"], "tiny"), (["--circular"], "tiny"),
+    (["--operator"], "tiny"), (["--filter"], "tiny"),
     (["--path", "fourstep"], "tiny"), (["--conv2d"], None), (["--conv3d", "--circular"], None),
     # full workloads in the launch configuration the benchmark times, checked on sampled outputs
     (["--circular"], "long64k"), (["--circular"], "lm125m"), (["--path", "partitioned"], "long64k"),
     (["--operator"], "lm125m"), (["--per-sample"], "long64k"), (["--backward", "--per-sample"], "lm125m"),
+    (["--backward", "--circular"], "lm125m"),
     ([], "long64k"), ([], "long64k_o3"), ([], "lm125m"), (["--synthesis"], "lm125m")])
 def test_bench_line(mode, workload):
     args = mode + COMMON + (["--workload", workload] if workload else [])
