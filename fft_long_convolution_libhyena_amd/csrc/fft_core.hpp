@@ -334,8 +334,11 @@ __device__ __forceinline__ float2 load_pair(const uint16_t* __restrict__ row, ui
 // Two floats to packed bf16 (lo in bits 0..15), rounded to nearest even by the
 // hardware conversion; a NaN stays a (quiet) NaN.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    // one two-lane conversion instruction (round to nearest even), lo in the low half
+    typedef float F2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 B2 __attribute__((ext_vector_type(2)));
+    const F2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, B2));
 }
 __device__ __forceinline__ void store_pair(float* __restrict__ row, uint32_t m, float2 v) {
     reinterpret_cast<float2*>(row)[m] = v;
