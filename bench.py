@@ -181,7 +181,7 @@ KERNEL_SOURCES = {
     "conv3d": ["fft_core.hpp", "pair.hpp", "fourstep.hpp", "kernels.hpp", "plan.hpp", "tables.hpp", "conv_nd.hpp",
                "conv3d.hip"],
     "partitioned": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "partitioned.hip", "hyena_api.hip"],
-    "operator": ["kernels.hpp", "inproj.hip", "hyena_operator.hip"],
+    "operator": ["kernels.hpp", "inproj.hip", "outproj.hip", "hyena_operator.hip"],
     "synthesis": ["plan.hpp", "kernel_synthesis.hip"],
 }
 

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhyena.so")
-SOURCES = ["hyena_api.hip", "hyena_backward.hip", "hyena_operator.hip", "fourstep.hip", "fourstep_backward.hip", "implicit_filter.hip", "kernel_synthesis.hip", "inproj.hip", "conv2d.hip", "conv3d.hip", "partitioned.hip", "lds_path_a.hip", "lds_path_b.hip", "lds_path_c.hip",
+SOURCES = ["hyena_api.hip", "hyena_backward.hip", "hyena_operator.hip", "fourstep.hip", "fourstep_backward.hip", "implicit_filter.hip", "kernel_synthesis.hip", "inproj.hip", "outproj.hip", "conv2d.hip", "conv3d.hip", "partitioned.hip", "lds_path_a.hip", "lds_path_b.hip", "lds_path_c.hip",
            "lds_path_d.hip", "lds_backward_a.hip", "lds_backward_b.hip", "lds_backward_c.hip", "lds_backward_d.hip",
            "lds_backward_e.hip", "lds_backward_f.hip"]
 HEADERS = ["fft_core.hpp", "kernels.hpp", "pair.hpp", "plan.hpp", "tables.hpp", "conv_nd.hpp", "lds_path.hpp", "fourstep.hpp", "backward.hpp",

@@ -15,8 +15,10 @@
 // epilogue does not apply) entering as the C operand (beta = 1) of a bias matrix
 // that a small kernel fills once per call; the path applies the short conv.
 //
-// The output projection is a hipBLASLt GEMM per sequence in both cases, with the
-// bias epilogue (one value per row):
+// The output projection of bf16 plans (D a multiple of 64, L of 8) runs in this
+// library's own matrix-core kernel (outproj.hip), one launch over every sequence,
+// with b_out added in its epilogue. Otherwise it is a hipBLASLt GEMM per
+// sequence, with the bias epilogue (one value per row):
 //   out[b] (row-major [L][D]) = y[b]^T W_out^T + b_out
 //   column-major view: O (D x L) = W_out (D x D) * Y (D x L) + b_out 1^T
 // Each sequence is one ordinary (non-batched) GEMM call: the weights are shared
@@ -148,6 +150,10 @@ void tune(hipblasLtHandle_t lt, Gemm& g, const void* alpha, const void* A, const
 // Descriptors of both GEMMs for one sequence (column-major views, see the file header).
 // bf16 plans whose width the matrix-core kernel tiles take the fused in_proj
 bool custom_inproj(const hyena_plan_s* plan) { return plan->dtype == HYENA_BF16 && hy::inproj_supported(plan->D); }
+// and the same plans (when L is a multiple of 8) the matrix-core out_proj
+bool custom_outproj(const hyena_plan_s* plan) {
+    return plan->dtype == HYENA_BF16 && hy::outproj_supported(plan->D, plan->L);
+}
 
 bool build(OpState& s, const hyena_plan_s* plan) {
     s.in.release();
@@ -171,6 +177,10 @@ bool build(OpState& s, const hyena_plan_s* plan) {
             !layout(&g1.d, dt, L, C, L))
             return false;
         if (!pick_algo(s.lt, g1)) return false;
+    }
+    if (custom_outproj(plan)) {
+        s.built = true;
+        return true;
     }
     // out_proj: O (D x L, ld D) = op_T(Wo: D x D, ld D) * op_T(Y: L x D, ld L) + b_out (bias epilogue, one
     //           value per row of O)
@@ -276,8 +286,10 @@ hyena_status_t operator_impl(hyena_plan_t plan, int64_t B, const void* x, const 
         // time the hipBLASLt candidates on sequence 0's operands (outputs are scratch)
         const float one = 1.f, zero = 0.f;
         if (!custom_inproj(plan)) tune(s.lt, s.in, &one, x, w_in, &one, c.cb, c.u, c.lt, stream);
-        hipblasLtMatmulDescSetAttribute(s.out.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &b_out, sizeof(b_out));
-        tune(s.lt, s.out, &one, w_out, c.y, &zero, out, out, c.lt, stream);
+        if (!custom_outproj(plan)) {
+            hipblasLtMatmulDescSetAttribute(s.out.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &b_out, sizeof(b_out));
+            tune(s.lt, s.out, &one, w_out, c.y, &zero, out, out, c.lt, stream);
+        }
         return hipStreamSynchronize(stream) == hipSuccess ? HYENA_OK : HYENA_ERR_DEVICE;
     }
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -326,10 +338,15 @@ hyena_status_t operator_impl(hyena_plan_t plan, int64_t B, const void* x, const 
     if (st == HYENA_OK)
         st = hyena_forward(plan, B, c.u, path_taps, spec, bias, c.y, c.path, c.path_bytes, stream);
     if (ms) (void)hipEventRecord(ev[2], stream);
-    // output projection with the bias epilogue
-    if (st == HYENA_OK)
+    // output projection with b_out
+    if (custom_outproj(plan)) {
+        if (st == HYENA_OK && hy::launch_outproj((const uint16_t*)c.y, (const uint16_t*)w_out, (const uint16_t*)b_out,
+                                                 (uint16_t*)out, B, L, D, stream) != hipSuccess)
+            st = HYENA_ERR_DEVICE;
+    } else if (st == HYENA_OK) {
         hipblasLtMatmulDescSetAttribute(s.out.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &b_out, sizeof(b_out));
-    for (int64_t b = 0; b < B && st == HYENA_OK; ++b) {
+    }
+    for (int64_t b = 0; b < B && st == HYENA_OK && !custom_outproj(plan); ++b) {
         const char* yb = static_cast<const char*>(c.y) + (size_t)b * D * L * es;
         char* ob = static_cast<char*>(out) + (size_t)b * L * D * es;
         if (hipblasLtMatmul(s.lt, s.out.desc, &one, w_out, s.out.a, yb, s.out.b, &zero, ob, s.out.c, ob, s.out.d,

@@ -386,9 +386,12 @@ size_t hyena_operator_workspace_bytes(hyena_plan_t plan, int64_t B);
  * the short conv (applied to the fp32 sums, then rounded once to bf16); the path
  * then runs with identity taps. Other plans: the input projection is a hipBLASLt
  * GEMM per sequence (u_proj rounded to the plan dtype) and the path applies the
- * short conv. The output projection is a hipBLASLt GEMM per sequence (fp32
- * accumulation). hipBLASLt's heuristic choice of kernel is used unless
- * hyena_operator_tune has run on the plan. The first call on a plan attaches the
+ * short conv. The output projection of bf16 plans with D a multiple of 64 and L
+ * a multiple of 8 runs in libhyena's own bf16 matrix-core kernel, one launch over
+ * every sequence (fp32 accumulation, b_out added, rounded once); otherwise it is a
+ * hipBLASLt GEMM per sequence (fp32 accumulation). hipBLASLt's heuristic choice of
+ * kernel is used unless hyena_operator_tune has run on the plan. The first call
+ * on a plan attaches the
  * GEMM state to it (a hipBLASLt handle and descriptors), so calls on one plan are
  * serialised internally; hyena_plan_destroy releases it. The call never waits on
  * the device.

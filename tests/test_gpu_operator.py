@@ -55,7 +55,8 @@ CASES = [
     (1, 16, 32768, 2, "f32", "auto"),
     (1, 64, 8192, 4, "bf16", "auto"),
     # bf16 with D a multiple of 64: the fused matrix-core in_proj + short conv
-    (3, 64, 1024, 2, "bf16", "auto"),      # five 254-step tiles per sequence, the last one partial
+    (3, 64, 1024, 2, "bf16", "auto"),      # five 252-step tiles per sequence, the last one partial
+    (3, 128, 128, 2, "bf16", "auto"),      # out_proj: one time tile per sequence, half of it past L
     (2, 320, 512, 3, "bf16", "auto"),      # C = 1280: five full channel tiles
     (1, 192, 65536, 2, "bf16", "auto"),    # C = 576: a partial channel tile; four-step path
 ]
