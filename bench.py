@@ -181,13 +181,13 @@ KERNEL_SOURCES = {
     "conv3d": ["fft_core.hpp", "pair.hpp", "fourstep.hpp", "kernels.hpp", "plan.hpp", "tables.hpp", "conv_nd.hpp",
                "conv3d.hip"],
     "partitioned": ["fft_core.hpp", "pair.hpp", "kernels.hpp", "plan.hpp", "partitioned.hip", "hyena_api.hip"],
-    "operator": ["kernels.hpp", "inproj.hip", "outproj.hip", "hyena_operator.hip"],
+    "operator": ["kernels.hpp", "inproj.hip", "outproj.hpp", "outproj.hip", "hyena_operator.hip"],
     "synthesis": ["plan.hpp", "kernel_synthesis.hip"],
 }
 
 
 def kernel_family(kernel: str) -> str:
-    if kernel.startswith("k_inproj"):
+    if kernel.startswith(("k_inproj", "k_outproj", "operator")):
         return "operator"
     if kernel.startswith("k_kernel_synthesis"):
         return "synthesis"

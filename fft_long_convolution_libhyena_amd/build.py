@@ -18,7 +18,7 @@ SOURCES = ["hyena_api.hip", "hyena_backward.hip", "hyena_operator.hip", "fourste
            "lds_path_d.hip", "lds_backward_a.hip", "lds_backward_b.hip", "lds_backward_c.hip", "lds_backward_d.hip",
            "lds_backward_e.hip", "lds_backward_f.hip"]
 HEADERS = ["fft_core.hpp", "kernels.hpp", "pair.hpp", "plan.hpp", "tables.hpp", "conv_nd.hpp", "lds_path.hpp", "fourstep.hpp", "backward.hpp",
-           "lds_backward.hpp"]
+           "lds_backward.hpp", "outproj.hpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

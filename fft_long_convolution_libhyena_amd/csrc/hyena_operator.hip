@@ -36,6 +36,7 @@
 
 #include "../../include/hyena.h"
 #include "kernels.hpp"
+#include "outproj.hpp"
 #include "plan.hpp"
 
 namespace {

@@ -146,10 +146,4 @@ bool inproj_supported(int64_t D);
 hipError_t launch_inproj_conv3(const uint16_t* x, const uint16_t* w, const uint16_t* b, const float* w3,
                                uint16_t* u, int64_t B, int64_t L, int64_t D, int64_t C, hipStream_t st);
 
-// Output projection on the bf16 matrix cores (outproj.hip):
-// out[b][t][n] = sum_k y[b][k][t] w_out[n][k] + b_out[n], y channels-first, out tokens-first.
-bool outproj_supported(int64_t D, int64_t L);
-hipError_t launch_outproj(const uint16_t* y, const uint16_t* w, const uint16_t* bo, uint16_t* out, int64_t B,
-                          int64_t L, int64_t D, hipStream_t st);
-
 }  // namespace hy

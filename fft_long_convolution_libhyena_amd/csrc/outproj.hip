@@ -31,6 +31,7 @@
 
 #include "fft_core.hpp"
 #include "kernels.hpp"
+#include "outproj.hpp"
 
 namespace hy {
 namespace {
