@@ -12,8 +12,10 @@
 // Otherwise (fp32 plans), the input projection is a hipBLASLt GEMM per sequence:
 //   column-major view: U (L x C) = X^T (L x D) * W_in^T (D x C) + 1 b_in^T
 // with the input bias (constant along the columns of U, where hipBLASLt's bias
-// epilogue does not apply) entering as the C operand (beta = 1) of a bias matrix
-// that a small kernel fills once per call; the path applies the short conv.
+// epilogue does not apply) folded into the product by one more term of the inner
+// dimension: x is copied with a column of ones appended ([L][Dp] per sequence,
+// Dp = D + 1 rounded up to 8, zeros after the ones) and w_in with b_in as that
+// column ([C][Dp]), so U = Xa^T Wa^T; the path applies the short conv.
 //
 // The output projection of bf16 plans (D a multiple of 64, L of 8) runs in this
 // library's own matrix-core kernel (outproj.hip), one launch over every sequence,
@@ -51,12 +53,49 @@ __global__ void k_identity_taps(float* __restrict__ w3, int64_t C) {
     if (i < 3 * C) w3[i] = (i % 3 == 2) ? 1.f : 0.f;
 }
 
+// Inner dimension of the bias-augmented input projection: D values, the bias
+// term, zeros up to a multiple of 8 (16-byte rows in both dtypes).
+int64_t aug_dim(int64_t D) { return (D + 1 + 7) / 8 * 8; }
+
+// Four values of T as one store: 16 bytes of fp32, 8 of bf16.
 template <class T>
-__global__ void k_bias_matrix(const T* __restrict__ b_in, T* __restrict__ cb, int64_t L, int64_t C) {
-    // cb[c*L + t] = b_in[c]: column c of the column-major L x C matrix is b_in[c]
-    const int64_t n = L * C;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-        cb[i] = b_in[i / L];
+struct Quad;
+template <>
+struct Quad<float> {
+    using type = float4;
+    static __device__ __forceinline__ float one() { return 1.f; }
+    static __device__ __forceinline__ float4 pack(const float (&v)[4]) { return make_float4(v[0], v[1], v[2], v[3]); }
+};
+template <>
+struct Quad<uint16_t> {
+    using type = uint2;
+    static __device__ __forceinline__ uint16_t one() { return 0x3f80; }  // bf16 1.0
+    static __device__ __forceinline__ uint2 pack(const uint16_t (&v)[4]) {
+        return make_uint2((uint32_t)v[0] | ((uint32_t)v[1] << 16), (uint32_t)v[2] | ((uint32_t)v[3] << 16));
+    }
+};
+
+// dst[r][k] = src[r][k] for k < D, extra[r] (or 1 when extra is null) at k = D,
+// 0 beyond, Dp a multiple of 8: xa from x (rows of D features) and wa from w_in
+// and b_in. One row per workgroup at a time, four values per store.
+template <class T>
+__global__ void __launch_bounds__(256) k_augment_rows(const T* __restrict__ src, const T* __restrict__ extra,
+                                                      T* __restrict__ dst, int64_t rows, int D, int Dp) {
+    using Q = Quad<T>;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const T* s = src + r * D;
+        typename Q::type* d = reinterpret_cast<typename Q::type*>(dst + r * Dp);
+        const T bias = extra ? extra[r] : Q::one();
+        for (int g = threadIdx.x; g < Dp / 4; g += blockDim.x) {
+            T v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int k = 4 * g + j;
+                v[j] = k < D ? s[k] : (k == D ? bias : T{});
+            }
+            d[g] = Q::pack(v);
+        }
+    }
 }
 
 struct Gemm {
@@ -164,8 +203,9 @@ bool build(OpState& s, const hyena_plan_s* plan) {
     const hipDataType dt = bf16 ? HIP_R_16BF : HIP_R_32F;
     const int64_t L = plan->L, D = plan->D, C = (int64_t)(plan->order + 1) * plan->D;
     const hipblasOperation_t T = HIPBLAS_OP_T, N = HIPBLAS_OP_N;
-    // in_proj: U (L x C, ld L) = op_T(X: D x L, ld D) * W (D x C, ld D) + CB (L x C, ld L)
+    // in_proj: U (L x C, ld L) = op_T(Xa: Dp x L, ld Dp) * Wa (Dp x C, ld Dp)
     if (!custom_inproj(plan)) {
+        const int64_t Dp = aug_dim(D);
         Gemm& g1 = s.in;
         if (hipblasLtMatmulDescCreate(&g1.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS)
             return false;
@@ -174,7 +214,7 @@ bool build(OpState& s, const hyena_plan_s* plan) {
             hipblasLtMatmulDescSetAttribute(g1.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &N, sizeof(N)) !=
                 HIPBLAS_STATUS_SUCCESS)
             return false;
-        if (!layout(&g1.a, dt, D, L, D) || !layout(&g1.b, dt, D, C, D) || !layout(&g1.c, dt, L, C, L) ||
+        if (!layout(&g1.a, dt, Dp, L, Dp) || !layout(&g1.b, dt, Dp, C, Dp) || !layout(&g1.c, dt, L, C, L) ||
             !layout(&g1.d, dt, L, C, L))
             return false;
         if (!pick_algo(s.lt, g1)) return false;
@@ -209,7 +249,8 @@ bool build(OpState& s, const hyena_plan_s* plan) {
 struct Carve {
     void* u;
     void* y;
-    void* cb;    // broadcast input-bias matrix (hipBLASLt in_proj only)
+    void* xa;    // x with the bias term appended, [B][L][Dp] (hipBLASLt in_proj only)
+    void* wa;    // w_in with b_in appended, [C][Dp] (hipBLASLt in_proj only)
     void* taps;  // identity short-conv taps (fused in_proj only)
     void* lt;
     void* path;
@@ -230,10 +271,12 @@ Carve carve(const hyena_plan_s* plan, int64_t B, void* base) {
     c.u = take((size_t)B * C * L * s);
     c.y = take((size_t)B * D * L * s);
     if (custom_inproj(plan)) {
-        c.cb = nullptr;
+        c.xa = c.wa = nullptr;
         c.taps = take(C * 3 * sizeof(float));
     } else {
-        c.cb = take(L * C * s);
+        const size_t Dp = (size_t)aug_dim((int64_t)D);
+        c.xa = take((size_t)B * L * Dp * s);
+        c.wa = take(C * Dp * s);
         c.taps = nullptr;
     }
     c.lt = take(kLtWorkspace);
@@ -283,10 +326,31 @@ hyena_status_t operator_impl(hyena_plan_t plan, int64_t B, const void* x, const 
     const bool bf16 = plan->dtype == HYENA_BF16;
     const size_t es = bf16 ? 2 : 4;
     const int64_t L = plan->L, D = plan->D, C = (int64_t)(plan->order + 1) * plan->D;
+    const int64_t Dp = aug_dim(D);
+    // the bias-augmented operands of the hipBLASLt input projection
+    auto augment = [&]() -> bool {
+        auto grid = [](int64_t rows) { return (unsigned)(rows < 16384 ? rows : 16384); };
+        const int d = (int)D, dp = (int)Dp;
+        if (bf16) {
+            hipLaunchKernelGGL(k_augment_rows<uint16_t>, dim3(grid(B * L)), dim3(256), 0, stream, (const uint16_t*)x,
+                               (const uint16_t*)nullptr, (uint16_t*)c.xa, B * L, d, dp);
+            hipLaunchKernelGGL(k_augment_rows<uint16_t>, dim3(grid(C)), dim3(256), 0, stream, (const uint16_t*)w_in,
+                               (const uint16_t*)b_in, (uint16_t*)c.wa, C, d, dp);
+        } else {
+            hipLaunchKernelGGL(k_augment_rows<float>, dim3(grid(B * L)), dim3(256), 0, stream, (const float*)x,
+                               (const float*)nullptr, (float*)c.xa, B * L, d, dp);
+            hipLaunchKernelGGL(k_augment_rows<float>, dim3(grid(C)), dim3(256), 0, stream, (const float*)w_in,
+                               (const float*)b_in, (float*)c.wa, C, d, dp);
+        }
+        return hipGetLastError() == hipSuccess;
+    };
     if (tune_only) {
         // time the hipBLASLt candidates on sequence 0's operands (outputs are scratch)
         const float one = 1.f, zero = 0.f;
-        if (!custom_inproj(plan)) tune(s.lt, s.in, &one, x, w_in, &one, c.cb, c.u, c.lt, stream);
+        if (!custom_inproj(plan)) {
+            if (!augment()) return HYENA_ERR_DEVICE;
+            tune(s.lt, s.in, &one, c.xa, c.wa, &zero, c.u, c.u, c.lt, stream);
+        }
         if (!custom_outproj(plan)) {
             hipblasLtMatmulDescSetAttribute(s.out.desc, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &b_out, sizeof(b_out));
             tune(s.lt, s.out, &one, w_out, c.y, &zero, out, out, c.lt, stream);
@@ -316,20 +380,12 @@ hyena_status_t operator_impl(hyena_plan_t plan, int64_t B, const void* x, const 
             st = HYENA_ERR_DEVICE;
         path_taps = (const float*)c.taps;
     } else {
-        // input projection, with b_in broadcast through the C operand
-        const int64_t n = L * C;
-        const unsigned grid = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-        if (bf16)
-            hipLaunchKernelGGL(k_bias_matrix<uint16_t>, dim3(grid), dim3(256), 0, stream, (const uint16_t*)b_in,
-                               (uint16_t*)c.cb, L, C);
-        else
-            hipLaunchKernelGGL(k_bias_matrix<float>, dim3(grid), dim3(256), 0, stream, (const float*)b_in,
-                               (float*)c.cb, L, C);
-        if (hipGetLastError() != hipSuccess) st = HYENA_ERR_DEVICE;
+        // input projection, with b_in as one more term of the inner dimension
+        if (!augment()) st = HYENA_ERR_DEVICE;
         for (int64_t b = 0; b < B && st == HYENA_OK; ++b) {
-            const char* xb = static_cast<const char*>(x) + (size_t)b * L * D * es;
+            const char* xb = static_cast<const char*>(c.xa) + (size_t)b * L * Dp * es;
             char* ub = static_cast<char*>(c.u) + (size_t)b * C * L * es;
-            if (hipblasLtMatmul(s.lt, s.in.desc, &one, xb, s.in.a, w_in, s.in.b, &one, c.cb, s.in.c, ub, s.in.d,
+            if (hipblasLtMatmul(s.lt, s.in.desc, &one, xb, s.in.a, c.wa, s.in.b, &zero, ub, s.in.c, ub, s.in.d,
                                 &s.in.algo, c.lt, kLtWorkspace, stream) != HIPBLAS_STATUS_SUCCESS)
                 st = HYENA_ERR_DEVICE;
         }

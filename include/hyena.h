@@ -365,9 +365,11 @@ hyena_status_t hyena_backward_per_sample(hyena_plan_t plan, int64_t B, const voi
 /* Bytes of workspace hyena_operator_forward needs for batch B: the in-projected
  * activation u_proj, the path output y, either the identity short-conv taps
  * (bf16 plans with D a multiple of 64, whose input projection is fused with the
- * short conv) or a broadcast input-bias matrix (other plans), 32 MiB of GEMM
- * scratch and the path's own workspace (hyena_workspace_bytes), each 256-byte
- * aligned. Returns 0 for a NULL plan or B < 1. */
+ * short conv) or, for the other plans, x and w_in with the input-bias term
+ * appended to each row (B*L + (N+1)*D rows of Dp = D + 1 rounded up to 8
+ * values), 32 MiB of GEMM scratch and the path's own workspace
+ * (hyena_workspace_bytes), each 256-byte aligned. Returns 0 for a NULL plan or
+ * B < 1. */
 size_t hyena_operator_workspace_bytes(hyena_plan_t plan, int64_t B);
 
 /* The whole operator forward around the hot path (HyenaDNA walkthrough, section
