@@ -59,6 +59,10 @@ CASES = [
     (3, 128, 128, 2, "bf16", "auto"),      # out_proj: one time tile per sequence, half of it past L
     (2, 320, 512, 3, "bf16", "auto"),      # C = 1280: five full channel tiles
     (1, 192, 65536, 2, "bf16", "auto"),    # C = 576: a partial channel tile; four-step path
+    # hipBLASLt in_proj with b_in as one more inner-dimension term: widths whose padded
+    # inner dimension (D + 1 rounded up to 8) holds zeros after the bias term
+    (2, 5, 512, 2, "f32", "auto"),         # inner dimension 8: five values, the bias term, two zeros
+    (1, 12, 1024, 3, "bf16", "auto"),      # inner dimension 16 (bf16 below the matrix-core width)
 ]
 
 
