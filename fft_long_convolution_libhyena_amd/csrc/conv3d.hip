@@ -112,6 +112,227 @@ hipError_t ccol(int logN, int kind, const float2* in, float2* out, const float2*
     return hipGetLastError();
 }
 
+// Slab pass (zero-padded plans whose height x row slab pair fits in LDS): the
+// height transforms, the row pass and the inverse height transforms of one pair of
+// depth slices in one launch, on chip. Workgroup j of a volume takes slices
+// {j, 2A - j} (j = 0: the two self-paired slices 0 and A): their tile-1 values
+// [h < H][m < W/2] go through column FFTs over h (length Th = 2H, first radix pass
+// pruned) into an LDS array of 2 Th padded rows, then row FFTs over m (length W,
+// pruned), the pair step with the kernel spectrum plus the bias exactly as in the
+// row pass (row (ka, kh) with (-ka, -kh), bin kw with -kw), inverse rows (m < W/2
+// kept) and inverse columns (h < H kept) back into tile 1. The same transforms as
+// passes A2, B and C2, without tile 2.
+template <int LOGTH, int LOGW>
+struct C3Slab {
+    static constexpr int Th = 1 << LOGTH, W = 1 << LOGW, H = Th / 2, W2 = W / 2;
+    static constexpr int T1 = Th / 16, T2 = W / 16;  // threads per column / row transform
+    static constexpr int NT = 2 * W2 * T1;            // one column transform set per launch of threads
+    static constexpr int RP = W + W / 16;             // padded LDS row
+    static constexpr bool OK = Th * W <= 4096 && NT >= 64 && NT % 64 == 0;
+};
+
+template <int LOGTH, int LOGW>
+__global__ void __launch_bounds__((C3Slab<LOGTH, LOGW>::NT))
+k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float* __restrict__ bias,
+          const float2* __restrict__ twh, const float2* __restrict__ tww, const float2* __restrict__ wpair, int A,
+          int D, int64_t row0, int64_t nrows, bool per_sample) {
+    using S = C3Slab<LOGTH, LOGW>;
+    constexpr int Th = S::Th, W = S::W, H = S::H, W2 = S::W2, T1 = S::T1, T2 = S::T2, NT = S::NT, RP = S::RP;
+    static_assert(S::OK, "slab pair must fit the workgroup");
+    __shared__ float2 lds[2 * Th * RP];
+    int64_t r;
+    int j;
+    if (!xcd_row_map(blockIdx.x, nrows, A, r, j)) return;
+    const int tid = threadIdx.x;
+    const int ka0 = j == 0 ? 0 : j, ka1 = j == 0 ? A : 2 * A - j;  // the two slices
+    const int64_t slice = (int64_t)H * W2;
+    float2* vol = t1 + r * (int64_t)(2 * A) * slice;
+    auto lds_at = [&](int row, int m) -> float2& { return lds[row * RP + m + m / 16]; };
+
+    // columns over h: thread (s, t, c), c fastest so that global rows are coalesced
+    const int cs = tid / (W2 * T1), cc = tid % W2, ct = (tid / W2) % T1;
+    const int cka = cs == 0 ? ka0 : ka1;
+    const ColAcc<RP> cacc{lds + cs * Th * RP + cc + cc / 16};
+    {
+        float2 a[16];
+        const float2* src = vol + cka * slice + cc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = src[(int64_t)(ct + T1 * e) * W2];
+#pragma unroll
+        for (int e = 8; e < 16; ++e) a[e] = make_float2(0.f, 0.f);
+        fft_strided<Th, false, true>(a, ct, twh, cacc);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 16; ++e) lds_at(cs * Th + ct + T1 * e, cc) = a[e];
+    }
+    // the pair step's units (Th units of two rows, 2 T2 threads each, two batches)
+    // and their spectrum values, fetched now so that the row transforms hide them
+    const int64_t flat = row0 + r;
+    const int d = (int)(flat % D);
+    const int NR = 2 * A * Th;  // rows of the spectrum, (ka, kh) flattened as ka * Th + kh
+    const float2* Sp = spec + (per_sample ? flat : (int64_t)d) * NR * (W + 1);
+    struct Unit {
+        int la, lb, ga, gb;  // LDS rows and spectrum rows
+        bool self;
+    };
+    auto unit_of = [&](int it) {
+        const int u = it * (NT / (2 * T2)) + tid / (2 * T2);
+        Unit q;
+        if (j != 0) {
+            const int kh2 = (Th - u) & (Th - 1);
+            q.la = u;
+            q.lb = Th + kh2;
+            q.ga = ka0 * Th + u;
+            q.gb = ka1 * Th + kh2;
+            q.self = false;
+        } else {
+            const int sl = u / H, p = u % H;  // slice ka0 = 0 (sl 0) or ka1 = A (sl 1)
+            const int ka = sl == 0 ? ka0 : ka1;
+            const int kb = p == 0 ? H : Th - p;
+            q.la = sl * Th + p;
+            q.lb = sl * Th + kb;
+            q.ga = ka * Th + p;
+            q.gb = ka * Th + kb;
+            q.self = p == 0;
+        }
+        return q;
+    };
+    const int tp = tid % (2 * T2);
+    // per pair slot: the spectrum values at (row a, kw) and (row b, W - kw); for the
+    // self-paired rows (row of jj, kw) and (same row, W - kw), kw = 0 taking bins 0 and W
+    float2 sa[2][8], sb[2][8];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const Unit q = unit_of(it);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int jj = tp + 2 * T2 * e;
+            int rowa = q.ga, rowb = q.gb, bina = jj, binb = W - jj;
+            if (q.self) {
+                const int kw = jj & (W2 - 1);
+                rowa = rowb = jj < W2 ? q.ga : q.gb;
+                bina = kw;
+                binb = W - kw;
+            }
+            sa[it][e] = Sp[(int64_t)rowa * (W + 1) + bina];
+            sb[it][e] = Sp[(int64_t)rowb * (W + 1) + binb];
+        }
+    }
+    // rows over m, two batches of the 2 Th rows
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int R = it * (NT / T2) + tid / T2, t = tid % T2;
+        const RowAcc racc{lds + R * RP};
+        float2 a[16];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = racc[t + T2 * e];
+#pragma unroll
+        for (int e = 8; e < 16; ++e) a[e] = make_float2(0.f, 0.f);
+        fft_strided<W, false, true>(a, t, tww, racc);
+        __syncthreads();
+        lds_store_strided<T2>(racc, t, a);
+    }
+    __syncthreads();
+    // pair step
+    const float nscale = 1.0f / (4.0f * (float)NR * (float)W);
+    const float bs = bias[d] * nscale;
+    auto hs = [&](int row, int bin) { return hadd(Sp[(int64_t)row * (W + 1) + bin], bs); };
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const Unit q = unit_of(it);
+        const RowAcc au0{lds + q.la * RP}, au1{lds + q.lb * RP};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int jj = tp + 2 * T2 * e;  // < W
+            const float2 ha = hadd(sa[it][e], bs), hb = hadd(sb[it][e], bs);
+            if (!q.self) {
+                const int kw = jj, kw2 = (W - kw) & (W - 1);
+                float2 Ya, Yb;
+                pair_conv(au0[kw], au1[kw2], ha, hb, wpair[kw], Ya, Yb);
+                au0[kw] = Ya;
+                au1[kw2] = Yb;
+            } else {
+                // two self-paired rows: jj < W/2 serves row la, jj >= W/2 row lb;
+                // kw = 0 also takes the self-paired bins 0, W/2 and W of its row
+                const int sel = jj < W2 ? 0 : 1;
+                const int gr = sel == 0 ? q.ga : q.gb;
+                const RowAcc ro = sel == 0 ? au0 : au1;
+                const int kw = jj & (W2 - 1);
+                if (kw == 0) {
+                    const float2 Z0 = ro[0], Zh = ro[W2];
+                    const float2 Hh = hs(gr, W2);
+                    float2 Y0, Yx, Yh, Yy;
+                    pair_conv(Z0, Z0, ha, hb, make_float2(1.f, 0.f), Y0, Yx);  // bins 0 and W
+                    pair_conv(Zh, Zh, Hh, Hh, wpair[W2], Yh, Yy);
+                    ro[0] = Y0;
+                    ro[W2] = Yh;
+                } else {
+                    float2 Ya, Yb;
+                    pair_conv(ro[kw], ro[W - kw], ha, hb, wpair[kw], Ya, Yb);
+                    ro[kw] = Ya;
+                    ro[W - kw] = Yb;
+                }
+            }
+        }
+    }
+    // inverse rows, columns m < W/2 kept
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int R = it * (NT / T2) + tid / T2, t = tid % T2;
+        const RowAcc racc{lds + R * RP};
+        float2 a[16];
+        __syncthreads();
+        lds_load_strided<T2>(racc, t, a);
+        fft_strided<W, true, false>(a, t, tww, racc);
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) racc[t + T2 * e] = a[e];
+    }
+    __syncthreads();
+    // inverse columns over kh, rows h < H kept, back to tile 1
+    {
+        float2 a[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) a[e] = lds_at(cs * Th + ct + T1 * e, cc);
+        fft_strided<Th, true, false>(a, ct, twh, cacc);
+        float2* dst = vol + cka * slice + cc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[(int64_t)(ct + T1 * e) * W2] = a[e];
+    }
+}
+
+template <int LOGTH, int LOGW>
+hipError_t launch_slab_t(float2* t1, const float2* spec, const float* bias, const float2* twh, const float2* tww,
+                         const float2* wpair, int A, int D, int64_t row0, int64_t n, bool per_sample,
+                         hipStream_t st) {
+    using S = C3Slab<LOGTH, LOGW>;
+    if constexpr (!S::OK) {
+        return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((k_c3_slab<LOGTH, LOGW>), dim3((unsigned)xcd_grid(n, A)), dim3(S::NT), 0, st, t1, spec,
+                           bias, twh, tww, wpair, A, D, row0, n, per_sample);
+        return hipGetLastError();
+    }
+}
+
+// Whether a zero-padded plan with height transforms of 2^lh and row transforms of
+// 2^lr packed points takes the slab pass.
+bool slab_ok(int lh, int lr) {
+    const int sum = lh + lr;
+    return lh >= 5 && lr >= 5 && sum >= 10 && sum <= 12;
+}
+
+hipError_t slab(int lh, int lr, float2* t1, const float2* spec, const float* bias, const float2* twh,
+                const float2* tww, const float2* wpair, int A, int D, int64_t row0, int64_t n, bool per_sample,
+                hipStream_t st) {
+#define C3_SLAB(a, b) \
+    if (lh == a && lr == b) return launch_slab_t<a, b>(t1, spec, bias, twh, tww, wpair, A, D, row0, n, per_sample, st);
+    C3_SLAB(5, 5) C3_SLAB(5, 6) C3_SLAB(5, 7) C3_SLAB(6, 5) C3_SLAB(6, 6) C3_SLAB(7, 5)
+#undef C3_SLAB
+    return hipErrorInvalidValue;
+}
+
 hyena_status_t check3d(const hyena_plan3d_t plan) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return HYENA_ERR_DEVICE;
@@ -269,19 +490,28 @@ static hyena_status_t conv3d_impl(hyena_plan3d_t plan, int64_t B, const void* v,
     float2* t1 = (float2*)workspace;
     float2* t2 = circ ? t1 : t1 + chunk * (int64_t)hy::tile1_elems(plan);
     const hy::PairMap3 pm{plan->pa, plan->ph};
+#ifndef HY_C3_SLAB
+#define HY_C3_SLAB 1
+#endif
+    const bool use_slab = HY_C3_SLAB && !circ && hy::slab_ok(plan->lh, plan->lr);
     for (int64_t r0 = 0; r0 < nv; r0 += chunk) {
         const int64_t n = nv - r0 < chunk ? nv - r0 : chunk;
         hipError_t e =
             hy::cols(plan->la, true, bf16, v, g, nullptr, t1, nullptr, plan->twa, plane, r0, n, stream, circ);
-        if (e == hipSuccess)
-            e = hy::ccol(plan->lh, circ ? hy::kColFwdFull : hy::kColFwdPruned, t1, t2, plan->twh, n * Ta, (int)W2,
-                         H * W2, W2, (int)W2, (int)W2, Th * W2, W2, (int)W2, (int)W2, stream);
-        if (e == hipSuccess)
-            e = hy::rows(plan->lr, 0, t2, (const float2*)spec, bias, plan->tww, plan->wpair, pm,
-                         2 * plan->pa * plan->ph, (int)plan->D, r0, n, per_sample, stream, circ);
-        if (e == hipSuccess)
-            e = hy::ccol(plan->lh, circ ? hy::kColInvFull : hy::kColInvHalf, t2, t1, plan->twh, n * Ta, (int)W2,
-                         Th * W2, W2, (int)W2, (int)W2, H * W2, W2, (int)W2, (int)W2, stream);
+        if (e == hipSuccess && use_slab) {
+            e = hy::slab(plan->lh, plan->lr, t1, (const float2*)spec, bias, plan->twh, plan->tww, plan->wpair,
+                         (int)plan->A, (int)plan->D, r0, n, per_sample, stream);
+        } else {
+            if (e == hipSuccess)
+                e = hy::ccol(plan->lh, circ ? hy::kColFwdFull : hy::kColFwdPruned, t1, t2, plan->twh, n * Ta,
+                             (int)W2, H * W2, W2, (int)W2, (int)W2, Th * W2, W2, (int)W2, (int)W2, stream);
+            if (e == hipSuccess)
+                e = hy::rows(plan->lr, 0, t2, (const float2*)spec, bias, plan->tww, plan->wpair, pm,
+                             2 * plan->pa * plan->ph, (int)plan->D, r0, n, per_sample, stream, circ);
+            if (e == hipSuccess)
+                e = hy::ccol(plan->lh, circ ? hy::kColInvFull : hy::kColInvHalf, t2, t1, plan->twh, n * Ta,
+                             (int)W2, Th * W2, W2, (int)W2, (int)W2, H * W2, W2, (int)W2, (int)W2, stream);
+        }
         if (e == hipSuccess)
             e = hy::cols(plan->la, false, bf16, nullptr, nullptr, x, t1, y, plan->twa, plane, r0, n, stream, circ);
         if (e != hipSuccess) return HYENA_ERR_DEVICE;

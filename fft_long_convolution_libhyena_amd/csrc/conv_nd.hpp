@@ -229,20 +229,39 @@ k_cnd_row(float2* __restrict__ buf, const float2* __restrict__ spec, const float
 #pragma unroll
         for (int e = 0; e < 16; ++e) a[e] = rowp[t + T2 * e];
     }
+    // pair-step role: 2*T2 threads per unit, W pairs per unit
+    const int unit = tau / (2 * T2), tp = tau % (2 * T2);
+    int ka, kb;
+    bool self;
+    map.unit(ug * U + unit, ka, kb, self);
+    const int64_t flat = row0 + r;
+    const int d = (int)(flat % D);
+    const float2* S = MODE == 0 ? spec + (per_sample ? flat : (int64_t)d) * NR * (W + 1) : nullptr;
+    // MODE 0: the spectrum values of this thread's pair slots, fetched before the
+    // row transform so that it hides their latency: (row a, kw) and (row b, W - kw);
+    // for self-paired rows (the slot's row, kw) and (same row, W - kw), kw = 0
+    // taking bins 0 and W
+    [[maybe_unused]] float2 sa[8], sb[8];
+    if constexpr (MODE == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int j = tp + 2 * T2 * e;
+            int rowa = ka, rowb = kb, bina = j, binb = W - j;
+            if (self) {
+                rowa = rowb = j < HW ? ka : kb;
+                bina = j & (HW - 1);
+                binb = W - bina;
+            }
+            sa[e] = S[(int64_t)rowa * (W + 1) + bina];
+            sb[e] = S[(int64_t)rowb * (W + 1) + binb];
+        }
+    }
     fft_strided<W, false, MODE == 0 && !CIRC>(a, t, tw2, racc);
     __syncthreads();
     lds_store_strided<T2>(racc, t, a);
     __syncthreads();
 
-    // pair step: 2*T2 threads per unit, W pairs per unit
-    const int unit = tau / (2 * T2), tp = tau % (2 * T2);
-    int ka, kb;
-    bool self;
-    map.unit(ug * U + unit, ka, kb, self);
     const RowAcc au[2] = {RowAcc{lds + (2 * unit) * RP}, RowAcc{lds + (2 * unit + 1) * RP}};
-    const int64_t flat = row0 + r;
-    const int d = (int)(flat % D);
-    const float2* S = MODE == 0 ? spec + (per_sample ? flat : (int64_t)d) * NR * (W + 1) : nullptr;
     const float nscale = 1.0f / (4.0f * (float)NR * (float)W);
     const float bs = MODE == 0 ? bias[d] * nscale : 0.f;
     const float sc = 0.5f * nscale;  // the unpacked values are twice the spectrum
@@ -256,7 +275,7 @@ k_cnd_row(float2* __restrict__ buf, const float2* __restrict__ spec, const float
             const float2 Za = au[0][kw], Zb = au[1][kw2];
             if constexpr (MODE == 0) {
                 float2 Ya, Yb;
-                pair_conv(Za, Zb, hs(ka, kw), hs(kb, W - kw), wpair[kw], Ya, Yb);
+                pair_conv(Za, Zb, hadd(sa[e], bs), hadd(sb[e], bs), wpair[kw], Ya, Yb);
                 au[0][kw] = Ya;
                 au[1][kw2] = Yb;
             } else {
@@ -280,7 +299,7 @@ k_cnd_row(float2* __restrict__ buf, const float2* __restrict__ spec, const float
                 const float2 Z0 = ro[0], Zh = ro[HW];
                 if constexpr (MODE == 0) {
                     float2 Y0, Yx, Yh, Yy;
-                    pair_conv(Z0, Z0, hs(kr, 0), hs(kr, W), make_float2(1.f, 0.f), Y0, Yx);
+                    pair_conv(Z0, Z0, hadd(sa[e], bs), hadd(sb[e], bs), make_float2(1.f, 0.f), Y0, Yx);
                     pair_conv(Zh, Zh, hs(kr, HW), hs(kr, HW), wpair[HW], Yh, Yy);
                     ro[0] = Y0;
                     ro[HW] = Yh;
@@ -296,7 +315,7 @@ k_cnd_row(float2* __restrict__ buf, const float2* __restrict__ spec, const float
                 const float2 Za = ro[kw], Zb = ro[W - kw];
                 if constexpr (MODE == 0) {
                     float2 Ya, Yb;
-                    pair_conv(Za, Zb, hs(kr, kw), hs(kr, W - kw), wpair[kw], Ya, Yb);
+                    pair_conv(Za, Zb, hadd(sa[e], bs), hadd(sb[e], bs), wpair[kw], Ya, Yb);
                     ro[kw] = Ya;
                     ro[W - kw] = Yb;
                 } else {
