@@ -112,32 +112,38 @@ hipError_t ccol(int logN, int kind, const float2* in, float2* out, const float2*
     return hipGetLastError();
 }
 
-// Slab pass (zero-padded plans whose height x row slab pair fits in LDS): the
-// height transforms, the row pass and the inverse height transforms of one pair of
-// depth slices in one launch, on chip. Workgroup j of a volume takes slices
-// {j, 2A - j} (j = 0: the two self-paired slices 0 and A): their tile-1 values
-// [h < H][m < W/2] go through column FFTs over h (length Th = 2H, first radix pass
-// pruned) into an LDS array of 2 Th padded rows, then row FFTs over m (length W,
-// pruned), the pair step with the kernel spectrum plus the bias exactly as in the
-// row pass (row (ka, kh) with (-ka, -kh), bin kw with -kw), inverse rows (m < W/2
-// kept) and inverse columns (h < H kept) back into tile 1. The same transforms as
-// passes A2, B and C2, without tile 2.
-template <int LOGTH, int LOGW>
+// Slab pass (plans whose height x row slab pair fits in LDS): the height
+// transforms, the row pass and the inverse height transforms of one pair of depth
+// slices in one launch, on chip. Workgroup j of a volume takes slices {j, 2A - j}
+// (j = 0: the two self-paired slices 0 and A; A here is half the depth transform):
+// their tile-1 values go through column FFTs over h (length Th) into an LDS array of
+// 2 Th padded rows, then row FFTs over m (length W), the pair step with the kernel
+// spectrum plus the bias exactly as in the row pass (row (ka, kh) with (-ka, -kh),
+// bin kw with -kw), inverse rows and inverse columns back into tile 1. The same
+// transforms as passes A2, B and C2, without tile 2. Zero-padded plans: tile-1 rows
+// h < Th/2 and columns m < W/2 hold data, the first radix passes are pruned and
+// only those outputs are kept. CIRC (circular plans): every row and column holds
+// data, nothing is pruned, everything is kept.
+template <int LOGTH, int LOGW, bool CIRC>
 struct C3Slab {
-    static constexpr int Th = 1 << LOGTH, W = 1 << LOGW, H = Th / 2, W2 = W / 2;
-    static constexpr int T1 = Th / 16, T2 = W / 16;  // threads per column / row transform
-    static constexpr int NT = 2 * W2 * T1;            // one column transform set per launch of threads
-    static constexpr int RP = W + W / 16;             // padded LDS row
-    static constexpr bool OK = Th * W <= 4096 && NT >= 64 && NT % 64 == 0;
+    static constexpr int Th = 1 << LOGTH, W = 1 << LOGW, HP = Th / 2, WH = W / 2;
+    static constexpr int HR = CIRC ? Th : HP, NC = CIRC ? W : WH;  // tile-1 rows and columns per slice
+    static constexpr int LD = CIRC ? 16 : 8;                       // values per thread holding data
+    static constexpr int T1 = Th / 16, T2 = W / 16;                // threads per column / row transform
+    static constexpr int NT = 2 * NC * T1;                         // the column transforms of both slices
+    static constexpr int IT = 2 * Th * T2 / NT;                    // row (and pair-unit) batches
+    static constexpr int RP = W + W / 16;                          // padded LDS row
+    static constexpr bool OK = Th * W <= 4096 && T1 >= 1 && NT >= 64 && NT % 64 == 0 && IT * NT == 2 * Th * T2;
 };
 
-template <int LOGTH, int LOGW>
-__global__ void __launch_bounds__((C3Slab<LOGTH, LOGW>::NT))
+template <int LOGTH, int LOGW, bool CIRC>
+__global__ void __launch_bounds__((C3Slab<LOGTH, LOGW, CIRC>::NT))
 k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float* __restrict__ bias,
           const float2* __restrict__ twh, const float2* __restrict__ tww, const float2* __restrict__ wpair, int A,
           int D, int64_t row0, int64_t nrows, bool per_sample) {
-    using S = C3Slab<LOGTH, LOGW>;
-    constexpr int Th = S::Th, W = S::W, H = S::H, W2 = S::W2, T1 = S::T1, T2 = S::T2, NT = S::NT, RP = S::RP;
+    using S = C3Slab<LOGTH, LOGW, CIRC>;
+    constexpr int Th = S::Th, W = S::W, HP = S::HP, WH = S::WH, HR = S::HR, NC = S::NC, LD = S::LD;
+    constexpr int T1 = S::T1, T2 = S::T2, NT = S::NT, IT = S::IT, RP = S::RP;
     static_assert(S::OK, "slab pair must fit the workgroup");
     __shared__ float2 lds[2 * Th * RP];
     int64_t r;
@@ -145,27 +151,27 @@ k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float*
     if (!xcd_row_map(blockIdx.x, nrows, A, r, j)) return;
     const int tid = threadIdx.x;
     const int ka0 = j == 0 ? 0 : j, ka1 = j == 0 ? A : 2 * A - j;  // the two slices
-    const int64_t slice = (int64_t)H * W2;
+    const int64_t slice = (int64_t)HR * NC;
     float2* vol = t1 + r * (int64_t)(2 * A) * slice;
     auto lds_at = [&](int row, int m) -> float2& { return lds[row * RP + m + m / 16]; };
 
     // columns over h: thread (s, t, c), c fastest so that global rows are coalesced
-    const int cs = tid / (W2 * T1), cc = tid % W2, ct = (tid / W2) % T1;
+    const int cs = tid / (NC * T1), cc = tid % NC, ct = (tid / NC) % T1;
     const int cka = cs == 0 ? ka0 : ka1;
     const ColAcc<RP> cacc{lds + cs * Th * RP + cc + cc / 16};
     {
         float2 a[16];
         const float2* src = vol + cka * slice + cc;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = src[(int64_t)(ct + T1 * e) * W2];
+        for (int e = 0; e < LD; ++e) a[e] = src[(int64_t)(ct + T1 * e) * NC];
 #pragma unroll
-        for (int e = 8; e < 16; ++e) a[e] = make_float2(0.f, 0.f);
-        fft_strided<Th, false, true>(a, ct, twh, cacc);
+        for (int e = LD; e < 16; ++e) a[e] = make_float2(0.f, 0.f);
+        fft_strided<Th, false, !CIRC>(a, ct, twh, cacc);
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < 16; ++e) lds_at(cs * Th + ct + T1 * e, cc) = a[e];
     }
-    // the pair step's units (Th units of two rows, 2 T2 threads each, two batches)
+    // the pair step's units (Th units of two rows, 2 T2 threads each, IT batches)
     // and their spectrum values, fetched now so that the row transforms hide them
     const int64_t flat = row0 + r;
     const int d = (int)(flat % D);
@@ -186,9 +192,9 @@ k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float*
             q.gb = ka1 * Th + kh2;
             q.self = false;
         } else {
-            const int sl = u / H, p = u % H;  // slice ka0 = 0 (sl 0) or ka1 = A (sl 1)
+            const int sl = u / HP, p = u % HP;  // slice ka0 = 0 (sl 0) or ka1 = A (sl 1)
             const int ka = sl == 0 ? ka0 : ka1;
-            const int kb = p == 0 ? H : Th - p;
+            const int kb = p == 0 ? HP : Th - p;
             q.la = sl * Th + p;
             q.lb = sl * Th + kb;
             q.ga = ka * Th + p;
@@ -200,17 +206,17 @@ k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float*
     const int tp = tid % (2 * T2);
     // per pair slot: the spectrum values at (row a, kw) and (row b, W - kw); for the
     // self-paired rows (row of jj, kw) and (same row, W - kw), kw = 0 taking bins 0 and W
-    float2 sa[2][8], sb[2][8];
+    float2 sa[IT][8], sb[IT][8];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < IT; ++it) {
         const Unit q = unit_of(it);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int jj = tp + 2 * T2 * e;
             int rowa = q.ga, rowb = q.gb, bina = jj, binb = W - jj;
             if (q.self) {
-                const int kw = jj & (W2 - 1);
-                rowa = rowb = jj < W2 ? q.ga : q.gb;
+                const int kw = jj & (WH - 1);
+                rowa = rowb = jj < WH ? q.ga : q.gb;
                 bina = kw;
                 binb = W - kw;
             }
@@ -218,18 +224,18 @@ k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float*
             sb[it][e] = Sp[(int64_t)rowb * (W + 1) + binb];
         }
     }
-    // rows over m, two batches of the 2 Th rows
+    // rows over m, IT batches of the 2 Th rows
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < IT; ++it) {
         const int R = it * (NT / T2) + tid / T2, t = tid % T2;
         const RowAcc racc{lds + R * RP};
         float2 a[16];
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = racc[t + T2 * e];
+        for (int e = 0; e < LD; ++e) a[e] = racc[t + T2 * e];
 #pragma unroll
-        for (int e = 8; e < 16; ++e) a[e] = make_float2(0.f, 0.f);
-        fft_strided<W, false, true>(a, t, tww, racc);
+        for (int e = LD; e < 16; ++e) a[e] = make_float2(0.f, 0.f);
+        fft_strided<W, false, !CIRC>(a, t, tww, racc);
         __syncthreads();
         lds_store_strided<T2>(racc, t, a);
     }
@@ -239,7 +245,7 @@ k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float*
     const float bs = bias[d] * nscale;
     auto hs = [&](int row, int bin) { return hadd(Sp[(int64_t)row * (W + 1) + bin], bs); };
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < IT; ++it) {
         const Unit q = unit_of(it);
         const RowAcc au0{lds + q.la * RP}, au1{lds + q.lb * RP};
 #pragma unroll
@@ -255,18 +261,18 @@ k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float*
             } else {
                 // two self-paired rows: jj < W/2 serves row la, jj >= W/2 row lb;
                 // kw = 0 also takes the self-paired bins 0, W/2 and W of its row
-                const int sel = jj < W2 ? 0 : 1;
+                const int sel = jj < WH ? 0 : 1;
                 const int gr = sel == 0 ? q.ga : q.gb;
                 const RowAcc ro = sel == 0 ? au0 : au1;
-                const int kw = jj & (W2 - 1);
+                const int kw = jj & (WH - 1);
                 if (kw == 0) {
-                    const float2 Z0 = ro[0], Zh = ro[W2];
-                    const float2 Hh = hs(gr, W2);
+                    const float2 Z0 = ro[0], Zh = ro[WH];
+                    const float2 Hh = hs(gr, WH);
                     float2 Y0, Yx, Yh, Yy;
                     pair_conv(Z0, Z0, ha, hb, make_float2(1.f, 0.f), Y0, Yx);  // bins 0 and W
-                    pair_conv(Zh, Zh, Hh, Hh, wpair[W2], Yh, Yy);
+                    pair_conv(Zh, Zh, Hh, Hh, wpair[WH], Yh, Yy);
                     ro[0] = Y0;
-                    ro[W2] = Yh;
+                    ro[WH] = Yh;
                 } else {
                     float2 Ya, Yb;
                     pair_conv(ro[kw], ro[W - kw], ha, hb, wpair[kw], Ya, Yb);
@@ -276,9 +282,9 @@ k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float*
             }
         }
     }
-    // inverse rows, columns m < W/2 kept
+    // inverse rows (zero-padded: columns m < W/2 kept)
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < IT; ++it) {
         const int R = it * (NT / T2) + tid / T2, t = tid % T2;
         const RowAcc racc{lds + R * RP};
         float2 a[16];
@@ -287,10 +293,10 @@ k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float*
         fft_strided<W, true, false>(a, t, tww, racc);
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) racc[t + T2 * e] = a[e];
+        for (int e = 0; e < LD; ++e) racc[t + T2 * e] = a[e];
     }
     __syncthreads();
-    // inverse columns over kh, rows h < H kept, back to tile 1
+    // inverse columns over kh (zero-padded: rows h < Th/2 kept), back to tile 1
     {
         float2 a[16];
 #pragma unroll
@@ -298,36 +304,38 @@ k_c3_slab(float2* __restrict__ t1, const float2* __restrict__ spec, const float*
         fft_strided<Th, true, false>(a, ct, twh, cacc);
         float2* dst = vol + cka * slice + cc;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dst[(int64_t)(ct + T1 * e) * W2] = a[e];
+        for (int e = 0; e < LD; ++e) dst[(int64_t)(ct + T1 * e) * NC] = a[e];
     }
 }
 
-template <int LOGTH, int LOGW>
+template <int LOGTH, int LOGW, bool CIRC>
 hipError_t launch_slab_t(float2* t1, const float2* spec, const float* bias, const float2* twh, const float2* tww,
                          const float2* wpair, int A, int D, int64_t row0, int64_t n, bool per_sample,
                          hipStream_t st) {
-    using S = C3Slab<LOGTH, LOGW>;
+    using S = C3Slab<LOGTH, LOGW, CIRC>;
     if constexpr (!S::OK) {
         return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((k_c3_slab<LOGTH, LOGW>), dim3((unsigned)xcd_grid(n, A)), dim3(S::NT), 0, st, t1, spec,
-                           bias, twh, tww, wpair, A, D, row0, n, per_sample);
+        hipLaunchKernelGGL((k_c3_slab<LOGTH, LOGW, CIRC>), dim3((unsigned)xcd_grid(n, A)), dim3(S::NT), 0, st, t1,
+                           spec, bias, twh, tww, wpair, A, D, row0, n, per_sample);
         return hipGetLastError();
     }
 }
 
-// Whether a zero-padded plan with height transforms of 2^lh and row transforms of
-// 2^lr packed points takes the slab pass.
+// Whether a plan with height transforms of 2^lh and row transforms of 2^lr packed
+// points takes the slab pass (the slice pair fits one workgroup's LDS).
 bool slab_ok(int lh, int lr) {
     const int sum = lh + lr;
     return lh >= 5 && lr >= 5 && sum >= 10 && sum <= 12;
 }
 
-hipError_t slab(int lh, int lr, float2* t1, const float2* spec, const float* bias, const float2* twh,
+hipError_t slab(int lh, int lr, bool circ, float2* t1, const float2* spec, const float* bias, const float2* twh,
                 const float2* tww, const float2* wpair, int A, int D, int64_t row0, int64_t n, bool per_sample,
                 hipStream_t st) {
-#define C3_SLAB(a, b) \
-    if (lh == a && lr == b) return launch_slab_t<a, b>(t1, spec, bias, twh, tww, wpair, A, D, row0, n, per_sample, st);
+#define C3_SLAB(a, b)                                                                                              \
+    if (lh == a && lr == b)                                                                                        \
+        return circ ? launch_slab_t<a, b, true>(t1, spec, bias, twh, tww, wpair, A, D, row0, n, per_sample, st)   \
+                    : launch_slab_t<a, b, false>(t1, spec, bias, twh, tww, wpair, A, D, row0, n, per_sample, st);
     C3_SLAB(5, 5) C3_SLAB(5, 6) C3_SLAB(5, 7) C3_SLAB(6, 5) C3_SLAB(6, 6) C3_SLAB(7, 5)
 #undef C3_SLAB
     return hipErrorInvalidValue;
@@ -493,14 +501,14 @@ static hyena_status_t conv3d_impl(hyena_plan3d_t plan, int64_t B, const void* v,
 #ifndef HY_C3_SLAB
 #define HY_C3_SLAB 1
 #endif
-    const bool use_slab = HY_C3_SLAB && !circ && hy::slab_ok(plan->lh, plan->lr);
+    const bool use_slab = HY_C3_SLAB && hy::slab_ok(plan->lh, plan->lr);
     for (int64_t r0 = 0; r0 < nv; r0 += chunk) {
         const int64_t n = nv - r0 < chunk ? nv - r0 : chunk;
         hipError_t e =
             hy::cols(plan->la, true, bf16, v, g, nullptr, t1, nullptr, plan->twa, plane, r0, n, stream, circ);
         if (e == hipSuccess && use_slab) {
-            e = hy::slab(plan->lh, plan->lr, t1, (const float2*)spec, bias, plan->twh, plan->tww, plan->wpair,
-                         (int)plan->A, (int)plan->D, r0, n, per_sample, stream);
+            e = hy::slab(plan->lh, plan->lr, circ, t1, (const float2*)spec, bias, plan->twh, plan->tww, plan->wpair,
+                         plan->pa, (int)plan->D, r0, n, per_sample, stream);
         } else {
             if (e == hipSuccess)
                 e = hy::ccol(plan->lh, circ ? hy::kColFwdFull : hy::kColFwdPruned, t1, t2, plan->twh, n * Ta,
