@@ -352,8 +352,13 @@ hyena_status_t check3d(const hyena_plan3d_t plan) {
 // transforms height in place: tile 2 is tile 1.
 size_t tile1_elems(const hyena_plan3d_t p) { return ((size_t)2 << p->la) * (size_t)p->H * (size_t)(p->W / 2); }
 size_t tile2_elems(const hyena_plan3d_t p) { return ((size_t)2 << p->la) * ((size_t)1 << p->lh) * (size_t)(p->W / 2); }
+#ifndef HY_C3_SLAB
+#define HY_C3_SLAB 1
+#endif
+// Whether the plan's forward takes the slab pass (then only tile 1 is used).
+bool uses_slab(const hyena_plan3d_t p) { return HY_C3_SLAB && slab_ok(p->lh, p->lr); }
 size_t vol_ws_bytes(const hyena_plan3d_t p) {
-    return (tile1_elems(p) + (p->circular ? 0 : tile2_elems(p))) * sizeof(float2);
+    return (tile1_elems(p) + (p->circular || uses_slab(p) ? 0 : tile2_elems(p))) * sizeof(float2);
 }
 
 }  // namespace
@@ -498,10 +503,7 @@ static hyena_status_t conv3d_impl(hyena_plan3d_t plan, int64_t B, const void* v,
     float2* t1 = (float2*)workspace;
     float2* t2 = circ ? t1 : t1 + chunk * (int64_t)hy::tile1_elems(plan);
     const hy::PairMap3 pm{plan->pa, plan->ph};
-#ifndef HY_C3_SLAB
-#define HY_C3_SLAB 1
-#endif
-    const bool use_slab = HY_C3_SLAB && hy::slab_ok(plan->lh, plan->lr);
+    const bool use_slab = hy::uses_slab(plan);
     for (int64_t r0 = 0; r0 < nv; r0 += chunk) {
         const int64_t n = nv - r0 < chunk ? nv - r0 : chunk;
         hipError_t e =

@@ -584,8 +584,11 @@ hyena_status_t hyena_plan3d_destroy(hyena_plan3d_t plan);
 size_t hyena_spectrum3d_bytes(hyena_plan3d_t plan);
 
 /* Workspace for hyena_conv3d_forward over batch B: any size of at least one
- * volume's two tiles (24 * A * H * W bytes) is accepted; this is the recommended
- * size (up to 192 MiB of tiles per launch). Returns 0 for a NULL plan or B < 1. */
+ * volume's tiles is accepted: for a zero-padded plan 24 * A * H * W bytes, or
+ * 8 * A * H * W when a depth slice's height x row transform (2H x W packed points)
+ * has at most 4096 points (the slab pass keeps one tile); 4 * A * H * W bytes for a
+ * circular plan. This is the recommended size (up to 192 MiB of tiles per launch).
+ * Returns 0 for a NULL plan or B < 1. */
 size_t hyena_workspace3d_bytes(hyena_plan3d_t plan, int64_t B);
 
 /* Kernel spectra, once per plan.
@@ -600,10 +603,12 @@ hyena_status_t hyena_filter_spectrum3d(hyena_plan3d_t plan, const float* k, void
  *   g, x [B][D][A][H][W] of the plan dtype, device, or NULL (no gate)
  *   spec from hyena_filter_spectrum3d of this plan; bias [D] fp32, device
  *   y    [B][D][A][H][W] of the plan dtype, device (output; must not alias inputs)
- *   workspace / workspace_bytes: at least 24*A*H*W bytes (hyena_workspace3d_bytes)
+ *   workspace / workspace_bytes: at least one volume's tiles (hyena_workspace3d_bytes)
  * Five passes per chunk of volumes: column FFTs over a of the gated volume and
  * over h, row FFTs over w with the spectrum multiply and the inverse rows, inverse
- * columns over h and over a with the gate; all intermediates fp32. Enqueued on
+ * columns over h and over a with the gate; all intermediates fp32. When a pair of
+ * depth slices fits one workgroup's LDS (the sizes above), the middle three run as
+ * one pass per slice pair on chip. Enqueued on
  * `stream`. Errors: HYENA_ERR_INVALID_ARG (NULL or misaligned pointers, B < 1,
  * B*D > 2^24), HYENA_ERR_WORKSPACE, HYENA_ERR_DEVICE. */
 hyena_status_t hyena_conv3d_forward(hyena_plan3d_t plan, int64_t B, const void* v, const void* g, const void* x,

@@ -143,14 +143,27 @@ def test_conv3d_error_paths():
         spec = p.spectrum(torch.from_numpy(inp.k).cuda())
         v = torch.from_numpy(inp.v).cuda()
         bias = torch.from_numpy(inp.bias).cuda()
+        # a 16 x 16 x 32 plan runs the slab pass: one tile of 8*A*H*W bytes per volume
         with pytest.raises(HyenaError) as e:
             p.forward(v, spec, bias,
-                      workspace=torch.empty(24 * 16 * 16 * 32 - 256, dtype=torch.uint8, device="cuda"))
+                      workspace=torch.empty(8 * 16 * 16 * 32 - 256, dtype=torch.uint8, device="cuda"))
         assert e.value.status == 3
+        assert p.workspace_bytes(1) % (8 * 16 * 16 * 32) == 0
         with pytest.raises(ValueError):
             p.forward(v[:, :1].contiguous(), spec, bias)
         with pytest.raises(ValueError):
             p.spectrum(torch.from_numpy(inp.k[:, :16]).contiguous().cuda())
+    # 16 x 16 x 512 (rows of 512 packed points) keeps the five passes and both tiles
+    inp = synth.conv3d_inputs(1, 1, 16, 16, 512, seed=2)
+    with Plan3D(16, 16, 512, 1) as p:
+        spec = p.spectrum(torch.from_numpy(inp.k).cuda())
+        v = torch.from_numpy(inp.v).cuda()
+        bias = torch.from_numpy(inp.bias).cuda()
+        with pytest.raises(HyenaError) as e:
+            p.forward(v, spec, bias,
+                      workspace=torch.empty(24 * 16 * 16 * 512 - 256, dtype=torch.uint8, device="cuda"))
+        assert e.value.status == 3
+        assert p.workspace_bytes(1) == 24 * 16 * 16 * 512
 
 
 def test_conv3d_per_sample_matches_oracle():
