@@ -182,7 +182,11 @@ __global__ void __launch_bounds__(kThreads, 2) k_inproj_conv3(Inproj a) {
             __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6): all but the next chunk's six fills are in
         else
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        __syncthreads();  // everyone's fills of chunk ch are in, and chunk ch - 1 is no longer read
+        // everyone's fills of chunk ch are in (each wave's own wait above), and chunk ch - 1
+        // is no longer read (its fragments fed this wave's last matrix products). A bare
+        // barrier: the fenced one waits for every load in flight, the fills of chunk ch + 1
+        // too, which would leave one chunk in flight instead of two.
+        asm volatile("s_barrier" ::: "memory");
         if (ch + 2 < nchunks) fill(stage == 0 ? 2 : stage - 1, ch + 2);
         const unsigned char* st = lds_raw + stage * kStageBytes;
         frag(0, st, 0);
