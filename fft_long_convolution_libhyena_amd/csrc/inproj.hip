@@ -70,7 +70,7 @@ static_assert(kTN == 2 * kWN && kTM == 2 * kWM && kTN == 2 * kRoundCols, "tile s
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // slot of 16-byte segment s (0..3) in staged 64-byte row r: s ^ swizzle(r)
-__device__ __forceinline__ uint32_t seg_swizzle(uint32_t r) { return ((r >> 1) ^ (r >> 3)) & 3u; }
+__device__ __forceinline__ uint32_t seg_swizzle(uint32_t r) { return (r ^ (r >> 3)) & 3u; }
 
 struct Inproj {
     const uint16_t* x;   // [B*L][D]
