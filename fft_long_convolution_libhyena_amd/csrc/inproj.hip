@@ -193,6 +193,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_inproj_conv3(Inproj a) {
         frag(1, st, 1);
         mma(0);
         mma(1);
+        // schedule: the six fragment reads of k-step 0, then the first six products
+        // each followed by one read of k-step 1, then the remaining ten products
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // LDS reads
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a matrix product
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
         stage = stage == kNS - 1 ? 0 : stage + 1;
     }
 
